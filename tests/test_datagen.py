@@ -1,0 +1,85 @@
+"""The synthetic workload generators: determinism and the distributions they promise (no GPU)."""
+import numpy as np
+
+import datagen
+
+
+def test_deterministic_and_thread_independent(monkeypatch):
+    a = datagen.csr_zipf(2000, 5000, seed=3, alpha=0.7, beta=0.3)
+    b = datagen.csr_zipf(2000, 5000, seed=3, alpha=0.7, beta=0.3)
+    for k in ("row_ptr", "col_idx", "values", "y", "v", "z"):
+        assert np.array_equal(getattr(a, k), getattr(b, k))
+    c = datagen.csr_zipf(2000, 5000, seed=4)
+    assert not np.array_equal(a.values[:100], c.values[:100])
+    d1 = datagen.dense_problem(300, 40, seed=1, x="normal")
+    d2 = datagen.dense_problem(300, 40, seed=1, x="normal")
+    assert np.array_equal(d1.X, d2.X)
+
+
+def test_uniform_and_normal_moments():
+    u = datagen.uniform(1_000_000, 0, "u")
+    assert u.min() >= -1 and u.max() < 1 and abs(u.mean()) < 3e-3 and abs(u.var() - 1 / 3) < 3e-3
+    assert np.all(u * 2 ** 23 == np.round(u * 2 ** 23))        # 24-bit grid, exact in fp32
+    g = datagen.normal(1_000_000, 0, "g")
+    assert abs(g.mean()) < 5e-3 and abs(g.std() - 1) < 5e-3
+    assert abs(np.mean(g ** 4) - 3) < 0.05                         # Gaussian kurtosis
+
+
+def test_bernoulli_density_and_structure():
+    m, n, p = 200_000, 1000, 0.01
+    c = datagen.csr_bernoulli(m, n, p, seed=0)
+    total = m * n
+    sigma = np.sqrt(total * p * (1 - p))
+    assert abs(c.nnz - total * p) < 4 * sigma
+    rl = np.diff(c.row_ptr)
+    # row lengths ~ Binomial(1000, 0.01): mean 10, variance 9.9, P(empty) = 0.99^1000
+    assert abs(rl.mean() - 10) < 0.05 and abs(rl.var() - 9.9) < 0.3
+    assert abs((rl == 0).mean() - 0.99 ** 1000) < 4 * np.sqrt(0.99 ** 1000 / m)
+    # columns sorted and distinct within rows, in range, spread uniformly
+    rows = np.repeat(np.arange(m), rl)
+    key = rows.astype(np.int64) * n + c.col_idx
+    assert np.all(np.diff(key) > 0)
+    counts = np.bincount(c.col_idx, minlength=n)
+    assert counts.std() < 4 * np.sqrt(c.nnz / n)
+    # v = p(1 - p) lies in (0, 1/4]
+    assert c.v.min() > 0 and c.v.max() <= 0.25
+
+
+def test_zipf_rows_and_columns():
+    m, n = 200_000, 1_000_000
+    c = datagen.csr_zipf(m, n, seed=0)
+    rl = np.diff(c.row_ptr)
+    # truncated Zipf(1.5) on 1..2726: mean 40.003
+    k = np.arange(1, 2727, dtype=np.float64)
+    pk = k ** -1.5 / np.sum(k ** -1.5)
+    mean = float(np.sum(k * pk))
+    sd = float(np.sqrt(np.sum(k * k * pk) - mean ** 2))
+    assert abs(mean - 40.003) < 1e-3
+    assert abs(rl.mean() - mean) < 4 * sd / np.sqrt(m)
+    assert rl.min() >= 1 and rl.max() <= 2726
+    assert abs((rl == 1).mean() - pk[0]) < 4 * np.sqrt(pk[0] / m)
+    # columns distinct and sorted within each row
+    rows = np.repeat(np.arange(m), rl)
+    key = rows.astype(np.int64) * n + c.col_idx
+    assert np.all(np.diff(key) > 0)
+    # column popularity decays like rank^-1.2 in the tail where rows rarely saturate
+    counts = np.bincount(c.col_idx, minlength=n).astype(np.float64)
+    r = np.arange(1000, 100_000)
+    slope = np.polyfit(np.log(r + 1.0), np.log(counts[r] + 0.5), 1)[0]
+    assert abs(slope + 1.2) < 0.08, slope
+
+
+def test_zipf_permuted_columns_keep_the_structure():
+    a = datagen.csr_zipf(5000, 20000, seed=2)
+    b = datagen.csr_zipf(5000, 20000, seed=2, permute_columns=True)
+    assert np.array_equal(a.row_ptr, b.row_ptr)
+    assert a.col_idx.sum() != b.col_idx.sum()
+    ca = np.sort(np.bincount(a.col_idx, minlength=20000))
+    cb = np.sort(np.bincount(b.col_idx, minlength=20000))
+    assert np.array_equal(ca, cb)          # same popularity profile, relabelled columns
+
+
+def test_dense_padding_is_nan():
+    p = datagen.dense_problem(4, 3, seed=0, ldx=5)
+    X = p.X.reshape(4, 5)
+    assert np.all(np.isnan(X[:, 3:])) and np.all(np.isfinite(X[:, :3]))

@@ -1,0 +1,83 @@
+"""Plants plausible mistakes in copies of the oracle and checks that the pins catch each one.
+
+Every mutant is the oracle source with one textual change (a dropped term, a
+wrong sign, a wrong or transposed index, an ignored argument), compiled with
+g++ into a temporary library. The pins of oracle_checks.py must fail on every
+mutant; a mutant that survives means a mistake of that kind would go unnoticed.
+"""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+import oracle
+from oracle_checks import CHECKS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "oracle.cpp")
+
+# (name, original text, replacement, which occurrence of the original text)
+MUTATIONS = [
+    ("dense_drops_v", "const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);",
+     "const double vi = 1.0;", 0),
+    ("csr_drops_v", "const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);",
+     "const double vi = 1.0;", 1),
+    ("beta_term_sign", "if (beta != 0.0f) r += val((double)beta, absolute)",
+     "if (beta != 0.0f) r -= val((double)beta, absolute)", 0),
+    ("beta_not_applied", "r += val((double)beta, absolute) * val((double)z[j], absolute);",
+     "r += val((double)z[j], absolute);", 0),
+    ("alpha_dropped", "double r = val((double)alpha, absolute) * S[j];", "double r = S[j];", 0),
+    ("dense_dot_drops_last_term", "for (int64_t k = 0; k < n; ++k) t +=",
+     "for (int64_t k = 0; k + 1 < n; ++k) t +=", 0),
+    ("dense_dot_wrong_y_index", "val((double)row[k], absolute) * val((double)y[k], absolute)",
+     "val((double)row[k], absolute) * val((double)y[n - 1 - k], absolute)", 0),
+    ("dense_transpose_wrong_column", "S[(size_t)j] += val((double)row[j], absolute) * ui;",
+     "S[(size_t)j] += val((double)row[n - 1 - j], absolute) * ui;", 0),
+    ("dense_step1_ignores_ldx", "const float* row = X + i * ldx;", "const float* row = X + i * n;", 0),
+    ("dense_step3_ignores_ldx", "const float* row = X + i * ldx;", "const float* row = X + i * n;", 1),
+    ("csr_gathers_y_by_row", "val((double)y[col_idx[p]], absolute)", "val((double)y[i % n], absolute)", 0),
+    ("csr_scatters_by_row", "S[(size_t)col_idx[p]] +=", "S[(size_t)(i % n)] +=", 0),
+    ("csr_drops_repeated_column",
+     "t += val((double)values[p], absolute) * val((double)y[col_idx[p]], absolute);",
+     "if (p == row_ptr[i] || col_idx[p] != col_idx[p - 1]) "
+     "t += val((double)values[p], absolute) * val((double)y[col_idx[p]], absolute);", 0),
+    ("csr_skips_first_entry", "for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)",
+     "for (int64_t p = row_ptr[i] + 1; p < row_ptr[i + 1]; ++p)", 0),
+    ("quick_return_ignores_beta", "(beta == 0.0f) ? 0.0 : val((double)beta, absolute) * val((double)z[j], absolute)",
+     "(beta == 0.0f) ? 0.0 : val((double)z[j], absolute)", 0),
+    ("bound_keeps_signs", "return absolute ? std::fabs(x) : x;", "return x;", 0),
+]
+
+
+def _mutate(src: str, old: str, new: str, occurrence: int) -> str:
+    pos = -1
+    for _ in range(occurrence + 1):
+        pos = src.find(old, pos + 1)
+        assert pos >= 0, "mutation target not found: %r (occurrence %d)" % (old, occurrence)
+    return src[:pos] + new + src[pos + len(old):]
+
+
+@pytest.fixture(scope="module")
+def mutants(tmp_path_factory):
+    src = open(SRC).read()
+    d = tmp_path_factory.mktemp("oracle_mutants")
+
+    def build(mut):
+        name, old, new, occ = mut
+        path = d / (name + ".cpp")
+        path.write_text(_mutate(src, old, new, occ))
+        return name, oracle.compile_source(str(path), str(d / ("lib" + name + ".so")))
+
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        return dict(ex.map(build, MUTATIONS))
+
+
+@pytest.mark.parametrize("mutation", [m[0] for m in MUTATIONS])
+def test_pins_catch_mutant(mutants, mutation):
+    lib = oracle._bind(mutants[mutation])
+    caught = []
+    for check in CHECKS:
+        try:
+            check(lib)
+        except (AssertionError, oracle.OracleError) as e:
+            caught.append(check.__name__)
+    assert caught, "mutant %s passes every pin" % mutation
