@@ -1,0 +1,274 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused out = alpha * X^T (v .* (X y)) + beta * z on one GPU.
+
+One step is one call of the fused path (main fused kernel + aggregation) on a
+batch of synthetic input already resident in HBM. Default workload: dense
+1,000,000 x 256 fp32 X ~ N(0, 1), v absent (= 1), beta = 0 — the
+normal-equations instance X^T X y. Prints one JSON line with:
+  value            effective GB/s = algorithmic bytes per step / wall time per step
+  roofline         the main fused kernel's algorithmic bytes / its mean duration
+                   (HIP events recorded around it on the call's stream) vs 8 TB/s
+  speedup_vs_unfused  wall time of the rocBLAS/rocSPARSE chain / fused wall time
+  cpu_baseline     the CPU oracle on the host cores (same algorithmic-bytes formula)
+Algorithmic bytes: every operand once — dense 4mn (X) + 4m (v, if given) + 4n (y)
++ 4n (z, if beta != 0) + 4n (out); CSR 8 nnz + 4(m + 1) + 4m (v) + 4n (y) + 4n (z)
++ 4n (out).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused X^T(v⊙Xy) effective GB/s, % of HBM peak, speedup vs unfused GEMV"
+DEFAULT_WORKLOAD = "dense_1000000x256_normal_equations"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
+
+
+def algorithmic_bytes(p) -> int:
+    if hasattr(p, "col_idx"):
+        b = 8 * p.nnz + 4 * (p.m + 1) + 4 * p.n + 4 * p.n
+        b += 4 * p.m if p.v is not None else 0
+    else:
+        b = 4 * p.m * p.n + 4 * p.n + 4 * p.n
+        b += 4 * p.m if p.v is not None else 0
+    b += 4 * p.n if p.beta != 0 else 0
+    return b
+
+
+class HipEvents:
+    """hipEvent_t pairs from libamdhip64 (the events the library records around its main kernel)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.hip.hipEventSynchronize(b) != 0 or self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def kernel_sources_hash(kind: str) -> str:
+    csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
+    files = ["device_util.h", "internal.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_name(plan, kind: str) -> str:
+    import dense_linear_algebra_alpha_amd as xt
+    names = {xt.XTVXY_DENSE_WAVE_ROWS: "dense_wave_rows", xt.XTVXY_DENSE_BLOCK_ROWS: "dense_block_rows",
+             xt.XTVXY_DENSE_GROUP_ROWS: "dense_block_rows(group)", xt.XTVXY_CSR_LDS_TILES: "csr_tiles(lds)",
+             xt.XTVXY_CSR_GLOBAL_TILES: "csr_tiles(global)"}
+    return names.get(plan.kernel, "kernel%d" % plan.kernel)
+
+
+def load_traffic(workload: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when it matches the source."""
+    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        c = json.load(f)
+    if c.get("kernel_source_sha256") != kernel_sources_hash(kind):
+        return None
+    fetch = c["fetch_kib_per_dispatch"] * 1024.0 * c.get("fetch_scale", 1.0)
+    write = c["write_kib_per_dispatch"] * 1024.0 * c.get("write_scale", 1.0)
+    return fetch + write
+
+
+def cpu_baseline(p, budget_s: float):
+    """The oracle, as it is, on the host cores: repeated runs of the full workload for ~budget_s."""
+    import oracle
+    threads = oracle.set_threads(len(os.sched_getaffinity(0)))
+    runs = []
+    t_end = time.perf_counter() + budget_s
+    while len(runs) < 3 or (time.perf_counter() < t_end and len(runs) < 200):
+        t0 = time.perf_counter()
+        if hasattr(p, "col_idx"):
+            oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+        else:
+            oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+        runs.append(time.perf_counter() - t0)
+    med = statistics.median(runs)
+    return {"value": round(algorithmic_bytes(p) / med / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "the full workload, %d runs (median %.3f s each)" % (len(runs), med)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle runs for cpu_baseline")
+    ap.add_argument("--fused-only", action="store_true", help="time the fused path only (for profilers)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the fused path is a single-GPU kernel here "
+              "(row sharding with one reduce-scatter is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import dense_linear_algebra_alpha_amd as xt
+
+    xt.load()  # fails loudly when the HIP library is not built
+    if args.workload not in datagen.WORKLOADS:
+        raise SystemExit("unknown workload %s (known: %s)" % (args.workload, ", ".join(datagen.WORKLOADS)))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    p = datagen.WORKLOADS[args.workload](seed=args.seed)
+    kind = "csr" if hasattr(p, "col_idx") else "dense"
+
+    def t(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    y, v, z = t(p.y), t(p.v), t(p.z)
+    out = torch.empty(p.n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream or None
+    if kind == "dense":
+        X = t(p.X)
+        plan = xt.xtvxy_dense_f32_plan(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
+        ws_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
+        uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev)
+
+        def fused():
+            xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                               xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+
+        def unfused():
+            xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(),
+                                                 p.beta, xt._ptr(z), out.data_ptr(), uws.data_ptr(), uws_bytes, sh)
+        shape = {"m": p.m, "n": p.n, "ldx": p.ldx}
+    else:
+        rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
+        plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
+        ws_bytes = xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        uplan = None
+
+        def fused():
+            xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), xt._ptr(v),
+                             y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+
+        def unfused():
+            xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                                               out.data_ptr(), sh)
+        if not args.no_unfused and not args.fused_only:
+            uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)  # structure analysis: outside every timed region
+        shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
+
+    abytes = algorithmic_bytes(p)
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def timed(fn, with_kernel_events):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            if with_kernel_events:
+                xt.xtvxy_set_kernel_timing_events(pairs[i][0], pairs[i][1])
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        xt.xtvxy_set_kernel_timing_events(None, None)
+        kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs] if with_kernel_events else None
+        return (t1 - t0) / args.steps, kernel_ms
+
+    step_s, kernel_ms = timed(fused, True)
+    fused_out = out.cpu().numpy()
+    unfused_s = None
+    if not args.no_unfused and not args.fused_only:
+        unfused_s, _ = timed(unfused, False)
+        unfused_out = out.cpu().numpy()
+
+    kernel_s = statistics.mean(kernel_ms) / 1e3
+    achieved = abytes / kernel_s / 1e9
+    record = {
+        "metric": METRIC,
+        "value": round(abytes / step_s / 1e9, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators, seed %d)" % args.seed,
+        "config": dict({"workload": args.workload, "algorithmic_bytes": abytes,
+                        "plan": {k: v_ for k, v_ in plan.as_dict().items() if k != "predicted_seconds"}},
+                       **shape),
+        "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(plan, kind), "achieved": round(achieved, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(args.workload, kind),
+                     "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
+                     "kernel_ms_min": round(min(kernel_ms), 5)},
+    }
+    if unfused_s is not None:
+        record["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
+        record["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
+
+    # parity of the timed outputs against the oracle (max elementwise error relative to the bound)
+    if not args.fused_only:
+        import oracle
+        if kind == "dense":
+            ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+            bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
+        else:
+            ref = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+            bnd = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
+        den = np.where(bnd > 0, bnd, 1.0)
+        record["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
+        if unfused_s is not None:
+            record["unfused_max_rel_err"] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
+        if not args.no_cpu_baseline:
+            record["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,318 @@
+"""Python binding of the xtvxy C ABI (include/xtvxy.h).
+
+Evaluates out = alpha * X^T (v .* (X y)) + beta * z — the generic pattern of
+"On optimizing machine learning workloads via kernel fusion" (abstract) — for
+dense row-major or CSR fp32 X on an AMD gfx950 GPU, in one fused pass of
+hand-written HIP kernels (libxtvxy.so), or through the operator-level library
+comparator.
+
+Two layers, both argument marshalling only:
+  * ``xtvxy_*`` functions with the C names and argument lists (device pointers
+    as ints, the stream as an int handle);
+  * tensor helpers (``dense``, ``csr``, ``dense_unfused``, ``CsrUnfusedPlan``)
+    that take torch CUDA tensors, allocate the workspace with torch, and call
+    the C entry points on the current torch stream.
+Every computation happens in the library's kernels; a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _abi
+from ._abi import (XTVXY_CSR_GLOBAL_TILES, XTVXY_CSR_LDS_TILES, XTVXY_DENSE_BLOCK_ROWS,  # noqa: F401
+                   XTVXY_DENSE_GROUP_ROWS, XTVXY_DENSE_WAVE_ROWS, XtvxyError, xtvxy_device_info,
+                   xtvxy_launch_params)
+
+__all__ = [
+    "xtvxy_get_device_info", "xtvxy_dense_f32_plan", "xtvxy_dense_f32_plan_complete", "xtvxy_csr_f32_plan",
+    "xtvxy_csr_f32_plan_complete", "xtvxy_dense_f32_workspace_size", "xtvxy_dense_f32", "xtvxy_dense_f32_ex",
+    "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
+    "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
+    "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
+    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
+    "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
+]
+
+load = _abi.load
+
+
+# ---------------------------------------------------------------------------
+# C names
+# ---------------------------------------------------------------------------
+
+def xtvxy_status_string(status: int) -> str:
+    return _abi.status_string(status)
+
+
+def xtvxy_set_kernel_timing_events(before_main, after_main):
+    return _abi.call("xtvxy_set_kernel_timing_events", before_main, after_main)
+
+
+def xtvxy_get_device_info(device: int = -1) -> xtvxy_device_info:
+    info = xtvxy_device_info()
+    _abi.call("xtvxy_get_device_info", device, ctypes.byref(info))
+    return info
+
+
+def xtvxy_dense_f32_plan(m, n, ldx, X_aligned16=1, dev=None) -> xtvxy_launch_params:
+    p = xtvxy_launch_params()
+    _abi.call("xtvxy_dense_f32_plan", m, n, ldx, int(X_aligned16), ctypes.byref(dev) if dev else None,
+              ctypes.byref(p))
+    return p
+
+
+def xtvxy_dense_f32_plan_complete(m, n, ldx, plan: xtvxy_launch_params, dev=None) -> xtvxy_launch_params:
+    _abi.call("xtvxy_dense_f32_plan_complete", m, n, ldx, ctypes.byref(dev) if dev else None, ctypes.byref(plan))
+    return plan
+
+
+def xtvxy_csr_f32_plan(m, n, nnz, dev=None) -> xtvxy_launch_params:
+    p = xtvxy_launch_params()
+    _abi.call("xtvxy_csr_f32_plan", m, n, nnz, ctypes.byref(dev) if dev else None, ctypes.byref(p))
+    return p
+
+
+def xtvxy_csr_f32_plan_complete(m, n, nnz, plan: xtvxy_launch_params, dev=None) -> xtvxy_launch_params:
+    _abi.call("xtvxy_csr_f32_plan_complete", m, n, nnz, ctypes.byref(dev) if dev else None, ctypes.byref(plan))
+    return plan
+
+
+def xtvxy_dense_f32_workspace_size(m, n, ldx) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_dense_f32_workspace_size", m, n, ldx, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_csr_f32_workspace_size(m, n, nnz) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_csr_f32_workspace_size", m, n, nnz, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_dense_f32_unfused_reference_workspace_size(m, n) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_dense_f32_unfused_reference_workspace_size", m, n, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_dense_f32(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream):
+    return _abi.call("xtvxy_dense_f32", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream)
+
+
+def xtvxy_dense_f32_ex(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force):
+    return _abi.call("xtvxy_dense_f32_ex", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_f32(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                  stream):
+    return _abi.call("xtvxy_csr_f32", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_f32_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream, force):
+    return _abi.call("xtvxy_csr_f32_ex", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out,
+                     workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_check(m, n, nnz, row_ptr, col_idx, d_flag, stream):
+    return _abi.call("xtvxy_csr_check", m, n, nnz, row_ptr, col_idx, d_flag, stream)
+
+
+def xtvxy_dense_f32_unfused_reference(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                                      stream):
+    return _abi.call("xtvxy_dense_f32_unfused_reference", m, n, alpha, X, ldx, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_f32_unfused_plan_create(m, n, nnz, row_ptr, col_idx, values, stream) -> int:
+    h = ctypes.c_void_p()
+    _abi.call("xtvxy_csr_f32_unfused_plan_create", m, n, nnz, row_ptr, col_idx, values, stream, ctypes.byref(h))
+    return h.value or 0
+
+
+def xtvxy_csr_f32_unfused_plan_destroy(plan: int):
+    return _abi.call("xtvxy_csr_f32_unfused_plan_destroy", plan)
+
+
+def xtvxy_csr_f32_unfused_reference(plan, alpha, v, y, beta, z, out, stream):
+    return _abi.call("xtvxy_csr_f32_unfused_reference", plan, alpha, v, y, beta, z, out, stream)
+
+
+# ---------------------------------------------------------------------------
+# torch tensor helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _check_vec(name, t, length, device, required=True):
+    torch = _torch()
+    if t is None:
+        if required:
+            raise ValueError("%s is required" % name)
+        return
+    if t.dtype != torch.float32 or t.device != device or t.numel() != length or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous float32 tensor of %d elements on %s" % (name, length, device))
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def dense_plan(m, n, ldx=None, aligned=True, dev=None) -> xtvxy_launch_params:
+    return xtvxy_dense_f32_plan(m, n, n if ldx is None else ldx, 1 if aligned else 0, dev)
+
+
+def csr_plan(m, n, nnz, dev=None) -> xtvxy_launch_params:
+    return xtvxy_csr_f32_plan(m, n, nnz, dev)
+
+
+def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None, ldx=None, plan=None,
+          workspace=None, stream=None):
+    """out = alpha X^T (v .* (X y)) + beta z for dense row-major X on the GPU.
+
+    X is a 2-D float32 CUDA tensor with unit column stride (row stride = ldx), or a
+    flat buffer with m, n and ldx given. ``plan`` forces launch parameters."""
+    torch = _torch()
+    if X.dim() == 2 and m is None:
+        m, n = X.shape
+        if X.stride(1) != 1 and n > 1:
+            raise ValueError("X needs unit column stride")
+        ldx = X.stride(0) if m > 1 else max(n, 1)
+        ldx = max(ldx, n, 1)
+    if m is None or n is None or ldx is None:
+        raise ValueError("flat X needs m, n and ldx")
+    if X.dtype != torch.float32:
+        raise ValueError("X must be float32")
+    device = X.device
+    _check_vec("y", y, n, device)
+    _check_vec("v", v, m, device, required=False)
+    _check_vec("z", z, n, device, required=beta != 0)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    _check_vec("out", out, n, device)
+    if plan is None:
+        need = xtvxy_dense_f32_workspace_size(m, n, ldx)
+    else:
+        need = int(plan.workspace_bytes)
+    if workspace is None:
+        workspace = _workspace(need, device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    args = (m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(),
+            ws_ptr, ws_bytes, _stream_handle(stream))
+    if plan is None:
+        xtvxy_dense_f32(*args)
+    else:
+        xtvxy_dense_f32_ex(*args, plan)
+    return out
+
+
+def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None,
+        workspace=None, stream=None):
+    """The same pattern for CSR X given as int32 row_ptr / col_idx and float32 values tensors."""
+    torch = _torch()
+    m = row_ptr.numel() - 1
+    nnz = col_idx.numel()
+    device = row_ptr.device
+    for name, t, dt in (("row_ptr", row_ptr, torch.int32), ("col_idx", col_idx, torch.int32),
+                        ("values", values, torch.float32)):
+        if t.dtype != dt or t.device != device or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s tensor on %s" % (name, dt, device))
+    if values.numel() != nnz:
+        raise ValueError("values and col_idx differ in length")
+    _check_vec("y", y, n, device)
+    _check_vec("v", v, m, device, required=False)
+    _check_vec("z", z, n, device, required=beta != 0)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    _check_vec("out", out, n, device)
+    need = xtvxy_csr_f32_workspace_size(m, n, nnz) if plan is None else int(plan.workspace_bytes)
+    if workspace is None:
+        workspace = _workspace(need, device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
+            _ptr(values) if nnz else None, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(), ws_ptr,
+            ws_bytes, _stream_handle(stream))
+    if plan is None:
+        xtvxy_csr_f32(*args)
+    else:
+        xtvxy_csr_f32_ex(*args, plan)
+    return out
+
+
+def csr_check(row_ptr, col_idx, n, stream=None) -> int:
+    """Device-side structure check; returns 0 for a well-formed matrix (synchronizes)."""
+    torch = _torch()
+    flag = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
+    xtvxy_csr_check(row_ptr.numel() - 1, n, col_idx.numel(), row_ptr.data_ptr(),
+                    col_idx.data_ptr() if col_idx.numel() else None, flag.data_ptr(), _stream_handle(stream))
+    return int(flag.item())
+
+
+def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, workspace=None, stream=None):
+    """The comparator: rocBLAS sgemv, elementwise scale, rocBLAS sgemv."""
+    torch = _torch()
+    m, n = X.shape
+    ldx = max(X.stride(0) if m > 1 else n, n, 1)
+    device = X.device
+    _check_vec("y", y, n, device)
+    _check_vec("v", v, m, device, required=False)
+    _check_vec("z", z, n, device, required=beta != 0)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    if workspace is None:
+        workspace = _workspace(xtvxy_dense_f32_unfused_reference_workspace_size(m, n), device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    xtvxy_dense_f32_unfused_reference(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta),
+                                      _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
+    return out
+
+
+class CsrUnfusedPlan:
+    """rocSPARSE descriptors and analysis for one CSR matrix (the comparator's setup)."""
+
+    def __init__(self, row_ptr, col_idx, values, n, stream=None):
+        self.m = row_ptr.numel() - 1
+        self.n = n
+        self.nnz = col_idx.numel()
+        self._keep = (row_ptr, col_idx, values)
+        self.handle = xtvxy_csr_f32_unfused_plan_create(
+            self.m, n, self.nnz, row_ptr.data_ptr(), col_idx.data_ptr() if self.nnz else None,
+            values.data_ptr() if self.nnz else None, _stream_handle(stream))
+
+    def __call__(self, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, stream=None):
+        torch = _torch()
+        if out is None:
+            out = torch.empty(self.n, dtype=torch.float32, device=y.device)
+        xtvxy_csr_f32_unfused_reference(self.handle, float(alpha), _ptr(v), y.data_ptr(), float(beta), _ptr(z),
+                                        out.data_ptr(), _stream_handle(stream))
+        return out
+
+    def close(self):
+        if self.handle:
+            xtvxy_csr_f32_unfused_plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,113 @@
+"""ctypes declarations of the C ABI in include/xtvxy.h (argument marshalling only).
+
+Every function here has the name and the argument list of its C counterpart;
+pointers are passed as Python ints (device addresses) and a nonzero status
+raises XtvxyError. The library must have been built (``build.py``); there is no
+fallback of any kind when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+XTVXY_SUCCESS = 0
+XTVXY_ERROR_INVALID_VALUE = 1
+XTVXY_ERROR_NULL_POINTER = 2
+XTVXY_ERROR_ALIASING = 3
+XTVXY_ERROR_WORKSPACE = 4
+XTVXY_ERROR_UNSUPPORTED = 5
+XTVXY_ERROR_LAUNCH = 6
+XTVXY_ERROR_LIBRARY = 7
+
+XTVXY_DENSE_WAVE_ROWS = 1
+XTVXY_DENSE_BLOCK_ROWS = 2
+XTVXY_DENSE_GROUP_ROWS = 3
+XTVXY_CSR_LDS_TILES = 11
+XTVXY_CSR_GLOBAL_TILES = 12
+
+
+class xtvxy_device_info(ctypes.Structure):
+    _fields_ = [("compute_units", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("l2_bytes", ctypes.c_int32), ("xcds", ctypes.c_int32),
+                ("hbm_bytes_per_s", ctypes.c_double)]
+
+
+class xtvxy_launch_params(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("vec", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("lanes_per_row", ctypes.c_int32), ("chunks", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("rows_per_unit", ctypes.c_int64),
+                ("entries_per_thread", ctypes.c_int32), ("lds_window", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_int64), ("predicted_seconds", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class XtvxyError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = int(status)
+        name = _lib.xtvxy_status_string(self.status).decode() if _lib is not None else str(status)
+        super().__init__("%s returned %s" % (where or "xtvxy", name))
+
+
+_i64, _f32, _vp, _sz, _i32 = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+_P = ctypes.POINTER
+
+# name -> argument types (all return xtvxy_status, an int)
+SIGNATURES = {
+    "xtvxy_get_device_info": [_i32, _P(xtvxy_device_info)],
+    "xtvxy_dense_f32_plan": [_i64, _i64, _i64, _i32, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_dense_f32_plan_complete": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_plan": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_plan_complete": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_dense_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
+    "xtvxy_dense_f32": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_dense_f32_ex": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                           _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
+    "xtvxy_csr_f32": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_f32_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                         _P(xtvxy_launch_params)],
+    "xtvxy_csr_check": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "xtvxy_dense_f32_unfused_reference_workspace_size": [_i64, _i64, _P(_sz)],
+    "xtvxy_dense_f32_unfused_reference": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_f32_unfused_plan_create": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _P(_vp)],
+    "xtvxy_csr_f32_unfused_plan_destroy": [_vp],
+    "xtvxy_csr_f32_unfused_reference": [_vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp],
+    "xtvxy_set_kernel_timing_events": [_vp, _vp],
+}
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libxtvxy.so and declare every exported entry point."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libxtvxy.so is not built (%s); run `python -m dense_linear_algebra_alpha_amd.build`"
+                           % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.xtvxy_status_string.argtypes = [_i32]
+    lib.xtvxy_status_string.restype = ctypes.c_char_p
+    for name, args in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def call(name: str, *args) -> int:
+    """Call entry point `name`; raise XtvxyError on a nonzero status."""
+    st = getattr(load(), name)(*args)
+    if st != XTVXY_SUCCESS:
+        raise XtvxyError(st, name)
+    return st
+
+
+def status_string(status: int) -> str:
+    return load().xtvxy_status_string(int(status)).decode()

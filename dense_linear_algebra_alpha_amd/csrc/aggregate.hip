@@ -1,0 +1,115 @@
+// Second level of the hierarchical aggregation ("On optimizing machine learning
+// workloads via kernel fusion", abstract: partial results are aggregated
+// hierarchically) and the small helper kernels of the library.
+//
+// aggregate: out_j = alpha * S_j + beta * z_j with S_j the sum of the fused
+// kernel's per-workgroup partials. Each 1024-thread workgroup owns 64 columns;
+// 16 thread rows each sum a strided subset of the partials in fp64, and the 16
+// results are combined in a fixed order, so the result is bitwise reproducible.
+// The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
+// reads z; out may alias z (each element is read before it is written by the
+// same thread).
+#include "internal.h"
+
+namespace xtvxy {
+namespace {
+
+constexpr int kAggCols = 64, kAggRows = 16;
+
+__global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const float* __restrict__ partial,
+                                                                        int64_t rows, int64_t n, float alpha,
+                                                                        float beta, const float* z, float* out) {
+  __shared__ double sh[kAggRows][kAggCols];
+  const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
+  const int64_t j = (int64_t)blockIdx.x * kAggCols + tx;
+  double s = 0.0;
+  if (j < n) {
+#pragma unroll 8
+    for (int64_t r = ty; r < rows; r += kAggRows) s += (double)partial[r * n + j];
+  }
+  sh[ty][tx] = s;
+  __syncthreads();
+  if (ty == 0 && j < n) {
+    double t = sh[0][tx];
+#pragma unroll
+    for (int k = 1; k < kAggRows; ++k) t += sh[k][tx];
+    double o = (double)alpha * t;
+    if (beta != 0.0f) o += (double)beta * (double)z[j];
+    out[j] = (float)o;
+  }
+}
+
+__global__ void beta_only_kernel(int64_t n, float beta, const float* z, float* out) {
+  for (int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; j < n; j += (int64_t)gridDim.x * blockDim.x)
+    out[j] = (beta != 0.0f) ? beta * z[j] : 0.0f;
+}
+
+__global__ void zero_kernel(uint32_t* p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+__global__ void scale_kernel(int64_t m, const float* __restrict__ v, float* t) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m; i += (int64_t)gridDim.x * blockDim.x)
+    t[i] = v[i] * t[i];
+}
+
+// flag: 0 ok, 1 row_ptr ends wrong, 2 row_ptr decreases, 3 column out of range (largest code wins)
+__global__ void csr_check_kernel(int64_t m, int64_t n, int64_t nnz, const int32_t* __restrict__ rp,
+                                 const int32_t* __restrict__ ci, int32_t* flag) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid == 0 && (rp[0] != 0 || (int64_t)rp[m] != nnz)) atomicMax(flag, 1);
+  for (int64_t i = tid; i < m; i += stride)
+    if (rp[i + 1] < rp[i]) atomicMax(flag, 2);
+  for (int64_t p = tid; p < nnz; p += stride)
+    if (ci[p] < 0 || (int64_t)ci[p] >= n) atomicMax(flag, 3);
+}
+
+unsigned grid_for(int64_t count, int block) {
+  int64_t g = (count + block - 1) / block;
+  if (g < 1) g = 1;
+  if (g > 65536) g = 65536;
+  return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t n, float alpha, float beta,
+                            const float* z, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)((n + kAggCols - 1) / kAggCols);
+  hipLaunchKernelGGL(aggregate_kernel, dim3(grid), dim3(kAggCols * kAggRows), 0, s, partial, rows, n, alpha,
+                     beta, z, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(beta_only_kernel, dim3(grid_for(n, 256)), dim3(256), 0, s, n, beta, z, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const int64_t words = (int64_t)(bytes / 4);
+  if (words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(words, 256)), dim3(256), 0, s, static_cast<uint32_t*>(p), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_scale(int64_t m, const float* v, float* t, hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scale_kernel, dim3(grid_for(m, 256)), dim3(256), 0, s, m, v, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                            int32_t* flag, hipStream_t s) {
+  hipError_t e = launch_zero(flag, sizeof(int32_t), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(csr_check_kernel, dim3(grid_for(m > nnz ? m : nnz, 256)), dim3(256), 0, s, m, n, nnz,
+                     row_ptr, col_idx, flag);
+  return hipGetLastError();
+}
+
+}  // namespace xtvxy

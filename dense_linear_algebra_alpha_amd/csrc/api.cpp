@@ -1,0 +1,412 @@
+// C ABI of the xtvxy library: argument checks, BLAS-style quick returns, launch
+// plans and kernel dispatch for the fused entry points declared in xtvxy.h.
+// Every argument error is detected here, on the host, before anything is
+// enqueued on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "internal.h"
+
+using namespace xtvxy;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_info_mutex;
+bool g_info_valid[kMaxDevices];
+xtvxy_device_info g_info[kMaxDevices];
+
+xtvxy_status device_info(int device, xtvxy_device_info* out) {
+  if (device < 0) {
+    if (hipGetDevice(&device) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  }
+  if (device >= kMaxDevices) return XTVXY_ERROR_INVALID_VALUE;
+  std::lock_guard<std::mutex> lock(g_info_mutex);
+  if (!g_info_valid[device]) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, device) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+    xtvxy_device_info d{};
+    d.compute_units = prop.multiProcessorCount;
+    d.lds_bytes = (int32_t)prop.sharedMemPerBlock;
+    d.l2_bytes = prop.l2CacheSize;
+    // gfx94x/gfx95x parts group 32 (or 38/40) CUs per XCD; the count only steers tile placement
+    d.xcds = prop.multiProcessorCount >= 64 ? prop.multiProcessorCount / 32 : 1;
+    // memoryClockRate is in kHz; double data rate over a bus of memoryBusWidth bits
+    d.hbm_bytes_per_s = 2.0 * prop.memoryClockRate * 1e3 * (prop.memoryBusWidth / 8.0);
+    if (d.hbm_bytes_per_s <= 0) d.hbm_bytes_per_s = 8.0e12;
+    g_info[device] = d;
+    g_info_valid[device] = true;
+  }
+  *out = g_info[device];
+  return XTVXY_SUCCESS;
+}
+
+// [a, a + an) and [b, b + bn) (in bytes) overlap
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  if (!a || !b || an == 0 || bn == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + bn && y < x + an;
+}
+
+bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
+
+xtvxy_status launch_status(hipError_t e) { return e == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH; }
+
+// Measurement hook: events recorded around the main fused kernel of each call.
+hipEvent_t g_before_main = nullptr, g_after_main = nullptr;
+
+hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) : hipSuccess; }
+
+// Checks shared by the dense fused entry point and its comparator. Returns SUCCESS with
+// *quick set when nothing beyond out = beta z (or nothing at all) has to be computed.
+xtvxy_status check_dense(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                         const float* y, float beta, const float* z, const float* out, bool* quick) {
+  *quick = false;
+  if (m < 0 || n < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  if (mul_overflows(m, ldx) || m * ldx > INT64_MAX / 8) return XTVXY_ERROR_INVALID_VALUE;
+  if (n == 0) {
+    *quick = true;
+    return XTVXY_SUCCESS;
+  }
+  if (!out || !y) return XTVXY_ERROR_NULL_POINTER;
+  if (beta != 0.0f && !z) return XTVXY_ERROR_NULL_POINTER;
+  const bool reads_x = alpha != 0.0f && m > 0;
+  if (reads_x && !X) return XTVXY_ERROR_NULL_POINTER;
+  const size_t nb = (size_t)n * sizeof(float);
+  if (reads_x) {
+    const size_t xb = ((size_t)(m - 1) * ldx + n) * sizeof(float);
+    if (overlap(out, nb, X, xb) || overlap(out, nb, y, nb) || (v && overlap(out, nb, v, (size_t)m * sizeof(float))))
+      return XTVXY_ERROR_ALIASING;
+  }
+  if (beta != 0.0f && z != out && overlap(out, nb, z, nb)) return XTVXY_ERROR_ALIASING;
+  if (!reads_x) *quick = true;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status check_csr(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                       const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                       const float* z, const float* out, bool* quick) {
+  *quick = false;
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (nnz > INT32_MAX || m >= INT32_MAX || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (n == 0) {
+    *quick = true;
+    return XTVXY_SUCCESS;
+  }
+  if (!out || !y) return XTVXY_ERROR_NULL_POINTER;
+  if (beta != 0.0f && !z) return XTVXY_ERROR_NULL_POINTER;
+  const bool reads_x = alpha != 0.0f && m > 0 && nnz > 0;
+  if (reads_x && (!row_ptr || !col_idx || !values)) return XTVXY_ERROR_NULL_POINTER;
+  const size_t nb = (size_t)n * sizeof(float);
+  if (reads_x) {
+    if (overlap(out, nb, row_ptr, (size_t)(m + 1) * 4) || overlap(out, nb, col_idx, (size_t)nnz * 4) ||
+        overlap(out, nb, values, (size_t)nnz * 4) || overlap(out, nb, y, nb) ||
+        (v && overlap(out, nb, v, (size_t)m * sizeof(float))))
+      return XTVXY_ERROR_ALIASING;
+  }
+  if (beta != 0.0f && z != out && overlap(out, nb, z, nb)) return XTVXY_ERROR_ALIASING;
+  if (!reads_x) *quick = true;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status dense_plan_for(int64_t m, int64_t n, int64_t ldx, bool aligned, const xtvxy_device_info& d,
+                            const xtvxy_launch_params* force, xtvxy_launch_params* plan) {
+  if (force) {
+    *plan = *force;
+    xtvxy_status st = complete_dense(m, n, ldx, d, plan);
+    if (st != XTVXY_SUCCESS) return st;
+    if (plan->vec == 4 && (!aligned || ldx % 4 != 0)) return XTVXY_ERROR_INVALID_VALUE;
+    return XTVXY_SUCCESS;
+  }
+  return model_dense(m, n, ldx, aligned, d, plan);
+}
+
+xtvxy_status csr_plan_for(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
+                          const xtvxy_launch_params* force, xtvxy_launch_params* plan) {
+  if (force) {
+    *plan = *force;
+    return complete_csr(m, n, nnz, d, plan);
+  }
+  return model_csr(m, n, nnz, d, plan);
+}
+
+// The co-resident limit of the cooperative group-row kernel is only known on the device:
+// shrink the grid to it (whole groups) and recompute the coarsening.
+xtvxy_status fit_group_grid(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
+                            xtvxy_launch_params* plan, bool forced) {
+  if (plan->kernel != XTVXY_DENSE_GROUP_ROWS) return XTVXY_SUCCESS;
+  const int64_t cap = dense_group_max_resident(*plan) / plan->group * plan->group;
+  if (cap < plan->group) return XTVXY_ERROR_LAUNCH;
+  if (plan->grid > cap) {
+    if (forced) return XTVXY_ERROR_INVALID_VALUE;
+    plan->grid = cap;
+    plan->rows_per_unit = 0;
+    return complete_dense(m, n, ldx, d, plan);
+  }
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                        const float* y, float beta, const float* z, float* out, void* ws, size_t ws_bytes,
+                        hipStream_t stream, const xtvxy_launch_params* force) {
+  bool quick = false;
+  xtvxy_status st = check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, &quick);
+  if (st != XTVXY_SUCCESS) return st;
+  if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
+  xtvxy_device_info d;
+  st = device_info(-1, &d);
+  if (st != XTVXY_SUCCESS) return st;
+  const bool aligned = (reinterpret_cast<uintptr_t>(X) % 16) == 0;
+  xtvxy_launch_params plan;
+  st = dense_plan_for(m, n, ldx, aligned, d, force, &plan);
+  if (st != XTVXY_SUCCESS) return st;
+  st = fit_group_grid(m, n, ldx, d, &plan, force != nullptr);
+  if (st != XTVXY_SUCCESS) return st;
+  if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
+
+  const DenseWorkspace w = dense_workspace(n, plan);
+  char* base = static_cast<char*>(ws);
+  DenseArgs a{};
+  a.m = m;
+  a.n = n;
+  a.ldx = ldx;
+  a.X = X;
+  a.v = v;
+  a.y = y;
+  a.partial = reinterpret_cast<float*>(base + w.partial_off);
+  a.rows_per_unit = plan.rows_per_unit;
+  a.lanes_per_row = plan.lanes_per_row;
+  a.group = plan.group;
+  if (plan.kernel == XTVXY_DENSE_GROUP_ROWS) {
+    a.xchg = reinterpret_cast<float*>(base + w.xchg_off);
+    a.counters = reinterpret_cast<uint32_t*>(base + w.counters_off);
+    a.error = reinterpret_cast<uint32_t*>(base + w.error_off);
+    hipError_t e = launch_zero(base + w.counters_off, w.total - w.counters_off, stream);
+    if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  }
+  const hipEvent_t before = g_before_main, after = g_after_main;
+  if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  hipError_t e = launch_dense(a, plan, stream);
+  if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, alpha, beta, z, out, stream);
+  return launch_status(e);
+}
+
+xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                      const xtvxy_launch_params* force) {
+  bool quick = false;
+  xtvxy_status st = check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick);
+  if (st != XTVXY_SUCCESS) return st;
+  if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
+  xtvxy_device_info d;
+  st = device_info(-1, &d);
+  if (st != XTVXY_SUCCESS) return st;
+  xtvxy_launch_params plan;
+  st = csr_plan_for(m, n, nnz, d, force, &plan);
+  if (st != XTVXY_SUCCESS) return st;
+  if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
+  const CsrWorkspace w = csr_workspace(n, plan);
+  CsrArgs a{};
+  a.m = m;
+  a.n = n;
+  a.nnz = nnz;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.values = values;
+  a.v = v;
+  a.y = y;
+  a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + w.partial_off);
+  a.entries_per_thread = plan.entries_per_thread;
+  a.lds_window = plan.lds_window;
+  hipError_t e;
+  if (plan.kernel == XTVXY_CSR_GLOBAL_TILES) {
+    e = launch_zero(a.partial, (size_t)n * sizeof(float), stream);
+    if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  }
+  const hipEvent_t before = g_before_main, after = g_after_main;
+  if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  e = launch_csr(a, plan, stream);
+  if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, alpha, beta, z, out, stream);
+  return launch_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* xtvxy_status_string(xtvxy_status s) {
+  switch (s) {
+    case XTVXY_SUCCESS: return "XTVXY_SUCCESS";
+    case XTVXY_ERROR_INVALID_VALUE: return "XTVXY_ERROR_INVALID_VALUE";
+    case XTVXY_ERROR_NULL_POINTER: return "XTVXY_ERROR_NULL_POINTER";
+    case XTVXY_ERROR_ALIASING: return "XTVXY_ERROR_ALIASING";
+    case XTVXY_ERROR_WORKSPACE: return "XTVXY_ERROR_WORKSPACE";
+    case XTVXY_ERROR_UNSUPPORTED: return "XTVXY_ERROR_UNSUPPORTED";
+    case XTVXY_ERROR_LAUNCH: return "XTVXY_ERROR_LAUNCH";
+    case XTVXY_ERROR_LIBRARY: return "XTVXY_ERROR_LIBRARY";
+  }
+  return "XTVXY_UNKNOWN_STATUS";
+}
+
+xtvxy_status xtvxy_set_kernel_timing_events(hipEvent_t before_main, hipEvent_t after_main) {
+  if ((before_main == nullptr) != (after_main == nullptr)) return XTVXY_ERROR_NULL_POINTER;
+  g_before_main = before_main;
+  g_after_main = after_main;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_get_device_info(int device, xtvxy_device_info* info) {
+  if (!info) return XTVXY_ERROR_NULL_POINTER;
+  return device_info(device, info);
+}
+
+xtvxy_status xtvxy_dense_f32_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info* dev,
+                                  xtvxy_launch_params* plan) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  if (d.compute_units <= 0 || d.hbm_bytes_per_s <= 0) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_status st = model_dense(m, n, ldx, X_aligned16 != 0, d, plan);
+  if (st == XTVXY_SUCCESS && !dev) st = fit_group_grid(m, n, ldx, d, plan, false);
+  return st;
+}
+
+xtvxy_status xtvxy_dense_f32_plan_complete(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info* dev,
+                                           xtvxy_launch_params* plan) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  return complete_dense(m, n, ldx, d, plan);
+}
+
+xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info* dev,
+                                xtvxy_launch_params* plan) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (nnz > INT32_MAX || m >= INT32_MAX || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  if (d.compute_units <= 0 || d.hbm_bytes_per_s <= 0) return XTVXY_ERROR_INVALID_VALUE;
+  return model_csr(m, n, nnz, d, plan);
+}
+
+xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info* dev,
+                                         xtvxy_launch_params* plan) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  return complete_csr(m, n, nnz, d, plan);
+}
+
+xtvxy_status xtvxy_dense_f32_workspace_size(int64_t m, int64_t n, int64_t ldx, size_t* bytes) {
+  if (!bytes) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  *bytes = 0;
+  if (m == 0 || n == 0) return XTVXY_SUCCESS;
+  size_t best = 0;
+  for (int aligned = 0; aligned < 2; ++aligned) {
+    xtvxy_launch_params p;
+    xtvxy_status st = xtvxy_dense_f32_plan(m, n, ldx, aligned, nullptr, &p);
+    if (st != XTVXY_SUCCESS) return st;
+    if ((size_t)p.workspace_bytes > best) best = (size_t)p.workspace_bytes;
+  }
+  *bytes = best;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_csr_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
+  if (!bytes) return XTVXY_ERROR_NULL_POINTER;
+  *bytes = 0;
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0 || nnz == 0) return XTVXY_SUCCESS;
+  xtvxy_launch_params p;
+  xtvxy_status st = xtvxy_csr_f32_plan(m, n, nnz, nullptr, &p);
+  if (st != XTVXY_SUCCESS) return st;
+  *bytes = (size_t)p.workspace_bytes;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_dense_f32(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                             const float* y, float beta, const float* z, float* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+xtvxy_status xtvxy_dense_f32_ex(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                                const float* y, float beta, const float* z, float* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force);
+}
+
+xtvxy_status xtvxy_csr_f32(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                           const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                           const float* z, float* out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                  stream, nullptr);
+}
+
+xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                              const int32_t* col_idx, const float* values, const float* v, const float* y,
+                              float beta, const float* z, float* out, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const xtvxy_launch_params* force) {
+  return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                  stream, force);
+}
+
+xtvxy_status xtvxy_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                             int32_t* d_flag, hipStream_t stream) {
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (nnz > INT32_MAX || m >= INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (!row_ptr || !d_flag || (nnz > 0 && !col_idx)) return XTVXY_ERROR_NULL_POINTER;
+  return launch_status(launch_csr_check(m, n, nnz, row_ptr, col_idx, d_flag, stream));
+}
+
+}  // extern "C"
+
+// Shared with unfused.cpp: the dense argument checks.
+namespace xtvxy {
+xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                              const float* y, float beta, const float* z, const float* out, bool* quick) {
+  return check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, quick);
+}
+xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* values, const float* v, const float* y,
+                            float beta, const float* z, const float* out, bool* quick) {
+  return check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, quick);
+}
+}  // namespace xtvxy

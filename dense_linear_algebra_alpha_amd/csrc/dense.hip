@@ -1,0 +1,308 @@
+// Fused dense kernels for out = alpha * X^T (v .* (X y)) + beta * z.
+//
+// "On optimizing machine learning workloads via kernel fusion" (abstract):
+// the fused kernel loads each element of X once and uses it twice — for the
+// row dot product t_i = x_i . y and, after the scale u_i = v_i t_i, for the
+// accumulation of u_i x_i into the transposed product — and aggregates partial
+// results hierarchically. Here the two uses of a row happen while the row is
+// still in registers; each workgroup sums its rows into one partial n-vector
+// (registers -> LDS -> workspace), and aggregate.hip sums the workgroups'
+// partials and applies alpha and beta. Thread coarsening: a workgroup walks a
+// contiguous block of rows_per_unit rows.
+//
+// Three layouts of a row over the threads (chosen by the launch model):
+//   wave rows  (n <= 1024): `lanes_per_row` lanes of a wavefront share a row,
+//              each holding `chunks` pieces of `VEC` columns; a wavefront keeps
+//              several rows in flight and reduces each dot within its lanes.
+//   block rows (n <= 8192): the 256 threads of a workgroup share a row; the dot
+//              is reduced across the four wavefronts through LDS.
+//   group rows (wider):     `group` co-resident workgroups split a row into
+//              column slices; partial dots go through global memory and a
+//              per-group arrival counter (cooperative launch guarantees that the
+//              members are resident together).
+#include "device_util.h"
+#include "internal.h"
+
+namespace xtvxy {
+namespace {
+
+constexpr uint32_t kSpinLimit = 1u << 22;  // barrier waits give up (and flag an error) after this
+
+template <int VEC, int NCH, int UNR>
+__global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
+  constexpr int W = 64 * VEC * NCH;  // widest row a wavefront covers
+  __shared__ float red[kWaves][W];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lpr = a.lanes_per_row;
+  const int sub = lane & (lpr - 1);  // lane within its row group
+  const int slot = lane / lpr;       // row group within the wavefront
+  const int slots = 64 / lpr;
+  const int units = kWaves * slots;  // row groups per workgroup
+  const int unit = wave * slots + slot;
+  const int64_t n = a.n;
+  const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_unit;
+  const int64_t r1 = min(a.m, r0 + a.rows_per_unit);
+
+  float yv[NCH][VEC], acc[NCH][VEC];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const int64_t col = ((int64_t)c * lpr + sub) * VEC + k;
+      yv[c][k] = col < n ? a.y[col] : 0.0f;
+      acc[c][k] = 0.0f;
+    }
+
+  for (int64_t base = r0 + unit; base < r1; base += (int64_t)units * UNR) {
+    float xv[UNR][NCH][VEC];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t row = base + (int64_t)u * units;
+      if (row < r1) {
+        const float* xr = a.X + row * a.ldx;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) load_chunk<VEC>(xr, ((int64_t)c * lpr + sub) * VEC, n, xv[u][c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) xv[u][c][k] = 0.0f;
+      }
+    }
+    float s[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      s[u] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) s[u] = fmaf(xv[u][c][k], yv[c][k], s[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) s[u] = group_sum(s[u], lpr);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int64_t row = base + (int64_t)u * units;
+      float uu = 0.0f;
+      if (row < r1) uu = (a.v ? a.v[row] : 1.0f) * s[u];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[u][c][k], acc[c][k]);
+    }
+  }
+
+  // Row groups of a wavefront that own the same columns are combined by lane exchanges,
+  // the four wavefronts through LDS, in a fixed order.
+  for (int off = lpr; off < 64; off <<= 1)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) acc[c][k] += __shfl_xor(acc[c][k], off, 64);
+  if (slot == 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) red[wave][(c * lpr + sub) * VEC + k] = acc[c][k];
+  }
+  __syncthreads();
+  float* dst = a.partial + (int64_t)blockIdx.x * n;
+  for (int64_t j = threadIdx.x; j < n; j += kBlock) {
+    float t = red[0][j];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) t += red[w][j];
+    dst[j] = t;
+  }
+}
+
+template <int VEC, int NCH, bool GROUP>
+__global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
+  constexpr int R = kBlockRowsInFlight;
+  __shared__ float red[2][R][kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = a.n;
+  const int64_t gsz = GROUP ? a.group : 1;
+  const int64_t unit = GROUP ? blockIdx.x / gsz : blockIdx.x;
+  const int64_t member = GROUP ? blockIdx.x % gsz : 0;
+  const int64_t c0 = member * ((int64_t)kBlock * VEC * NCH);  // first column of this slice
+  const int64_t r0 = unit * a.rows_per_unit;
+  const int64_t r1 = min(a.m, r0 + a.rows_per_unit);
+
+  float yv[NCH][VEC], acc[NCH][VEC];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const int64_t col = c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC + k;
+      yv[c][k] = col < n ? a.y[col] : 0.0f;
+      acc[c][k] = 0.0f;
+    }
+
+  int parity = 0;
+  uint32_t step = 0;
+  for (int64_t base = r0; base < r1; base += R) {
+    float xv[R][NCH][VEC];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = base + r;
+      if (row < r1) {
+        const float* xr = a.X + row * a.ldx;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          load_chunk<VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, n, xv[r][c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) xv[r][c][k] = 0.0f;
+      }
+    }
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) s[r] = fmaf(xv[r][c][k], yv[c][k], s[r]);
+      s[r] = group_sum(s[r], 64);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) red[parity][r][wave] = s[r];
+    }
+    __syncthreads();
+    float t[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      t[r] = red[parity][r][0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) t[r] += red[parity][r][w];
+    }
+    if constexpr (GROUP) {
+      // Exchange the slice dots with the other members of the group. Slot (parity) double
+      // buffering lets a member run one step ahead without overwriting values in use.
+      float* xb = a.xchg + ((unit * 2 + parity) * gsz) * R;
+      if (threadIdx.x == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+          __hip_atomic_store(xb + member * R + r, t[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t target = (step + 1) * (uint32_t)gsz;
+        uint32_t spins = 0;
+        while (__hip_atomic_load(a.counters + unit, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+          if (++spins > kSpinLimit) {
+            __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float tr = 0.0f;
+        for (int64_t c = 0; c < gsz; ++c)
+          tr += __hip_atomic_load(xb + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t[r] = tr;
+      }
+      ++step;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t row = base + r;
+      float uu = 0.0f;
+      if (row < r1) uu = (a.v ? a.v[row] : 1.0f) * t[r];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[r][c][k], acc[c][k]);
+    }
+    parity ^= 1;
+  }
+
+  float* dst = a.partial + unit * n;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+      const int64_t col = c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC + k;
+      if (col < n) dst[col] = acc[c][k];
+    }
+}
+
+template <int VEC>
+hipError_t launch_wave(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block(kBlock);
+  switch (p.chunks) {
+    case 1: hipLaunchKernelGGL((dense_wave_rows<VEC, 1, 8>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dense_wave_rows<VEC, 2, 4>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dense_wave_rows<VEC, 4, 2>), grid, block, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int VEC, int NCH>
+const void* block_kernel(bool group) {
+  return group ? reinterpret_cast<const void*>(&dense_block_rows<VEC, NCH, true>)
+               : reinterpret_cast<const void*>(&dense_block_rows<VEC, NCH, false>);
+}
+
+const void* block_kernel_for(int vec, int chunks, bool group) {
+  if (vec == 4) {
+    switch (chunks) {
+      case 1: return block_kernel<4, 1>(group);
+      case 2: return block_kernel<4, 2>(group);
+      case 4: return block_kernel<4, 4>(group);
+      case 8: return block_kernel<4, 8>(group);
+    }
+  } else if (vec == 1) {
+    switch (chunks) {
+      case 1: return block_kernel<1, 1>(group);
+      case 2: return block_kernel<1, 2>(group);
+      case 4: return block_kernel<1, 4>(group);
+      case 8: return block_kernel<1, 8>(group);
+    }
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+int64_t dense_group_max_resident(const xtvxy_launch_params& p) {
+  const void* k = block_kernel_for(p.vec, p.chunks, true);
+  if (!k) return 0;
+  int per_cu = 0, dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, 0) != hipSuccess) return 0;
+  return (int64_t)per_cu * prop.multiProcessorCount;
+}
+
+hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX) return hipErrorInvalidValue;
+  switch (p.kernel) {
+    case XTVXY_DENSE_WAVE_ROWS:
+      if (p.vec == 4) return launch_wave<4>(a, p, s);
+      if (p.vec == 1) return launch_wave<1>(a, p, s);
+      return hipErrorInvalidValue;
+    case XTVXY_DENSE_BLOCK_ROWS: {
+      const void* k = block_kernel_for(p.vec, p.chunks, false);
+      if (!k) return hipErrorInvalidValue;
+      DenseArgs args = a;
+      void* params[] = {&args};
+      return hipLaunchKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
+    }
+    case XTVXY_DENSE_GROUP_ROWS: {
+      const void* k = block_kernel_for(p.vec, p.chunks, true);
+      if (!k) return hipErrorInvalidValue;
+      DenseArgs args = a;
+      void* params[] = {&args};
+      return hipLaunchCooperativeKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace xtvxy

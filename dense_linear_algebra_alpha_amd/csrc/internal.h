@@ -1,0 +1,103 @@
+// Internal declarations shared by the host layer (api.cpp, model.cpp) and the
+// kernels (*.hip) of the xtvxy library. Not installed; the public ABI is
+// include/xtvxy.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "xtvxy.h"
+
+namespace xtvxy {
+
+constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
+constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
+constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
+constexpr int kCsrRowsPerTile = 2048;  // CSR: most rows one tile covers
+constexpr size_t kAlign = 256;       // alignment of every workspace region
+
+inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+
+// Arguments of the dense fused kernels.
+struct DenseArgs {
+  int64_t m, n, ldx;
+  const float* X;
+  const float* v;     // nullptr: v = 1
+  const float* y;
+  float* partial;     // [rows of partials][n] fp32
+  int64_t rows_per_unit;
+  int32_t lanes_per_row;
+  int32_t group;      // group-row path: workgroups per row
+  float* xchg;        // group-row path: [groups][2][group][kBlockRowsInFlight] partial dots
+  uint32_t* counters; // group-row path: [groups] arrival counters (zeroed before launch)
+  uint32_t* error;    // group-row path: set when a barrier wait gives up
+};
+
+// Arguments of the CSR fused kernels.
+struct CsrArgs {
+  int64_t m, n, nnz;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const float* values;
+  const float* v;
+  const float* y;
+  float* partial;     // LDS path: [grid][n]; global path: [n] accumulator (zeroed before launch)
+  int32_t entries_per_thread;
+  int32_t lds_window;
+};
+
+// Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first
+// HIP error it meets.
+hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s);
+hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
+// out[j] = alpha * sum_{r < rows} partial[r * n + j] + (beta != 0 ? beta * z[j] : 0), fp64 sums
+// taken over r in ascending order.
+hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t n, float alpha, float beta,
+                            const float* z, float* out, hipStream_t s);
+// out[j] = (beta != 0) ? beta * z[j] : 0
+hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s);
+// p[i] = 0 for i < count (a kernel, so that the call stays graph-capturable)
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+// t[i] *= v[i]
+hipError_t launch_scale(int64_t m, const float* v, float* t, hipStream_t s);
+hipError_t launch_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
+                            const int32_t* col_idx, int32_t* flag, hipStream_t s);
+
+// Largest co-resident grid of the dense group-row kernel for a plan (0 on error).
+int64_t dense_group_max_resident(const xtvxy_launch_params& p);
+
+// Analytical launch model (model.cpp).
+xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, const xtvxy_device_info& d,
+                         xtvxy_launch_params* p);
+xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
+                            xtvxy_launch_params* p);
+xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
+                       xtvxy_launch_params* p);
+xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
+                          xtvxy_launch_params* p);
+
+// Argument checks shared by the fused entry points and the comparator (api.cpp). On
+// success *quick tells that only out = beta z (or nothing, when n == 0) remains to do.
+xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                              const float* y, float beta, const float* z, const float* out, bool* quick);
+xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* values, const float* v, const float* y,
+                            float beta, const float* z, const float* out, bool* quick);
+
+// Workspace layout of a dense plan.
+struct DenseWorkspace {
+  size_t partial_off, partial_rows;  // partial sums [partial_rows][n]
+  size_t xchg_off, counters_off, error_off;
+  size_t total;
+};
+DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p);
+
+struct CsrWorkspace {
+  size_t partial_off, partial_rows;  // LDS path: [grid][n]; global path: one accumulator row
+  size_t total;
+};
+CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p);
+
+}  // namespace xtvxy

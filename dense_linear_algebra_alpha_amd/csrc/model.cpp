@@ -1,0 +1,234 @@
+// Analytical launch-parameter model.
+//
+// "On optimizing machine learning workloads via kernel fusion" (abstract): an
+// analytical model takes the characteristics of the input and the resources of
+// the GPU and estimates near-optimal kernel launch parameters. The page gives
+// no formula; this model is the plainest one for a kernel bound by HBM
+// bandwidth:
+//
+//   time(plan) = bytes(X, v, y, z, out) / bandwidth(plan)
+//              + bytes(partials written and read back) / bandwidth
+//              + launches * launch_cost
+//   bandwidth(plan) = min(sustained_fraction * peak,
+//                         compute_units * bytes_in_flight_per_cu / latency)
+//
+// where bytes_in_flight_per_cu follows from the row layout (rows kept in
+// flight per workgroup times their bytes) and the workgroups resident per CU.
+// The row layout itself is fixed by n (the smallest layout that covers a row),
+// so the model chooses the number of workgroups per CU, hence the grid and the
+// coarsening factor rows_per_unit = ceil(m / units). More workgroups hide
+// more latency but write more partial n-vectors; the model trades the two.
+// The constants are calibrated on MI355X: a plain streaming read sustains
+// about 0.88 of the 8 TB/s peak, and about 2 us of load latency has to be covered.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "internal.h"
+
+namespace xtvxy {
+namespace {
+
+constexpr double kSustained = 0.88;     // sustained fraction of peak HBM bandwidth (streaming read)
+constexpr double kLatency = 2.0e-6;     // seconds of memory latency that loads in flight must cover
+constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
+constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
+
+int next_pow2(int64_t x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+double bandwidth(const xtvxy_device_info& d, double inflight_per_cu) {
+  const double bw_latency = d.compute_units * inflight_per_cu / kLatency;
+  return std::min(kSustained * d.hbm_bytes_per_s, bw_latency);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Wave-row layout: rows a wavefront keeps in flight per row group and column chunks.
+int wave_unroll(int chunks) { return 8 / chunks; }
+
+}  // namespace
+
+DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
+  DenseWorkspace w{};
+  if (p.kernel == XTVXY_DENSE_GROUP_ROWS) {
+    const int64_t groups = p.grid / std::max<int32_t>(p.group, 1);
+    w.partial_rows = (size_t)groups;
+    w.partial_off = 0;
+    w.xchg_off = align_up(w.partial_off + (size_t)groups * n * sizeof(float));
+    w.counters_off = align_up(w.xchg_off + (size_t)groups * 2 * p.group * kBlockRowsInFlight * sizeof(float));
+    w.error_off = align_up(w.counters_off + (size_t)groups * sizeof(uint32_t));
+    w.total = align_up(w.error_off + sizeof(uint32_t));
+  } else {
+    w.partial_rows = (size_t)p.grid;
+    w.partial_off = 0;
+    w.total = align_up((size_t)p.grid * n * sizeof(float));
+  }
+  return w;
+}
+
+CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p) {
+  CsrWorkspace w{};
+  w.partial_off = 0;
+  w.partial_rows = (p.kernel == XTVXY_CSR_LDS_TILES) ? (size_t)p.grid : 1;
+  w.total = align_up(w.partial_rows * (size_t)n * sizeof(float));
+  return w;
+}
+
+xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
+                            xtvxy_launch_params* p) {
+  (void)ldx;
+  if (p->block_threads != kBlock || (p->vec != 1 && p->vec != 4) || p->grid <= 0 || p->grid > INT32_MAX)
+    return XTVXY_ERROR_INVALID_VALUE;
+  switch (p->kernel) {
+    case XTVXY_DENSE_WAVE_ROWS: {
+      const int lpr = p->lanes_per_row;
+      if (lpr < 1 || lpr > 64 || (lpr & (lpr - 1)) != 0) return XTVXY_ERROR_INVALID_VALUE;
+      if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4) return XTVXY_ERROR_INVALID_VALUE;
+      if ((int64_t)lpr * p->vec * p->chunks < n) return XTVXY_ERROR_INVALID_VALUE;
+      p->group = 1;
+      break;
+    }
+    case XTVXY_DENSE_BLOCK_ROWS:
+    case XTVXY_DENSE_GROUP_ROWS: {
+      if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4 && p->chunks != 8) return XTVXY_ERROR_INVALID_VALUE;
+      const int64_t slice = (int64_t)kBlock * p->vec * p->chunks;
+      if (p->kernel == XTVXY_DENSE_BLOCK_ROWS) {
+        p->group = 1;
+        if (slice < n) return XTVXY_ERROR_INVALID_VALUE;
+      } else {
+        if (p->group < 1 || (int64_t)p->group * slice < n || p->grid % p->group != 0)
+          return XTVXY_ERROR_INVALID_VALUE;
+      }
+      p->lanes_per_row = kBlock;
+      break;
+    }
+    default:
+      return XTVXY_ERROR_INVALID_VALUE;
+  }
+  const int64_t units = p->grid / p->group;
+  if (p->rows_per_unit <= 0) p->rows_per_unit = std::max<int64_t>(1, ceil_div(m, units));
+  if (p->rows_per_unit * units < m) return XTVXY_ERROR_INVALID_VALUE;
+  p->workspace_bytes = (int64_t)dense_workspace(n, *p).total;
+  (void)d;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, const xtvxy_device_info& d,
+                         xtvxy_launch_params* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->block_threads = kBlock;
+  p->vec = (aligned16 && ldx % 4 == 0) ? 4 : 1;
+  const int vec = p->vec;
+  double inflight_per_wg;  // bytes of X a workgroup has requested before it needs the first of them
+  int64_t rows_per_step;   // rows a workgroup (or group) consumes per step
+  if (n <= 64 * vec * 4) {
+    p->kernel = XTVXY_DENSE_WAVE_ROWS;
+    p->chunks = (n <= 64 * vec) ? 1 : (n <= 128 * vec) ? 2 : 4;
+    p->lanes_per_row = next_pow2(std::max<int64_t>(1, ceil_div(n, (int64_t)vec * p->chunks)));
+    p->group = 1;
+    rows_per_step = (int64_t)kWaves * (64 / p->lanes_per_row) * wave_unroll(p->chunks);
+    inflight_per_wg = (double)rows_per_step * n * sizeof(float);
+  } else if (n <= (int64_t)kBlock * vec * 8) {
+    p->kernel = XTVXY_DENSE_BLOCK_ROWS;
+    const int64_t per = (int64_t)kBlock * vec;
+    p->chunks = (n <= per) ? 1 : (n <= 2 * per) ? 2 : (n <= 4 * per) ? 4 : 8;
+    p->group = 1;
+    p->lanes_per_row = kBlock;
+    rows_per_step = kBlockRowsInFlight;
+    inflight_per_wg = (double)kBlockRowsInFlight * n * sizeof(float);
+  } else {
+    p->kernel = XTVXY_DENSE_GROUP_ROWS;
+    const int64_t per = (int64_t)kBlock * vec;
+    p->group = (int32_t)ceil_div(n, per * 8);
+    const int64_t slice = ceil_div(n, p->group);
+    p->chunks = (slice <= per) ? 1 : (slice <= 2 * per) ? 2 : (slice <= 4 * per) ? 4 : 8;
+    p->lanes_per_row = kBlock;
+    rows_per_step = kBlockRowsInFlight;
+    inflight_per_wg = (double)kBlockRowsInFlight * slice * sizeof(float);
+  }
+
+  const double io_bytes = 4.0 * ((double)m * n + m + 3.0 * n);
+  const int max_per_cu = (p->kernel == XTVXY_DENSE_GROUP_ROWS) ? 2 : kMaxWgPerCu;
+  double best = 1e300;
+  int64_t best_grid = 1;
+  for (int k = 1; k <= max_per_cu; k *= 2) {
+    int64_t grid = (int64_t)d.compute_units * k;
+    const int64_t units_needed = std::max<int64_t>(1, ceil_div(m, rows_per_step));  // no idle units
+    if (p->kernel == XTVXY_DENSE_GROUP_ROWS) {
+      grid = grid / p->group * p->group;
+      if (grid < p->group) grid = p->group;
+      grid = std::min<int64_t>(grid, units_needed * p->group);
+    } else {
+      grid = std::min<int64_t>(grid, units_needed);
+    }
+    const double resident_per_cu = std::min<double>(k, (double)grid / d.compute_units);
+    const double bw = bandwidth(d, std::max(resident_per_cu, 1.0 / d.compute_units) * inflight_per_wg);
+    const double partial_bytes = 2.0 * (double)(grid / p->group) * n * sizeof(float);
+    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + 2 * kLaunch;
+    if (t < best * 0.999) {
+      best = t;
+      best_grid = grid;
+    }
+  }
+  p->grid = best_grid;
+  p->rows_per_unit = 0;
+  p->predicted_seconds = best;
+  return complete_dense(m, n, ldx, d, p);
+}
+
+xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
+                          xtvxy_launch_params* p) {
+  (void)m;
+  (void)nnz;
+  if (p->block_threads != kBlock || p->grid <= 0 || p->grid > INT32_MAX) return XTVXY_ERROR_INVALID_VALUE;
+  if (p->entries_per_thread < 1 || p->entries_per_thread > 8) return XTVXY_ERROR_INVALID_VALUE;
+  if (p->kernel == XTVXY_CSR_LDS_TILES) {
+    const int64_t static_lds = (int64_t)(kCsrRowsPerTile + 1) * 4 + kCsrRowsPerTile * 4 + 64;
+    if ((int64_t)n * 4 + static_lds > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
+    p->lds_window = (int32_t)n;
+  } else if (p->kernel == XTVXY_CSR_GLOBAL_TILES) {
+    p->lds_window = 0;
+  } else {
+    return XTVXY_ERROR_INVALID_VALUE;
+  }
+  p->group = 1;
+  p->workspace_bytes = (int64_t)csr_workspace(n, *p).total;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d, xtvxy_launch_params* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->block_threads = kBlock;
+  p->vec = 1;
+  p->entries_per_thread = 8;
+  p->chunks = 1;
+  p->group = 1;
+  // LDS path when a workgroup's partial output fits next to a few co-resident workgroups
+  p->kernel = ((int64_t)n * 4 <= 64 * 1024) ? XTVXY_CSR_LDS_TILES : XTVXY_CSR_GLOBAL_TILES;
+  const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
+  const int64_t tile = (int64_t)kBlock * p->entries_per_thread;
+  double best = 1e300;
+  int64_t best_grid = 1;
+  for (int k = 1; k <= kMaxWgPerCu; k *= 2) {
+    int64_t grid = (int64_t)d.compute_units * k;
+    grid = std::max<int64_t>(1, std::min<int64_t>(grid, ceil_div(std::max<int64_t>(nnz, 1), tile)));
+    const double resident = std::min<double>(k, (double)grid / d.compute_units);
+    const double bw = bandwidth(d, std::max(resident, 1.0 / d.compute_units) * tile * 8.0);
+    const double partial_bytes =
+        (p->kernel == XTVXY_CSR_LDS_TILES) ? 2.0 * grid * n * sizeof(float) : 2.0 * n * sizeof(float);
+    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + 2 * kLaunch;
+    if (t < best * 0.999) {
+      best = t;
+      best_grid = grid;
+    }
+  }
+  p->grid = best_grid;
+  p->predicted_seconds = best;
+  return complete_csr(m, n, nnz, d, p);
+}
+
+}  // namespace xtvxy

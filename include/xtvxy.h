@@ -1,0 +1,225 @@
+/*
+ * xtvxy: fused evaluation of out = alpha * X^T (v .* (X y)) + beta * z on AMD gfx950.
+ *
+ * The operation is the generic pattern of "On optimizing machine learning
+ * workloads via kernel fusion" (abstract): alpha * X^T (v * (X * y)) + beta * z,
+ * computed by one fused kernel over dense or sparse X instead of a chain of
+ * operator-level library calls. Shapes (the only well-typed reading):
+ *     X  m x n,  y, z, out  n-vectors,  v  m-vector,  alpha, beta  scalars,
+ *     X y is the matrix-vector product, v .* (X y) the elementwise product.
+ * Special cases follow BLAS: n == 0 is a no-op; alpha == 0 or m == 0 (or
+ * nnz == 0) gives out = beta * z without reading X, v or y; beta == 0 gives
+ * out = alpha * X^T(...) without reading z (z may then be NULL). v == NULL
+ * means v = 1 (the normal-equations instance X^T X y). Rows with v_i == 0 are
+ * not skipped: NaN and Inf propagate as the formula says.
+ *
+ * Conventions of every entry point:
+ *   - All array pointers are DEVICE pointers on the current HIP device; the
+ *     caller owns every buffer. The library keeps no pointer after a call returns
+ *     and the fused entry points allocate no device memory: partial results live
+ *     in the caller's workspace (size from the *_workspace_size query).
+ *   - Calls are asynchronous on `stream` (0 = the null stream). The inputs and
+ *     the workspace must stay valid and unmodified until the stream passes the
+ *     call. Concurrent calls need distinct workspaces.
+ *   - The return value is the only error channel. Argument errors are detected
+ *     on the host before anything is enqueued and leave `out` untouched.
+ *     XTVXY_ERROR_LAUNCH reports a HIP error from an enqueue (possibly after an
+ *     earlier kernel of the same call was enqueued).
+ *   - fp32 storage and arithmetic; cross-workgroup sums of partial results are
+ *     taken in fp64 in a fixed order, so dense results are bitwise reproducible
+ *     for a given device and launch plan. The CSR path accumulates with LDS and
+ *     global atomics and is reproducible only up to rounding.
+ */
+#ifndef XTVXY_H_
+#define XTVXY_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define XTVXY_VERSION_MAJOR 0
+#define XTVXY_VERSION_MINOR 1
+
+typedef enum xtvxy_status {
+  XTVXY_SUCCESS = 0,
+  XTVXY_ERROR_INVALID_VALUE = 1, /* negative size, ldx < max(1, n), byte size overflow, bad plan field */
+  XTVXY_ERROR_NULL_POINTER = 2,  /* a required pointer is NULL (see each entry point) */
+  XTVXY_ERROR_ALIASING = 3,      /* out overlaps an input other than z (out == z is allowed) */
+  XTVXY_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than the query returned */
+  XTVXY_ERROR_UNSUPPORTED = 5,   /* nnz or m beyond int32 indexing */
+  XTVXY_ERROR_LAUNCH = 6,        /* a HIP call failed (no device, launch failure, ...) */
+  XTVXY_ERROR_LIBRARY = 7        /* rocBLAS / rocSPARSE failed (comparator entry points only) */
+} xtvxy_status;
+
+/* Human-readable name of a status code (static storage). */
+const char *xtvxy_status_string(xtvxy_status status);
+
+/* ------------------------------------------------------------------------ */
+/* Device description and launch plans                                     */
+/* ------------------------------------------------------------------------ */
+
+/* The GPU resources the launch model reads (the pages' model maps input
+ * characteristics and available GPU resources to launch parameters). */
+typedef struct xtvxy_device_info {
+  int32_t compute_units;     /* CUs (256 on MI355X) */
+  int32_t lds_bytes;         /* LDS bytes one workgroup may allocate (163840) */
+  int32_t l2_bytes;          /* L2 bytes of one XCD (4 MiB) */
+  int32_t xcds;              /* XCDs sharing the grid (8) */
+  double hbm_bytes_per_s;    /* peak HBM bandwidth (8.0e12) */
+} xtvxy_device_info;
+
+/* Resources of HIP device `device` (-1 = current device). */
+xtvxy_status xtvxy_get_device_info(int device, xtvxy_device_info *info);
+
+/* Dense kernel variants. */
+enum {
+  XTVXY_DENSE_WAVE_ROWS = 1,  /* rows of <= 1024 columns: lane groups within a wavefront own a row */
+  XTVXY_DENSE_BLOCK_ROWS = 2, /* rows of <= 8192 columns: one workgroup owns a row */
+  XTVXY_DENSE_GROUP_ROWS = 3  /* wider rows: `group` co-resident workgroups split a row by columns */
+};
+/* CSR kernel variants. */
+enum {
+  XTVXY_CSR_LDS_TILES = 11,   /* partial output of a workgroup held in LDS (n <= lds window) */
+  XTVXY_CSR_GLOBAL_TILES = 12 /* scatter straight into a global fp32 accumulator (any n) */
+};
+
+/* Launch parameters chosen by the analytical model (the *_plan queries) or
+ * forced by the caller (the *_ex entry points). */
+typedef struct xtvxy_launch_params {
+  int32_t kernel;          /* one of the XTVXY_DENSE_* / XTVXY_CSR_* values above */
+  int32_t vec;             /* 4: 16-byte loads of X (needs ldx % 4 == 0 and 16-byte aligned X), 1: 4-byte */
+  int32_t block_threads;   /* threads per workgroup (256) */
+  int32_t lanes_per_row;   /* dense wave path: lanes sharing one row (1..64, power of two) */
+  int32_t chunks;          /* dense: column chunks of `vec` floats per lane and row */
+  int32_t group;           /* dense group path: workgroups per row (column slices); 1 otherwise */
+  int64_t grid;            /* workgroups launched */
+  int64_t rows_per_unit;   /* dense: rows per workgroup (wave/block paths) or per group */
+  int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile */
+  int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS */
+  int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries) */
+  double predicted_seconds;/* the model's estimate for this plan */
+} xtvxy_launch_params;
+
+/* Model-chosen plan for a dense problem; `dev` NULL = the current device.
+ * X_aligned16 states whether X is 16-byte aligned (pointer % 16 == 0). */
+xtvxy_status xtvxy_dense_f32_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16,
+                                  const xtvxy_device_info *dev, xtvxy_launch_params *plan);
+
+/* Model-chosen plan for a CSR problem; `dev` NULL = the current device. */
+xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info *dev,
+                                xtvxy_launch_params *plan);
+
+/* ------------------------------------------------------------------------ */
+/* Fused entry points                                                       */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes xtvxy_dense_f32 needs for this shape on the current device
+ * (assuming a 16-byte aligned X; an unaligned X never needs more). */
+xtvxy_status xtvxy_dense_f32_workspace_size(int64_t m, int64_t n, int64_t ldx, size_t *bytes);
+
+/* out = alpha * X^T (v .* (X y)) + beta * z for dense row-major X: element
+ * (i, k) at X[i * ldx + k], ldx >= max(1, n), at least (m-1)*ldx + n floats.
+ * Pointers: y and out required when n > 0; X required when alpha != 0, m > 0
+ * and n > 0; v optional (NULL = 1); z required iff beta != 0; workspace may be
+ * NULL iff the query returned 0. `out` may equal `z` but may not otherwise
+ * overlap X, v, y or z. */
+xtvxy_status xtvxy_dense_f32(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx,
+                             const float *v, const float *y, float beta, const float *z, float *out,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* As xtvxy_dense_f32 with the launch parameters forced (NULL = model). The
+ * workspace must hold force->workspace_bytes as returned by xtvxy_dense_f32_plan
+ * after the caller's edits (call the plan query with the edited plan to refresh
+ * it via xtvxy_dense_f32_plan_complete). */
+xtvxy_status xtvxy_dense_f32_ex(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx,
+                                const float *v, const float *y, float beta, const float *z,
+                                float *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream, const xtvxy_launch_params *force);
+
+/* Checks a caller-edited dense plan against the shape and fills in grid-derived
+ * fields (rows_per_unit when 0, workspace_bytes). */
+xtvxy_status xtvxy_dense_f32_plan_complete(int64_t m, int64_t n, int64_t ldx,
+                                           const xtvxy_device_info *dev, xtvxy_launch_params *plan);
+
+/* Workspace bytes xtvxy_csr_f32 needs for this shape on the current device. */
+xtvxy_status xtvxy_csr_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t *bytes);
+
+/* The same pattern for CSR X: zero-based int32 row_ptr[m + 1] (row_ptr[0] == 0,
+ * non-decreasing, row_ptr[m] == nnz), int32 col_idx[nnz] in [0, n), fp32
+ * values[nnz]. Columns may be unsorted within a row; a column stored twice in
+ * a row contributes twice; empty rows are allowed. A malformed structure is
+ * undefined behaviour (check it with xtvxy_csr_check). Pointer rules as for the
+ * dense entry point, with row_ptr, col_idx and values in place of X (col_idx
+ * and values may be NULL when nnz == 0). */
+xtvxy_status xtvxy_csr_f32(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                           const int32_t *col_idx, const float *values, const float *v,
+                           const float *y, float beta, const float *z, float *out, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha,
+                              const int32_t *row_ptr, const int32_t *col_idx, const float *values,
+                              const float *v, const float *y, float beta, const float *z,
+                              float *out, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream, const xtvxy_launch_params *force);
+
+xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
+                                         const xtvxy_device_info *dev, xtvxy_launch_params *plan);
+
+/* Device-side structure check of a CSR matrix. Writes to *d_flag (a device
+ * int32) 0 when row_ptr[0] == 0, row_ptr is non-decreasing, row_ptr[m] == nnz
+ * and every column index lies in [0, n); otherwise a positive code (1: row_ptr
+ * ends, 2: row_ptr decreases, 3: column out of range). Asynchronous. */
+xtvxy_status xtvxy_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
+                             const int32_t *col_idx, int32_t *d_flag, hipStream_t stream);
+
+/* Timing hook for measurements (process-wide, not thread-safe). While both
+ * events are non-NULL, every fused call records `before_main` on its stream
+ * just before its main fused kernel and `after_main` just after it (before the
+ * aggregation kernel), so that hipEventElapsedTime gives that kernel's time.
+ * NULL, NULL switches the hook off. The events are the caller's. */
+xtvxy_status xtvxy_set_kernel_timing_events(hipEvent_t before_main, hipEvent_t after_main);
+
+/* ------------------------------------------------------------------------ */
+/* Unfused comparator: the same result from operator-level library calls    */
+/* (the pages' baseline of several library kernel launches)               */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes of the dense comparator: the m-vector t = X y. */
+xtvxy_status xtvxy_dense_f32_unfused_reference_workspace_size(int64_t m, int64_t n, size_t *bytes);
+
+/* rocBLAS sgemv (t = X y), an elementwise kernel (t = v .* t, skipped when v
+ * is NULL), a copy of z into out when beta != 0 and out != z, and rocBLAS
+ * sgemv (out = alpha X^T t + beta out). Same arguments and rules as
+ * xtvxy_dense_f32. Not thread-safe (one rocBLAS handle per device). */
+xtvxy_status xtvxy_dense_f32_unfused_reference(int64_t m, int64_t n, float alpha, const float *X,
+                                               int64_t ldx, const float *v, const float *y,
+                                               float beta, const float *z, float *out,
+                                               void *workspace, size_t workspace_bytes,
+                                               hipStream_t stream);
+
+/* The CSR comparator keeps rocSPARSE descriptors and the result of the
+ * structure analysis in a plan, made once per matrix (blocking, allocates). */
+typedef struct xtvxy_csr_unfused_plan_s *xtvxy_csr_unfused_plan;
+
+xtvxy_status xtvxy_csr_f32_unfused_plan_create(int64_t m, int64_t n, int64_t nnz,
+                                               const int32_t *row_ptr, const int32_t *col_idx,
+                                               const float *values, hipStream_t stream,
+                                               xtvxy_csr_unfused_plan *plan);
+xtvxy_status xtvxy_csr_f32_unfused_plan_destroy(xtvxy_csr_unfused_plan plan);
+
+/* rocSPARSE SpMV (t = X y), the elementwise kernel, and rocSPARSE SpMV with
+ * the transposed matrix (out = alpha X^T t + beta out). Uses the plan's
+ * buffers; not thread-safe per plan. */
+xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan plan, float alpha,
+                                             const float *v, const float *y, float beta,
+                                             const float *z, float *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* XTVXY_H_ */

@@ -1,0 +1,173 @@
+"""The C ABI without a GPU: exports, host-side argument checks, and the launch model.
+
+Every call here returns before the library touches the HIP runtime (argument
+errors are detected first), or is a pure host computation (plans for a stated
+device description). No kernel is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_linear_algebra_alpha_amd as xt
+from dense_linear_algebra_alpha_amd import _abi, build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "xtvxy.h")
+
+MI355X = xt.xtvxy_device_info(compute_units=256, lds_bytes=163840, l2_bytes=4 << 20, xcds=8,
+                              hbm_bytes_per_s=8.0e12)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if build.sources_newer_than_library():
+        build.build()
+    return _abi.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(xtvxy_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 18
+    for name in names:
+        assert hasattr(lib, name), name
+    # and the binding wraps each of them under the same name
+    for name in names:
+        assert hasattr(xt, name), name
+
+
+def test_status_strings(lib):
+    assert xt.xtvxy_status_string(0) == "XTVXY_SUCCESS"
+    assert xt.xtvxy_status_string(4) == "XTVXY_ERROR_WORKSPACE"
+    assert xt.xtvxy_status_string(99) == "XTVXY_UNKNOWN_STATUS"
+
+
+FAKE = 1 << 40  # an address that is never dereferenced: every call below fails its host checks first
+
+
+def dense_status(m=8, n=8, alpha=1.0, X=FAKE, ldx=8, v=None, y=FAKE + 4096, beta=0.0, z=None, out=FAKE + 8192,
+                 ws=None, ws_bytes=0, fn="xtvxy_dense_f32"):
+    return getattr(_abi.load(), fn)(m, n, alpha, X, ldx, v, y, beta, z, out, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("fn", ["xtvxy_dense_f32", "xtvxy_dense_f32_unfused_reference"])
+def test_dense_argument_errors(lib, fn):
+    assert dense_status(m=-1, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert dense_status(n=-2, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert dense_status(ldx=7, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE          # ldx < n
+    assert dense_status(n=0, ldx=0, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE     # ldx < 1
+    assert dense_status(m=1 << 60, ldx=1 << 10, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE  # bytes overflow
+    assert dense_status(y=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert dense_status(out=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert dense_status(X=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert dense_status(beta=0.5, z=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    # out overlapping X, y, v, or z (other than out == z) is rejected
+    assert dense_status(out=FAKE + 16, fn=fn) == _abi.XTVXY_ERROR_ALIASING
+    assert dense_status(out=FAKE + 4096 + 4, fn=fn) == _abi.XTVXY_ERROR_ALIASING
+    assert dense_status(v=FAKE + 8192 + 8, fn=fn) == _abi.XTVXY_ERROR_ALIASING
+    assert dense_status(beta=1.0, z=FAKE + 8192 + 4, fn=fn) == _abi.XTVXY_ERROR_ALIASING
+    # n == 0 is a successful no-op that touches nothing
+    assert dense_status(n=0, ldx=1, fn=fn) == _abi.XTVXY_SUCCESS
+
+
+def csr_status(m=8, n=8, nnz=16, alpha=1.0, rp=FAKE, ci=FAKE + 1024, vals=FAKE + 2048, v=None, y=FAKE + 4096,
+               beta=0.0, z=None, out=FAKE + 8192):
+    return _abi.load().xtvxy_csr_f32(m, n, nnz, alpha, rp, ci, vals, v, y, beta, z, out, None, 0, None)
+
+
+def test_csr_argument_errors(lib):
+    assert csr_status(m=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert csr_status(nnz=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert csr_status(nnz=1 << 31) == _abi.XTVXY_ERROR_UNSUPPORTED
+    assert csr_status(m=1 << 31) == _abi.XTVXY_ERROR_UNSUPPORTED
+    assert csr_status(rp=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(ci=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(vals=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(y=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(beta=2.0) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(out=FAKE + 1024 + 60) == _abi.XTVXY_ERROR_ALIASING        # overlaps col_idx
+    assert csr_status(out=FAKE + 4) == _abi.XTVXY_ERROR_ALIASING                # overlaps row_ptr
+    assert csr_status(n=0) == _abi.XTVXY_SUCCESS
+    st = lib.xtvxy_csr_check(4, 4, 4, None, FAKE, FAKE, None)
+    assert st == _abi.XTVXY_ERROR_NULL_POINTER
+
+
+def test_query_argument_errors(lib):
+    b = ctypes.c_size_t()
+    assert lib.xtvxy_dense_f32_workspace_size(4, 8, 4, ctypes.byref(b)) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_dense_f32_workspace_size(4, 8, 8, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert lib.xtvxy_csr_f32_workspace_size(-1, 8, 8, ctypes.byref(b)) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_dense_f32_unfused_reference_workspace_size(100, 8, ctypes.byref(b)) == 0
+    assert b.value >= 400 and b.value % 256 == 0
+    assert lib.xtvxy_csr_f32_unfused_plan_create(4, 4, 4, None, FAKE, FAKE, None, None) == \
+        _abi.XTVXY_ERROR_NULL_POINTER
+
+
+SHAPES = [(2048, 128), (1_000_000, 256), (65_536, 8192), (8192, 65_536), (1, 1), (7, 3), (100, 1000),
+          (5, 1025), (3, 8193), (1000, 200_000)]
+
+
+@pytest.mark.parametrize("m,n", SHAPES)
+@pytest.mark.parametrize("aligned", [1, 0])
+def test_dense_model_plans_cover_the_problem(lib, m, n, aligned):
+    p = xt.xtvxy_dense_f32_plan(m, n, n, aligned, MI355X)
+    assert p.block_threads == 256 and p.grid >= 1
+    assert p.vec == (4 if aligned and n % 4 == 0 else 1)
+    if p.kernel == xt.XTVXY_DENSE_WAVE_ROWS:
+        assert p.lanes_per_row * p.vec * p.chunks >= n and p.lanes_per_row <= 64 and p.group == 1
+        units = p.grid
+    elif p.kernel == xt.XTVXY_DENSE_BLOCK_ROWS:
+        assert 256 * p.vec * p.chunks >= n and p.group == 1
+        units = p.grid
+    else:
+        assert p.kernel == xt.XTVXY_DENSE_GROUP_ROWS
+        assert p.group * 256 * p.vec * p.chunks >= n and p.grid % p.group == 0
+        units = p.grid // p.group
+    assert p.rows_per_unit * units >= m and (p.rows_per_unit - 1) * units < m + p.rows_per_unit
+    assert p.workspace_bytes >= units * n * 4 and p.workspace_bytes % 256 == 0
+    assert p.predicted_seconds > 0
+
+
+def test_dense_model_picks_the_row_layout_by_width(lib):
+    assert xt.xtvxy_dense_f32_plan(2048, 128, 128, 1, MI355X).kernel == xt.XTVXY_DENSE_WAVE_ROWS
+    assert xt.xtvxy_dense_f32_plan(2048, 128, 128, 1, MI355X).lanes_per_row == 32
+    assert xt.xtvxy_dense_f32_plan(10**6, 256, 256, 1, MI355X).lanes_per_row == 64
+    assert xt.xtvxy_dense_f32_plan(65536, 8192, 8192, 1, MI355X).kernel == xt.XTVXY_DENSE_BLOCK_ROWS
+    p = xt.xtvxy_dense_f32_plan(8192, 65536, 65536, 1, MI355X)
+    assert p.kernel == xt.XTVXY_DENSE_GROUP_ROWS and p.group == 8
+    # the model's estimate is close to the bandwidth bound on the big shapes
+    p = xt.xtvxy_dense_f32_plan(10**6, 256, 256, 1, MI355X)
+    assert 1.024e9 / 8.0e12 < p.predicted_seconds < 1.024e9 / 8.0e12 / 0.8
+
+
+def test_plan_complete_rejects_plans_that_do_not_cover(lib):
+    p = xt.xtvxy_dense_f32_plan(1000, 256, 256, 1, MI355X)
+    q = xt.xtvxy_launch_params.from_buffer_copy(p)
+    q.lanes_per_row = 16  # 16 lanes * 4 * 1 = 64 columns < 256
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_dense_f32_plan_complete(1000, 256, 256, q, MI355X)
+    q = xt.xtvxy_launch_params.from_buffer_copy(p)
+    q.lanes_per_row = 48  # not a power of two
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_dense_f32_plan_complete(1000, 256, 256, q, MI355X)
+    q = xt.xtvxy_launch_params.from_buffer_copy(p)
+    q.grid, q.rows_per_unit = 64, 0
+    xt.xtvxy_dense_f32_plan_complete(1000, 256, 256, q, MI355X)
+    assert q.rows_per_unit == 16 and q.workspace_bytes == 64 * 256 * 4
+
+
+@pytest.mark.parametrize("m,n,nnz", [(10_000_000, 1000, 100_000_000), (5_000_000, 1_000_000, 200_000_000),
+                                     (10, 5, 7), (1, 1, 1)])
+def test_csr_model_plans(lib, m, n, nnz):
+    p = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
+    assert p.grid >= 1 and 1 <= p.entries_per_thread <= 8
+    if n * 4 <= 64 * 1024:
+        assert p.kernel == xt.XTVXY_CSR_LDS_TILES and p.workspace_bytes >= p.grid * n * 4
+    else:
+        assert p.kernel == xt.XTVXY_CSR_GLOBAL_TILES and p.workspace_bytes >= n * 4

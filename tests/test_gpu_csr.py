@@ -1,0 +1,188 @@
+"""GPU parity of the fused CSR path against the fp64 oracle (runs through the C ABI)."""
+import numpy as np
+import pytest
+
+import datagen
+import dense_linear_algebra_alpha_amd as xt
+from gpu_util import CsrOnDevice, DenseOnDevice, assert_parity, csr_oracle, dense_oracle, note
+
+pytestmark = pytest.mark.gpu
+
+
+def check(p, plan=None, what=""):
+    note("csr %s m=%d n=%d nnz=%d plan=%s" % (what or p.name, p.m, p.n, p.nnz,
+                                             None if plan is None else plan.as_dict()))
+    got = CsrOnDevice(p).run(plan=plan)
+    ref, bnd = csr_oracle(p)
+    return assert_parity(got, ref, bnd, "%s m=%d n=%d" % (what or p.name, p.m, p.n))
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (5, 7), (100, 3), (100, 1000), (3000, 64), (3000, 1000), (2500, 20000),
+                                 (4000, 70000), (700, 300000)])
+@pytest.mark.parametrize("mean_len", [1.0, 6.0, 40.0])
+def test_irregular_matrices(m, n, mean_len):
+    check(datagen.csr_random(m, n, seed=m + n + int(mean_len), mean_len=mean_len, empty_frac=0.2, dup_frac=0.1),
+          what="random")
+
+
+def forced_plans(m, n, nnz):
+    kernels = [xt.XTVXY_CSR_GLOBAL_TILES]
+    if n * 4 + 16448 <= 163840:
+        kernels.append(xt.XTVXY_CSR_LDS_TILES)
+    out = []
+    for k in kernels:
+        for ept in (1, 3, 8):
+            for grid in (1, 7, 256):
+                lp = xt.xtvxy_launch_params(kernel=k, block_threads=256, entries_per_thread=ept, grid=grid, vec=1,
+                                            chunks=1, group=1)
+                out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
+    return out
+
+
+@pytest.mark.parametrize("m,n,mean_len", [(2000, 500, 9.0), (500, 30000, 30.0)])
+def test_every_kernel_variant(m, n, mean_len):
+    p = datagen.csr_random(m, n, seed=31, mean_len=mean_len, empty_frac=0.1, dup_frac=0.05)
+    ref, bnd = csr_oracle(p)
+    d = CsrOnDevice(p)
+    for plan in forced_plans(m, n, p.nnz):
+        note("forced %s" % plan.as_dict())
+        assert_parity(d.run(plan=plan), ref, bnd, "forced %s" % plan.as_dict())
+
+
+def test_rows_longer_than_a_tile():
+    # rows of 3000..9000 entries (more than one 2048-entry tile) between short and empty rows
+    g = np.random.default_rng(5)
+    m, n = 64, 12000
+    lens = g.integers(0, 5, size=m)
+    lens[[3, 17, 40, 63]] = [3000, 9000, 2049, 5000]
+    rp = np.zeros(m + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    cols = np.concatenate([np.sort(g.choice(n, size=L, replace=False)) for L in lens]).astype(np.int32)
+    p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols, datagen.uniform(int(rp[-1]), 1, "vals"),
+                           datagen.uniform(n, 1, "y"), datagen.uniform(m, 1, "v"), datagen.uniform(n, 1, "z"),
+                           1.25, -0.5, "long rows")
+    check(p)
+    for plan in forced_plans(m, n, p.nnz)[::4]:
+        check(p, plan=plan, what="long rows forced")
+
+
+def test_long_runs_of_empty_rows():
+    # stretches of empty rows longer than the rows a tile can stage
+    m, n = 20000, 300
+    g = np.random.default_rng(6)
+    lens = np.zeros(m, np.int64)
+    lens[::2999] = g.integers(1, 40, size=lens[::2999].size)
+    lens[-1] = 0
+    rp = np.zeros(m + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    cols = g.integers(0, n, size=int(rp[-1])).astype(np.int32)
+    p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols, datagen.uniform(int(rp[-1]), 2, "vals"),
+                           datagen.uniform(n, 2, "y"), datagen.uniform(m, 2, "v"), None, 2.0, 0.0, "sparse rows")
+    check(p)
+    for plan in forced_plans(m, n, p.nnz)[::3]:
+        check(p, plan=plan, what="sparse rows forced")
+
+
+@pytest.mark.parametrize("n", [50, 900, 40000])
+def test_csr_agrees_with_dense_on_the_same_matrix(n):
+    m = 300
+    p = datagen.dense_problem(m, n, seed=41)
+    X = p.X2d().copy()
+    X[np.random.default_rng(1).random((m, n)) < 0.9] = 0.0
+    rp, ci, vals = datagen.csr_from_dense(X)
+    q = datagen.CsrProblem(m, n, rp, ci, vals, p.y, p.v, p.z, p.alpha, p.beta, "from dense")
+    pd = datagen.DenseProblem(m, n, n, X.ravel().copy(), p.y, p.v, p.z, p.alpha, p.beta, "dense twin")
+    note("csr vs dense n=%d" % n)
+    got_csr = CsrOnDevice(q).run()
+    got_dense = DenseOnDevice(pd).run()
+    ref, bnd = dense_oracle(pd)
+    assert_parity(got_csr, ref, bnd, "csr")
+    assert_parity(got_dense, ref, bnd, "dense")
+
+
+def test_exact_integers_bitwise():
+    g = np.random.default_rng(3)
+    m, n = 5000, 700
+    X = (g.integers(-1, 2, size=(m, n)) * (g.random((m, n)) < 0.05)).astype(np.float32)
+    rp, ci, vals = datagen.csr_from_dense(X)
+    y, v, z = (g.integers(-1, 2, size=s).astype(np.float32) for s in (n, m, n))
+    p = datagen.CsrProblem(m, n, rp, ci, vals, y, v, z, 1.5, 0.5, "integers")
+    note("csr exact integers")
+    got = CsrOnDevice(p).run()
+    S = X.astype(np.int64).T @ (v.astype(np.int64) * (X.astype(np.int64) @ y.astype(np.int64)))
+    assert np.array_equal(got, (1.5 * S + 0.5 * z).astype(np.float32))
+
+
+def test_special_cases():
+    import torch
+    p = datagen.csr_random(200, 50, seed=7)
+    d = CsrOnDevice(p)
+    note("csr alpha == 0")
+    assert np.array_equal(d.run(alpha=0.0, beta=0.5), (np.float32(0.5) * p.z).astype(np.float32))
+    ref = d.run(beta=0.0)
+    d.z = torch.full_like(d.z, float("nan"))
+    out = d.run(beta=0.0)
+    assert np.array_equal(out, ref) and np.all(np.isfinite(out))
+    empty = datagen.CsrProblem(4, 50, np.zeros(5, np.int32), np.zeros(0, np.int32), np.zeros(0, np.float32),
+                               p.y, np.ones(4, np.float32), p.z, 1.0, -2.0, "no entries")
+    assert np.array_equal(CsrOnDevice(empty).run(), (np.float32(-2.0) * p.z).astype(np.float32))
+    # NaN in one stored entry reaches exactly the columns of its row
+    X = np.zeros((10, 8), np.float32)
+    X[2, 1], X[2, 5], X[3, 0], X[3, 5], X[7, 2] = 1.0, 2.0, -1.0, 0.5, 3.0
+    rp, ci, vals = datagen.csr_from_dense(X)
+    vals[0] = np.nan
+    q = datagen.CsrProblem(10, 8, rp, ci, vals, p.y[:8].copy(), np.ones(10, np.float32), p.z[:8].copy(), 1.0, 1.0)
+    out = CsrOnDevice(q).run()
+    assert set(np.nonzero(np.isnan(out))[0].tolist()) == {1, 5}
+
+
+def test_structure_check():
+    import torch
+    p = datagen.csr_random(100, 20, seed=8)
+    d = CsrOnDevice(p)
+    note("csr_check")
+    assert xt.csr_check(d.rp, d.ci, 20) == 0
+    bad = d.ci.clone()
+    bad[3] = 20
+    assert xt.csr_check(d.rp, bad, 20) == 3
+    rp = d.rp.clone()
+    a, b = int(rp[10].item()), int(rp[11].item())
+    rp[10], rp[11] = b + 1, a  # row_ptr decreases from position 10 to 11
+    assert xt.csr_check(rp, d.ci, 20) >= 2
+    rp = d.rp.clone()
+    rp[-1] -= 1
+    assert xt.csr_check(rp, d.ci, 20) >= 1
+
+
+def test_logistic_hvp_scaled():
+    check(datagen.WORKLOADS["csr_10000000x1000_logistic_hvp"](m=300_000))
+
+
+def test_zipf_scaled():
+    check(datagen.WORKLOADS["csr_5000000x1000000_zipf"](m=100_000, n=200_000))
+
+
+def test_zipf_permuted_columns_scaled():
+    check(datagen.WORKLOADS["csr_5000000x1000000_zipf"](m=100_000, n=200_000, permute_columns=True),
+          what="zipf permuted")
+
+
+def test_full_size_logistic_hvp_10000000x1000():
+    check(datagen.WORKLOADS["csr_10000000x1000_logistic_hvp"]())
+
+
+def test_full_size_zipf_5000000x1000000():
+    check(datagen.WORKLOADS["csr_5000000x1000000_zipf"]())
+
+
+def test_repeated_calls_reuse_a_workspace():
+    import torch
+    p = datagen.csr_random(5000, 900, seed=9, mean_len=12.0)
+    d = CsrOnDevice(p)
+    ws = torch.empty(xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz), dtype=torch.uint8, device="cuda")
+    ref, bnd = csr_oracle(p)
+    note("csr workspace reuse")
+    for _ in range(3):
+        out = xt.csr(d.rp, d.ci, d.vals, p.n, d.y, d.v, d.z, p.alpha, p.beta, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out.cpu().numpy(), ref, bnd, "reuse")
