@@ -183,10 +183,9 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64
   a.lanes_per_row = plan.lanes_per_row;
   a.group = plan.group;
   if (plan.kernel == XTVXY_DENSE_GROUP_ROWS) {
-    a.xchg = reinterpret_cast<float*>(base + w.xchg_off);
-    a.counters = reinterpret_cast<uint32_t*>(base + w.counters_off);
+    a.xchg = base + w.xchg_off;
     a.error = reinterpret_cast<uint32_t*>(base + w.error_off);
-    hipError_t e = launch_zero(base + w.counters_off, w.total - w.counters_off, stream);
+    hipError_t e = launch_zero(base + w.xchg_off, w.total - w.xchg_off, stream);
     if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   }
   const hipEvent_t before = g_before_main, after = g_after_main;

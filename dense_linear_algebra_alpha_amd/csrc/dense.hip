@@ -13,20 +13,27 @@
 // Three layouts of a row over the threads (chosen by the launch model):
 //   wave rows  (n <= 1024): `lanes_per_row` lanes of a wavefront share a row,
 //              each holding `chunks` pieces of `VEC` columns; a wavefront keeps
-//              several rows in flight and reduces each dot within its lanes.
+//              UNR rows per row group in flight and reduces their dots with DPP
+//              and permlane-swap lane exchanges (no LDS round trips).
 //   block rows (n <= 8192): the 256 threads of a workgroup share a row; the dot
 //              is reduced across the four wavefronts through LDS.
 //   group rows (wider):     `group` co-resident workgroups split a row into
-//              column slices; partial dots go through global memory and a
-//              per-group arrival counter (cooperative launch guarantees that the
-//              members are resident together).
+//              column slices. Each member publishes its slice dots in 64-bit
+//              slots that carry the value and the step number together, so a
+//              reader needs no fence: it waits until a slot shows the step it
+//              expects. Cooperative launch guarantees that the members are
+//              resident together; a bounded wait flags an error instead of hanging.
+//
+// Every loop runs the same number of iterations in all lanes of a workgroup
+// (rows past the end are masked to zero), so cross-lane exchanges never execute
+// under divergent control flow.
 #include "device_util.h"
 #include "internal.h"
 
 namespace xtvxy {
 namespace {
 
-constexpr uint32_t kSpinLimit = 1u << 22;  // barrier waits give up (and flag an error) after this
+constexpr uint32_t kSpinLimit = 1u << 24;  // a barrier wait gives up (and flags an error) after this
 
 template <int VEC, int NCH, int UNR>
 __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
@@ -42,32 +49,31 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
   const int64_t n = a.n;
   const int64_t r0 = (int64_t)blockIdx.x * a.rows_per_unit;
   const int64_t r1 = min(a.m, r0 + a.rows_per_unit);
+  const int64_t per_batch = (int64_t)units * UNR;  // rows of the workgroup per batch
 
   float yv[NCH][VEC], acc[NCH][VEC];
+  bool cok[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
+  for (int c = 0; c < NCH; ++c) {
+    const int64_t col0 = ((int64_t)c * lpr + sub) * VEC;
+    cok[c] = col0 < n;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-      const int64_t col = ((int64_t)c * lpr + sub) * VEC + k;
-      yv[c][k] = col < n ? a.y[col] : 0.0f;
+      yv[c][k] = (col0 + k < n) ? a.y[col0 + k] : 0.0f;
       acc[c][k] = 0.0f;
     }
+  }
 
-  for (int64_t base = r0 + unit; base < r1; base += (int64_t)units * UNR) {
+  // Row u of a batch for this lane's group: r0 + batch_start + u * units + unit.
+  auto process = [&](int64_t start, bool check) {
     float xv[UNR][NCH][VEC];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t row = base + (int64_t)u * units;
-      if (row < r1) {
-        const float* xr = a.X + row * a.ldx;
+      const int64_t row = start + (int64_t)u * units + unit;
+      const bool rok = !check || row < r1;
+      const float* xr = a.X + (rok ? row : r0) * a.ldx;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c) load_chunk<VEC>(xr, ((int64_t)c * lpr + sub) * VEC, n, xv[u][c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) xv[u][c][k] = 0.0f;
-      }
+      for (int c = 0; c < NCH; ++c) load_chunk<VEC>(xr, ((int64_t)c * lpr + sub) * VEC, cok[c] && rok, xv[u][c]);
     }
     float s[UNR];
 #pragma unroll
@@ -78,27 +84,49 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) s[u] = fmaf(xv[u][c][k], yv[c][k], s[u]);
     }
+    if constexpr (UNR == 8) {
+      if (lpr == 64) {
+        // lane i ends with the dot of row i >> 3 of the batch; scale it there, then broadcast
+        const float t = wave_sum8_transposed(s);
+        const int64_t row = start + (lane >> 3) * (int64_t)units + unit;
+        const bool rok = !check || row < r1;
+        const float vv = a.v ? (rok ? a.v[row] : 0.0f) : 1.0f;
+        const float uu = rok ? vv * t : 0.0f;
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) s[u] = group_sum(s[u], lpr);
+        for (int u = 0; u < UNR; ++u) {
+          const float uu_b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(uu), 8 * u));
+#pragma unroll
+          for (int c = 0; c < NCH; ++c)
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu_b, xv[u][c][k], acc[c][k]);
+        }
+        return;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int64_t row = base + (int64_t)u * units;
-      float uu = 0.0f;
-      if (row < r1) uu = (a.v ? a.v[row] : 1.0f) * s[u];
+      const float t = group_sum(s[u], lpr);
+      const int64_t row = start + (int64_t)u * units + unit;
+      const bool rok = !check || row < r1;
+      const float vv = a.v ? (rok ? a.v[row] : 0.0f) : 1.0f;
+      const float uu = rok ? vv * t : 0.0f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[u][c][k], acc[c][k]);
     }
-  }
+  };
+
+  int64_t start = r0;
+  for (; start + per_batch <= r1; start += per_batch) process(start, false);
+  if (start < r1) process(start, true);
 
   // Row groups of a wavefront that own the same columns are combined by lane exchanges,
   // the four wavefronts through LDS, in a fixed order.
-  for (int off = lpr; off < 64; off <<= 1)
 #pragma unroll
-    for (int c = 0; c < NCH; ++c)
+  for (int c = 0; c < NCH; ++c)
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) acc[c][k] += __shfl_xor(acc[c][k], off, 64);
+    for (int k = 0; k < VEC; ++k) acc[c][k] = slot_sum(acc[c][k], lpr);
   if (slot == 0) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c)
@@ -115,28 +143,39 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
   }
 }
 
+// 64-bit exchange slot: the float's bits in the low word, the step tag (step + 1) in the high word.
+__device__ __forceinline__ uint64_t pack_slot(float v, uint32_t tag) {
+  return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+}
+
 template <int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   constexpr int R = kBlockRowsInFlight;
+  constexpr int kMaxGroup = kBlock / R;
   __shared__ float red[2][R][kWaves];
+  __shared__ float gx[GROUP ? R : 1][GROUP ? kMaxGroup : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n = a.n;
-  const int64_t gsz = GROUP ? a.group : 1;
+  const int gsz = GROUP ? a.group : 1;
   const int64_t unit = GROUP ? blockIdx.x / gsz : blockIdx.x;
-  const int64_t member = GROUP ? blockIdx.x % gsz : 0;
-  const int64_t c0 = member * ((int64_t)kBlock * VEC * NCH);  // first column of this slice
+  const int member = GROUP ? (int)(blockIdx.x % gsz) : 0;
+  const int64_t c0 = (int64_t)member * ((int64_t)kBlock * VEC * NCH);  // first column of this slice
   const int64_t r0 = unit * a.rows_per_unit;
   const int64_t r1 = min(a.m, r0 + a.rows_per_unit);
 
   float yv[NCH][VEC], acc[NCH][VEC];
+  bool cok[NCH];
 #pragma unroll
-  for (int c = 0; c < NCH; ++c)
+  for (int c = 0; c < NCH; ++c) {
+    const int64_t col0 = c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC;
+    cok[c] = col0 < n;
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
-      const int64_t col = c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC + k;
-      yv[c][k] = col < n ? a.y[col] : 0.0f;
+      yv[c][k] = (col0 + k < n) ? a.y[col0 + k] : 0.0f;
       acc[c][k] = 0.0f;
     }
+  }
+  uint64_t* slots = GROUP ? reinterpret_cast<uint64_t*>(a.xchg) + unit * 2 * gsz * R : nullptr;
 
   int parity = 0;
   uint32_t step = 0;
@@ -145,17 +184,11 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r;
-      if (row < r1) {
-        const float* xr = a.X + row * a.ldx;
+      const bool rok = row < r1;
+      const float* xr = a.X + (rok ? row : r0) * a.ldx;
 #pragma unroll
-        for (int c = 0; c < NCH; ++c)
-          load_chunk<VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, n, xv[r][c]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < NCH; ++c)
-#pragma unroll
-          for (int k = 0; k < VEC; ++k) xv[r][c][k] = 0.0f;
-      }
+      for (int c = 0; c < NCH; ++c)
+        load_chunk<VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, xv[r][c]);
     }
     float s[R];
 #pragma unroll
@@ -180,30 +213,37 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
       for (int w = 1; w < kWaves; ++w) t[r] += red[parity][r][w];
     }
     if constexpr (GROUP) {
-      // Exchange the slice dots with the other members of the group. Slot (parity) double
-      // buffering lets a member run one step ahead without overwriting values in use.
-      float* xb = a.xchg + ((unit * 2 + parity) * gsz) * R;
-      if (threadIdx.x == 0) {
+      // Publish this slice's dots, then collect every member's for this step. Slot parity
+      // lets a member run one step ahead without overwriting values still being read.
+      uint64_t* sl = slots + parity * gsz * R;
+      const uint32_t tag = step + 1;
+      if (threadIdx.x < R) {
+        float mine = t[0];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
-          __hip_atomic_store(xb + member * R + r, t[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_fetch_add(a.counters + unit, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t target = (step + 1) * (uint32_t)gsz;
+        for (int r = 1; r < R; ++r)
+          if (threadIdx.x == r) mine = t[r];
+        __hip_atomic_store(sl + member * R + threadIdx.x, pack_slot(mine, tag), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (threadIdx.x < gsz * R) {
+        const int c = threadIdx.x / R, r = threadIdx.x % R;
+        uint64_t w = __hip_atomic_load(sl + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
-        while (__hip_atomic_load(a.counters + unit, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        while ((uint32_t)(w >> 32) != tag) {
           if (++spins > kSpinLimit) {
             __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
-          __builtin_amdgcn_s_sleep(2);
+          __builtin_amdgcn_s_sleep(1);
+          w = __hip_atomic_load(sl + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        gx[r][c] = __uint_as_float((uint32_t)w);
       }
       __syncthreads();
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        float tr = 0.0f;
-        for (int64_t c = 0; c < gsz; ++c)
-          tr += __hip_atomic_load(xb + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        float tr = gx[r][0];
+        for (int c = 1; c < gsz; ++c) tr += gx[r][c];
         t[r] = tr;
       }
       ++step;
@@ -211,8 +251,9 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r;
-      float uu = 0.0f;
-      if (row < r1) uu = (a.v ? a.v[row] : 1.0f) * t[r];
+      const bool rok = row < r1;
+      const float vv = a.v ? (rok ? a.v[row] : 0.0f) : 1.0f;
+      const float uu = rok ? vv * t[r] : 0.0f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
@@ -295,6 +336,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
       return hipLaunchKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
     }
     case XTVXY_DENSE_GROUP_ROWS: {
+      if (p.group < 1 || p.group > kBlock / kBlockRowsInFlight) return hipErrorInvalidValue;
       const void* k = block_kernel_for(p.vec, p.chunks, true);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;

@@ -1,4 +1,14 @@
-// Device-side helpers shared by the xtvxy kernels (wavefront reductions, loads).
+// Device-side helpers shared by the xtvxy kernels: cross-lane sums built from
+// gfx950 DPP and permlane-swap instructions, and row-chunk loads.
+//
+// Lane movements used (wave64):
+//   DPP quad_perm [1,0,3,2] / [2,3,0,1]  lane i reads lane i^1 / i^2
+//   DPP row_half_mirror                  lane i reads lane 7-i within its 8-lane half-row
+//   DPP row_mirror                       lane i reads lane 15-i within its 16-lane row
+//   DPP row_ror:k                        lane i reads lane (i+k) mod 16 within its row
+//   v_permlane16_swap(x, y)              -> {x r0, y r0, x r2, y r2}, {x r1, y r1, x r3, y r3}
+//   v_permlane32_swap(x, y)              -> {x lo, y lo}, {x hi, y hi}
+// (r0..r3 are the 16-lane rows, lo/hi the 32-lane halves of a register.)
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,32 +19,99 @@ namespace xtvxy {
 
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-// Sum over aligned groups of `width` lanes (power of two, <= 64) of a wavefront,
-// by a butterfly of lane exchanges; every lane of a group ends with the same
-// (bitwise identical) group total.
+namespace dpp {
+constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;
+constexpr int kMirror = 0x140;
+constexpr int kRor1 = 0x121, kRor2 = 0x122, kRor4 = 0x124, kRor8 = 0x128;
+}  // namespace dpp
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// x of lanes i and i^16 (aligned 32-lane halves), summed; same value in both lanes.
+__device__ __forceinline__ float add_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// x of lanes i and i^32, summed; same value in both lanes.
+__device__ __forceinline__ float add_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over aligned groups of `width` lanes (power of two, <= 64); every lane of a
+// group ends with the same, bitwise identical, total.
 __device__ __forceinline__ float group_sum(float x, int width) {
-  for (int off = width >> 1; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  if (width >= 2) x += dpp_mov<dpp::kXor1>(x);
+  if (width >= 4) x += dpp_mov<dpp::kXor2>(x);
+  if (width >= 8) x += dpp_mov<dpp::kHalfMirror>(x);
+  if (width >= 16) x += dpp_mov<dpp::kMirror>(x);
+  if (width >= 32) x = add_xor16(x);
+  if (width >= 64) x = add_xor32(x);
   return x;
 }
 
-// `VEC` consecutive floats of row `xr` starting at column `col`, zero past column n.
-// X is streamed exactly once, so the loads carry the non-temporal hint.
-template <int VEC>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ xr, int64_t col, int64_t n,
-                                           float (&o)[VEC]) {
-  if constexpr (VEC == 4) {
-    if (col + 4 <= n) {
-      f4 t = __builtin_nontemporal_load(reinterpret_cast<const f4*>(xr + col));
-      o[0] = t.x;
-      o[1] = t.y;
-      o[2] = t.z;
-      o[3] = t.w;
-    } else {
+// Sum of x over the lanes that share i mod `stride` (stride a power of two <= 64),
+// i.e. over the 64/stride "slots" of a wavefront; every lane gets its class total.
+__device__ __forceinline__ float slot_sum(float x, int stride) {
+  if (stride <= 1) x += dpp_mov<dpp::kRor1>(x);
+  if (stride <= 2) x += dpp_mov<dpp::kRor2>(x);
+  if (stride <= 4) x += dpp_mov<dpp::kRor4>(x);
+  if (stride <= 8) x += dpp_mov<dpp::kRor8>(x);
+  if (stride <= 16) x = add_xor16(x);
+  if (stride <= 32) x = add_xor32(x);
+  return x;
+}
+
+// Eight per-lane partial sums s[0..7] of eight rows that each span the whole
+// wavefront, reduced together: the returned value in lane i is the complete sum
+// of row i >> 3. 18 lane-exchange instructions for eight rows instead of six
+// exchanges per row.
+__device__ __forceinline__ float wave_sum8_transposed(const float (&s)[8]) {
+  float a[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) o[k] = (col + k < n) ? __builtin_nontemporal_load(xr + col + k) : 0.0f;
-    }
+  for (int k = 0; k < 4; ++k) {  // halves: lanes 0-31 keep row k, lanes 32-63 row k+4
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(s[k]), __float_as_uint(s[k + 4]), false, false);
+    a[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  float b[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {  // 16-lane rows: r0 keeps row k, r1 row k+2, r2 row k+4, r3 row k+6
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a[k]), __float_as_uint(a[k + 2]), false, false);
+    b[k] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  const bool upper8 = (threadIdx.x & 8) != 0;  // 8-lane half of a row: the lower keeps b0, the upper b1
+  const float keep = upper8 ? b[1] : b[0];
+  const float send = upper8 ? b[0] : b[1];
+  float c = keep + dpp_mov<dpp::kRor8>(send);
+  c += dpp_mov<dpp::kXor1>(c);
+  c += dpp_mov<dpp::kXor2>(c);
+  c += dpp_mov<dpp::kHalfMirror>(c);
+  return c;
+}
+
+// `VEC` consecutive floats of row `xr` starting at column `col` when `ok`, else zeros.
+// With VEC == 4 the caller guarantees that a chunk lies entirely inside or outside
+// the row (n % 4 == 0). The address is clamped instead of branched around, so the
+// load is issued unconditionally and the result selected. X is streamed exactly once:
+// the loads carry the non-temporal hint.
+template <int VEC>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ xr, int64_t col, bool ok, float (&o)[VEC]) {
+  const int64_t c = ok ? col : 0;
+  if constexpr (VEC == 4) {
+    const f4 t = __builtin_nontemporal_load(reinterpret_cast<const f4*>(xr + c));
+    o[0] = ok ? t.x : 0.0f;
+    o[1] = ok ? t.y : 0.0f;
+    o[2] = ok ? t.z : 0.0f;
+    o[3] = ok ? t.w : 0.0f;
   } else {
-    o[0] = (col < n) ? __builtin_nontemporal_load(xr + col) : 0.0f;
+    const float t = __builtin_nontemporal_load(xr + c);
+    o[0] = ok ? t : 0.0f;
   }
 }
 

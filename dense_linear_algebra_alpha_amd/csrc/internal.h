@@ -30,9 +30,8 @@ struct DenseArgs {
   int64_t rows_per_unit;
   int32_t lanes_per_row;
   int32_t group;      // group-row path: workgroups per row
-  float* xchg;        // group-row path: [groups][2][group][kBlockRowsInFlight] partial dots
-  uint32_t* counters; // group-row path: [groups] arrival counters (zeroed before launch)
-  uint32_t* error;    // group-row path: set when a barrier wait gives up
+  void* xchg;         // group-row path: [groups][2][group][kBlockRowsInFlight] 64-bit tagged slots (zeroed)
+  uint32_t* error;    // group-row path: set when a wait for the other members gives up
 };
 
 // Arguments of the CSR fused kernels.
@@ -89,7 +88,7 @@ xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, cons
 // Workspace layout of a dense plan.
 struct DenseWorkspace {
   size_t partial_off, partial_rows;  // partial sums [partial_rows][n]
-  size_t xchg_off, counters_off, error_off;
+  size_t xchg_off, error_off;  // group-row path only
   size_t total;
 };
 DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p);

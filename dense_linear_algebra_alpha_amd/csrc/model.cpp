@@ -19,7 +19,8 @@
 // coarsening factor rows_per_unit = ceil(m / units). More workgroups hide
 // more latency but write more partial n-vectors; the model trades the two.
 // The constants are calibrated on MI355X: a plain streaming read sustains
-// about 0.88 of the 8 TB/s peak, and about 2 us of load latency has to be covered.
+// about 0.88 of the 8 TB/s peak, and the fused kernels reach it once about
+// 128 KiB of loads are in flight per CU, i.e. about 4.5 us of latency under load.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -30,7 +31,7 @@ namespace xtvxy {
 namespace {
 
 constexpr double kSustained = 0.88;     // sustained fraction of peak HBM bandwidth (streaming read)
-constexpr double kLatency = 2.0e-6;     // seconds of memory latency that loads in flight must cover
+constexpr double kLatency = 4.5e-6;     // seconds of loaded-memory latency that loads in flight must cover
 constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
 
@@ -59,8 +60,7 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
     w.partial_rows = (size_t)groups;
     w.partial_off = 0;
     w.xchg_off = align_up(w.partial_off + (size_t)groups * n * sizeof(float));
-    w.counters_off = align_up(w.xchg_off + (size_t)groups * 2 * p.group * kBlockRowsInFlight * sizeof(float));
-    w.error_off = align_up(w.counters_off + (size_t)groups * sizeof(uint32_t));
+    w.error_off = align_up(w.xchg_off + (size_t)groups * 2 * p.group * kBlockRowsInFlight * sizeof(uint64_t));
     w.total = align_up(w.error_off + sizeof(uint32_t));
   } else {
     w.partial_rows = (size_t)p.grid;
@@ -83,6 +83,7 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
   (void)ldx;
   if (p->block_threads != kBlock || (p->vec != 1 && p->vec != 4) || p->grid <= 0 || p->grid > INT32_MAX)
     return XTVXY_ERROR_INVALID_VALUE;
+  if (p->vec == 4 && n % 4 != 0) return XTVXY_ERROR_INVALID_VALUE;  // 16-byte chunks never straddle the row end
   switch (p->kernel) {
     case XTVXY_DENSE_WAVE_ROWS: {
       const int lpr = p->lanes_per_row;
@@ -100,7 +101,8 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
         p->group = 1;
         if (slice < n) return XTVXY_ERROR_INVALID_VALUE;
       } else {
-        if (p->group < 1 || (int64_t)p->group * slice < n || p->grid % p->group != 0)
+        if (p->group < 1 || p->group > kBlock / kBlockRowsInFlight || (int64_t)p->group * slice < n ||
+            p->grid % p->group != 0)
           return XTVXY_ERROR_INVALID_VALUE;
       }
       p->lanes_per_row = kBlock;
@@ -121,7 +123,7 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
                          xtvxy_launch_params* p) {
   std::memset(p, 0, sizeof(*p));
   p->block_threads = kBlock;
-  p->vec = (aligned16 && ldx % 4 == 0) ? 4 : 1;
+  p->vec = (aligned16 && ldx % 4 == 0 && n % 4 == 0) ? 4 : 1;
   const int vec = p->vec;
   double inflight_per_wg;  // bytes of X a workgroup has requested before it needs the first of them
   int64_t rows_per_step;   // rows a workgroup (or group) consumes per step
