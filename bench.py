@@ -83,8 +83,7 @@ def kernel_sources_hash(kind: str) -> str:
 def kernel_name(plan, kind: str) -> str:
     import dense_linear_algebra_alpha_amd as xt
     names = {xt.XTVXY_DENSE_WAVE_ROWS: "dense_wave_rows", xt.XTVXY_DENSE_BLOCK_ROWS: "dense_block_rows",
-             xt.XTVXY_DENSE_GROUP_ROWS: "dense_block_rows(group)", xt.XTVXY_CSR_LDS_TILES: "csr_tiles(lds)",
-             xt.XTVXY_CSR_GLOBAL_TILES: "csr_tiles(global)"}
+             xt.XTVXY_DENSE_GROUP_ROWS: "dense_block_rows(group)", xt.XTVXY_CSR_TILES: "csr_fused"}
     return names.get(plan.kernel, "kernel%d" % plan.kernel)
 
 
@@ -131,7 +130,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle runs for cpu_baseline")
     ap.add_argument("--fused-only", action="store_true", help="time the fused path only (for profilers)")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
+                         "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    if args.calibration_copy:
+        import torch
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "repeats": 3}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -19,9 +19,8 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (XTVXY_CSR_GLOBAL_TILES, XTVXY_CSR_LDS_TILES, XTVXY_DENSE_BLOCK_ROWS,  # noqa: F401
-                   XTVXY_DENSE_GROUP_ROWS, XTVXY_DENSE_WAVE_ROWS, XtvxyError, xtvxy_device_info,
-                   xtvxy_launch_params)
+from ._abi import (XTVXY_CSR_TILES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
+                   XTVXY_DENSE_WAVE_ROWS, XtvxyError, xtvxy_device_info, xtvxy_launch_params)
 
 __all__ = [
     "xtvxy_get_device_info", "xtvxy_dense_f32_plan", "xtvxy_dense_f32_plan_complete", "xtvxy_csr_f32_plan",

@@ -24,8 +24,7 @@ XTVXY_ERROR_LIBRARY = 7
 XTVXY_DENSE_WAVE_ROWS = 1
 XTVXY_DENSE_BLOCK_ROWS = 2
 XTVXY_DENSE_GROUP_ROWS = 3
-XTVXY_CSR_LDS_TILES = 11
-XTVXY_CSR_GLOBAL_TILES = 12
+XTVXY_CSR_TILES = 11
 
 
 class xtvxy_device_info(ctypes.Structure):
@@ -39,6 +38,7 @@ class xtvxy_launch_params(ctypes.Structure):
                 ("lanes_per_row", ctypes.c_int32), ("chunks", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("rows_per_unit", ctypes.c_int64),
                 ("entries_per_thread", ctypes.c_int32), ("lds_window", ctypes.c_int32),
+                ("y_in_lds", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("predicted_seconds", ctypes.c_double)]
 
     def as_dict(self) -> dict:

@@ -3,7 +3,8 @@
 // hierarchically) and the small helper kernels of the library.
 //
 // aggregate: out_j = alpha * S_j + beta * z_j with S_j the sum of the fused
-// kernel's per-workgroup partials. Each 1024-thread workgroup owns 64 columns;
+// kernel's per-workgroup partials (plus, for the CSR path, a global accumulator
+// of the columns outside the LDS window). Each 1024-thread workgroup owns 64 columns;
 // 16 thread rows each sum a strided subset of the partials in fp64, and the 16
 // results are combined in a fixed order, so the result is bitwise reproducible.
 // The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
@@ -17,15 +18,17 @@ namespace {
 constexpr int kAggCols = 64, kAggRows = 16;
 
 __global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const float* __restrict__ partial,
-                                                                        int64_t rows, int64_t n, float alpha,
-                                                                        float beta, const float* z, float* out) {
+                                                                        int64_t rows, int64_t ldp,
+                                                                        const float* __restrict__ acc, int64_t n,
+                                                                        float alpha, float beta, const float* z,
+                                                                        float* out) {
   __shared__ double sh[kAggRows][kAggCols];
   const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
   const int64_t j = (int64_t)blockIdx.x * kAggCols + tx;
   double s = 0.0;
-  if (j < n) {
+  if (j < ldp) {
 #pragma unroll 8
-    for (int64_t r = ty; r < rows; r += kAggRows) s += (double)partial[r * n + j];
+    for (int64_t r = ty; r < rows; r += kAggRows) s += (double)partial[r * ldp + j];
   }
   sh[ty][tx] = s;
   __syncthreads();
@@ -33,6 +36,7 @@ __global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const fl
     double t = sh[0][tx];
 #pragma unroll
     for (int k = 1; k < kAggRows; ++k) t += sh[k][tx];
+    if (acc) t += (double)acc[j];
     double o = (double)alpha * t;
     if (beta != 0.0f) o += (double)beta * (double)z[j];
     out[j] = (float)o;
@@ -75,12 +79,12 @@ unsigned grid_for(int64_t count, int block) {
 
 }  // namespace
 
-hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t n, float alpha, float beta,
-                            const float* z, float* out, hipStream_t s) {
+hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
+                            float alpha, float beta, const float* z, float* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + kAggCols - 1) / kAggCols);
-  hipLaunchKernelGGL(aggregate_kernel, dim3(grid), dim3(kAggCols * kAggRows), 0, s, partial, rows, n, alpha,
-                     beta, z, out);
+  hipLaunchKernelGGL(aggregate_kernel, dim3(grid), dim3(kAggCols * kAggRows), 0, s, partial, rows, ldp, acc, n,
+                     alpha, beta, z, out);
   return hipGetLastError();
 }
 

@@ -34,8 +34,9 @@ xtvxy_status device_info(int device, xtvxy_device_info* out) {
     d.l2_bytes = prop.l2CacheSize;
     // gfx94x/gfx95x parts group 32 (or 38/40) CUs per XCD; the count only steers tile placement
     d.xcds = prop.multiProcessorCount >= 64 ? prop.multiProcessorCount / 32 : 1;
-    // memoryClockRate is in kHz; double data rate over a bus of memoryBusWidth bits
-    d.hbm_bytes_per_s = 2.0 * prop.memoryClockRate * 1e3 * (prop.memoryBusWidth / 8.0);
+    // memoryClockRate is in kHz; HBM3/HBM3E parts transfer 4 bits per pin per reported clock
+    // (MI300X: 1.3 GHz x 4 x 1024 B = 5.3 TB/s; MI355X: 2.0 GHz x 4 x 1024 B = 8.2 TB/s)
+    d.hbm_bytes_per_s = 4.0 * prop.memoryClockRate * 1e3 * (prop.memoryBusWidth / 8.0);
     if (d.hbm_bytes_per_s <= 0) d.hbm_bytes_per_s = 8.0e12;
     g_info[device] = d;
     g_info_valid[device] = true;
@@ -193,7 +194,7 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64
   hipError_t e = launch_dense(a, plan, stream);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, alpha, beta, z, out, stream);
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, nullptr, n, alpha, beta, z, out, stream);
   return launch_status(e);
 }
 
@@ -223,12 +224,14 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   a.values = values;
   a.v = v;
   a.y = y;
-  a.partial = reinterpret_cast<float*>(static_cast<char*>(ws) + w.partial_off);
-  a.entries_per_thread = plan.entries_per_thread;
+  char* base = static_cast<char*>(ws);
+  a.partial = reinterpret_cast<float*>(base + w.partial_off);
   a.lds_window = plan.lds_window;
+  a.acc = plan.lds_window < n ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
+  a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
   hipError_t e;
-  if (plan.kernel == XTVXY_CSR_GLOBAL_TILES) {
-    e = launch_zero(a.partial, (size_t)n * sizeof(float), stream);
+  if (a.acc) {
+    e = launch_zero(a.acc, (size_t)n * sizeof(float), stream);
     if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   }
   const hipEvent_t before = g_before_main, after = g_after_main;
@@ -236,7 +239,7 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   e = launch_csr(a, plan, stream);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, alpha, beta, z, out, stream);
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, plan.lds_window, a.acc, n, alpha, beta, z, out, stream);
   return launch_status(e);
 }
 

@@ -1,4 +1,4 @@
-// Fused CSR kernels for out = alpha * X^T (v .* (X y)) + beta * z.
+// Fused CSR kernel for out = alpha * X^T (v .* (X y)) + beta * z.
 //
 // "On optimizing machine learning workloads via kernel fusion" (abstract): one
 // fused kernel with techniques specific to sparse X; each stored entry is
@@ -7,28 +7,45 @@
 //
 // Work split: workgroup w owns the rows whose first entry lies in
 // [w q, (w + 1) q), q = ceil(nnz / grid), so every workgroup streams about the
-// same number of entries (found by a 64-way search of row_ptr by one
-// wavefront). A workgroup walks its rows in tiles of at most
-// 256 * entries_per_thread entries and kCsrRowsPerTile rows:
-//   1. row_ptr of the tile's rows is staged in LDS;
-//   2. each thread loads a run of consecutive entries (value, column), gathers
-//      y[column], and adds its per-row runs of products into LDS dots with LDS
-//      atomics (t_i = sum of the row's entries times y);
+// same number of entries (one wavefront finds the two boundaries with a 64-way
+// search of row_ptr). The workgroup then walks its rows in tiles of at most
+// 256 rows and 256 * K entries:
+//   1. row_ptr of up to 256 rows sits in LDS, and the tile is the longest run
+//      of whole rows whose entries fit;
+//   2. thread t holds the K consecutive entries starting at base + K t (base =
+//      the tile's first entry rounded down to a multiple of 4), loaded as
+//      16-byte vectors of values and of column indices, gathers y[column] (from
+//      an LDS copy of y when it is small), finds each entry's row from the next
+//      K row boundaries, and adds its per-row runs of products into the tile's
+//      dots in LDS (t_i);
 //   3. t_i becomes u_i = v_i t_i;
-//   4. each thread scatters u_row * value for the entries still in its registers:
-//      into an LDS copy of the output (LDS path: the workgroup's partial output,
-//      written to the workspace at the end and summed by aggregate.hip), or
-//      straight into a global fp32 accumulator with hardware float atomics
-//      (global path, any n).
+//   4. every entry still in registers is scattered as u_row * value: columns
+//      below the LDS window W accumulate in the workgroup's LDS copy of the
+//      output (written to the workspace at the end and summed across
+//      workgroups by aggregate.hip), columns at or above W go to a global fp32
+//      accumulator with hardware float atomics.
+// The LDS accumulations (steps 2 and 4) are compare-and-swap float adds: on gfx950
+// they retire several times faster than the native LDS float atomic.
 // A row with more entries than a tile is handled by the whole workgroup in two
 // sweeps over its entries (dot, then scatter).
+//
+// Software pipeline: while a tile is processed, the next tile's row_ptr, v and
+// entries (which start where this tile ends) are already loading. Every one of
+// these loads is issued unconditionally (addresses clamped, results selected),
+// and the y gathers of a tile are issued before the prefetch of the next, so
+// the compiler can wait for exactly the values it needs: the counter of
+// outstanding vector-memory operations completes in order, and a conditional
+// load anywhere in between forces a wait for everything.
 #include "device_util.h"
 #include "internal.h"
 
 namespace xtvxy {
 namespace {
 
-constexpr int kMaxEntries = 8;  // entries per thread per tile
+constexpr int kTileRows = kBlock;  // rows a tile stages: one row_ptr per thread
+
+typedef __attribute__((address_space(1))) float global_float;
+typedef int32_t i4 __attribute__((ext_vector_type(4)));
 
 // Smallest r in [0, m] with rp[r] >= target (m when none), by one full wavefront.
 __device__ int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64_t m, int64_t target) {
@@ -53,34 +70,50 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64_t m, i
   return min(lo + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi);
 }
 
-template <bool LDS_OUT>
-__device__ __forceinline__ void scatter_add(const CsrArgs& a, float* out_s, int32_t col, float c) {
-  if constexpr (LDS_OUT) {
-    atomicAdd(out_s + col, c);
+// Scatter-add of one product. Both atomics name their address space explicitly: written as
+// plain atomicAdd on float*, the compiler merges the two branches into a single flat atomic,
+// which is slower and makes every later wait cover outstanding loads.
+__device__ __forceinline__ void scatter(const CsrArgs& a, float* out_s, int32_t col, float c) {
+  if (col < a.lds_window) {
+    lds_add_f32(out_s + col, c);
   } else {
-    unsafeAtomicAdd(a.partial + col, c);
+    __hip_atomic_fetch_add((global_float*)a.acc + col, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-template <bool LDS_OUT>
-__global__ __launch_bounds__(kBlock) void csr_tiles(CsrArgs a) {
-  constexpr int RM = kCsrRowsPerTile;
-  __shared__ int32_t rp_s[RM + 1];
-  __shared__ float t_s[RM];
+// The loads one tile needs, held in registers while the previous tile is processed.
+template <int K>
+struct TileRegs {
+  float val[K];
+  int32_t col[K];
+  int32_t rp;      // row_ptr[r + tid] (the tile's rows start at r)
+  int32_t rp_end;  // row_ptr[r + kTileRows] (used by thread 0 when the tile stages 256 rows)
+  float v;         // v[r + tid]
+};
+
+template <int K, bool YLDS, bool HAS_V, bool ALIGNED>
+__global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
+  static_assert(K % 4 == 0, "entries are loaded as 16-byte vectors");
+  __shared__ int32_t rp_s[2][kTileRows + 1];
+  __shared__ float t_s[kTileRows];
   __shared__ float lred[kWaves];
   __shared__ int64_t range_s[2];
-  extern __shared__ float out_s[];
+  extern __shared__ float dyn[];
+  float* out_s = dyn;                 // [lds_window]
+  float* y_s = dyn + a.lds_window;    // [n] when YLDS
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int K = a.entries_per_thread;
-  const int T = kBlock * K;
+  constexpr int T = kBlock * K;
+  const int64_t nnz = a.nnz;
 
-  if constexpr (LDS_OUT) {
-    for (int64_t j = tid; j < a.n; j += kBlock) out_s[j] = 0.0f;
+  for (int64_t j = tid; j < a.lds_window; j += kBlock) out_s[j] = 0.0f;
+  if constexpr (YLDS) {
+    for (int64_t j = tid; j < a.n; j += kBlock) y_s[j] = a.y[j];
   }
   if (wave == 0) {
-    const int64_t q = (a.nnz + gridDim.x - 1) / gridDim.x;
+    const int64_t q = (nnz + gridDim.x - 1) / gridDim.x;
     const int64_t rb = wave_lower_bound(a.row_ptr, a.m, (int64_t)blockIdx.x * q);
-    const int64_t re = (blockIdx.x + 1 == gridDim.x) ? a.m : wave_lower_bound(a.row_ptr, a.m, (int64_t)(blockIdx.x + 1) * q);
+    const int64_t re =
+        (blockIdx.x + 1 == gridDim.x) ? a.m : wave_lower_bound(a.row_ptr, a.m, (int64_t)(blockIdx.x + 1) * q);
     if (lane == 0) {
       range_s[0] = rb;
       range_s[1] = re;
@@ -88,121 +121,250 @@ __global__ __launch_bounds__(kBlock) void csr_tiles(CsrArgs a) {
   }
   __syncthreads();
   const int64_t rb = range_s[0], re = range_s[1];
-
-  for (int64_t ra = rb; ra < re;) {
-    const int cnt = (int)min((int64_t)RM, re - ra);
-    __syncthreads();  // the previous tile is done with rp_s, t_s, lred
-    for (int k = tid; k <= cnt; k += kBlock) rp_s[k] = a.row_ptr[ra + k];
-    __syncthreads();
-    const int32_t pa = rp_s[0];
-    int j;  // rows [ra, ra + j) form the tile: the largest j with rp_s[j] - pa <= T
-    {
-      int lo = 0, hi = cnt;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (rp_s[mid] - pa <= T) lo = mid; else hi = mid - 1;
-      }
-      j = lo;
+  if (rb >= re) {
+    if (a.lds_window > 0) {
+      float* dst = a.partial + (int64_t)blockIdx.x * a.lds_window;
+      for (int64_t c = tid; c < a.lds_window; c += kBlock) dst[c] = 0.0f;
     }
-    if (j == 0) {
-      // row ra alone holds more than T entries: dot sweep, then scatter sweep
-      const int32_t p0 = rp_s[0], p1 = rp_s[1];
+    return;
+  }
+  const float* ysrc = YLDS ? y_s : a.y;
+
+  // Loads for the tile whose rows start at r and whose entries start at `first_entry`;
+  // every load is unconditional (clamped address), entries past the arrays read as zero.
+  // Only used when nnz >= 4 (the vector loads then never leave the arrays).
+  const int64_t nnz_full = nnz & ~(int64_t)3;  // entries in whole aligned quads
+  auto issue = [&](int64_t r, int64_t first_entry, TileRegs<K>& g) {
+    g.rp = a.row_ptr[min(r + tid, re)];
+    g.rp_end = a.row_ptr[min(r + (int64_t)kTileRows, re)];
+    g.v = HAS_V ? a.v[min(r + tid, re - 1)] : 1.0f;
+    const int64_t e0 = (first_entry & ~(int64_t)3) + (int64_t)tid * K;
+    // the last partial quad (nnz % 4 entries), read by every lane and used by the one lane whose
+    // quad starts at nnz_full
+    float tv[3];
+    int32_t tc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      const int64_t p = min(nnz_full + q, nnz - 1);
+      tv[q] = a.values[p];
+      tc[q] = a.col_idx[p];
+    }
+#pragma unroll
+    for (int k = 0; k < K; k += 4) {
+      const int64_t e = e0 + k;
+      const int64_t ec = min(e, nnz_full - 4);
+      float xv[4];
+      int32_t xc[4];
+      if constexpr (ALIGNED) {
+        const f4 vv = *reinterpret_cast<const f4*>(a.values + ec);
+        const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + ec);
+        xv[0] = vv.x; xv[1] = vv.y; xv[2] = vv.z; xv[3] = vv.w;
+        xc[0] = cc.x; xc[1] = cc.y; xc[2] = cc.z; xc[3] = cc.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          xv[q] = a.values[ec + q];
+          xc[q] = a.col_idx[ec + q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool full = e < nnz_full;
+        const bool tail = (e == nnz_full) && (e + q < nnz);
+        g.val[k + q] = full ? xv[q] : (tail && q < 3 ? tv[q < 3 ? q : 0] : 0.0f);
+        g.col[k + q] = full ? xc[q] : (tail && q < 3 ? tc[q < 3 ? q : 0] : 0);
+      }
+    }
+  };
+  // Small matrices (nnz < 4): element loads, guarded.
+  auto issue_small = [&](int64_t r, int64_t first_entry, TileRegs<K>& g) {
+    g.rp = a.row_ptr[min(r + tid, re)];
+    g.rp_end = a.row_ptr[min(r + (int64_t)kTileRows, re)];
+    g.v = HAS_V ? a.v[min(r + tid, re - 1)] : 1.0f;
+    const int64_t e0 = (first_entry & ~(int64_t)3) + (int64_t)tid * K;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const bool in = e0 + k < nnz;
+      g.val[k] = in ? a.values[e0 + k] : 0.0f;
+      g.col[k] = in ? a.col_idx[e0 + k] : 0;
+    }
+  };
+  auto stage = [&](int b, int cnt, const TileRegs<K>& g) {
+    if (tid <= cnt) rp_s[b][tid] = g.rp;
+    if (tid == 0 && cnt == kTileRows) rp_s[b][kTileRows] = g.rp_end;
+  };
+  // rows [ra, ra + j) of buffer b whose entries end within [base, base + T); the predicate is
+  // monotone in the thread index, so the count is the length of the run
+  auto count_rows = [&](int b, int cnt) -> int {
+    const int64_t base = (int64_t)rp_s[b][0] & ~(int64_t)3;
+    return __syncthreads_count(tid < cnt && (int64_t)rp_s[b][tid + 1] - base <= T);
+  };
+
+  TileRegs<K> ga, gb;
+  int buf = 0;
+  int64_t ra = rb;
+  int cnt = (int)min((int64_t)kTileRows, re - ra);
+  {
+    const int64_t p0 = a.row_ptr[ra];
+    if (nnz >= 4) issue(ra, p0, ga); else issue_small(ra, p0, ga);
+  }
+  stage(0, cnt, ga);
+  t_s[tid] = 0.0f;
+  __syncthreads();
+  int j = count_rows(0, cnt);
+
+  auto step = [&](TileRegs<K>& g, TileRegs<K>& gn) -> bool {
+    const int32_t* rps = rp_s[buf];
+    const int32_t pa = rps[0];
+    const int64_t base = (int64_t)pa & ~(int64_t)3;
+    const bool long_row = (j == 0);  // row ra alone holds more entries than a tile
+    const int32_t pb = long_row ? rps[1] : rps[j];
+    const int64_t ra_next = ra + (long_row ? 1 : j);
+    const bool more = ra_next < re;
+    const int cnt_next = more ? (int)min((int64_t)kTileRows, re - ra_next) : 0;
+    const int64_t e0 = base + (int64_t)tid * K;
+
+    // (a) gathers of y for this tile's entries, before anything of the next tile is issued
+    float yv[K];
+    if (!long_row) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) yv[k] = ysrc[g.col[k]];
+    }
+    // (b) the next tile's row_ptr, v and entries (they start where this tile ends)
+    if (nnz >= 4) issue(min(ra_next, re - 1), pb, gn); else issue_small(min(ra_next, re - 1), pb, gn);
+
+    if (long_row) {
+      // the whole workgroup sweeps the row twice: dot, then scatter
       float s = 0.0f;
-      for (int64_t p = p0 + tid; p < p1; p += kBlock) s = fmaf(a.values[p], a.y[a.col_idx[p]], s);
+      for (int64_t p = pa + tid; p < pb; p += kBlock) s = fmaf(a.values[p], ysrc[a.col_idx[p]], s);
       s = group_sum(s, 64);
       if (lane == 0) lred[wave] = s;
       __syncthreads();
       float t = lred[0];
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) t += lred[w];
-      const float u = (a.v ? a.v[ra] : 1.0f) * t;
-      for (int64_t p = p0 + tid; p < p1; p += kBlock) scatter_add<LDS_OUT>(a, out_s, a.col_idx[p], u * a.values[p]);
-      ra += 1;
-      continue;
-    }
-    const int32_t pb = rp_s[j];
-    for (int k = tid; k < j; k += kBlock) t_s[k] = 0.0f;
-    __syncthreads();
-
-    const int32_t e0 = pa + tid * K;
-    float val[kMaxEntries];
-    int32_t col[kMaxEntries];
-    int row0 = 0;
-    if (e0 < pb) {
-      int lo = 0, hi = j - 1;  // row of entry e0: the largest r with rp_s[r] <= e0
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (rp_s[mid] <= e0) lo = mid; else hi = mid - 1;
-      }
-      row0 = lo;
+      const float u = (HAS_V ? a.v[ra] : 1.0f) * t;
+      for (int64_t p = pa + tid; p < pb; p += kBlock) scatter(a, out_s, a.col_idx[p], u * a.values[p]);
+    } else {
+      // (c) the row of each entry: one binary search for the first, then the next K row
+      // boundaries at once; the row of entry e is that row plus the number of those
+      // boundaries <= e (only runs of more than K boundaries, i.e. of empty rows, walk)
+      const int64_t first = max(e0, (int64_t)pa);
+      const bool mine = first < min(e0 + K, (int64_t)pb);
+      int rk[K];
+      bool ok[K];
 #pragma unroll
-      for (int k = 0; k < kMaxEntries; ++k) {
-        const int32_t e = e0 + k;
-        const bool ok = k < K && e < pb;
-        val[k] = ok ? __builtin_nontemporal_load(a.values + e) : 0.0f;
-        col[k] = ok ? __builtin_nontemporal_load(a.col_idx + e) : 0;
+      for (int k = 0; k < K; ++k) {
+        ok[k] = (e0 + k >= pa) && (e0 + k < pb);
+        rk[k] = 0;
       }
-      int r = row0;
-      float run = 0.0f;
-      bool any = false;
+      if (mine) {
+        int lo = 0, hi = j - 1;  // the largest r with rps[r] <= first
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if ((int64_t)rps[mid] <= first) lo = mid; else hi = mid - 1;
+        }
+        const int r0 = lo;
+        int32_t bnd[K];
 #pragma unroll
-      for (int k = 0; k < kMaxEntries; ++k) {
-        const int32_t e = e0 + k;
-        if (k < K && e < pb) {
-          while (e >= rp_s[r + 1]) {
-            if (any) atomicAdd(t_s + r, run);
-            run = 0.0f;
-            any = false;
-            ++r;
+        for (int i = 0; i < K; ++i) bnd[i] = rps[min(r0 + 1 + i, j)];
+        const int64_t last = min(e0 + K, (int64_t)pb) - 1;
+        if (r0 + K >= j || (int64_t)bnd[K - 1] > last) {
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            int c = 0;
+#pragma unroll
+            for (int i = 0; i < K; ++i) c += ((int64_t)bnd[i] <= e0 + k) ? 1 : 0;
+            rk[k] = r0 + c;
           }
-          run = fmaf(val[k], a.y[col[k]], run);
-          any = true;
-        }
-      }
-      if (any) atomicAdd(t_s + r, run);
-    }
-    __syncthreads();
-    for (int k = tid; k < j; k += kBlock) t_s[k] = (a.v ? a.v[ra + k] : 1.0f) * t_s[k];
-    __syncthreads();
-    if (e0 < pb) {
-      int r = row0;
+        } else {
+          int r = r0;
 #pragma unroll
-      for (int k = 0; k < kMaxEntries; ++k) {
-        const int32_t e = e0 + k;
-        if (k < K && e < pb) {
-          while (e >= rp_s[r + 1]) ++r;
-          scatter_add<LDS_OUT>(a, out_s, col[k], t_s[r] * val[k]);
+          for (int k = 0; k < K; ++k) {
+            if (ok[k])
+              while (e0 + k >= rps[r + 1]) ++r;
+            rk[k] = r;
+          }
         }
+        // per-row runs of products, one LDS atomic per run
+        float run = 0.0f;
+        int rprev = -1;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          if (ok[k]) {
+            const float p = g.val[k] * yv[k];
+            if (rk[k] != rprev) {
+              if (rprev >= 0) lds_add_f32(t_s + rprev, run);
+              run = p;
+              rprev = rk[k];
+            } else {
+              run += p;
+            }
+          }
+        }
+        if (rprev >= 0) lds_add_f32(t_s + rprev, run);
+      }
+      __syncthreads();
+      if (tid < j) t_s[tid] = g.v * t_s[tid];
+      __syncthreads();
+      if (mine) {
+#pragma unroll
+        for (int k = 0; k < K; ++k)
+          if (ok[k]) scatter(a, out_s, g.col[k], t_s[rk[k]] * g.val[k]);
       }
     }
-    ra += j;
+    // the long-row path reads v and the entries itself; its prefetched values for rows after
+    // it are the ones issued above with r = ra_next, so nothing is lost
+    if (more) stage(buf ^ 1, cnt_next, gn);
+    __syncthreads();  // this tile is done with rp_s[buf], t_s and lred; the next row_ptr is staged
+    if (!more) return false;
+    ra = ra_next;
+    buf ^= 1;
+    cnt = cnt_next;
+    t_s[tid] = 0.0f;
+    j = count_rows(buf, cnt);
+    return true;
+  };
+
+  while (step(ga, gb) && step(gb, ga)) {
   }
 
-  if constexpr (LDS_OUT) {
+  if (a.lds_window > 0) {
     __syncthreads();
-    float* dst = a.partial + (int64_t)blockIdx.x * a.n;
-    for (int64_t c = tid; c < a.n; c += kBlock) dst[c] = out_s[c];
+    float* dst = a.partial + (int64_t)blockIdx.x * a.lds_window;
+    for (int64_t c = tid; c < a.lds_window; c += kBlock) dst[c] = out_s[c];
   }
+}
+
+template <int K, bool YLDS, bool HAS_V, bool ALIGNED>
+hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  const size_t lds = ((size_t)a.lds_window + (YLDS ? (size_t)a.n : 0)) * sizeof(float);
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YLDS, HAS_V, ALIGNED>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((csr_fused<K, YLDS, HAS_V, ALIGNED>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int K>
+hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  const bool yl = p.y_in_lds != 0, hv = a.v != nullptr, al = a.aligned;
+  if (yl) {
+    if (hv) return al ? launch_k<K, true, true, true>(a, p, s) : launch_k<K, true, true, false>(a, p, s);
+    return al ? launch_k<K, true, false, true>(a, p, s) : launch_k<K, true, false, false>(a, p, s);
+  }
+  if (hv) return al ? launch_k<K, false, true, true>(a, p, s) : launch_k<K, false, true, false>(a, p, s);
+  return al ? launch_k<K, false, false, true>(a, p, s) : launch_k<K, false, false, false>(a, p, s);
 }
 
 }  // namespace
 
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX) return hipErrorInvalidValue;
-  if (p.entries_per_thread < 1 || p.entries_per_thread > kMaxEntries) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)p.grid), block(kBlock);
-  switch (p.kernel) {
-    case XTVXY_CSR_LDS_TILES: {
-      const size_t lds = (size_t)a.n * sizeof(float);
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&csr_tiles<true>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(csr_tiles<true>, grid, block, lds, s, a);
-      return hipGetLastError();
-    }
-    case XTVXY_CSR_GLOBAL_TILES:
-      hipLaunchKernelGGL(csr_tiles<false>, grid, block, 0, s, a);
-      return hipGetLastError();
+  if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES)
+    return hipErrorInvalidValue;
+  switch (p.entries_per_thread) {
+    case 4: return launch_kk<4>(a, p, s);
+    case 8: return launch_kk<8>(a, p, s);
   }
   return hipErrorInvalidValue;
 }

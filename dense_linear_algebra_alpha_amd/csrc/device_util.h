@@ -95,6 +95,25 @@ __device__ __forceinline__ float wave_sum8_transposed(const float (&s)[8]) {
   return c;
 }
 
+typedef __attribute__((address_space(3))) unsigned int lds_uint;
+typedef __attribute__((address_space(3))) float lds_float;
+
+// Atomic fp32 add to an LDS word. On gfx950 the native LDS float atomic (ds_add_f32) retires
+// about 0.33 lanes per clock per CU whatever the address pattern, while a compare-and-swap of
+// the word's bits (ds_cmpst_rtn_b32) sustains about 1.9 lanes per clock on scattered
+// addresses. A compare-and-swap fails when another lane changed the word first, which on
+// skewed (hot-column) patterns happens to most lanes of an instruction and would serialise a
+// retry loop; so there is one attempt, and the lanes that lose it use the native atomic.
+// `p` must point into LDS.
+__device__ __forceinline__ void lds_add_f32(float* p, float v) {
+  lds_uint* w = (lds_uint*)p;  // address-space cast: the word lives in LDS
+  unsigned int expected = *w;
+  if (!__hip_atomic_compare_exchange_strong(w, &expected, __float_as_uint(__uint_as_float(expected) + v),
+                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+    __builtin_amdgcn_ds_faddf((lds_float*)p, v, 0, 0, false);
+  }
+}
+
 // `VEC` consecutive floats of row `xr` starting at column `col` when `ok`, else zeros.
 // With VEC == 4 the caller guarantees that a chunk lies entirely inside or outside
 // the row (n % 4 == 0). The address is clamped instead of branched around, so the

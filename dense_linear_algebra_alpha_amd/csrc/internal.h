@@ -15,7 +15,7 @@ namespace xtvxy {
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
-constexpr int kCsrRowsPerTile = 2048;  // CSR: most rows one tile covers
+constexpr size_t kCsrStaticLds = 3584; // CSR kernel: LDS besides the output window and y (3372 used)
 constexpr size_t kAlign = 256;       // alignment of every workspace region
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -42,19 +42,21 @@ struct CsrArgs {
   const float* values;
   const float* v;
   const float* y;
-  float* partial;     // LDS path: [grid][n]; global path: [n] accumulator (zeroed before launch)
-  int32_t entries_per_thread;
-  int32_t lds_window;
+  float* partial;     // [grid][lds_window] per-workgroup partial sums of output columns [0, lds_window)
+  float* acc;         // [n] global accumulator of columns >= lds_window (zeroed before launch), or null
+  int64_t lds_window;
+  bool aligned;       // values and col_idx are 16-byte aligned: entries load as vectors
 };
 
 // Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first
 // HIP error it meets.
 hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s);
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
-// out[j] = alpha * sum_{r < rows} partial[r * n + j] + (beta != 0 ? beta * z[j] : 0), fp64 sums
-// taken over r in ascending order.
-hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t n, float alpha, float beta,
-                            const float* z, float* out, hipStream_t s);
+// out[j] = alpha * (sum_{r < rows} partial[r * ldp + j] [j < ldp] + acc[j] [acc != null])
+//          + (beta != 0 ? beta * z[j] : 0),
+// in fp64, the partial rows summed in ascending order, rounded once.
+hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
+                            float alpha, float beta, const float* z, float* out, hipStream_t s);
 // out[j] = (beta != 0) ? beta * z[j] : 0
 hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s);
 // p[i] = 0 for i < count (a kernel, so that the call stays graph-capturable)
@@ -94,7 +96,8 @@ struct DenseWorkspace {
 DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p);
 
 struct CsrWorkspace {
-  size_t partial_off, partial_rows;  // LDS path: [grid][n]; global path: one accumulator row
+  size_t partial_off, partial_rows;  // [grid][lds_window]
+  size_t acc_off;                    // [n] accumulator when lds_window < n
   size_t total;
 };
 CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p);

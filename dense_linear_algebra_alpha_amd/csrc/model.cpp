@@ -34,6 +34,9 @@ constexpr double kSustained = 0.88;     // sustained fraction of peak HBM bandwi
 constexpr double kLatency = 4.5e-6;     // seconds of loaded-memory latency that loads in flight must cover
 constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
+constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
+constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output window and y
+constexpr int64_t kCsrYLdsMax = 16 * 1024;    // CSR: largest y copied into LDS
 
 int next_pow2(int64_t x) {
   int p = 1;
@@ -73,8 +76,9 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
 CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p) {
   CsrWorkspace w{};
   w.partial_off = 0;
-  w.partial_rows = (p.kernel == XTVXY_CSR_LDS_TILES) ? (size_t)p.grid : 1;
-  w.total = align_up(w.partial_rows * (size_t)n * sizeof(float));
+  w.partial_rows = (size_t)p.grid;
+  w.acc_off = align_up((size_t)p.grid * (size_t)p.lds_window * sizeof(float));
+  w.total = (p.lds_window < n) ? align_up(w.acc_off + (size_t)n * sizeof(float)) : w.acc_off;
   return w;
 }
 
@@ -186,17 +190,14 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
                           xtvxy_launch_params* p) {
   (void)m;
   (void)nnz;
-  if (p->block_threads != kBlock || p->grid <= 0 || p->grid > INT32_MAX) return XTVXY_ERROR_INVALID_VALUE;
-  if (p->entries_per_thread < 1 || p->entries_per_thread > 8) return XTVXY_ERROR_INVALID_VALUE;
-  if (p->kernel == XTVXY_CSR_LDS_TILES) {
-    const int64_t static_lds = (int64_t)(kCsrRowsPerTile + 1) * 4 + kCsrRowsPerTile * 4 + 64;
-    if ((int64_t)n * 4 + static_lds > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
-    p->lds_window = (int32_t)n;
-  } else if (p->kernel == XTVXY_CSR_GLOBAL_TILES) {
-    p->lds_window = 0;
-  } else {
+  if (p->kernel != XTVXY_CSR_TILES || p->block_threads != kBlock || p->grid <= 0 || p->grid > INT32_MAX)
     return XTVXY_ERROR_INVALID_VALUE;
-  }
+  if (p->entries_per_thread != 4 && p->entries_per_thread != 8)
+    return XTVXY_ERROR_INVALID_VALUE;
+  if (p->lds_window < 0 || p->lds_window > n || (p->y_in_lds != 0 && p->y_in_lds != 1))
+    return XTVXY_ERROR_INVALID_VALUE;
+  const int64_t lds = ((int64_t)p->lds_window + (p->y_in_lds ? n : 0)) * (int64_t)sizeof(float) + kCsrStaticLds;
+  if (lds > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
   p->group = 1;
   p->workspace_bytes = (int64_t)csr_workspace(n, *p).total;
   return XTVXY_SUCCESS;
@@ -204,25 +205,34 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
 
 xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d, xtvxy_launch_params* p) {
   std::memset(p, 0, sizeof(*p));
+  p->kernel = XTVXY_CSR_TILES;
   p->block_threads = kBlock;
   p->vec = 1;
-  p->entries_per_thread = 8;
   p->chunks = 1;
   p->group = 1;
-  // LDS path when a workgroup's partial output fits next to a few co-resident workgroups
-  p->kernel = ((int64_t)n * 4 <= 64 * 1024) ? XTVXY_CSR_LDS_TILES : XTVXY_CSR_GLOBAL_TILES;
+  p->entries_per_thread = 8;
+  // y is copied into LDS when it is small; the output window takes what remains of a
+  // budget that leaves room for several workgroups per CU
+  p->y_in_lds = ((int64_t)n * 4 <= kCsrYLdsMax) ? 1 : 0;
+  const int64_t ybytes = p->y_in_lds ? (int64_t)n * 4 : 0;
+  p->lds_window = (int32_t)std::min<int64_t>(n, (kCsrLdsBudget - ybytes) / 4);
+  const int64_t wg_lds = (int64_t)p->lds_window * 4 + ybytes + (int64_t)kCsrStaticLds;
+  const int max_per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxWgPerCu, d.lds_bytes / wg_lds));
   const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
   const int64_t tile = (int64_t)kBlock * p->entries_per_thread;
+  // the model knows nothing of the column distribution: it prices the columns outside
+  // the window as uniformly hit
+  const double cold = n > 0 ? (double)(n - p->lds_window) / n * nnz : 0.0;
   double best = 1e300;
   int64_t best_grid = 1;
-  for (int k = 1; k <= kMaxWgPerCu; k *= 2) {
+  for (int k = 1; k <= max_per_cu; k *= 2) {
     int64_t grid = (int64_t)d.compute_units * k;
     grid = std::max<int64_t>(1, std::min<int64_t>(grid, ceil_div(std::max<int64_t>(nnz, 1), tile)));
     const double resident = std::min<double>(k, (double)grid / d.compute_units);
     const double bw = bandwidth(d, std::max(resident, 1.0 / d.compute_units) * tile * 8.0);
-    const double partial_bytes =
-        (p->kernel == XTVXY_CSR_LDS_TILES) ? 2.0 * grid * n * sizeof(float) : 2.0 * n * sizeof(float);
-    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + 2 * kLaunch;
+    const double partial_bytes = 2.0 * grid * p->lds_window * sizeof(float);
+    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + cold / kAtomicRate +
+                     3 * kLaunch;
     if (t < best * 0.999) {
       best = t;
       best_grid = grid;

@@ -81,11 +81,9 @@ enum {
   XTVXY_DENSE_BLOCK_ROWS = 2, /* rows of <= 8192 columns: one workgroup owns a row */
   XTVXY_DENSE_GROUP_ROWS = 3  /* wider rows: `group` co-resident workgroups split a row by columns */
 };
-/* CSR kernel variants. */
-enum {
-  XTVXY_CSR_LDS_TILES = 11,   /* partial output of a workgroup held in LDS (n <= lds window) */
-  XTVXY_CSR_GLOBAL_TILES = 12 /* scatter straight into a global fp32 accumulator (any n) */
-};
+/* CSR kernel: tiles of whole rows; output columns [0, lds_window) accumulate in
+ * LDS, the others in a global fp32 accumulator (hardware float atomics). */
+enum { XTVXY_CSR_TILES = 11 };
 
 /* Launch parameters chosen by the analytical model (the *_plan queries) or
  * forced by the caller (the *_ex entry points). */
@@ -98,8 +96,9 @@ typedef struct xtvxy_launch_params {
   int32_t group;           /* dense group path: workgroups per row (column slices); 1 otherwise */
   int64_t grid;            /* workgroups launched */
   int64_t rows_per_unit;   /* dense: rows per workgroup (wave/block paths) or per group */
-  int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile */
-  int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS */
+  int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile (4 or 8) */
+  int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS (0..n) */
+  int32_t y_in_lds;        /* csr: 1 = each workgroup copies y into LDS and gathers from there */
   int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries) */
   double predicted_seconds;/* the model's estimate for this plan */
 } xtvxy_launch_params;

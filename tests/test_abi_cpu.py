@@ -166,8 +166,9 @@ def test_plan_complete_rejects_plans_that_do_not_cover(lib):
                                      (10, 5, 7), (1, 1, 1)])
 def test_csr_model_plans(lib, m, n, nnz):
     p = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
-    assert p.grid >= 1 and 1 <= p.entries_per_thread <= 8
-    if n * 4 <= 64 * 1024:
-        assert p.kernel == xt.XTVXY_CSR_LDS_TILES and p.workspace_bytes >= p.grid * n * 4
-    else:
-        assert p.kernel == xt.XTVXY_CSR_GLOBAL_TILES and p.workspace_bytes >= n * 4
+    assert p.kernel == xt.XTVXY_CSR_TILES and p.grid >= 1 and p.entries_per_thread in (4, 8, 16)
+    assert 0 < p.lds_window <= n and p.workspace_bytes >= p.grid * p.lds_window * 4
+    lds = (p.lds_window + (n if p.y_in_lds else 0)) * 4
+    assert lds <= 64 * 1024
+    if p.lds_window < n:
+        assert p.workspace_bytes >= p.grid * p.lds_window * 4 + n * 4

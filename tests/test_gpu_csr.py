@@ -26,16 +26,18 @@ def test_irregular_matrices(m, n, mean_len):
 
 
 def forced_plans(m, n, nnz):
-    kernels = [xt.XTVXY_CSR_GLOBAL_TILES]
-    if n * 4 + 16448 <= 163840:
-        kernels.append(xt.XTVXY_CSR_LDS_TILES)
+    """Output windows from none to all of n, y in LDS or not, each tile size, a few grids."""
+    windows = sorted({0, min(n, 7), min(n, 4096), n if n * 4 + 3584 <= 163840 else min(n, 30000)})
     out = []
-    for k in kernels:
-        for ept in (1, 3, 8):
-            for grid in (1, 7, 256):
-                lp = xt.xtvxy_launch_params(kernel=k, block_threads=256, entries_per_thread=ept, grid=grid, vec=1,
-                                            chunks=1, group=1)
-                out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
+    for w in windows:
+        for y_lds in (0, 1):
+            if (w + (n if y_lds else 0)) * 4 + 3584 > 163840:
+                continue
+            for ept in (4, 8):
+                for grid in (1, 7, 256):
+                    lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=ept,
+                                                grid=grid, vec=1, chunks=1, group=1, lds_window=w, y_in_lds=y_lds)
+                    out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
     return out
 
 
