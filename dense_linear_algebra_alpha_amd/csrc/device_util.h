@@ -25,11 +25,61 @@ constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kHalfMirror = 0x141;
 constexpr int kMirror = 0x140;
 constexpr int kRor1 = 0x121, kRor2 = 0x122, kRor4 = 0x124, kRor8 = 0x128;
+constexpr int kShr1 = 0x111, kShr2 = 0x112, kShr4 = 0x114, kShr8 = 0x118;  // row_shr:k, lane i reads i-k in its row
+constexpr int kBcast15 = 0x142;   // row_bcast:15, rows 1 and 3 (row mask 0xa) read lane 15 of the row before
+constexpr int kBcast31 = 0x143;   // row_bcast:31, rows 2 and 3 (row mask 0xc) read lane 31
+constexpr int kWaveShl1 = 0x130;  // wave_shl:1, lane i reads lane i+1
+constexpr int kWaveShr1 = 0x138;  // wave_shr:1, lane i reads lane i-1
 }  // namespace dpp
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// DPP move; lanes without a source lane, or outside the row mask, get `old`. The source
+// lanes must be active: call from wavefront-uniform control flow.
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_int(int old, int x) {
+  return __builtin_amdgcn_update_dpp(old, x, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ float dpp_float(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+
+// Lane i gets the maximum of x over lanes 0..i (wavefront-uniform control flow).
+__device__ __forceinline__ int wave_max_scan(int x) {
+  constexpr int lo = INT32_MIN;
+  x = max(x, dpp_int<dpp::kShr1>(lo, x));
+  x = max(x, dpp_int<dpp::kShr2>(lo, x));
+  x = max(x, dpp_int<dpp::kShr4>(lo, x));
+  x = max(x, dpp_int<dpp::kShr8>(lo, x));
+  x = max(x, dpp_int<dpp::kBcast15, 0xa>(lo, x));
+  x = max(x, dpp_int<dpp::kBcast31, 0xc>(lo, x));
+  return x;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void seg_sum_step(float& x, int key) {
+  const float xs = dpp_float<CTRL, ROWS>(0.0f, x);
+  const int ks = dpp_int<CTRL, ROWS>(~key, key);  // ~key never equals key
+  x += (ks == key) ? xs : 0.0f;
+}
+
+// Segmented inclusive sum over a wavefront (wavefront-uniform control flow). Lanes with
+// equal `key` must be contiguous (e.g. keys nondecreasing with the lane index); lane i
+// gets the sum of x over the lanes j <= i with key_j == key_i. Each step adds the partial
+// sum d lanes back when that lane carries the same key: by contiguity, every lane between
+// carries it too, so the partial sums of one key never mix with another's.
+__device__ __forceinline__ float wave_segmented_sum(float x, int key) {
+  seg_sum_step<dpp::kShr1, 0xf>(x, key);
+  seg_sum_step<dpp::kShr2, 0xf>(x, key);
+  seg_sum_step<dpp::kShr4, 0xf>(x, key);
+  seg_sum_step<dpp::kShr8, 0xf>(x, key);
+  seg_sum_step<dpp::kBcast15, 0xa>(x, key);
+  seg_sum_step<dpp::kBcast31, 0xc>(x, key);
+  return x;
 }
 
 // x of lanes i and i^16 (aligned 32-lane halves), summed; same value in both lanes.

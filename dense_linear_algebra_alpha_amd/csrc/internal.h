@@ -15,7 +15,10 @@ namespace xtvxy {
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
-constexpr size_t kCsrStaticLds = 3584; // CSR kernel: LDS besides the output window and y (3372 used)
+// CSR kernel: LDS besides the output window and y, for `ept` entries per thread (row_ptr,
+// v and dots of two tiles and small scalars, 6472 bytes, plus two tiles of 16-bit row-start
+// marks)
+constexpr size_t csr_static_lds(int ept) { return 6656 + 1024 * (size_t)ept; }
 constexpr size_t kAlign = 256;       // alignment of every workspace region
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }

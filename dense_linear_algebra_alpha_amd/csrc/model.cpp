@@ -196,7 +196,8 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
     return XTVXY_ERROR_INVALID_VALUE;
   if (p->lds_window < 0 || p->lds_window > n || (p->y_in_lds != 0 && p->y_in_lds != 1))
     return XTVXY_ERROR_INVALID_VALUE;
-  const int64_t lds = ((int64_t)p->lds_window + (p->y_in_lds ? n : 0)) * (int64_t)sizeof(float) + kCsrStaticLds;
+  const int64_t lds = ((int64_t)p->lds_window + (p->y_in_lds ? n : 0)) * (int64_t)sizeof(float) +
+                      (int64_t)csr_static_lds(p->entries_per_thread);
   if (lds > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
   p->group = 1;
   p->workspace_bytes = (int64_t)csr_workspace(n, *p).total;
@@ -216,7 +217,7 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   p->y_in_lds = ((int64_t)n * 4 <= kCsrYLdsMax) ? 1 : 0;
   const int64_t ybytes = p->y_in_lds ? (int64_t)n * 4 : 0;
   p->lds_window = (int32_t)std::min<int64_t>(n, (kCsrLdsBudget - ybytes) / 4);
-  const int64_t wg_lds = (int64_t)p->lds_window * 4 + ybytes + (int64_t)kCsrStaticLds;
+  const int64_t wg_lds = (int64_t)p->lds_window * 4 + ybytes + (int64_t)csr_static_lds(p->entries_per_thread);
   const int max_per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxWgPerCu, d.lds_bytes / wg_lds));
   const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
   const int64_t tile = (int64_t)kBlock * p->entries_per_thread;

@@ -27,11 +27,12 @@ def test_irregular_matrices(m, n, mean_len):
 
 def forced_plans(m, n, nnz):
     """Output windows from none to all of n, y in LDS or not, each tile size, a few grids."""
-    windows = sorted({0, min(n, 7), min(n, 4096), n if n * 4 + 3584 <= 163840 else min(n, 30000)})
+    fixed = 16384  # more than the kernel's own LDS for any tile size
+    windows = sorted({0, min(n, 7), min(n, 4096), n if n * 4 + fixed <= 163840 else min(n, 30000)})
     out = []
     for w in windows:
         for y_lds in (0, 1):
-            if (w + (n if y_lds else 0)) * 4 + 3584 > 163840:
+            if (w + (n if y_lds else 0)) * 4 + fixed > 163840:
                 continue
             for ept in (4, 8):
                 for grid in (1, 7, 256):
