@@ -72,7 +72,7 @@ class HipEvents:
 
 def kernel_sources_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
-    files = ["device_util.h", "internal.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
+    files = ["device_util.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -80,16 +80,19 @@ def kernel_sources_hash(kind: str) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(plan, kind: str) -> str:
+def kernel_name(plan) -> str:
+    """Name of the main fused kernel a plan launches (dense_block_rows serves both block paths;
+    dense_group_rows is its group-row form)."""
     import dense_linear_algebra_alpha_amd as xt
     names = {xt.XTVXY_DENSE_WAVE_ROWS: "dense_wave_rows", xt.XTVXY_DENSE_BLOCK_ROWS: "dense_block_rows",
-             xt.XTVXY_DENSE_GROUP_ROWS: "dense_block_rows(group)", xt.XTVXY_CSR_TILES: "csr_fused"}
+             xt.XTVXY_DENSE_GROUP_ROWS: "dense_group_rows", xt.XTVXY_CSR_TILES: "csr_fused"}
     return names.get(plan.kernel, "kernel%d" % plan.kernel)
 
 
-def load_traffic(workload: str, kind: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, when it matches the source."""
-    path = os.path.join(ROOT, "profiles", "counters_%s.json" % workload)
+def load_traffic(workload: str, kernel: str, kind: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE,
+    each scaled by what it reads on a plain copy of known size), when it was taken on this source."""
+    path = os.path.join(ROOT, "profiles", "%s__%s.counters.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -250,9 +253,9 @@ def main():
                         "plan": {k: v_ for k, v_ in plan.as_dict().items() if k != "predicted_seconds"}},
                        **shape),
         "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": kernel_name(plan, kind), "achieved": round(achieved, 3),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(plan), "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload, kind),
+                     "traffic": load_traffic(args.workload, kernel_name(plan), kind),
                      "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
                      "kernel_ms_min": round(min(kernel_ms), 5)},
     }
