@@ -3,8 +3,9 @@
 // hierarchically) and the small helper kernels of the library.
 //
 // aggregate: out_j = alpha * S_j + beta * z_j with S_j the sum of the fused
-// kernel's per-workgroup partials (plus, for the CSR path, a global accumulator
-// of the columns outside the LDS window). Each 1024-thread workgroup owns 64 columns;
+// kernel's per-workgroup partials (plus, for the CSR path, the columns outside
+// the LDS window: a global accumulator, or the partial rows of the units of the
+// column's bin written by csr_bins.hip). Each 1024-thread workgroup owns 64 columns;
 // 16 thread rows each sum a strided subset of the partials in fp64, and the 16
 // results are combined in a fixed order, so the result is bitwise reproducible.
 // The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
@@ -21,7 +22,7 @@ __global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const fl
                                                                         int64_t rows, int64_t ldp,
                                                                         const float* __restrict__ acc, int64_t n,
                                                                         float alpha, float beta, const float* z,
-                                                                        float* out) {
+                                                                        float* out, BinPartials bins) {
   __shared__ double sh[kAggRows][kAggCols];
   const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
   const int64_t j = (int64_t)blockIdx.x * kAggCols + tx;
@@ -29,6 +30,13 @@ __global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const fl
   if (j < ldp) {
 #pragma unroll 8
     for (int64_t r = ty; r < rows; r += kAggRows) s += (double)partial[r * ldp + j];
+  } else if (bins.partial2 != nullptr && j >= bins.first_col && j < n) {
+    const int64_t rel = j - bins.first_col;
+    const int64_t b = rel >> bins.bin_shift, off = rel & ((1 << bins.bin_shift) - 1);
+    const int64_t u1 = bins.unit_start[b + 1];
+#pragma unroll 4
+    for (int64_t u = bins.unit_start[b] + ty; u < u1; u += kAggRows)
+      s += (double)bins.partial2[(u << bins.bin_shift) + off];
   }
   sh[ty][tx] = s;
   __syncthreads();
@@ -80,11 +88,13 @@ unsigned grid_for(int64_t count, int block) {
 }  // namespace
 
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
-                            float alpha, float beta, const float* z, float* out, hipStream_t s) {
+                            float alpha, float beta, const float* z, float* out, hipStream_t s,
+                            const BinPartials* bins) {
   if (n <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((n + kAggCols - 1) / kAggCols);
+  const BinPartials none{nullptr, nullptr, 0, 0};
   hipLaunchKernelGGL(aggregate_kernel, dim3(grid), dim3(kAggCols * kAggRows), 0, s, partial, rows, ldp, acc, n,
-                     alpha, beta, z, out);
+                     alpha, beta, z, out, bins ? *bins : none);
   return hipGetLastError();
 }
 

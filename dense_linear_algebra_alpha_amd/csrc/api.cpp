@@ -93,7 +93,7 @@ xtvxy_status check_csr(int64_t m, int64_t n, int64_t nnz, float alpha, const int
                        const float* z, const float* out, bool* quick) {
   *quick = false;
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
-  if (nnz > INT32_MAX || m >= INT32_MAX || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   if (n == 0) {
     *quick = true;
     return XTVXY_SUCCESS;
@@ -214,7 +214,7 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   if (st != XTVXY_SUCCESS) return st;
   if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
-  const CsrWorkspace w = csr_workspace(n, plan);
+  const CsrWorkspace w = csr_workspace(m, n, nnz, plan);
   CsrArgs a{};
   a.m = m;
   a.n = n;
@@ -227,11 +227,39 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   char* base = static_cast<char*>(ws);
   a.partial = reinterpret_cast<float*>(base + w.partial_off);
   a.lds_window = plan.lds_window;
-  a.acc = plan.lds_window < n ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
+  const bool binned = w.bins > 0;
+  a.acc = (plan.lds_window < n && !binned) ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
   a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
+  CsrBinArgs bargs{};
+  if (binned) {
+    a.bins = w.bins;
+    a.bin_shift = w.bin_shift;
+    a.pool_chunks = w.pool_chunks;
+    a.pool_next = reinterpret_cast<uint32_t*>(base + w.counter_off);
+    a.pool = reinterpret_cast<int2*>(base + w.pool_off);
+    a.chunk_bin = reinterpret_cast<int32_t*>(base + w.chunk_bin_off);
+    a.chunk_fill = reinterpret_cast<int32_t*>(base + w.chunk_fill_off);
+    bargs.lds_window = plan.lds_window;
+    bargs.bins = w.bins;
+    bargs.bin_shift = w.bin_shift;
+    bargs.pool_chunks = w.pool_chunks;
+    bargs.max_units = w.max_units;
+    bargs.pool_next = a.pool_next;
+    bargs.pool = a.pool;
+    bargs.chunk_bin = a.chunk_bin;
+    bargs.chunk_fill = a.chunk_fill;
+    bargs.order = reinterpret_cast<int32_t*>(base + w.order_off);
+    bargs.bin_start = reinterpret_cast<int32_t*>(base + w.bin_start_off);
+    bargs.unit_start = reinterpret_cast<int32_t*>(base + w.unit_start_off);
+    bargs.partial2 = reinterpret_cast<float*>(base + w.partial2_off);
+  }
   hipError_t e;
   if (a.acc) {
     e = launch_zero(a.acc, (size_t)n * sizeof(float), stream);
+    if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  }
+  if (binned) {
+    e = launch_zero(a.pool_next, sizeof(uint32_t), stream);
     if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   }
   const hipEvent_t before = g_before_main, after = g_after_main;
@@ -239,7 +267,13 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   e = launch_csr(a, plan, stream);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, plan.lds_window, a.acc, n, alpha, beta, z, out, stream);
+  BinPartials bp{bargs.partial2, bargs.unit_start, plan.lds_window, w.bin_shift};
+  if (binned) {
+    e = launch_csr_bins(bargs, stream);
+    if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  }
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, plan.lds_window, a.acc, n, alpha, beta, z, out, stream,
+                       binned ? &bp : nullptr);
   return launch_status(e);
 }
 
@@ -308,7 +342,7 @@ xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_d
                                 xtvxy_launch_params* plan) {
   if (!plan) return XTVXY_ERROR_NULL_POINTER;
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
-  if (nnz > INT32_MAX || m >= INT32_MAX || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   xtvxy_device_info d;
   if (dev) {
     d = *dev;

@@ -52,6 +52,7 @@ namespace {
 constexpr int kTileRows = kBlock;  // rows a tile stages: one row_ptr per thread
 
 typedef __attribute__((address_space(1))) float global_float;
+typedef __attribute__((address_space(1))) uint32_t global_uint;
 typedef int32_t i4 __attribute__((ext_vector_type(4)));
 typedef int32_t i2 __attribute__((ext_vector_type(2)));
 
@@ -78,16 +79,9 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64_t m, i
   return min(lo + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi);
 }
 
-// Scatter-add of one product. Both atomics name their address space explicitly: written as
-// plain atomicAdd on float*, the compiler merges the two branches into a single flat atomic,
-// which is slower and makes every later wait cover outstanding loads.
-__device__ __forceinline__ void scatter(const CsrArgs& a, float* out_s, int32_t col, float c) {
-  if (col < a.lds_window) {
-    lds_add_f32(out_s + col, c);
-  } else {
-    __hip_atomic_fetch_add((global_float*)a.acc + col, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
+// Columns outside the LDS window: none (the window holds all of them), global float
+// atomics, or binned (see csr_bins.hip).
+enum ColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
 
 // The loads one tile needs, held in registers while the previous tile is processed.
 template <int K>
@@ -99,27 +93,33 @@ struct TileRegs {
   float v;      // v[r + tid]
 };
 
-template <int K, bool YLDS, bool HAS_V, bool ALIGNED>
+template <int K, bool YLDS, bool HAS_V, bool ALIGNED, int COLD>
 __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
   constexpr int T = kBlock * K;
+  constexpr bool BINNED = COLD == kColdBinned;
   // per-tile state, double-buffered by tile parity
   __shared__ int32_t rp_s[2][kTileRows + 1];  // row_ptr of the tile's rows
   __shared__ float v_s[2][kTileRows];         // v of the tile's rows
   __shared__ float u_s[2][kTileRows];         // u_row = v_row * (row dot), built by the dots
   __shared__ __align__(16) uint16_t mark_s[2][T];  // 1 + tile row whose first entry sits at slot q, else 0
   __shared__ int32_t wfirst_s[2][kWaves];     // tile row holding the first entry of each wavefront
+  __shared__ float sink_s[kBlock];            // a private LDS word per thread for masked-off adds
   __shared__ float lred[kWaves];
-  __shared__ int64_t range_s[2];
-  extern __shared__ float dyn[];
+  __shared__ int32_t range_s[2];
+  extern __shared__ __align__(16) float dyn[];
   float* out_s = dyn;                 // [lds_window]
   float* y_s = dyn + a.lds_window;    // [n] when YLDS
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t nnz = a.nnz;
+  // Entry positions are unsigned 32-bit (nnz < 2^31, so a position plus a tile never wraps);
+  // rows are signed 32-bit (m <= 2^31 - 1025, so a row plus 256 never overflows).
+  const uint32_t nnz = (uint32_t)a.nnz;
+  const uint32_t nnz_full = nnz & ~3u;  // entries in whole aligned quads
+  const int32_t window = (int32_t)a.lds_window;
 
-  for (int64_t j = tid; j < a.lds_window; j += kBlock) out_s[j] = 0.0f;
+  for (int32_t j = tid; j < window; j += kBlock) out_s[j] = 0.0f;
   if constexpr (YLDS) {
-    for (int64_t j = tid; j < a.n; j += kBlock) y_s[j] = a.y[j];
+    for (int32_t j = tid; j < (int32_t)a.n; j += kBlock) y_s[j] = a.y[j];
   }
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -127,104 +127,191 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     for (int k = 0; k < K; ++k) mark_s[b][tid * K + k] = 0;
     if (tid < kWaves) wfirst_s[b][tid] = 0;
   }
+  sink_s[tid] = 0.0f;
+  // Binning of the columns >= window. Per bin, in LDS: the items of the current batch (a
+  // tile, or a slice of a long row), the workgroup's current chunk and its fill, and where the
+  // batch's items go: `room` items from pos1 on, the rest from pos2 on (new chunks, contiguous).
+  constexpr uint32_t S = kBinChunkItems;
+  const uint64_t pool_items = (uint64_t)a.pool_chunks * S;
+  uint64_t* pos1_s = nullptr;
+  uint64_t* pos2_s = nullptr;
+  uint32_t* cnt_s = nullptr;
+  int32_t* cur_s = nullptr;
+  int32_t* fill_s = nullptr;
+  uint32_t* room_s = nullptr;
+  if constexpr (BINNED) {
+    const int64_t words = (a.lds_window + (YLDS ? a.n : 0) + 1) & ~(int64_t)1;  // 8-byte aligned
+    pos1_s = reinterpret_cast<uint64_t*>(dyn + words);
+    pos2_s = pos1_s + a.bins;
+    cnt_s = reinterpret_cast<uint32_t*>(pos2_s + a.bins);
+    cur_s = reinterpret_cast<int32_t*>(cnt_s + a.bins);
+    fill_s = cur_s + a.bins;
+    room_s = reinterpret_cast<uint32_t*>(fill_s + a.bins);
+    for (int t = tid; t < a.bins; t += kBlock) {
+      cnt_s[t] = 0;
+      cur_s[t] = -1;
+      fill_s[t] = (int32_t)S;
+    }
+  }
+  // (cold column) -> its rank among the batch's items of its bin
+  auto bin_rank = [&](int32_t col) -> uint32_t {
+    const int bin = (col - window) >> a.bin_shift;
+    return __hip_atomic_fetch_add((lds_uint*)(cnt_s + bin), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // After a barrier that follows the batch's ranks: one thread per bin finds room for the
+  // bin's items, handing out new pool chunks (one global atomic per bin and batch that spills),
+  // and resets the count. A barrier must follow before bin_write.
+  auto bin_alloc = [&]() {
+    for (int t = tid; t < a.bins; t += kBlock) {
+      const uint32_t cnt = cnt_s[t];
+      if (cnt == 0) continue;
+      cnt_s[t] = 0;
+      const int32_t cur = cur_s[t], fill = fill_s[t];
+      const uint32_t room = cur >= 0 ? S - (uint32_t)fill : 0u;
+      room_s[t] = room;
+      pos1_s[t] = (uint64_t)(cur >= 0 ? cur : 0) * S + (uint32_t)fill;
+      if (cnt <= room) {
+        fill_s[t] = fill + (int32_t)cnt;
+        continue;
+      }
+      const uint32_t need = cnt - room, k = (need + S - 1) / S;
+      const uint32_t first =
+          __hip_atomic_fetch_add((global_uint*)a.pool_next, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if ((int64_t)first + k > a.pool_chunks) {  // cannot happen with the pool sized for the plan
+        pos2_s[t] = pool_items;                  // the items are dropped rather than written out of bounds
+        cur_s[t] = -1;
+        fill_s[t] = (int32_t)S;
+        continue;
+      }
+      for (uint32_t c = 0; c < k; ++c) {
+        a.chunk_bin[first + c] = t;
+        a.chunk_fill[first + c] = (int32_t)S;  // the last one is corrected when it stops filling
+      }
+      pos2_s[t] = (uint64_t)first * S;
+      cur_s[t] = (int32_t)(first + k - 1);
+      fill_s[t] = (int32_t)(need - (k - 1) * S);
+    }
+  };
+  auto bin_write = [&](int32_t col, float c, uint32_t rank) {
+    const int bin = (col - window) >> a.bin_shift;
+    const uint32_t room = room_s[bin];
+    const uint64_t pos = rank < room ? pos1_s[bin] + rank : pos2_s[bin] + (rank - room);
+    if (pos < pool_items) a.pool[pos] = make_int2(col, __float_as_int(c));
+  };
+  // Scatter of K products c[k] to columns col[k] where on[k]. Columns in the window go to the
+  // LDS copy of the output (a masked-off lane adds 0 to its own sink word, so the add needs no
+  // branch); the others go to the global accumulator or to the bins. With bins, every thread of
+  // the workgroup must call this together (it holds two barriers).
+  auto scatter_k = [&](const float (&c)[K], const int32_t (&col)[K], const bool (&on)[K]) {
+    if constexpr (COLD == kColdNone) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) lds_add_f32(on[k] ? out_s + col[k] : sink_s + tid, on[k] ? c[k] : 0.0f);
+    } else if constexpr (COLD == kColdAtomic) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const bool hot = on[k] && col[k] < window;
+        lds_add_f32(hot ? out_s + col[k] : sink_s + tid, hot ? c[k] : 0.0f);
+        if (on[k] && !hot)
+          __hip_atomic_fetch_add((global_float*)a.acc + col[k], c[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      uint32_t rank[K];
+      bool cold[K];
+#pragma unroll
+      for (int k = 0; k < K; ++k) {
+        const bool hot = on[k] && col[k] < window;
+        cold[k] = on[k] && !hot;
+        lds_add_f32(hot ? out_s + col[k] : sink_s + tid, hot ? c[k] : 0.0f);
+        if (cold[k]) rank[k] = bin_rank(col[k]);
+      }
+      __syncthreads();  // the batch's bin counts are complete
+      bin_alloc();
+      __syncthreads();  // room for every bin is known
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (cold[k]) bin_write(col[k], c[k], rank[k]);
+    }
+  };
+
   if (wave == 0) {
-    const int64_t q = (nnz + gridDim.x - 1) / gridDim.x;
+    const int64_t q = (a.nnz + gridDim.x - 1) / gridDim.x;
     const int64_t rb = wave_lower_bound(a.row_ptr, a.m, (int64_t)blockIdx.x * q);
     const int64_t re =
         (blockIdx.x + 1 == gridDim.x) ? a.m : wave_lower_bound(a.row_ptr, a.m, (int64_t)(blockIdx.x + 1) * q);
     if (lane == 0) {
-      range_s[0] = rb;
-      range_s[1] = re;
+      range_s[0] = (int32_t)rb;
+      range_s[1] = (int32_t)re;
     }
   }
   __syncthreads();
-  const int64_t rb = range_s[0], re = range_s[1];
+  const int32_t rb = range_s[0], re = range_s[1];
   if (rb >= re) {
-    if (a.lds_window > 0) {
-      float* dst = a.partial + (int64_t)blockIdx.x * a.lds_window;
-      for (int64_t c = tid; c < a.lds_window; c += kBlock) dst[c] = 0.0f;
-    }
+    float* dst = a.partial + (int64_t)blockIdx.x * window;
+    for (int32_t c = tid; c < window; c += kBlock) dst[c] = 0.0f;
     return;
   }
   const float* ysrc = YLDS ? y_s : a.y;
 
-  // Loads for the tile whose rows start at r and whose entries start at `first_entry`;
-  // every load is unconditional (clamped address), entries past the arrays read as zero.
-  // Only used when nnz >= 4 (the vector loads then never leave the arrays).
-  const int64_t nnz_full = nnz & ~(int64_t)3;  // entries in whole aligned quads
-  auto issue_rows = [&](int64_t r, TileRegs<K>& g) {
+  auto issue_rows = [&](int32_t r, TileRegs<K>& g) {
     g.rp = a.row_ptr[min(r + tid, re)];
     g.rp1 = a.row_ptr[min(r + tid + 1, re)];
     g.v = HAS_V ? a.v[min(r + tid, re - 1)] : 1.0f;
   };
-  auto issue = [&](int64_t r, int64_t first_entry, TileRegs<K>& g) {
-    issue_rows(r, g);
-    const int64_t e0 = (first_entry & ~(int64_t)3) + (int64_t)tid * K;
-    // the last partial quad (nnz % 4 entries), read by every lane and used by the one lane whose
-    // quad starts at nnz_full
-    float tv[3];
-    int32_t tc[3];
+  // The K entries from base + K tid (base a multiple of 4). Tiles whose T slots lie inside the
+  // whole quads of the arrays (all but the last one or two) load without any guard; the others
+  // load element by element with clamped addresses, entries past nnz reading as zero. The
+  // branch is the same for the whole workgroup.
+  auto load_entries = [&](uint32_t base, float (&val)[K], int32_t (&col)[K]) {
+    const uint32_t e0 = base + (uint32_t)tid * K;
+    if (base + T <= nnz_full) {
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-      const int64_t p = min(nnz_full + q, nnz - 1);
-      tv[q] = a.values[p];
-      tc[q] = a.col_idx[p];
-    }
+      for (int k = 0; k < K; k += 4) {
+        if constexpr (ALIGNED) {
+          const f4 vv = *reinterpret_cast<const f4*>(a.values + e0 + k);
+          const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + e0 + k);
+          val[k] = vv.x; val[k + 1] = vv.y; val[k + 2] = vv.z; val[k + 3] = vv.w;
+          col[k] = cc.x; col[k + 1] = cc.y; col[k + 2] = cc.z; col[k + 3] = cc.w;
+        } else {
 #pragma unroll
-    for (int k = 0; k < K; k += 4) {
-      const int64_t e = e0 + k;
-      const int64_t ec = min(e, nnz_full - 4);
-      float xv[4];
-      int32_t xc[4];
-      if constexpr (ALIGNED) {
-        const f4 vv = *reinterpret_cast<const f4*>(a.values + ec);
-        const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + ec);
-        xv[0] = vv.x; xv[1] = vv.y; xv[2] = vv.z; xv[3] = vv.w;
-        xc[0] = cc.x; xc[1] = cc.y; xc[2] = cc.z; xc[3] = cc.w;
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          xv[q] = a.values[ec + q];
-          xc[q] = a.col_idx[ec + q];
+          for (int q = 0; q < 4; ++q) {
+            val[k + q] = a.values[e0 + k + q];
+            col[k + q] = a.col_idx[e0 + k + q];
+          }
         }
       }
+    } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool full = e < nnz_full;
-        const bool tail = (e == nnz_full) && (e + q < nnz);
-        g.val[k + q] = full ? xv[q] : (tail && q < 3 ? tv[q < 3 ? q : 0] : 0.0f);
-        g.col[k + q] = full ? xc[q] : (tail && q < 3 ? tc[q < 3 ? q : 0] : 0);
+      for (int k = 0; k < K; ++k) {
+        const bool in = e0 + k < nnz;
+        const uint32_t p = in ? e0 + k : nnz - 1;
+        const float x = a.values[p];
+        const int32_t c = a.col_idx[p];
+        val[k] = in ? x : 0.0f;
+        col[k] = in ? c : 0;
       }
     }
   };
-  // Small matrices (nnz < 4): element loads, guarded.
-  auto issue_small = [&](int64_t r, int64_t first_entry, TileRegs<K>& g) {
+  auto issue = [&](int32_t r, uint32_t first_entry, TileRegs<K>& g) {
     issue_rows(r, g);
-    const int64_t e0 = (first_entry & ~(int64_t)3) + (int64_t)tid * K;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-      const bool in = e0 + k < nnz;
-      g.val[k] = in ? a.values[e0 + k] : 0.0f;
-      g.col[k] = in ? a.col_idx[e0 + k] : 0;
-    }
+    load_entries(first_entry & ~3u, g.val, g.col);
   };
   // Publishes the state of the tile of `cnt` rows whose first entry is `first` into buffer b
   // (row_ptr, v, zeroed dots, row-start marks, the row of each wavefront's first entry) and
   // returns whether this thread's row ends inside the tile's T entry slots; the rows that do
   // form a prefix, so their count is the number of rows of the tile.
-  auto stage = [&](int b, int cnt, int64_t first, const TileRegs<K>& g) -> bool {
-    const int64_t base = first & ~(int64_t)3;
+  auto stage = [&](int b, int cnt, uint32_t first, const TileRegs<K>& g) -> bool {
+    const uint32_t base = first & ~3u;
     u_s[b][tid] = 0.0f;
     bool fits = false;
     if (tid < cnt) {
       if (tid == 0) rp_s[b][0] = g.rp;
       rp_s[b][tid + 1] = g.rp1;
       v_s[b][tid] = g.v;
-      const int64_t s = (int64_t)g.rp - base, e = (int64_t)g.rp1 - base;
+      const uint32_t s = (uint32_t)g.rp - base, e = (uint32_t)g.rp1 - base;
       if (e > s && s < T) mark_s[b][s] = (uint16_t)(tid + 1);
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const int64_t pw = max((int64_t)w * 64 * K, first - base);
+        const uint32_t pw = w == 0 ? first - base : (uint32_t)(w * 64 * K);
         if (s <= pw && pw < e) wfirst_s[b][w] = tid;
       }
       fits = e <= T;
@@ -234,34 +321,32 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
 
   TileRegs<K> ga, gb;
   int buf = 0;
-  int64_t ra = rb;
-  int cnt = (int)min((int64_t)kTileRows, re - ra);
+  int32_t ra = rb;
+  int cnt = min(kTileRows, re - ra);
   int j;
   {
-    const int64_t p0 = a.row_ptr[ra];
-    if (nnz >= 4) issue(ra, p0, ga); else issue_small(ra, p0, ga);
+    const uint32_t p0 = (uint32_t)a.row_ptr[ra];
+    issue(ra, p0, ga);
     j = __syncthreads_count(stage(0, cnt, p0, ga));
   }
 
   auto step = [&](TileRegs<K>& g, TileRegs<K>& gn) -> bool {
     const int b = buf;
-    const int32_t pa = rp_s[b][0];
-    const int64_t base = (int64_t)pa & ~(int64_t)3;
+    const uint32_t pa = (uint32_t)rp_s[b][0];
+    const uint32_t base = pa & ~3u;
     const bool long_row = (j == 0);  // row ra alone holds more entries than a tile
-    const int32_t pb = long_row ? rp_s[b][1] : rp_s[b][j];
-    const int64_t ra_next = ra + (long_row ? 1 : j);
+    const uint32_t pb = (uint32_t)(long_row ? rp_s[b][1] : rp_s[b][j]);
+    const int32_t ra_next = ra + (long_row ? 1 : j);
     const bool more = ra_next < re;
-    const int cnt_next = more ? (int)min((int64_t)kTileRows, re - ra_next) : 0;
-    const int64_t e0 = base + (int64_t)tid * K;
+    const int cnt_next = more ? min(kTileRows, re - ra_next) : 0;
+    const uint32_t e0 = base + (uint32_t)tid * K;
 
     // (a) gathers of y for this tile's entries, before anything of the next tile is issued
     float yv[K];
-    if (!long_row) {
 #pragma unroll
-      for (int k = 0; k < K; ++k) yv[k] = ysrc[g.col[k]];
-    }
+    for (int k = 0; k < K; ++k) yv[k] = ysrc[g.col[k]];
     // (b) the next tile's row_ptr, v and entries (they start where this tile ends)
-    if (nnz >= 4) issue(min(ra_next, re - 1), pb, gn); else issue_small(min(ra_next, re - 1), pb, gn);
+    issue(min(ra_next, re - 1), pb, gn);
 
     // this thread's K row-start marks, cleared for the tile after next
     int mk[K];
@@ -287,9 +372,20 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     }
 
     if (long_row) {
-      // the whole workgroup sweeps the row twice: dot, then scatter
+      // The whole workgroup takes the row in slices of T entries, twice: the dot, then the
+      // scatter. The first slice is the one already in registers.
       float s = 0.0f;
-      for (int64_t p = pa + tid; p < pb; p += kBlock) s = fmaf(a.values[p], ysrc[a.col_idx[p]], s);
+      const uint32_t len = pb - pa;
+#pragma unroll
+      for (int k = 0; k < K; ++k) s += (e0 + k - pa < len) ? g.val[k] * yv[k] : 0.0f;
+      for (uint32_t sb = base + T; sb < pb; sb += T) {
+        float hv[K];
+        int32_t hc[K];
+        load_entries(sb, hv, hc);
+        const uint32_t h0 = sb + (uint32_t)tid * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * ysrc[hc[k]] : 0.0f;
+      }
       s = group_sum(s, 64);
       if (lane == 0) lred[wave] = s;
       __syncthreads();
@@ -297,16 +393,40 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
 #pragma unroll
       for (int w = 1; w < kWaves; ++w) t += lred[w];
       const float u = v_s[b][0] * t;
-      for (int64_t p = pa + tid; p < pb; p += kBlock) scatter(a, out_s, a.col_idx[p], u * a.values[p]);
+      {
+        float c[K];
+        bool on[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          on[k] = e0 + k - pa < len;
+          c[k] = u * g.val[k];
+        }
+        scatter_k(c, g.col, on);
+      }
+      for (uint32_t sb = base + T; sb < pb; sb += T) {
+        float hv[K];
+        int32_t hc[K];
+        load_entries(sb, hv, hc);
+        const uint32_t h0 = sb + (uint32_t)tid * K;
+        float c[K];
+        bool on[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          on[k] = h0 + k < pb;
+          c[k] = u * hv[k];
+        }
+        scatter_k(c, hc, on);
+      }
     } else {
       // (c) the row of each entry: the latest row-start mark at or before it, within the thread,
       // then across the wavefront, then the row that holds the wavefront's first entry
       bool ok[K];
       int rk[K];
       int run_max = -1;
+      const uint32_t len = pb - pa;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        ok[k] = (e0 + k >= pa) && (e0 + k < pb);
+        ok[k] = e0 + k - pa < len;  // unsigned: positions before pa wrap to large values
         run_max = max(run_max, mk[k]);
         mk[k] = run_max;
       }
@@ -322,20 +442,13 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
       float head = 0.0f, run = 0.0f;
 #pragma unroll
       for (int k = 0; k < K; ++k) {
-        if (ok[k]) {
-          const float p = g.val[k] * yv[k];
-          if (rk[k] != r1) {
-            if (r1 >= 0) {
-              if (r1 == r0) head = run;
-              else u_s[b][r1] = v_s[b][r1] * run;
-            }
-            if (r0 < 0) r0 = rk[k];
-            r1 = rk[k];
-            run = p;
-          } else {
-            run += p;
-          }
-        }
+        const float p = ok[k] ? g.val[k] * yv[k] : 0.0f;
+        const bool fresh = ok[k] && rk[k] != r1;  // a new run starts at k
+        if (fresh && r1 >= 0 && r1 != r0) u_s[b][r1] = v_s[b][r1] * run;  // a row inside the thread
+        head = (fresh && r1 >= 0 && r1 == r0) ? run : head;                // the first run ended
+        r0 = (ok[k] && r0 < 0) ? rk[k] : r0;
+        run = fresh ? p : run + p;
+        r1 = ok[k] ? rk[k] : r1;
       }
       // Tails summed across the wavefront per row (keys are rows, nondecreasing with the lane;
       // lanes without entries come last with a key no row has). A lane whose tail row does not
@@ -359,9 +472,10 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
       }
       __syncthreads();  // u_s[b] complete
       // (e) scatter
+      float c[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k)
-        if (ok[k]) scatter(a, out_s, g.col[k], u_s[b][rk[k]] * g.val[k]);
+      for (int k = 0; k < K; ++k) c[k] = u_s[b][rk[k]] * g.val[k];
+      scatter_k(c, g.col, ok);
     }
     if (!more) return false;
     const bool fits = stage(b ^ 1, cnt_next, pb, gn);
@@ -374,33 +488,46 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
 
   while (step(ga, gb) && step(gb, ga)) {
   }
+  if constexpr (BINNED) {
+    // the fill of each bin's last chunk (every other handed-out chunk is full)
+    for (int t = tid; t < a.bins; t += kBlock)
+      if (cur_s[t] >= 0) a.chunk_fill[cur_s[t]] = fill_s[t];
+  }
 
-  if (a.lds_window > 0) {
+  if (window > 0) {
     __syncthreads();
-    float* dst = a.partial + (int64_t)blockIdx.x * a.lds_window;
-    for (int64_t c = tid; c < a.lds_window; c += kBlock) dst[c] = out_s[c];
+    float* dst = a.partial + (int64_t)blockIdx.x * window;
+    for (int32_t c = tid; c < window; c += kBlock) dst[c] = out_s[c];
   }
 }
 
-template <int K, bool YLDS, bool HAS_V, bool ALIGNED>
+template <int K, bool YLDS, bool HAS_V, bool ALIGNED, int COLD>
 hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const size_t lds = ((size_t)a.lds_window + (YLDS ? (size_t)a.n : 0)) * sizeof(float);
-  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YLDS, HAS_V, ALIGNED>);
+  size_t lds = ((size_t)a.lds_window + (YLDS ? (size_t)a.n : 0)) * sizeof(float);
+  if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YLDS, HAS_V, ALIGNED, COLD>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_fused<K, YLDS, HAS_V, ALIGNED>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL((csr_fused<K, YLDS, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
   return hipGetLastError();
 }
 
-template <int K>
+template <int K, int COLD>
 hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const bool yl = p.y_in_lds != 0, hv = a.v != nullptr, al = a.aligned;
   if (yl) {
-    if (hv) return al ? launch_k<K, true, true, true>(a, p, s) : launch_k<K, true, true, false>(a, p, s);
-    return al ? launch_k<K, true, false, true>(a, p, s) : launch_k<K, true, false, false>(a, p, s);
+    if (hv) return al ? launch_k<K, true, true, true, COLD>(a, p, s) : launch_k<K, true, true, false, COLD>(a, p, s);
+    return al ? launch_k<K, true, false, true, COLD>(a, p, s) : launch_k<K, true, false, false, COLD>(a, p, s);
   }
-  if (hv) return al ? launch_k<K, false, true, true>(a, p, s) : launch_k<K, false, true, false>(a, p, s);
-  return al ? launch_k<K, false, false, true>(a, p, s) : launch_k<K, false, false, false>(a, p, s);
+  if (hv) return al ? launch_k<K, false, true, true, COLD>(a, p, s) : launch_k<K, false, true, false, COLD>(a, p, s);
+  return al ? launch_k<K, false, false, true, COLD>(a, p, s) : launch_k<K, false, false, false, COLD>(a, p, s);
+}
+
+template <int K>
+hipError_t launch_cold(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  if (a.bins > 0) return launch_kk<K, kColdBinned>(a, p, s);
+  if (a.lds_window < a.n) return launch_kk<K, kColdAtomic>(a, p, s);
+  return launch_kk<K, kColdNone>(a, p, s);
 }
 
 }  // namespace
@@ -408,9 +535,17 @@ hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES)
     return hipErrorInvalidValue;
+  if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
+      a.lds_window > a.n)
+    return hipErrorInvalidValue;
+  const bool binned = a.bins > 0;
+  if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
+                 a.bins > kMaxBins || a.acc != nullptr))
+    return hipErrorInvalidValue;
+  if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
   switch (p.entries_per_thread) {
-    case 4: return launch_kk<4>(a, p, s);
-    case 8: return launch_kk<8>(a, p, s);
+    case 4: return launch_cold<4>(a, p, s);
+    case 8: return launch_cold<8>(a, p, s);
   }
   return hipErrorInvalidValue;
 }

@@ -16,10 +16,17 @@ constexpr int kBlock = 256;          // threads per workgroup of every fused ker
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
 // CSR kernel: LDS besides the output window and y, for `ept` entries per thread (row_ptr,
-// v and dots of two tiles and small scalars, 6472 bytes, plus two tiles of 16-bit row-start
+// v and dots of two tiles, a sink word per thread and small scalars, 7488 bytes, plus two tiles of 16-bit row-start
 // marks)
-constexpr size_t csr_static_lds(int ept) { return 6656 + 1024 * (size_t)ept; }
+constexpr size_t csr_static_lds(int ept) { return 7680 + 1024 * (size_t)ept; }
 constexpr size_t kAlign = 256;       // alignment of every workspace region
+// CSR binning of the columns outside the LDS window
+constexpr int kBinChunkItems = 512;  // (column, product) items per workspace chunk (4 KiB)
+constexpr int kMaxBins = 512;        // column bins of one call
+constexpr int kBinUnitChunks = 128;  // chunks one workgroup of the bin pass accumulates
+// LDS of the fused CSR kernel for the per-bin state (count, current chunk, fill, room, two
+// positions) when binning
+constexpr size_t kCsrBinStateBytes = 32;
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -49,17 +56,51 @@ struct CsrArgs {
   float* acc;         // [n] global accumulator of columns >= lds_window (zeroed before launch), or null
   int64_t lds_window;
   bool aligned;       // values and col_idx are 16-byte aligned: entries load as vectors
+  // binning of the columns >= lds_window (bins > 0; acc is then null)
+  int32_t bins;            // B = ceil((n - lds_window) / 2^bin_shift)
+  int32_t bin_shift;       // log2 of the columns per bin
+  int64_t pool_chunks;     // P: chunks in the pool (never exceeded: ceil(nnz / S) + grid * B)
+  uint32_t* pool_next;     // chunks handed out (zeroed before launch)
+  int2* pool;              // [P][kBinChunkItems] items {column, product bits}
+  int32_t* chunk_bin;      // [P] bin of each handed-out chunk
+  int32_t* chunk_fill;     // [P] items in each handed-out chunk
+};
+
+// Arguments of the bin passes (csr_bins.hip) that follow a binned fused launch.
+struct CsrBinArgs {
+  int64_t lds_window;
+  int32_t bins, bin_shift;
+  int64_t pool_chunks, max_units;
+  const uint32_t* pool_next;
+  const int2* pool;
+  const int32_t* chunk_bin;
+  const int32_t* chunk_fill;
+  int32_t* order;          // [P] chunk ids grouped by bin
+  int32_t* bin_start;      // [B + 1] first position in `order` of each bin
+  int32_t* unit_start;     // [B + 1] first unit of each bin (unit_start[B] = units in all)
+  float* partial2;         // [max_units][2^bin_shift] per-unit sums of the bin's columns
 };
 
 // Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first
 // HIP error it meets.
 hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s);
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
-// out[j] = alpha * (sum_{r < rows} partial[r * ldp + j] [j < ldp] + acc[j] [acc != null])
+// Bin passes: group the handed-out chunks by bin, then accumulate every unit of a bin in LDS.
+hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s);
+// Per-bin partial sums for the aggregation (null: no binning).
+struct BinPartials {
+  const float* partial2;
+  const int32_t* unit_start;
+  int64_t first_col;  // the first binned column (the LDS window)
+  int32_t bin_shift;
+};
+// out[j] = alpha * (sum_{r < rows} partial[r * ldp + j] [j < ldp] + acc[j] [acc != null]
+//                   + sum over the units u of j's bin of partial2[u][j - bin start] [binned j])
 //          + (beta != 0 ? beta * z[j] : 0),
 // in fp64, the partial rows summed in ascending order, rounded once.
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
-                            float alpha, float beta, const float* z, float* out, hipStream_t s);
+                            float alpha, float beta, const float* z, float* out, hipStream_t s,
+                            const BinPartials* bins = nullptr);
 // out[j] = (beta != 0) ? beta * z[j] : 0
 hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s);
 // p[i] = 0 for i < count (a kernel, so that the call stays graph-capturable)
@@ -100,9 +141,14 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p);
 
 struct CsrWorkspace {
   size_t partial_off, partial_rows;  // [grid][lds_window]
-  size_t acc_off;                    // [n] accumulator when lds_window < n
+  size_t acc_off;                    // [n] accumulator when lds_window < n and no binning
+  // binning (bins > 0)
+  int32_t bins, bin_shift;
+  int64_t pool_chunks, max_units;
+  size_t counter_off, pool_off, chunk_bin_off, chunk_fill_off, order_off, bin_start_off, unit_start_off,
+      partial2_off;
   size_t total;
 };
-CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p);
+CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p);
 
 }  // namespace xtvxy

@@ -73,12 +73,46 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
   return w;
 }
 
-CsrWorkspace csr_workspace(int64_t n, const xtvxy_launch_params& p) {
+CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p) {
+  (void)m;
   CsrWorkspace w{};
   w.partial_off = 0;
   w.partial_rows = (size_t)p.grid;
-  w.acc_off = align_up((size_t)p.grid * (size_t)p.lds_window * sizeof(float));
-  w.total = (p.lds_window < n) ? align_up(w.acc_off + (size_t)n * sizeof(float)) : w.acc_off;
+  size_t off = align_up((size_t)p.grid * (size_t)p.lds_window * sizeof(float));
+  if (p.lds_window >= n) {
+    w.total = off;
+    return w;
+  }
+  if (p.bin_columns <= 0) {
+    w.acc_off = off;
+    w.total = align_up(off + (size_t)n * sizeof(float));
+    return w;
+  }
+  // binning: every (workgroup, bin) pair leaves at most one chunk partly filled, so
+  // ceil(nnz / S) + grid * B chunks always suffice
+  int shift = 0;
+  while ((1 << shift) < p.bin_columns) ++shift;
+  w.bin_shift = shift;
+  w.bins = (int32_t)ceil_div(n - p.lds_window, (int64_t)p.bin_columns);
+  w.pool_chunks = ceil_div(std::max<int64_t>(nnz, 1), kBinChunkItems) + p.grid * (int64_t)w.bins;
+  w.max_units = ceil_div(w.pool_chunks, kBinUnitChunks) + w.bins;
+  w.counter_off = off;
+  off = align_up(off + sizeof(uint32_t));
+  w.pool_off = off;
+  off = align_up(off + (size_t)w.pool_chunks * kBinChunkItems * 2 * sizeof(int32_t));
+  w.chunk_bin_off = off;
+  off = align_up(off + (size_t)w.pool_chunks * sizeof(int32_t));
+  w.chunk_fill_off = off;
+  off = align_up(off + (size_t)w.pool_chunks * sizeof(int32_t));
+  w.order_off = off;
+  off = align_up(off + (size_t)w.pool_chunks * sizeof(int32_t));
+  w.bin_start_off = off;
+  off = align_up(off + (size_t)(w.bins + 1) * sizeof(int32_t));
+  w.unit_start_off = off;
+  off = align_up(off + (size_t)(w.bins + 1) * sizeof(int32_t));
+  w.partial2_off = off;
+  off = align_up(off + (size_t)w.max_units * (size_t)p.bin_columns * sizeof(float));
+  w.total = off;
   return w;
 }
 
@@ -186,21 +220,33 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
   return complete_dense(m, n, ldx, d, p);
 }
 
+int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
+  int64_t lds = ((int64_t)p.lds_window + (p.y_in_lds ? n : 0)) * (int64_t)sizeof(float);
+  if (bins > 0) lds = ((lds + 7) & ~(int64_t)7) + (int64_t)bins * (int64_t)kCsrBinStateBytes;
+  return lds + (int64_t)csr_static_lds(p.entries_per_thread);
+}
+
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p) {
-  (void)m;
-  (void)nnz;
   if (p->kernel != XTVXY_CSR_TILES || p->block_threads != kBlock || p->grid <= 0 || p->grid > INT32_MAX)
     return XTVXY_ERROR_INVALID_VALUE;
   if (p->entries_per_thread != 4 && p->entries_per_thread != 8)
     return XTVXY_ERROR_INVALID_VALUE;
   if (p->lds_window < 0 || p->lds_window > n || (p->y_in_lds != 0 && p->y_in_lds != 1))
     return XTVXY_ERROR_INVALID_VALUE;
-  const int64_t lds = ((int64_t)p->lds_window + (p->y_in_lds ? n : 0)) * (int64_t)sizeof(float) +
-                      (int64_t)csr_static_lds(p->entries_per_thread);
-  if (lds > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
+  const int32_t bc = p->bin_columns;
+  if (bc != 0 && (bc < 1024 || bc > 32768 || (bc & (bc - 1)) != 0)) return XTVXY_ERROR_INVALID_VALUE;
+  if (p->lds_window >= n) p->bin_columns = 0;  // nothing outside the window
+  const int32_t bins = p->bin_columns > 0 ? (int32_t)ceil_div(n - p->lds_window, p->bin_columns) : 0;
+  if (bins > kMaxBins) return XTVXY_ERROR_INVALID_VALUE;
+  if (csr_fused_lds(n, *p, bins) > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
+  if (bins > 0 && (int64_t)p->bin_columns * (int64_t)sizeof(float) > d.lds_bytes) return XTVXY_ERROR_INVALID_VALUE;
   p->group = 1;
-  p->workspace_bytes = (int64_t)csr_workspace(n, *p).total;
+  const CsrWorkspace w = csr_workspace(m, n, nnz, *p);
+  if (bins > 0 && (w.pool_chunks > INT32_MAX || (uint64_t)w.pool_chunks * kBinChunkItems > UINT32_MAX * 4ull ||
+                   w.max_units > INT32_MAX))
+    return XTVXY_ERROR_UNSUPPORTED;
+  p->workspace_bytes = (int64_t)w.total;
   return XTVXY_SUCCESS;
 }
 
@@ -217,13 +263,47 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   p->y_in_lds = ((int64_t)n * 4 <= kCsrYLdsMax) ? 1 : 0;
   const int64_t ybytes = p->y_in_lds ? (int64_t)n * 4 : 0;
   p->lds_window = (int32_t)std::min<int64_t>(n, (kCsrLdsBudget - ybytes) / 4);
-  const int64_t wg_lds = (int64_t)p->lds_window * 4 + ybytes + (int64_t)csr_static_lds(p->entries_per_thread);
+  // Columns outside the window: binned when the bins fit (bins of 16384 columns, or 32768
+  // when there would be too many), else global atomics. Binning costs a write and a read
+  // of 8 bytes per cold product and two more launches; atomics run at about kAtomicRate.
+  // The bin state takes LDS from the window so that two workgroups still fit on a CU.
+  int32_t bins = 0;
+  if (p->lds_window < n) {
+    for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
+      // the window shrinks by less than one bin, so one bin more than now is an upper bound
+      const int64_t b_max = ceil_div(n - p->lds_window, bc) + 1;
+      const int64_t win = std::max<int64_t>(
+          0, (d.lds_bytes / 2 - 512 - (int64_t)csr_static_lds(p->entries_per_thread) - ybytes - 8 -
+              b_max * (int64_t)kCsrBinStateBytes) / 4);
+      const int64_t w = std::min<int64_t>(win, p->lds_window);
+      const int64_t b = ceil_div(n - w, bc);
+      if (b <= kMaxBins && b <= b_max) {
+        bins = (int32_t)b;
+        p->bin_columns = bc;
+        p->lds_window = (int32_t)w;
+        break;
+      }
+    }
+  }
+  const int64_t wg_lds = csr_fused_lds(n, *p, bins);
   const int max_per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxWgPerCu, d.lds_bytes / wg_lds));
   const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
   const int64_t tile = (int64_t)kBlock * p->entries_per_thread;
   // the model knows nothing of the column distribution: it prices the columns outside
   // the window as uniformly hit
   const double cold = n > 0 ? (double)(n - p->lds_window) / n * nnz : 0.0;
+  double cold_cost = cold / kAtomicRate;
+  if (bins > 0) {
+    const double binned = 16.0 * cold / (kSustained * d.hbm_bytes_per_s) +
+                          (cold / ((double)kBinChunkItems * kBinUnitChunks) + bins) * p->bin_columns * 8.0 /
+                              (kSustained * d.hbm_bytes_per_s) +
+                          2 * kLaunch + 5e-6;
+    if (binned < cold_cost) {
+      cold_cost = binned;
+    } else {
+      p->bin_columns = 0;
+    }
+  }
   double best = 1e300;
   int64_t best_grid = 1;
   for (int k = 1; k <= max_per_cu; k *= 2) {
@@ -232,7 +312,7 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
     const double resident = std::min<double>(k, (double)grid / d.compute_units);
     const double bw = bandwidth(d, std::max(resident, 1.0 / d.compute_units) * tile * 8.0);
     const double partial_bytes = 2.0 * grid * p->lds_window * sizeof(float);
-    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + cold / kAtomicRate +
+    const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + cold_cost +
                      3 * kLaunch;
     if (t < best * 0.999) {
       best = t;

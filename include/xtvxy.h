@@ -50,7 +50,8 @@ typedef enum xtvxy_status {
   XTVXY_ERROR_NULL_POINTER = 2,  /* a required pointer is NULL (see each entry point) */
   XTVXY_ERROR_ALIASING = 3,      /* out overlaps an input other than z (out == z is allowed) */
   XTVXY_ERROR_WORKSPACE = 4,     /* workspace NULL or smaller than the query returned */
-  XTVXY_ERROR_UNSUPPORTED = 5,   /* nnz or m beyond int32 indexing */
+  XTVXY_ERROR_UNSUPPORTED = 5,   /* beyond int32 indexing: CSR nnz or n above 2^31 - 1, m above 2^31 - 1025;
+                                    the comparator: m, n or ldx above 2^31 - 1 */
   XTVXY_ERROR_LAUNCH = 6,        /* a HIP call failed (no device, launch failure, ...) */
   XTVXY_ERROR_LIBRARY = 7        /* rocBLAS / rocSPARSE failed (comparator entry points only) */
 } xtvxy_status;
@@ -82,7 +83,10 @@ enum {
   XTVXY_DENSE_GROUP_ROWS = 3  /* wider rows: `group` co-resident workgroups split a row by columns */
 };
 /* CSR kernel: tiles of whole rows; output columns [0, lds_window) accumulate in
- * LDS, the others in a global fp32 accumulator (hardware float atomics). */
+ * LDS. The other ("cold") columns either go to a global fp32 accumulator with
+ * hardware float atomics (bin_columns == 0), or are binned: the fused kernel
+ * appends each cold product to workspace chunks of its bin of bin_columns
+ * columns, and a second pass accumulates every bin in LDS (bin_columns > 0). */
 enum { XTVXY_CSR_TILES = 11 };
 
 /* Launch parameters chosen by the analytical model (the *_plan queries) or
@@ -99,7 +103,10 @@ typedef struct xtvxy_launch_params {
   int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile (4 or 8) */
   int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS (0..n) */
   int32_t y_in_lds;        /* csr: 1 = each workgroup copies y into LDS and gathers from there */
-  int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries) */
+  int32_t bin_columns;     /* csr: 0 = cold columns by global atomics; else columns per bin (power of
+                              two, 1024..32768; at most 512 bins, i.e. n - lds_window <= 512 bin_columns) */
+  int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries); with binning it
+                              grows with nnz: about 8 bytes per stored entry plus per-bin partial sums */
   double predicted_seconds;/* the model's estimate for this plan */
 } xtvxy_launch_params;
 

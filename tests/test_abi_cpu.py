@@ -170,5 +170,31 @@ def test_csr_model_plans(lib, m, n, nnz):
     assert 0 < p.lds_window <= n and p.workspace_bytes >= p.grid * p.lds_window * 4
     lds = (p.lds_window + (n if p.y_in_lds else 0)) * 4
     assert lds <= 64 * 1024
-    if p.lds_window < n:
+    if p.lds_window < n and p.bin_columns == 0:
         assert p.workspace_bytes >= p.grid * p.lds_window * 4 + n * 4
+    if p.bin_columns:
+        # binned: two workgroups per CU still fit, and the pool holds every stored entry
+        bins = -(-(n - p.lds_window) // p.bin_columns)
+        assert bins <= 512 and p.bin_columns & (p.bin_columns - 1) == 0
+        assert 2 * (lds + bins * 32 + 7680 + 8 * 1024) <= MI355X.lds_bytes
+        assert p.workspace_bytes >= nnz * 8
+
+
+def test_csr_model_bins_the_wide_zipf_matrix_and_not_the_narrow_one(lib):
+    assert xt.xtvxy_csr_f32_plan(5_000_000, 1_000_000, 200_000_000, MI355X).bin_columns == 16384
+    assert xt.xtvxy_csr_f32_plan(10_000_000, 1000, 100_000_000, MI355X).bin_columns == 0
+
+
+def test_csr_plan_complete_checks_the_bins(lib):
+    def lp(window, bc):
+        return xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=8, grid=64,
+                                      vec=1, chunks=1, group=1, lds_window=window, y_in_lds=0, bin_columns=bc)
+    n = 1000 + 512 * 1024
+    q = xt.xtvxy_csr_f32_plan_complete(1000, n, 10**6, lp(1000, 1024), MI355X)  # exactly 512 bins
+    assert q.workspace_bytes >= 10**6 * 8
+    for bad in (lp(999, 1024), lp(1000, 1000), lp(1000, 512), lp(1000, 65536)):
+        with pytest.raises(xt.XtvxyError):
+            xt.xtvxy_csr_f32_plan_complete(1000, n, 10**6, bad, MI355X)
+    # a window that covers every column needs no bins
+    q = xt.xtvxy_csr_f32_plan_complete(1000, 500, 10**4, lp(500, 1024), MI355X)
+    assert q.bin_columns == 0 and q.workspace_bytes == 64 * 500 * 4

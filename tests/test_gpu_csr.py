@@ -36,10 +36,19 @@ def forced_plans(m, n, nnz):
                 continue
             for ept in (4, 8):
                 for grid in (1, 7, 256):
-                    lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=ept,
-                                                grid=grid, vec=1, chunks=1, group=1, lds_window=w, y_in_lds=y_lds)
-                    out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
+                    # columns outside the window: global atomics, or bins of 1024 columns
+                    for bc in ((0, 1024) if w < n else (0,)):
+                        lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256,
+                                                    entries_per_thread=ept, grid=grid, vec=1, chunks=1, group=1,
+                                                    lds_window=w, y_in_lds=y_lds, bin_columns=bc)
+                        out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
     return out
+
+
+def binned_plan(m, n, nnz, window, bin_columns, grid=64, ept=8):
+    lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=ept, grid=grid,
+                                vec=1, chunks=1, group=1, lds_window=window, y_in_lds=0, bin_columns=bin_columns)
+    return xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp)
 
 
 @pytest.mark.parametrize("m,n,mean_len", [(2000, 500, 9.0), (500, 30000, 30.0)])
@@ -193,3 +202,46 @@ def test_repeated_calls_reuse_a_workspace():
         out = xt.csr(d.rp, d.ci, d.vals, p.n, d.y, d.v, d.z, p.alpha, p.beta, workspace=ws)
         torch.cuda.synchronize()
         assert_parity(out.cpu().numpy(), ref, bnd, "reuse")
+
+
+def test_binned_many_bins_spills_and_long_rows():
+    # 293 bins of 1024 columns; most entries fall in a few bins, so a tile hands a bin more
+    # items than one 512-item chunk holds; some rows are longer than a tile (binned in slices)
+    g = np.random.default_rng(12)
+    m, n = 3000, 300000
+    lens = g.integers(0, 30, size=m)
+    lens[[10, 500, 2999]] = [5000, 2100, 9000]
+    rp = np.zeros(m + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    hot = g.random(int(rp[-1])) < 0.7
+    cols = np.where(hot, g.integers(2048, 4096, size=hot.size), g.integers(0, n, size=hot.size))
+    row_of = np.repeat(np.arange(m), lens)
+    cols = cols[np.lexsort((cols, row_of))]  # sorted within rows (repeats allowed: each one counts)
+    p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols.astype(np.int32), datagen.uniform(int(rp[-1]), 12, "vals"),
+                           datagen.uniform(n, 12, "y"), datagen.uniform(m, 12, "v"), datagen.uniform(n, 12, "z"),
+                           0.75, 0.5, "binned spills")
+    for window, bc, grid, ept in [(0, 1024, 64, 8), (1000, 1024, 7, 4), (100, 2048, 256, 8), (16000, 32768, 1, 8)]:
+        check(p, plan=binned_plan(m, n, p.nnz, window, bc, grid, ept), what="binned w=%d bc=%d" % (window, bc))
+
+
+def test_binned_workspace_reuse_and_shrinking_input():
+    import torch
+    p = datagen.WORKLOADS["csr_5000000x1000000_zipf"](m=20_000, n=100_000)
+    plan = binned_plan(p.m, p.n, p.nnz, 2000, 4096, grid=128)
+    ws = torch.full((plan.workspace_bytes,), 255, dtype=torch.uint8, device="cuda")  # dirty workspace
+    d = CsrOnDevice(p)
+    ref, bnd = csr_oracle(p)
+    note("csr binned workspace reuse")
+    for _ in range(2):
+        out = xt.csr(d.rp, d.ci, d.vals, p.n, d.y, d.v, d.z, p.alpha, p.beta, plan=plan, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(out.cpu().numpy(), ref, bnd, "binned reuse")
+    # then a smaller matrix in the same workspace
+    q = datagen.csr_random(3000, 100_000, seed=13, mean_len=20.0)
+    plan_q = binned_plan(q.m, q.n, q.nnz, 2000, 4096, grid=128)
+    assert plan_q.workspace_bytes <= ws.numel()
+    dq = CsrOnDevice(q)
+    out = xt.csr(dq.rp, dq.ci, dq.vals, q.n, dq.y, dq.v, dq.z, q.alpha, q.beta, plan=plan_q, workspace=ws)
+    torch.cuda.synchronize()
+    ref_q, bnd_q = csr_oracle(q)
+    assert_parity(out.cpu().numpy(), ref_q, bnd_q, "binned smaller")
