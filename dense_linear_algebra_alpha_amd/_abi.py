@@ -38,7 +38,7 @@ class xtvxy_launch_params(ctypes.Structure):
                 ("lanes_per_row", ctypes.c_int32), ("chunks", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("rows_per_unit", ctypes.c_int64),
                 ("entries_per_thread", ctypes.c_int32), ("lds_window", ctypes.c_int32),
-                ("y_in_lds", ctypes.c_int32), ("bin_columns", ctypes.c_int32),
+                ("y_window", ctypes.c_int32), ("bin_columns", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_int64), ("predicted_seconds", ctypes.c_double)]
 
     def as_dict(self) -> dict:

@@ -227,6 +227,7 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   char* base = static_cast<char*>(ws);
   a.partial = reinterpret_cast<float*>(base + w.partial_off);
   a.lds_window = plan.lds_window;
+  a.y_window = plan.y_window;
   const bool binned = w.bins > 0;
   a.acc = (plan.lds_window < n && !binned) ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
   a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;

@@ -82,6 +82,9 @@ __device__ int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64_t m, i
 // Columns outside the LDS window: none (the window holds all of them), global float
 // atomics, or binned (see csr_bins.hip).
 enum ColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
+// Where y is gathered from: global memory, an LDS copy of all of it, or an LDS copy of
+// y[0, y_window) and global memory beyond.
+enum YMode { kYGlobal = 0, kYLds = 1, kYSplit = 2 };
 
 // The loads one tile needs, held in registers while the previous tile is processed.
 template <int K>
@@ -93,7 +96,7 @@ struct TileRegs {
   float v;      // v[r + tid]
 };
 
-template <int K, bool YLDS, bool HAS_V, bool ALIGNED, int COLD>
+template <int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
 __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
   constexpr int T = kBlock * K;
@@ -109,7 +112,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   __shared__ int32_t range_s[2];
   extern __shared__ __align__(16) float dyn[];
   float* out_s = dyn;                 // [lds_window]
-  float* y_s = dyn + a.lds_window;    // [n] when YLDS
+  float* y_s = dyn + a.lds_window;    // [y_window]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // Entry positions are unsigned 32-bit (nnz < 2^31, so a position plus a tile never wraps);
   // rows are signed 32-bit (m <= 2^31 - 1025, so a row plus 256 never overflows).
@@ -118,9 +121,8 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   const int32_t window = (int32_t)a.lds_window;
 
   for (int32_t j = tid; j < window; j += kBlock) out_s[j] = 0.0f;
-  if constexpr (YLDS) {
-    for (int32_t j = tid; j < (int32_t)a.n; j += kBlock) y_s[j] = a.y[j];
-  }
+  const int32_t y_window = YMODE == kYGlobal ? 0 : (int32_t)a.y_window;
+  for (int32_t j = tid; j < y_window; j += kBlock) y_s[j] = a.y[j];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   int32_t* fill_s = nullptr;
   uint32_t* room_s = nullptr;
   if constexpr (BINNED) {
-    const int64_t words = (a.lds_window + (YLDS ? a.n : 0) + 1) & ~(int64_t)1;  // 8-byte aligned
+    const int64_t words = (a.lds_window + y_window + 1) & ~(int64_t)1;  // 8-byte aligned
     pos1_s = reinterpret_cast<uint64_t*>(dyn + words);
     pos2_s = pos1_s + a.bins;
     cnt_s = reinterpret_cast<uint32_t*>(pos2_s + a.bins);
@@ -250,7 +252,15 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     for (int32_t c = tid; c < window; c += kBlock) dst[c] = 0.0f;
     return;
   }
-  const float* ysrc = YLDS ? y_s : a.y;
+  auto gather_y = [&](int32_t col) -> float {
+    if constexpr (YMODE == kYGlobal) return a.y[col];
+    if constexpr (YMODE == kYLds) return y_s[col];
+    // split: the LDS read is clamped (every lane issues it), the global read only where needed
+    const float fast = y_s[min(col, y_window - 1)];
+    float slow = 0.0f;
+    if (col >= y_window) slow = a.y[col];
+    return col < y_window ? fast : slow;
+  };
 
   auto issue_rows = [&](int32_t r, TileRegs<K>& g) {
     g.rp = a.row_ptr[min(r + tid, re)];
@@ -344,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     // (a) gathers of y for this tile's entries, before anything of the next tile is issued
     float yv[K];
 #pragma unroll
-    for (int k = 0; k < K; ++k) yv[k] = ysrc[g.col[k]];
+    for (int k = 0; k < K; ++k) yv[k] = gather_y(g.col[k]);
     // (b) the next tile's row_ptr, v and entries (they start where this tile ends)
     issue(min(ra_next, re - 1), pb, gn);
 
@@ -384,7 +394,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
         load_entries(sb, hv, hc);
         const uint32_t h0 = sb + (uint32_t)tid * K;
 #pragma unroll
-        for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * ysrc[hc[k]] : 0.0f;
+        for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * gather_y(hc[k]) : 0.0f;
       }
       s = group_sum(s, 64);
       if (lane == 0) lred[wave] = s;
@@ -501,26 +511,29 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   }
 }
 
-template <int K, bool YLDS, bool HAS_V, bool ALIGNED, int COLD>
+template <int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
 hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  size_t lds = ((size_t)a.lds_window + (YLDS ? (size_t)a.n : 0)) * sizeof(float);
+  size_t lds = ((size_t)a.lds_window + (YMODE == kYGlobal ? 0 : (size_t)a.y_window)) * sizeof(float);
   if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
-  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YLDS, HAS_V, ALIGNED, COLD>);
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YMODE, HAS_V, ALIGNED, COLD>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_fused<K, YLDS, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL((csr_fused<K, YMODE, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
   return hipGetLastError();
+}
+
+template <int K, int COLD, int YMODE>
+hipError_t launch_kv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  const bool hv = a.v != nullptr, al = a.aligned;
+  if (hv) return al ? launch_k<K, YMODE, true, true, COLD>(a, p, s) : launch_k<K, YMODE, true, false, COLD>(a, p, s);
+  return al ? launch_k<K, YMODE, false, true, COLD>(a, p, s) : launch_k<K, YMODE, false, false, COLD>(a, p, s);
 }
 
 template <int K, int COLD>
 hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const bool yl = p.y_in_lds != 0, hv = a.v != nullptr, al = a.aligned;
-  if (yl) {
-    if (hv) return al ? launch_k<K, true, true, true, COLD>(a, p, s) : launch_k<K, true, true, false, COLD>(a, p, s);
-    return al ? launch_k<K, true, false, true, COLD>(a, p, s) : launch_k<K, true, false, false, COLD>(a, p, s);
-  }
-  if (hv) return al ? launch_k<K, false, true, true, COLD>(a, p, s) : launch_k<K, false, true, false, COLD>(a, p, s);
-  return al ? launch_k<K, false, false, true, COLD>(a, p, s) : launch_k<K, false, false, false, COLD>(a, p, s);
+  if (a.y_window >= a.n) return launch_kv<K, COLD, kYLds>(a, p, s);
+  if (a.y_window > 0) return launch_kv<K, COLD, kYSplit>(a, p, s);
+  return launch_kv<K, COLD, kYGlobal>(a, p, s);
 }
 
 template <int K>
@@ -536,7 +549,7 @@ hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_
   if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES)
     return hipErrorInvalidValue;
   if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
-      a.lds_window > a.n)
+      a.lds_window > a.n || a.y_window < 0 || a.y_window > a.n)
     return hipErrorInvalidValue;
   const bool binned = a.bins > 0;
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||

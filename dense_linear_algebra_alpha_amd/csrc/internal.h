@@ -55,6 +55,7 @@ struct CsrArgs {
   float* partial;     // [grid][lds_window] per-workgroup partial sums of output columns [0, lds_window)
   float* acc;         // [n] global accumulator of columns >= lds_window (zeroed before launch), or null
   int64_t lds_window;
+  int64_t y_window;   // y[0, y_window) is gathered from an LDS copy, the rest from global memory
   bool aligned;       // values and col_idx are 16-byte aligned: entries load as vectors
   // binning of the columns >= lds_window (bins > 0; acc is then null)
   int32_t bins;            // B = ceil((n - lds_window) / 2^bin_shift)

@@ -35,8 +35,8 @@ constexpr double kLatency = 4.5e-6;     // seconds of loaded-memory latency that
 constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
 constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
-constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output window and y
-constexpr int64_t kCsrYLdsMax = 16 * 1024;    // CSR: largest y copied into LDS
+constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output and y windows
+constexpr int kCsrWgPerCuLarge = 4;          // CSR: workgroups per CU the windows leave room for when n is large
 
 int next_pow2(int64_t x) {
   int p = 1;
@@ -221,7 +221,8 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
 }
 
 int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
-  int64_t lds = ((int64_t)p.lds_window + (p.y_in_lds ? n : 0)) * (int64_t)sizeof(float);
+  (void)n;
+  int64_t lds = ((int64_t)p.lds_window + (int64_t)p.y_window) * (int64_t)sizeof(float);
   if (bins > 0) lds = ((lds + 7) & ~(int64_t)7) + (int64_t)bins * (int64_t)kCsrBinStateBytes;
   return lds + (int64_t)csr_static_lds(p.entries_per_thread);
 }
@@ -232,7 +233,7 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
     return XTVXY_ERROR_INVALID_VALUE;
   if (p->entries_per_thread != 4 && p->entries_per_thread != 8)
     return XTVXY_ERROR_INVALID_VALUE;
-  if (p->lds_window < 0 || p->lds_window > n || (p->y_in_lds != 0 && p->y_in_lds != 1))
+  if (p->lds_window < 0 || p->lds_window > n || p->y_window < 0 || p->y_window > n)
     return XTVXY_ERROR_INVALID_VALUE;
   const int32_t bc = p->bin_columns;
   if (bc != 0 && (bc < 1024 || bc > 32768 || (bc & (bc - 1)) != 0)) return XTVXY_ERROR_INVALID_VALUE;
@@ -258,31 +259,32 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   p->chunks = 1;
   p->group = 1;
   p->entries_per_thread = 8;
-  // y is copied into LDS when it is small; the output window takes what remains of a
-  // budget that leaves room for several workgroups per CU
-  p->y_in_lds = ((int64_t)n * 4 <= kCsrYLdsMax) ? 1 : 0;
-  const int64_t ybytes = p->y_in_lds ? (int64_t)n * 4 : 0;
-  p->lds_window = (int32_t)std::min<int64_t>(n, (kCsrLdsBudget - ybytes) / 4);
-  // Columns outside the window: binned when the bins fit (bins of 16384 columns, or 32768
-  // when there would be too many), else global atomics. Binning costs a write and a read
-  // of 8 bytes per cold product and two more launches; atomics run at about kAtomicRate.
-  // The bin state takes LDS from the window so that two workgroups still fit on a CU.
+  // Both windows (the output columns accumulated in LDS, and the part of y gathered from
+  // LDS) cover all of n when they fit a budget that leaves room for several workgroups per
+  // CU. Otherwise latency hiding matters more than window size (measured on a Zipf-skewed
+  // 10^6-column matrix): the windows share what four workgroups per CU leave, three parts
+  // for the output and one for y, and the columns outside the output window are binned when
+  // the bins fit (bins of 16384 columns, or 32768 when there would be too many), else sent to
+  // global atomics. Binning costs a write and a read of 8 bytes per cold product and two more
+  // launches; atomics run at about kAtomicRate.
   int32_t bins = 0;
-  if (p->lds_window < n) {
+  if ((int64_t)n * 8 <= kCsrLdsBudget) {
+    p->lds_window = (int32_t)n;
+    p->y_window = (int32_t)n;
+  } else {
+    p->lds_window = (int32_t)std::min<int64_t>(n, kCsrLdsBudget / 8);
+    p->y_window = p->lds_window;
     for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
-      // the window shrinks by less than one bin, so one bin more than now is an upper bound
-      const int64_t b_max = ceil_div(n - p->lds_window, bc) + 1;
-      const int64_t win = std::max<int64_t>(
-          0, (d.lds_bytes / 2 - 512 - (int64_t)csr_static_lds(p->entries_per_thread) - ybytes - 8 -
-              b_max * (int64_t)kCsrBinStateBytes) / 4);
-      const int64_t w = std::min<int64_t>(win, p->lds_window);
-      const int64_t b = ceil_div(n - w, bc);
-      if (b <= kMaxBins && b <= b_max) {
-        bins = (int32_t)b;
-        p->bin_columns = bc;
-        p->lds_window = (int32_t)w;
-        break;
-      }
+      const int64_t b = ceil_div(n, bc);  // at least as many bins as any window leaves
+      if (b > kMaxBins) continue;
+      const int64_t avail = d.lds_bytes / kCsrWgPerCuLarge - 512 - (int64_t)csr_static_lds(p->entries_per_thread) -
+                            8 - b * (int64_t)kCsrBinStateBytes;
+      const int64_t cols = std::max<int64_t>(avail, 0) / 4;
+      bins = (int32_t)ceil_div(n - std::min<int64_t>(n, cols * 3 / 4), bc);
+      p->bin_columns = bc;
+      p->lds_window = (int32_t)std::min<int64_t>(n, cols * 3 / 4);
+      p->y_window = (int32_t)std::min<int64_t>(n, cols - p->lds_window);
+      break;
     }
   }
   const int64_t wg_lds = csr_fused_lds(n, *p, bins);

@@ -102,7 +102,8 @@ typedef struct xtvxy_launch_params {
   int64_t rows_per_unit;   /* dense: rows per workgroup (wave/block paths) or per group */
   int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile (4 or 8) */
   int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS (0..n) */
-  int32_t y_in_lds;        /* csr: 1 = each workgroup copies y into LDS and gathers from there */
+  int32_t y_window;        /* csr: y[0, y_window) is copied into each workgroup's LDS and gathered from
+                              there, columns >= y_window from global memory (0..n) */
   int32_t bin_columns;     /* csr: 0 = cold columns by global atomics; else columns per bin (power of
                               two, 1024..32768; at most 512 bins, i.e. n - lds_window <= 512 bin_columns) */
   int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries); with binning it

@@ -168,7 +168,7 @@ def test_csr_model_plans(lib, m, n, nnz):
     p = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
     assert p.kernel == xt.XTVXY_CSR_TILES and p.grid >= 1 and p.entries_per_thread in (4, 8, 16)
     assert 0 < p.lds_window <= n and p.workspace_bytes >= p.grid * p.lds_window * 4
-    lds = (p.lds_window + (n if p.y_in_lds else 0)) * 4
+    lds = (p.lds_window + p.y_window) * 4
     assert lds <= 64 * 1024
     if p.lds_window < n and p.bin_columns == 0:
         assert p.workspace_bytes >= p.grid * p.lds_window * 4 + n * 4
@@ -188,7 +188,7 @@ def test_csr_model_bins_the_wide_zipf_matrix_and_not_the_narrow_one(lib):
 def test_csr_plan_complete_checks_the_bins(lib):
     def lp(window, bc):
         return xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=8, grid=64,
-                                      vec=1, chunks=1, group=1, lds_window=window, y_in_lds=0, bin_columns=bc)
+                                      vec=1, chunks=1, group=1, lds_window=window, y_window=0, bin_columns=bc)
     n = 1000 + 512 * 1024
     q = xt.xtvxy_csr_f32_plan_complete(1000, n, 10**6, lp(1000, 1024), MI355X)  # exactly 512 bins
     assert q.workspace_bytes >= 10**6 * 8
