@@ -8,9 +8,9 @@
 // Work split: workgroup w owns the rows whose first entry lies in
 // [w q, (w + 1) q), q = ceil(nnz / grid), so every workgroup streams about the
 // same number of entries (one wavefront finds the two boundaries with a 64-way
-// search of row_ptr). The workgroup then walks its rows in tiles of at most
-// 256 rows and T = 256 K entries, the tile being the longest run of whole rows
-// whose entries fit:
+// search of row_ptr). The workgroup (BLK = 256 or 512 threads) then walks its
+// rows in tiles of at most BLK rows and T = BLK K entries, the tile being the
+// longest run of whole rows whose entries fit:
 //   1. thread t holds the K consecutive entries starting at base + K t (base =
 //      the tile's first entry rounded down to a multiple of 4), loaded as
 //      16-byte vectors of values and of column indices, and gathers y[column]
@@ -49,7 +49,6 @@
 namespace xtvxy {
 namespace {
 
-constexpr int kTileRows = kBlock;  // rows a tile stages: one row_ptr per thread
 
 typedef __attribute__((address_space(1))) float global_float;
 typedef __attribute__((address_space(1))) uint32_t global_uint;
@@ -96,19 +95,20 @@ struct TileRegs {
   float v;      // v[r + tid]
 };
 
-template <int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
-__global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+__global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
+  static_assert(BLK == 256 || BLK == 512, "workgroups of 256 or 512 threads");
   static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
-  constexpr int T = kBlock * K;
+  constexpr int T = BLK * K;  // entry slots of a tile; a tile also holds at most BLK rows
   constexpr bool BINNED = COLD == kColdBinned;
   // per-tile state, double-buffered by tile parity
-  __shared__ int32_t rp_s[2][kTileRows + 1];  // row_ptr of the tile's rows
-  __shared__ float v_s[2][kTileRows];         // v of the tile's rows
-  __shared__ float u_s[2][kTileRows];         // u_row = v_row * (row dot), built by the dots
+  __shared__ int32_t rp_s[2][BLK + 1];  // row_ptr of the tile's rows
+  __shared__ float v_s[2][BLK];         // v of the tile's rows
+  __shared__ float u_s[2][BLK];         // u_row = v_row * (row dot), built by the dots
   __shared__ __align__(16) uint16_t mark_s[2][T];  // 1 + tile row whose first entry sits at slot q, else 0
-  __shared__ int32_t wfirst_s[2][kWaves];     // tile row holding the first entry of each wavefront
-  __shared__ float sink_s[kBlock];            // a private LDS word per thread for masked-off adds
-  __shared__ float lred[kWaves];
+  __shared__ int32_t wfirst_s[2][(BLK / 64)];     // tile row holding the first entry of each wavefront
+  __shared__ float sink_s[BLK];            // a private LDS word per thread for masked-off adds
+  __shared__ float lred[(BLK / 64)];
   __shared__ int32_t range_s[2];
   extern __shared__ __align__(16) float dyn[];
   float* out_s = dyn;                 // [lds_window]
@@ -120,14 +120,14 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   const uint32_t nnz_full = nnz & ~3u;  // entries in whole aligned quads
   const int32_t window = (int32_t)a.lds_window;
 
-  for (int32_t j = tid; j < window; j += kBlock) out_s[j] = 0.0f;
+  for (int32_t j = tid; j < window; j += BLK) out_s[j] = 0.0f;
   const int32_t y_window = YMODE == kYGlobal ? 0 : (int32_t)a.y_window;
-  for (int32_t j = tid; j < y_window; j += kBlock) y_s[j] = a.y[j];
+  for (int32_t j = tid; j < y_window; j += BLK) y_s[j] = a.y[j];
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
 #pragma unroll
     for (int k = 0; k < K; ++k) mark_s[b][tid * K + k] = 0;
-    if (tid < kWaves) wfirst_s[b][tid] = 0;
+    if (tid < (BLK / 64)) wfirst_s[b][tid] = 0;
   }
   sink_s[tid] = 0.0f;
   // Binning of the columns >= window. Per bin, in LDS: the items of the current batch (a
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     cur_s = reinterpret_cast<int32_t*>(cnt_s + a.bins);
     fill_s = cur_s + a.bins;
     room_s = reinterpret_cast<uint32_t*>(fill_s + a.bins);
-    for (int t = tid; t < a.bins; t += kBlock) {
+    for (int t = tid; t < a.bins; t += BLK) {
       cnt_s[t] = 0;
       cur_s[t] = -1;
       fill_s[t] = (int32_t)S;
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   // bin's items, handing out new pool chunks (one global atomic per bin and batch that spills),
   // and resets the count. A barrier must follow before bin_write.
   auto bin_alloc = [&]() {
-    for (int t = tid; t < a.bins; t += kBlock) {
+    for (int t = tid; t < a.bins; t += BLK) {
       const uint32_t cnt = cnt_s[t];
       if (cnt == 0) continue;
       cnt_s[t] = 0;
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   const int32_t rb = range_s[0], re = range_s[1];
   if (rb >= re) {
     float* dst = a.partial + (int64_t)blockIdx.x * window;
-    for (int32_t c = tid; c < window; c += kBlock) dst[c] = 0.0f;
+    for (int32_t c = tid; c < window; c += BLK) dst[c] = 0.0f;
     return;
   }
   auto gather_y = [&](int32_t col) -> float {
@@ -320,7 +320,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
       const uint32_t s = (uint32_t)g.rp - base, e = (uint32_t)g.rp1 - base;
       if (e > s && s < T) mark_s[b][s] = (uint16_t)(tid + 1);
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
+      for (int w = 0; w < (BLK / 64); ++w) {
         const uint32_t pw = w == 0 ? first - base : (uint32_t)(w * 64 * K);
         if (s <= pw && pw < e) wfirst_s[b][w] = tid;
       }
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   TileRegs<K> ga, gb;
   int buf = 0;
   int32_t ra = rb;
-  int cnt = min(kTileRows, re - ra);
+  int cnt = min(BLK, re - ra);
   int j;
   {
     const uint32_t p0 = (uint32_t)a.row_ptr[ra];
@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
     const uint32_t pb = (uint32_t)(long_row ? rp_s[b][1] : rp_s[b][j]);
     const int32_t ra_next = ra + (long_row ? 1 : j);
     const bool more = ra_next < re;
-    const int cnt_next = more ? min(kTileRows, re - ra_next) : 0;
+    const int cnt_next = more ? min(BLK, re - ra_next) : 0;
     const uint32_t e0 = base + (uint32_t)tid * K;
 
     // (a) gathers of y for this tile's entries, before anything of the next tile is issued
@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
       __syncthreads();
       float t = lred[0];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) t += lred[w];
+      for (int w = 1; w < (BLK / 64); ++w) t += lred[w];
       const float u = v_s[b][0] * t;
       {
         float c[K];
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
       const int wf = wfirst_s[b][wave];
       const int before = max(wf, dpp_int<dpp::kWaveShr1>(-1, wave_max_scan(run_max)));
 #pragma unroll
-      for (int k = 0; k < K; ++k) rk[k] = max(before, mk[k]);  // in [0, kTileRows)
+      for (int k = 0; k < K; ++k) rk[k] = max(before, mk[k]);  // in [0, BLK)
 
       // (d) per-row dots. Runs of one row inside the thread are summed in registers; a row
       // strictly inside the thread is complete and stored; the first run (head) and the last
@@ -500,54 +500,54 @@ __global__ __launch_bounds__(kBlock) void csr_fused(CsrArgs a) {
   }
   if constexpr (BINNED) {
     // the fill of each bin's last chunk (every other handed-out chunk is full)
-    for (int t = tid; t < a.bins; t += kBlock)
+    for (int t = tid; t < a.bins; t += BLK)
       if (cur_s[t] >= 0) a.chunk_fill[cur_s[t]] = fill_s[t];
   }
 
   if (window > 0) {
     __syncthreads();
     float* dst = a.partial + (int64_t)blockIdx.x * window;
-    for (int32_t c = tid; c < window; c += kBlock) dst[c] = out_s[c];
+    for (int32_t c = tid; c < window; c += BLK) dst[c] = out_s[c];
   }
 }
 
-template <int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
 hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   size_t lds = ((size_t)a.lds_window + (YMODE == kYGlobal ? 0 : (size_t)a.y_window)) * sizeof(float);
   if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
-  const void* fn = reinterpret_cast<const void*>(&csr_fused<K, YMODE, HAS_V, ALIGNED, COLD>);
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_fused<K, YMODE, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(kBlock), lds, s, a);
+  hipLaunchKernelGGL((csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(BLK), lds, s, a);
   return hipGetLastError();
 }
 
-template <int K, int COLD, int YMODE>
+template <int BLK, int K, int COLD, int YMODE>
 hipError_t launch_kv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const bool hv = a.v != nullptr, al = a.aligned;
-  if (hv) return al ? launch_k<K, YMODE, true, true, COLD>(a, p, s) : launch_k<K, YMODE, true, false, COLD>(a, p, s);
-  return al ? launch_k<K, YMODE, false, true, COLD>(a, p, s) : launch_k<K, YMODE, false, false, COLD>(a, p, s);
+  if (hv)
+    return al ? launch_k<BLK, K, YMODE, true, true, COLD>(a, p, s) : launch_k<BLK, K, YMODE, true, false, COLD>(a, p, s);
+  return al ? launch_k<BLK, K, YMODE, false, true, COLD>(a, p, s) : launch_k<BLK, K, YMODE, false, false, COLD>(a, p, s);
 }
 
-template <int K, int COLD>
+template <int BLK, int K, int COLD>
 hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.y_window >= a.n) return launch_kv<K, COLD, kYLds>(a, p, s);
-  if (a.y_window > 0) return launch_kv<K, COLD, kYSplit>(a, p, s);
-  return launch_kv<K, COLD, kYGlobal>(a, p, s);
+  if (a.y_window >= a.n) return launch_kv<BLK, K, COLD, kYLds>(a, p, s);
+  if (a.y_window > 0) return launch_kv<BLK, K, COLD, kYSplit>(a, p, s);
+  return launch_kv<BLK, K, COLD, kYGlobal>(a, p, s);
 }
 
-template <int K>
+template <int BLK, int K>
 hipError_t launch_cold(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.bins > 0) return launch_kk<K, kColdBinned>(a, p, s);
-  if (a.lds_window < a.n) return launch_kk<K, kColdAtomic>(a, p, s);
-  return launch_kk<K, kColdNone>(a, p, s);
+  if (a.bins > 0) return launch_kk<BLK, K, kColdBinned>(a, p, s);
+  if (a.lds_window < a.n) return launch_kk<BLK, K, kColdAtomic>(a, p, s);
+  return launch_kk<BLK, K, kColdNone>(a, p, s);
 }
 
 }  // namespace
 
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES)
-    return hipErrorInvalidValue;
+  if (p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES) return hipErrorInvalidValue;
   if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
       a.lds_window > a.n || a.y_window < 0 || a.y_window > a.n)
     return hipErrorInvalidValue;
@@ -556,10 +556,10 @@ hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
   if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
-  switch (p.entries_per_thread) {
-    case 4: return launch_cold<4>(a, p, s);
-    case 8: return launch_cold<8>(a, p, s);
-  }
+  // (threads, entries per thread): 256 x 4, 256 x 8 and 512 x 8
+  if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4>(a, p, s);
+  if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8>(a, p, s);
+  if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8>(a, p, s);
   return hipErrorInvalidValue;
 }
 

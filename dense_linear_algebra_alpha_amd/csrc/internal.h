@@ -15,10 +15,10 @@ namespace xtvxy {
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
-// CSR kernel: LDS besides the output window and y, for `ept` entries per thread (row_ptr,
-// v and dots of two tiles, a sink word per thread and small scalars, 7488 bytes, plus two tiles of 16-bit row-start
-// marks)
-constexpr size_t csr_static_lds(int ept) { return 7680 + 1024 * (size_t)ept; }
+// CSR kernel: LDS besides the output and y windows, for workgroups of `blk` threads holding
+// `ept` entries each: row_ptr, v and dots of two tiles, a sink word per thread and small
+// scalars (29 blk + 64 bytes), plus two tiles of 16-bit row-start marks (4 blk ept bytes)
+constexpr size_t csr_static_lds(int ept, int blk) { return 29 * (size_t)blk + 256 + 4 * (size_t)blk * ept; }
 constexpr size_t kAlign = 256;       // alignment of every workspace region
 // CSR binning of the columns outside the LDS window
 constexpr int kBinChunkItems = 512;  // (column, product) items per workspace chunk (4 KiB)

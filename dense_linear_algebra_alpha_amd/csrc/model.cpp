@@ -36,7 +36,8 @@ constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
 constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
 constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output and y windows
-constexpr int kCsrWgPerCuLarge = 4;          // CSR: workgroups per CU the windows leave room for when n is large
+constexpr int kCsrThreadsPerCuLarge = 1024;  // CSR: threads per CU the windows leave room for when n is large
+constexpr int kMaxThreadsPerCu = 2048;       // 32 wavefronts
 
 int next_pow2(int64_t x) {
   int p = 1;
@@ -224,15 +225,16 @@ int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
   (void)n;
   int64_t lds = ((int64_t)p.lds_window + (int64_t)p.y_window) * (int64_t)sizeof(float);
   if (bins > 0) lds = ((lds + 7) & ~(int64_t)7) + (int64_t)bins * (int64_t)kCsrBinStateBytes;
-  return lds + (int64_t)csr_static_lds(p.entries_per_thread);
+  return lds + (int64_t)csr_static_lds(p.entries_per_thread, p.block_threads);
 }
 
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p) {
-  if (p->kernel != XTVXY_CSR_TILES || p->block_threads != kBlock || p->grid <= 0 || p->grid > INT32_MAX)
-    return XTVXY_ERROR_INVALID_VALUE;
-  if (p->entries_per_thread != 4 && p->entries_per_thread != 8)
-    return XTVXY_ERROR_INVALID_VALUE;
+  if (p->kernel != XTVXY_CSR_TILES || p->grid <= 0 || p->grid > INT32_MAX) return XTVXY_ERROR_INVALID_VALUE;
+  // (threads, entries per thread): 256 x 4, 256 x 8 or 512 x 8
+  const bool shape_ok = (p->block_threads == 256 && (p->entries_per_thread == 4 || p->entries_per_thread == 8)) ||
+                        (p->block_threads == 512 && p->entries_per_thread == 8);
+  if (!shape_ok) return XTVXY_ERROR_INVALID_VALUE;
   if (p->lds_window < 0 || p->lds_window > n || p->y_window < 0 || p->y_window > n)
     return XTVXY_ERROR_INVALID_VALUE;
   const int32_t bc = p->bin_columns;
@@ -254,7 +256,7 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
 xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d, xtvxy_launch_params* p) {
   std::memset(p, 0, sizeof(*p));
   p->kernel = XTVXY_CSR_TILES;
-  p->block_threads = kBlock;
+  p->block_threads = 256;
   p->vec = 1;
   p->chunks = 1;
   p->group = 1;
@@ -262,8 +264,9 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   // Both windows (the output columns accumulated in LDS, and the part of y gathered from
   // LDS) cover all of n when they fit a budget that leaves room for several workgroups per
   // CU. Otherwise latency hiding matters more than window size (measured on a Zipf-skewed
-  // 10^6-column matrix): the windows share what four workgroups per CU leave, three parts
-  // for the output and one for y, and the columns outside the output window are binned when
+  // 10^6-column matrix): workgroups of 512 threads (tiles of 4096 entries, half the barriers
+  // per entry), sized so that two fit on a CU, and the windows share the LDS that leaves,
+  // three parts for the output and one for y. The columns outside the output window are binned when
   // the bins fit (bins of 16384 columns, or 32768 when there would be too many), else sent to
   // global atomics. Binning costs a write and a read of 8 bytes per cold product and two more
   // launches; atomics run at about kAtomicRate.
@@ -274,10 +277,12 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   } else {
     p->lds_window = (int32_t)std::min<int64_t>(n, kCsrLdsBudget / 8);
     p->y_window = p->lds_window;
+    p->block_threads = 512;
     for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
       const int64_t b = ceil_div(n, bc);  // at least as many bins as any window leaves
       if (b > kMaxBins) continue;
-      const int64_t avail = d.lds_bytes / kCsrWgPerCuLarge - 512 - (int64_t)csr_static_lds(p->entries_per_thread) -
+      const int64_t avail = d.lds_bytes / (kCsrThreadsPerCuLarge / p->block_threads) - 512 -
+                            (int64_t)csr_static_lds(p->entries_per_thread, p->block_threads) -
                             8 - b * (int64_t)kCsrBinStateBytes;
       const int64_t cols = std::max<int64_t>(avail, 0) / 4;
       bins = (int32_t)ceil_div(n - std::min<int64_t>(n, cols * 3 / 4), bc);
@@ -288,9 +293,10 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
     }
   }
   const int64_t wg_lds = csr_fused_lds(n, *p, bins);
-  const int max_per_cu = (int)std::max<int64_t>(1, std::min<int64_t>(kMaxWgPerCu, d.lds_bytes / wg_lds));
+  const int max_per_cu =
+      (int)std::max<int64_t>(1, std::min<int64_t>(kMaxThreadsPerCu / p->block_threads, d.lds_bytes / wg_lds));
   const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
-  const int64_t tile = (int64_t)kBlock * p->entries_per_thread;
+  const int64_t tile = (int64_t)p->block_threads * p->entries_per_thread;
   // the model knows nothing of the column distribution: it prices the columns outside
   // the window as uniformly hit
   const double cold = n > 0 ? (double)(n - p->lds_window) / n * nnz : 0.0;

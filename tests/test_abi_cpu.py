@@ -176,7 +176,8 @@ def test_csr_model_plans(lib, m, n, nnz):
         # binned: two workgroups per CU still fit, and the pool holds every stored entry
         bins = -(-(n - p.lds_window) // p.bin_columns)
         assert bins <= 512 and p.bin_columns & (p.bin_columns - 1) == 0
-        assert 2 * (lds + bins * 32 + 7680 + 8 * 1024) <= MI355X.lds_bytes
+        static = 29 * p.block_threads + 256 + 4 * p.block_threads * p.entries_per_thread
+        assert (2048 // p.block_threads) // 2 * (lds + bins * 32 + static) <= MI355X.lds_bytes
         assert p.workspace_bytes >= nnz * 8
 
 

@@ -28,26 +28,26 @@ def test_irregular_matrices(m, n, mean_len):
 def forced_plans(m, n, nnz):
     """Output windows from none to all of n, y gathered from global memory, from LDS or split,
     each tile size, a few grids, and the columns outside the window by atomics or in bins."""
-    fixed = 16384  # more than the kernel's own LDS for any tile size
+    fixed = 32768  # more than the kernel's own LDS for any workgroup and tile size
     windows = sorted({0, min(n, 7), min(n, 4096), n if n * 4 + fixed <= 163840 else min(n, 30000)})
     out = []
     for w in windows:
         for yw in sorted({0, min(n, 300), n}):
             if (w + yw) * 4 + fixed > 163840:
                 continue
-            for ept in (4, 8):
+            for blk, ept in ((256, 4), (256, 8), (512, 8)):
                 for grid in (1, 7, 256):
                     # columns outside the window: global atomics, or bins of 1024 columns
                     for bc in ((0, 1024) if w < n else (0,)):
-                        lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256,
+                        lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=blk,
                                                     entries_per_thread=ept, grid=grid, vec=1, chunks=1, group=1,
                                                     lds_window=w, y_window=yw, bin_columns=bc)
                         out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
     return out
 
 
-def binned_plan(m, n, nnz, window, bin_columns, grid=64, ept=8, y_window=0):
-    lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=256, entries_per_thread=ept, grid=grid,
+def binned_plan(m, n, nnz, window, bin_columns, grid=64, ept=8, y_window=0, blk=256):
+    lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=blk, entries_per_thread=ept, grid=grid,
                                 vec=1, chunks=1, group=1, lds_window=window, y_window=y_window,
                                 bin_columns=bin_columns)
     return xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp)
@@ -222,9 +222,11 @@ def test_binned_many_bins_spills_and_long_rows():
     p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols.astype(np.int32), datagen.uniform(int(rp[-1]), 12, "vals"),
                            datagen.uniform(n, 12, "y"), datagen.uniform(m, 12, "v"), datagen.uniform(n, 12, "z"),
                            0.75, 0.5, "binned spills")
-    for window, bc, grid, ept, yw in [(0, 1024, 64, 8, 0), (1000, 1024, 7, 4, 3000), (100, 2048, 256, 8, 0),
-                                      (16000, 32768, 1, 8, 16000)]:
-        check(p, plan=binned_plan(m, n, p.nnz, window, bc, grid, ept, yw), what="binned w=%d bc=%d yw=%d" % (window, bc, yw))
+    for window, bc, grid, ept, yw, blk in [(0, 1024, 64, 8, 0, 256), (1000, 1024, 7, 4, 3000, 256),
+                                           (100, 2048, 256, 8, 0, 512), (16000, 32768, 1, 8, 16000, 256),
+                                           (9000, 16384, 5, 8, 3000, 512)]:
+        check(p, plan=binned_plan(m, n, p.nnz, window, bc, grid, ept, yw, blk),
+              what="binned w=%d bc=%d yw=%d blk=%d" % (window, bc, yw, blk))
 
 
 def test_binned_workspace_reuse_and_shrinking_input():
