@@ -250,6 +250,7 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
     bargs.chunk_bin = a.chunk_bin;
     bargs.chunk_fill = a.chunk_fill;
     bargs.order = reinterpret_cast<int32_t*>(base + w.order_off);
+    bargs.counts = reinterpret_cast<int32_t*>(base + w.counts_off);
     bargs.bin_start = reinterpret_cast<int32_t*>(base + w.bin_start_off);
     bargs.unit_start = reinterpret_cast<int32_t*>(base + w.unit_start_off);
     bargs.partial2 = reinterpret_cast<float*>(base + w.partial2_off);

@@ -4,11 +4,12 @@
 // partial results are aggregated hierarchically. For the columns the fused
 // kernel cannot hold in LDS, it does not add into global memory with atomics;
 // it appends each product u_i * x_ij, with its column, to workspace chunks of
-// the column's bin (bins of 2^bin_shift columns). These two kernels finish the
+// the column's bin (bins of 2^bin_shift columns). These kernels finish the
 // sum:
-//   bin_sort        one workgroup groups the handed-out chunks by bin (a
-//                   counting sort of chunk ids) and cuts every bin into units
-//                   of at most kBinUnitChunks chunks;
+//   bin_count, bin_scan, bin_place
+//                   a counting sort of the handed-out chunk ids by bin (per
+//                   workgroup counts, one scan, placement), which also cuts
+//                   every bin into units of at most kBinUnitChunks chunks;
 //   bin_accumulate  one workgroup per unit adds the unit's items into an LDS
 //                   copy of the bin's columns and writes it as one partial row.
 // aggregate.hip then sums, for each binned column, the partial rows of its
@@ -20,36 +21,81 @@ namespace xtvxy {
 namespace {
 
 constexpr int kSortThreads = 1024;
+constexpr int kCountThreads = 256;
 constexpr int kAccThreads = 1024;
 
-__global__ __launch_bounds__(kSortThreads) void bin_sort_kernel(CsrBinArgs a) {
-  __shared__ uint32_t hist[kMaxBins];
-  __shared__ uint32_t cursor[kMaxBins];
-  const int tid = threadIdx.x;
+// The handed-out chunks split evenly over the sorting workgroups (the same split in both passes).
+__device__ inline void sort_range(const CsrBinArgs& a, int64_t* c0, int64_t* c1) {
   const int64_t handed = (int64_t)*a.pool_next;
   const int64_t chunks = handed < a.pool_chunks ? handed : a.pool_chunks;
-  for (int b = tid; b < kMaxBins; b += kSortThreads) hist[b] = 0;
+  const int64_t per = (chunks + kBinSortGroups - 1) / kBinSortGroups;
+  *c0 = min((int64_t)blockIdx.x * per, chunks);
+  *c1 = min(*c0 + per, chunks);
+}
+
+// Pass 1: chunks of each bin in this workgroup's range -> counts[bin][group].
+__global__ __launch_bounds__(kCountThreads) void bin_count_kernel(CsrBinArgs a) {
+  __shared__ uint32_t hist[kMaxBins];
+  int64_t c0, c1;
+  sort_range(a, &c0, &c1);
+  for (int b = threadIdx.x; b < a.bins; b += kCountThreads) hist[b] = 0;
   __syncthreads();
-  for (int64_t c = tid; c < chunks; c += kSortThreads) {
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += kCountThreads) {
     const int32_t b = a.chunk_bin[c];
     if ((uint32_t)b < (uint32_t)a.bins) atomicAdd(&hist[b], 1u);
   }
   __syncthreads();
-  if (tid == 0) {
-    // exclusive prefix sums: chunk positions and units per bin
-    int64_t pos = 0, units = 0;
-    for (int b = 0; b < a.bins; ++b) {
-      a.bin_start[b] = (int32_t)pos;
-      cursor[b] = (uint32_t)pos;
-      a.unit_start[b] = (int32_t)units;
-      pos += hist[b];
-      units += (hist[b] + kBinUnitChunks - 1) / kBinUnitChunks;
-    }
-    a.bin_start[a.bins] = (int32_t)pos;
-    a.unit_start[a.bins] = (int32_t)(units < a.max_units ? units : a.max_units);
+  for (int b = threadIdx.x; b < a.bins; b += kCountThreads) a.counts[b * kBinSortGroups + blockIdx.x] = (int32_t)hist[b];
+}
+
+// Pass 2 (one workgroup): counts -> exclusive offsets in (bin, group) order, the first position
+// of every bin, and the units of every bin.
+__global__ __launch_bounds__(kSortThreads) void bin_scan_kernel(CsrBinArgs a) {
+  __shared__ int32_t part[kSortThreads];
+  const int tid = threadIdx.x;
+  const int total = a.bins * kBinSortGroups;
+  const int per = (total + kSortThreads - 1) / kSortThreads;
+  const int s0 = min(tid * per, total), s1 = min(s0 + per, total);
+  int32_t sum = 0;
+  for (int i = s0; i < s1; ++i) sum += a.counts[i];
+  part[tid] = sum;
+  __syncthreads();
+  for (int d = 1; d < kSortThreads; d <<= 1) {  // inclusive scan of the per-thread sums
+    const int32_t t = tid >= d ? part[tid - d] : 0;
+    __syncthreads();
+    part[tid] += t;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - sum;  // exclusive start of this thread's segment
+  for (int i = s0; i < s1; ++i) {
+    const int32_t c = a.counts[i];
+    a.counts[i] = run;
+    run += c;
   }
   __syncthreads();
-  for (int64_t c = tid; c < chunks; c += kSortThreads) {
+  if (tid == 0) {
+    int64_t units = 0;
+    for (int b = 0; b < a.bins; ++b) {
+      const int32_t start = a.counts[b * kBinSortGroups];
+      const int32_t end = b + 1 < a.bins ? a.counts[(b + 1) * kBinSortGroups] : part[kSortThreads - 1];
+      a.bin_start[b] = start;
+      a.unit_start[b] = (int32_t)units;
+      units += (end - start + kBinUnitChunks - 1) / kBinUnitChunks;
+    }
+    a.bin_start[a.bins] = part[kSortThreads - 1];
+    a.unit_start[a.bins] = (int32_t)(units < a.max_units ? units : a.max_units);
+  }
+}
+
+// Pass 3: every chunk id to its place in `order` (ranks within a workgroup from LDS counters).
+__global__ __launch_bounds__(kCountThreads) void bin_place_kernel(CsrBinArgs a) {
+  __shared__ uint32_t cursor[kMaxBins];
+  int64_t c0, c1;
+  sort_range(a, &c0, &c1);
+  for (int b = threadIdx.x; b < a.bins; b += kCountThreads)
+    cursor[b] = (uint32_t)a.counts[b * kBinSortGroups + blockIdx.x];
+  __syncthreads();
+  for (int64_t c = c0 + threadIdx.x; c < c1; c += kCountThreads) {
     const int32_t b = a.chunk_bin[c];
     if ((uint32_t)b < (uint32_t)a.bins) a.order[atomicAdd(&cursor[b], 1u)] = (int32_t)c;
   }
@@ -101,7 +147,9 @@ hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s) {
   if (a.bins <= 0 || a.bins > kMaxBins || a.bin_shift < 10 || a.bin_shift > 15 || a.max_units <= 0 ||
       a.max_units > INT32_MAX)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bin_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, a);
+  hipLaunchKernelGGL(bin_count_kernel, dim3(kBinSortGroups), dim3(kCountThreads), 0, s, a);
+  hipLaunchKernelGGL(bin_scan_kernel, dim3(1), dim3(kSortThreads), 0, s, a);
+  hipLaunchKernelGGL(bin_place_kernel, dim3(kBinSortGroups), dim3(kCountThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(float) << a.bin_shift;

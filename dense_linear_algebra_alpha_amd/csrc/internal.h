@@ -24,6 +24,7 @@ constexpr size_t kAlign = 256;       // alignment of every workspace region
 constexpr int kBinChunkItems = 512;  // (column, product) items per workspace chunk (4 KiB)
 constexpr int kMaxBins = 512;        // column bins of one call
 constexpr int kBinUnitChunks = 128;  // chunks one workgroup of the bin pass accumulates
+constexpr int kBinSortGroups = 256;  // workgroups of the counting sort of chunks by bin
 // LDS of the fused CSR kernel for the per-bin state (count, current chunk, fill, room, two
 // positions) when binning
 constexpr size_t kCsrBinStateBytes = 32;
@@ -77,6 +78,7 @@ struct CsrBinArgs {
   const int32_t* chunk_bin;
   const int32_t* chunk_fill;
   int32_t* order;          // [P] chunk ids grouped by bin
+  int32_t* counts;         // [B][kBinSortGroups] chunks per bin and sorting workgroup, then their offsets
   int32_t* bin_start;      // [B + 1] first position in `order` of each bin
   int32_t* unit_start;     // [B + 1] first unit of each bin (unit_start[B] = units in all)
   float* partial2;         // [max_units][2^bin_shift] per-unit sums of the bin's columns
@@ -146,8 +148,8 @@ struct CsrWorkspace {
   // binning (bins > 0)
   int32_t bins, bin_shift;
   int64_t pool_chunks, max_units;
-  size_t counter_off, pool_off, chunk_bin_off, chunk_fill_off, order_off, bin_start_off, unit_start_off,
-      partial2_off;
+  size_t counter_off, pool_off, chunk_bin_off, chunk_fill_off, order_off, counts_off, bin_start_off,
+      unit_start_off, partial2_off;
   size_t total;
 };
 CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p);

@@ -107,6 +107,8 @@ CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch
   off = align_up(off + (size_t)w.pool_chunks * sizeof(int32_t));
   w.order_off = off;
   off = align_up(off + (size_t)w.pool_chunks * sizeof(int32_t));
+  w.counts_off = off;
+  off = align_up(off + (size_t)w.bins * kBinSortGroups * sizeof(int32_t));
   w.bin_start_off = off;
   off = align_up(off + (size_t)(w.bins + 1) * sizeof(int32_t));
   w.unit_start_off = off;
