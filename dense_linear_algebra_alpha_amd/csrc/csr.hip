@@ -34,10 +34,11 @@
 // sweeps over its entries (dot, then scatter).
 //
 // Software pipeline: while a tile is processed, the next tile's row_ptr, v and
-// entries (which start where this tile ends) are already loading. Every one of
-// these loads is issued unconditionally (addresses clamped, results selected),
-// and the y gathers of a tile are issued before the prefetch of the next, so
-// the compiler can wait for exactly the values it needs: the counter of
+// entries (which start where this tile ends) are already loading, and (when y is
+// read from global memory) at the end of the step, once they have arrived, the
+// next tile's y gathers are issued so that they overlap the barrier and the
+// start of the next step. Every load is
+// issued unconditionally (addresses clamped, results selected): the counter of
 // outstanding vector-memory operations completes in order, and a conditional
 // load anywhere in between forces a wait for everything. The per-tile LDS state
 // (row_ptr, v, marks, dots) is double-buffered, so a tile costs two workgroup
@@ -93,6 +94,7 @@ struct TileRegs {
   int32_t rp;   // row_ptr[r + tid] (the tile's rows start at r): first entry of this thread's row
   int32_t rp1;  // row_ptr[r + tid + 1]: its end
   float v;      // v[r + tid]
+  float yv[K];  // y[col] of the entries (gathered one step ahead when y is read from global memory)
 };
 
 template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
@@ -252,6 +254,9 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     for (int32_t c = tid; c < window; c += BLK) dst[c] = 0.0f;
     return;
   }
+  // Gathers from global memory are issued a step ahead (their latency then overlaps a barrier);
+  // gathers from an LDS copy of all of y measured faster at the start of the step.
+  constexpr bool kGatherAhead = YMODE != kYLds;
   auto gather_y = [&](int32_t col) -> float {
     if constexpr (YMODE == kYGlobal) return a.y[col];
     if constexpr (YMODE == kYLds) return y_s[col];
@@ -337,6 +342,10 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   {
     const uint32_t p0 = (uint32_t)a.row_ptr[ra];
     issue(ra, p0, ga);
+    if constexpr (kGatherAhead) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) ga.yv[k] = gather_y(ga.col[k]);
+    }
     j = __syncthreads_count(stage(0, cnt, p0, ga));
   }
 
@@ -351,10 +360,13 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     const int cnt_next = more ? min(BLK, re - ra_next) : 0;
     const uint32_t e0 = base + (uint32_t)tid * K;
 
-    // (a) gathers of y for this tile's entries, before anything of the next tile is issued
-    float yv[K];
+    // (a) this tile's y values: from LDS now, or from global memory gathered at the end of the
+    // previous step
+    if constexpr (!kGatherAhead) {
 #pragma unroll
-    for (int k = 0; k < K; ++k) yv[k] = gather_y(g.col[k]);
+      for (int k = 0; k < K; ++k) g.yv[k] = gather_y(g.col[k]);
+    }
+    const float (&yv)[K] = g.yv;
     // (b) the next tile's row_ptr, v and entries (they start where this tile ends)
     issue(min(ra_next, re - 1), pb, gn);
 
@@ -488,6 +500,13 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
       scatter_k(c, g.col, ok);
     }
     if (!more) return false;
+    // the next tile's y gathers, a step ahead: its entries were issued at the start of this
+    // step and have arrived by now, and the gathers overlap the barrier below and the start of
+    // the next step
+    if constexpr (kGatherAhead) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) gn.yv[k] = gather_y(gn.col[k]);
+    }
     const bool fits = stage(b ^ 1, cnt_next, pb, gn);
     ra = ra_next;
     buf = b ^ 1;
