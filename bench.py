@@ -108,6 +108,17 @@ def load_traffic(workload: str, kernel: str, kind: str):
     return fetch + write
 
 
+def override(plan, text):
+    """Replace fields of the model's plan with those of a JSON object (--plan); True when forced."""
+    if not text:
+        return False
+    for k, val in json.loads(text).items():
+        if k not in dict(plan._fields_):
+            raise SystemExit("unknown plan field %s" % k)
+        setattr(plan, k, val)
+    return True
+
+
 def cpu_baseline(p, budget_s: float):
     """The oracle, as it is, on the host cores: repeated runs of the full workload for ~budget_s."""
     import oracle
@@ -138,6 +149,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle runs for cpu_baseline")
     ap.add_argument("--fused-only", action="store_true", help="time the fused path only (for profilers)")
+    ap.add_argument("--plan", default=None,
+                    help="JSON object of launch-parameter fields that replace the model's choice, e.g. "
+                         "'{\"lds_window\": 16384, \"y_window\": 0, \"bin_columns\": 0}' (the library checks the result)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -182,14 +196,21 @@ def main():
     if kind == "dense":
         X = t(p.X)
         plan = xt.xtvxy_dense_f32_plan(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
-        ws_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
+        forced = override(plan, args.plan)
+        if forced:
+            plan = xt.xtvxy_dense_f32_plan_complete(p.m, p.n, p.ldx, plan)
+        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
         uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev)
 
         def fused():
-            xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
-                               xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+            if forced:
+                xt.xtvxy_dense_f32_ex(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                                      xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
+            else:
+                xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                                   xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
 
         def unfused():
             xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(),
@@ -198,13 +219,22 @@ def main():
     else:
         rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
         plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
-        ws_bytes = xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
+        forced = override(plan, args.plan)
+        if forced:
+            plan = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, plan)
+        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uplan = None
 
         def fused():
-            xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), xt._ptr(v),
-                             y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+            if forced:
+                xt.xtvxy_csr_f32_ex(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
+                                    ws_bytes, sh, plan)
+            else:
+                xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                                 xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
+                                 ws_bytes, sh)
 
         def unfused():
             xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
@@ -254,7 +284,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators, seed %d)" % args.seed,
-        "config": dict({"workload": args.workload, "algorithmic_bytes": abytes,
+        "config": dict({"workload": args.workload, "algorithmic_bytes": abytes, "plan_forced": bool(forced),
                         "plan": {k: v_ for k, v_ in plan.as_dict().items() if k != "predicted_seconds"}},
                        **shape),
         "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
