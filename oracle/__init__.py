@@ -47,7 +47,10 @@ def _bind(path: str):
     dense_args = [i64, i64, f32, vp, i64, vp, vp, f32, vp, vp]
     csr_args = [i64, i64, i64, f32, vp, vp, vp, vp, vp, f32, vp, vp]
     for name, args in (("oracle_dense", dense_args), ("oracle_dense_bound", dense_args),
-                       ("oracle_csr", csr_args), ("oracle_csr_bound", csr_args)):
+                       ("oracle_csr", csr_args), ("oracle_csr_bound", csr_args),
+                       ("oracle_csr_rowdot", csr_args), ("oracle_csr_rowdot_bound", csr_args),
+                       ("oracle_csr_tmv", csr_args[:8] + [f32, vp, vp]),
+                       ("oracle_csr_tmv_bound", csr_args[:8] + [f32, vp, vp])):
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
@@ -130,3 +133,39 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, *, 
             out.ctypes.data_as(ctypes.c_void_p))
     _check(rc, fn.__name__)
     return out
+
+
+def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=0.0, *, bound=False, lib=None):
+    """t_i = alpha v_i (X y)_i + beta t0_i (the first half of the pattern), or its normaliser."""
+    rpa, rpp = _ptr(row_ptr, np.int32)
+    cia, cip = _ptr(col_idx, np.int32)
+    vaa, vap = _ptr(values, np.float32)
+    ya, yp = _ptr(y, np.float32)
+    va, vp_ = _ptr(v, np.float32)
+    ta, tp = _ptr(t0, np.float32)
+    m = rpa.shape[0] - 1
+    out = np.empty(int(m), dtype=np.float64)
+    lib = lib or _load()
+    fn = lib.oracle_csr_rowdot_bound if bound else lib.oracle_csr_rowdot
+    rc = fn(int(m), int(n), int(cia.shape[0]), float(alpha), rpp, cip, vap, vp_, yp, float(beta), tp,
+            out.ctypes.data_as(ctypes.c_void_p))
+    _check(rc, fn.__name__)
+    return out
+
+
+def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, *, bound=False, lib=None):
+    """out_j = alpha (X^T u)_j + beta z_j (the second half of the pattern), or its normaliser."""
+    rpa, rpp = _ptr(row_ptr, np.int32)
+    cia, cip = _ptr(col_idx, np.int32)
+    vaa, vap = _ptr(values, np.float32)
+    ua, up = _ptr(u, np.float32)
+    za, zp = _ptr(z, np.float32)
+    m = rpa.shape[0] - 1
+    out = np.empty(int(n), dtype=np.float64)
+    lib = lib or _load()
+    fn = lib.oracle_csr_tmv_bound if bound else lib.oracle_csr_tmv
+    rc = fn(int(m), int(n), int(cia.shape[0]), float(alpha), rpp, cip, vap, up, float(beta), zp,
+            out.ctypes.data_as(ctypes.c_void_p))
+    _check(rc, fn.__name__)
+    return out
+

@@ -22,6 +22,8 @@
 //     step 2  u_i = v_i t_i                    (v absent => v_i = 1)
 //     step 3  S_j = sum_i X_ij u_i             (i ascending)
 //     step 4  out_j = alpha S_j + beta z_j     (beta == 0 => z is not read)
+// The two halves of the pattern are also exported on their own for CSR X
+// (oracle_csr_rowdot: steps 1-2, oracle_csr_tmv: steps 3-4 with u given).
 // Special cases (BLAS conventions, the plainest reading where the page is
 // silent): n == 0 does nothing; alpha == 0 or m == 0 gives out_j = beta z_j
 // (0 when beta == 0) without reading X, v or y. Rows with v_i == 0 are not
@@ -155,6 +157,79 @@ int csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_
   return ORACLE_OK;
 }
 
+// The two halves of the pattern, each on its own, for iterative solvers that need them
+// separately (a generalized linear model's margins X w and gradient X^T r are the same two
+// products the pattern chains):
+//   rowdot  t_i   = alpha v_i (X y)_i + beta t0_i   (steps 1-2, then an epilogue on rows)
+//   tmv     out_j = alpha (X^T u)_j + beta z_j      (steps 3-4 with u given)
+// Same conventions as the full pattern: beta == 0 leaves t0 / z unread, alpha == 0 (or an
+// empty dimension) reads no X, y, v or u.
+int csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+              const float* values) {
+  if (row_ptr == nullptr) return ORACLE_NULL;
+  if (nnz > 0 && (col_idx == nullptr || values == nullptr)) return ORACLE_NULL;
+  if (row_ptr[0] != 0 || (int64_t)row_ptr[m] != nnz) return ORACLE_BAD_SIZE;
+  for (int64_t i = 0; i < m; ++i)
+    if (row_ptr[i + 1] < row_ptr[i]) return ORACLE_BAD_SIZE;
+  for (int64_t p = 0; p < nnz; ++p)
+    if (col_idx[p] < 0 || (int64_t)col_idx[p] >= n) return ORACLE_BAD_SIZE;
+  return ORACLE_OK;
+}
+
+int csr_rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                    const int32_t* col_idx, const float* values, const float* v, const float* y,
+                    float beta, const float* t0, double* out, bool absolute) {
+  if (m < 0 || n < 0 || nnz < 0) return ORACLE_BAD_SIZE;
+  if (m == 0) return ORACLE_OK;
+  if (out == nullptr) return ORACLE_NULL;
+  if (beta != 0.0f && t0 == nullptr) return ORACLE_NULL;
+  const bool reads_x = alpha != 0.0f && n > 0;
+  if (reads_x) {
+    if (y == nullptr) return ORACLE_NULL;
+    const int rc = csr_check(m, n, nnz, row_ptr, col_idx, values);
+    if (rc != ORACLE_OK) return rc;
+  }
+#pragma omp parallel for schedule(dynamic, 4096)
+  for (int64_t i = 0; i < m; ++i) {
+    double r = 0.0;
+    if (reads_x) {
+      double t = 0.0;
+      for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+        t += val((double)values[p], absolute) * val((double)y[col_idx[p]], absolute);
+      const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);
+      r = val((double)alpha, absolute) * (vi * t);
+    }
+    if (beta != 0.0f) r += val((double)beta, absolute) * val((double)t0[i], absolute);
+    out[i] = r;
+  }
+  return ORACLE_OK;
+}
+
+int csr_tmv_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                 const int32_t* col_idx, const float* values, const float* u, float beta, const float* z,
+                 double* out, bool absolute) {
+  if (m < 0 || n < 0 || nnz < 0) return ORACLE_BAD_SIZE;
+  if (n == 0) return ORACLE_OK;
+  if (out == nullptr) return ORACLE_NULL;
+  if (beta != 0.0f && z == nullptr) return ORACLE_NULL;
+  if (alpha == 0.0f || m == 0) {
+    beta_only(n, beta, z, absolute, out);
+    return ORACLE_OK;
+  }
+  if (u == nullptr) return ORACLE_NULL;
+  const int rc = csr_check(m, n, nnz, row_ptr, col_idx, values);
+  if (rc != ORACLE_OK) return rc;
+  // S_j = sum over stored entries (i, j) of X_ij u_i, rows ascending
+  std::vector<double> S((size_t)n, 0.0);
+  for (int64_t i = 0; i < m; ++i) {
+    const double ui = val((double)u[i], absolute);
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)
+      S[(size_t)col_idx[p]] += val((double)values[p], absolute) * ui;
+  }
+  epilogue(n, alpha, S, beta, z, absolute, out);
+  return ORACLE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -195,6 +270,31 @@ int oracle_csr_bound(int64_t m, int64_t n, int64_t nnz, float alpha, const int32
                      const int32_t* col_idx, const float* values, const float* v, const float* y,
                      float beta, const float* z, double* bound) {
   return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, bound, true);
+}
+
+
+// t_i = alpha v_i (X y)_i + beta t0_i for CSR X (the first half of the pattern), and its bound.
+int oracle_csr_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                      const float* t0, double* ref) {
+  return csr_rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, ref, false);
+}
+int oracle_csr_rowdot_bound(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                            const int32_t* col_idx, const float* values, const float* v, const float* y,
+                            float beta, const float* t0, double* bound) {
+  return csr_rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, bound, true);
+}
+
+// out_j = alpha (X^T u)_j + beta z_j for CSR X (the second half of the pattern), and its bound.
+int oracle_csr_tmv(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                   const int32_t* col_idx, const float* values, const float* u, float beta, const float* z,
+                   double* ref) {
+  return csr_tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, ref, false);
+}
+int oracle_csr_tmv_bound(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                         const int32_t* col_idx, const float* values, const float* u, float beta,
+                         const float* z, double* bound) {
+  return csr_tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, bound, true);
 }
 
 }  // extern "C"

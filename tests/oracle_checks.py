@@ -315,7 +315,96 @@ def check_error_codes(lib):
                                vals, 3, y))                                                   # end != nnz
 
 
+# --- the two halves of the pattern (CSR): rowdot t = alpha v (X y) + beta t0, tmv out = alpha X^T u + beta z
+
+
+def _rowdot(lib, rp, ci, vals, n, y, v=None, t0=None, alpha=1.0, beta=0.0, bound=False):
+    return oracle.csr_rowdot(rp, ci, vals, n, y, v, t0, alpha, beta, bound=bound, lib=lib)
+
+
+def _tmv(lib, rp, ci, vals, n, u, z=None, alpha=1.0, beta=0.0, bound=False):
+    return oracle.csr_tmv(rp, ci, vals, n, u, z, alpha, beta, bound=bound, lib=lib)
+
+
+def check_halves_golden(lib):
+    g = read_golden("halves/csr_4x3_rowdot_tmv.txt")
+    t = _rowdot(lib, g["row_ptr"], g["col_idx"], g["values"], g["n"], g["y"], g["v"], g["t0"],
+                float(g["alpha_r"][0]), float(g["beta_r"][0]))
+    assert np.array_equal(t, g["expected_rowdot"].astype(np.float64)), t
+    o = _tmv(lib, g["row_ptr"], g["col_idx"], g["values"], g["n"], g["u"], g["z"], float(g["alpha_t"][0]),
+             float(g["beta_t"][0]))
+    assert np.array_equal(o, g["expected_tmv"].astype(np.float64)), o
+
+
+def check_halves_explicit_matrix(lib):
+    for m, n, seed in [(40, 30, 1), (7, 200, 2), (300, 5, 3)]:
+        p = datagen.csr_random(m, n, seed=seed, mean_len=5.0, empty_frac=0.2, dup_frac=0.2)
+        X = _csr_to_dense(p.row_ptr, p.col_idx, p.values, m, n)
+        g = np.random.default_rng(seed)
+        t0 = g.standard_normal(m).astype(np.float32)
+        u = g.standard_normal(m).astype(np.float32)
+        t = _rowdot(lib, p.row_ptr, p.col_idx, p.values, n, p.y, p.v, t0, 1.5, -0.25)
+        expect = 1.5 * p.v.astype(np.float64) * (X @ p.y.astype(np.float64)) - 0.25 * t0
+        assert np.allclose(t, expect, rtol=1e-12, atol=1e-12)
+        o = _tmv(lib, p.row_ptr, p.col_idx, p.values, n, u, p.z, -0.5, 2.0)
+        expect = -0.5 * (X.T @ u.astype(np.float64)) + 2.0 * p.z.astype(np.float64)
+        assert np.allclose(o, expect, rtol=1e-12, atol=1e-12)
+
+
+def check_halves_compose_into_the_pattern(lib):
+    # small integers: every intermediate is exact, so the chain equals the full pattern bitwise
+    g = np.random.default_rng(9)
+    m, n = 60, 45
+    X = (g.integers(-3, 4, size=(m, n)) * (g.random((m, n)) < 0.3)).astype(np.float32)
+    rp, ci, vals = datagen.csr_from_dense(X)
+    y = g.integers(-2, 3, size=n).astype(np.float32)
+    v = g.integers(-2, 3, size=m).astype(np.float32)
+    z = g.integers(-5, 6, size=n).astype(np.float32)
+    u = _rowdot(lib, rp, ci, vals, n, y, v).astype(np.float32)
+    assert np.array_equal(_tmv(lib, rp, ci, vals, n, u, z, 2.0, -3.0), _csr(lib, rp, ci, vals, n, y, v, z, 2.0, -3.0))
+
+
+def check_halves_special_cases(lib):
+    p = datagen.csr_random(20, 9, seed=4)
+    nan_m = np.full(20, np.nan, np.float32)
+    nan_n = np.full(9, np.nan, np.float32)
+    t0 = np.arange(20, dtype=np.float32)
+    z = np.arange(9, dtype=np.float32)
+    # alpha == 0 reads no X, y, v or u; beta == 0 reads no t0 or z
+    assert np.array_equal(_rowdot(lib, p.row_ptr, p.col_idx, p.values, 9, nan_n, nan_m, t0, 0.0, 2.0),
+                          2.0 * t0.astype(np.float64))
+    assert not np.isnan(_rowdot(lib, p.row_ptr, p.col_idx, p.values, 9, p.y, None, nan_m, 1.0, 0.0)).any()
+    assert np.array_equal(_tmv(lib, p.row_ptr, p.col_idx, p.values, 9, nan_m, z, 0.0, -1.0), -z.astype(np.float64))
+    assert not np.isnan(_tmv(lib, p.row_ptr, p.col_idx, p.values, 9, p.v, nan_n, 1.0, 0.0)).any()
+    # v absent means v = 1
+    assert np.array_equal(_rowdot(lib, p.row_ptr, p.col_idx, p.values, 9, p.y, None),
+                          _rowdot(lib, p.row_ptr, p.col_idx, p.values, 9, p.y, np.ones(20, np.float32)))
+    # malformed structure is refused
+    bad = p.col_idx.copy()
+    bad[0] = 9
+    for fn in (lambda: _rowdot(lib, p.row_ptr, bad, p.values, 9, p.y), lambda: _tmv(lib, p.row_ptr, bad, p.values, 9, p.v)):
+        try:
+            fn()
+        except oracle.OracleError:
+            continue
+        raise AssertionError("malformed CSR accepted")
+
+
+def check_halves_bounds(lib):
+    p = datagen.csr_random(50, 30, seed=6)
+    t = _rowdot(lib, p.row_ptr, p.col_idx, p.values, 30, p.y, p.v, p.v, 1.5, -0.5)
+    tb = _rowdot(lib, p.row_ptr, p.col_idx, p.values, 30, p.y, p.v, p.v, 1.5, -0.5, bound=True)
+    assert (tb >= np.abs(t) - 1e-12).all()
+    o = _tmv(lib, p.row_ptr, p.col_idx, p.values, 30, p.v, p.z, 1.5, -0.5)
+    ob = _tmv(lib, p.row_ptr, p.col_idx, p.values, 30, p.v, p.z, 1.5, -0.5, bound=True)
+    assert (ob >= np.abs(o) - 1e-12).all()
+    a = [np.abs(x) for x in (p.values, p.v, p.z)]
+    assert np.array_equal(_tmv(lib, p.row_ptr, p.col_idx, a[0], 30, a[1], a[2], 2.0, 3.0),
+                          _tmv(lib, p.row_ptr, p.col_idx, a[0], 30, a[1], a[2], 2.0, 3.0, bound=True))
+
+
 CHECKS = [check_golden, check_brute_force_dense, check_brute_force_csr, check_exact_integers,
           check_closed_forms, check_special_cases, check_invariants, check_csr_dense_agree,
           check_nan_propagation, check_scipy, check_bound, check_thread_independence,
-          check_error_codes]
+          check_error_codes, check_halves_golden, check_halves_explicit_matrix,
+          check_halves_compose_into_the_pattern, check_halves_special_cases, check_halves_bounds]

@@ -45,6 +45,17 @@ MUTATIONS = [
     ("quick_return_ignores_beta", "(beta == 0.0f) ? 0.0 : val((double)beta, absolute) * val((double)z[j], absolute)",
      "(beta == 0.0f) ? 0.0 : val((double)z[j], absolute)", 0),
     ("bound_keeps_signs", "return absolute ? std::fabs(x) : x;", "return x;", 0),
+    # the two halves
+    ("rowdot_drops_v", "const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);",
+     "const double vi = 1.0;", 2),
+    ("rowdot_drops_alpha", "r = val((double)alpha, absolute) * (vi * t);", "r = vi * t;", 0),
+    ("rowdot_beta_sign", "if (beta != 0.0f) r += val((double)beta, absolute) * val((double)t0[i], absolute);",
+     "if (beta != 0.0f) r -= val((double)beta, absolute) * val((double)t0[i], absolute);", 0),
+    ("rowdot_skips_first_entry", "for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p)",
+     "for (int64_t p = row_ptr[i] + 1; p < row_ptr[i + 1]; ++p)", 2),
+    ("tmv_reads_u_backwards", "const double ui = val((double)u[i], absolute);",
+     "const double ui = val((double)u[m - 1 - i], absolute);", 0),
+    ("tmv_scatters_by_row", "S[(size_t)col_idx[p]] +=", "S[(size_t)(i % n)] +=", 1),
 ]
 
 
