@@ -116,6 +116,27 @@ def xtvxy_csr_f32_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, 
                      workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
 
 
+def xtvxy_csr_f32_rowdot(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream):
+    return _abi.call("xtvxy_csr_f32_rowdot", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream)
+
+
+def xtvxy_csr_f32_rowdot_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, force):
+    return _abi.call("xtvxy_csr_f32_rowdot_ex", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t,
+                     stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_f32_tmv(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes,
+                      stream):
+    return _abi.call("xtvxy_csr_f32_tmv", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_f32_tmv_ex(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes,
+                         stream, force):
+    return _abi.call("xtvxy_csr_f32_tmv_ex", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out,
+                     workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
 def xtvxy_csr_check(m, n, nnz, row_ptr, col_idx, d_flag, stream):
     return _abi.call("xtvxy_csr_check", m, n, nnz, row_ptr, col_idx, d_flag, stream)
 
@@ -254,6 +275,63 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
         xtvxy_csr_f32(*args)
     else:
         xtvxy_csr_f32_ex(*args, plan)
+    return out
+
+
+def _check_csr_arrays(row_ptr, col_idx, values):
+    torch = _torch()
+    device = row_ptr.device
+    for name, t, dt in (("row_ptr", row_ptr, torch.int32), ("col_idx", col_idx, torch.int32),
+                        ("values", values, torch.float32)):
+        if t.dtype != dt or t.device != device or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous %s tensor on %s" % (name, dt, device))
+    if values.numel() != col_idx.numel():
+        raise ValueError("values and col_idx differ in length")
+    return row_ptr.numel() - 1, col_idx.numel(), device
+
+
+def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=0.0, out=None, *, plan=None,
+               stream=None):
+    """t = alpha v .* (X y) + beta t0 (the first half of the pattern) for CSR X; returns t."""
+    torch = _torch()
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    _check_vec("y", y, n, device)
+    _check_vec("v", v, m, device, required=False)
+    _check_vec("t0", t0, m, device, required=beta != 0)
+    if out is None:
+        out = torch.empty(m, dtype=torch.float32, device=device)
+    _check_vec("out", out, m, device)
+    args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
+            _ptr(values) if nnz else None, _ptr(v), y.data_ptr(), float(beta), _ptr(t0), out.data_ptr(),
+            _stream_handle(stream))
+    if plan is None:
+        xtvxy_csr_f32_rowdot(*args)
+    else:
+        xtvxy_csr_f32_rowdot_ex(*args, plan)
+    return out
+
+
+def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None,
+            stream=None):
+    """out = alpha X^T u + beta z (the second half of the pattern) for CSR X; returns out."""
+    torch = _torch()
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    _check_vec("u", u, m, device)
+    _check_vec("z", z, n, device, required=beta != 0)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    _check_vec("out", out, n, device)
+    need = xtvxy_csr_f32_workspace_size(m, n, nnz) if plan is None else int(plan.workspace_bytes)
+    if workspace is None:
+        workspace = _workspace(need, device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+    args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
+            _ptr(values) if nnz else None, u.data_ptr(), float(beta), _ptr(z), out.data_ptr(), ws_ptr, ws_bytes,
+            _stream_handle(stream))
+    if plan is None:
+        xtvxy_csr_f32_tmv(*args)
+    else:
+        xtvxy_csr_f32_tmv_ex(*args, plan)
     return out
 
 

@@ -198,20 +198,24 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64
   return launch_status(e);
 }
 
-xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
-                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                      const xtvxy_launch_params* force) {
-  bool quick = false;
-  xtvxy_status st = check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick);
-  if (st != XTVXY_SUCCESS) return st;
-  if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
+// The fused kernel (mode kCsrFused, with v and y) or its second half alone (kCsrTmv, with u
+// passed as v and no y), then the bin passes and the aggregation, for checked arguments.
+xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                     const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                     const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                     const xtvxy_launch_params* force) {
   xtvxy_device_info d;
-  st = device_info(-1, &d);
+  xtvxy_status st = device_info(-1, &d);
   if (st != XTVXY_SUCCESS) return st;
   xtvxy_launch_params plan;
   st = csr_plan_for(m, n, nnz, d, force, &plan);
   if (st != XTVXY_SUCCESS) return st;
+  if (mode == kCsrTmv && plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
+  if (mode == kCsrTmv && plan.y_window != 0) {  // no y to gather: the plan with no y window
+    plan.y_window = 0;
+    st = complete_csr(m, n, nnz, d, &plan);
+    if (st != XTVXY_SUCCESS) return st;
+  }
   if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
   const CsrWorkspace w = csr_workspace(m, n, nnz, plan);
@@ -266,7 +270,7 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   }
   const hipEvent_t before = g_before_main, after = g_after_main;
   if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = launch_csr(a, plan, stream);
+  e = launch_csr(a, plan, stream, mode);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   BinPartials bp{bargs.partial2, bargs.unit_start, plan.lds_window, w.bin_shift};
@@ -277,6 +281,96 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   e = launch_aggregate(a.partial, (int64_t)w.partial_rows, plan.lds_window, a.acc, n, alpha, beta, z, out, stream,
                        binned ? &bp : nullptr);
   return launch_status(e);
+}
+
+xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                      const xtvxy_launch_params* force) {
+  bool quick = false;
+  xtvxy_status st = check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick);
+  if (st != XTVXY_SUCCESS) return st;
+  if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
+  return csr_run(kCsrFused, m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, ws, ws_bytes, stream,
+                 force);
+}
+
+// out = alpha X^T u + beta z (the second half of the pattern alone).
+xtvxy_status tmv_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                      const int32_t* col_idx, const float* values, const float* u, float beta, const float* z,
+                      float* out, void* ws, size_t ws_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (n == 0) return XTVXY_SUCCESS;
+  if (!out) return XTVXY_ERROR_NULL_POINTER;
+  if (beta != 0.0f && !z) return XTVXY_ERROR_NULL_POINTER;
+  const bool reads_x = alpha != 0.0f && m > 0 && nnz > 0;
+  const size_t nb = (size_t)n * sizeof(float);
+  if (reads_x) {
+    if (!row_ptr || !col_idx || !values || !u) return XTVXY_ERROR_NULL_POINTER;
+    if (overlap(out, nb, row_ptr, (size_t)(m + 1) * 4) || overlap(out, nb, col_idx, (size_t)nnz * 4) ||
+        overlap(out, nb, values, (size_t)nnz * 4) || overlap(out, nb, u, (size_t)m * sizeof(float)))
+      return XTVXY_ERROR_ALIASING;
+  }
+  if (beta != 0.0f && z != out && overlap(out, nb, z, nb)) return XTVXY_ERROR_ALIASING;
+  if (!reads_x) return launch_status(launch_beta_only(n, beta, z, out, stream));
+  return csr_run(kCsrTmv, m, n, nnz, alpha, row_ptr, col_idx, values, u, nullptr, beta, z, out, ws, ws_bytes,
+                 stream, force);
+}
+
+// t = alpha v .* (X y) + beta t0 (the first half of the pattern alone); needs no workspace.
+xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                         const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                         const float* t0, float* t, hipStream_t stream, const xtvxy_launch_params* force) {
+  if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (m == 0) return XTVXY_SUCCESS;
+  if (!t) return XTVXY_ERROR_NULL_POINTER;
+  if (beta != 0.0f && !t0) return XTVXY_ERROR_NULL_POINTER;
+  const bool reads_x = alpha != 0.0f && n > 0 && nnz > 0;
+  const size_t mb = (size_t)m * sizeof(float);
+  if (reads_x) {
+    if (!row_ptr || !col_idx || !values || !y) return XTVXY_ERROR_NULL_POINTER;
+    if (overlap(t, mb, row_ptr, (size_t)(m + 1) * 4) || overlap(t, mb, col_idx, (size_t)nnz * 4) ||
+        overlap(t, mb, values, (size_t)nnz * 4) || overlap(t, mb, y, (size_t)n * sizeof(float)) ||
+        (v && overlap(t, mb, v, mb)))
+      return XTVXY_ERROR_ALIASING;
+  }
+  if (beta != 0.0f && t0 != t && overlap(t, mb, t0, mb)) return XTVXY_ERROR_ALIASING;
+  if (!reads_x) return launch_status(launch_beta_only(m, beta, t0, t, stream));
+  xtvxy_device_info d;
+  xtvxy_status st = device_info(-1, &d);
+  if (st != XTVXY_SUCCESS) return st;
+  xtvxy_launch_params plan;
+  st = csr_plan_for(m, n, nnz, d, force, &plan);
+  if (st != XTVXY_SUCCESS) return st;
+  if (plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
+  // no scatter: no output window, no bins (the LDS left holds the y window)
+  plan.lds_window = 0;
+  plan.bin_columns = 0;
+  st = complete_csr(m, n, nnz, d, &plan);
+  if (st != XTVXY_SUCCESS) return st;
+  CsrArgs a{};
+  a.m = m;
+  a.n = n;
+  a.nnz = nnz;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.values = values;
+  a.v = v;
+  a.y = y;
+  a.lds_window = 0;
+  a.y_window = plan.y_window;
+  a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.t0 = t0;
+  a.t_out = t;
+  const hipEvent_t before = g_before_main, after = g_after_main;
+  if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (launch_csr(a, plan, stream, kCsrRowdot) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  return XTVXY_SUCCESS;
 }
 
 }  // namespace
@@ -424,6 +518,35 @@ xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha, co
                               hipStream_t stream, const xtvxy_launch_params* force) {
   return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
                   stream, force);
+}
+
+xtvxy_status xtvxy_csr_f32_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                  const int32_t* col_idx, const float* values, const float* v, const float* y,
+                                  float beta, const float* t0, float* t, hipStream_t stream) {
+  return rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, nullptr);
+}
+
+xtvxy_status xtvxy_csr_f32_rowdot_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                     const int32_t* col_idx, const float* values, const float* v, const float* y,
+                                     float beta, const float* t0, float* t, hipStream_t stream,
+                                     const xtvxy_launch_params* force) {
+  return rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, force);
+}
+
+xtvxy_status xtvxy_csr_f32_tmv(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                               const int32_t* col_idx, const float* values, const float* u, float beta,
+                               const float* z, float* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes, stream,
+                  nullptr);
+}
+
+xtvxy_status xtvxy_csr_f32_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                  const int32_t* col_idx, const float* values, const float* u, float beta,
+                                  const float* z, float* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream, const xtvxy_launch_params* force) {
+  return tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes, stream,
+                  force);
 }
 
 xtvxy_status xtvxy_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,

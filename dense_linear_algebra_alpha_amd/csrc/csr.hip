@@ -85,6 +85,10 @@ enum ColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
 // Where y is gathered from: global memory, an LDS copy of all of it, or an LDS copy of
 // y[0, y_window) and global memory beyond.
 enum YMode { kYGlobal = 0, kYLds = 1, kYSplit = 2 };
+// What the kernel computes: the whole pattern (partials of X^T (v .* (X y))), only its first
+// half (t = alpha v .* (X y) + beta t0, written per row), or only its second half (partials of
+// X^T u, with u given in place of v and no y).
+enum CsrMode { kModeFused = 0, kModeRowdot = 1, kModeTmv = 2 };
 
 // The loads one tile needs, held in registers while the previous tile is processed.
 template <int K>
@@ -97,7 +101,7 @@ struct TileRegs {
   float yv[K];  // y[col] of the entries (gathered one step ahead when y is read from global memory)
 };
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512, "workgroups of 256 or 512 threads");
   static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
@@ -256,7 +260,8 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   }
   // Gathers from global memory are issued a step ahead (their latency then overlaps a barrier);
   // gathers from an LDS copy of all of y measured faster at the start of the step.
-  constexpr bool kGatherAhead = YMODE != kYLds;
+  constexpr bool kGathers = MODE != kModeTmv;  // the second half alone reads no y
+  constexpr bool kGatherAhead = kGathers && YMODE != kYLds;
   auto gather_y = [&](int32_t col) -> float {
     if constexpr (YMODE == kYGlobal) return a.y[col];
     if constexpr (YMODE == kYLds) return y_s[col];
@@ -316,7 +321,8 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   // form a prefix, so their count is the number of rows of the tile.
   auto stage = [&](int b, int cnt, uint32_t first, const TileRegs<K>& g) -> bool {
     const uint32_t base = first & ~3u;
-    u_s[b][tid] = 0.0f;
+    // the row values u: built by the dots, or (second half alone) the given vector
+    u_s[b][tid] = (MODE == kModeTmv && tid < cnt) ? g.v : 0.0f;
     bool fits = false;
     if (tid < cnt) {
       if (tid == 0) rp_s[b][0] = g.rp;
@@ -362,7 +368,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
 
     // (a) this tile's y values: from LDS now, or from global memory gathered at the end of the
     // previous step
-    if constexpr (!kGatherAhead) {
+    if constexpr (kGathers && !kGatherAhead) {
 #pragma unroll
       for (int k = 0; k < K; ++k) g.yv[k] = gather_y(g.col[k]);
     }
@@ -396,48 +402,55 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     if (long_row) {
       // The whole workgroup takes the row in slices of T entries, twice: the dot, then the
       // scatter. The first slice is the one already in registers.
-      float s = 0.0f;
       const uint32_t len = pb - pa;
+      float u = v_s[b][0];  // the given u of the row (second half alone), else v of the row
+      if constexpr (MODE != kModeTmv) {
+        float s = 0.0f;
 #pragma unroll
-      for (int k = 0; k < K; ++k) s += (e0 + k - pa < len) ? g.val[k] * yv[k] : 0.0f;
-      for (uint32_t sb = base + T; sb < pb; sb += T) {
-        float hv[K];
-        int32_t hc[K];
-        load_entries(sb, hv, hc);
-        const uint32_t h0 = sb + (uint32_t)tid * K;
+        for (int k = 0; k < K; ++k) s += (e0 + k - pa < len) ? g.val[k] * yv[k] : 0.0f;
+        for (uint32_t sb = base + T; sb < pb; sb += T) {
+          float hv[K];
+          int32_t hc[K];
+          load_entries(sb, hv, hc);
+          const uint32_t h0 = sb + (uint32_t)tid * K;
 #pragma unroll
-        for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * gather_y(hc[k]) : 0.0f;
-      }
-      s = group_sum(s, 64);
-      if (lane == 0) lred[wave] = s;
-      __syncthreads();
-      float t = lred[0];
-#pragma unroll
-      for (int w = 1; w < (BLK / 64); ++w) t += lred[w];
-      const float u = v_s[b][0] * t;
-      {
-        float c[K];
-        bool on[K];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-          on[k] = e0 + k - pa < len;
-          c[k] = u * g.val[k];
+          for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * gather_y(hc[k]) : 0.0f;
         }
-        scatter_k(c, g.col, on);
-      }
-      for (uint32_t sb = base + T; sb < pb; sb += T) {
-        float hv[K];
-        int32_t hc[K];
-        load_entries(sb, hv, hc);
-        const uint32_t h0 = sb + (uint32_t)tid * K;
-        float c[K];
-        bool on[K];
+        s = group_sum(s, 64);
+        if (lane == 0) lred[wave] = s;
+        __syncthreads();
+        float t = lred[0];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          on[k] = h0 + k < pb;
-          c[k] = u * hv[k];
+        for (int w = 1; w < (BLK / 64); ++w) t += lred[w];
+        u = u * t;
+      }
+      if constexpr (MODE == kModeRowdot) {
+        if (tid == 0) a.t_out[ra] = a.alpha * u + (a.beta != 0.0f ? a.beta * a.t0[ra] : 0.0f);
+      } else {
+        {
+          float c[K];
+          bool on[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            on[k] = e0 + k - pa < len;
+            c[k] = u * g.val[k];
+          }
+          scatter_k(c, g.col, on);
         }
-        scatter_k(c, hc, on);
+        for (uint32_t sb = base + T; sb < pb; sb += T) {
+          float hv[K];
+          int32_t hc[K];
+          load_entries(sb, hv, hc);
+          const uint32_t h0 = sb + (uint32_t)tid * K;
+          float c[K];
+          bool on[K];
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            on[k] = h0 + k < pb;
+            c[k] = u * hv[k];
+          }
+          scatter_k(c, hc, on);
+        }
       }
     } else {
       // (c) the row of each entry: the latest row-start mark at or before it, within the thread,
@@ -457,6 +470,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
 #pragma unroll
       for (int k = 0; k < K; ++k) rk[k] = max(before, mk[k]);  // in [0, BLK)
 
+      if constexpr (MODE != kModeTmv) {
       // (d) per-row dots. Runs of one row inside the thread are summed in registers; a row
       // strictly inside the thread is complete and stored; the first run (head) and the last
       // (tail) may continue in neighbouring threads and are finished below.
@@ -493,11 +507,18 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
         if (r1 == wf || lane == 63) lds_add_f32(&u_s[b][r1], c); else u_s[b][r1] = c;
       }
       __syncthreads();  // u_s[b] complete
-      // (e) scatter
-      float c[K];
+      }  // (with the second half alone, u_s[b] holds the given u since the tile was staged)
+      if constexpr (MODE == kModeRowdot) {
+        // the first half alone: t = alpha u + beta t0 for the tile's rows
+        for (int r = tid; r < j; r += BLK)
+          a.t_out[ra + r] = a.alpha * u_s[b][r] + (a.beta != 0.0f ? a.beta * a.t0[ra + r] : 0.0f);
+      } else {
+        // (e) scatter
+        float c[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) c[k] = u_s[b][rk[k]] * g.val[k];
-      scatter_k(c, g.col, ok);
+        for (int k = 0; k < K; ++k) c[k] = u_s[b][rk[k]] * g.val[k];
+        scatter_k(c, g.col, ok);
+      }
     }
     if (!more) return false;
     // the next tile's y gathers, a step ahead: its entries were issued at the start of this
@@ -530,42 +551,58 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   }
 }
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   size_t lds = ((size_t)a.lds_window + (YMODE == kYGlobal ? 0 : (size_t)a.y_window)) * sizeof(float);
   if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
-  const void* fn = reinterpret_cast<const void*>(&csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD>);
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(BLK), lds, s, a);
+  hipLaunchKernelGGL((csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
+                     s, a);
   return hipGetLastError();
 }
 
-template <int BLK, int K, int COLD, int YMODE>
+template <int BLK, int K, int COLD, int YMODE, int MODE>
 hipError_t launch_kv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const bool hv = a.v != nullptr, al = a.aligned;
-  if (hv)
-    return al ? launch_k<BLK, K, YMODE, true, true, COLD>(a, p, s) : launch_k<BLK, K, YMODE, true, false, COLD>(a, p, s);
-  return al ? launch_k<BLK, K, YMODE, false, true, COLD>(a, p, s) : launch_k<BLK, K, YMODE, false, false, COLD>(a, p, s);
+  const bool al = a.aligned;
+  if constexpr (MODE == kModeTmv) {  // u is always given
+    return al ? launch_k<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+              : launch_k<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+  } else {
+    if (a.v != nullptr)
+      return al ? launch_k<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+                : launch_k<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+    return al ? launch_k<BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
+              : launch_k<BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
+  }
 }
 
-template <int BLK, int K, int COLD>
+template <int BLK, int K, int COLD, int MODE>
 hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.y_window >= a.n) return launch_kv<BLK, K, COLD, kYLds>(a, p, s);
-  if (a.y_window > 0) return launch_kv<BLK, K, COLD, kYSplit>(a, p, s);
-  return launch_kv<BLK, K, COLD, kYGlobal>(a, p, s);
+  if constexpr (MODE == kModeTmv) {
+    return launch_kv<BLK, K, COLD, kYGlobal, MODE>(a, p, s);  // no y
+  } else {
+    if (a.y_window >= a.n) return launch_kv<BLK, K, COLD, kYLds, MODE>(a, p, s);
+    if (a.y_window > 0) return launch_kv<BLK, K, COLD, kYSplit, MODE>(a, p, s);
+    return launch_kv<BLK, K, COLD, kYGlobal, MODE>(a, p, s);
+  }
 }
 
-template <int BLK, int K>
+template <int BLK, int K, int MODE>
 hipError_t launch_cold(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.bins > 0) return launch_kk<BLK, K, kColdBinned>(a, p, s);
-  if (a.lds_window < a.n) return launch_kk<BLK, K, kColdAtomic>(a, p, s);
-  return launch_kk<BLK, K, kColdNone>(a, p, s);
+  if constexpr (MODE == kModeRowdot) {
+    return launch_kk<BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
+  } else {
+    if (a.bins > 0) return launch_kk<BLK, K, kColdBinned, MODE>(a, p, s);
+    if (a.lds_window < a.n) return launch_kk<BLK, K, kColdAtomic, MODE>(a, p, s);
+    return launch_kk<BLK, K, kColdNone, MODE>(a, p, s);
+  }
 }
 
 }  // namespace
 
-hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode) {
   if (p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_TILES) return hipErrorInvalidValue;
   if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
       a.lds_window > a.n || a.y_window < 0 || a.y_window > a.n)
@@ -574,11 +611,26 @@ hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
+  if (mode == kCsrRowdot) {
+    // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
+    if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))
+      return hipErrorInvalidValue;
+    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeRowdot>(a, p, s);
+    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeRowdot>(a, p, s);
+    return hipErrorInvalidValue;
+  }
   if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
+  if (mode == kCsrTmv) {
+    if (a.v == nullptr) return hipErrorInvalidValue;  // u
+    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeTmv>(a, p, s);
+    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeTmv>(a, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (mode != kCsrFused) return hipErrorInvalidValue;
   // (threads, entries per thread): 256 x 4, 256 x 8 and 512 x 8
-  if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4>(a, p, s);
-  if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8>(a, p, s);
-  if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8>(a, p, s);
+  if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4, kModeFused>(a, p, s);
+  if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeFused>(a, p, s);
+  if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeFused>(a, p, s);
   return hipErrorInvalidValue;
 }
 

@@ -58,6 +58,10 @@ struct CsrArgs {
   int64_t lds_window;
   int64_t y_window;   // y[0, y_window) is gathered from an LDS copy, the rest from global memory
   bool aligned;       // values and col_idx are 16-byte aligned: entries load as vectors
+  // the first half of the pattern alone (launch mode kCsrRowdot): t_out = alpha v .* (X y) + beta t0
+  float alpha, beta;
+  const float* t0;    // read only when beta != 0 (may equal t_out)
+  float* t_out;
   // binning of the columns >= lds_window (bins > 0; acc is then null)
   int32_t bins;            // B = ceil((n - lds_window) / 2^bin_shift)
   int32_t bin_shift;       // log2 of the columns per bin
@@ -87,7 +91,11 @@ struct CsrBinArgs {
 // Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first
 // HIP error it meets.
 hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s);
-hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
+// What a CSR launch computes: the whole pattern's partials, the first half alone (row values
+// written to t_out; no window, no partials) or the second half alone (X^T u partials, u passed
+// as v, no y).
+enum CsrLaunchMode { kCsrFused = 0, kCsrRowdot = 1, kCsrTmv = 2 };
+hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
 // Bin passes: group the handed-out chunks by bin, then accumulate every unit of a bin in LDS.
 hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s);
 // Per-bin partial sums for the aggregation (null: no binning).

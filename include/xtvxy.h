@@ -176,6 +176,35 @@ xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha,
 xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
                                          const xtvxy_device_info *dev, xtvxy_launch_params *plan);
 
+/* The two halves of the pattern on their own, for CSR X ("On optimizing machine learning
+ * workloads via kernel fusion", abstract: the pattern chains X y and X^T (.); iterative solvers
+ * such as Newton-CG for logistic regression also need each product by itself: the margins X w
+ * and the gradient X^T r):
+ *   xtvxy_csr_f32_rowdot:  t = alpha * v .* (X y) + beta * t0     (m-vector, one kernel)
+ *   xtvxy_csr_f32_tmv:     out = alpha * X^T u + beta * z          (n-vector)
+ * Same CSR conventions, limits and error codes as xtvxy_csr_f32. rowdot: v optional (NULL = 1);
+ * t0 read only when beta != 0 and may equal t (in place); y, v and t0 read only when alpha != 0;
+ * no workspace. tmv: u required when alpha != 0 and m, nnz > 0; z read only when beta != 0 and
+ * may equal out; the workspace of xtvxy_csr_f32_workspace_size(m, n, nnz) suffices (with _ex:
+ * force->workspace_bytes after xtvxy_csr_f32_plan_complete). The _ex forms take a launch plan
+ * (entries_per_thread must be 8; rowdot ignores lds_window and bin_columns, tmv y_window).
+ * Asynchronous on `stream`. */
+xtvxy_status xtvxy_csr_f32_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                  const int32_t *col_idx, const float *values, const float *v, const float *y,
+                                  float beta, const float *t0, float *t, hipStream_t stream);
+xtvxy_status xtvxy_csr_f32_rowdot_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                     const int32_t *col_idx, const float *values, const float *v, const float *y,
+                                     float beta, const float *t0, float *t, hipStream_t stream,
+                                     const xtvxy_launch_params *force);
+xtvxy_status xtvxy_csr_f32_tmv(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                               const int32_t *col_idx, const float *values, const float *u, float beta,
+                               const float *z, float *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+xtvxy_status xtvxy_csr_f32_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                  const int32_t *col_idx, const float *values, const float *u, float beta,
+                                  const float *z, float *out, void *workspace, size_t workspace_bytes,
+                                  hipStream_t stream, const xtvxy_launch_params *force);
+
 /* Device-side structure check of a CSR matrix. Writes to *d_flag (a device
  * int32) 0 when row_ptr[0] == 0, row_ptr is non-decreasing, row_ptr[m] == nnz
  * and every column index lies in [0, n); otherwise a positive code (1: row_ptr

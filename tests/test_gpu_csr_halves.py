@@ -1,0 +1,151 @@
+"""GPU parity of the two halves of the pattern for CSR X (rowdot t = alpha v(Xy) + beta t0 and
+tmv out = alpha X^T u + beta z) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import datagen
+import dense_linear_algebra_alpha_amd as xt
+import oracle
+from gpu_util import CsrOnDevice, assert_parity, csr_oracle, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def aux(p, seed):
+    """t0 (m) and u (m) vectors for a problem."""
+    g = np.random.default_rng(seed)
+    return g.uniform(-1, 1, p.m).astype(np.float32), g.uniform(-1, 1, p.m).astype(np.float32)
+
+
+def rowdot_case(p, d, t0, alpha, beta, plan=None, what=""):
+    import torch
+    note("rowdot %s m=%d n=%d nnz=%d plan=%s" % (what or p.name, p.m, p.n, p.nnz, None if plan is None else plan.as_dict()))
+    got = xt.csr_rowdot(d.rp, d.ci, d.vals, p.n, d.y, d.v, to_dev(t0), alpha, beta, plan=plan)
+    torch.cuda.synchronize()
+    ref = oracle.csr_rowdot(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, t0, alpha, beta)
+    bnd = oracle.csr_rowdot(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, t0, alpha, beta, bound=True)
+    return assert_parity(got.cpu().numpy(), ref, bnd, "rowdot " + (what or p.name))
+
+
+def tmv_case(p, d, u, alpha, beta, plan=None, what=""):
+    import torch
+    note("tmv %s m=%d n=%d nnz=%d plan=%s" % (what or p.name, p.m, p.n, p.nnz, None if plan is None else plan.as_dict()))
+    got = xt.csr_tmv(d.rp, d.ci, d.vals, p.n, to_dev(u), d.z, alpha, beta, plan=plan)
+    torch.cuda.synchronize()
+    ref = oracle.csr_tmv(p.row_ptr, p.col_idx, p.values, p.n, u, p.z, alpha, beta)
+    bnd = oracle.csr_tmv(p.row_ptr, p.col_idx, p.values, p.n, u, p.z, alpha, beta, bound=True)
+    return assert_parity(got.cpu().numpy(), ref, bnd, "tmv " + (what or p.name))
+
+
+@pytest.mark.parametrize("m,n,mean_len", [(1, 1, 1.0), (5, 7, 3.0), (3000, 64, 6.0), (3000, 1000, 40.0),
+                                          (2500, 20000, 9.0), (700, 300000, 30.0)])
+def test_halves_on_irregular_matrices(m, n, mean_len):
+    p = datagen.csr_random(m, n, seed=m + n, mean_len=mean_len, empty_frac=0.2, dup_frac=0.1)
+    d = CsrOnDevice(p)
+    t0, u = aux(p, 1)
+    rowdot_case(p, d, t0, 1.25, -0.5)
+    tmv_case(p, d, u, -0.75, 0.5)
+
+
+def half_plans(m, n, nnz):
+    out = []
+    for blk in (256, 512):
+        for grid in (1, 7, 256):
+            for w, yw, bc in sorted({(0, 0, 0), (min(n, 300), min(n, 300), 0), (min(n, 4096), 0, 0),
+                                     (min(n, 300), n, 1024 if n > 300 else 0), (n, n, 0)}):
+                if (w + yw) * 4 + 32768 > 163840:
+                    continue
+                lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=blk, entries_per_thread=8,
+                                            grid=grid, vec=1, chunks=1, group=1, lds_window=w, y_window=yw,
+                                            bin_columns=bc)
+                out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
+    return out
+
+
+@pytest.mark.parametrize("m,n,mean_len", [(2000, 500, 9.0), (500, 30000, 30.0)])
+def test_halves_every_variant(m, n, mean_len):
+    p = datagen.csr_random(m, n, seed=77, mean_len=mean_len, empty_frac=0.1, dup_frac=0.05)
+    d = CsrOnDevice(p)
+    t0, u = aux(p, 2)
+    for plan in half_plans(m, n, p.nnz):
+        rowdot_case(p, d, t0, 0.5, 2.0, plan=plan, what="forced")
+        tmv_case(p, d, u, 1.5, -1.0, plan=plan, what="forced")
+
+
+def test_halves_with_rows_longer_than_a_tile_and_empty_runs():
+    g = np.random.default_rng(15)
+    m, n = 4000, 12000
+    lens = np.where(g.random(m) < 0.5, 0, g.integers(1, 6, size=m))
+    lens[[3, 1700, 3999]] = [5000, 9000, 4097]
+    rp = np.zeros(m + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    cols = g.integers(0, n, size=int(rp[-1])).astype(np.int32)
+    p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols, datagen.uniform(int(rp[-1]), 15, "vals"),
+                           datagen.uniform(n, 15, "y"), datagen.uniform(m, 15, "v"), datagen.uniform(n, 15, "z"),
+                           1.0, 0.5, "long rows")
+    d = CsrOnDevice(p)
+    t0, u = aux(p, 3)
+    rowdot_case(p, d, t0, 2.0, 1.0)
+    tmv_case(p, d, u, -1.0, 0.25)
+    for blk in (256, 512):
+        lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=blk, entries_per_thread=8, grid=9,
+                                    vec=1, chunks=1, group=1, lds_window=500, y_window=700, bin_columns=1024)
+        plan = xt.xtvxy_csr_f32_plan_complete(m, n, p.nnz, lp)
+        rowdot_case(p, d, t0, 2.0, 1.0, plan=plan, what="long rows forced")
+        tmv_case(p, d, u, -1.0, 0.25, plan=plan, what="long rows forced")
+
+
+def test_in_place_and_quick_returns():
+    import torch
+    p = datagen.csr_random(3000, 800, seed=21, mean_len=8.0)
+    d = CsrOnDevice(p)
+    t0, u = aux(p, 4)
+    # rowdot in place: t0 is t
+    t = to_dev(t0)
+    note("rowdot in place")
+    xt.csr_rowdot(d.rp, d.ci, d.vals, p.n, d.y, d.v, t, 1.5, -2.0, out=t)
+    torch.cuda.synchronize()
+    ref = oracle.csr_rowdot(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, t0, 1.5, -2.0)
+    bnd = oracle.csr_rowdot(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, t0, 1.5, -2.0, bound=True)
+    assert_parity(t.cpu().numpy(), ref, bnd, "rowdot in place")
+    # tmv with out == z
+    zz = to_dev(p.z)
+    note("tmv out == z")
+    xt.csr_tmv(d.rp, d.ci, d.vals, p.n, to_dev(u), zz, 0.5, 3.0, out=zz)
+    torch.cuda.synchronize()
+    ref = oracle.csr_tmv(p.row_ptr, p.col_idx, p.values, p.n, u, p.z, 0.5, 3.0)
+    bnd = oracle.csr_tmv(p.row_ptr, p.col_idx, p.values, p.n, u, p.z, 0.5, 3.0, bound=True)
+    assert_parity(zz.cpu().numpy(), ref, bnd, "tmv out == z")
+    # alpha == 0 reads neither X nor y/v/u; beta == 0 reads neither t0 nor z
+    nan_m = to_dev(np.full(p.m, np.nan, np.float32))
+    nan_n = to_dev(np.full(p.n, np.nan, np.float32))
+    note("quick returns")
+    r = xt.csr_rowdot(d.rp, d.ci, d.vals, p.n, nan_n, nan_m, to_dev(t0), 0.0, 2.0)
+    assert np.array_equal(r.cpu().numpy(), 2.0 * t0)
+    r = xt.csr_rowdot(d.rp, d.ci, d.vals, p.n, d.y, d.v, nan_m, 1.0, 0.0)
+    assert not np.isnan(r.cpu().numpy()).any()
+    r = xt.csr_tmv(d.rp, d.ci, d.vals, p.n, nan_m, d.z, 0.0, -1.0)
+    assert np.array_equal(r.cpu().numpy(), -p.z)
+    r = xt.csr_tmv(d.rp, d.ci, d.vals, p.n, to_dev(u), nan_n, 1.0, 0.0)
+    assert not np.isnan(r.cpu().numpy()).any()
+
+
+def test_halves_compose_into_the_fused_pattern():
+    import torch
+    p = datagen.WORKLOADS["csr_10000000x1000_logistic_hvp"](m=200_000)
+    d = CsrOnDevice(p)
+    note("halves compose")
+    u = xt.csr_rowdot(d.rp, d.ci, d.vals, p.n, d.y, d.v)
+    out = xt.csr_tmv(d.rp, d.ci, d.vals, p.n, u, d.z, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    ref, bnd = csr_oracle(p)
+    assert_parity(out.cpu().numpy(), ref, bnd, "rowdot then tmv")
+
+
+@pytest.mark.parametrize("name", ["csr_10000000x1000_logistic_hvp", "csr_5000000x1000000_zipf"])
+def test_halves_full_size(name):
+    p = datagen.WORKLOADS[name]()
+    d = CsrOnDevice(p)
+    t0, u = aux(p, 5)
+    rowdot_case(p, d, t0, 1.0, 0.5)
+    tmv_case(p, d, u, 0.7, 0.3 if p.z is not None else 0.0)
