@@ -66,8 +66,9 @@ def _load():
     lib.dg_zipf_lengths.argtypes = [i64, f64, i64, u64, vp]
     lib.dg_zipf_columns.argtypes = [i64, i64, f64, u64, vp, vp, vp]
     lib.dg_logistic_weights.argtypes = [i64, vp, vp, vp, vp, vp]
+    lib.dg_logistic_labels.argtypes = [i64, vp, vp, vp, vp, u64, vp]
     for name in ("dg_bernoulli_count", "dg_bernoulli_fill", "dg_zipf_lengths", "dg_zipf_columns",
-                 "dg_logistic_weights"):
+                 "dg_logistic_weights", "dg_logistic_labels"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -195,6 +196,34 @@ def csr_bernoulli(m, n, p, seed=0, *, values="normal", y="normal", v="logistic",
                       {"density": p})
 
 
+@dataclass
+class LogisticProblem:
+    """L2-regularised logistic regression data: CSR X (in ``X``, whose y, v, z are unused),
+    labels c_i in {0, 1} and the regularisation weight lambda."""
+    X: CsrProblem
+    labels: np.ndarray
+    lam: float
+    name: str = ""
+
+
+def logistic_labels(X: CsrProblem, seed=0, w_std=0.1) -> np.ndarray:
+    """Labels c_i ~ Bernoulli(sigmoid(x_i . w)) of the planted model w ~ N(0, w_std^2) that
+    ``csr_bernoulli(..., v="logistic")`` draws for the same seed."""
+    lib = _load()
+    w = normal(X.n, seed, "w", 0.0, w_std)
+    out = np.empty(X.m, dtype=np.float32)
+    lib.dg_logistic_labels(X.m, _p(np.ascontiguousarray(X.row_ptr, np.int64)), _p(X.col_idx), _p(X.values),
+                           _p(w), stream_key(seed, "labels"), _p(out))
+    return out
+
+
+def logistic_problem(m, n, density, seed=0, *, lam=1.0, w_std=0.1, name="") -> LogisticProblem:
+    """Bernoulli(density) CSR X with N(0, 1) values and labels of a planted model."""
+    X = csr_bernoulli(m, n, density, seed, values="normal", y="normal", v="logistic", z=None, alpha=1.0,
+                      beta=0.0, w_std=w_std, name=name)
+    return LogisticProblem(X, logistic_labels(X, seed, w_std), float(lam), name)
+
+
 def csr_zipf(m, n, seed=0, *, s_row=1.5, max_row=2726, s_col=1.2, permute_columns=False,
              values="uniform", y="uniform", v="uniform", z="uniform", alpha=0.7, beta=0.3,
              name="") -> CsrProblem:
@@ -251,6 +280,13 @@ def csr_from_dense(X2d: np.ndarray):
     np.cumsum(np.bincount(rows, minlength=X2d.shape[0]), out=rp[1:])
     return rp.astype(np.int32), cols.astype(np.int32), X2d[rows, cols].astype(np.float32)
 
+
+# Newton-CG for L2-regularised logistic regression on the 10,000,000 x 1000 Hessian-vector workload's
+# generator: 1% Bernoulli sparsity, N(0, 1) values, labels of the planted w ~ N(0, 0.1^2), lambda 1.
+LOGISTIC_WORKLOADS = {
+    "logreg_csr_10000000x1000": lambda seed=0, m=10_000_000, n=1000, lam=1.0: logistic_problem(
+        m, n, 0.01, seed, lam=lam, w_std=0.1, name="logreg_csr_10000000x1000"),
+}
 
 # The measured workloads, named by what they are. Each entry builds the full-size
 # problem; ``scaled`` variants with the same recipe and smaller sizes serve parity tests.

@@ -192,3 +192,17 @@ int dg_logistic_weights(int64_t m, const int64_t* row_ptr, const int32_t* col_id
   }
   return 0;
 }
+
+/* Labels of the same planted logistic model: c_i = 1 when U_i < sigmoid(x_i . w), else 0,
+ * with U_i a 53-bit uniform from stream `key` (counter i). */
+int dg_logistic_labels(int64_t m, const int64_t* row_ptr, const int32_t* col_idx, const float* values,
+                       const float* w, uint64_t key, float* labels) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; ++i) {
+    double eta = 0.0;
+    for (int64_t p = row_ptr[i]; p < row_ptr[i + 1]; ++p) eta += (double)values[p] * (double)w[col_idx[p]];
+    double pr = 1.0 / (1.0 + exp(-eta));
+    labels[i] = unif53(draw(key, (uint64_t)i)) < pr ? 1.0f : 0.0f;
+  }
+  return 0;
+}

@@ -83,3 +83,24 @@ def test_dense_padding_is_nan():
     p = datagen.dense_problem(4, 3, seed=0, ldx=5)
     X = p.X.reshape(4, 5)
     assert np.all(np.isnan(X[:, 3:])) and np.all(np.isfinite(X[:, :3]))
+
+
+def test_logistic_labels():
+    P = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000"](m=200_000)
+    Q = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000"](m=200_000)
+    assert np.array_equal(P.labels, Q.labels) and P.lam == 1.0
+    assert set(np.unique(P.labels)) <= {0.0, 1.0}
+    # the planted w ~ N(0, 0.01) is symmetric, so P(c = 1) = 1/2; rows whose curvature weight
+    # v = p(1 - p) is lowest have |p - 1/2| largest, and their labels follow the sign of p - 1/2
+    m = P.X.m
+    assert abs(P.labels.mean() - 0.5) < 4 * np.sqrt(0.25 / m)
+    w = datagen.normal(P.X.n, 0, "w", 0.0, 0.1).astype(np.float64)
+    rows = np.repeat(np.arange(m), np.diff(P.X.row_ptr))
+    eta = np.bincount(rows, weights=P.X.values.astype(np.float64) * w[P.X.col_idx], minlength=m)
+    p = 1.0 / (1.0 + np.exp(-eta))
+    assert np.allclose(P.X.v, p * (1 - p), rtol=1e-6, atol=0)
+    # calibration: among rows with p in a bin, the label frequency matches the bin's mean p
+    for lo, hi in ((0.3, 0.45), (0.55, 0.7)):
+        sel = (p >= lo) & (p < hi)
+        k = int(sel.sum())
+        assert k > 1000 and abs(P.labels[sel].mean() - p[sel].mean()) < 4 * np.sqrt(0.25 / k)
