@@ -9,7 +9,8 @@ algorithm built on the fused kernel, but names no algorithm. The reading used he
 textbook one in which the pattern is the inner step: L2-regularised logistic regression
 solved by Newton's method with a conjugate-gradient inner solve and a backtracking line
 search (Nocedal and Wright, "Numerical Optimization", 2nd ed.: Algorithm 7.1, line search
-Newton-CG, for the outer and inner loops; Algorithm 3.1, backtracking, for the step length).
+Newton-CG, for the outer and inner loops; Algorithm 3.1, backtracking, for the step length,
+with its sufficient-decrease test evaluated on the change of f summed row by row).
 
 The objective, for labels c_i in [0, 1] and lambda >= 0, with t = X w:
 
@@ -66,6 +67,16 @@ def objective(t, c, w, lam) -> float:
     return float(np.sum(pointwise_loss(t, c)) + 0.5 * lam * np.dot(w, w))
 
 
+def objective_change(t, xs, c, w, s, lam, a) -> float:
+    """f(w + a s) - f(w) for the iterate with margins t = X w and xs = X s, summed term by term
+    (the change of every row's loss, then of the penalty), so that the rounding of f itself,
+    which grows with the number of rows, does not swamp the small decreases near the minimiser."""
+    t = np.asarray(t, np.float64)
+    w = np.asarray(w, np.float64)
+    rows = pointwise_loss(t + a * xs, c) - pointwise_loss(t, c)
+    return float(np.sum(rows) + lam * (a * np.dot(w, s) + 0.5 * a * a * np.dot(s, s)))
+
+
 def curvature_weights(p):
     """Diagonal of the Hessian's middle factor: p_i (1 - p_i)."""
     return p * (1.0 - p)
@@ -112,8 +123,9 @@ def cg_solve(hvp, g, max_cg, eps, fixed_cg):
 
 def backtrack(trial, f0, gs, max_backtracks, c1=1e-4, shrink=0.5):
     """Backtracking line search: the first a in 1, shrink, shrink^2, ... with
-    trial(a) <= f0 + c1 a gs (sufficient decrease). Returns (a, f(a), trials), or
-    (None, None, trials) when no trial is accepted."""
+    trial(a) <= f0 + c1 a gs (sufficient decrease). Returns (a, trial(a), trials), or
+    (None, None, trials) when no trial is accepted. Newton-CG passes trial(a) = f(w + a s) - f(w)
+    and f0 = 0."""
     a = 1.0
     for k in range(max_backtracks):
         fa = trial(a)
@@ -172,7 +184,7 @@ def newton_cg(row_ptr, col_idx, values, n, labels, lam, w0=None, *, max_newton=2
         cg_total += used
         xs = X @ s
         gs = float(np.dot(g, s))
-        a, _, tried = backtrack(lambda a: objective(t + a * xs, c, w + a * s, lam), f, gs, max_backtracks)
+        a, _, tried = backtrack(lambda a: objective_change(t, xs, c, w, s, lam, a), 0.0, gs, max_backtracks)
         trials_total += tried
         hist[-1].update({"cg": used, "gs": gs, "step": a})
         if a is None:

@@ -94,11 +94,12 @@ def check_optimality_by_loops(lr):
     for seed, soft in ((1, False), (2, True)):
         rp, ci, vals, n, c, lam = _problem(40, 6, seed, lam=0.7, soft=soft)
         w0 = np.random.Generator(np.random.PCG64(seed)).normal(0, 8.0, n)
-        r = lr.newton_cg(rp, ci, vals, n, c, lam, w0=w0, grad_tol=1e-13, max_newton=60)
+        r = lr.newton_cg(rp, ci, vals, n, c, lam, w0=w0, grad_tol=1e-11, max_newton=60)
         assert r.status == lr.CONVERGED, r.status
         g = _grad_loops(rp, ci, vals, c, lam, r.w)
         g0 = _grad_loops(rp, ci, vals, c, lam, w0)
         assert np.max(np.abs(g)) <= 1e-10 * np.max(np.abs(g0)), (np.max(np.abs(g)), np.max(np.abs(g0)))
+        assert r.history[-1]["grad_norm"] <= 1e-11 * r.history[0]["grad_norm"]
         if not soft:
             steps = [h["step"] for h in r.history if "step" in h]
             assert min(steps) < 1.0, steps  # the fixture exercises shortened steps
@@ -188,6 +189,20 @@ def check_descent_and_sufficient_decrease(lr):
         assert h[k + 1]["loss"] <= h[k]["loss"] + 1e-4 * h[k]["step"] * h[k]["gs"] + 1e-12 * abs(h[k]["loss"])
 
 
+def check_objective_change(lr):
+    # the line search's f(w + a s) - f(w), summed row by row, against two evaluations of the
+    # dense objective
+    rp, ci, vals, n, c, lam = _problem(50, 5, 9, lam=0.8, soft=True)
+    X = _dense(rp, ci, vals, 50, n)
+    f = _f_dense(X, c, lam)
+    gen = np.random.Generator(np.random.PCG64(9))
+    w, s = gen.normal(0, 1, n), gen.normal(0, 1, n)
+    for a in (1.0, 0.25, 1e-3):
+        got = lr.objective_change(X @ w, X @ s, c, w, s, lam, a)
+        want = f(w + a * s) - f(w)
+        assert abs(got - want) <= 1e-9 * abs(want), (a, got, want)
+
+
 def check_line_search_rule(lr):
     # hand-made trials: no decrease at all is never accepted; a decrease of exactly the
     # required slope is accepted at once; the step halves until the rule holds
@@ -224,4 +239,5 @@ def check_conventions(lr):
 
 CHECKS = [check_closed_form_single_feature, check_optimality_by_loops, check_matches_bfgs,
           check_derivatives_by_differences, check_cg_solves_exactly, check_newton_rate,
-          check_descent_and_sufficient_decrease, check_line_search_rule, check_conventions]
+          check_descent_and_sufficient_decrease, check_objective_change, check_line_search_rule,
+          check_conventions]

@@ -34,6 +34,9 @@ MUTATIONS = [
     ("cg_beta_inverted", "b = rr_new / rr", "b = rr / rr_new"),
     ("cg_no_conjugation", "d = -r + b * d", "d = -r"),
     ("forcing_constant", "eps = min(cg_forcing, np.sqrt(gnorm)) * gnorm", "eps = cg_forcing * gnorm"),
+    ("change_drops_cross_term", "lam * (a * np.dot(w, s) + 0.5 * a * a * np.dot(s, s))",
+     "lam * (0.5 * a * a * np.dot(s, s))"),
+    ("change_penalty_not_halved", "0.5 * a * a * np.dot(s, s)", "a * a * np.dot(s, s)"),
     ("armijo_wrong_sign", "if fa <= f0 + c1 * a * gs:", "if fa <= f0 - c1 * a * gs:"),
     ("margins_ignore_step", "t = t + a * xs", "t = t + xs"),
     ("iterate_ignores_step", "w = w + a * s", "w = w + s"),
