@@ -20,7 +20,9 @@ import ctypes
 
 from . import _abi
 from ._abi import (XTVXY_CSR_TILES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
-                   XTVXY_DENSE_WAVE_ROWS, XtvxyError, xtvxy_device_info, xtvxy_launch_params)
+                   XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
+                   XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,
+                   xtvxy_device_info, xtvxy_launch_params, xtvxy_logreg_options, xtvxy_logreg_report)
 
 __all__ = [
     "xtvxy_get_device_info", "xtvxy_dense_f32_plan", "xtvxy_dense_f32_plan_complete", "xtvxy_csr_f32_plan",
@@ -30,6 +32,9 @@ __all__ = [
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
     "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
     "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
+    "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
+    "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
+    "xtvxy_logreg_options", "xtvxy_logreg_report",
 ]
 
 load = _abi.load
@@ -159,6 +164,19 @@ def xtvxy_csr_f32_unfused_plan_destroy(plan: int):
 
 def xtvxy_csr_f32_unfused_reference(plan, alpha, v, y, beta, z, out, stream):
     return _abi.call("xtvxy_csr_f32_unfused_reference", plan, alpha, v, y, beta, z, out, stream)
+
+
+def xtvxy_logreg_newton_cg_f32_workspace_size(m, n, nnz) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_logreg_newton_cg_f32_workspace_size", m, n, nnz, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_logreg_newton_cg_f32(m, n, nnz, row_ptr, col_idx, values, labels, w, opt, unfused, workspace,
+                               workspace_bytes, stream, report, history, history_rows):
+    return _abi.call("xtvxy_logreg_newton_cg_f32", m, n, nnz, row_ptr, col_idx, values, labels, w,
+                     ctypes.byref(opt), unfused, workspace, workspace_bytes, stream,
+                     ctypes.byref(report) if report is not None else None, history, history_rows)
 
 
 # ---------------------------------------------------------------------------
@@ -393,3 +411,48 @@ class CsrUnfusedPlan:
             self.close()
         except Exception:
             pass
+
+
+_HISTORY_KEYS = ("loss", "grad_norm", "cg", "gs", "step", "trials")
+
+
+def logreg_newton_cg(row_ptr, col_idx, values, n, labels, lam, w=None, *, max_newton=20, max_cg=50,
+                     max_backtracks=30, grad_tol=1e-6, cg_forcing=0.5, fixed_cg=False, engine="fused",
+                     unfused_plan=None, workspace=None, stream=None):
+    """Newton-CG for L2-regularised logistic regression on CSR X (xtvxy_logreg_newton_cg_f32).
+
+    ``w`` (float32 CUDA tensor of n elements) is the start point and is overwritten with the
+    result; None starts from zeros. ``engine`` is "fused" (this library's products) or "unfused"
+    (rocSPARSE through ``unfused_plan``, a CsrUnfusedPlan of the same tensors; made here when
+    None). Returns (w, report dict, history list of per-iterate dicts)."""
+    torch = _torch()
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    _check_vec("labels", labels, m, device)
+    if w is None:
+        w = torch.zeros(n, dtype=torch.float32, device=device)
+    _check_vec("w", w, n, device)
+    if engine not in ("fused", "unfused"):
+        raise ValueError("engine must be 'fused' or 'unfused'")
+    plan_handle = None
+    if engine == "unfused":
+        if unfused_plan is None:
+            unfused_plan = CsrUnfusedPlan(row_ptr, col_idx, values, n, stream)
+        plan_handle = unfused_plan.handle
+    opt = xtvxy_logreg_options(float(lam), int(max_newton), int(max_cg), int(max_backtracks), float(grad_tol),
+                               float(cg_forcing), 1 if fixed_cg else 0,
+                               XTVXY_LOGREG_FUSED if engine == "fused" else XTVXY_LOGREG_UNFUSED)
+    need = xtvxy_logreg_newton_cg_f32_workspace_size(m, n, nnz)
+    if workspace is None:
+        workspace = _workspace(need, device)
+    rows = int(max_newton) + 1
+    hist = (ctypes.c_double * (rows * len(_HISTORY_KEYS)))()
+    rep = xtvxy_logreg_report()
+    xtvxy_logreg_newton_cg_f32(m, n, nnz, row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
+                               _ptr(values) if nnz else None, _ptr(labels) if m else None, _ptr(w) if n else None,
+                               opt, plan_handle, workspace.data_ptr(), workspace.numel(), _stream_handle(stream),
+                               rep, hist, rows)
+    history = []
+    for k in range(min(rows, rep.newton_iterations + 1)):
+        row = {key: hist[k * len(_HISTORY_KEYS) + i] for i, key in enumerate(_HISTORY_KEYS)}
+        history.append(row)
+    return w, rep.as_dict(), history

@@ -45,6 +45,29 @@ class xtvxy_launch_params(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+XTVXY_LOGREG_FUSED = 0
+XTVXY_LOGREG_UNFUSED = 1
+XTVXY_LOGREG_CONVERGED = 0
+XTVXY_LOGREG_ITERATION_LIMIT = 1
+XTVXY_LOGREG_LINE_SEARCH_FAILED = 2
+
+
+class xtvxy_logreg_options(ctypes.Structure):
+    _fields_ = [("lambda_", ctypes.c_float), ("max_newton", ctypes.c_int32), ("max_cg", ctypes.c_int32),
+                ("max_backtracks", ctypes.c_int32), ("grad_tol", ctypes.c_double), ("cg_forcing", ctypes.c_double),
+                ("fixed_cg", ctypes.c_int32), ("engine", ctypes.c_int32)]
+
+
+class xtvxy_logreg_report(ctypes.Structure):
+    _fields_ = [("status", ctypes.c_int32), ("newton_iterations", ctypes.c_int32),
+                ("cg_iterations", ctypes.c_int32), ("line_search_trials", ctypes.c_int32),
+                ("loss0", ctypes.c_double), ("loss", ctypes.c_double), ("grad_norm0", ctypes.c_double),
+                ("grad_norm", ctypes.c_double), ("seconds", ctypes.c_double)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
 class XtvxyError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = int(status)
@@ -83,6 +106,9 @@ SIGNATURES = {
     "xtvxy_csr_f32_unfused_plan_destroy": [_vp],
     "xtvxy_csr_f32_unfused_reference": [_vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
+    "xtvxy_logreg_newton_cg_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
+    "xtvxy_logreg_newton_cg_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _P(xtvxy_logreg_options), _vp, _vp,
+                                   _sz, _vp, _P(xtvxy_logreg_report), _P(ctypes.c_double), _i64],
 }
 
 _lib = None

@@ -142,6 +142,44 @@ xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, cons
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
                             float beta, const float* z, const float* out, bool* quick);
 
+// Halves of the pattern through the rocSPARSE comparator's plan (unfused.cpp).
+xtvxy_status unfused_rowdot(xtvxy_csr_unfused_plan p, const float* y, float* t, hipStream_t stream);
+xtvxy_status unfused_tmv(xtvxy_csr_unfused_plan p, float alpha, const float* u, float beta, const float* z,
+                         float* out, hipStream_t stream);
+void unfused_plan_shape(xtvxy_csr_unfused_plan p, int64_t* m, int64_t* n, int64_t* nnz, const int32_t** row_ptr,
+                        const int32_t** col_idx, const float** values);
+
+// Newton-CG logistic-regression solver (logreg.hip kernels, logreg.cpp driver).
+struct LrScalars {  // device-side scalars of the solver, in its workspace
+  double f, gg, ww;        // objective, g.g and w.w at the current iterate
+  double gs, ws, ss;       // g.s, w.s, s.s for the line search
+  double df;               // f(w + a s) - f(w) at the last trial step
+  double rr, kappa, alpha, beta;  // CG: r.r, d.Hd and the two step coefficients
+  int32_t neg, pad;        // CG met a direction of non-positive curvature
+};
+constexpr int kLrMaxParts = 2048;     // partial sums per reduction row (workgroups of a streaming kernel)
+constexpr int kLrRows = 4;            // reduction rows
+constexpr int64_t kLrSmallCg = 16384; // n up to which one workgroup runs a whole CG update
+enum LrFinish { kLrObjective = 0, kLrLine = 1, kLrTrial = 2, kLrCgAlpha = 3, kLrCgBeta = 4 };
+// Workgroups of a streaming kernel over `count` elements (256 threads, at least 4 elements each).
+inline int lr_grid(int64_t count) {
+  if (count <= 0) return 0;
+  const int64_t g = (count + 1023) / 1024;
+  return (int)(g < kLrMaxParts ? g : kLrMaxParts);
+}
+hipError_t launch_lr_link(int64_t m, float* t, const float* xs, float step, const float* c, float* u, float* v,
+                          double* part, hipStream_t s);
+hipError_t launch_lr_trial(int64_t m, const float* t, const float* xs, double a, const float* c, double* part,
+                           hipStream_t s);
+hipError_t launch_lr_dots(int64_t n, int k, const float* const* x, const float* const* y, int row0, double* part,
+                          hipStream_t s);
+hipError_t launch_lr_finish(int op, const double* part, int64_t m, int64_t n, LrScalars* S, double a, double lam,
+                            hipStream_t s);
+hipError_t launch_lr_cg_init(int64_t n, const float* g, float* z, float* r, float* d, LrScalars* S, hipStream_t s);
+hipError_t launch_lr_cg_step(int64_t n, const float* q, float* d, float* z, float* r, LrScalars* S, bool first,
+                             double* part, hipStream_t s);
+hipError_t launch_lr_axpy(int64_t n, float a, const float* x, float* y, hipStream_t s);
+
 // Workspace layout of a dense plan.
 struct DenseWorkspace {
   size_t partial_off, partial_rows;  // partial sums [partial_rows][n]

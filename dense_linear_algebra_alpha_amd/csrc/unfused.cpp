@@ -206,6 +206,7 @@ xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan p, float alp
                                                                                            : XTVXY_ERROR_LAUNCH);
   if (rocsparse_set_stream(p->handle, stream) != rocsparse_status_success) return XTVXY_ERROR_LIBRARY;
   if (rocsparse_dnvec_set_values(p->vec_n, const_cast<float*>(y)) != rocsparse_status_success ||
+      rocsparse_dnvec_set_values(p->vec_m, p->t) != rocsparse_status_success ||
       rocsparse_dnvec_set_values(p->vec_n2, out) != rocsparse_status_success)
     return XTVXY_ERROR_LIBRARY;
   const float one = 1.0f, zero = 0.0f;
@@ -229,3 +230,68 @@ xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan p, float alp
 }
 
 }  // extern "C"
+
+namespace xtvxy {
+
+// t = X y with the comparator's rocSPARSE SpMV (the margins step of an unfused solver).
+xtvxy_status unfused_rowdot(xtvxy_csr_unfused_plan p, const float* y, float* t, hipStream_t stream) {
+  if (!p) return XTVXY_ERROR_NULL_POINTER;
+  if (p->m == 0) return XTVXY_SUCCESS;
+  if (!t) return XTVXY_ERROR_NULL_POINTER;
+  if (!p->handle)  // n == 0 or nnz == 0: every row product is empty
+    return launch_zero(t, (size_t)p->m * sizeof(float), stream) == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH;
+  if (!y) return XTVXY_ERROR_NULL_POINTER;
+  if (rocsparse_set_stream(p->handle, stream) != rocsparse_status_success ||
+      rocsparse_dnvec_set_values(p->vec_n, const_cast<float*>(y)) != rocsparse_status_success ||
+      rocsparse_dnvec_set_values(p->vec_m, t) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  const float one = 1.0f, zero = 0.0f;
+  size_t bytes = p->buf_fwd_bytes;
+  const rocsparse_status r = spmv(p, rocsparse_operation_none, &one, p->vec_n, &zero, p->vec_m,
+                                  rocsparse_spmv_stage_compute, &bytes, p->buf_fwd);
+  if (rocsparse_dnvec_set_values(p->vec_m, p->t) != rocsparse_status_success || r != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  return XTVXY_SUCCESS;
+}
+
+// out = alpha X^T u + beta z with the comparator's transposed rocSPARSE SpMV (the gradient step
+// of an unfused solver); z is read only when beta != 0 and may equal out.
+xtvxy_status unfused_tmv(xtvxy_csr_unfused_plan p, float alpha, const float* u, float beta, const float* z,
+                         float* out, hipStream_t stream) {
+  if (!p) return XTVXY_ERROR_NULL_POINTER;
+  if (p->n == 0) return XTVXY_SUCCESS;
+  if (!out || (beta != 0.0f && !z)) return XTVXY_ERROR_NULL_POINTER;
+  if (!p->handle || alpha == 0.0f)
+    return launch_beta_only(p->n, beta, z, out, stream) == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH;
+  if (!u) return XTVXY_ERROR_NULL_POINTER;
+  if (beta != 0.0f) {
+    if (out != z &&
+        hipMemcpyAsync(out, z, (size_t)p->n * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return XTVXY_ERROR_LAUNCH;
+  } else if (launch_zero(out, (size_t)p->n * sizeof(float), stream) != hipSuccess) {
+    return XTVXY_ERROR_LAUNCH;
+  }
+  if (rocsparse_set_stream(p->handle, stream) != rocsparse_status_success ||
+      rocsparse_dnvec_set_values(p->vec_m, const_cast<float*>(u)) != rocsparse_status_success ||
+      rocsparse_dnvec_set_values(p->vec_n2, out) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  size_t bytes = p->buf_tr_bytes;
+  const rocsparse_status r = spmv(p, rocsparse_operation_transpose, &alpha, p->vec_m, &beta, p->vec_n2,
+                                  rocsparse_spmv_stage_compute, &bytes, p->buf_tr);
+  if (rocsparse_dnvec_set_values(p->vec_m, p->t) != rocsparse_status_success || r != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  return XTVXY_SUCCESS;
+}
+
+// The plan's shape and matrix, for callers that check that a plan belongs to their matrix.
+void unfused_plan_shape(xtvxy_csr_unfused_plan p, int64_t* m, int64_t* n, int64_t* nnz, const int32_t** row_ptr,
+                        const int32_t** col_idx, const float** values) {
+  *m = p->m;
+  *n = p->n;
+  *nnz = p->nnz;
+  *row_ptr = p->row_ptr;
+  *col_idx = p->col_idx;
+  *values = p->values;
+}
+
+}  // namespace xtvxy

@@ -254,6 +254,84 @@ xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan plan, float 
                                              const float *v, const float *y, float beta,
                                              const float *z, float *out, hipStream_t stream);
 
+/* ------------------------------------------------------------------------ */
+/* An ML algorithm on the pattern: Newton-CG for logistic regression        */
+/* ------------------------------------------------------------------------ */
+
+/* "On optimizing machine learning workloads via kernel fusion" (abstract) finds the pattern
+ * inside ML algorithms and closes with a whole algorithm run on the fused kernel; it names no
+ * algorithm. This solver is the textbook one whose inner step is the pattern: L2-regularised
+ * logistic regression,
+ *     minimise f(w) = sum_i [log(1 + exp(t_i)) - c_i t_i] + (lambda / 2) |w|^2,   t = X w,
+ * by line search Newton-CG (Nocedal and Wright, "Numerical Optimization", Algorithm 7.1, with
+ * the backtracking of Algorithm 3.1). With p = sigmoid(t), the gradient is X^T (p - c) + lambda w
+ * and every Hessian-vector product H d = X^T (p(1 - p) .* (X d)) + lambda d is the pattern with
+ * alpha = 1, v = p(1 - p), y = z = d, beta = lambda.
+ *
+ * One Newton step k, all on `stream`:
+ *   link     t += a_{k-1} X s_{k-1}; u = p - c; v = p(1 - p); loss terms (one m-length kernel)
+ *   gradient g = X^T u + lambda w                        (the pattern's second half)
+ *   stop     when |g_k| <= grad_tol |g_0|, or k == max_newton
+ *   CG       s ~ -H^{-1} g: each iteration one Hessian-vector product and one vector-update
+ *            kernel; stops at |r| < min(cg_forcing, sqrt|g_k|) |g_k| (unless fixed_cg), at
+ *            max_cg iterations, or at a direction of non-positive curvature (then s = -g if
+ *            that happens at once, else the current s)
+ *   margins  X s                                         (the pattern's first half)
+ *   step     a = 1, 1/2, 1/4, ... until f(w + a s) - f(w) <= 1e-4 a g.s, where the change of f
+ *            is summed row by row in fp64 (one m-length kernel per trial); w += a s.
+ * The host reads a few scalars after each reduction to take the decisions (one
+ * synchronisation per CG iteration, per line-search trial and per Newton step), so the call
+ * is synchronous. Vectors are fp32; reductions (dot products, loss sums) are fp64 in a fixed
+ * order.
+ *
+ * Engines: XTVXY_LOGREG_FUSED runs the three products with this library's kernels
+ * (xtvxy_csr_f32, xtvxy_csr_f32_tmv, xtvxy_csr_f32_rowdot); XTVXY_LOGREG_UNFUSED runs them with
+ * the rocSPARSE comparator of `unfused` (a plan made for the same matrix), everything else
+ * being the same kernels, so the two differ only in how X is multiplied. */
+enum { XTVXY_LOGREG_FUSED = 0, XTVXY_LOGREG_UNFUSED = 1 };
+enum { XTVXY_LOGREG_CONVERGED = 0, XTVXY_LOGREG_ITERATION_LIMIT = 1, XTVXY_LOGREG_LINE_SEARCH_FAILED = 2 };
+
+typedef struct xtvxy_logreg_options {
+  float lambda;            /* L2 weight, finite and >= 0 */
+  int32_t max_newton;      /* Newton steps, >= 0 */
+  int32_t max_cg;          /* CG iterations per step, >= 1 */
+  int32_t max_backtracks;  /* step lengths tried per step (1, 1/2, ...), >= 1 */
+  double grad_tol;         /* stop at |g_k| <= grad_tol |g_0|; finite, >= 0 */
+  double cg_forcing;       /* CG forcing cap, in (0, 1] (0.5 in the textbook) */
+  int32_t fixed_cg;        /* nonzero: no early CG stop on the residual (fixed work per step) */
+  int32_t engine;          /* XTVXY_LOGREG_FUSED or XTVXY_LOGREG_UNFUSED */
+} xtvxy_logreg_options;
+
+typedef struct xtvxy_logreg_report {
+  int32_t status;              /* XTVXY_LOGREG_CONVERGED, _ITERATION_LIMIT or _LINE_SEARCH_FAILED */
+  int32_t newton_iterations;   /* steps taken */
+  int32_t cg_iterations;       /* Hessian-vector products, all steps */
+  int32_t line_search_trials;  /* objective changes evaluated, all steps */
+  double loss0, loss;          /* f at the start and at the returned w */
+  double grad_norm0, grad_norm;/* |g| at the start and at the returned w */
+  double seconds;              /* host wall time from the first enqueue to the last synchronisation */
+} xtvxy_logreg_report;
+
+/* Workspace bytes of xtvxy_logreg_newton_cg_f32 for this shape on the current device (4 m-vectors,
+ * 5 n-vectors, reduction partials, and the workspace of xtvxy_csr_f32_workspace_size). */
+xtvxy_status xtvxy_logreg_newton_cg_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t *bytes);
+
+/* Runs the solver from the caller's w (device, n floats; overwritten with the result).
+ * X is CSR as for xtvxy_csr_f32; labels (device, m floats) are the c_i, normally in {0, 1}
+ * (any value in [0, 1] is a valid soft label). `unfused` must be a plan of the same m, n, nnz
+ * and matrix pointers when opt->engine is XTVXY_LOGREG_UNFUSED and is ignored otherwise.
+ * `report` (host) may be NULL. `history` (host, may be NULL) receives up to history_rows rows of
+ * 6 doubles per iterate k = 0, 1, ...: f_k, |g_k|, CG iterations of step k, g_k.s_k, the accepted
+ * step a_k, line-search trials of step k (the last four are NaN for the final iterate).
+ * Returns argument errors before anything is enqueued; after a HIP or library error, w holds an
+ * unspecified iterate. Not thread-safe for one workspace; the workspace and the inputs must stay
+ * valid for the call (it synchronises `stream` before returning). */
+xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                        const int32_t *col_idx, const float *values, const float *labels,
+                                        float *w, const xtvxy_logreg_options *opt, xtvxy_csr_unfused_plan unfused,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                        xtvxy_logreg_report *report, double *history, int64_t history_rows);
+
 #ifdef __cplusplus
 }
 #endif

@@ -199,3 +199,62 @@ def test_csr_plan_complete_checks_the_bins(lib):
     # a window that covers every column needs no bins
     q = xt.xtvxy_csr_f32_plan_complete(1000, 500, 10**4, lp(500, 1024), MI355X)
     assert q.bin_columns == 0 and q.workspace_bytes == 64 * 500 * 4
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    # sizeof / offsetof of every ABI struct as a C compiler lays them out, against the ctypes mirrors
+    structs = {"xtvxy_device_info": xt.xtvxy_device_info, "xtvxy_launch_params": xt.xtvxy_launch_params,
+               "xtvxy_logreg_options": xt.xtvxy_logreg_options, "xtvxy_logreg_report": xt.xtvxy_logreg_report}
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "xtvxy.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append('  printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for field, _ in cls._fields_:
+            cfield = "lambda" if field == "lambda_" else field
+            lines.append('  printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, field, cname, cfield))
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.dirname(HEADER), "-I/opt/rocm/include",
+                    str(src), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                 check=True).stdout.splitlines())
+    for cname, cls in structs.items():
+        assert int(got[cname]) == ctypes.sizeof(cls), cname
+        for field, _ in cls._fields_:
+            assert int(got["%s.%s" % (cname, field)]) == getattr(cls, field).offset, (cname, field)
+
+
+def logreg_status(m=8, n=4, nnz=16, rp=FAKE, ci=FAKE + 1024, vals=FAKE + 2048, labels=FAKE + 4096, w=FAKE + 8192,
+                  opt=None, plan=None, ws=FAKE + 65536, ws_bytes=1 << 20, history=None, rows=0, **kw):
+    o = xt.xtvxy_logreg_options(1.0, 5, 10, 30, 1e-6, 0.5, 0, xt.XTVXY_LOGREG_FUSED)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return _abi.load().xtvxy_logreg_newton_cg_f32(m, n, nnz, rp, ci, vals, labels, w,
+                                                  ctypes.byref(o) if opt is None else opt, plan, ws, ws_bytes,
+                                                  None, None, history, rows)
+
+
+def test_logreg_argument_errors(lib):
+    E = _abi
+    assert logreg_status(m=-1) == E.XTVXY_ERROR_INVALID_VALUE
+    assert logreg_status(rows=-1) == E.XTVXY_ERROR_INVALID_VALUE
+    assert logreg_status(nnz=1 << 31) == E.XTVXY_ERROR_UNSUPPORTED
+    assert lib.xtvxy_logreg_newton_cg_f32(8, 4, 16, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1, None, None,
+                                          None, 0) == E.XTVXY_ERROR_NULL_POINTER  # no options
+    for field, bad in (("lambda_", -1.0), ("lambda_", float("inf")), ("lambda_", float("nan")), ("max_newton", -1),
+                       ("max_cg", 0), ("max_backtracks", 0), ("grad_tol", -1e-3), ("grad_tol", float("nan")),
+                       ("cg_forcing", 0.0), ("cg_forcing", 1.5), ("engine", 2)):
+        assert logreg_status(**{field: bad}) == E.XTVXY_ERROR_INVALID_VALUE, field
+    assert logreg_status(rp=None) == E.XTVXY_ERROR_NULL_POINTER
+    assert logreg_status(ci=None) == E.XTVXY_ERROR_NULL_POINTER
+    assert logreg_status(labels=None) == E.XTVXY_ERROR_NULL_POINTER
+    assert logreg_status(w=None) == E.XTVXY_ERROR_NULL_POINTER
+    assert logreg_status(rows=3) == E.XTVXY_ERROR_NULL_POINTER                  # history rows without history
+    assert logreg_status(engine=xt.XTVXY_LOGREG_UNFUSED) == E.XTVXY_ERROR_NULL_POINTER  # no comparator plan
+    assert logreg_status(ws=None) == E.XTVXY_ERROR_WORKSPACE
+    assert logreg_status(ws=FAKE + 65536 + 64) == E.XTVXY_ERROR_WORKSPACE     # not 256-byte aligned
+    b = ctypes.c_size_t()
+    assert lib.xtvxy_logreg_newton_cg_f32_workspace_size(-1, 4, 4, ctypes.byref(b)) == E.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_logreg_newton_cg_f32_workspace_size(4, 4, 4, None) == E.XTVXY_ERROR_NULL_POINTER
