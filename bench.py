@@ -137,6 +137,137 @@ def cpu_baseline(p, budget_s: float):
             "kind": "oracle", "sample": "the full workload, %d runs (median %.3f s each)" % (len(runs), med)}
 
 
+LOGREG_METRIC = "Newton-CG logistic regression: ms per Newton iteration (fixed schedule), fused vs unfused products"
+
+
+def logreg_iteration_bytes(m, n, nnz, J, trials) -> int:
+    """Algorithmic bytes of one Newton step with J CG iterations and `trials` line-search trials:
+    the link pass (read t, X s, labels; write t, u, v), the gradient X^T u + lambda w, J
+    Hessian-vector products, X s, and the trials (read t, X s, labels). The n-vector algebra
+    is left out (n << m)."""
+    rows = 4 * (m + 1) + 8 * nnz
+    link = 24 * m
+    grad = rows + 4 * m + 12 * n
+    hvp = rows + 4 * m + 12 * n
+    xs = rows + 4 * n + 4 * m
+    return link + grad + J * hvp + xs + trials * 12 * m
+
+
+def bench_logreg(args):
+    """The Newton-CG solver on its workload: a fixed schedule (K Newton steps of J CG iterations,
+    grad_tol 0) timed for both engines, a run to |g| <= 1e-4 |g_0| for both, the Hessian-vector
+    kernel's roofline at the solver's final curvature weights, and the oracle's time for one step
+    of the same schedule on the host cores."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import dense_linear_algebra_alpha_amd as xt
+
+    xt.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    P = datagen.LOGISTIC_WORKLOADS[args.workload](seed=args.seed)
+    X = P.X
+    rp, ci, vals = (torch.from_numpy(a).to(dev) for a in (X.row_ptr, X.col_idx, X.values))
+    lab = torch.from_numpy(P.labels).to(dev)
+    uplan = xt.CsrUnfusedPlan(rp, ci, vals, X.n)
+    ws = torch.empty(xt.xtvxy_logreg_newton_cg_f32_workspace_size(X.m, X.n, X.nnz), dtype=torch.uint8, device=dev)
+    K, J = args.newton_steps, args.cg_steps
+
+    def solve(engine, **kw):
+        w = torch.zeros(X.n, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        w, rep, hist = xt.logreg_newton_cg(rp, ci, vals, X.n, lab, P.lam, w, engine=engine, unfused_plan=uplan,
+                                           workspace=ws, **kw)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, w, rep, hist
+
+    fixed = dict(grad_tol=0.0, max_newton=K, max_cg=J, fixed_cg=True)
+    results = {}
+    for engine in ("fused", "unfused"):
+        for _ in range(args.warmup_solves):
+            solve(engine, **fixed)
+        runs = [solve(engine, **fixed) for _ in range(args.solves)]
+        wall = statistics.median(r[0] for r in runs)
+        rep = runs[-1][2]
+        conv = solve(engine, grad_tol=1e-4, max_newton=50)
+        results[engine] = {"ms_per_newton_iteration": round(wall / K * 1e3, 4), "solve_ms": round(wall * 1e3, 3),
+                           "line_search_trials": rep["line_search_trials"],
+                           "to_1e-4": {"ms": round(conv[0] * 1e3, 3), "newton_iterations": conv[2]["newton_iterations"],
+                                       "cg_iterations": conv[2]["cg_iterations"], "status": conv[2]["status"],
+                                       "loss": conv[2]["loss"]}}
+    fz = results["fused"]
+    trials = fz["line_search_trials"] / K
+    ibytes = logreg_iteration_bytes(X.m, X.n, X.nnz, J, trials)
+    # the Hessian-vector kernel alone, with the generator's curvature weights p(1 - p) of the planted
+    # model and the generator's y as the direction
+    v = torch.from_numpy(X.v).to(dev)
+    d = torch.from_numpy(X.y).to(dev)
+    q = torch.empty_like(d)
+    hws_bytes = xt.xtvxy_csr_f32_workspace_size(X.m, X.n, X.nnz)
+    hws = torch.empty(max(hws_bytes, 1), dtype=torch.uint8, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream or None
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        xt.xtvxy_csr_f32(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+                         d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh)
+    for i in range(args.steps):
+        xt.xtvxy_set_kernel_timing_events(pairs[i][0], pairs[i][1])
+        xt.xtvxy_csr_f32(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+                         d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh)
+    torch.cuda.synchronize()
+    xt.xtvxy_set_kernel_timing_events(None, None)
+    kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    hvp_bytes = 8 * X.nnz + 4 * (X.m + 1) + 4 * X.m + 12 * X.n
+    achieved = hvp_bytes / (statistics.mean(kernel_ms) / 1e3) / 1e9
+    iter_s = fz["ms_per_newton_iteration"] / 1e3
+    record = {
+        "metric": LOGREG_METRIC,
+        "value": fz["ms_per_newton_iteration"],
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup_solves,
+        "ms_per_step": fz["ms_per_newton_iteration"],
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded generators, seed %d): labels of a planted model" % args.seed,
+        "config": {"workload": args.workload, "m": X.m, "n": X.n, "nnz": X.nnz, "lambda": P.lam,
+                   "schedule": "%d Newton steps x %d CG iterations, grad_tol 0" % (K, J),
+                   "iteration_algorithmic_bytes": int(ibytes)},
+        "iteration_effective_gbs": round(ibytes / iter_s / 1e9, 3),
+        "fused": fz,
+        "unfused": results["unfused"],
+        "speedup_vs_unfused": round(results["unfused"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
+        "roofline": {"bound": "hbm", "kernel": "csr_fused", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "what": "the Hessian-vector product alone (one fused call, v = p(1 - p), y = z = d, "
+                             "beta = lambda)",
+                     "kernel_ms_mean": round(statistics.mean(kernel_ms), 5)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        import oracle.logreg as lr
+        threads = oracle.set_threads(len(os.sched_getaffinity(0)))
+        t0 = time.perf_counter()
+        lr.newton_cg(X.row_ptr, X.col_idx, X.values, X.n, P.labels, P.lam, max_newton=1, max_cg=J, fixed_cg=True,
+                     grad_tol=0.0)
+        cpu_s = time.perf_counter() - t0
+        record["cpu_baseline"] = {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+                                  "sample": "one Newton step of the same schedule on the full workload (fp64 "
+                                            "scipy.sparse products, single-threaded), setup included; threads "
+                                            "available %d" % threads}
+    print(json.dumps(record), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +283,10 @@ def main():
     ap.add_argument("--plan", default=None,
                     help="JSON object of launch-parameter fields that replace the model's choice, e.g. "
                          "'{\"lds_window\": 16384, \"y_window\": 0, \"bin_columns\": 0}' (the library checks the result)")
+    ap.add_argument("--newton-steps", type=int, default=5, help="solver workloads: Newton steps of the timed schedule")
+    ap.add_argument("--cg-steps", type=int, default=10, help="solver workloads: CG iterations per Newton step")
+    ap.add_argument("--solves", type=int, default=5, help="solver workloads: timed solves per engine")
+    ap.add_argument("--warmup-solves", type=int, default=2, help="solver workloads: untimed solves per engine")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -179,8 +314,11 @@ def main():
     import dense_linear_algebra_alpha_amd as xt
 
     xt.load()  # fails loudly when the HIP library is not built
+    if args.workload in datagen.LOGISTIC_WORKLOADS:
+        return bench_logreg(args)
     if args.workload not in datagen.WORKLOADS:
-        raise SystemExit("unknown workload %s (known: %s)" % (args.workload, ", ".join(datagen.WORKLOADS)))
+        known = list(datagen.WORKLOADS) + list(datagen.LOGISTIC_WORKLOADS)
+        raise SystemExit("unknown workload %s (known: %s)" % (args.workload, ", ".join(known)))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     p = datagen.WORKLOADS[args.workload](seed=args.seed)

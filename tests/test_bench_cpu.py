@@ -36,3 +36,12 @@ def test_algorithmic_bytes_count_each_operand_once():
     c = datagen.csr_random(10, 7, seed=2)
     expect = 8 * c.nnz + 4 * 11 + 4 * 7 + 4 * 7 + (4 * 10 if c.v is not None else 0) + (4 * 7 if c.beta else 0)
     assert bench.algorithmic_bytes(c) == expect
+
+
+def test_newton_iteration_bytes():
+    m, n, nnz = 100, 7, 1000
+    rows = 4 * (m + 1) + 8 * nnz
+    # link 24m; gradient and each HVP: rows + 4m + 12n; X s: rows + 4n + 4m; trials 12m each
+    assert bench.logreg_iteration_bytes(m, n, nnz, 0, 0) == 24 * m + (rows + 4 * m + 12 * n) + (rows + 4 * n + 4 * m)
+    assert bench.logreg_iteration_bytes(m, n, nnz, 3, 2) - bench.logreg_iteration_bytes(m, n, nnz, 0, 0) == \
+        3 * (rows + 4 * m + 12 * n) + 2 * 12 * m
