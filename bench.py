@@ -171,7 +171,8 @@ def bench_logreg(args):
     X = P.X
     rp, ci, vals = (torch.from_numpy(a).to(dev) for a in (X.row_ptr, X.col_idx, X.values))
     lab = torch.from_numpy(P.labels).to(dev)
-    uplan = xt.CsrUnfusedPlan(rp, ci, vals, X.n)
+    plans = {"unfused": xt.CsrUnfusedPlan(rp, ci, vals, X.n),
+             "unfused_explicit_transpose": xt.CsrUnfusedPlan(rp, ci, vals, X.n, explicit_transpose=True)}
     ws = torch.empty(xt.xtvxy_logreg_newton_cg_f32_workspace_size(X.m, X.n, X.nnz), dtype=torch.uint8, device=dev)
     K, J = args.newton_steps, args.cg_steps
 
@@ -179,14 +180,15 @@ def bench_logreg(args):
         w = torch.zeros(X.n, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        w, rep, hist = xt.logreg_newton_cg(rp, ci, vals, X.n, lab, P.lam, w, engine=engine, unfused_plan=uplan,
-                                           workspace=ws, **kw)
+        w, rep, hist = xt.logreg_newton_cg(rp, ci, vals, X.n, lab, P.lam, w,
+                                           engine="fused" if engine == "fused" else "unfused",
+                                           unfused_plan=plans.get(engine), workspace=ws, **kw)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, w, rep, hist
 
     fixed = dict(grad_tol=0.0, max_newton=K, max_cg=J, fixed_cg=True)
     results = {}
-    for engine in ("fused", "unfused"):
+    for engine in ("fused", "unfused", "unfused_explicit_transpose"):
         for _ in range(args.warmup_solves):
             solve(engine, **fixed)
         runs = [solve(engine, **fixed) for _ in range(args.solves)]
@@ -246,7 +248,10 @@ def bench_logreg(args):
         "iteration_effective_gbs": round(ibytes / iter_s / 1e9, 3),
         "fused": fz,
         "unfused": results["unfused"],
+        "unfused_explicit_transpose": results["unfused_explicit_transpose"],
         "speedup_vs_unfused": round(results["unfused"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
+        "speedup_vs_unfused_explicit_transpose": round(
+            results["unfused_explicit_transpose"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
         "roofline": {"bound": "hbm", "kernel": "csr_fused", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "what": "the Hessian-vector product alone (one fused call, v = p(1 - p), y = z = d, "
@@ -377,8 +382,14 @@ def main():
         def unfused():
             xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
                                                out.data_ptr(), sh)
+
+        def unfused_explicit():
+            xt.xtvxy_csr_f32_unfused_reference(uplan_t.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta,
+                                               xt._ptr(z), out.data_ptr(), sh)
         if not args.no_unfused and not args.fused_only:
-            uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)  # structure analysis: outside every timed region
+            # structure analysis and the transposed copy: outside every timed region
+            uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)
+            uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
         shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
 
     abytes = algorithmic_bytes(p)
@@ -402,10 +413,13 @@ def main():
 
     step_s, kernel_ms = timed(fused, True)
     fused_out = out.cpu().numpy()
-    unfused_s = None
+    unfused_s = explicit_s = None
     if not args.no_unfused and not args.fused_only:
         unfused_s, _ = timed(unfused, False)
         unfused_out = out.cpu().numpy()
+        if kind == "csr":
+            explicit_s, _ = timed(unfused_explicit, False)
+            explicit_out = out.cpu().numpy()
 
     kernel_s = statistics.mean(kernel_ms) / 1e3
     achieved = abytes / kernel_s / 1e9
@@ -435,6 +449,9 @@ def main():
     if unfused_s is not None:
         record["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
         record["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
+    if explicit_s is not None:  # the same chain with X^T kept as a second CSR matrix
+        record["unfused_explicit_transpose_ms_per_step"] = round(explicit_s * 1e3, 5)
+        record["speedup_vs_unfused_explicit_transpose"] = round(explicit_s / step_s, 3)
 
     # parity of the timed outputs against the oracle (max elementwise error relative to the bound)
     if not args.fused_only:
@@ -449,6 +466,9 @@ def main():
         record["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
         if unfused_s is not None:
             record["unfused_max_rel_err"] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
+        if explicit_s is not None:
+            record["unfused_explicit_transpose_max_rel_err"] = float(
+                np.max(np.abs(explicit_out.astype(np.float64) - ref) / den))
         if not args.no_cpu_baseline:
             record["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
     for a, b in pairs:

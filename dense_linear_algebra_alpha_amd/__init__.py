@@ -21,6 +21,7 @@ import ctypes
 from . import _abi
 from ._abi import (XTVXY_CSR_TILES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
                    XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
+                   XTVXY_UNFUSED_EXPLICIT_TRANSPOSE, XTVXY_UNFUSED_TRANSPOSE_OP,
                    XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,
                    xtvxy_device_info, xtvxy_launch_params, xtvxy_logreg_options, xtvxy_logreg_report)
 
@@ -34,7 +35,7 @@ __all__ = [
     "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
-    "xtvxy_logreg_options", "xtvxy_logreg_report",
+    "xtvxy_logreg_options", "xtvxy_logreg_report", "xtvxy_csr_f32_unfused_plan_create_ex",
 ]
 
 load = _abi.load
@@ -155,6 +156,13 @@ def xtvxy_dense_f32_unfused_reference(m, n, alpha, X, ldx, v, y, beta, z, out, w
 def xtvxy_csr_f32_unfused_plan_create(m, n, nnz, row_ptr, col_idx, values, stream) -> int:
     h = ctypes.c_void_p()
     _abi.call("xtvxy_csr_f32_unfused_plan_create", m, n, nnz, row_ptr, col_idx, values, stream, ctypes.byref(h))
+    return h.value or 0
+
+
+def xtvxy_csr_f32_unfused_plan_create_ex(m, n, nnz, row_ptr, col_idx, values, options, stream) -> int:
+    h = ctypes.c_void_p()
+    _abi.call("xtvxy_csr_f32_unfused_plan_create_ex", m, n, nnz, row_ptr, col_idx, values, int(options), stream,
+              ctypes.byref(h))
     return h.value or 0
 
 
@@ -382,16 +390,19 @@ def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, worksp
 
 
 class CsrUnfusedPlan:
-    """rocSPARSE descriptors and analysis for one CSR matrix (the comparator's setup)."""
+    """rocSPARSE descriptors and analysis for one CSR matrix (the comparator's setup). With
+    ``explicit_transpose`` the plan also keeps a CSR copy of X^T, so that X^T t is a forward SpMV."""
 
-    def __init__(self, row_ptr, col_idx, values, n, stream=None):
+    def __init__(self, row_ptr, col_idx, values, n, stream=None, explicit_transpose=False):
         self.m = row_ptr.numel() - 1
         self.n = n
         self.nnz = col_idx.numel()
         self._keep = (row_ptr, col_idx, values)
-        self.handle = xtvxy_csr_f32_unfused_plan_create(
+        self.handle = xtvxy_csr_f32_unfused_plan_create_ex(
             self.m, n, self.nnz, row_ptr.data_ptr(), col_idx.data_ptr() if self.nnz else None,
-            values.data_ptr() if self.nnz else None, _stream_handle(stream))
+            values.data_ptr() if self.nnz else None,
+            XTVXY_UNFUSED_EXPLICIT_TRANSPOSE if explicit_transpose else XTVXY_UNFUSED_TRANSPOSE_OP,
+            _stream_handle(stream))
 
     def __call__(self, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, stream=None):
         torch = _torch()

@@ -45,6 +45,9 @@ class xtvxy_launch_params(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+XTVXY_UNFUSED_TRANSPOSE_OP = 0
+XTVXY_UNFUSED_EXPLICIT_TRANSPOSE = 1
+
 XTVXY_LOGREG_FUSED = 0
 XTVXY_LOGREG_UNFUSED = 1
 XTVXY_LOGREG_CONVERGED = 0
@@ -104,6 +107,7 @@ SIGNATURES = {
     "xtvxy_dense_f32_unfused_reference": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_unfused_plan_create": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _P(_vp)],
     "xtvxy_csr_f32_unfused_plan_destroy": [_vp],
+    "xtvxy_csr_f32_unfused_plan_create_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _P(_vp)],
     "xtvxy_csr_f32_unfused_reference": [_vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
     "xtvxy_logreg_newton_cg_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],

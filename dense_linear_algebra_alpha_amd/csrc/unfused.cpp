@@ -8,7 +8,10 @@
 //   t   = v .* t                   (elementwise kernel; skipped when v is absent)
 //   out = z                        (device copy, when beta != 0 and out != z)
 //   out = alpha X^T t + beta out   (sgemv / spmv on the transpose, reads X again)
-// so X crosses HBM twice and t makes a round trip, against once for the fused path.
+// so X crosses HBM twice and t makes a round trip, against once for the fused path. rocSPARSE's
+// transposed SpMV serialises on output columns that many rows share; the plan option
+// XTVXY_UNFUSED_EXPLICIT_TRANSPOSE keeps a CSR copy of X^T (made once with csr2csc) so that the
+// last step is a forward SpMV: the stronger operator-level baseline.
 #include <hip/hip_runtime.h>
 #include <rocblas/rocblas.h>
 #include <rocsparse/rocsparse.h>
@@ -56,6 +59,14 @@ struct xtvxy_csr_unfused_plan_s {
   size_t buf_fwd_bytes = 0, buf_tr_bytes = 0;
   float* t = nullptr;       // m floats
   float* dummy_n = nullptr; // n floats, stands in for y/out while the plan is analysed
+  // explicit transpose: X^T as a CSR matrix (n x m), so that X^T t is a forward SpMV
+  bool explicit_t = false;
+  rocsparse_spmat_descr AT = nullptr;
+  int32_t* at_ptr = nullptr;  // n + 1
+  int32_t* at_idx = nullptr;  // nnz
+  float* at_val = nullptr;    // nnz
+  void* buf_at = nullptr;
+  size_t buf_at_bytes = 0;
 };
 
 namespace {
@@ -71,18 +82,80 @@ void destroy_plan(xtvxy_csr_unfused_plan p) {
   if (p->buf_tr) (void)hipFree(p->buf_tr);
   if (p->t) (void)hipFree(p->t);
   if (p->dummy_n) (void)hipFree(p->dummy_n);
+  if (p->AT) rocsparse_destroy_spmat_descr(p->AT);
+  if (p->at_ptr) (void)hipFree(p->at_ptr);
+  if (p->at_idx) (void)hipFree(p->at_idx);
+  if (p->at_val) (void)hipFree(p->at_val);
+  if (p->buf_at) (void)hipFree(p->buf_at);
   delete p;
 }
 
 constexpr rocsparse_spmv_alg kAlg = rocsparse_spmv_alg_default;
 
+rocsparse_status spmv_with(xtvxy_csr_unfused_plan p, rocsparse_spmat_descr mat, rocsparse_operation op,
+                           const float* alpha, rocsparse_dnvec_descr x, const float* beta, rocsparse_dnvec_descr y,
+                           rocsparse_spmv_stage stage, size_t* bytes, void* buf) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Wdeprecated-declarations"
+  return rocsparse_spmv(p->handle, op, alpha, mat, x, beta, y, rocsparse_datatype_f32_r, kAlg, stage, bytes, buf);
+#pragma clang diagnostic pop
+}
+
 rocsparse_status spmv(xtvxy_csr_unfused_plan p, rocsparse_operation op, const float* alpha,
                       rocsparse_dnvec_descr x, const float* beta, rocsparse_dnvec_descr y, rocsparse_spmv_stage stage,
                       size_t* bytes, void* buf) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Wdeprecated-declarations"
-  return rocsparse_spmv(p->handle, op, alpha, p->A, x, beta, y, rocsparse_datatype_f32_r, kAlg, stage, bytes, buf);
-#pragma clang diagnostic pop
+  return spmv_with(p, p->A, op, alpha, x, beta, y, stage, bytes, buf);
+}
+
+// alpha X^T x + beta y: the library's transposed SpMV, or a forward SpMV with the explicit X^T.
+rocsparse_status spmv_transposed(xtvxy_csr_unfused_plan p, const float* alpha, rocsparse_dnvec_descr x,
+                                 const float* beta, rocsparse_dnvec_descr y) {
+  if (p->explicit_t) {
+    size_t bytes = p->buf_at_bytes;
+    return spmv_with(p, p->AT, rocsparse_operation_none, alpha, x, beta, y, rocsparse_spmv_stage_compute, &bytes,
+                     p->buf_at);
+  }
+  size_t bytes = p->buf_tr_bytes;
+  return spmv(p, rocsparse_operation_transpose, alpha, x, beta, y, rocsparse_spmv_stage_compute, &bytes, p->buf_tr);
+}
+
+// Builds X^T (the CSC form of X read as CSR) and analyses the forward SpMV with it.
+xtvxy_status build_transpose(xtvxy_csr_unfused_plan p) {
+  const int64_t m = p->m, n = p->n, nnz = p->nnz;
+  if (hipMalloc(&p->at_ptr, (size_t)(n + 1) * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc(&p->at_idx, (size_t)nnz * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc(&p->at_val, (size_t)nnz * sizeof(float)) != hipSuccess)
+    return XTVXY_ERROR_LAUNCH;
+  size_t tmp_bytes = 0;
+  if (rocsparse_csr2csc_buffer_size(p->handle, (rocsparse_int)m, (rocsparse_int)n, (rocsparse_int)nnz, p->row_ptr,
+                                    p->col_idx, rocsparse_action_numeric, &tmp_bytes) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  void* tmp = nullptr;
+  if (hipMalloc(&tmp, tmp_bytes > 0 ? tmp_bytes : 256) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  const rocsparse_status cs =
+      rocsparse_scsr2csc(p->handle, (rocsparse_int)m, (rocsparse_int)n, (rocsparse_int)nnz, p->values, p->row_ptr,
+                         p->col_idx, p->at_val, p->at_idx, p->at_ptr, rocsparse_action_numeric,
+                         rocsparse_index_base_zero, tmp);
+  hipStream_t s = nullptr;
+  rocsparse_get_stream(p->handle, &s);
+  const hipError_t sync = hipStreamSynchronize(s);
+  (void)hipFree(tmp);
+  if (cs != rocsparse_status_success) return XTVXY_ERROR_LIBRARY;
+  if (sync != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (rocsparse_create_csr_descr(&p->AT, n, m, nnz, p->at_ptr, p->at_idx, p->at_val, rocsparse_indextype_i32,
+                                 rocsparse_indextype_i32, rocsparse_index_base_zero,
+                                 rocsparse_datatype_f32_r) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  const float one = 1.0f, zero = 0.0f;
+  if (spmv_with(p, p->AT, rocsparse_operation_none, &one, p->vec_m, &zero, p->vec_n2,
+                rocsparse_spmv_stage_buffer_size, &p->buf_at_bytes, nullptr) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  if (hipMalloc(&p->buf_at, p->buf_at_bytes > 0 ? p->buf_at_bytes : 256) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (spmv_with(p, p->AT, rocsparse_operation_none, &one, p->vec_m, &zero, p->vec_n2,
+                rocsparse_spmv_stage_preprocess, &p->buf_at_bytes, p->buf_at) != rocsparse_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  p->explicit_t = true;
+  return XTVXY_SUCCESS;
 }
 
 }  // namespace
@@ -134,9 +207,18 @@ xtvxy_status xtvxy_dense_f32_unfused_reference(int64_t m, int64_t n, float alpha
 xtvxy_status xtvxy_csr_f32_unfused_plan_create(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
                                                const int32_t* col_idx, const float* values, hipStream_t stream,
                                                xtvxy_csr_unfused_plan* out_plan) {
+  return xtvxy_csr_f32_unfused_plan_create_ex(m, n, nnz, row_ptr, col_idx, values, XTVXY_UNFUSED_TRANSPOSE_OP,
+                                              stream, out_plan);
+}
+
+xtvxy_status xtvxy_csr_f32_unfused_plan_create_ex(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
+                                                  const int32_t* col_idx, const float* values, int32_t options,
+                                                  hipStream_t stream, xtvxy_csr_unfused_plan* out_plan) {
   if (!out_plan) return XTVXY_ERROR_NULL_POINTER;
   *out_plan = nullptr;
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (options != XTVXY_UNFUSED_TRANSPOSE_OP && options != XTVXY_UNFUSED_EXPLICIT_TRANSPOSE)
+    return XTVXY_ERROR_INVALID_VALUE;
   if (nnz > INT32_MAX || m >= INT32_MAX || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   if (!row_ptr || (nnz > 0 && (!col_idx || !values))) return XTVXY_ERROR_NULL_POINTER;
   xtvxy_csr_unfused_plan p = new xtvxy_csr_unfused_plan_s;
@@ -183,6 +265,10 @@ xtvxy_status xtvxy_csr_f32_unfused_plan_create(int64_t m, int64_t n, int64_t nnz
       spmv(p, rocsparse_operation_transpose, &one, p->vec_m, &zero, p->vec_n2, rocsparse_spmv_stage_preprocess,
            &p->buf_tr_bytes, p->buf_tr) != rocsparse_status_success)
     return fail(XTVXY_ERROR_LIBRARY);
+  if (options == XTVXY_UNFUSED_EXPLICIT_TRANSPOSE) {
+    const xtvxy_status st = build_transpose(p);
+    if (st != XTVXY_SUCCESS) return fail(st);
+  }
   if (hipStreamSynchronize(stream) != hipSuccess) return fail(XTVXY_ERROR_LAUNCH);
   *out_plan = p;
   return XTVXY_SUCCESS;
@@ -222,9 +308,7 @@ xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan p, float alp
   } else if (launch_zero(out, (size_t)p->n * sizeof(float), stream) != hipSuccess) {
     return XTVXY_ERROR_LAUNCH;  // the transposed product scales out by beta: start from zeros
   }
-  bytes = p->buf_tr_bytes;
-  if (spmv(p, rocsparse_operation_transpose, &alpha, p->vec_m, &beta, p->vec_n2, rocsparse_spmv_stage_compute,
-           &bytes, p->buf_tr) != rocsparse_status_success)
+  if (spmv_transposed(p, &alpha, p->vec_m, &beta, p->vec_n2) != rocsparse_status_success)
     return XTVXY_ERROR_LIBRARY;
   return XTVXY_SUCCESS;
 }
@@ -275,9 +359,7 @@ xtvxy_status unfused_tmv(xtvxy_csr_unfused_plan p, float alpha, const float* u, 
       rocsparse_dnvec_set_values(p->vec_m, const_cast<float*>(u)) != rocsparse_status_success ||
       rocsparse_dnvec_set_values(p->vec_n2, out) != rocsparse_status_success)
     return XTVXY_ERROR_LIBRARY;
-  size_t bytes = p->buf_tr_bytes;
-  const rocsparse_status r = spmv(p, rocsparse_operation_transpose, &alpha, p->vec_m, &beta, p->vec_n2,
-                                  rocsparse_spmv_stage_compute, &bytes, p->buf_tr);
+  const rocsparse_status r = spmv_transposed(p, &alpha, p->vec_m, &beta, p->vec_n2);
   if (rocsparse_dnvec_set_values(p->vec_m, p->t) != rocsparse_status_success || r != rocsparse_status_success)
     return XTVXY_ERROR_LIBRARY;
   return XTVXY_SUCCESS;

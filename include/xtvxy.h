@@ -247,9 +247,22 @@ xtvxy_status xtvxy_csr_f32_unfused_plan_create(int64_t m, int64_t n, int64_t nnz
                                                xtvxy_csr_unfused_plan *plan);
 xtvxy_status xtvxy_csr_f32_unfused_plan_destroy(xtvxy_csr_unfused_plan plan);
 
+/* Plan options. XTVXY_UNFUSED_TRANSPOSE_OP: X^T t is rocSPARSE's SpMV with the transpose
+ * operation on X (the plain operator-level chain). XTVXY_UNFUSED_EXPLICIT_TRANSPOSE: the plan
+ * also builds X^T as a second CSR matrix once (rocSPARSE csr2csc; 8 nnz + 4 (n + 1) more bytes
+ * of device memory, made at plan creation, blocking) and X^T t becomes a forward SpMV with it:
+ * the stronger comparator wherever the library's transposed SpMV is slow (it serialises on
+ * shared output columns). The plan must be destroyed before X's buffers are freed; the copy
+ * holds X's values as of plan creation. */
+enum { XTVXY_UNFUSED_TRANSPOSE_OP = 0, XTVXY_UNFUSED_EXPLICIT_TRANSPOSE = 1 };
+xtvxy_status xtvxy_csr_f32_unfused_plan_create_ex(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                                  const int32_t *col_idx, const float *values, int32_t options,
+                                                  hipStream_t stream, xtvxy_csr_unfused_plan *plan);
+
 /* rocSPARSE SpMV (t = X y), the elementwise kernel, and rocSPARSE SpMV with
- * the transposed matrix (out = alpha X^T t + beta out). Uses the plan's
- * buffers; not thread-safe per plan. */
+ * the transposed matrix (out = alpha X^T t + beta out; with the explicit
+ * transpose, a forward SpMV with the plan's X^T). Uses the plan's buffers;
+ * not thread-safe per plan. */
 xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan plan, float alpha,
                                              const float *v, const float *y, float beta,
                                              const float *z, float *out, hipStream_t stream);

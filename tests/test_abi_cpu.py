@@ -107,6 +107,11 @@ def test_query_argument_errors(lib):
     assert b.value >= 400 and b.value % 256 == 0
     assert lib.xtvxy_csr_f32_unfused_plan_create(4, 4, 4, None, FAKE, FAKE, None, None) == \
         _abi.XTVXY_ERROR_NULL_POINTER
+    h = ctypes.c_void_p()
+    assert lib.xtvxy_csr_f32_unfused_plan_create_ex(4, 4, 4, FAKE, FAKE, FAKE, 7, None, ctypes.byref(h)) == \
+        _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_csr_f32_unfused_plan_create_ex(4, 4, 4, None, FAKE, FAKE, 1, None, ctypes.byref(h)) == \
+        _abi.XTVXY_ERROR_NULL_POINTER
 
 
 SHAPES = [(2048, 128), (1_000_000, 256), (65_536, 8192), (8192, 65_536), (1, 1), (7, 3), (100, 1000),

@@ -31,14 +31,15 @@ def test_dense_comparator_in_place_and_quick_returns():
     assert np.array_equal(d.run(unfused=True, alpha=0.0, beta=0.5), (np.float32(0.5) * p.z).astype(np.float32))
 
 
+@pytest.mark.parametrize("explicit", [False, True])
 @pytest.mark.parametrize("m,n,mean_len", [(3000, 1000, 10.0), (2000, 50000, 30.0), (10, 5, 2.0)])
 @pytest.mark.parametrize("beta", [0.0, 0.75])
-def test_csr_comparator(m, n, mean_len, beta):
+def test_csr_comparator(m, n, mean_len, beta, explicit):
     import torch
-    p = datagen.csr_random(m, n, seed=m + n, mean_len=mean_len, beta=beta)
+    p = datagen.csr_random(m, n, seed=m + n, mean_len=mean_len, beta=beta)  # unsorted and repeated columns
     d = CsrOnDevice(p)
-    note("csr unfused m=%d n=%d" % (m, n))
-    plan = xt.CsrUnfusedPlan(d.rp, d.ci, d.vals, n)
+    note("csr unfused m=%d n=%d explicit_transpose=%s" % (m, n, explicit))
+    plan = xt.CsrUnfusedPlan(d.rp, d.ci, d.vals, n, explicit_transpose=explicit)
     out = torch.full((n,), float("nan"), device="cuda")  # beta == 0 must not read out
     plan(d.y, d.v, d.z if beta else None, p.alpha, beta, out=out)
     torch.cuda.synchronize()
@@ -46,3 +47,35 @@ def test_csr_comparator(m, n, mean_len, beta):
                                              p.z if beta else None, p.alpha, beta))
     assert_parity(out.cpu().numpy(), ref, bnd, "csr unfused")
     plan.close()
+
+
+def test_explicit_transpose_halves_and_empty_matrices():
+    # the solver's unfused engine uses both halves through the plan; the explicit copy must give
+    # the same products, including the shapes with nothing to multiply
+    import torch
+    p = datagen.csr_random(4000, 700, seed=21, mean_len=12.0, beta=0.5)
+    d = CsrOnDevice(p)
+    note("csr unfused explicit transpose, solver engine")
+    for explicit in (False, True):
+        plan = xt.CsrUnfusedPlan(d.rp, d.ci, d.vals, p.n, explicit_transpose=explicit)
+        lab = torch.from_numpy((np.arange(p.m) % 3 == 0).astype(np.float32)).cuda()
+        w, rep, hist = xt.logreg_newton_cg(d.rp, d.ci, d.vals, p.n, lab, 1.0, engine="unfused", unfused_plan=plan,
+                                           max_newton=3, max_cg=2, fixed_cg=True, grad_tol=0.0)
+        torch.cuda.synchronize()
+        if not explicit:
+            base = (w.cpu().numpy(), [h["loss"] for h in hist])
+        else:
+            # the same steps; the products differ only in fp32 summation order
+            assert np.max(np.abs(w.cpu().numpy() - base[0])) <= 1e-4 * np.max(np.abs(base[0]))
+            assert np.allclose([h["loss"] for h in hist], base[1], rtol=1e-6)
+        plan.close()
+    for m, n in ((0, 5), (6, 0), (6, 5)):
+        rp = torch.zeros(m + 1, dtype=torch.int32, device="cuda")
+        e = torch.zeros(0, dtype=torch.int32, device="cuda")
+        ev = torch.zeros(0, dtype=torch.float32, device="cuda")
+        plan = xt.CsrUnfusedPlan(rp, e, ev, n, explicit_transpose=True)
+        z = torch.ones(n, device="cuda")
+        out = plan(torch.ones(n, device="cuda"), None, z, 1.0, 0.5)
+        torch.cuda.synchronize()
+        assert np.all(out.cpu().numpy() == 0.5)
+        plan.close()
