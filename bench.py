@@ -273,6 +273,36 @@ def bench_logreg(args):
     print(json.dumps(record), flush=True)
 
 
+def report_tuning(args, p, kind, abytes, env):
+    """--tune: the empirical tuner on this workload; prints the model's plan, the best measured plan,
+    their times and the model's regret (model time / best time - 1)."""
+    import dense_linear_algebra_alpha_amd as xt
+    y, v, z, out, sh = env["y"], env["v"], env["z"], env["out"], env["sh"]
+    t0 = time.perf_counter()
+    if kind == "dense":
+        X = env["X"]
+        rep = xt.xtvxy_dense_f32_tune(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                                      xt._ptr(z), out.data_ptr(), args.tune_repeats, sh)
+    else:
+        rp, ci, vals = env["rp"], env["ci"], env["vals"]
+        rep = xt.xtvxy_csr_f32_tune(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
+                                    args.tune_repeats, sh)
+    wall = time.perf_counter() - t0
+    r = rep.as_dict()
+    keep = lambda d: {k: v_ for k, v_ in d.items() if k != "predicted_seconds"}
+    record = {"metric": "analytical model regret against the empirical tuner (model time / best time - 1)",
+              "value": round(r["model_seconds"] / r["best_seconds"] - 1.0, 4), "unit": "fraction",
+              "higher_is_better": False, "config": {"workload": args.workload, "repeats": args.tune_repeats},
+              "model_ms": round(r["model_seconds"] * 1e3, 5), "best_ms": round(r["best_seconds"] * 1e3, 5),
+              "model_gbs": round(abytes / r["model_seconds"] / 1e9, 1),
+              "best_gbs": round(abytes / r["best_seconds"] / 1e9, 1), "candidates": r["candidates"],
+              "tuning_seconds": round(wall, 2), "model_plan": keep(r["model"]), "best_plan": keep(r["best"])}
+    if args.tune_cache:
+        xt.xtvxy_tune_cache_save(args.tune_cache)
+    print(json.dumps(record), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +322,10 @@ def main():
     ap.add_argument("--cg-steps", type=int, default=10, help="solver workloads: CG iterations per Newton step")
     ap.add_argument("--solves", type=int, default=5, help="solver workloads: timed solves per engine")
     ap.add_argument("--warmup-solves", type=int, default=2, help="solver workloads: untimed solves per engine")
+    ap.add_argument("--tune", action="store_true",
+                    help="run the empirical tuner on the workload and report the analytical model's regret")
+    ap.add_argument("--tune-repeats", type=int, default=10, help="timed calls per candidate plan (--tune)")
+    ap.add_argument("--tune-cache", default=None, help="save the tuner's cache to this file (--tune)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -386,13 +420,15 @@ def main():
         def unfused_explicit():
             xt.xtvxy_csr_f32_unfused_reference(uplan_t.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta,
                                                xt._ptr(z), out.data_ptr(), sh)
-        if not args.no_unfused and not args.fused_only:
+        if not args.no_unfused and not args.fused_only and not args.tune:
             # structure analysis and the transposed copy: outside every timed region
             uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)
             uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
         shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
 
     abytes = algorithmic_bytes(p)
+    if args.tune:
+        return report_tuning(args, p, kind, abytes, locals())
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
 

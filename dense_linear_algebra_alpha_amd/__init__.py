@@ -23,7 +23,8 @@ from ._abi import (XTVXY_CSR_TILES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_RO
                    XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
                    XTVXY_UNFUSED_EXPLICIT_TRANSPOSE, XTVXY_UNFUSED_TRANSPOSE_OP,
                    XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,
-                   xtvxy_device_info, xtvxy_launch_params, xtvxy_logreg_options, xtvxy_logreg_report)
+                   xtvxy_device_info, xtvxy_launch_params, xtvxy_logreg_options, xtvxy_logreg_report,
+                   xtvxy_tune_report)
 
 __all__ = [
     "xtvxy_get_device_info", "xtvxy_dense_f32_plan", "xtvxy_dense_f32_plan_complete", "xtvxy_csr_f32_plan",
@@ -36,6 +37,8 @@ __all__ = [
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
     "xtvxy_logreg_options", "xtvxy_logreg_report", "xtvxy_csr_f32_unfused_plan_create_ex",
+    "xtvxy_dense_f32_tune", "xtvxy_csr_f32_tune", "xtvxy_tune_cache_lookup", "xtvxy_tune_cache_clear",
+    "xtvxy_tune_cache_save", "xtvxy_tune_cache_load", "xtvxy_tune_report", "dense_tune", "csr_tune",
 ]
 
 load = _abi.load
@@ -172,6 +175,41 @@ def xtvxy_csr_f32_unfused_plan_destroy(plan: int):
 
 def xtvxy_csr_f32_unfused_reference(plan, alpha, v, y, beta, z, out, stream):
     return _abi.call("xtvxy_csr_f32_unfused_reference", plan, alpha, v, y, beta, z, out, stream)
+
+
+def xtvxy_dense_f32_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream) -> xtvxy_tune_report:
+    rep = xtvxy_tune_report()
+    _abi.call("xtvxy_dense_f32_tune", m, n, alpha, X, ldx, v, y, beta, z, out, int(repeats), stream,
+              ctypes.byref(rep))
+    return rep
+
+
+def xtvxy_csr_f32_tune(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, repeats,
+                       stream) -> xtvxy_tune_report:
+    rep = xtvxy_tune_report()
+    _abi.call("xtvxy_csr_f32_tune", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, int(repeats),
+              stream, ctypes.byref(rep))
+    return rep
+
+
+def xtvxy_tune_cache_lookup(kind, m, n, k, aligned):
+    """(report, found) for a shape on the current device."""
+    rep = xtvxy_tune_report()
+    found = ctypes.c_int32()
+    _abi.call("xtvxy_tune_cache_lookup", int(kind), m, n, k, int(aligned), ctypes.byref(rep), ctypes.byref(found))
+    return rep, bool(found.value)
+
+
+def xtvxy_tune_cache_clear():
+    return _abi.call("xtvxy_tune_cache_clear")
+
+
+def xtvxy_tune_cache_save(path: str):
+    return _abi.call("xtvxy_tune_cache_save", path.encode())
+
+
+def xtvxy_tune_cache_load(path: str):
+    return _abi.call("xtvxy_tune_cache_load", path.encode())
 
 
 def xtvxy_logreg_newton_cg_f32_workspace_size(m, n, nnz) -> int:
@@ -467,3 +505,26 @@ def logreg_newton_cg(row_ptr, col_idx, values, n, labels, lam, w=None, *, max_ne
         row = {key: hist[k * len(_HISTORY_KEYS) + i] for i, key in enumerate(_HISTORY_KEYS)}
         history.append(row)
     return w, rep.as_dict(), history
+
+
+def dense_tune(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=10, stream=None) -> dict:
+    """Tune the dense fused call on these tensors (2-D X with unit column stride); returns the report."""
+    torch = _torch()
+    m, n = X.shape
+    ldx = max(X.stride(0) if m > 1 else n, n, 1)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=X.device)
+    return xtvxy_dense_f32_tune(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z),
+                                out.data_ptr(), repeats, _stream_handle(stream)).as_dict()
+
+
+def csr_tune(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=10,
+             stream=None) -> dict:
+    """Tune the CSR fused call on these tensors; returns the report."""
+    torch = _torch()
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=device)
+    return xtvxy_csr_f32_tune(m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx), _ptr(values), _ptr(v),
+                              y.data_ptr(), float(beta), _ptr(z), out.data_ptr(), repeats,
+                              _stream_handle(stream)).as_dict()

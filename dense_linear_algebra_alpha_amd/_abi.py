@@ -71,6 +71,15 @@ class xtvxy_logreg_report(ctypes.Structure):
         return {name: getattr(self, name) for name, _ in self._fields_}
 
 
+class xtvxy_tune_report(ctypes.Structure):
+    _fields_ = [("model", xtvxy_launch_params), ("best", xtvxy_launch_params), ("model_seconds", ctypes.c_double),
+                ("best_seconds", ctypes.c_double), ("candidates", ctypes.c_int32), ("from_cache", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {"model": self.model.as_dict(), "best": self.best.as_dict(), "model_seconds": self.model_seconds,
+                "best_seconds": self.best_seconds, "candidates": self.candidates, "from_cache": self.from_cache}
+
+
 class XtvxyError(RuntimeError):
     def __init__(self, status: int, where: str = ""):
         self.status = int(status)
@@ -110,6 +119,14 @@ SIGNATURES = {
     "xtvxy_csr_f32_unfused_plan_create_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _P(_vp)],
     "xtvxy_csr_f32_unfused_reference": [_vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
+    "xtvxy_dense_f32_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                             _P(xtvxy_tune_report)],
+    "xtvxy_csr_f32_tune": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                           _P(xtvxy_tune_report)],
+    "xtvxy_tune_cache_lookup": [_i32, _i64, _i64, _i64, _i32, _P(xtvxy_tune_report), _P(ctypes.c_int32)],
+    "xtvxy_tune_cache_clear": [],
+    "xtvxy_tune_cache_save": [ctypes.c_char_p],
+    "xtvxy_tune_cache_load": [ctypes.c_char_p],
     "xtvxy_logreg_newton_cg_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_logreg_newton_cg_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _P(xtvxy_logreg_options), _vp, _vp,
                                    _sz, _vp, _P(xtvxy_logreg_report), _P(ctypes.c_double), _i64],

@@ -5,9 +5,11 @@
 // aggregate: out_j = alpha * S_j + beta * z_j with S_j the sum of the fused
 // kernel's per-workgroup partials (plus, for the CSR path, the columns outside
 // the LDS window: a global accumulator, or the partial rows of the units of the
-// column's bin written by csr_bins.hip). Each 1024-thread workgroup owns 64 columns;
-// 16 thread rows each sum a strided subset of the partials in fp64, and the 16
-// results are combined in a fixed order, so the result is bitwise reproducible.
+// column's bin written by csr_bins.hip). Each 1024-thread workgroup owns COLS columns
+// (64, or 16 for outputs of at most 4096 columns, so that a narrow output still spreads
+// over several CUs); 1024 / COLS thread rows each sum a strided subset of the partials in
+// fp64, and their results are combined in a fixed order, so the result is bitwise
+// reproducible for a given plan.
 // The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
 // reads z; out may alias z (each element is read before it is written by the
 // same thread).
@@ -16,13 +18,15 @@
 namespace xtvxy {
 namespace {
 
-constexpr int kAggCols = 64, kAggRows = 16;
+constexpr int kAggThreads = 1024;
+constexpr int64_t kNarrowOutput = 4096;  // outputs up to this width use 16 columns per workgroup
 
-__global__ __launch_bounds__(kAggCols * kAggRows) void aggregate_kernel(const float* __restrict__ partial,
-                                                                        int64_t rows, int64_t ldp,
-                                                                        const float* __restrict__ acc, int64_t n,
-                                                                        float alpha, float beta, const float* z,
-                                                                        float* out, BinPartials bins) {
+template <int kAggCols>
+__global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __restrict__ partial, int64_t rows,
+                                                                int64_t ldp, const float* __restrict__ acc,
+                                                                int64_t n, float alpha, float beta, const float* z,
+                                                                float* out, BinPartials bins) {
+  constexpr int kAggRows = kAggThreads / kAggCols;
   __shared__ double sh[kAggRows][kAggCols];
   const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
   const int64_t j = (int64_t)blockIdx.x * kAggCols + tx;
@@ -91,10 +95,14 @@ hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, con
                             float alpha, float beta, const float* z, float* out, hipStream_t s,
                             const BinPartials* bins) {
   if (n <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)((n + kAggCols - 1) / kAggCols);
   const BinPartials none{nullptr, nullptr, 0, 0};
-  hipLaunchKernelGGL(aggregate_kernel, dim3(grid), dim3(kAggCols * kAggRows), 0, s, partial, rows, ldp, acc, n,
-                     alpha, beta, z, out, bins ? *bins : none);
+  if (n <= kNarrowOutput) {
+    hipLaunchKernelGGL(aggregate_kernel<16>, dim3((unsigned)((n + 15) / 16)), dim3(kAggThreads), 0, s, partial,
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+  } else {
+    hipLaunchKernelGGL(aggregate_kernel<64>, dim3((unsigned)((n + 63) / 64)), dim3(kAggThreads), 0, s, partial,
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+  }
   return hipGetLastError();
 }
 

@@ -268,6 +268,54 @@ xtvxy_status xtvxy_csr_f32_unfused_reference(xtvxy_csr_unfused_plan plan, float 
                                              const float *z, float *out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
+/* Empirical tuning beside the analytical model                            */
+/* ------------------------------------------------------------------------ */
+
+/* The pages' analytical model picks launch parameters from the input's characteristics and the
+ * GPU's resources and calls the choice near-optimal ("On optimizing machine learning workloads via
+ * kernel fusion", abstract). The tuner checks that on the actual input: it times the fused call
+ * under every candidate plan the kernels accept for the shape (row layouts, chunks, group sizes and
+ * grid sizes for dense X; tile shapes, output and y windows, atomics or bins and grid sizes for
+ * CSR; the model's plan among them), re-times the fastest few with the model's plan, and reports
+ * both. The model's regret is model_seconds / best_seconds - 1.
+ *
+ * A set-up call, not a fused entry point: it allocates its own workspace (the largest any
+ * candidate needs, e.g. about 2 GB for binned plans of a 2e8-entry matrix), synchronises `stream`,
+ * runs the full computation many times and leaves in `out` the result of the last call timed.
+ * Arguments as for xtvxy_dense_f32 / xtvxy_csr_f32, plus `repeats` (1..10000) timed calls per
+ * candidate (the finalists take 3x). A call whose only work is out = beta z has nothing to tune
+ * and returns XTVXY_ERROR_INVALID_VALUE. Results are cached per (device, kind, m, n, ldx or nnz,
+ * 16-byte alignment of X) for the life of the process; a cached shape returns at once with
+ * from_cache = 1. Pass report.best to the _ex entry points to use the tuned plan (their
+ * workspace is report.best.workspace_bytes). */
+typedef struct xtvxy_tune_report {
+  xtvxy_launch_params model;  /* the analytical model's plan */
+  xtvxy_launch_params best;   /* the fastest plan measured */
+  double model_seconds;       /* mean seconds per call with the model's plan (final round) */
+  double best_seconds;        /* mean seconds per call with the best plan (final round) */
+  int32_t candidates;         /* plans timed */
+  int32_t from_cache;         /* 1: answered from the cache */
+} xtvxy_tune_report;
+
+xtvxy_status xtvxy_dense_f32_tune(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx, const float *v,
+                                  const float *y, float beta, const float *z, float *out, int32_t repeats,
+                                  hipStream_t stream, xtvxy_tune_report *report);
+xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                const int32_t *col_idx, const float *values, const float *v, const float *y,
+                                float beta, const float *z, float *out, int32_t repeats, hipStream_t stream,
+                                xtvxy_tune_report *report);
+/* Cache access: kind 0 = dense (k = ldx, aligned = X % 16 == 0), 1 = CSR (k = nnz, aligned = values
+ * and col_idx 16-byte aligned); *found = 0 when the shape was not tuned on the current device.
+ * save/load use a text file (one line per entry); load merges, and takes nothing from a file with
+ * a malformed line (XTVXY_ERROR_INVALID_VALUE). Plans read from a file are checked again by the
+ * _ex entry points that use them. */
+xtvxy_status xtvxy_tune_cache_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t aligned,
+                                     xtvxy_tune_report *report, int32_t *found);
+xtvxy_status xtvxy_tune_cache_clear(void);
+xtvxy_status xtvxy_tune_cache_save(const char *path);
+xtvxy_status xtvxy_tune_cache_load(const char *path);
+
+/* ------------------------------------------------------------------------ */
 /* An ML algorithm on the pattern: Newton-CG for logistic regression        */
 /* ------------------------------------------------------------------------ */
 

@@ -209,7 +209,8 @@ def test_csr_plan_complete_checks_the_bins(lib):
 def test_struct_layouts_match_the_header(tmp_path):
     # sizeof / offsetof of every ABI struct as a C compiler lays them out, against the ctypes mirrors
     structs = {"xtvxy_device_info": xt.xtvxy_device_info, "xtvxy_launch_params": xt.xtvxy_launch_params,
-               "xtvxy_logreg_options": xt.xtvxy_logreg_options, "xtvxy_logreg_report": xt.xtvxy_logreg_report}
+               "xtvxy_logreg_options": xt.xtvxy_logreg_options, "xtvxy_logreg_report": xt.xtvxy_logreg_report,
+               "xtvxy_tune_report": xt.xtvxy_tune_report}
     lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "xtvxy.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append('  printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
@@ -263,3 +264,47 @@ def test_logreg_argument_errors(lib):
     b = ctypes.c_size_t()
     assert lib.xtvxy_logreg_newton_cg_f32_workspace_size(-1, 4, 4, ctypes.byref(b)) == E.XTVXY_ERROR_INVALID_VALUE
     assert lib.xtvxy_logreg_newton_cg_f32_workspace_size(4, 4, 4, None) == E.XTVXY_ERROR_NULL_POINTER
+
+
+def test_tune_argument_errors(lib):
+    rep = xt.xtvxy_tune_report()
+    assert lib.xtvxy_dense_f32_tune(8, 8, 1.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 10, None,
+                                    None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert lib.xtvxy_dense_f32_tune(8, 8, 1.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 0, None,
+                                    ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # repeats
+    assert lib.xtvxy_dense_f32_tune(8, 8, 1.0, FAKE, 7, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5, None,
+                                    ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # ldx < n
+    # alpha = 0: the call reads no X, nothing to tune
+    assert lib.xtvxy_dense_f32_tune(8, 8, 0.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5, None,
+                                    ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_csr_f32_tune(8, 8, 16, 1.0, None, FAKE, FAKE, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5,
+                                  None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert lib.xtvxy_csr_f32_tune(8, 8, 0, 1.0, FAKE, None, None, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5,
+                                  None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # nnz = 0
+    found = ctypes.c_int32()
+    assert lib.xtvxy_tune_cache_lookup(2, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) == \
+        _abi.XTVXY_ERROR_INVALID_VALUE
+
+
+def test_tune_cache_file_round_trip(lib, tmp_path):
+    # a hand-written cache line loads, saves back unchanged, and a malformed file changes nothing
+    plan = "11 1 256 0 1 1 1024 0 8 1000 1000 0 4096000"
+    model = "11 1 256 0 1 1 1024 0 8 1000 1000 0 4096000"
+    line = "gfx950:256 1 10000000 1000 100006237 1 %s %s 2.140000000e-04 2.150000000e-04 24" % (plan, model)
+    src = tmp_path / "in.txt"
+    src.write_text("# comment\n" + line + "\n")
+    xt.xtvxy_tune_cache_clear()
+    xt.xtvxy_tune_cache_load(str(src))
+    out = tmp_path / "out.txt"
+    xt.xtvxy_tune_cache_save(str(out))
+    body = [l for l in out.read_text().splitlines() if not l.startswith("#")]
+    assert body == [line]
+    bad = tmp_path / "bad.txt"
+    bad.write_text(line + "\n" + "gfx950:256 1 5 5\n")
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_tune_cache_load(str(bad))
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_tune_cache_load(str(tmp_path / "missing.txt"))
+    xt.xtvxy_tune_cache_clear()
+    xt.xtvxy_tune_cache_save(str(out))
+    assert [l for l in out.read_text().splitlines() if not l.startswith("#")] == []
