@@ -96,6 +96,22 @@ def normal(count: int, seed: int, name: str, mean: float = 0.0, std: float = 1.0
     return out
 
 
+def to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), rounding to nearest with ties to even; NaN stays a
+    quiet NaN of the same sign. Storage rounding of an input, done once here."""
+    bits = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16)
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    if nan.any():
+        rounded[nan] = ((bits[nan] >> 16).astype(np.uint16) & 0x8000) | 0x7FC0
+    return rounded
+
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the fp32 values they denote (exact)."""
+    return (np.asarray(h, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def _vector(kind: Optional[str], count: int, seed: int, name: str) -> Optional[np.ndarray]:
     if kind is None:
         return None
@@ -116,13 +132,14 @@ class DenseProblem:
     m: int
     n: int
     ldx: int
-    X: np.ndarray                 # flat fp32, length m*ldx (padding columns hold NaN)
+    X: np.ndarray                 # flat, length m*ldx (padding columns hold NaN): fp32, or uint16 bf16 bits
     y: np.ndarray
     v: Optional[np.ndarray]
     z: Optional[np.ndarray]
     alpha: float
     beta: float
     name: str = ""
+    x_dtype: str = "f32"          # "f32" or "bf16"
 
     def X2d(self) -> np.ndarray:
         return self.X.reshape(self.m, self.ldx)[:, : self.n]
@@ -150,19 +167,24 @@ class CsrProblem:
 
 
 def dense_problem(m, n, seed=0, *, x="uniform", y="uniform", v="uniform", z="uniform", alpha=1.5,
-                  beta=0.5, ldx=None, name="") -> DenseProblem:
-    """Dense problem whose entries follow the named distributions (None = argument absent)."""
+                  beta=0.5, ldx=None, name="", x_dtype="f32") -> DenseProblem:
+    """Dense problem whose entries follow the named distributions (None = argument absent). With
+    x_dtype "bf16" the same X is rounded to bf16 (to_bf16) and stored as uint16 bit patterns."""
     ldx = n if ldx is None else int(ldx)
     if ldx < n:
         raise ValueError("ldx < n")
+    if x_dtype not in ("f32", "bf16"):
+        raise ValueError("x_dtype must be f32 or bf16")
     body = _vector(x, m * n, seed, "X")
     if ldx == n:
         X = body if body is not None else np.zeros(m * n, np.float32)
     else:
         X = np.full(m * ldx, np.nan, dtype=np.float32)
         X.reshape(m, ldx)[:, :n] = body.reshape(m, n)
+    if x_dtype == "bf16":
+        X = to_bf16(X)
     return DenseProblem(m, n, ldx, X, _vector(y, n, seed, "y"), _vector(v, m, seed, "v"),
-                        _vector(z, n, seed, "z"), float(alpha), float(beta), name)
+                        _vector(z, n, seed, "z"), float(alpha), float(beta), name, x_dtype)
 
 
 def _row_ptr(row_len: np.ndarray) -> np.ndarray:
@@ -307,6 +329,16 @@ WORKLOADS = {
     "dense_8192x65536": lambda seed=0, m=8192, n=65536: dense_problem(
         m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
         name="dense_8192x65536"),
+    # the same three dense workloads with X stored as bf16 (rounded to nearest even from the fp32 draw)
+    "dense_1000000x256_normal_equations_bf16": lambda seed=0, m=1_000_000, n=256: dense_problem(
+        m, n, seed, x="normal", y="normal", v=None, z=None, alpha=1.0, beta=0.0,
+        name="dense_1000000x256_normal_equations_bf16", x_dtype="bf16"),
+    "dense_65536x8192_bf16": lambda seed=0, m=65536, n=8192: dense_problem(
+        m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
+        name="dense_65536x8192_bf16", x_dtype="bf16"),
+    "dense_8192x65536_bf16": lambda seed=0, m=8192, n=65536: dense_problem(
+        m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
+        name="dense_8192x65536_bf16", x_dtype="bf16"),
     # logistic-regression Hessian-vector product: 1% Bernoulli sparsity, values and y ~ N(0, 1),
     # v = p(1 - p) with p = sigmoid(X w), w ~ N(0, 0.1^2), beta 0
     "csr_10000000x1000_logistic_hvp": lambda seed=0, m=10_000_000, n=1000: csr_bernoulli(

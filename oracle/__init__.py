@@ -47,6 +47,7 @@ def _bind(path: str):
     dense_args = [i64, i64, f32, vp, i64, vp, vp, f32, vp, vp]
     csr_args = [i64, i64, i64, f32, vp, vp, vp, vp, vp, f32, vp, vp]
     for name, args in (("oracle_dense", dense_args), ("oracle_dense_bound", dense_args),
+                       ("oracle_dense_bf16", dense_args), ("oracle_dense_bf16_bound", dense_args),
                        ("oracle_csr", csr_args), ("oracle_csr_bound", csr_args),
                        ("oracle_csr_rowdot", csr_args), ("oracle_csr_rowdot_bound", csr_args),
                        ("oracle_csr_tmv", csr_args[:8] + [f32, vp, vp]),
@@ -91,7 +92,8 @@ def _check(rc: int, name: str):
 
 def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, *, ldx=None, m=None, n=None, bound=False,
           lib=None):
-    """Oracle value (or the error normaliser when ``bound``) for dense row-major fp32 X.
+    """Oracle value (or the error normaliser when ``bound``) for dense row-major X, fp32 or
+    bf16 (a uint16 array of bf16 bit patterns).
 
     ``X`` is a 2-D array (m x n) or, with ``ldx``/``m``/``n`` given, a flat
     buffer whose row i starts at element i*ldx.
@@ -102,13 +104,17 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, *, ldx=None, m=None, n=None
         ldx = n
     if m is None or n is None or ldx is None:
         raise ValueError("flat X needs m, n and ldx")
-    Xa, Xp = _ptr(X, np.float32)
+    bf16 = np.asarray(X).dtype == np.uint16
+    Xa, Xp = _ptr(X, np.uint16 if bf16 else np.float32)
     ya, yp = _ptr(y, np.float32)
     va, vp_ = _ptr(v, np.float32)
     za, zp = _ptr(z, np.float32)
     out = np.empty(int(n), dtype=np.float64)
     lib = lib or _load()
-    fn = lib.oracle_dense_bound if bound else lib.oracle_dense
+    if bf16:
+        fn = lib.oracle_dense_bf16_bound if bound else lib.oracle_dense_bf16
+    else:
+        fn = lib.oracle_dense_bound if bound else lib.oracle_dense
     rc = fn(int(m), int(n), float(alpha), Xp, int(ldx), vp_, yp, float(beta), zp,
             out.ctypes.data_as(ctypes.c_void_p))
     _check(rc, fn.__name__)

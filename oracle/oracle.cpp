@@ -15,9 +15,11 @@
 //                         of two m-vectors that gives an m-vector)
 //     X^T (.)  ordinary transposed matrix-vector product (n-vector)
 //     z        n-vector,  alpha, beta scalars.
-// Every input is the exact fp32 array given to the GPU; each element is
-// promoted to fp64 exactly and all arithmetic below is fp64, evaluated in the
-// plain order of the definition:
+// Every input is the exact array given to the GPU; each element is promoted
+// to fp64 exactly and all arithmetic below is fp64, evaluated in the plain
+// order of the definition. Dense X may also be stored as bf16 (reduced-precision
+// storage of X): a bf16 element is the upper 16 bits of an fp32 bit pattern,
+// so it widens exactly by appending 16 zero bits; the rest is unchanged.
 //     step 1  t_i = sum_k X_ik y_k             (k ascending; CSR: storage order)
 //     step 2  u_i = v_i t_i                    (v absent => v_i = 1)
 //     step 3  S_j = sum_i X_ij u_i             (i ascending)
@@ -46,6 +48,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 #include <omp.h>
 
@@ -54,6 +57,16 @@ namespace {
 enum { ORACLE_OK = 0, ORACLE_BAD_SIZE = 1, ORACLE_NULL = 2 };
 
 inline double val(double x, bool absolute) { return absolute ? std::fabs(x) : x; }
+
+// An element of X as a double: fp32 promoted exactly; bf16 widened to the fp32 with these
+// upper 16 bits and zero lower bits, then promoted.
+inline double elem(float x) { return (double)x; }
+inline double elem(uint16_t h) {
+  const uint32_t b = (uint32_t)h << 16;
+  float f;
+  std::memcpy(&f, &b, sizeof f);
+  return (double)f;
+}
 
 // step 4 for the cases where the sum S is not formed (alpha == 0 or m == 0):
 // out_j = beta z_j, and 0 when beta == 0 (z unread).
@@ -72,7 +85,8 @@ void epilogue(int64_t n, float alpha, const std::vector<double>& S, float beta, 
   }
 }
 
-int dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+template <class Elem>
+int dense_impl(int64_t m, int64_t n, float alpha, const Elem* X, int64_t ldx, const float* v,
                const float* y, float beta, const float* z, double* out, bool absolute) {
   if (m < 0 || n < 0) return ORACLE_BAD_SIZE;
   if (n == 0) return ORACLE_OK;
@@ -89,9 +103,9 @@ int dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, c
   std::vector<double> u((size_t)m);
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < m; ++i) {
-    const float* row = X + i * ldx;
+    const Elem* row = X + i * ldx;
     double t = 0.0;
-    for (int64_t k = 0; k < n; ++k) t += val((double)row[k], absolute) * val((double)y[k], absolute);
+    for (int64_t k = 0; k < n; ++k) t += val(elem(row[k]), absolute) * val((double)y[k], absolute);
     const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);
     u[(size_t)i] = vi * t;
   }
@@ -103,9 +117,9 @@ int dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, c
     const int64_t T = omp_get_num_threads(), me = omp_get_thread_num();
     const int64_t j0 = n * me / T, j1 = n * (me + 1) / T;
     for (int64_t i = 0; i < m; ++i) {
-      const float* row = X + i * ldx;
+      const Elem* row = X + i * ldx;
       const double ui = u[(size_t)i];
-      for (int64_t j = j0; j < j1; ++j) S[(size_t)j] += val((double)row[j], absolute) * ui;
+      for (int64_t j = j0; j < j1; ++j) S[(size_t)j] += val(elem(row[j]), absolute) * ui;
     }
   }
 
@@ -256,6 +270,17 @@ int oracle_dense(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx,
 // D_j, the same steps on absolute values.
 int oracle_dense_bound(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx,
                        const float* v, const float* y, float beta, const float* z, double* bound) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, bound, true);
+}
+
+// The same for dense X stored as bf16 bit patterns (row-major, leading dimension ldx).
+int oracle_dense_bf16(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx, const float* v,
+                      const float* y, float beta, const float* z, double* ref) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, ref, false);
+}
+
+int oracle_dense_bf16_bound(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx,
+                            const float* v, const float* y, float beta, const float* z, double* bound) {
   return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, bound, true);
 }
 

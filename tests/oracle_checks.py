@@ -403,8 +403,50 @@ def check_halves_bounds(lib):
                           _tmv(lib, p.row_ptr, p.col_idx, a[0], 30, a[1], a[2], 2.0, 3.0, bound=True))
 
 
+def check_bf16_worked_example(lib):
+    # X = [[1.5, -2], [0.25, 3]] in bf16 (bits 0x3FC0, 0xC000, 0x3E80, 0x4040), y = (1, 2), v = (2, -1):
+    # t = (1.5 - 4, 0.25 + 6) = (-2.5, 6.25); u = v t = (-5, -6.25);
+    # S = X^T u = (1.5(-5) + 0.25(-6.25), -2(-5) + 3(-6.25)) = (-9.0625, -8.75);
+    # out = 2 S + 0.5 z with z = (1, -1): (-17.625, -18)
+    X = np.array([[0x3FC0, 0xC000], [0x3E80, 0x4040]], dtype=np.uint16)
+    y = np.array([1, 2], np.float32)
+    v = np.array([2, -1], np.float32)
+    z = np.array([1, -1], np.float32)
+    got = _dense(lib, X, y, v, z, 2.0, 0.5)
+    assert np.array_equal(got, [-17.625, -18.0]), got
+    # the bound: |X|^T (|v| (|X| |y|)) = (1.5 * 11 + 0.25 * 6.5, 2 * 11 + 3 * 6.5) with |X||y| = (5.5, 6.25)
+    bnd = _dense(lib, X, y, v, z, 2.0, 0.5, bound=True)
+    want = 2 * np.array([1.5 * 11 + 0.25 * 6.25, 2 * 11 + 3 * 6.25]) + 0.5
+    assert np.array_equal(bnd, want), (bnd, want)
+
+
+def check_bf16_equals_the_widened_matrix(lib):
+    # bf16 X gives exactly the fp32 result of the matrix it denotes (widened here by numpy), for
+    # every value class: normal, subnormal, +-0, +-inf, NaN, and a padded leading dimension
+    g = np.random.default_rng(7)
+    m, n, ldx = 37, 29, 33
+    h = datagen.to_bf16(g.normal(0, 3, m * ldx).astype(np.float32))
+    specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F7F, 0xFF7F], dtype=np.uint16)
+    h[: specials.size] = specials
+    y = g.uniform(-1, 1, n).astype(np.float32)
+    v = g.uniform(-1, 1, m).astype(np.float32)
+    z = g.uniform(-1, 1, n).astype(np.float32)
+    wide = datagen.bf16_to_f32(h)
+    for bound in (False, True):
+        a = _dense(lib, h, y, v, z, 0.75, -0.5, m=m, n=n, ldx=ldx, bound=bound)
+        b = _dense(lib, wide, y, v, z, 0.75, -0.5, m=m, n=n, ldx=ldx, bound=bound)
+        assert np.array_equal(a, b)
+    inf_nan = h.copy()
+    inf_nan[3 * ldx + 4] = 0x7F80   # +inf in row 3
+    inf_nan[5 * ldx + 2] = 0xFFC0   # NaN in row 5
+    a = _dense(lib, inf_nan, y, v, z, 0.75, -0.5, m=m, n=n, ldx=ldx)
+    b = _dense(lib, datagen.bf16_to_f32(inf_nan), y, v, z, 0.75, -0.5, m=m, n=n, ldx=ldx)
+    assert np.array_equal(a, b, equal_nan=True) and np.isnan(a).any()
+
+
 CHECKS = [check_golden, check_brute_force_dense, check_brute_force_csr, check_exact_integers,
           check_closed_forms, check_special_cases, check_invariants, check_csr_dense_agree,
           check_nan_propagation, check_scipy, check_bound, check_thread_independence,
           check_error_codes, check_halves_golden, check_halves_explicit_matrix,
-          check_halves_compose_into_the_pattern, check_halves_special_cases, check_halves_bounds]
+          check_halves_compose_into_the_pattern, check_halves_special_cases, check_halves_bounds,
+          check_bf16_worked_example, check_bf16_equals_the_widened_matrix]

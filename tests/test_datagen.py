@@ -104,3 +104,18 @@ def test_logistic_labels():
         sel = (p >= lo) & (p < hi)
         k = int(sel.sum())
         assert k > 1000 and abs(P.labels[sel].mean() - p[sel].mean()) < 4 * np.sqrt(0.25 / k)
+
+
+def test_bf16_rounding():
+    # ties go to the even neighbour; other values to the nearest; bf16 values round-trip exactly
+    f = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -(1.0 + 2.0 ** -8),
+                  np.finfo(np.float32).max, np.inf, -0.0], dtype=np.float32)
+    h = datagen.to_bf16(f)
+    assert list(h) == [0x3F80, 0x3F82, 0x3F81, 0xBF80, 0x7F80, 0x7F80, 0x8000], [hex(x) for x in h]
+    g = datagen.bf16_to_f32(np.arange(0, 0x7F80, 7, dtype=np.uint16))
+    assert np.array_equal(datagen.to_bf16(g), np.arange(0, 0x7F80, 7, dtype=np.uint16))
+    n = datagen.to_bf16(np.array([np.nan, -np.nan], dtype=np.float32))
+    assert np.all(np.isnan(datagen.bf16_to_f32(n)))
+    p = datagen.dense_problem(20, 8, seed=3, x_dtype="bf16", ldx=9)
+    q = datagen.dense_problem(20, 8, seed=3, ldx=9)
+    assert p.X.dtype == np.uint16 and np.array_equal(p.X, datagen.to_bf16(q.X))

@@ -28,12 +28,16 @@ MUTATIONS = [
     ("alpha_dropped", "double r = val((double)alpha, absolute) * S[j];", "double r = S[j];", 0),
     ("dense_dot_drops_last_term", "for (int64_t k = 0; k < n; ++k) t +=",
      "for (int64_t k = 0; k + 1 < n; ++k) t +=", 0),
-    ("dense_dot_wrong_y_index", "val((double)row[k], absolute) * val((double)y[k], absolute)",
-     "val((double)row[k], absolute) * val((double)y[n - 1 - k], absolute)", 0),
-    ("dense_transpose_wrong_column", "S[(size_t)j] += val((double)row[j], absolute) * ui;",
-     "S[(size_t)j] += val((double)row[n - 1 - j], absolute) * ui;", 0),
-    ("dense_step1_ignores_ldx", "const float* row = X + i * ldx;", "const float* row = X + i * n;", 0),
-    ("dense_step3_ignores_ldx", "const float* row = X + i * ldx;", "const float* row = X + i * n;", 1),
+    ("dense_dot_wrong_y_index", "val(elem(row[k]), absolute) * val((double)y[k], absolute)",
+     "val(elem(row[k]), absolute) * val((double)y[n - 1 - k], absolute)", 0),
+    ("dense_transpose_wrong_column", "S[(size_t)j] += val(elem(row[j]), absolute) * ui;",
+     "S[(size_t)j] += val(elem(row[n - 1 - j]), absolute) * ui;", 0),
+    ("dense_step1_ignores_ldx", "const Elem* row = X + i * ldx;", "const Elem* row = X + i * n;", 0),
+    ("dense_step3_ignores_ldx", "const Elem* row = X + i * ldx;", "const Elem* row = X + i * n;", 1),
+    ("bf16_widened_by_15_bits", "const uint32_t b = (uint32_t)h << 16;", "const uint32_t b = (uint32_t)h << 15;", 0),
+    ("bf16_read_as_low_half", "const uint32_t b = (uint32_t)h << 16;", "const uint32_t b = (uint32_t)h;", 0),
+    ("bf16_sign_dropped", "const uint32_t b = (uint32_t)h << 16;", "const uint32_t b = (uint32_t)(h & 0x7fff) << 16;",
+     0),
     ("csr_gathers_y_by_row", "val((double)y[col_idx[p]], absolute)", "val((double)y[i % n], absolute)", 0),
     ("csr_scatters_by_row", "S[(size_t)col_idx[p]] +=", "S[(size_t)(i % n)] +=", 0),
     ("csr_drops_repeated_column",
