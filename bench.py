@@ -38,7 +38,8 @@ def algorithmic_bytes(p) -> int:
         b = 8 * p.nnz + 4 * (p.m + 1) + 4 * p.n + 4 * p.n
         b += 4 * p.m if p.v is not None else 0
     else:
-        b = 4 * p.m * p.n + 4 * p.n + 4 * p.n
+        xb = 2 if getattr(p, "x_dtype", "f32") == "bf16" else 4  # bf16 storage of X: 2 bytes per element
+        b = xb * p.m * p.n + 4 * p.n + 4 * p.n
         b += 4 * p.m if p.v is not None else 0
     b += 4 * p.n if p.beta != 0 else 0
     return b
@@ -281,7 +282,8 @@ def report_tuning(args, p, kind, abytes, env):
     t0 = time.perf_counter()
     if kind == "dense":
         X = env["X"]
-        rep = xt.xtvxy_dense_f32_tune(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+        tune_fn = xt.xtvxy_dense_bf16_tune if env["bf16"] else xt.xtvxy_dense_f32_tune
+        rep = tune_fn(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
                                       xt._ptr(z), out.data_ptr(), args.tune_repeats, sh)
     else:
         rp, ci, vals = env["rp"], env["ci"], env["vals"]
@@ -307,8 +309,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    # the GPU's clocks and translation caches settle over the first ~10 ms of work
-    ap.add_argument("--warmup", type=int, default=50)
+    # the GPU's clocks and translation caches settle over the first ~10-20 ms of work
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-unfused", action="store_true")
@@ -364,35 +366,55 @@ def main():
     kind = "csr" if hasattr(p, "col_idx") else "dense"
 
     def t(a):
-        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:  # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
 
     y, v, z = t(p.y), t(p.v), t(p.z)
     out = torch.empty(p.n, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream or None
+    bf16 = getattr(p, "x_dtype", "f32") == "bf16"
     if kind == "dense":
         X = t(p.X)
-        plan = xt.xtvxy_dense_f32_plan(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
+        plan_fn, complete_fn, ws_fn, call, call_ex = (
+            (xt.xtvxy_dense_bf16_plan, xt.xtvxy_dense_bf16_plan_complete, xt.xtvxy_dense_bf16_workspace_size,
+             xt.xtvxy_dense_bf16, xt.xtvxy_dense_bf16_ex) if bf16 else
+            (xt.xtvxy_dense_f32_plan, xt.xtvxy_dense_f32_plan_complete, xt.xtvxy_dense_f32_workspace_size,
+             xt.xtvxy_dense_f32, xt.xtvxy_dense_f32_ex))
+        plan = plan_fn(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
         forced = override(plan, args.plan)
         if forced:
-            plan = xt.xtvxy_dense_f32_plan_complete(p.m, p.n, p.ldx, plan)
-        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
+            plan = complete_fn(p.m, p.n, p.ldx, plan)
+        ws_bytes = plan.workspace_bytes if forced else ws_fn(p.m, p.n, p.ldx)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
         uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev)
+        # bf16 X: the comparison is the fp32 fused path on the same matrix widened to fp32
+        X32 = t(datagen.bf16_to_f32(p.X)) if bf16 and not args.no_unfused and not args.fused_only else X
+        ws32_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
+        ws32 = torch.empty(max(ws32_bytes, 1), dtype=torch.uint8, device=dev)
 
         def fused():
             if forced:
-                xt.xtvxy_dense_f32_ex(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
-                                      xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
+                call_ex(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                        out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
             else:
-                xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
-                                   xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+                call(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                     out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
 
         def unfused():
-            xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(),
-                                                 p.beta, xt._ptr(z), out.data_ptr(), uws.data_ptr(), uws_bytes, sh)
-        shape = {"m": p.m, "n": p.n, "ldx": p.ldx}
+            if bf16:
+                xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X32.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                                   xt._ptr(z), out.data_ptr(), ws32.data_ptr(), ws32_bytes, sh)
+            else:
+                xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v),
+                                                     y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
+                                                     uws.data_ptr(), uws_bytes, sh)
+        shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": "bf16" if bf16 else "f32"}
     else:
         rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
         plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
@@ -482,7 +504,10 @@ def main():
                      "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
                      "kernel_ms_min": round(min(kernel_ms), 5)},
     }
-    if unfused_s is not None:
+    if unfused_s is not None and bf16:  # the comparison is the fp32 fused path on the widened X
+        record["f32_fused_ms_per_step"] = round(unfused_s * 1e3, 5)
+        record["speedup_vs_f32_fused"] = round(unfused_s / step_s, 3)
+    elif unfused_s is not None:
         record["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
         record["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
     if explicit_s is not None:  # the same chain with X^T kept as a second CSR matrix
@@ -501,7 +526,8 @@ def main():
         den = np.where(bnd > 0, bnd, 1.0)
         record["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
         if unfused_s is not None:
-            record["unfused_max_rel_err"] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
+            key = "f32_fused_max_rel_err" if bf16 else "unfused_max_rel_err"
+            record[key] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
         if explicit_s is not None:
             record["unfused_explicit_transpose_max_rel_err"] = float(
                 np.max(np.abs(explicit_out.astype(np.float64) - ref) / den))

@@ -39,6 +39,8 @@ __all__ = [
     "xtvxy_logreg_options", "xtvxy_logreg_report", "xtvxy_csr_f32_unfused_plan_create_ex",
     "xtvxy_dense_f32_tune", "xtvxy_csr_f32_tune", "xtvxy_tune_cache_lookup", "xtvxy_tune_cache_clear",
     "xtvxy_tune_cache_save", "xtvxy_tune_cache_load", "xtvxy_tune_report", "dense_tune", "csr_tune",
+    "xtvxy_dense_bf16_workspace_size", "xtvxy_dense_bf16_plan", "xtvxy_dense_bf16_plan_complete",
+    "xtvxy_dense_bf16", "xtvxy_dense_bf16_ex", "xtvxy_dense_bf16_tune",
 ]
 
 load = _abi.load
@@ -72,6 +74,34 @@ def xtvxy_dense_f32_plan(m, n, ldx, X_aligned16=1, dev=None) -> xtvxy_launch_par
 def xtvxy_dense_f32_plan_complete(m, n, ldx, plan: xtvxy_launch_params, dev=None) -> xtvxy_launch_params:
     _abi.call("xtvxy_dense_f32_plan_complete", m, n, ldx, ctypes.byref(dev) if dev else None, ctypes.byref(plan))
     return plan
+
+
+def xtvxy_dense_bf16_plan(m, n, ldx, X_aligned16=1, dev=None) -> xtvxy_launch_params:
+    p = xtvxy_launch_params()
+    _abi.call("xtvxy_dense_bf16_plan", m, n, ldx, int(X_aligned16), ctypes.byref(dev) if dev else None,
+              ctypes.byref(p))
+    return p
+
+
+def xtvxy_dense_bf16_plan_complete(m, n, ldx, plan: xtvxy_launch_params, dev=None) -> xtvxy_launch_params:
+    _abi.call("xtvxy_dense_bf16_plan_complete", m, n, ldx, ctypes.byref(dev) if dev else None, ctypes.byref(plan))
+    return plan
+
+
+def xtvxy_dense_bf16_workspace_size(m, n, ldx) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_dense_bf16_workspace_size", m, n, ldx, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_dense_bf16(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream):
+    return _abi.call("xtvxy_dense_bf16", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream)
+
+
+def xtvxy_dense_bf16_ex(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force):
+    return _abi.call("xtvxy_dense_bf16_ex", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream, ctypes.byref(force) if force is not None else None)
 
 
 def xtvxy_csr_f32_plan(m, n, nnz, dev=None) -> xtvxy_launch_params:
@@ -184,6 +214,13 @@ def xtvxy_dense_f32_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, strea
     return rep
 
 
+def xtvxy_dense_bf16_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream) -> xtvxy_tune_report:
+    rep = xtvxy_tune_report()
+    _abi.call("xtvxy_dense_bf16_tune", m, n, alpha, X, ldx, v, y, beta, z, out, int(repeats), stream,
+              ctypes.byref(rep))
+    return rep
+
+
 def xtvxy_csr_f32_tune(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, repeats,
                        stream) -> xtvxy_tune_report:
     rep = xtvxy_tune_report()
@@ -261,8 +298,9 @@ def _workspace(nbytes: int, device):
     return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
 
 
-def dense_plan(m, n, ldx=None, aligned=True, dev=None) -> xtvxy_launch_params:
-    return xtvxy_dense_f32_plan(m, n, n if ldx is None else ldx, 1 if aligned else 0, dev)
+def dense_plan(m, n, ldx=None, aligned=True, dev=None, bf16=False) -> xtvxy_launch_params:
+    fn = xtvxy_dense_bf16_plan if bf16 else xtvxy_dense_f32_plan
+    return fn(m, n, n if ldx is None else ldx, 1 if aligned else 0, dev)
 
 
 def csr_plan(m, n, nnz, dev=None) -> xtvxy_launch_params:
@@ -273,8 +311,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
           workspace=None, stream=None):
     """out = alpha X^T (v .* (X y)) + beta z for dense row-major X on the GPU.
 
-    X is a 2-D float32 CUDA tensor with unit column stride (row stride = ldx), or a
-    flat buffer with m, n and ldx given. ``plan`` forces launch parameters."""
+    X is a 2-D CUDA tensor with unit column stride (row stride = ldx), or a flat buffer with m,
+    n and ldx given; float32, or bf16 storage (torch.bfloat16, or uint16 bit patterns), which
+    takes the xtvxy_dense_bf16 entry points. ``plan`` forces launch parameters."""
     torch = _torch()
     if X.dim() == 2 and m is None:
         m, n = X.shape
@@ -284,8 +323,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
         ldx = max(ldx, n, 1)
     if m is None or n is None or ldx is None:
         raise ValueError("flat X needs m, n and ldx")
-    if X.dtype != torch.float32:
-        raise ValueError("X must be float32")
+    bf16 = X.dtype in (torch.bfloat16, torch.uint16)
+    if X.dtype != torch.float32 and not bf16:
+        raise ValueError("X must be float32, bfloat16 or uint16 (bf16 bits)")
     device = X.device
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
@@ -294,7 +334,7 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
         out = torch.empty(n, dtype=torch.float32, device=device)
     _check_vec("out", out, n, device)
     if plan is None:
-        need = xtvxy_dense_f32_workspace_size(m, n, ldx)
+        need = (xtvxy_dense_bf16_workspace_size if bf16 else xtvxy_dense_f32_workspace_size)(m, n, ldx)
     else:
         need = int(plan.workspace_bytes)
     if workspace is None:
@@ -303,9 +343,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
     args = (m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(),
             ws_ptr, ws_bytes, _stream_handle(stream))
     if plan is None:
-        xtvxy_dense_f32(*args)
+        (xtvxy_dense_bf16 if bf16 else xtvxy_dense_f32)(*args)
     else:
-        xtvxy_dense_f32_ex(*args, plan)
+        (xtvxy_dense_bf16_ex if bf16 else xtvxy_dense_f32_ex)(*args, plan)
     return out
 
 
@@ -514,7 +554,8 @@ def dense_tune(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=1
     ldx = max(X.stride(0) if m > 1 else n, n, 1)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=X.device)
-    return xtvxy_dense_f32_tune(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z),
+    fn = xtvxy_dense_bf16_tune if X.dtype in (torch.bfloat16, torch.uint16) else xtvxy_dense_f32_tune
+    return fn(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z),
                                 out.data_ptr(), repeats, _stream_handle(stream)).as_dict()
 
 

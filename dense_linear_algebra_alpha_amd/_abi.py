@@ -101,6 +101,12 @@ SIGNATURES = {
     "xtvxy_dense_f32": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_dense_f32_ex": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
                            _P(xtvxy_launch_params)],
+    "xtvxy_dense_bf16_workspace_size": [_i64, _i64, _i64, _P(_sz)],
+    "xtvxy_dense_bf16_plan": [_i64, _i64, _i64, _i32, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_dense_bf16_plan_complete": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_dense_bf16": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_dense_bf16_ex": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                            _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_csr_f32": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
@@ -121,6 +127,8 @@ SIGNATURES = {
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
     "xtvxy_dense_f32_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
                              _P(xtvxy_tune_report)],
+    "xtvxy_dense_bf16_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                              _P(xtvxy_tune_report)],
     "xtvxy_csr_f32_tune": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
                            _P(xtvxy_tune_report)],
     "xtvxy_tune_cache_lookup": [_i32, _i64, _i64, _i64, _i32, _P(xtvxy_tune_report), _P(ctypes.c_int32)],

@@ -63,8 +63,9 @@ hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) :
 
 // Checks shared by the dense fused entry point and its comparator. Returns SUCCESS with
 // *quick set when nothing beyond out = beta z (or nothing at all) has to be computed.
-xtvxy_status check_dense(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
-                         const float* y, float beta, const float* z, const float* out, bool* quick) {
+xtvxy_status check_dense(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
+                         const float* y, float beta, const float* z, const float* out, bool* quick,
+                         int elem_bytes = 4) {
   *quick = false;
   if (m < 0 || n < 0) return XTVXY_ERROR_INVALID_VALUE;
   if (ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
@@ -79,7 +80,7 @@ xtvxy_status check_dense(int64_t m, int64_t n, float alpha, const float* X, int6
   if (reads_x && !X) return XTVXY_ERROR_NULL_POINTER;
   const size_t nb = (size_t)n * sizeof(float);
   if (reads_x) {
-    const size_t xb = ((size_t)(m - 1) * ldx + n) * sizeof(float);
+    const size_t xb = ((size_t)(m - 1) * ldx + n) * (size_t)elem_bytes;
     if (overlap(out, nb, X, xb) || overlap(out, nb, y, nb) || (v && overlap(out, nb, v, (size_t)m * sizeof(float))))
       return XTVXY_ERROR_ALIASING;
   }
@@ -114,16 +115,20 @@ xtvxy_status check_csr(int64_t m, int64_t n, int64_t nnz, float alpha, const int
   return XTVXY_SUCCESS;
 }
 
+xtvxy_status dense_plan_query(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info* dev,
+                              xtvxy_launch_params* plan, int elem_bytes);
+
 xtvxy_status dense_plan_for(int64_t m, int64_t n, int64_t ldx, bool aligned, const xtvxy_device_info& d,
-                            const xtvxy_launch_params* force, xtvxy_launch_params* plan) {
+                            const xtvxy_launch_params* force, xtvxy_launch_params* plan, int elem_bytes = 4) {
   if (force) {
     *plan = *force;
-    xtvxy_status st = complete_dense(m, n, ldx, d, plan);
+    xtvxy_status st = complete_dense(m, n, ldx, d, plan, elem_bytes);
     if (st != XTVXY_SUCCESS) return st;
-    if (plan->vec == 4 && (!aligned || ldx % 4 != 0)) return XTVXY_ERROR_INVALID_VALUE;
+    const int wide = 16 / elem_bytes;  // a 16-byte load per chunk needs an aligned X and ldx
+    if (plan->vec == wide && (!aligned || ldx % wide != 0)) return XTVXY_ERROR_INVALID_VALUE;
     return XTVXY_SUCCESS;
   }
-  return model_dense(m, n, ldx, aligned, d, plan);
+  return dense_plan_query(m, n, ldx, aligned ? 1 : 0, nullptr, plan, elem_bytes);
 }
 
 xtvxy_status csr_plan_for(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
@@ -138,24 +143,79 @@ xtvxy_status csr_plan_for(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
 // The co-resident limit of the cooperative group-row kernel is only known on the device:
 // shrink the grid to it (whole groups) and recompute the coarsening.
 xtvxy_status fit_group_grid(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
-                            xtvxy_launch_params* plan, bool forced) {
+                            xtvxy_launch_params* plan, bool forced, int elem_bytes = 4) {
   if (plan->kernel != XTVXY_DENSE_GROUP_ROWS) return XTVXY_SUCCESS;
-  const int64_t cap = dense_group_max_resident(*plan) / plan->group * plan->group;
+  const int64_t cap = dense_group_max_resident(*plan, elem_bytes) / plan->group * plan->group;
   if (cap < plan->group) return XTVXY_ERROR_LAUNCH;
   if (plan->grid > cap) {
     if (forced) return XTVXY_ERROR_INVALID_VALUE;
     plan->grid = cap;
     plan->rows_per_unit = 0;
-    return complete_dense(m, n, ldx, d, plan);
+    return complete_dense(m, n, ldx, d, plan, elem_bytes);
   }
   return XTVXY_SUCCESS;
 }
 
-xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+xtvxy_status dense_plan_query(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info* dev,
+                              xtvxy_launch_params* plan, int elem_bytes) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  if (d.compute_units <= 0 || d.hbm_bytes_per_s <= 0) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_status st = model_dense(m, n, ldx, X_aligned16 != 0, d, plan, elem_bytes);
+  if (st == XTVXY_SUCCESS && !dev) {
+    // on the current device the kernel's residency is known: cap the workgroups per CU by it
+    const int resident = dense_resident_per_cu(*plan, elem_bytes);
+    int cap = 1;
+    while (cap * 2 <= resident) cap *= 2;
+    if (resident > 0 && plan->grid > (int64_t)d.compute_units * cap)
+      st = model_dense(m, n, ldx, X_aligned16 != 0, d, plan, elem_bytes, cap);
+    if (st == XTVXY_SUCCESS) st = fit_group_grid(m, n, ldx, d, plan, false, elem_bytes);
+  }
+  return st;
+}
+
+xtvxy_status dense_complete_query(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info* dev,
+                                  xtvxy_launch_params* plan, int elem_bytes) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else {
+    xtvxy_status st = device_info(-1, &d);
+    if (st != XTVXY_SUCCESS) return st;
+  }
+  return complete_dense(m, n, ldx, d, plan, elem_bytes);
+}
+
+xtvxy_status dense_workspace_query(int64_t m, int64_t n, int64_t ldx, size_t* bytes, int elem_bytes) {
+  if (!bytes) return XTVXY_ERROR_NULL_POINTER;
+  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
+  *bytes = 0;
+  if (m == 0 || n == 0) return XTVXY_SUCCESS;
+  size_t best = 0;
+  for (int aligned = 0; aligned < 2; ++aligned) {
+    xtvxy_launch_params p;
+    xtvxy_status st = dense_plan_query(m, n, ldx, aligned, nullptr, &p, elem_bytes);
+    if (st != XTVXY_SUCCESS) return st;
+    if ((size_t)p.workspace_bytes > best) best = (size_t)p.workspace_bytes;
+  }
+  *bytes = best;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
                         const float* y, float beta, const float* z, float* out, void* ws, size_t ws_bytes,
-                        hipStream_t stream, const xtvxy_launch_params* force) {
+                        hipStream_t stream, const xtvxy_launch_params* force, int elem_bytes = 4) {
   bool quick = false;
-  xtvxy_status st = check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, &quick);
+  xtvxy_status st = check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, &quick, elem_bytes);
   if (st != XTVXY_SUCCESS) return st;
   if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
   xtvxy_device_info d;
@@ -163,9 +223,9 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64
   if (st != XTVXY_SUCCESS) return st;
   const bool aligned = (reinterpret_cast<uintptr_t>(X) % 16) == 0;
   xtvxy_launch_params plan;
-  st = dense_plan_for(m, n, ldx, aligned, d, force, &plan);
+  st = dense_plan_for(m, n, ldx, aligned, d, force, &plan, elem_bytes);
   if (st != XTVXY_SUCCESS) return st;
-  st = fit_group_grid(m, n, ldx, d, &plan, force != nullptr);
+  st = fit_group_grid(m, n, ldx, d, &plan, force != nullptr, elem_bytes);
   if (st != XTVXY_SUCCESS) return st;
   if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
@@ -177,6 +237,7 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const float* X, int64
   a.n = n;
   a.ldx = ldx;
   a.X = X;
+  a.elem_bytes = elem_bytes;
   a.v = v;
   a.y = y;
   a.partial = reinterpret_cast<float*>(base + w.partial_off);
@@ -403,35 +464,26 @@ xtvxy_status xtvxy_get_device_info(int device, xtvxy_device_info* info) {
   return device_info(device, info);
 }
 
+
+
 xtvxy_status xtvxy_dense_f32_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info* dev,
                                   xtvxy_launch_params* plan) {
-  if (!plan) return XTVXY_ERROR_NULL_POINTER;
-  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
-  xtvxy_device_info d;
-  if (dev) {
-    d = *dev;
-  } else {
-    xtvxy_status st = device_info(-1, &d);
-    if (st != XTVXY_SUCCESS) return st;
-  }
-  if (d.compute_units <= 0 || d.hbm_bytes_per_s <= 0) return XTVXY_ERROR_INVALID_VALUE;
-  xtvxy_status st = model_dense(m, n, ldx, X_aligned16 != 0, d, plan);
-  if (st == XTVXY_SUCCESS && !dev) st = fit_group_grid(m, n, ldx, d, plan, false);
-  return st;
+  return dense_plan_query(m, n, ldx, X_aligned16, dev, plan, 4);
 }
 
 xtvxy_status xtvxy_dense_f32_plan_complete(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info* dev,
                                            xtvxy_launch_params* plan) {
-  if (!plan) return XTVXY_ERROR_NULL_POINTER;
-  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
-  xtvxy_device_info d;
-  if (dev) {
-    d = *dev;
-  } else {
-    xtvxy_status st = device_info(-1, &d);
-    if (st != XTVXY_SUCCESS) return st;
-  }
-  return complete_dense(m, n, ldx, d, plan);
+  return dense_complete_query(m, n, ldx, dev, plan, 4);
+}
+
+xtvxy_status xtvxy_dense_bf16_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info* dev,
+                                   xtvxy_launch_params* plan) {
+  return dense_plan_query(m, n, ldx, X_aligned16, dev, plan, 2);
+}
+
+xtvxy_status xtvxy_dense_bf16_plan_complete(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info* dev,
+                                            xtvxy_launch_params* plan) {
+  return dense_complete_query(m, n, ldx, dev, plan, 2);
 }
 
 xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info* dev,
@@ -464,20 +516,13 @@ xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz, cons
   return complete_csr(m, n, nnz, d, plan);
 }
 
+
 xtvxy_status xtvxy_dense_f32_workspace_size(int64_t m, int64_t n, int64_t ldx, size_t* bytes) {
-  if (!bytes) return XTVXY_ERROR_NULL_POINTER;
-  if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
-  *bytes = 0;
-  if (m == 0 || n == 0) return XTVXY_SUCCESS;
-  size_t best = 0;
-  for (int aligned = 0; aligned < 2; ++aligned) {
-    xtvxy_launch_params p;
-    xtvxy_status st = xtvxy_dense_f32_plan(m, n, ldx, aligned, nullptr, &p);
-    if (st != XTVXY_SUCCESS) return st;
-    if ((size_t)p.workspace_bytes > best) best = (size_t)p.workspace_bytes;
-  }
-  *bytes = best;
-  return XTVXY_SUCCESS;
+  return dense_workspace_query(m, n, ldx, bytes, 4);
+}
+
+xtvxy_status xtvxy_dense_bf16_workspace_size(int64_t m, int64_t n, int64_t ldx, size_t* bytes) {
+  return dense_workspace_query(m, n, ldx, bytes, 2);
 }
 
 xtvxy_status xtvxy_csr_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t* bytes) {
@@ -502,6 +547,18 @@ xtvxy_status xtvxy_dense_f32_ex(int64_t m, int64_t n, float alpha, const float* 
                                 const float* y, float beta, const float* z, float* out, void* workspace,
                                 size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
   return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force);
+}
+
+xtvxy_status xtvxy_dense_bf16(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx, const float* v,
+                              const float* y, float beta, const float* z, float* out, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, nullptr, 2);
+}
+
+xtvxy_status xtvxy_dense_bf16_ex(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx, const float* v,
+                                 const float* y, float beta, const float* z, float* out, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force, 2);
 }
 
 xtvxy_status xtvxy_csr_f32(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
@@ -561,9 +618,10 @@ xtvxy_status xtvxy_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* r
 
 // Shared with unfused.cpp: the dense argument checks.
 namespace xtvxy {
-xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
-                              const float* y, float beta, const float* z, const float* out, bool* quick) {
-  return check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, quick);
+xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
+                              const float* y, float beta, const float* z, const float* out, bool* quick,
+                              int elem_bytes) {
+  return check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, quick, elem_bytes);
 }
 xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* values, const float* v, const float* y,

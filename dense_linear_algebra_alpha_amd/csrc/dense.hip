@@ -24,9 +24,16 @@
 //              expects. Cooperative launch guarantees that the members are
 //              resident together; a bounded wait flags an error instead of hanging.
 //
+// X is fp32, or bf16 (reduced-precision storage: each element widened to fp32 as it is
+// loaded, all arithmetic fp32). A chunk is VEC consecutive elements read by one load: 4 fp32 or
+// 8 bf16 per 16-byte load, or 1 element when X is not aligned for that.
+//
 // Every loop runs the same number of iterations in all lanes of a workgroup
 // (rows past the end are masked to zero), so cross-lane exchanges never execute
 // under divergent control flow.
+#include <map>
+#include <mutex>
+
 #include "device_util.h"
 #include "internal.h"
 
@@ -35,7 +42,7 @@ namespace {
 
 constexpr uint32_t kSpinLimit = 1u << 24;  // a barrier wait gives up (and flags an error) after this
 
-template <int VEC, int NCH, int UNR>
+template <class E, int VEC, int NCH, int UNR>
 __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
   constexpr int W = 64 * VEC * NCH;  // widest row a wavefront covers
   __shared__ float red[kWaves][W];
@@ -66,14 +73,14 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
 
   // Row u of a batch for this lane's group: r0 + batch_start + u * units + unit.
   auto process = [&](int64_t start, bool check) {
-    float xv[UNR][NCH][VEC];
+    XChunk<E, VEC> xv[UNR][NCH];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
       const int64_t row = start + (int64_t)u * units + unit;
       const bool rok = !check || row < r1;
-      const float* xr = a.X + (rok ? row : r0) * a.ldx;
+      const E* xr = static_cast<const E*>(a.X) + (rok ? row : r0) * a.ldx;
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) load_chunk<VEC>(xr, ((int64_t)c * lpr + sub) * VEC, cok[c] && rok, xv[u][c]);
+      for (int c = 0; c < NCH; ++c) load_x<E, VEC>(xr, ((int64_t)c * lpr + sub) * VEC, cok[c] && rok, xv[u][c]);
     }
     float s[UNR];
 #pragma unroll
@@ -82,7 +89,7 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) s[u] = fmaf(xv[u][c][k], yv[c][k], s[u]);
+        for (int k = 0; k < VEC; ++k) s[u] = fmaf(xv[u][c].get(k), yv[c][k], s[u]);
     }
     if constexpr (UNR == 8) {
       if (lpr == 64) {
@@ -98,7 +105,7 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
 #pragma unroll
           for (int c = 0; c < NCH; ++c)
 #pragma unroll
-            for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu_b, xv[u][c][k], acc[c][k]);
+            for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu_b, xv[u][c].get(k), acc[c][k]);
         }
         return;
       }
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[u][c][k], acc[c][k]);
+        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[u][c].get(k), acc[c][k]);
     }
   };
 
@@ -148,7 +155,7 @@ __device__ __forceinline__ uint64_t pack_slot(float v, uint32_t tag) {
   return ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
 }
 
-template <int VEC, int NCH, bool GROUP>
+template <class E, int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   constexpr int R = kBlockRowsInFlight;
   constexpr int kMaxGroup = kBlock / R;
@@ -180,15 +187,15 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   int parity = 0;
   uint32_t step = 0;
   for (int64_t base = r0; base < r1; base += R) {
-    float xv[R][NCH][VEC];
+    XChunk<E, VEC> xv[R][NCH];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r;
       const bool rok = row < r1;
-      const float* xr = a.X + (rok ? row : r0) * a.ldx;
+      const E* xr = static_cast<const E*>(a.X) + (rok ? row : r0) * a.ldx;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        load_chunk<VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, xv[r][c]);
+        load_x<E, VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, xv[r][c]);
     }
     float s[R];
 #pragma unroll
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) s[r] = fmaf(xv[r][c][k], yv[c][k], s[r]);
+        for (int k = 0; k < VEC; ++k) s[r] = fmaf(xv[r][c].get(k), yv[c][k], s[r]);
       s[r] = group_sum(s[r], 64);
     }
     if (lane == 0) {
@@ -257,7 +264,7 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[r][c][k], acc[c][k]);
+        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[r][c].get(k), acc[c][k]);
     }
     parity ^= 1;
   }
@@ -272,38 +279,70 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
     }
 }
 
-template <int VEC>
+template <class E, int VEC>
 hipError_t launch_wave(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const dim3 grid((unsigned)p.grid), block(kBlock);
   switch (p.chunks) {
-    case 1: hipLaunchKernelGGL((dense_wave_rows<VEC, 1, 8>), grid, block, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((dense_wave_rows<VEC, 2, 4>), grid, block, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((dense_wave_rows<VEC, 4, 2>), grid, block, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((dense_wave_rows<E, VEC, 1, 8>), grid, block, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((dense_wave_rows<E, VEC, 2, 4>), grid, block, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((dense_wave_rows<E, VEC, 4, 2>), grid, block, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int VEC, int NCH>
-const void* block_kernel(bool group) {
-  return group ? reinterpret_cast<const void*>(&dense_block_rows<VEC, NCH, true>)
-               : reinterpret_cast<const void*>(&dense_block_rows<VEC, NCH, false>);
+// The wave-row kernel for an element size, chunk width and chunk count (nullptr: none).
+const void* wave_kernel_for(int elem_bytes, int vec, int chunks) {
+#define XTVXY_WAVE(E, V)                                                                       \
+  switch (chunks) {                                                                          \
+    case 1: return reinterpret_cast<const void*>(&dense_wave_rows<E, V, 1, 8>);              \
+    case 2: return reinterpret_cast<const void*>(&dense_wave_rows<E, V, 2, 4>);              \
+    case 4: return reinterpret_cast<const void*>(&dense_wave_rows<E, V, 4, 2>);              \
+  }                                                                                          \
+  return nullptr;
+  if (elem_bytes == 4 && vec == 4) { XTVXY_WAVE(float, 4) }
+  if (elem_bytes == 4 && vec == 1) { XTVXY_WAVE(float, 1) }
+  if (elem_bytes == 2 && vec == 8) { XTVXY_WAVE(bf16_t, 8) }
+  if (elem_bytes == 2 && vec == 1) { XTVXY_WAVE(bf16_t, 1) }
+#undef XTVXY_WAVE
+  return nullptr;
 }
 
-const void* block_kernel_for(int vec, int chunks, bool group) {
-  if (vec == 4) {
+template <class E, int VEC, int NCH>
+const void* block_kernel(bool group) {
+  return group ? reinterpret_cast<const void*>(&dense_block_rows<E, VEC, NCH, true>)
+               : reinterpret_cast<const void*>(&dense_block_rows<E, VEC, NCH, false>);
+}
+
+// The block/group-row kernel for an element size, chunk width and chunk count (nullptr: none).
+// bf16 chunks of 8 stop at 4 chunks per thread, the same registers as 8 fp32 chunks of 4.
+const void* block_kernel_for(int elem_bytes, int vec, int chunks, bool group) {
+  if (elem_bytes == 4 && vec == 4) {
     switch (chunks) {
-      case 1: return block_kernel<4, 1>(group);
-      case 2: return block_kernel<4, 2>(group);
-      case 4: return block_kernel<4, 4>(group);
-      case 8: return block_kernel<4, 8>(group);
+      case 1: return block_kernel<float, 4, 1>(group);
+      case 2: return block_kernel<float, 4, 2>(group);
+      case 4: return block_kernel<float, 4, 4>(group);
+      case 8: return block_kernel<float, 4, 8>(group);
     }
-  } else if (vec == 1) {
+  } else if (elem_bytes == 4 && vec == 1) {
     switch (chunks) {
-      case 1: return block_kernel<1, 1>(group);
-      case 2: return block_kernel<1, 2>(group);
-      case 4: return block_kernel<1, 4>(group);
-      case 8: return block_kernel<1, 8>(group);
+      case 1: return block_kernel<float, 1, 1>(group);
+      case 2: return block_kernel<float, 1, 2>(group);
+      case 4: return block_kernel<float, 1, 4>(group);
+      case 8: return block_kernel<float, 1, 8>(group);
+    }
+  } else if (elem_bytes == 2 && vec == 8) {
+    switch (chunks) {
+      case 1: return block_kernel<bf16_t, 8, 1>(group);
+      case 2: return block_kernel<bf16_t, 8, 2>(group);
+      case 4: return block_kernel<bf16_t, 8, 4>(group);
+    }
+  } else if (elem_bytes == 2 && vec == 1) {
+    switch (chunks) {
+      case 1: return block_kernel<bf16_t, 1, 1>(group);
+      case 2: return block_kernel<bf16_t, 1, 2>(group);
+      case 4: return block_kernel<bf16_t, 1, 4>(group);
+      case 8: return block_kernel<bf16_t, 1, 8>(group);
     }
   }
   return nullptr;
@@ -311,25 +350,60 @@ const void* block_kernel_for(int vec, int chunks, bool group) {
 
 }  // namespace
 
-int64_t dense_group_max_resident(const xtvxy_launch_params& p) {
-  const void* k = block_kernel_for(p.vec, p.chunks, true);
-  if (!k) return 0;
-  int per_cu = 0, dev = 0;
+namespace {
+
+// Workgroups of kernel k resident per CU, and the device's CU count, cached per (device, kernel):
+// the plan queries run on every fused call.
+std::mutex g_occ_mutex;
+std::map<std::pair<int, const void*>, int> g_occ;
+
+int resident_per_cu(const void* k, int* cus) {
+  int dev = 0;
+  if (!k || hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(g_occ_mutex);
+  auto it = g_occ.find({dev, k});
+  auto cu_it = g_occ.find({dev, nullptr});
+  if (it != g_occ.end() && cu_it != g_occ.end()) {
+    if (cus) *cus = cu_it->second;
+    return it->second;
+  }
+  int per_cu = 0;
   hipDeviceProp_t prop;
-  if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, 0) != hipSuccess) return 0;
-  return (int64_t)per_cu * prop.multiProcessorCount;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, kBlock, 0) != hipSuccess ||
+      hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return 0;
+  g_occ[{dev, k}] = per_cu;
+  g_occ[{dev, nullptr}] = prop.multiProcessorCount;
+  if (cus) *cus = prop.multiProcessorCount;
+  return per_cu;
+}
+
+}  // namespace
+
+int dense_resident_per_cu(const xtvxy_launch_params& p, int elem_bytes) {
+  const void* k = p.kernel == XTVXY_DENSE_WAVE_ROWS ? wave_kernel_for(elem_bytes, p.vec, p.chunks)
+                                                    : block_kernel_for(elem_bytes, p.vec, p.chunks,
+                                                                       p.kernel == XTVXY_DENSE_GROUP_ROWS);
+  return resident_per_cu(k, nullptr);
+}
+
+int64_t dense_group_max_resident(const xtvxy_launch_params& p, int elem_bytes) {
+  int cus = 0;
+  const int per_cu = resident_per_cu(block_kernel_for(elem_bytes, p.vec, p.chunks, true), &cus);
+  return (int64_t)per_cu * cus;
 }
 
 hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if (p.block_threads != kBlock || p.grid <= 0 || p.grid > INT32_MAX) return hipErrorInvalidValue;
   switch (p.kernel) {
     case XTVXY_DENSE_WAVE_ROWS:
-      if (p.vec == 4) return launch_wave<4>(a, p, s);
-      if (p.vec == 1) return launch_wave<1>(a, p, s);
+      if (a.elem_bytes == 4 && p.vec == 4) return launch_wave<float, 4>(a, p, s);
+      if (a.elem_bytes == 4 && p.vec == 1) return launch_wave<float, 1>(a, p, s);
+      if (a.elem_bytes == 2 && p.vec == 8) return launch_wave<bf16_t, 8>(a, p, s);
+      if (a.elem_bytes == 2 && p.vec == 1) return launch_wave<bf16_t, 1>(a, p, s);
       return hipErrorInvalidValue;
     case XTVXY_DENSE_BLOCK_ROWS: {
-      const void* k = block_kernel_for(p.vec, p.chunks, false);
+      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, false);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;
       void* params[] = {&args};
@@ -337,7 +411,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
     }
     case XTVXY_DENSE_GROUP_ROWS: {
       if (p.group < 1 || p.group > kBlock / kBlockRowsInFlight) return hipErrorInvalidValue;
-      const void* k = block_kernel_for(p.vec, p.chunks, true);
+      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, true);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;
       void* params[] = {&args};

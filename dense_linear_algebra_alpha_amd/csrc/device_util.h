@@ -184,4 +184,54 @@ __device__ __forceinline__ void load_chunk(const float* __restrict__ xr, int64_t
   }
 }
 
+// bf16 storage of X: an element is the upper 16 bits of an fp32 bit pattern.
+typedef uint16_t bf16_t;
+typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(unsigned int w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned int w) { return __uint_as_float(w & 0xffff0000u); }
+
+// A chunk of VEC consecutive elements of a row of X as it sits in registers: fp32 values, or
+// bf16 kept packed two to a 32-bit word (half the registers of the widened values, so twice the
+// rows fit in flight) and widened at each use by one shift or mask. get(k) is element k as fp32.
+template <class E, int VEC>
+struct XChunk {
+  float v[VEC];
+  __device__ __forceinline__ float get(int k) const { return v[k]; }
+};
+template <>
+struct XChunk<bf16_t, 8> {
+  unsigned int w[4];
+  __device__ __forceinline__ float get(int k) const { return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]); }
+};
+template <>
+struct XChunk<bf16_t, 1> {
+  unsigned int w;
+  __device__ __forceinline__ float get(int) const { return bf16_lo(w); }
+};
+
+// Chunk of row `xr` from column `col` when `ok`, else zeros. fp32 rows take load_chunk; bf16 rows
+// take one 16-byte load of 8 elements (VEC == 8: the caller guarantees 16-byte alignment and
+// n % 8 == 0) or one 2-byte load (VEC == 1). Clamped address, unconditional non-temporal load,
+// as in load_chunk.
+template <class E, int VEC>
+__device__ __forceinline__ void load_x(const E* __restrict__ xr, int64_t col, bool ok, XChunk<E, VEC>& o) {
+  if constexpr (sizeof(E) == 4) {
+    load_chunk<VEC>(reinterpret_cast<const float*>(xr), col, ok, o.v);
+  } else {
+    const int64_t c = ok ? col : 0;
+    if constexpr (VEC == 8) {
+      const u4 t = __builtin_nontemporal_load(reinterpret_cast<const u4*>(xr + c));
+      o.w[0] = ok ? t.x : 0u;
+      o.w[1] = ok ? t.y : 0u;
+      o.w[2] = ok ? t.z : 0u;
+      o.w[3] = ok ? t.w : 0u;
+    } else {
+      static_assert(VEC == 1, "bf16 rows load 8 or 1 elements");
+      const unsigned int h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(xr + c));
+      o.w = ok ? h : 0u;
+    }
+  }
+}
+
 }  // namespace xtvxy

@@ -34,7 +34,8 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 // Arguments of the dense fused kernels.
 struct DenseArgs {
   int64_t m, n, ldx;
-  const float* X;
+  const void* X;      // fp32 or bf16 elements (elem_bytes 4 or 2)
+  int32_t elem_bytes;
   const float* v;     // nullptr: v = 1
   const float* y;
   float* partial;     // [rows of partials][n] fp32
@@ -122,13 +123,15 @@ hipError_t launch_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t* ro
                             const int32_t* col_idx, int32_t* flag, hipStream_t s);
 
 // Largest co-resident grid of the dense group-row kernel for a plan (0 on error).
-int64_t dense_group_max_resident(const xtvxy_launch_params& p);
+int64_t dense_group_max_resident(const xtvxy_launch_params& p, int elem_bytes = 4);
+// Workgroups of a dense plan's kernel that fit on one CU at once (registers, LDS); 0 if unknown.
+int dense_resident_per_cu(const xtvxy_launch_params& p, int elem_bytes = 4);
 
 // Analytical launch model (model.cpp).
 xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, const xtvxy_device_info& d,
-                         xtvxy_launch_params* p);
+                         xtvxy_launch_params* p, int elem_bytes = 4, int max_wg_per_cu = 0);
 xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
-                            xtvxy_launch_params* p);
+                            xtvxy_launch_params* p, int elem_bytes = 4);
 xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                        xtvxy_launch_params* p);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
@@ -136,8 +139,8 @@ xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
 
 // Argument checks shared by the fused entry points and the comparator (api.cpp). On
 // success *quick tells that only out = beta z (or nothing, when n == 0) remains to do.
-xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
-                              const float* y, float beta, const float* z, const float* out, bool* quick);
+xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
+                              const float* y, float beta, const float* z, const float* out, bool* quick, int elem_bytes = 4);
 xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
                             float beta, const float* z, const float* out, bool* quick);

@@ -17,10 +17,13 @@
 // The row layout itself is fixed by n (the smallest layout that covers a row),
 // so the model chooses the number of workgroups per CU, hence the grid and the
 // coarsening factor rows_per_unit = ceil(m / units). More workgroups hide
-// more latency but write more partial n-vectors; the model trades the two.
+// more latency but write more partial n-vectors; the model trades the two, and
+// never asks for more workgroups per CU than the chosen kernel can keep resident
+// (a grid beyond that runs as a second, thinly populated round).
 // The constants are calibrated on MI355X: a plain streaming read sustains
-// about 0.88 of the 8 TB/s peak, and the fused kernels reach it once about
-// 128 KiB of loads are in flight per CU, i.e. about 4.5 us of latency under load.
+// about 0.88 of the 8 TB/s peak; the CSR and group-row kernels reach it once
+// about 128 KiB of loads are in flight per CU (about 4.5 us of latency under
+// load), the dense wave- and block-row kernels with about 2 us worth.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -32,6 +35,10 @@ namespace {
 
 constexpr double kSustained = 0.88;     // sustained fraction of peak HBM bandwidth (streaming read)
 constexpr double kLatency = 4.5e-6;     // seconds of loaded-memory latency that loads in flight must cover
+// The dense wave- and block-row kernels need no barrier between their rows' loads and reach the
+// sustained rate with about 2 us worth of loads in flight (one 32 KiB workgroup per CU streams
+// ~6.7 TB/s); the group-row kernels wait for the other members every two rows and keep kLatency.
+constexpr double kLatencyDenseRows = 2.0e-6;
 constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
 constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
@@ -45,8 +52,8 @@ int next_pow2(int64_t x) {
   return p;
 }
 
-double bandwidth(const xtvxy_device_info& d, double inflight_per_cu) {
-  const double bw_latency = d.compute_units * inflight_per_cu / kLatency;
+double bandwidth(const xtvxy_device_info& d, double inflight_per_cu, double latency = kLatency) {
+  const double bw_latency = d.compute_units * inflight_per_cu / latency;
   return std::min(kSustained * d.hbm_bytes_per_s, bw_latency);
 }
 
@@ -120,11 +127,13 @@ CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch
 }
 
 xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
-                            xtvxy_launch_params* p) {
+                            xtvxy_launch_params* p, int elem_bytes) {
   (void)ldx;
-  if (p->block_threads != kBlock || (p->vec != 1 && p->vec != 4) || p->grid <= 0 || p->grid > INT32_MAX)
+  if (elem_bytes != 4 && elem_bytes != 2) return XTVXY_ERROR_INVALID_VALUE;
+  const int wide = 16 / elem_bytes;  // elements per 16-byte load: 4 fp32 or 8 bf16
+  if (p->block_threads != kBlock || (p->vec != 1 && p->vec != wide) || p->grid <= 0 || p->grid > INT32_MAX)
     return XTVXY_ERROR_INVALID_VALUE;
-  if (p->vec == 4 && n % 4 != 0) return XTVXY_ERROR_INVALID_VALUE;  // 16-byte chunks never straddle the row end
+  if (p->vec == wide && n % wide != 0) return XTVXY_ERROR_INVALID_VALUE;  // chunks never straddle the row end
   switch (p->kernel) {
     case XTVXY_DENSE_WAVE_ROWS: {
       const int lpr = p->lanes_per_row;
@@ -137,6 +146,7 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
     case XTVXY_DENSE_BLOCK_ROWS:
     case XTVXY_DENSE_GROUP_ROWS: {
       if (p->chunks != 1 && p->chunks != 2 && p->chunks != 4 && p->chunks != 8) return XTVXY_ERROR_INVALID_VALUE;
+      if (elem_bytes == 2 && p->vec == 8 && p->chunks == 8) return XTVXY_ERROR_INVALID_VALUE;  // registers
       const int64_t slice = (int64_t)kBlock * p->vec * p->chunks;
       if (p->kernel == XTVXY_DENSE_BLOCK_ROWS) {
         p->group = 1;
@@ -161,11 +171,14 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
 }
 
 xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, const xtvxy_device_info& d,
-                         xtvxy_launch_params* p) {
+                         xtvxy_launch_params* p, int elem_bytes, int max_wg_per_cu) {
   std::memset(p, 0, sizeof(*p));
+  if (elem_bytes != 4 && elem_bytes != 2) return XTVXY_ERROR_INVALID_VALUE;
   p->block_threads = kBlock;
-  p->vec = (aligned16 && ldx % 4 == 0 && n % 4 == 0) ? 4 : 1;
+  const int wide = 16 / elem_bytes;  // elements per 16-byte load
+  p->vec = (aligned16 && ldx % wide == 0 && n % wide == 0) ? wide : 1;
   const int vec = p->vec;
+  const int max_chunks = (elem_bytes == 2 && vec == 8) ? 4 : 8;  // block/group rows
   double inflight_per_wg;  // bytes of X a workgroup has requested before it needs the first of them
   int64_t rows_per_step;   // rows a workgroup (or group) consumes per step
   if (n <= 64 * vec * 4) {
@@ -174,28 +187,30 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
     p->lanes_per_row = next_pow2(std::max<int64_t>(1, ceil_div(n, (int64_t)vec * p->chunks)));
     p->group = 1;
     rows_per_step = (int64_t)kWaves * (64 / p->lanes_per_row) * wave_unroll(p->chunks);
-    inflight_per_wg = (double)rows_per_step * n * sizeof(float);
-  } else if (n <= (int64_t)kBlock * vec * 8) {
+    inflight_per_wg = (double)rows_per_step * n * elem_bytes;
+  } else if (n <= (int64_t)kBlock * vec * max_chunks) {
     p->kernel = XTVXY_DENSE_BLOCK_ROWS;
     const int64_t per = (int64_t)kBlock * vec;
     p->chunks = (n <= per) ? 1 : (n <= 2 * per) ? 2 : (n <= 4 * per) ? 4 : 8;
     p->group = 1;
     p->lanes_per_row = kBlock;
     rows_per_step = kBlockRowsInFlight;
-    inflight_per_wg = (double)kBlockRowsInFlight * n * sizeof(float);
+    inflight_per_wg = (double)kBlockRowsInFlight * n * elem_bytes;
   } else {
     p->kernel = XTVXY_DENSE_GROUP_ROWS;
     const int64_t per = (int64_t)kBlock * vec;
-    p->group = (int32_t)ceil_div(n, per * 8);
+    p->group = (int32_t)ceil_div(n, per * max_chunks);
     const int64_t slice = ceil_div(n, p->group);
     p->chunks = (slice <= per) ? 1 : (slice <= 2 * per) ? 2 : (slice <= 4 * per) ? 4 : 8;
     p->lanes_per_row = kBlock;
     rows_per_step = kBlockRowsInFlight;
-    inflight_per_wg = (double)kBlockRowsInFlight * slice * sizeof(float);
+    inflight_per_wg = (double)kBlockRowsInFlight * slice * elem_bytes;
   }
 
-  const double io_bytes = 4.0 * ((double)m * n + m + 3.0 * n);
-  const int max_per_cu = (p->kernel == XTVXY_DENSE_GROUP_ROWS) ? 2 : kMaxWgPerCu;
+  const double io_bytes = (double)elem_bytes * m * n + 4.0 * ((double)m + 3.0 * n);
+  // workgroups per CU: at most what the kernel's registers and LDS let reside at once, when known
+  int max_per_cu = (p->kernel == XTVXY_DENSE_GROUP_ROWS) ? 2 : kMaxWgPerCu;
+  if (max_wg_per_cu > 0) max_per_cu = std::min(max_per_cu, max_wg_per_cu);
   double best = 1e300;
   int64_t best_grid = 1;
   for (int k = 1; k <= max_per_cu; k *= 2) {
@@ -209,7 +224,8 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
       grid = std::min<int64_t>(grid, units_needed);
     }
     const double resident_per_cu = std::min<double>(k, (double)grid / d.compute_units);
-    const double bw = bandwidth(d, std::max(resident_per_cu, 1.0 / d.compute_units) * inflight_per_wg);
+    const double latency = p->kernel == XTVXY_DENSE_GROUP_ROWS ? kLatency : kLatencyDenseRows;
+    const double bw = bandwidth(d, std::max(resident_per_cu, 1.0 / d.compute_units) * inflight_per_wg, latency);
     const double partial_bytes = 2.0 * (double)(grid / p->group) * n * sizeof(float);
     const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + 2 * kLaunch;
     if (t < best * 0.999) {
@@ -220,7 +236,7 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
   p->grid = best_grid;
   p->rows_per_unit = 0;
   p->predicted_seconds = best;
-  return complete_dense(m, n, ldx, d, p);
+  return complete_dense(m, n, ldx, d, p, elem_bytes);
 }
 
 int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {

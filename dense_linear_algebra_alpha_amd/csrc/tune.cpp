@@ -34,7 +34,7 @@ constexpr int kFinalists = 4;  // re-timed together with the model's plan
 
 struct Key {
   std::string device;
-  int32_t kind;  // 0 dense, 1 csr
+  int32_t kind;  // 0 dense fp32, 1 csr, 2 dense bf16
   int64_t m, n, k;  // k: ldx (dense) or nnz (csr)
   int32_t aligned;
   bool operator<(const Key& o) const {
@@ -73,13 +73,13 @@ int next_pow2(int64_t x) {
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 std::vector<xtvxy_launch_params> dense_candidates(int64_t m, int64_t n, int64_t ldx, int vec,
-                                                  const xtvxy_device_info& d) {
+                                                  const xtvxy_device_info& d, int elem_bytes) {
   std::vector<xtvxy_launch_params> out;
   auto add = [&](xtvxy_launch_params p) {
     p.block_threads = kBlock;
     p.vec = vec;
     p.rows_per_unit = 0;
-    if (complete_dense(m, n, ldx, d, &p) == XTVXY_SUCCESS) out.push_back(p);
+    if (complete_dense(m, n, ldx, d, &p, elem_bytes) == XTVXY_SUCCESS) out.push_back(p);
   };
   const int cus = d.compute_units;
   for (int chunks : {1, 2, 4}) {  // wave rows
@@ -315,19 +315,19 @@ void ints_to_plan(const long long* v, xtvxy_launch_params* p) {
 
 extern "C" {
 
-xtvxy_status xtvxy_dense_f32_tune(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
-                                  const float* y, float beta, const float* z, float* out, int32_t repeats,
-                                  hipStream_t stream, xtvxy_tune_report* report) {
+static xtvxy_status dense_tune(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
+                               const float* y, float beta, const float* z, float* out, int32_t repeats,
+                               hipStream_t stream, xtvxy_tune_report* report, int elem_bytes) {
   if (!report) return XTVXY_ERROR_NULL_POINTER;
   if (repeats < 1 || repeats > 10000) return XTVXY_ERROR_INVALID_VALUE;
   bool quick = false;
-  xtvxy_status st = check_dense_args(m, n, alpha, X, ldx, v, y, beta, z, out, &quick);
+  xtvxy_status st = check_dense_args(m, n, alpha, X, ldx, v, y, beta, z, out, &quick, elem_bytes);
   if (st != XTVXY_SUCCESS) return st;
   if (quick) return XTVXY_ERROR_INVALID_VALUE;  // nothing to tune: the call reads no X
   const int aligned = (reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
   Key key;
   if ((st = device_key(&key.device)) != XTVXY_SUCCESS) return st;
-  key.kind = 0;
+  key.kind = elem_bytes == 2 ? 2 : 0;
   key.m = m;
   key.n = n;
   key.k = ldx;
@@ -336,20 +336,38 @@ xtvxy_status xtvxy_dense_f32_tune(int64_t m, int64_t n, float alpha, const float
   const xtvxy_device_info d = current_info(&st);
   if (st != XTVXY_SUCCESS) return st;
   xtvxy_launch_params model;
-  if ((st = xtvxy_dense_f32_plan(m, n, ldx, aligned, nullptr, &model)) != XTVXY_SUCCESS) return st;
-  std::vector<xtvxy_launch_params> cands = dense_candidates(m, n, ldx, model.vec, d);
+  st = elem_bytes == 2 ? xtvxy_dense_bf16_plan(m, n, ldx, aligned, nullptr, &model)
+                       : xtvxy_dense_f32_plan(m, n, ldx, aligned, nullptr, &model);
+  if (st != XTVXY_SUCCESS) return st;
+  std::vector<xtvxy_launch_params> cands = dense_candidates(m, n, ldx, model.vec, d, elem_bytes);
   size_t ws_bytes = (size_t)model.workspace_bytes;
   for (const auto& c : cands) ws_bytes = std::max(ws_bytes, (size_t)c.workspace_bytes);
   DeviceBuffer ws;
   if (ws_bytes > 0 && hipMalloc(&ws.p, ws_bytes) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   auto run = [&](const xtvxy_launch_params& p) {
-    return xtvxy_dense_f32_ex(m, n, alpha, X, ldx, v, y, beta, z, out, ws.p, ws_bytes, stream, &p);
+    if (elem_bytes == 2)
+      return xtvxy_dense_bf16_ex(m, n, alpha, static_cast<const uint16_t*>(X), ldx, v, y, beta, z, out, ws.p,
+                                 ws_bytes, stream, &p);
+    return xtvxy_dense_f32_ex(m, n, alpha, static_cast<const float*>(X), ldx, v, y, beta, z, out, ws.p, ws_bytes,
+                              stream, &p);
   };
   xtvxy_tune_report rep{};
   if ((st = tune(cands, model, run, repeats, stream, &rep)) != XTVXY_SUCCESS) return st;
   cache_put(key, rep);
   *report = rep;
   return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_dense_f32_tune(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx, const float* v,
+                                  const float* y, float beta, const float* z, float* out, int32_t repeats,
+                                  hipStream_t stream, xtvxy_tune_report* report) {
+  return dense_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream, report, 4);
+}
+
+xtvxy_status xtvxy_dense_bf16_tune(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx,
+                                   const float* v, const float* y, float beta, const float* z, float* out,
+                                   int32_t repeats, hipStream_t stream, xtvxy_tune_report* report) {
+  return dense_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream, report, 2);
 }
 
 xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
@@ -393,7 +411,7 @@ xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, 
 xtvxy_status xtvxy_tune_cache_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t aligned,
                                      xtvxy_tune_report* report, int32_t* found) {
   if (!report || !found) return XTVXY_ERROR_NULL_POINTER;
-  if (kind != 0 && kind != 1) return XTVXY_ERROR_INVALID_VALUE;
+  if (kind != 0 && kind != 1 && kind != 2) return XTVXY_ERROR_INVALID_VALUE;
   Key key;
   const xtvxy_status st = device_key(&key.device);
   if (st != XTVXY_SUCCESS) return st;
@@ -459,7 +477,7 @@ xtvxy_status xtvxy_tune_cache_load(const char* path) {
     }
     double best_s = 0, model_s = 0;
     if (!bad && std::sscanf(p, " %lf %lf %d", &best_s, &model_s, &cands) != 3) bad = true;
-    if (bad || (kind != 0 && kind != 1) || m < 0 || n < 0 || k < 0 || !(best_s > 0) || !(model_s > 0)) {
+    if (bad || kind < 0 || kind > 2 || m < 0 || n < 0 || k < 0 || !(best_s > 0) || !(model_s > 0)) {
       bad = true;
       break;
     }

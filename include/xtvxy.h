@@ -152,6 +152,27 @@ xtvxy_status xtvxy_dense_f32_ex(int64_t m, int64_t n, float alpha, const float *
 xtvxy_status xtvxy_dense_f32_plan_complete(int64_t m, int64_t n, int64_t ldx,
                                            const xtvxy_device_info *dev, xtvxy_launch_params *plan);
 
+/* Reduced-precision storage of dense X: the same pattern with X held as bf16 (bfloat16 bit
+ * patterns, uint16_t; an element is the upper 16 bits of an fp32 and widens to it exactly).
+ * v, y, z and out stay fp32 and every operation is fp32 as in xtvxy_dense_f32, so the result is
+ * that of xtvxy_dense_f32 on the widened matrix up to rounding order; X takes half the bytes.
+ * The pages describe the pattern in fp32 only ("On optimizing machine learning workloads via
+ * kernel fusion", abstract); bf16 storage is this library's extension. Same arguments, rules and
+ * error codes as the fp32 entry points; a plan's vec is 8 (16-byte loads of 8 elements: X 16-byte
+ * aligned, ldx % 8 == 0 and n % 8 == 0) or 1, and block/group-row plans with vec 8 take at most 4
+ * chunks. */
+xtvxy_status xtvxy_dense_bf16_workspace_size(int64_t m, int64_t n, int64_t ldx, size_t *bytes);
+xtvxy_status xtvxy_dense_bf16_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16, const xtvxy_device_info *dev,
+                                   xtvxy_launch_params *plan);
+xtvxy_status xtvxy_dense_bf16_plan_complete(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info *dev,
+                                            xtvxy_launch_params *plan);
+xtvxy_status xtvxy_dense_bf16(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx, const float *v,
+                              const float *y, float beta, const float *z, float *out, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+xtvxy_status xtvxy_dense_bf16_ex(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx, const float *v,
+                                 const float *y, float beta, const float *z, float *out, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params *force);
+
 /* Workspace bytes xtvxy_csr_f32 needs for this shape on the current device. */
 xtvxy_status xtvxy_csr_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t *bytes);
 
@@ -300,12 +321,16 @@ typedef struct xtvxy_tune_report {
 xtvxy_status xtvxy_dense_f32_tune(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx, const float *v,
                                   const float *y, float beta, const float *z, float *out, int32_t repeats,
                                   hipStream_t stream, xtvxy_tune_report *report);
+xtvxy_status xtvxy_dense_bf16_tune(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx,
+                                   const float *v, const float *y, float beta, const float *z, float *out,
+                                   int32_t repeats, hipStream_t stream, xtvxy_tune_report *report);
 xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
                                 const int32_t *col_idx, const float *values, const float *v, const float *y,
                                 float beta, const float *z, float *out, int32_t repeats, hipStream_t stream,
                                 xtvxy_tune_report *report);
-/* Cache access: kind 0 = dense (k = ldx, aligned = X % 16 == 0), 1 = CSR (k = nnz, aligned = values
- * and col_idx 16-byte aligned); *found = 0 when the shape was not tuned on the current device.
+/* Cache access: kind 0 = dense fp32 X and 2 = dense bf16 X (k = ldx, aligned = X % 16 == 0), 1 = CSR
+ * (k = nnz, aligned = values and col_idx 16-byte aligned); *found = 0 when the shape was not tuned
+ * on the current device.
  * save/load use a text file (one line per entry); load merges, and takes nothing from a file with
  * a malformed line (XTVXY_ERROR_INVALID_VALUE). Plans read from a file are checked again by the
  * _ex entry points that use them. */

@@ -22,11 +22,19 @@ def dev():
     return torch.device("cuda:0")
 
 
-def to_dev(a):
+def _as_tensor(a):
+    """numpy -> torch on the host; uint16 arrays are bf16 bit patterns and become torch.bfloat16."""
     import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    return torch.from_numpy(a)
+
+
+def to_dev(a):
     if a is None:
         return None
-    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    return _as_tensor(a).to(dev())
 
 
 def dense_oracle(p):
@@ -48,8 +56,9 @@ class DenseOnDevice:
         import torch
         self.p = p
         if X_offset:
-            buf = torch.empty(p.X.size + X_offset, dtype=torch.float32, device=dev())
-            buf[X_offset:].copy_(torch.from_numpy(p.X))
+            src = _as_tensor(p.X)  # float32, or bf16
+            buf = torch.empty(p.X.size + X_offset, dtype=src.dtype, device=dev())
+            buf[X_offset:].copy_(src)
             self.X = buf[X_offset:]
         else:
             self.X = to_dev(p.X)

@@ -282,7 +282,7 @@ def test_tune_argument_errors(lib):
     assert lib.xtvxy_csr_f32_tune(8, 8, 0, 1.0, FAKE, None, None, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5,
                                   None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # nnz = 0
     found = ctypes.c_int32()
-    assert lib.xtvxy_tune_cache_lookup(2, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) == \
+    assert lib.xtvxy_tune_cache_lookup(3, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) == \
         _abi.XTVXY_ERROR_INVALID_VALUE
 
 
@@ -308,3 +308,35 @@ def test_tune_cache_file_round_trip(lib, tmp_path):
     xt.xtvxy_tune_cache_clear()
     xt.xtvxy_tune_cache_save(str(out))
     assert [l for l in out.read_text().splitlines() if not l.startswith("#")] == []
+
+
+def test_bf16_plans_and_checks(lib):
+    # model plans for bf16 X: 16-byte loads of 8 elements when aligned; the layout thresholds double
+    p = xt.xtvxy_dense_bf16_plan(1000, 256, 256, 1, MI355X)
+    assert (p.kernel, p.vec, p.lanes_per_row, p.chunks) == (xt.XTVXY_DENSE_WAVE_ROWS, 8, 32, 1)
+    p = xt.xtvxy_dense_bf16_plan(1000, 2048, 2048, 1, MI355X)
+    assert (p.kernel, p.vec, p.chunks) == (xt.XTVXY_DENSE_WAVE_ROWS, 8, 4)
+    p = xt.xtvxy_dense_bf16_plan(1000, 8192, 8192, 1, MI355X)
+    assert (p.kernel, p.vec, p.chunks) == (xt.XTVXY_DENSE_BLOCK_ROWS, 8, 4)
+    p = xt.xtvxy_dense_bf16_plan(1000, 65536, 65536, 1, MI355X)
+    assert (p.kernel, p.vec, p.group, p.chunks) == (xt.XTVXY_DENSE_GROUP_ROWS, 8, 8, 4)
+    assert xt.xtvxy_dense_bf16_plan(1000, 256, 260, 1, MI355X).vec == 1   # ldx % 8 != 0
+    assert xt.xtvxy_dense_bf16_plan(1000, 256, 256, 0, MI355X).vec == 1   # X not 16-byte aligned
+    # the fp32 model keeps 4-element loads; the bf16 one predicts half the X time
+    f = xt.xtvxy_dense_f32_plan(1_000_000, 256, 256, 1, MI355X)
+    h = xt.xtvxy_dense_bf16_plan(1_000_000, 256, 256, 1, MI355X)
+    assert f.vec == 4 and h.predicted_seconds < 0.6 * f.predicted_seconds
+    # forced plans: vec 4 is not a bf16 width, vec 8 needs n % 8 == 0, and 8 chunks of 8 are refused
+    bad = [dict(kernel=xt.XTVXY_DENSE_WAVE_ROWS, vec=4, chunks=1, lanes_per_row=64, grid=8, group=1),
+           dict(kernel=xt.XTVXY_DENSE_BLOCK_ROWS, vec=8, chunks=8, grid=8, group=1)]
+    for d in bad:
+        with pytest.raises(xt.XtvxyError):
+            xt.xtvxy_dense_bf16_plan_complete(100, 256, 256, xt.xtvxy_launch_params(block_threads=256, **d), MI355X)
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_dense_bf16_plan_complete(100, 260, 260, xt.xtvxy_launch_params(
+            block_threads=256, kernel=xt.XTVXY_DENSE_BLOCK_ROWS, vec=8, chunks=1, grid=8, group=1), MI355X)
+    # the aliasing check measures X in 2-byte elements: out just past X's last byte is fine
+    st = lib.xtvxy_dense_bf16(8, 8, 1.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 126, None, 0, None)
+    assert st == _abi.XTVXY_ERROR_ALIASING      # X spans 128 bytes: out at +126 overlaps
+    st = lib.xtvxy_dense_bf16(8, 0, 1.0, FAKE, 1, None, FAKE + 4096, 0.0, None, FAKE + 128, None, 0, None)
+    assert st == _abi.XTVXY_SUCCESS              # n == 0

@@ -45,3 +45,9 @@ def test_newton_iteration_bytes():
     assert bench.logreg_iteration_bytes(m, n, nnz, 0, 0) == 24 * m + (rows + 4 * m + 12 * n) + (rows + 4 * n + 4 * m)
     assert bench.logreg_iteration_bytes(m, n, nnz, 3, 2) - bench.logreg_iteration_bytes(m, n, nnz, 0, 0) == \
         3 * (rows + 4 * m + 12 * n) + 2 * 12 * m
+
+
+def test_algorithmic_bytes_of_bf16_storage():
+    import datagen
+    d = datagen.dense_problem(10, 8, seed=1, x_dtype="bf16")
+    assert bench.algorithmic_bytes(d) == 2 * 10 * 8 + 4 * 10 + 4 * 8 + 4 * 8 + 4 * 8  # X in 2 bytes per element
