@@ -184,10 +184,8 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   }
   uint64_t* slots = GROUP ? reinterpret_cast<uint64_t*>(a.xchg) + unit * 2 * gsz * R : nullptr;
 
-  int parity = 0;
-  uint32_t step = 0;
-  for (int64_t base = r0; base < r1; base += R) {
-    XChunk<E, VEC> xv[R][NCH];
+  // Rows base .. base+R-1 into x (rows past r1 masked to zero, address clamped to row r0).
+  auto load_rows = [&](int64_t base, XChunk<E, VEC> (&x)[R][NCH]) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r;
@@ -195,7 +193,36 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
       const E* xr = static_cast<const E*>(a.X) + (rok ? row : r0) * a.ldx;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
-        load_x<E, VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, xv[r][c]);
+        load_x<E, VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, x[r][c]);
+    }
+  };
+  // Block rows: when a second set of the step's rows fits in 32 more registers, the next step's
+  // rows are requested as soon as this step's dots are formed, so their latency overlaps the
+  // barrier and the accumulation instead of adding to them. Group rows do not prefetch: the
+  // lanes that wait for the other members' dots would first wait for their own prefetch (the
+  // vector-memory counter completes in order), and the second set costs a wave per SIMD
+  // (measured slower on 8192 x 65536).
+  constexpr int kWordsPerChunk = (VEC * (int)sizeof(E) + 3) / 4;
+  constexpr bool kPrefetch = !GROUP && R * NCH * kWordsPerChunk <= 32;
+  XChunk<E, VEC> xv[R][NCH];
+  XChunk<E, VEC> xn[kPrefetch ? R : 1][kPrefetch ? NCH : 1];
+  if constexpr (kPrefetch) {
+    if (r0 < r1) load_rows(r0, xv);
+  }
+
+  int parity = 0;
+  uint32_t step = 0;
+  for (int64_t base = r0; base < r1; base += R) {
+    if constexpr (!kPrefetch) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int64_t row = base + r;
+        const bool rok = row < r1;
+        const E* xr = static_cast<const E*>(a.X) + (rok ? row : r0) * a.ldx;
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+          load_x<E, VEC>(xr, c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC, cok[c] && rok, xv[r][c]);
+      }
     }
     float s[R];
 #pragma unroll
@@ -206,6 +233,9 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
         for (int k = 0; k < VEC; ++k) s[r] = fmaf(xv[r][c].get(k), yv[c][k], s[r]);
       s[r] = group_sum(s[r], 64);
+    }
+    if constexpr (kPrefetch) {
+      if (base + R < r1) load_rows(base + R, xn);  // uniform across the workgroup
     }
     if (lane == 0) {
 #pragma unroll
@@ -265,6 +295,12 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[r][c].get(k), acc[c][k]);
+    }
+    if constexpr (kPrefetch) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) xv[r][c] = xn[r][c];
     }
     parity ^= 1;
   }
