@@ -157,7 +157,7 @@ __device__ __forceinline__ uint64_t pack_slot(float v, uint32_t tag) {
 
 template <class E, int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
-  constexpr int R = kBlockRowsInFlight;
+  constexpr int R = GROUP ? group_rows_per_step(NCH) : kBlockRowsInFlight;
   constexpr int kMaxGroup = kBlock / R;
   __shared__ float red[2][R][kWaves];
   __shared__ float gx[GROUP ? R : 1][GROUP ? kMaxGroup : 1];
@@ -446,7 +446,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
       return hipLaunchKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
     }
     case XTVXY_DENSE_GROUP_ROWS: {
-      if (p.group < 1 || p.group > kBlock / kBlockRowsInFlight) return hipErrorInvalidValue;
+      if (p.group < 1 || p.group > kBlock / group_rows_per_step(p.chunks)) return hipErrorInvalidValue;
       const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, true);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;

@@ -14,7 +14,11 @@ namespace xtvxy {
 
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
-constexpr int kBlockRowsInFlight = 2;  // rows a block-row / group-row workgroup loads per step
+constexpr int kBlockRowsInFlight = 2;  // rows a block-row workgroup loads per step
+// Rows a group-row workgroup loads per step: 16 / chunks, so that a step always holds 16 chunks
+// per thread (the registers of 2 rows of 8 chunks) and fewer chunks per thread (wider groups)
+// buy more rows per exchange of partial dots between the members.
+constexpr int group_rows_per_step(int chunks) { return chunks >= 1 && chunks <= 16 ? 16 / chunks : 1; }
 // CSR kernel: LDS besides the output and y windows, for workgroups of `blk` threads holding
 // `ept` entries each: row_ptr, v and dots of two tiles, a sink word per thread and small
 // scalars (29 blk + 64 bytes), plus two tiles of 16-bit row-start marks (4 blk ept bytes)
@@ -42,7 +46,7 @@ struct DenseArgs {
   int64_t rows_per_unit;
   int32_t lanes_per_row;
   int32_t group;      // group-row path: workgroups per row
-  void* xchg;         // group-row path: [groups][2][group][kBlockRowsInFlight] 64-bit tagged slots (zeroed)
+  void* xchg;         // group-row path: [groups][2][group][rows per step] 64-bit tagged slots (zeroed)
   uint32_t* error;    // group-row path: set when a wait for the other members gives up
 };
 

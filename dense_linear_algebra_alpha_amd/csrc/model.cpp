@@ -71,7 +71,8 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
     w.partial_rows = (size_t)groups;
     w.partial_off = 0;
     w.xchg_off = align_up(w.partial_off + (size_t)groups * n * sizeof(float));
-    w.error_off = align_up(w.xchg_off + (size_t)groups * 2 * p.group * kBlockRowsInFlight * sizeof(uint64_t));
+    w.error_off =
+        align_up(w.xchg_off + (size_t)groups * 2 * p.group * group_rows_per_step(p.chunks) * sizeof(uint64_t));
     w.total = align_up(w.error_off + sizeof(uint32_t));
   } else {
     w.partial_rows = (size_t)p.grid;
@@ -152,7 +153,7 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
         p->group = 1;
         if (slice < n) return XTVXY_ERROR_INVALID_VALUE;
       } else {
-        if (p->group < 1 || p->group > kBlock / kBlockRowsInFlight || (int64_t)p->group * slice < n ||
+        if (p->group < 1 || p->group > kBlock / group_rows_per_step(p->chunks) || (int64_t)p->group * slice < n ||
             p->grid % p->group != 0)
           return XTVXY_ERROR_INVALID_VALUE;
       }
@@ -203,8 +204,8 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
     const int64_t slice = ceil_div(n, p->group);
     p->chunks = (slice <= per) ? 1 : (slice <= 2 * per) ? 2 : (slice <= 4 * per) ? 4 : 8;
     p->lanes_per_row = kBlock;
-    rows_per_step = kBlockRowsInFlight;
-    inflight_per_wg = (double)kBlockRowsInFlight * slice * elem_bytes;
+    rows_per_step = group_rows_per_step(p->chunks);
+    inflight_per_wg = (double)rows_per_step * slice * elem_bytes;
   }
 
   const double io_bytes = (double)elem_bytes * m * n + 4.0 * ((double)m + 3.0 * n);
