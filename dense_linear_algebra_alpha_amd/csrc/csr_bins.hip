@@ -49,14 +49,17 @@ __global__ __launch_bounds__(kCountThreads) void bin_count_kernel(CsrBinArgs a) 
 }
 
 // Pass 2 (one workgroup): counts -> exclusive offsets in (bin, group) order, the first position
-// of every bin, and the units of every bin.
+// of every bin, and the units of every bin (an exclusive scan of the bins' unit counts).
 __global__ __launch_bounds__(kSortThreads) void bin_scan_kernel(CsrBinArgs a) {
   __shared__ int32_t part[kSortThreads];
+  __shared__ int32_t bstart[kMaxBins + 1];
+  __shared__ int32_t ucount[kMaxBins];
   const int tid = threadIdx.x;
   const int total = a.bins * kBinSortGroups;
   const int per = (total + kSortThreads - 1) / kSortThreads;
   const int s0 = min(tid * per, total), s1 = min(s0 + per, total);
   int32_t sum = 0;
+#pragma unroll 8
   for (int i = s0; i < s1; ++i) sum += a.counts[i];
   part[tid] = sum;
   __syncthreads();
@@ -67,22 +70,33 @@ __global__ __launch_bounds__(kSortThreads) void bin_scan_kernel(CsrBinArgs a) {
     __syncthreads();
   }
   int32_t run = part[tid] - sum;  // exclusive start of this thread's segment
+#pragma unroll 8
   for (int i = s0; i < s1; ++i) {
     const int32_t c = a.counts[i];
     a.counts[i] = run;
+    if (i % kBinSortGroups == 0) bstart[i / kBinSortGroups] = run;  // the first position of bin i / groups
     run += c;
   }
+  const int32_t placed = part[kSortThreads - 1];
+  if (tid == 0) bstart[a.bins] = placed;
   __syncthreads();
+  // units of every bin, then their exclusive scan over the bins (at most kMaxBins <= kSortThreads)
+  const int32_t mine = tid < a.bins ? (bstart[tid + 1] - bstart[tid] + kBinUnitChunks - 1) / kBinUnitChunks : 0;
+  if (tid < kMaxBins) ucount[tid] = mine;
+  __syncthreads();
+  for (int d = 1; d < kMaxBins; d <<= 1) {
+    const int32_t t = (tid < kMaxBins && tid >= d) ? ucount[tid - d] : 0;
+    __syncthreads();
+    if (tid < kMaxBins) ucount[tid] += t;
+    __syncthreads();
+  }
+  if (tid < a.bins) {
+    a.bin_start[tid] = bstart[tid];
+    a.unit_start[tid] = ucount[tid] - mine;
+  }
   if (tid == 0) {
-    int64_t units = 0;
-    for (int b = 0; b < a.bins; ++b) {
-      const int32_t start = a.counts[b * kBinSortGroups];
-      const int32_t end = b + 1 < a.bins ? a.counts[(b + 1) * kBinSortGroups] : part[kSortThreads - 1];
-      a.bin_start[b] = start;
-      a.unit_start[b] = (int32_t)units;
-      units += (end - start + kBinUnitChunks - 1) / kBinUnitChunks;
-    }
-    a.bin_start[a.bins] = part[kSortThreads - 1];
+    const int64_t units = a.bins > 0 ? ucount[a.bins - 1] : 0;
+    a.bin_start[a.bins] = placed;
     a.unit_start[a.bins] = (int32_t)(units < a.max_units ? units : a.max_units);
   }
 }
