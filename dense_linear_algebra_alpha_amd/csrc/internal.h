@@ -162,7 +162,10 @@ struct LrScalars {  // device-side scalars of the solver, in its workspace
   double gs, ws, ss;       // g.s, w.s, s.s for the line search
   double df;               // f(w + a s) - f(w) at the last trial step
   double rr, kappa, alpha, beta;  // CG: r.r, d.Hd and the two step coefficients
-  int32_t neg, pad;        // CG met a direction of non-positive curvature
+  int32_t neg;             // CG met a direction of non-positive curvature (later iterations do nothing)
+  int32_t done;            // CG's residual vanished exactly (later iterations do nothing)
+  int32_t iters;           // CG iterations performed (the one that met neg included)
+  int32_t pad;
 };
 constexpr int kLrMaxParts = 2048;     // partial sums per reduction row (workgroups of a streaming kernel)
 constexpr int kLrRows = 4;            // reduction rows

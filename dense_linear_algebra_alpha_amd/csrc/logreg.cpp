@@ -8,8 +8,9 @@
 //
 // The driver enqueues kernels on the caller's stream and copies the solver's device scalars
 // (LrScalars) to the host only where a decision needs them: after the gradient (stop?), after
-// each CG iteration (converged? curvature?), after each line-search trial (accept?). Everything
-// that touches an m- or n-vector runs in the library's kernels.
+// each CG iteration when CG stops on its residual (converged? curvature?) or once after a fixed
+// number of them, after each line-search trial (accept?). Everything that touches an m- or
+// n-vector runs in the library's kernels.
 #include <hip/hip_runtime.h>
 
 #include <chrono>
@@ -211,15 +212,18 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
     // ---- CG on H s = -g
     const double eps = std::fmin(opt->cg_forcing, std::sqrt(gnorm)) * gnorm;
     if ((st = launched(launch_lr_cg_init(n, g, s, r, d, S, stream))) != XTVXY_SUCCESS) return st;
-    int used = 0;
+    // With fixed_cg the iterations are enqueued back to back and read once: the stops that do
+    // not depend on the residual test (non-positive curvature, an exactly vanished residual) are
+    // taken on the device, which then leaves the remaining iterations without effect.
     for (int j = 0; j < opt->max_cg; ++j) {
       if ((st = E.hvp(v, lam, d, q)) != XTVXY_SUCCESS) return st;
       if ((st = launched(launch_lr_cg_step(n, q, d, s, r, S, j == 0, part, stream))) != XTVXY_SUCCESS) return st;
+      if (opt->fixed_cg) continue;
       if ((st = read_scalars()) != XTVXY_SUCCESS) return st;
-      used = j + 1;
-      if (h.neg) break;
-      if (h.rr == 0.0 || (!opt->fixed_cg && std::sqrt(h.rr) < eps)) break;
+      if (h.neg || h.done || std::sqrt(h.rr) < eps) break;
     }
+    if (opt->fixed_cg && (st = read_scalars()) != XTVXY_SUCCESS) return st;
+    const int used = h.iters;
     rep.cg_iterations += used;
     record(k, 2, used);
     // ---- line search along s: X s, slopes, then trials of the objective change

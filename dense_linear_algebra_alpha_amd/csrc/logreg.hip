@@ -142,24 +142,26 @@ __global__ __launch_bounds__(kThreads) void lr_finish_kernel(int op, const doubl
       if (lead) S->df = rows + lam * (a * S->ws + 0.5 * a * a * S->ss);
       break;
     }
-    case kLrCgAlpha: {  // row 1: d.Hd
+    case kLrCgAlpha: {  // row 1: d.Hd (nothing once CG has stopped)
       const double kappa = row_sum(part, 1, np_n, red);
-      if (lead) {
+      if (lead && !S->neg && !S->done) {
         S->kappa = kappa;
         if (kappa > 0.0) {
           S->alpha = S->rr / kappa;
-          S->neg = 0;
         } else {
           S->neg = 1;  // also for NaN
+          S->iters += 1;
         }
       }
       break;
     }
     case kLrCgBeta: {  // row 1: the new r.r
       const double rn = row_sum(part, 1, np_n, red);
-      if (lead && !S->neg) {
+      if (lead && !S->neg && !S->done) {
         S->beta = rn / S->rr;
         S->rr = rn;
+        S->iters += 1;
+        if (rn == 0.0) S->done = 1;
       }
       break;
     }
@@ -181,18 +183,23 @@ __global__ __launch_bounds__(kThreads) void lr_cg_init_kernel(int64_t n, const f
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     S->rr = S->gg;
     S->neg = 0;
+    S->done = 0;
+    S->iters = 0;
   }
 }
 
 // One CG iteration after q = H d, in one workgroup (n <= kLrSmallCg):
 // kappa = d.q; on kappa <= 0 (or NaN) flag it and, at the first iteration, set s = d (= -g);
-// else alpha = r.r / kappa, s += alpha d, r += alpha q, beta = r.r(new) / r.r, d = -r + beta d.
+// else alpha = r.r / kappa, s += alpha d, r += alpha q, beta = r.r(new) / r.r, d = -r + beta d,
+// and flag an exactly vanished residual. Once either flag is set the iteration does nothing, so
+// the host may enqueue a fixed number of iterations without reading anything back.
 __global__ __launch_bounds__(kSmallThreads) void lr_cg_small_kernel(int64_t n, const float* __restrict__ q,
                                                                     float* __restrict__ d, float* __restrict__ z,
                                                                     float* __restrict__ r,
                                                                     LrScalars* __restrict__ S, int first) {
   __shared__ double red[kSmallThreads / 64];
   const int tid = threadIdx.x;
+  if (S->neg || S->done) return;  // the same value in every thread
   double kap = 0.0;
   for (int64_t j = tid; j < n; j += kSmallThreads) kap += (double)d[j] * (double)q[j];
   kap = block_sum<kSmallThreads>(kap, red);
@@ -202,6 +209,7 @@ __global__ __launch_bounds__(kSmallThreads) void lr_cg_small_kernel(int64_t n, c
     if (tid == 0) {
       S->kappa = kap;
       S->neg = 1;
+      S->iters += 1;
     }
     return;
   }
@@ -216,7 +224,7 @@ __global__ __launch_bounds__(kSmallThreads) void lr_cg_small_kernel(int64_t n, c
     r[j] = rj;
     rn += (double)rj * (double)rj;
   }
-  rn = block_sum<kSmallThreads>(rn, red);  // every thread read S->rr before this barrier
+  rn = block_sum<kSmallThreads>(rn, red);  // every thread read S before this barrier
   const double be = rn / rr;
   const float bef = (float)be;
   for (int64_t j = tid; j < n; j += kSmallThreads) d[j] = -r[j] + bef * d[j];
@@ -225,7 +233,8 @@ __global__ __launch_bounds__(kSmallThreads) void lr_cg_small_kernel(int64_t n, c
     S->alpha = al;
     S->beta = be;
     S->rr = rn;
-    S->neg = 0;
+    S->iters += 1;
+    if (rn == 0.0) S->done = 1;
   }
 }
 
@@ -239,7 +248,9 @@ __global__ __launch_bounds__(kThreads) void lr_cg_update_kernel(int64_t n, const
   __shared__ double red[kThreads / 64];
   const bool neg = S->neg != 0;
   double rn = 0.0;
-  if (neg) {
+  if (S->done) {
+    // CG has stopped: nothing to update
+  } else if (neg) {
     if (first)
       for (int64_t j = first_index(); j < n; j += grid_stride()) z[j] = d[j];
   } else {
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void lr_cg_update_kernel(int64_t n, const
 __global__ __launch_bounds__(kThreads) void lr_cg_direction_kernel(int64_t n, const float* __restrict__ r,
                                                                    float* __restrict__ d,
                                                                    const LrScalars* __restrict__ S) {
-  if (S->neg) return;
+  if (S->neg || S->done) return;
   const float bef = (float)S->beta;
   for (int64_t j = first_index(); j < n; j += grid_stride()) d[j] = -r[j] + bef * d[j];
 }

@@ -365,9 +365,10 @@ xtvxy_status xtvxy_tune_cache_load(const char *path);
  *   margins  X s                                         (the pattern's first half)
  *   step     a = 1, 1/2, 1/4, ... until f(w + a s) - f(w) <= 1e-4 a g.s, where the change of f
  *            is summed row by row in fp64 (one m-length kernel per trial); w += a s.
- * The host reads a few scalars after each reduction to take the decisions (one
- * synchronisation per CG iteration, per line-search trial and per Newton step), so the call
- * is synchronous. Vectors are fp32; reductions (dot products, loss sums) are fp64 in a fixed
+ * The host reads a few scalars back to take the decisions (one synchronisation per Newton
+ * step, per line-search trial, and per CG iteration, or once per CG solve with fixed_cg, whose
+ * stops on curvature or a vanished residual are taken on the device), so the call is
+ * synchronous. Vectors are fp32; reductions (dot products, loss sums) are fp64 in a fixed
  * order.
  *
  * Engines: XTVXY_LOGREG_FUSED runs the three products with this library's kernels
