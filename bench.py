@@ -77,7 +77,7 @@ class HipEvents:
 
 def kernel_sources_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
-    files = ["device_util.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
+    files = ["device_util.h", "internal.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
