@@ -37,10 +37,11 @@
 // entries (which start where this tile ends) are already loading, and (when y is
 // read from global memory) at the end of the step, once they have arrived, the
 // next tile's y gathers are issued so that they overlap the barrier and the
-// start of the next step. Every load is
-// issued unconditionally (addresses clamped, results selected): the counter of
-// outstanding vector-memory operations completes in order, and a conditional
-// load anywhere in between forces a wait for everything. The per-tile LDS state
+// start of the next step. The loads issued ahead run without any branch around
+// them (addresses clamped, slots past the tile masked where they are used): the
+// counter of outstanding vector-memory operations completes in order, and a
+// conditional load, or two paths that leave a prefetched value in different
+// registers, anywhere in between forces a wait for everything. The per-tile LDS state
 // (row_ptr, v, marks, dots) is double-buffered, so a tile costs two workgroup
 // barriers: one between the dots and the scatter, one that publishes the next
 // tile's state and counts its rows.
@@ -113,6 +114,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   __shared__ float u_s[2][BLK];         // u_row = v_row * (row dot), built by the dots
   __shared__ __align__(16) uint16_t mark_s[2][T];  // 1 + tile row whose first entry sits at slot q, else 0
   __shared__ int32_t wfirst_s[2][(BLK / 64)];     // tile row holding the first entry of each wavefront
+  __shared__ int32_t rows_s[2];                    // rows of the tile
   __shared__ float sink_s[BLK];            // a private LDS word per thread for masked-off adds
   __shared__ float lred[(BLK / 64)];
   __shared__ int32_t range_s[2];
@@ -265,10 +267,10 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   auto gather_y = [&](int32_t col) -> float {
     if constexpr (YMODE == kYGlobal) return a.y[col];
     if constexpr (YMODE == kYLds) return y_s[col];
-    // split: the LDS read is clamped (every lane issues it), the global read only where needed
+    // split: both reads are issued by every lane, without a branch; lanes whose column is in
+    // the LDS copy read y[0] from global memory (one cache line for all of them)
     const float fast = y_s[min(col, y_window - 1)];
-    float slow = 0.0f;
-    if (col >= y_window) slow = a.y[col];
+    const float slow = a.y[col < y_window ? 0 : col];
     return col < y_window ? fast : slow;
   };
 
@@ -277,10 +279,10 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     g.rp1 = a.row_ptr[min(r + tid + 1, re)];
     g.v = HAS_V ? a.v[min(r + tid, re - 1)] : 1.0f;
   };
-  // The K entries from base + K tid (base a multiple of 4). Tiles whose T slots lie inside the
-  // whole quads of the arrays (all but the last one or two) load without any guard; the others
-  // load element by element with clamped addresses, entries past nnz reading as zero. The
-  // branch is the same for the whole workgroup.
+  // The K entries from base + K tid (base a multiple of 4), loaded and used at once (the slices
+  // of a long row). Tiles whose T slots lie inside the whole quads of the arrays load without
+  // any guard; the others load element by element with clamped addresses, entries past nnz
+  // reading as zero. The branch is the same for the whole workgroup.
   auto load_entries = [&](uint32_t base, float (&val)[K], int32_t (&col)[K]) {
     const uint32_t e0 = base + (uint32_t)tid * K;
     if (base + T <= nnz_full) {
@@ -311,19 +313,71 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
       }
     }
   };
+  // The same entries loaded a step ahead, with no branch at all (see the top of the file): with
+  // 16-byte loads a quad at or past the last whole quad of the arrays is read at the last whole
+  // quad instead (the launch guarantees nnz >= 4), element loads are clamped to nnz - 1. Slots
+  // past the tile then hold entries of other positions; every use masks them, and their column
+  // indices are valid. The up to three entries after the whole quads are patched in by
+  // fix_tail before the tile's first use.
+  const uint32_t last_quad = ALIGNED ? nnz_full - 4u : 0u;
+  auto load_entries_ahead = [&](uint32_t base, float (&val)[K], int32_t (&col)[K]) {
+    const uint32_t e0 = base + (uint32_t)tid * K;
+#pragma unroll
+    for (int k = 0; k < K; k += 4) {
+      if constexpr (ALIGNED) {
+        const uint32_t q = min(e0 + k, last_quad);
+        const f4 vv = *reinterpret_cast<const f4*>(a.values + q);
+        const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + q);
+        val[k] = vv.x; val[k + 1] = vv.y; val[k + 2] = vv.z; val[k + 3] = vv.w;
+        col[k] = cc.x; col[k + 1] = cc.y; col[k + 2] = cc.z; col[k + 3] = cc.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t p = min(e0 + k + q, nnz - 1u);
+          val[k + q] = a.values[p];
+          col[k + q] = a.col_idx[p];
+        }
+      }
+    }
+  };
+  // Entries nnz_full .. nnz - 1 of a tile loaded by load_entries_ahead with 16-byte loads. The
+  // branch is the same for the whole workgroup and taken by the last tile or two only.
+  auto fix_tail = [&](uint32_t first_entry, TileRegs<K>& g) {
+    if constexpr (ALIGNED && kGatherAhead) {
+      const uint32_t base = first_entry & ~3u;
+      if (nnz != nnz_full && base + T > nnz_full) {
+        const uint32_t e0 = base + (uint32_t)tid * K;
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          const uint32_t p = e0 + k;
+          if (p >= nnz_full && p < nnz) {
+            g.val[k] = a.values[p];
+            g.col[k] = a.col_idx[p];
+          }
+        }
+      }
+    }
+  };
+  // Kernels that gather y a step ahead load the entries branch-free (measured faster on the Zipf
+  // workload, where the two paths of load_entries left the prefetched entries in different
+  // registers and the copies waited for them at once); the others keep the guarded loads
+  // (measured faster on the logistic-regression workload).
   auto issue = [&](int32_t r, uint32_t first_entry, TileRegs<K>& g) {
     issue_rows(r, g);
-    load_entries(first_entry & ~3u, g.val, g.col);
+    if constexpr (kGatherAhead)
+      load_entries_ahead(first_entry & ~3u, g.val, g.col);
+    else
+      load_entries(first_entry & ~3u, g.val, g.col);
   };
-  // Publishes the state of the tile of `cnt` rows whose first entry is `first` into buffer b
-  // (row_ptr, v, zeroed dots, row-start marks, the row of each wavefront's first entry) and
-  // returns whether this thread's row ends inside the tile's T entry slots; the rows that do
-  // form a prefix, so their count is the number of rows of the tile.
-  auto stage = [&](int b, int cnt, uint32_t first, const TileRegs<K>& g) -> bool {
+  // Publishes the state of the tile of at most `cnt` rows whose first entry is `first` into
+  // buffer b (row_ptr, v, zeroed dots, row-start marks, the row of each wavefront's first entry,
+  // the number of rows). The tile's rows are those that end inside its T entry slots: a prefix
+  // of the cnt candidates, so the one thread whose row is the first that does not fit (or the
+  // last candidate, when all fit) writes the count. A barrier must follow before it is read.
+  auto stage = [&](int b, int cnt, uint32_t first, const TileRegs<K>& g) {
     const uint32_t base = first & ~3u;
     // the row values u: built by the dots, or (second half alone) the given vector
     u_s[b][tid] = (MODE == kModeTmv && tid < cnt) ? g.v : 0.0f;
-    bool fits = false;
     if (tid < cnt) {
       if (tid == 0) rp_s[b][0] = g.rp;
       rp_s[b][tid + 1] = g.rp1;
@@ -335,9 +389,11 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
         const uint32_t pw = w == 0 ? first - base : (uint32_t)(w * 64 * K);
         if (s <= pw && pw < e) wfirst_s[b][w] = tid;
       }
-      fits = e <= T;
+      const bool fits = e <= T;
+      const bool prev_fits = tid == 0 || s <= T;  // the row before ends where this one starts
+      if (prev_fits && !fits) rows_s[b] = tid;
+      if (fits && tid == cnt - 1) rows_s[b] = cnt;
     }
-    return fits;
   };
 
   TileRegs<K> ga, gb;
@@ -348,11 +404,14 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   {
     const uint32_t p0 = (uint32_t)a.row_ptr[ra];
     issue(ra, p0, ga);
+    fix_tail(p0, ga);
     if constexpr (kGatherAhead) {
 #pragma unroll
       for (int k = 0; k < K; ++k) ga.yv[k] = gather_y(ga.col[k]);
     }
-    j = __syncthreads_count(stage(0, cnt, p0, ga));
+    stage(0, cnt, p0, ga);
+    __syncthreads();
+    j = rows_s[0];
   }
 
   auto step = [&](TileRegs<K>& g, TileRegs<K>& gn) -> bool {
@@ -469,6 +528,18 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
       const int before = max(wf, dpp_int<dpp::kWaveShr1>(-1, wave_max_scan(run_max)));
 #pragma unroll
       for (int k = 0; k < K; ++k) rk[k] = max(before, mk[k]);  // in [0, BLK)
+      // (c') with bins: the rank of each product of a column outside the window among the
+      // tile's items of its bin. It depends on the column alone, so it is taken before the dots
+      // and the barrier that completes the dots also completes the bins' counts.
+      uint32_t crank[K];
+      bool cold[K];
+      if constexpr (BINNED && MODE != kModeRowdot) {
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+          cold[k] = ok[k] && g.col[k] >= window;
+          crank[k] = cold[k] ? bin_rank(g.col[k]) : 0u;
+        }
+      }
 
       if constexpr (MODE != kModeTmv) {
       // (d) per-row dots. Runs of one row inside the thread are summed in registers; a row
@@ -517,7 +588,23 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
         float c[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) c[k] = u_s[b][rk[k]] * g.val[k];
-        scatter_k(c, g.col, ok);
+        if constexpr (BINNED) {
+          // room for the bins' items (the threads that hand it out are busy while the others
+          // add the window's products), then the items
+          if constexpr (MODE == kModeTmv) __syncthreads();  // the bins' counts are complete
+          bin_alloc();
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            const bool hot = ok[k] && !cold[k];
+            lds_add_f32(hot ? out_s + g.col[k] : sink_s + tid, hot ? c[k] : 0.0f);
+          }
+          __syncthreads();  // room for every bin is known
+#pragma unroll
+          for (int k = 0; k < K; ++k)
+            if (cold[k]) bin_write(g.col[k], c[k], crank[k]);
+        } else {
+          scatter_k(c, g.col, ok);
+        }
       }
     }
     if (!more) return false;
@@ -525,14 +612,16 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     // step and have arrived by now, and the gathers overlap the barrier below and the start of
     // the next step
     if constexpr (kGatherAhead) {
+      fix_tail(pb, gn);
 #pragma unroll
       for (int k = 0; k < K; ++k) gn.yv[k] = gather_y(gn.col[k]);
     }
-    const bool fits = stage(b ^ 1, cnt_next, pb, gn);
+    stage(b ^ 1, cnt_next, pb, gn);
     ra = ra_next;
     buf = b ^ 1;
     cnt = cnt_next;
-    j = __syncthreads_count(fits);  // the next tile's state is published
+    __syncthreads();  // the next tile's state is published
+    j = rows_s[b ^ 1];
     return true;
   };
 
@@ -565,7 +654,7 @@ hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t 
 
 template <int BLK, int K, int COLD, int YMODE, int MODE>
 hipError_t launch_kv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const bool al = a.aligned;
+  const bool al = a.aligned && a.nnz >= 4;  // 16-byte loads need one whole quad of entries
   if constexpr (MODE == kModeTmv) {  // u is always given
     return al ? launch_k<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
               : launch_k<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);

@@ -81,9 +81,22 @@ class DenseOnDevice:
 
 
 class CsrOnDevice:
-    def __init__(self, p):
+    """The arrays of a CsrProblem copied to the GPU; with entry_offset > 0, col_idx and values
+    start that many elements into their buffers (4-byte aligned, not 16-byte aligned for 1-3)."""
+
+    def __init__(self, p, entry_offset: int = 0):
+        import torch
         self.p = p
-        self.rp, self.ci, self.vals = to_dev(p.row_ptr), to_dev(p.col_idx), to_dev(p.values)
+        self.rp = to_dev(p.row_ptr)
+        if entry_offset:
+            def shifted(a):
+                src = _as_tensor(a)
+                buf = torch.empty(a.size + entry_offset, dtype=src.dtype, device=dev())
+                buf[entry_offset:].copy_(src)
+                return buf[entry_offset:]
+            self.ci, self.vals = shifted(p.col_idx), shifted(p.values)
+        else:
+            self.ci, self.vals = to_dev(p.col_idx), to_dev(p.values)
         self.y, self.v, self.z = to_dev(p.y), to_dev(p.v), to_dev(p.z)
 
     def run(self, plan=None, out=None, alpha=None, beta=None):

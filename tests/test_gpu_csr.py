@@ -63,6 +63,35 @@ def test_every_kernel_variant(m, n, mean_len):
         assert_parity(d.run(plan=plan), ref, bnd, "forced %s" % plan.as_dict())
 
 
+@pytest.mark.parametrize("entry_offset", [0, 1, 3])
+def test_entry_tails_and_misaligned_arrays(entry_offset):
+    """nnz of every residue mod 4 (1 to 9 entries, and a matrix of several tiles), with col_idx and
+    values 16-byte aligned or not: the entries after the last whole quad, and the element-wise
+    loads of misaligned arrays, under every kernel variant."""
+    cases = []
+    for nnz in range(1, 10):
+        rng = np.random.default_rng(100 + nnz)
+        m, n = 3, 11
+        rows = np.sort(rng.integers(0, m, nnz))
+        rp = np.zeros(m + 1, np.int32)
+        rp[1:] = np.cumsum(np.bincount(rows, minlength=m))
+        ci = np.concatenate([np.sort(rng.choice(n, int(c), replace=False)) for c in np.diff(rp)]).astype(np.int32)
+        vals = rng.uniform(-1, 1, nnz).astype(np.float32)
+        y, v, z = (rng.uniform(-1, 1, k).astype(np.float32) for k in (n, m, n))
+        cases.append(datagen.CsrProblem(m, n, rp, ci, vals, y, v, z, 0.9, 0.4, "nnz=%d" % nnz))
+    p = datagen.csr_random(5000, 3000, seed=77, mean_len=9.0, empty_frac=0.1)
+    if p.nnz % 4 == 0:  # keep a ragged last quad
+        p = datagen.csr_random(5001, 3000, seed=77, mean_len=9.0, empty_frac=0.1)
+    assert p.nnz % 4 != 0
+    cases.append(p)
+    for q in cases:
+        ref, bnd = csr_oracle(q)
+        d = CsrOnDevice(q, entry_offset=entry_offset)
+        for plan in [None] + forced_plans(q.m, q.n, q.nnz)[::5]:
+            note("tails nnz=%d offset=%d plan=%s" % (q.nnz, entry_offset, None if plan is None else plan.as_dict()))
+            assert_parity(d.run(plan=plan), ref, bnd, "nnz=%d offset=%d" % (q.nnz, entry_offset))
+
+
 def test_rows_longer_than_a_tile():
     # rows of 3000..9000 entries (more than one 2048-entry tile) between short and empty rows
     g = np.random.default_rng(5)
