@@ -77,7 +77,7 @@ class HipEvents:
 
 def kernel_sources_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
-    files = ["device_util.h", "internal.h"] + (["csr.hip"] if kind == "csr" else ["dense.hip"])
+    files = ["device_util.h", "internal.h"] + {"csr": ["csr.hip"], "csr_waves": ["csr_waves.hip"]}.get(kind, ["dense.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -90,7 +90,8 @@ def kernel_name(plan) -> str:
     dense_group_rows is its group-row form)."""
     import dense_linear_algebra_alpha_amd as xt
     names = {xt.XTVXY_DENSE_WAVE_ROWS: "dense_wave_rows", xt.XTVXY_DENSE_BLOCK_ROWS: "dense_block_rows",
-             xt.XTVXY_DENSE_GROUP_ROWS: "dense_group_rows", xt.XTVXY_CSR_TILES: "csr_fused"}
+             xt.XTVXY_DENSE_GROUP_ROWS: "dense_group_rows", xt.XTVXY_CSR_TILES: "csr_fused",
+             xt.XTVXY_CSR_WAVES: "csr_waves"}
     return names.get(plan.kernel, "kernel%d" % plan.kernel)
 
 
@@ -253,7 +254,8 @@ def bench_logreg(args):
         "speedup_vs_unfused": round(results["unfused"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
         "speedup_vs_unfused_explicit_transpose": round(
             results["unfused_explicit_transpose"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
-        "roofline": {"bound": "hbm", "kernel": "csr_fused", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+        "roofline": {"bound": "hbm", "kernel": kernel_name(xt.xtvxy_csr_f32_plan(X.m, X.n, X.nnz)),
+                     "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "what": "the Hessian-vector product alone (one fused call, v = p(1 - p), y = z = d, "
                              "beta = lambda)",
@@ -500,7 +502,8 @@ def main():
         "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": kernel_name(plan), "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload, kernel_name(plan), kind),
+                     "traffic": load_traffic(args.workload, kernel_name(plan),
+                                             "csr_waves" if kernel_name(plan) == "csr_waves" else kind),
                      "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
                      "kernel_ms_min": round(min(kernel_ms), 5)},
     }

@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (XTVXY_CSR_TILES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
+from ._abi import (XTVXY_CSR_TILES, XTVXY_CSR_WAVES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
                    XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
                    XTVXY_UNFUSED_EXPLICIT_TRANSPOSE, XTVXY_UNFUSED_TRANSPOSE_OP,
                    XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,

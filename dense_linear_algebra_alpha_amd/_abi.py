@@ -25,6 +25,7 @@ XTVXY_DENSE_WAVE_ROWS = 1
 XTVXY_DENSE_BLOCK_ROWS = 2
 XTVXY_DENSE_GROUP_ROWS = 3
 XTVXY_CSR_TILES = 11
+XTVXY_CSR_WAVES = 12
 
 
 class xtvxy_device_info(ctypes.Structure):

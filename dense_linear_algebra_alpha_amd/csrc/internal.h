@@ -32,6 +32,15 @@ constexpr int kBinSortGroups = 256;  // workgroups of the counting sort of chunk
 // LDS of the fused CSR kernel for the per-bin state (count, current chunk, fill, room, two
 // positions) when binning
 constexpr size_t kCsrBinStateBytes = 32;
+// Wavefront CSR kernel (csr_waves.hip): static LDS per workgroup of `blk` threads (row-start
+// marks of 512 entry slots, u and v of 64 rows per wavefront, a sink word per thread), and the
+// dynamic LDS: output and y windows, then each wavefront's bin state (6 words per bin).
+constexpr size_t kCsrWaveBinStateBytes = 24;
+constexpr size_t csr_waves_static_lds(int blk) { return (size_t)(blk / 64) * (512 + 512) + 4 * (size_t)blk; }
+constexpr size_t csr_waves_dynamic_lds(int64_t window, int64_t y_window, int32_t bins, int blk) {
+  return (((size_t)(window + y_window) * 4 + 7) & ~(size_t)7) +
+         (bins > 0 ? (size_t)bins * kCsrWaveBinStateBytes * (size_t)(blk / 64) : 0);
+}
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 
@@ -101,6 +110,8 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
 // as v, no y).
 enum CsrLaunchMode { kCsrFused = 0, kCsrRowdot = 1, kCsrTmv = 2 };
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
+// The whole pattern's partials by the wavefront kernel (plan kernel XTVXY_CSR_WAVES).
+hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
 // Bin passes: group the handed-out chunks by bin, then accumulate every unit of a bin in LDS.
 hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s);
 // Per-bin partial sums for the aggregation (null: no binning).
@@ -136,8 +147,10 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
                          xtvxy_launch_params* p, int elem_bytes = 4, int max_wg_per_cu = 0);
 xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
                             xtvxy_launch_params* p, int elem_bytes = 4);
+// fused: the plan is for the whole pattern (the wavefront kernel is a candidate); else for one
+// of its halves (workgroup tiles only).
 xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
-                       xtvxy_launch_params* p);
+                       xtvxy_launch_params* p, bool fused = true);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p);
 

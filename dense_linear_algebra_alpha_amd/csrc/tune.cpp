@@ -147,20 +147,28 @@ std::vector<xtvxy_launch_params> csr_candidates(int64_t m, int64_t n, int64_t nn
       win(w, w / 3);
     }
   }
-  const std::pair<int, int> shapes[] = {{256, 4}, {256, 8}, {512, 8}};
+  // (kernel, threads, entries per thread): workgroup tiles, and for narrow matrices (whose
+  // windows hold all of n) the wavefront kernel too
+  struct Shape {
+    int32_t kernel, threads, ept;
+  };
+  std::vector<Shape> shapes = {{XTVXY_CSR_TILES, 256, 4}, {XTVXY_CSR_TILES, 256, 8}, {XTVXY_CSR_TILES, 512, 8}};
+  if ((int64_t)n * 8 <= 64 * 1024)
+    for (int32_t t : {256, 512, 1024}) shapes.push_back({XTVXY_CSR_WAVES, t, 8});
   for (const auto& sh : shapes) {
     for (const auto& wy : windows) {
       for (int32_t bc : {0, 16384, 32768}) {
         if (wy.first >= n && bc != 0) continue;
+        if (sh.kernel == XTVXY_CSR_WAVES && wy.first < n) continue;
         for (int k : {1, 2, 4, 8}) {
-          if ((int64_t)sh.first * k > 2048) continue;  // threads per CU
+          if ((int64_t)sh.threads * k > 2048) continue;  // threads per CU
           xtvxy_launch_params p{};
-          p.kernel = XTVXY_CSR_TILES;
+          p.kernel = sh.kernel;
           p.vec = 1;
           p.chunks = 1;
           p.group = 1;
-          p.block_threads = sh.first;
-          p.entries_per_thread = sh.second;
+          p.block_threads = sh.threads;
+          p.entries_per_thread = sh.ept;
           p.lds_window = wy.first;
           p.y_window = wy.second;
           p.bin_columns = bc;

@@ -87,7 +87,14 @@ enum {
  * hardware float atomics (bin_columns == 0), or are binned: the fused kernel
  * appends each cold product to workspace chunks of its bin of bin_columns
  * columns, and a second pass accumulates every bin in LDS (bin_columns > 0). */
-enum { XTVXY_CSR_TILES = 11 };
+enum {
+  XTVXY_CSR_TILES = 11,
+  /* the same scatter (LDS window, then atomics or bins), but every wavefront walks
+   * tiles of whole rows of its own (at most 64 rows and 512 entries), so the
+   * workgroup never waits at a barrier per tile; block_threads 256, 512 or 1024,
+   * entries_per_thread 8 */
+  XTVXY_CSR_WAVES = 12
+};
 
 /* Launch parameters chosen by the analytical model (the *_plan queries) or
  * forced by the caller (the *_ex entry points). */

@@ -171,7 +171,10 @@ def test_plan_complete_rejects_plans_that_do_not_cover(lib):
                                      (10, 5, 7), (1, 1, 1)])
 def test_csr_model_plans(lib, m, n, nnz):
     p = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
-    assert p.kernel == xt.XTVXY_CSR_TILES and p.grid >= 1 and p.entries_per_thread in (4, 8, 16)
+    # narrow matrices of short rows take the wavefront kernel, the rest workgroup tiles
+    waves = n * 8 <= 64 * 1024 and nnz <= 16 * m
+    assert p.kernel == (xt.XTVXY_CSR_WAVES if waves else xt.XTVXY_CSR_TILES)
+    assert p.grid >= 1 and p.entries_per_thread in (4, 8, 16)
     assert 0 < p.lds_window <= n and p.workspace_bytes >= p.grid * p.lds_window * 4
     lds = (p.lds_window + p.y_window) * 4
     assert lds <= 64 * 1024
@@ -181,9 +184,41 @@ def test_csr_model_plans(lib, m, n, nnz):
         # binned: two workgroups per CU still fit, and the pool holds every stored entry
         bins = -(-(n - p.lds_window) // p.bin_columns)
         assert bins <= 512 and p.bin_columns & (p.bin_columns - 1) == 0
+        assert p.kernel == xt.XTVXY_CSR_TILES
         static = 29 * p.block_threads + 256 + 4 * p.block_threads * p.entries_per_thread
         assert (2048 // p.block_threads) // 2 * (lds + bins * 32 + static) <= MI355X.lds_bytes
         assert p.workspace_bytes >= nnz * 8
+
+
+def test_csr_wave_plans(lib):
+    """The wavefront kernel: 256, 512 or 1024 threads of 8 entries; its LDS (windows, 1 KiB of
+    marks, u and v per wavefront, a word per thread, 24 bytes per bin and wavefront) must fit;
+    its bin pool leaves room for one partly filled chunk per (wavefront, bin)."""
+    def lp(blk, window, y_window, bc, grid=64, ept=8):
+        return xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_WAVES, block_threads=blk, entries_per_thread=ept, grid=grid,
+                                      vec=1, chunks=1, group=1, lds_window=window, y_window=y_window, bin_columns=bc)
+    for blk in (256, 512, 1024):
+        q = xt.xtvxy_csr_f32_plan_complete(1000, 900, 9000, lp(blk, 900, 900, 0), MI355X)
+        assert q.kernel == xt.XTVXY_CSR_WAVES and q.workspace_bytes == 64 * 900 * 4
+    for blk, ept in ((128, 8), (256, 4), (2048, 8)):
+        with pytest.raises(xt.XtvxyError):
+            xt.xtvxy_csr_f32_plan_complete(1000, 900, 9000, lp(blk, 900, 900, 0, ept=ept), MI355X)
+    # the largest window that fits beside the 1024-thread workgroup's static LDS (20 KiB)
+    static = 16 * 1024 + 4 * 1024
+    w = (MI355X.lds_bytes - static) // 4
+    xt.xtvxy_csr_f32_plan_complete(1000, 10**6, 10**6, lp(1024, w, 0, 0), MI355X)
+    with pytest.raises(xt.XtvxyError):
+        xt.xtvxy_csr_f32_plan_complete(1000, 10**6, 10**6, lp(1024, w + 2, 0, 0), MI355X)
+    # binned: 60 bins of 16384 columns, 24 bytes per bin and wavefront
+    n, w = 1_000_000, 20000
+    bins = -(-(n - w) // 16384)
+    q = xt.xtvxy_csr_f32_plan_complete(5_000_000, n, 2 * 10**8, lp(1024, w, 0, 16384, grid=256), MI355X)
+    chunks = -(-2 * 10**8 // 512) + 256 * 16 * bins
+    assert q.workspace_bytes >= chunks * 512 * 8
+    with pytest.raises(xt.XtvxyError):  # the bin state of 16 wavefronts no longer fits
+        xt.xtvxy_csr_f32_plan_complete(5_000_000, n, 2 * 10**8,
+                                       lp(1024, (MI355X.lds_bytes - static - 16 * 24 * bins) // 4 + 2, 0, 16384),
+                                       MI355X)
 
 
 def test_csr_model_bins_the_wide_zipf_matrix_and_not_the_narrow_one(lib):
