@@ -397,27 +397,27 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       for (int k = 0; k < K; ++k) rk[k] = max(before, mk[k]);  // in [0, R)
       // per-row dots: runs of one row inside the lane summed in registers; a row strictly
       // inside the lane is stored; the first and last runs are finished by a segmented sum
-      // across the wavefront. Every row ends inside the tile, so each gets one write.
-      int r0 = -1, r1 = -1;
-      float head = 0.0f, run = 0.0f;
+      // across the wavefront. Every row ends inside the tile, so each gets one write. Slots
+      // outside the tile belong to its first row (before it) or its last nonempty row (after
+      // it) and add a zero product there, so the row logic needs no mask.
+      float pk[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) {
-        const float p = ok[k] ? g.val[k] * g.yv[k] : 0.0f;
-        const bool fresh = ok[k] && rk[k] != r1;
-        if (fresh && r1 >= 0 && r1 != r0) u_s[wave][r1] = v_s[wave][r1] * run;
-        head = (fresh && r1 >= 0 && r1 == r0) ? run : head;
-        r0 = (ok[k] && r0 < 0) ? rk[k] : r0;
-        run = fresh ? p : run + p;
-        r1 = ok[k] ? rk[k] : r1;
+      for (int k = 0; k < K; ++k) pk[k] = ok[k] ? g.val[k] * g.yv[k] : 0.0f;
+      const int r0 = rk[0], r1 = rk[K - 1];
+      float head = 0.0f, run = pk[0];
+#pragma unroll
+      for (int k = 1; k < K; ++k) {
+        const bool fresh = rk[k] != rk[k - 1];
+        if (fresh && rk[k - 1] != r0) u_s[wave][rk[k - 1]] = v_s[wave][rk[k - 1]] * run;
+        head = (fresh && rk[k - 1] == r0) ? run : head;
+        run = fresh ? pk[k] : run + pk[k];
       }
-      const bool has = r1 >= 0;
-      const int key = has ? r1 : INT32_MAX;
-      const float tails = wave_segmented_sum(has ? run : 0.0f, key);
+      const float tails = wave_segmented_sum(run, r1);
       const float prev_tails = dpp_float<dpp::kWaveShr1>(0.0f, tails);
-      const int prev_key = dpp_int<dpp::kWaveShr1>(-1, key);
+      const int prev_key = dpp_int<dpp::kWaveShr1>(-1, r1);
       const int next_r0 = dpp_int<dpp::kWaveShl1>(-1, r0);
-      if (has && r0 != r1) u_s[wave][r0] = v_s[wave][r0] * (head + (prev_key == r0 ? prev_tails : 0.0f));
-      if (has && next_r0 != r1) u_s[wave][r1] = v_s[wave][r1] * tails;
+      if (r0 != r1) u_s[wave][r0] = v_s[wave][r0] * (head + (prev_key == r0 ? prev_tails : 0.0f));
+      if (next_r0 != r1) u_s[wave][r1] = v_s[wave][r1] * tails;
       wave_lds_sync();
       float c[K];
 #pragma unroll
