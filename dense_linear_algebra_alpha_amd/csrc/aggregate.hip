@@ -6,10 +6,11 @@
 // kernel's per-workgroup partials (plus, for the CSR path, the columns outside
 // the LDS window: a global accumulator, or the partial rows of the units of the
 // column's bin written by csr_bins.hip). Each 1024-thread workgroup owns COLS columns
-// (64, or 16 for outputs of at most 4096 columns, so that a narrow output still spreads
-// over several CUs); 1024 / COLS thread rows each sum a strided subset of the partials in
-// fp64, and their results are combined in a fixed order, so the result is bitwise
-// reproducible for a given plan.
+// (64; 16 for outputs of at most 4096 columns, so that a narrow output still spreads
+// over several CUs; 256 for outputs wider than 65536 columns, whose binned columns have
+// few partial rows each, so that fewer, fuller workgroups cover them); 1024 / COLS thread
+// rows each sum a strided subset of the partials in fp64, and their results are combined
+// in a fixed order, so the result is bitwise reproducible for a given plan.
 // The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
 // reads z; out may alias z (each element is read before it is written by the
 // same thread).
@@ -20,6 +21,7 @@ namespace {
 
 constexpr int kAggThreads = 1024;
 constexpr int64_t kNarrowOutput = 4096;  // outputs up to this width use 16 columns per workgroup
+constexpr int64_t kWideOutput = 65536;   // outputs beyond this width use 256 columns per workgroup
 
 template <int kAggCols>
 __global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __restrict__ partial, int64_t rows,
@@ -99,8 +101,11 @@ hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, con
   if (n <= kNarrowOutput) {
     hipLaunchKernelGGL(aggregate_kernel<16>, dim3((unsigned)((n + 15) / 16)), dim3(kAggThreads), 0, s, partial,
                        rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
-  } else {
+  } else if (n <= kWideOutput) {
     hipLaunchKernelGGL(aggregate_kernel<64>, dim3((unsigned)((n + 63) / 64)), dim3(kAggThreads), 0, s, partial,
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+  } else {
+    hipLaunchKernelGGL(aggregate_kernel<256>, dim3((unsigned)((n + 255) / 256)), dim3(kAggThreads), 0, s, partial,
                        rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
   }
   return hipGetLastError();

@@ -50,46 +50,65 @@ __global__ __launch_bounds__(kCountThreads) void bin_count_kernel(CsrBinArgs a) 
 
 // Pass 2 (one workgroup): counts -> exclusive offsets in (bin, group) order, the first position
 // of every bin, and the units of every bin (an exclusive scan of the bins' unit counts).
+// The counts pass through LDS in chunks of kScanChunk, loaded and stored coalesced; each thread
+// scans a contiguous segment of a chunk.
+constexpr int kScanChunk = 8192;
+
+// Inclusive sum of x over the threads 0..tid of a kSortThreads workgroup: a scan within each
+// wavefront by lane shuffles, then the wavefronts' totals (two barriers; every thread calls it).
+__device__ int32_t block_inclusive_scan(int32_t x, int32_t* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int32_t t = __shfl_up(x, d, 64);
+    if (lane >= d) x += t;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int32_t before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  __syncthreads();  // wsum may be reused by the next call
+  return x + before;
+}
 __global__ __launch_bounds__(kSortThreads) void bin_scan_kernel(CsrBinArgs a) {
-  __shared__ int32_t part[kSortThreads];
+  __shared__ int32_t chunk_total;
   __shared__ int32_t bstart[kMaxBins + 1];
   __shared__ int32_t ucount[kMaxBins];
+  __shared__ int32_t cs[kScanChunk];
+  __shared__ int32_t wsum[kSortThreads / 64];
   const int tid = threadIdx.x;
   const int total = a.bins * kBinSortGroups;
-  const int per = (total + kSortThreads - 1) / kSortThreads;
-  const int s0 = min(tid * per, total), s1 = min(s0 + per, total);
-  int32_t sum = 0;
-#pragma unroll 8
-  for (int i = s0; i < s1; ++i) sum += a.counts[i];
-  part[tid] = sum;
-  __syncthreads();
-  for (int d = 1; d < kSortThreads; d <<= 1) {  // inclusive scan of the per-thread sums
-    const int32_t t = tid >= d ? part[tid - d] : 0;
+  int32_t carry = 0;  // counts of the chunks before
+  for (int c0 = 0; c0 < total; c0 += kScanChunk) {
+    const int len = min(kScanChunk, total - c0);
+    for (int i = tid; i < len; i += kSortThreads) cs[i] = a.counts[c0 + i];
     __syncthreads();
-    part[tid] += t;
+    const int per = (len + kSortThreads - 1) / kSortThreads;
+    const int s0 = min(tid * per, len), s1 = min(s0 + per, len);
+    int32_t sum = 0;
+    for (int i = s0; i < s1; ++i) sum += cs[i];
+    const int32_t incl = block_inclusive_scan(sum, wsum);  // of the per-thread sums
+    if (tid == kSortThreads - 1) chunk_total = incl;
+    int32_t run = carry + incl - sum;  // exclusive start of this thread's segment
+    for (int i = s0; i < s1; ++i) {
+      const int32_t c = cs[i];
+      cs[i] = run;
+      if ((c0 + i) % kBinSortGroups == 0) bstart[(c0 + i) / kBinSortGroups] = run;  // first position of a bin
+      run += c;
+    }
+    __syncthreads();
+    carry += chunk_total;
+    for (int i = tid; i < len; i += kSortThreads) a.counts[c0 + i] = cs[i];
     __syncthreads();
   }
-  int32_t run = part[tid] - sum;  // exclusive start of this thread's segment
-#pragma unroll 8
-  for (int i = s0; i < s1; ++i) {
-    const int32_t c = a.counts[i];
-    a.counts[i] = run;
-    if (i % kBinSortGroups == 0) bstart[i / kBinSortGroups] = run;  // the first position of bin i / groups
-    run += c;
-  }
-  const int32_t placed = part[kSortThreads - 1];
+  const int32_t placed = carry;
   if (tid == 0) bstart[a.bins] = placed;
   __syncthreads();
   // units of every bin, then their exclusive scan over the bins (at most kMaxBins <= kSortThreads)
   const int32_t mine = tid < a.bins ? (bstart[tid + 1] - bstart[tid] + kBinUnitChunks - 1) / kBinUnitChunks : 0;
-  if (tid < kMaxBins) ucount[tid] = mine;
+  const int32_t uincl = block_inclusive_scan(mine, wsum);
+  if (tid < kMaxBins) ucount[tid] = uincl;
   __syncthreads();
-  for (int d = 1; d < kMaxBins; d <<= 1) {
-    const int32_t t = (tid < kMaxBins && tid >= d) ? ucount[tid - d] : 0;
-    __syncthreads();
-    if (tid < kMaxBins) ucount[tid] += t;
-    __syncthreads();
-  }
   if (tid < a.bins) {
     a.bin_start[tid] = bstart[tid];
     a.unit_start[tid] = ucount[tid] - mine;
