@@ -77,7 +77,8 @@ class HipEvents:
 
 def kernel_sources_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
-    files = ["device_util.h", "internal.h"] + {"csr": ["csr.hip"], "csr_waves": ["csr_waves.hip"]}.get(kind, ["dense.hip"])
+    files = ["device_util.h", "internal.h"] + {"csr": ["csr_common.h", "csr.hip"],
+                                                "csr_waves": ["csr_common.h", "csr_waves.hip"]}.get(kind, ["dense.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:

@@ -23,7 +23,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "model.cpp", "unfused.cpp", "logreg.cpp", "tune.cpp", "dense.hip", "csr.hip", "csr_waves.hip", "csr_bins.hip",
            "aggregate.hip", "logreg.hip"]
-HEADERS = ["internal.h", "device_util.h"]
+HEADERS = ["internal.h", "device_util.h", "csr_common.h"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -45,47 +45,16 @@
 // (row_ptr, v, marks, dots) is double-buffered, so a tile costs two workgroup
 // barriers: one between the dots and the scatter, one that publishes the next
 // tile's state and counts its rows.
+#include "csr_common.h"
 #include "device_util.h"
 #include "internal.h"
 
 namespace xtvxy {
 namespace {
 
-
-typedef __attribute__((address_space(1))) float global_float;
-typedef __attribute__((address_space(1))) uint32_t global_uint;
 typedef int32_t i4 __attribute__((ext_vector_type(4)));
 typedef int32_t i2 __attribute__((ext_vector_type(2)));
 
-// Smallest r in [0, m] with rp[r] >= target (m when none), by one full wavefront.
-__device__ int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64_t m, int64_t target) {
-  const int lane = threadIdx.x & 63;
-  if (target <= 0) return 0;
-  int64_t lo = 0, hi = m;  // the answer lies in [lo, hi]; position hi counts as ">= target"
-  while (hi - lo > 64) {
-    const int64_t step = (hi - lo + 63) / 64;
-    const int64_t probe = min(lo + (int64_t)(lane + 1) * step, hi);
-    const bool ge = (probe >= hi) || ((int64_t)rp[probe] >= target);
-    const uint64_t mask = __ballot(ge);
-    const int k = __ffsll((unsigned long long)mask) - 1;  // lane 63 always qualifies
-    const int64_t nhi = __shfl(probe, k, 64);
-    const int64_t nlo = (k == 0) ? lo : __shfl(probe, k - 1, 64) + 1;
-    lo = nlo;
-    hi = nhi;
-  }
-  const int64_t probe = lo + lane;
-  const bool ge = (probe >= hi) || ((int64_t)rp[probe] >= target);
-  const uint64_t mask = __ballot(ge);
-  if (mask == 0) return hi;
-  return min(lo + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi);
-}
-
-// Columns outside the LDS window: none (the window holds all of them), global float
-// atomics, or binned (see csr_bins.hip).
-enum ColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
-// Where y is gathered from: global memory, an LDS copy of all of it, or an LDS copy of
-// y[0, y_window) and global memory beyond.
-enum YMode { kYGlobal = 0, kYLds = 1, kYSplit = 2 };
 // What the kernel computes: the whole pattern (partials of X^T (v .* (X y))), only its first
 // half (t = alpha v .* (X y) + beta t0, written per row), or only its second half (partials of
 // X^T u, with u given in place of v and no y).

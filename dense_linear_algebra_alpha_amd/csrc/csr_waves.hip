@@ -31,19 +31,15 @@
 // processed, and its y gathers are issued at the end of the step, as in the
 // tiled kernel (no branch around loads issued ahead: the vector-memory counter
 // completes in order).
+#include "csr_common.h"
 #include "device_util.h"
 #include "internal.h"
 
 namespace xtvxy {
 namespace {
 
-typedef __attribute__((address_space(1))) float global_float;
-typedef __attribute__((address_space(1))) uint32_t global_uint;
 typedef int32_t i4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-
-enum ColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
-enum YMode { kYGlobal = 0, kYLds = 1, kYSplit = 2 };
 
 // The wavefront's LDS writes made visible to its own later LDS reads: a wavefront's LDS
 // operations complete in order, so only the compiler has to be kept from moving accesses
@@ -52,29 +48,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Smallest r in [0, m] with rp[r] >= target (m when none), by one full wavefront.
-__device__ int64_t lower_bound_wave(const int32_t* __restrict__ rp, int64_t m, int64_t target) {
-  const int lane = threadIdx.x & 63;
-  if (target <= 0) return 0;
-  int64_t lo = 0, hi = m;  // the answer lies in [lo, hi]; position hi counts as ">= target"
-  while (hi - lo > 64) {
-    const int64_t step = (hi - lo + 63) / 64;
-    const int64_t probe = min(lo + (int64_t)(lane + 1) * step, hi);
-    const bool ge = (probe >= hi) || ((int64_t)rp[probe] >= target);
-    const uint64_t mask = __ballot(ge);
-    const int k = __ffsll((unsigned long long)mask) - 1;  // lane 63 always qualifies
-    const int64_t nhi = __shfl(probe, k, 64);
-    const int64_t nlo = (k == 0) ? lo : __shfl(probe, k - 1, 64) + 1;
-    lo = nlo;
-    hi = nhi;
-  }
-  const int64_t probe = lo + lane;
-  const bool ge = (probe >= hi) || ((int64_t)rp[probe] >= target);
-  const uint64_t mask = __ballot(ge);
-  if (mask == 0) return hi;
-  return min(lo + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi);
 }
 
 // The loads of one tile, held in registers while the previous tile is processed.
@@ -280,8 +253,8 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   const int64_t G = (int64_t)gridDim.x * NW;
   const int64_t gw = (int64_t)blockIdx.x * NW + wave;
   const int64_t q = (a.nnz + G - 1) / G;
-  const int32_t rb = (int32_t)lower_bound_wave(a.row_ptr, a.m, gw * q);
-  const int32_t re = (gw + 1 == G) ? (int32_t)a.m : (int32_t)lower_bound_wave(a.row_ptr, a.m, (gw + 1) * q);
+  const int32_t rb = (int32_t)wave_lower_bound(a.row_ptr, a.m, gw * q);
+  const int32_t re = (gw + 1 == G) ? (int32_t)a.m : (int32_t)wave_lower_bound(a.row_ptr, a.m, (gw + 1) * q);
 
   auto issue = [&](int32_t r, int32_t re_, uint32_t first_entry, WaveTile<K>& g) {
     g.rp = a.row_ptr[min(r + lane, re_)];
