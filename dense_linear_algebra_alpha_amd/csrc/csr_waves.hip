@@ -277,8 +277,10 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
     const bool more = r_next < re;
     const uint32_t e0 = base + (uint32_t)lane * K;
     const uint32_t len = pb - pa;
-    // the next tile's row_ptr, v and entries (they start where this tile ends)
-    issue(min(r_next, re - 1), re, pb, gn);
+    // the next tile's row_ptr, v and entries (they start where this tile ends); after the last
+    // tile the same loads read this tile's entries again (cached) instead of the next
+    // wavefront's, with no branch around them
+    issue(min(r_next, re - 1), re, more ? pb : pa, gn);
     if constexpr (!kGatherAhead) {
 #pragma unroll
       for (int k = 0; k < K; ++k) g.yv[k] = gather_y(g.col[k]);
