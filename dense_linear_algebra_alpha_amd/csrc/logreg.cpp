@@ -192,6 +192,27 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
       if ((st = launched(launch_lr_dots(n, 2, x, y, 1, part, stream))) != XTVXY_SUCCESS) return st;
     }
     if ((st = launched(launch_lr_finish(kLrObjective, part, m, n, S, 0.0, lam, stream))) != XTVXY_SUCCESS) return st;
+    // CG on H s = -g: with fixed_cg the iterations are enqueued back to back and read once; the
+    // stops that do not depend on the residual test (non-positive curvature, an exactly vanished
+    // residual) are taken on the device, which then leaves the remaining iterations without
+    // effect. Without a gradient tolerance (grad_tol == 0) nothing can stop the solve before the
+    // step limit but g == 0, which CG meets as a vanished residual, so the fixed solve is
+    // enqueued right behind the gradient and one read-back serves both (the CG kernels leave
+    // f, g.g and w.w in the scalars as they are).
+    auto enqueue_cg = [&](double eps) -> xtvxy_status {
+      xtvxy_status e;
+      if ((e = launched(launch_lr_cg_init(n, g, s, r, d, S, stream))) != XTVXY_SUCCESS) return e;
+      for (int j = 0; j < opt->max_cg; ++j) {
+        if ((e = E.hvp(v, lam, d, q)) != XTVXY_SUCCESS) return e;
+        if ((e = launched(launch_lr_cg_step(n, q, d, s, r, S, j == 0, part, stream))) != XTVXY_SUCCESS) return e;
+        if (opt->fixed_cg) continue;
+        if ((e = read_scalars()) != XTVXY_SUCCESS) return e;
+        if (h.neg || h.done || std::sqrt(h.rr) < eps) break;
+      }
+      return XTVXY_SUCCESS;
+    };
+    const bool cg_ahead = opt->fixed_cg && opt->grad_tol == 0.0 && k < opt->max_newton;
+    if (cg_ahead && (st = enqueue_cg(0.0)) != XTVXY_SUCCESS) return st;
     if ((st = read_scalars()) != XTVXY_SUCCESS) return st;
     const double f = h.f, gnorm = std::sqrt(h.gg);
     if (k == 0) {
@@ -209,20 +230,11 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
       break;
     }
     if (k == opt->max_newton) break;
-    // ---- CG on H s = -g
-    const double eps = std::fmin(opt->cg_forcing, std::sqrt(gnorm)) * gnorm;
-    if ((st = launched(launch_lr_cg_init(n, g, s, r, d, S, stream))) != XTVXY_SUCCESS) return st;
-    // With fixed_cg the iterations are enqueued back to back and read once: the stops that do
-    // not depend on the residual test (non-positive curvature, an exactly vanished residual) are
-    // taken on the device, which then leaves the remaining iterations without effect.
-    for (int j = 0; j < opt->max_cg; ++j) {
-      if ((st = E.hvp(v, lam, d, q)) != XTVXY_SUCCESS) return st;
-      if ((st = launched(launch_lr_cg_step(n, q, d, s, r, S, j == 0, part, stream))) != XTVXY_SUCCESS) return st;
-      if (opt->fixed_cg) continue;
-      if ((st = read_scalars()) != XTVXY_SUCCESS) return st;
-      if (h.neg || h.done || std::sqrt(h.rr) < eps) break;
+    if (!cg_ahead) {
+      const double eps = std::fmin(opt->cg_forcing, std::sqrt(gnorm)) * gnorm;
+      if ((st = enqueue_cg(eps)) != XTVXY_SUCCESS) return st;
+      if (opt->fixed_cg && (st = read_scalars()) != XTVXY_SUCCESS) return st;
     }
-    if (opt->fixed_cg && (st = read_scalars()) != XTVXY_SUCCESS) return st;
     const int used = h.iters;
     rep.cg_iterations += used;
     record(k, 2, used);

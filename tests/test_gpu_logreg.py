@@ -87,6 +87,28 @@ def test_fixed_schedule_matches_oracle(engine, m, n, mean_len, lam, soft):
 
 
 @pytest.mark.parametrize("engine", ["fused", "unfused"])
+def test_fixed_schedule_reads_back_once_per_stage_or_not(engine):
+    """With grad_tol == 0 the fixed CG solve is enqueued behind the gradient and both are read back
+    once; a tolerance too small to stop on (1e-30) takes the path that reads the gradient first.
+    Same kernels in the same order: the same steps, counts and iterates (to the run-to-run
+    variation of the CSR sums' order)."""
+    rp, ci, vals, n, labels, lam = small_problem(4000, 200, 21, 0.7, mean_len=8.0)
+    d = LogregOnDevice(rp, ci, vals, n, labels)
+    note("logreg fixed schedule read-backs %s" % engine)
+    w1, rep1, hist1 = d.solve(lam, None, engine, max_newton=4, max_cg=3, fixed_cg=True, grad_tol=0.0)
+    w2, rep2, hist2 = d.solve(lam, None, engine, max_newton=4, max_cg=3, fixed_cg=True, grad_tol=1e-30)
+    for key in ("status", "newton_iterations", "cg_iterations", "line_search_trials"):
+        assert rep1[key] == rep2[key], key
+    def same(x, y):  # rows after the last step hold NaN for the CG and line-search fields
+        return (x is None and y is None) or x == y or (np.isnan(x) and np.isnan(y))
+
+    for a, b in zip(hist1, hist2):
+        assert abs(a["loss"] - b["loss"]) <= 1e-9 * abs(b["loss"]), (a, b)
+        assert same(a.get("cg"), b.get("cg")) and same(a.get("step"), b.get("step")), (a, b)
+    assert np.max(np.abs(w1 - w2)) <= 1e-5 * max(np.max(np.abs(w2)), 1e-30)
+
+
+@pytest.mark.parametrize("engine", ["fused", "unfused"])
 def test_fixed_schedule_from_a_far_start_backtracks(engine):
     prob = small_problem(2000, 30, 11, 0.3, mean_len=4.0)
     w0 = np.random.Generator(np.random.PCG64(3)).normal(0, 6.0, 30)
