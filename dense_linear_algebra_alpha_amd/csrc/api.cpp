@@ -272,7 +272,6 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   st = csr_plan_for(m, n, nnz, d, force, &plan, mode == kCsrFused);
   if (st != XTVXY_SUCCESS) return st;
   if (mode == kCsrTmv && plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
-  if (mode != kCsrFused && plan.kernel != XTVXY_CSR_TILES) return XTVXY_ERROR_INVALID_VALUE;
   if (mode == kCsrTmv && plan.y_window != 0) {  // no y to gather: the plan with no y window
     plan.y_window = 0;
     st = complete_csr(m, n, nnz, d, &plan);
@@ -332,7 +331,7 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   }
   const hipEvent_t before = g_before_main, after = g_after_main;
   if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = plan.kernel == XTVXY_CSR_WAVES ? launch_csr_waves(a, plan, stream) : launch_csr(a, plan, stream, mode);
+  e = plan.kernel == XTVXY_CSR_WAVES ? launch_csr_waves(a, plan, stream, mode) : launch_csr(a, plan, stream, mode);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   BinPartials bp{bargs.partial2, bargs.unit_start, plan.lds_window, w.bin_shift};
@@ -406,7 +405,7 @@ xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const i
   xtvxy_launch_params plan;
   st = csr_plan_for(m, n, nnz, d, force, &plan, false);
   if (st != XTVXY_SUCCESS) return st;
-  if (plan.entries_per_thread != 8 || plan.kernel != XTVXY_CSR_TILES) return XTVXY_ERROR_INVALID_VALUE;
+  if (plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
   // no scatter: no output window, no bins (the LDS left holds the y window)
   plan.lds_window = 0;
   plan.bin_columns = 0;
@@ -430,7 +429,9 @@ xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const i
   a.t_out = t;
   const hipEvent_t before = g_before_main, after = g_after_main;
   if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  if (launch_csr(a, plan, stream, kCsrRowdot) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  const hipError_t e = plan.kernel == XTVXY_CSR_WAVES ? launch_csr_waves(a, plan, stream, kCsrRowdot)
+                                                      : launch_csr(a, plan, stream, kCsrRowdot);
+  if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   return XTVXY_SUCCESS;
 }

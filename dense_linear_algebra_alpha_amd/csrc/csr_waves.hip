@@ -61,13 +61,21 @@ struct WaveTile {
   float v;      // v[r + lane]
 };
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+// What the kernel computes: the whole pattern (partials of X^T (v .* (X y))), its first half
+// alone (t = alpha v .* (X y) + beta t0 per row, no scatter) or its second half alone (partials
+// of X^T u, u given in place of v, no y and no dots).
+enum WaveMode { kWaveFused = 0, kWaveRowdot = 1, kWaveTmv = 2 };
+
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512 || BLK == 1024, "workgroups of 256, 512 or 1024 threads");
   static_assert(K == 8, "eight entries per lane: two 16-byte vectors, one 8-byte word of marks");
   constexpr int NW = BLK / 64;  // wavefronts of the workgroup
   constexpr int TW = 64 * K;    // entry slots of a wavefront's tile
   constexpr bool BINNED = COLD == kColdBinned;
+  constexpr bool kGathers = MODE != kWaveTmv;     // the second half alone reads no y
+  constexpr bool kScatter = MODE != kWaveRowdot;  // the first half alone writes rows, not columns
+  static_assert(kScatter || COLD == kColdNone, "the first half alone has no window and no bins");
   constexpr uint32_t S = kBinChunkItems;
   __shared__ __align__(16) uint8_t mark_s[NW][TW];  // 1 + tile row whose first entry sits at slot q, else 0
   __shared__ float u_s[NW][64];                     // u_row = v_row * dot of the tile's rows
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
     g.v = HAS_V ? a.v[min(r + lane, re_ - 1)] : 1.0f;
     load_clamped(first_entry & ~3u, g.val, g.col);
   };
-  constexpr bool kGatherAhead = YMODE != kYLds;
+  constexpr bool kGatherAhead = kGathers && YMODE != kYLds;
 
   int32_t r = rb;
   auto step = [&](WaveTile<K>& g, WaveTile<K>& gn) -> bool {
@@ -281,7 +289,7 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
     // tile the same loads read this tile's entries again (cached) instead of the next
     // wavefront's, with no branch around them
     issue(min(r_next, re - 1), re, more ? pb : pa, gn);
-    if constexpr (!kGatherAhead) {
+    if constexpr (kGathers && !kGatherAhead) {
 #pragma unroll
       for (int k = 0; k < K; ++k) g.yv[k] = gather_y(g.col[k]);
     }
@@ -294,58 +302,67 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       // The wavefront takes the row in slices of TW entries, twice (the dot, then the scatter);
       // the first slice is in registers for the dot, and each later slice is requested while
       // the one before is used.
-      float s = 0.0f;
-#pragma unroll
-      for (int k = 0; k < K; ++k) s += ok[k] ? g.val[k] * g.yv[k] : 0.0f;
       float hv[K], nv[K];
       int32_t hc[K], nc[K];
-      uint32_t sb = base + TW;  // < pb: the row does not fit one tile
-      load_slice(sb, hv, hc);
-      while (true) {
-        float yy[K];
+      uint32_t sb;
+      float u = __shfl(g.v, 0, 64);  // v of the row; the given u when the second half runs alone
+      if constexpr (kGathers) {
+        float s = 0.0f;
 #pragma unroll
-        for (int k = 0; k < K; ++k) yy[k] = gather_y(hc[k]);
-        const uint32_t nb = sb + TW;
-        load_slice(nb, nv, nc);
-        const uint32_t h0 = sb + (uint32_t)lane * K;
+        for (int k = 0; k < K; ++k) s += ok[k] ? g.val[k] * g.yv[k] : 0.0f;
+        sb = base + TW;  // < pb: the row does not fit one tile
+        load_slice(sb, hv, hc);
+        while (true) {
+          float yy[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * yy[k] : 0.0f;
-        if (nb >= pb) break;
-        sb = nb;
+          for (int k = 0; k < K; ++k) yy[k] = gather_y(hc[k]);
+          const uint32_t nb = sb + TW;
+          load_slice(nb, nv, nc);
+          const uint32_t h0 = sb + (uint32_t)lane * K;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          hv[k] = nv[k];
-          hc[k] = nc[k];
+          for (int k = 0; k < K; ++k) s += (h0 + k < pb) ? hv[k] * yy[k] : 0.0f;
+          if (nb >= pb) break;
+          sb = nb;
+#pragma unroll
+          for (int k = 0; k < K; ++k) {
+            hv[k] = nv[k];
+            hc[k] = nc[k];
+          }
         }
+        u *= group_sum(s, 64);
       }
-      // the scatter reloads the first slice too, so that its registers are free in the loops
-      sb = base;
-      load_slice(sb, hv, hc);
-      const float u = __shfl(g.v, 0, 64) * group_sum(s, 64);
-      while (true) {
-        const uint32_t nb = sb + TW;
-        load_slice(nb, nv, nc);
-        const uint32_t h0 = sb + (uint32_t)lane * K;
-        float c[K];
-        bool on[K];
+      if constexpr (MODE == kWaveRowdot) {
+        if (lane == 0) a.t_out[r] = a.alpha * u + (a.beta != 0.0f ? a.beta * a.t0[r] : 0.0f);
+      } else {
+        // the scatter reloads the first slice too, so that its registers are free in the loops
+        sb = base;
+        load_slice(sb, hv, hc);
+        while (true) {
+          const uint32_t nb = sb + TW;
+          load_slice(nb, nv, nc);
+          const uint32_t h0 = sb + (uint32_t)lane * K;
+          float c[K];
+          bool on[K];
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          on[k] = h0 + k - pa < len;  // unsigned: positions before pa wrap
-          c[k] = u * hv[k];
-        }
-        scatter_k(c, hc, on);
-        if (nb >= pb) break;
-        sb = nb;
+          for (int k = 0; k < K; ++k) {
+            on[k] = h0 + k - pa < len;  // unsigned: positions before pa wrap
+            c[k] = u * hv[k];
+          }
+          scatter_k(c, hc, on);
+          if (nb >= pb) break;
+          sb = nb;
 #pragma unroll
-        for (int k = 0; k < K; ++k) {
-          hv[k] = nv[k];
-          hc[k] = nc[k];
+          for (int k = 0; k < K; ++k) {
+            hv[k] = nv[k];
+            hc[k] = nc[k];
+          }
         }
       }
     } else {
       // row-start marks of the tile's nonempty rows, and v of its rows
       if (lane < R && g.rp1 > g.rp) mark_s[wave][(uint32_t)g.rp - base] = (uint8_t)(lane + 1);
       v_s[wave][lane] = g.v;
+      if constexpr (MODE == kWaveRowdot) u_s[wave][lane] = 0.0f;  // empty rows get t = beta t0
       wave_lds_sync();
       int mk[K];
       {
@@ -375,6 +392,9 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       // across the wavefront. Every row ends inside the tile, so each gets one write. Slots
       // outside the tile belong to its first row (before it) or its last nonempty row (after
       // it) and add a zero product there, so the row logic needs no mask.
+      if constexpr (MODE == kWaveTmv) {
+        u_s[wave][lane] = g.v;  // the given u of the tile's rows
+      } else {
       float pk[K];
 #pragma unroll
       for (int k = 0; k < K; ++k) pk[k] = ok[k] ? g.val[k] * g.yv[k] : 0.0f;
@@ -393,11 +413,16 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       const int next_r0 = dpp_int<dpp::kWaveShl1>(-1, r0);
       if (r0 != r1) u_s[wave][r0] = v_s[wave][r0] * (head + (prev_key == r0 ? prev_tails : 0.0f));
       if (next_r0 != r1) u_s[wave][r1] = v_s[wave][r1] * tails;
+      }
       wave_lds_sync();
-      float c[K];
+      if constexpr (MODE == kWaveRowdot) {
+        if (lane < R) a.t_out[r + lane] = a.alpha * u_s[wave][lane] + (a.beta != 0.0f ? a.beta * a.t0[r + lane] : 0.0f);
+      } else {
+        float c[K];
 #pragma unroll
-      for (int k = 0; k < K; ++k) c[k] = u_s[wave][rk[k]] * g.val[k];
-      scatter_k(c, g.col, ok);
+        for (int k = 0; k < K; ++k) c[k] = u_s[wave][rk[k]] * g.val[k];
+        scatter_k(c, g.col, ok);
+      }
     }
     if (!more) return false;
     // the next tile's y gathers, a step ahead
@@ -435,41 +460,62 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   }
 }
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD>
+template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 hipError_t launch_w(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const size_t lds = csr_waves_dynamic_lds(a.lds_window, YMODE == kYGlobal ? 0 : a.y_window, a.bins, BLK);
-  const void* fn = reinterpret_cast<const void*>(&csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD>);
+  const void* fn = reinterpret_cast<const void*>(&csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD>), dim3((unsigned)p.grid), dim3(BLK), lds, s, a);
+  hipLaunchKernelGGL((csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
+                     s, a);
   return hipGetLastError();
 }
 
-template <int BLK, int K, int YMODE, int COLD>
+template <int BLK, int K, int YMODE, int COLD, int MODE>
 hipError_t launch_wv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const bool al = a.aligned && a.nnz >= 4;  // 16-byte loads need one whole quad of entries
-  if (a.v != nullptr)
-    return al ? launch_w<BLK, K, YMODE, true, true, COLD>(a, p, s) : launch_w<BLK, K, YMODE, true, false, COLD>(a, p, s);
-  return al ? launch_w<BLK, K, YMODE, false, true, COLD>(a, p, s) : launch_w<BLK, K, YMODE, false, false, COLD>(a, p, s);
+  if (MODE == kWaveTmv || a.v != nullptr)   // u is always given to the second half
+    return al ? launch_w<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+              : launch_w<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+  if constexpr (MODE != kWaveTmv)
+    return al ? launch_w<BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
+              : launch_w<BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
+  return hipErrorInvalidValue;
 }
 
-template <int BLK, int K, int COLD>
+template <int BLK, int K, int COLD, int MODE>
 hipError_t launch_wy(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.y_window >= a.n) return launch_wv<BLK, K, kYLds, COLD>(a, p, s);
-  if (a.y_window > 0) return launch_wv<BLK, K, kYSplit, COLD>(a, p, s);
-  return launch_wv<BLK, K, kYGlobal, COLD>(a, p, s);
+  if constexpr (MODE == kWaveTmv) {
+    return launch_wv<BLK, K, kYGlobal, COLD, MODE>(a, p, s);  // no y
+  } else {
+    if (a.y_window >= a.n) return launch_wv<BLK, K, kYLds, COLD, MODE>(a, p, s);
+    if (a.y_window > 0) return launch_wv<BLK, K, kYSplit, COLD, MODE>(a, p, s);
+    return launch_wv<BLK, K, kYGlobal, COLD, MODE>(a, p, s);
+  }
 }
 
-template <int BLK, int K>
+template <int BLK, int K, int MODE>
 hipError_t launch_wc(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (a.bins > 0) return launch_wy<BLK, K, kColdBinned>(a, p, s);
-  if (a.lds_window < a.n) return launch_wy<BLK, K, kColdAtomic>(a, p, s);
-  return launch_wy<BLK, K, kColdNone>(a, p, s);
+  if constexpr (MODE == kWaveRowdot) {
+    return launch_wy<BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
+  } else {
+    if (a.bins > 0) return launch_wy<BLK, K, kColdBinned, MODE>(a, p, s);
+    if (a.lds_window < a.n) return launch_wy<BLK, K, kColdAtomic, MODE>(a, p, s);
+    return launch_wy<BLK, K, kColdNone, MODE>(a, p, s);
+  }
+}
+
+template <int MODE>
+hipError_t launch_wb(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+  if (p.block_threads == 256) return launch_wc<256, 8, MODE>(a, p, s);
+  if (p.block_threads == 512) return launch_wc<512, 8, MODE>(a, p, s);
+  if (p.block_threads == 1024) return launch_wc<1024, 8, MODE>(a, p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
+hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode) {
   if (p.grid <= 0 || p.grid > INT32_MAX || p.kernel != XTVXY_CSR_WAVES || p.entries_per_thread != 8)
     return hipErrorInvalidValue;
   if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
@@ -479,11 +525,19 @@ hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipS
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
+  if (mode == kCsrRowdot) {
+    // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
+    if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))
+      return hipErrorInvalidValue;
+    return launch_wb<kWaveRowdot>(a, p, s);
+  }
   if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
-  if (p.block_threads == 256) return launch_wc<256, 8>(a, p, s);
-  if (p.block_threads == 512) return launch_wc<512, 8>(a, p, s);
-  if (p.block_threads == 1024) return launch_wc<1024, 8>(a, p, s);
-  return hipErrorInvalidValue;
+  if (mode == kCsrTmv) {
+    if (a.v == nullptr) return hipErrorInvalidValue;  // u
+    return launch_wb<kWaveTmv>(a, p, s);
+  }
+  if (mode != kCsrFused) return hipErrorInvalidValue;
+  return launch_wb<kWaveFused>(a, p, s);
 }
 
 }  // namespace xtvxy

@@ -110,8 +110,8 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
 // as v, no y).
 enum CsrLaunchMode { kCsrFused = 0, kCsrRowdot = 1, kCsrTmv = 2 };
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
-// The whole pattern's partials by the wavefront kernel (plan kernel XTVXY_CSR_WAVES).
-hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
+// The same launches by the wavefront kernel (plan kernel XTVXY_CSR_WAVES).
+hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
 // Bin passes: group the handed-out chunks by bin, then accumulate every unit of a bin in LDS.
 hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s);
 // Per-bin partial sums for the aggregation (null: no binning).
@@ -148,7 +148,7 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
 xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
                             xtvxy_launch_params* p, int elem_bytes = 4);
 // fused: the plan is for the whole pattern (the wavefront kernel is a candidate); else for one
-// of its halves (workgroup tiles only).
+// of its halves alone (workgroup tiles).
 xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                        xtvxy_launch_params* p, bool fused = true);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,

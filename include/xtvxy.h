@@ -215,8 +215,8 @@ xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
  * no workspace. tmv: u required when alpha != 0 and m, nnz > 0; z read only when beta != 0 and
  * may equal out; the workspace of xtvxy_csr_f32_workspace_size(m, n, nnz) suffices (with _ex:
  * force->workspace_bytes after xtvxy_csr_f32_plan_complete). The _ex forms take a launch plan
- * (entries_per_thread must be 8; rowdot ignores lds_window and bin_columns, tmv y_window).
- * Asynchronous on `stream`. */
+ * (entries_per_thread must be 8; rowdot ignores lds_window and bin_columns, tmv y_window; either
+ * CSR kernel; without a plan the workgroup-tile kernel runs). Asynchronous on `stream`. */
 xtvxy_status xtvxy_csr_f32_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
                                   const int32_t *col_idx, const float *values, const float *v, const float *y,
                                   float beta, const float *t0, float *t, hipStream_t stream);

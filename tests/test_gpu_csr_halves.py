@@ -59,6 +59,23 @@ def half_plans(m, n, nnz):
                                             grid=grid, vec=1, chunks=1, group=1, lds_window=w, y_window=yw,
                                             bin_columns=bc)
                 out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
+    return out + wave_half_plans(m, n, nnz)
+
+
+def wave_half_plans(m, n, nnz):
+    """The same windows for the wavefront kernel (256, 512 and 1024 threads)."""
+    out = []
+    for blk in (256, 512, 1024):
+        for grid in (1, 7, 256):
+            for w, yw, bc in sorted({(0, 0, 0), (min(n, 300), min(n, 300), 0), (min(n, 4096), 0, 0),
+                                     (min(n, 300), n, 1024 if n > 300 else 0), (n, n, 0)}):
+                bins = -(-(n - w) // bc) if bc else 0
+                if (w + yw) * 4 + 20480 + 16 * 24 * bins > 163840:
+                    continue
+                lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_WAVES, block_threads=blk, entries_per_thread=8,
+                                            grid=grid, vec=1, chunks=1, group=1, lds_window=w, y_window=yw,
+                                            bin_columns=bc)
+                out.append(xt.xtvxy_csr_f32_plan_complete(m, n, nnz, lp))
     return out
 
 
@@ -87,8 +104,9 @@ def test_halves_with_rows_longer_than_a_tile_and_empty_runs():
     t0, u = aux(p, 3)
     rowdot_case(p, d, t0, 2.0, 1.0)
     tmv_case(p, d, u, -1.0, 0.25)
-    for blk in (256, 512):
-        lp = xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_TILES, block_threads=blk, entries_per_thread=8, grid=9,
+    for kernel, blk in ((xt.XTVXY_CSR_TILES, 256), (xt.XTVXY_CSR_TILES, 512), (xt.XTVXY_CSR_WAVES, 256),
+                        (xt.XTVXY_CSR_WAVES, 1024)):
+        lp = xt.xtvxy_launch_params(kernel=kernel, block_threads=blk, entries_per_thread=8, grid=9,
                                     vec=1, chunks=1, group=1, lds_window=500, y_window=700, bin_columns=1024)
         plan = xt.xtvxy_csr_f32_plan_complete(m, n, p.nnz, lp)
         rowdot_case(p, d, t0, 2.0, 1.0, plan=plan, what="long rows forced")

@@ -103,7 +103,7 @@ def test_fixed_schedule_reads_back_once_per_stage_or_not(engine):
         return (x is None and y is None) or x == y or (np.isnan(x) and np.isnan(y))
 
     for a, b in zip(hist1, hist2):
-        assert abs(a["loss"] - b["loss"]) <= 1e-9 * abs(b["loss"]), (a, b)
+        assert abs(a["loss"] - b["loss"]) <= 1e-7 * abs(b["loss"]), (a, b)  # the sums' order varies
         assert same(a.get("cg"), b.get("cg")) and same(a.get("step"), b.get("step")), (a, b)
     assert np.max(np.abs(w1 - w2)) <= 1e-5 * max(np.max(np.abs(w2)), 1e-30)
 
