@@ -280,6 +280,43 @@ def check_bound(lib):
     assert np.array_equal(b, [7.0, 10.5])
 
 
+def check_csr_bound(lib):
+    """The CSR normaliser D_j on its own: a hand-derived example with mixed signs everywhere, an
+    empty row and a repeated column; equality with the dense normaliser of the same matrix (pinned
+    by check_bound); D >= |value|; and D equal to the value when every input is non-negative."""
+    for name in golden_names():
+        g = read_golden(name)
+        if "expected_bound" not in g:
+            continue
+        bnd = _csr(lib, g["row_ptr"], g["col_idx"], g["values"], g["n"], g["y"], g.get("v"), g.get("z"),
+                   g["alpha"], g["beta"], bound=True)
+        assert np.array_equal(bnd, g["expected_bound"]), (name, bnd, g["expected_bound"])
+    # the same matrix stored densely: same sums in the same order (zeros add exactly), so the
+    # CSR and dense normalisers agree bit for bit, for signed alpha, beta, v, y, z
+    m, n = 90, 41
+    p = datagen.dense_problem(m, n, seed=31)
+    X = p.X2d().copy()
+    X[np.random.default_rng(32).random((m, n)) < 0.75] = 0.0
+    X[[3, 40]] = 0.0                                   # empty rows
+    rp, ci, vals = _dense_to_csr(X)
+    for alpha, beta, v in ((-1.25, -0.5, p.v), (0.75, 2.0, None), (1.0, 0.0, p.v)):
+        z = p.z if beta != 0.0 else None
+        a = _dense(lib, X, p.y, v, z, alpha, beta, bound=True)
+        b = _csr(lib, rp, ci, vals, n, p.y, v, z, alpha, beta, bound=True)
+        assert np.array_equal(a, b), (alpha, beta)
+    # D >= |value| on an irregular matrix (empty rows, repeated columns), and D == value on
+    # non-negative inputs with alpha, beta > 0
+    c = datagen.csr_random(300, 70, seed=33, mean_len=6.0, empty_frac=0.2, dup_frac=0.3)
+    for alpha, beta in ((-0.7, -1.5), (2.0, 0.25)):
+        ref = _csr(lib, c.row_ptr, c.col_idx, c.values, 70, c.y, c.v, c.z, alpha, beta)
+        bnd = _csr(lib, c.row_ptr, c.col_idx, c.values, 70, c.y, c.v, c.z, alpha, beta, bound=True)
+        assert np.all(bnd >= np.abs(ref))
+    pos = [np.abs(t) for t in (c.values, c.y, c.v, c.z)]
+    assert np.array_equal(_csr(lib, c.row_ptr, c.col_idx, pos[0], 70, pos[1], pos[2], pos[3], 1.5, 0.5),
+                          _csr(lib, c.row_ptr, c.col_idx, pos[0], 70, pos[1], pos[2], pos[3], 1.5, 0.5,
+                               bound=True))
+
+
 def check_thread_independence(lib):
     p = datagen.dense_problem(3001, 37, seed=15)
     c = datagen.csr_random(3001, 37, seed=15, mean_len=6.0)
@@ -446,7 +483,7 @@ def check_bf16_equals_the_widened_matrix(lib):
 
 CHECKS = [check_golden, check_brute_force_dense, check_brute_force_csr, check_exact_integers,
           check_closed_forms, check_special_cases, check_invariants, check_csr_dense_agree,
-          check_nan_propagation, check_scipy, check_bound, check_thread_independence,
+          check_nan_propagation, check_scipy, check_bound, check_csr_bound, check_thread_independence,
           check_error_codes, check_halves_golden, check_halves_explicit_matrix,
           check_halves_compose_into_the_pattern, check_halves_special_cases, check_halves_bounds,
           check_bf16_worked_example, check_bf16_equals_the_widened_matrix]

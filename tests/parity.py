@@ -26,7 +26,7 @@ def read_golden(name: str) -> dict:
                 out[key] = float(vals[0])
             elif key in ("row_ptr", "col_idx"):
                 out[key] = np.array([int(x) for x in vals], dtype=np.int32)
-            elif key == "expected":
+            elif key.startswith("expected"):
                 out[key] = np.array([float(x) for x in vals], dtype=np.float64)
             else:
                 out[key] = np.array([float(x) for x in vals], dtype=np.float32)

@@ -49,6 +49,20 @@ MUTATIONS = [
     ("quick_return_ignores_beta", "(beta == 0.0f) ? 0.0 : val((double)beta, absolute) * val((double)z[j], absolute)",
      "(beta == 0.0f) ? 0.0 : val((double)z[j], absolute)", 0),
     ("bound_keeps_signs", "return absolute ? std::fabs(x) : x;", "return x;", 0),
+    # the CSR normaliser alone (every CSR parity verdict divides by it)
+    ("csr_bound_y_keeps_sign", "t += val((double)values[p], absolute) * val((double)y[col_idx[p]], absolute);",
+     "t += val((double)values[p], absolute) * (double)y[col_idx[p]];", 0),
+    ("csr_bound_step1_values_keep_sign",
+     "t += val((double)values[p], absolute) * val((double)y[col_idx[p]], absolute);",
+     "t += (double)values[p] * val((double)y[col_idx[p]], absolute);", 0),
+    ("csr_bound_step3_values_keep_sign", "S[(size_t)col_idx[p]] += val((double)values[p], absolute) * ui;",
+     "S[(size_t)col_idx[p]] += (double)values[p] * ui;", 0),
+    ("csr_bound_v_keeps_sign", "const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);",
+     "const double vi = (v == nullptr) ? 1.0 : (double)v[i];", 1),
+    ("bound_beta_keeps_sign", "r += val((double)beta, absolute) * val((double)z[j], absolute);",
+     "r += (double)beta * val((double)z[j], absolute);", 0),
+    ("bound_z_keeps_sign", "r += val((double)beta, absolute) * val((double)z[j], absolute);",
+     "r += val((double)beta, absolute) * (double)z[j];", 0),
     # the two halves
     ("rowdot_drops_v", "const double vi = (v == nullptr) ? 1.0 : val((double)v[i], absolute);",
      "const double vi = 1.0;", 2),
