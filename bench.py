@@ -3,11 +3,17 @@
 
 One step is one call of the fused path (main fused kernel + aggregation) on a
 batch of synthetic input already resident in HBM. Default workload: dense
-1,000,000 x 256 fp32 X ~ N(0, 1), v absent (= 1), beta = 0 — the
-normal-equations instance X^T X y. Prints one JSON line with:
+65,536 x 8192 fp32 X ~ U(-1, 1), v ~ U(0, 1), y, z ~ U(-1, 1), alpha = beta = 1 —
+the largest configuration (2 GiB of X) — with the other measured configurations
+(dense 1,000,000 x 256 normal equations, the CSR logistic Hessian-vector product,
+the CSR Zipf matrix and its column-permuted form) carried on the same line under
+``other_configs``. Prints one JSON line with:
   value            effective GB/s = algorithmic bytes per step / wall time per step
+  call_ms          median, p10, p90 of per-call times (HIP events around each call)
   roofline         the main fused kernel's algorithmic bytes / its mean duration
                    (HIP events recorded around it on the call's stream) vs 8 TB/s
+  peaks            the published 8 TB/s, the device properties' theoretical peak and
+                   the measured streaming-read ceiling, with the kernel's fraction of each
   speedup_vs_unfused  wall time of the rocBLAS/rocSPARSE chain / fused wall time
   cpu_baseline     the CPU oracle on the host cores (same algorithmic-bytes formula)
 Algorithmic bytes: every operand once — dense 4mn (X) + 4m (v, if given) + 4n (y)
@@ -29,7 +35,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fused X^T(v⊙Xy) effective GB/s, % of HBM peak, speedup vs unfused GEMV"
-DEFAULT_WORKLOAD = "dense_1000000x256_normal_equations"
+DEFAULT_WORKLOAD = "dense_65536x8192"
+# the other configurations measured by a default run (each timed with --also-steps calls)
+ALSO_DEFAULT = ["dense_1000000x256_normal_equations", "csr_10000000x1000_logistic_hvp", "csr_5000000x1000000_zipf",
+                "csr_5000000x1000000_zipf_permuted"]
+# workloads whose oracle is also timed on one host thread
+SINGLE_THREAD_CPU = ("dense_2048x128", "dense_1000000x256_normal_equations")
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
 
 
@@ -58,6 +69,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self) -> int:
         e = ctypes.c_void_p()
@@ -70,6 +82,10 @@ class HipEvents:
         if self.hip.hipEventSynchronize(b) != 0 or self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
+
+    def record(self, e, stream):
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def destroy(self, e):
         self.hip.hipEventDestroy(e)
@@ -122,13 +138,13 @@ def override(plan, text):
     return True
 
 
-def cpu_baseline(p, budget_s: float):
+def cpu_baseline(p, budget_s: float, threads=None, min_runs=3):
     """The oracle, as it is, on the host cores: repeated runs of the full workload for ~budget_s."""
     import oracle
-    threads = oracle.set_threads(len(os.sched_getaffinity(0)))
+    threads = oracle.set_threads(threads or len(os.sched_getaffinity(0)))
     runs = []
     t_end = time.perf_counter() + budget_s
-    while len(runs) < 3 or (time.perf_counter() < t_end and len(runs) < 200):
+    while len(runs) < min_runs or (time.perf_counter() < t_end and len(runs) < 200):
         t0 = time.perf_counter()
         if hasattr(p, "col_idx"):
             oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
@@ -136,8 +152,46 @@ def cpu_baseline(p, budget_s: float):
             oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
         runs.append(time.perf_counter() - t0)
     med = statistics.median(runs)
+    oracle.set_threads(len(os.sched_getaffinity(0)))
     return {"value": round(algorithmic_bytes(p) / med / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "sample": "the full workload, %d runs (median %.3f s each)" % (len(runs), med)}
+
+
+def percentiles(ms):
+    """median, p10, p90 and mean of a list of per-call times (ms)."""
+    q = sorted(ms)
+
+    def pct(f):
+        k = (len(q) - 1) * f
+        lo, hi = int(k), min(int(k) + 1, len(q) - 1)
+        return q[lo] + (q[hi] - q[lo]) * (k - lo)
+    return {"median": round(pct(0.5), 5), "p10": round(pct(0.1), 5), "p90": round(pct(0.9), 5),
+            "mean": round(statistics.mean(q), 5)}
+
+
+def stream_read_ceiling(xt, torch, dev, nbytes=2 << 30, reps=20):
+    """GB/s of the library's streaming-read probe over a 2 GiB buffer: the best of `reps` timed
+    launches after 5 warmup launches (HIP events on the current stream)."""
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream or None
+    grid = 8 * xt.xtvxy_get_device_info().compute_units
+    for _ in range(5):
+        xt.xtvxy_read_probe(buf.data_ptr(), nbytes, grid, sink.data_ptr(), sh)
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    for a, b in pairs:
+        ev.record(a, sh)
+        xt.xtvxy_read_probe(buf.data_ptr(), nbytes, grid, sink.data_ptr(), sh)
+        ev.record(b, sh)
+    torch.cuda.synchronize()
+    ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    del buf
+    return {"gbs": round(nbytes / (min(ms) / 1e3) / 1e9, 1), "median_gbs": round(nbytes / (statistics.median(ms) / 1e3) / 1e9, 1),
+            "bytes": nbytes, "what": "16-byte non-temporal loads over %d workgroups, best of %d launches" % (grid, reps)}
 
 
 LOGREG_METRIC = "Newton-CG logistic regression: ms per Newton iteration (fixed schedule), fused vs unfused products"
@@ -306,6 +360,211 @@ def report_tuning(args, p, kind, abytes, env):
     if args.tune_cache:
         xt.xtvxy_tune_cache_save(args.tune_cache)
     print(json.dumps(record), flush=True)
+    return record
+
+
+def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headline, ctx):
+    """Times one workload's fused call (and its comparators); returns the record's fields."""
+    import numpy as np
+    import torch
+
+    import datagen
+    import dense_linear_algebra_alpha_amd as xt
+
+    dev = torch.device("cuda:0")
+    p = datagen.WORKLOADS[name](seed=args.seed)
+    kind = "csr" if hasattr(p, "col_idx") else "dense"
+
+    def t(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:  # bf16 bit patterns
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    y, v, z = t(p.y), t(p.v), t(p.z)
+    out = torch.empty(p.n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream or None
+    bf16 = getattr(p, "x_dtype", "f32") == "bf16"
+    plan_text = args.plan if headline else None
+    with_unfused = unfused_calls > 0 and not args.fused_only
+    if kind == "dense":
+        X = t(p.X)
+        plan_fn, complete_fn, ws_fn, call, call_ex = (
+            (xt.xtvxy_dense_bf16_plan, xt.xtvxy_dense_bf16_plan_complete, xt.xtvxy_dense_bf16_workspace_size,
+             xt.xtvxy_dense_bf16, xt.xtvxy_dense_bf16_ex) if bf16 else
+            (xt.xtvxy_dense_f32_plan, xt.xtvxy_dense_f32_plan_complete, xt.xtvxy_dense_f32_workspace_size,
+             xt.xtvxy_dense_f32, xt.xtvxy_dense_f32_ex))
+        plan = plan_fn(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
+        forced = override(plan, plan_text)
+        if forced:
+            plan = complete_fn(p.m, p.n, p.ldx, plan)
+        ws_bytes = plan.workspace_bytes if forced else ws_fn(p.m, p.n, p.ldx)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
+        uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev) if with_unfused else None
+        # bf16 X: the comparison is the fp32 fused path on the same matrix widened to fp32
+        X32 = t(datagen.bf16_to_f32(p.X)) if bf16 and with_unfused else X
+        ws32_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
+        ws32 = torch.empty(max(ws32_bytes, 1), dtype=torch.uint8, device=dev) if bf16 and with_unfused else None
+
+        def fused():
+            if forced:
+                call_ex(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                        out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
+            else:
+                call(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                     out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
+
+        def unfused():
+            if bf16:
+                xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X32.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
+                                   xt._ptr(z), out.data_ptr(), ws32.data_ptr(), ws32_bytes, sh)
+            else:
+                xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v),
+                                                     y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
+                                                     uws.data_ptr(), uws_bytes, sh)
+        unfused_explicit = None
+        shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": "bf16" if bf16 else "f32"}
+        env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
+    else:
+        rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
+        plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
+        forced = override(plan, plan_text)
+        if forced:
+            plan = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, plan)
+        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
+        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        uplan = uplan_t = None
+
+        def fused():
+            if forced:
+                xt.xtvxy_csr_f32_ex(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
+                                    ws_bytes, sh, plan)
+            else:
+                xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                                 xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
+                                 ws_bytes, sh)
+
+        def unfused():
+            xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                                               out.data_ptr(), sh)
+
+        def unfused_explicit():
+            xt.xtvxy_csr_f32_unfused_reference(uplan_t.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta,
+                                               xt._ptr(z), out.data_ptr(), sh)
+        if with_unfused and not args.tune:
+            # structure analysis and the transposed copy: outside every timed region
+            uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)
+            uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
+        else:
+            unfused_explicit = None
+        shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
+        env = {"rp": rp, "ci": ci, "vals": vals, "y": y, "v": v, "z": z, "out": out, "sh": sh}
+
+    abytes = algorithmic_bytes(p)
+    if args.tune:
+        return {"tune": report_tuning(args, p, kind, abytes, env)}
+    ev = HipEvents()
+    kpairs = [(ev.create(), ev.create()) for _ in range(steps)]
+    cpairs = [(ev.create(), ev.create()) for _ in range(steps)]
+
+    def timed(fn, n_calls, n_warm, with_events):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_calls):
+            if with_events:
+                xt.xtvxy_set_kernel_timing_events(kpairs[i][0], kpairs[i][1])
+                ev.record(cpairs[i][0], sh)
+            fn()
+            if with_events:
+                ev.record(cpairs[i][1], sh)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        xt.xtvxy_set_kernel_timing_events(None, None)
+        if not with_events:
+            return (t1 - t0) / n_calls, None, None
+        return ((t1 - t0) / n_calls, [ev.elapsed_ms(a, b) for a, b in kpairs[:n_calls]],
+                [ev.elapsed_ms(a, b) for a, b in cpairs[:n_calls]])
+
+    step_s, kernel_ms, call_ms = timed(fused, steps, warmup, True)
+    fused_out = out.cpu().numpy()
+    unfused_s = explicit_s = None
+    if with_unfused:
+        unfused_s, _, _ = timed(unfused, unfused_calls, min(warmup, max(2, unfused_calls // 2)), False)
+        unfused_out = out.cpu().numpy()
+        if unfused_explicit is not None:
+            explicit_s, _, _ = timed(unfused_explicit, unfused_calls, min(warmup, max(2, unfused_calls // 2)), False)
+            explicit_out = out.cpu().numpy()
+    for a, b in kpairs + cpairs:
+        ev.destroy(a)
+        ev.destroy(b)
+
+    kernel_s = statistics.mean(kernel_ms) / 1e3
+    achieved = abytes / kernel_s / 1e9
+    kname = kernel_name(plan)
+    rec = {
+        "value": round(abytes / step_s / 1e9, 3),
+        "ms_per_step": round(step_s * 1e3, 5),
+        "steps": steps,
+        "warmup": warmup,
+        "config": dict({"workload": name, "algorithmic_bytes": abytes, "plan_forced": bool(forced),
+                        "plan": {k: v_ for k, v_ in plan.as_dict().items() if k != "predicted_seconds"}}, **shape),
+        "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "call_ms": percentiles(call_ms),
+        "kernel_ms": percentiles(kernel_ms),
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 3),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(name, kname, "csr_waves" if kname == "csr_waves" else kind),
+                     "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
+                     "kernel_ms_min": round(min(kernel_ms), 5)},
+        "peaks": {"published_gbs": HBM_PEAK_GBS, "device_properties_gbs": ctx["device_peak_gbs"],
+                  "stream_read_ceiling_gbs": ctx["ceiling_gbs"],
+                  "kernel_frac_of_device_peak": round(achieved / ctx["device_peak_gbs"], 4),
+                  "kernel_frac_of_ceiling": (round(achieved / ctx["ceiling_gbs"], 4)
+                                             if ctx["ceiling_gbs"] else None),
+                  "call_frac_of_ceiling": (round(abytes / step_s / 1e9 / ctx["ceiling_gbs"], 4)
+                                           if ctx["ceiling_gbs"] else None)},
+    }
+    if unfused_s is not None and bf16:  # the comparison is the fp32 fused path on the widened X
+        rec["f32_fused_ms_per_step"] = round(unfused_s * 1e3, 5)
+        rec["speedup_vs_f32_fused"] = round(unfused_s / step_s, 3)
+    elif unfused_s is not None:
+        rec["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
+        rec["unfused_calls_timed"] = unfused_calls
+        rec["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
+    if explicit_s is not None:  # the same chain with X^T kept as a second CSR matrix
+        rec["unfused_explicit_transpose_ms_per_step"] = round(explicit_s * 1e3, 5)
+        rec["speedup_vs_unfused_explicit_transpose"] = round(explicit_s / step_s, 3)
+
+    # parity of the timed outputs against the oracle (max elementwise error relative to the bound)
+    if not args.fused_only:
+        import oracle
+        if kind == "dense":
+            ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+            bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
+        else:
+            ref = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+            bnd = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
+        den = np.where(bnd > 0, bnd, 1.0)
+        rec["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
+        if unfused_s is not None:
+            key = "f32_fused_max_rel_err" if bf16 else "unfused_max_rel_err"
+            rec[key] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
+        if explicit_s is not None:
+            rec["unfused_explicit_transpose_max_rel_err"] = float(
+                np.max(np.abs(explicit_out.astype(np.float64) - ref) / den))
+        if not args.no_cpu_baseline and cpu_budget > 0:
+            rec["cpu_baseline"] = cpu_baseline(p, cpu_budget)
+            if name in SINGLE_THREAD_CPU:
+                rec["cpu_baseline_single_thread"] = cpu_baseline(p, min(cpu_budget, 5.0), threads=1, min_runs=1)
+    del p
+    return rec
 
 
 def main():
@@ -315,11 +574,20 @@ def main():
     # the GPU's clocks and translation caches settle over the first ~10-20 ms of work
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--also", default="default",
+                    help="comma-separated further workloads measured on the same line ('default': the other "
+                         "configurations when the default workload runs; 'none': no others)")
+    ap.add_argument("--also-steps", type=int, default=40, help="timed fused calls of each further workload")
+    ap.add_argument("--also-warmup", type=int, default=60, help="untimed fused calls of each further workload")
+    ap.add_argument("--unfused-steps", type=int, default=20,
+                    help="timed calls of the unfused comparators (their transposed products are slow)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle runs for cpu_baseline")
+    ap.add_argument("--also-cpu-budget", type=float, default=2.0, help="seconds of oracle runs per further workload")
     ap.add_argument("--fused-only", action="store_true", help="time the fused path only (for profilers)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--plan", default=None,
                     help="JSON object of launch-parameter fields that replace the model's choice, e.g. "
                          "'{\"lds_window\": 16384, \"y_window\": 0, \"bin_columns\": 0}' (the library checks the result)")
@@ -351,7 +619,6 @@ def main():
               "(row sharding with one reduce-scatter is a design note, not built)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import datagen
@@ -363,183 +630,57 @@ def main():
     if args.workload not in datagen.WORKLOADS:
         known = list(datagen.WORKLOADS) + list(datagen.LOGISTIC_WORKLOADS)
         raise SystemExit("unknown workload %s (known: %s)" % (args.workload, ", ".join(known)))
+    if args.also == "default":
+        also = [w for w in ALSO_DEFAULT if w != args.workload] if (
+            args.workload == DEFAULT_WORKLOAD and not args.tune and not args.fused_only and not args.plan) else []
+    elif args.also == "none":
+        also = []
+    else:
+        also = [w for w in args.also.split(",") if w]
+        for w in also:
+            if w not in datagen.WORKLOADS:
+                raise SystemExit("unknown workload %s" % w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    p = datagen.WORKLOADS[args.workload](seed=args.seed)
-    kind = "csr" if hasattr(p, "col_idx") else "dense"
-
-    def t(a):
-        if a is None:
-            return None
-        a = np.ascontiguousarray(a)
-        if a.dtype == np.uint16:  # bf16 bit patterns
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(a).to(dev)
-
-    y, v, z = t(p.y), t(p.v), t(p.z)
-    out = torch.empty(p.n, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream or None
-    bf16 = getattr(p, "x_dtype", "f32") == "bf16"
-    if kind == "dense":
-        X = t(p.X)
-        plan_fn, complete_fn, ws_fn, call, call_ex = (
-            (xt.xtvxy_dense_bf16_plan, xt.xtvxy_dense_bf16_plan_complete, xt.xtvxy_dense_bf16_workspace_size,
-             xt.xtvxy_dense_bf16, xt.xtvxy_dense_bf16_ex) if bf16 else
-            (xt.xtvxy_dense_f32_plan, xt.xtvxy_dense_f32_plan_complete, xt.xtvxy_dense_f32_workspace_size,
-             xt.xtvxy_dense_f32, xt.xtvxy_dense_f32_ex))
-        plan = plan_fn(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
-        forced = override(plan, args.plan)
-        if forced:
-            plan = complete_fn(p.m, p.n, p.ldx, plan)
-        ws_bytes = plan.workspace_bytes if forced else ws_fn(p.m, p.n, p.ldx)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
-        uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev)
-        # bf16 X: the comparison is the fp32 fused path on the same matrix widened to fp32
-        X32 = t(datagen.bf16_to_f32(p.X)) if bf16 and not args.no_unfused and not args.fused_only else X
-        ws32_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
-        ws32 = torch.empty(max(ws32_bytes, 1), dtype=torch.uint8, device=dev)
-
-        def fused():
-            if forced:
-                call_ex(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
-                        out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
-            else:
-                call(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
-                     out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
-
-        def unfused():
-            if bf16:
-                xt.xtvxy_dense_f32(p.m, p.n, p.alpha, X32.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
-                                   xt._ptr(z), out.data_ptr(), ws32.data_ptr(), ws32_bytes, sh)
-            else:
-                xt.xtvxy_dense_f32_unfused_reference(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v),
-                                                     y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
-                                                     uws.data_ptr(), uws_bytes, sh)
-        shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": "bf16" if bf16 else "f32"}
-    else:
-        rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
-        plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
-        forced = override(plan, args.plan)
-        if forced:
-            plan = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, plan)
-        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
-        ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-        uplan = None
-
-        def fused():
-            if forced:
-                xt.xtvxy_csr_f32_ex(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
-                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
-                                    ws_bytes, sh, plan)
-            else:
-                xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
-                                 xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
-                                 ws_bytes, sh)
-
-        def unfused():
-            xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
-                                               out.data_ptr(), sh)
-
-        def unfused_explicit():
-            xt.xtvxy_csr_f32_unfused_reference(uplan_t.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta,
-                                               xt._ptr(z), out.data_ptr(), sh)
-        if not args.no_unfused and not args.fused_only and not args.tune:
-            # structure analysis and the transposed copy: outside every timed region
-            uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)
-            uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
-        shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
-
-    abytes = algorithmic_bytes(p)
-    if args.tune:
-        return report_tuning(args, p, kind, abytes, locals())
-    ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-
-    def timed(fn, with_kernel_events):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            if with_kernel_events:
-                xt.xtvxy_set_kernel_timing_events(pairs[i][0], pairs[i][1])
-            fn()
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        xt.xtvxy_set_kernel_timing_events(None, None)
-        kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs] if with_kernel_events else None
-        return (t1 - t0) / args.steps, kernel_ms
-
-    step_s, kernel_ms = timed(fused, True)
-    fused_out = out.cpu().numpy()
-    unfused_s = explicit_s = None
-    if not args.no_unfused and not args.fused_only:
-        unfused_s, _ = timed(unfused, False)
-        unfused_out = out.cpu().numpy()
-        if kind == "csr":
-            explicit_s, _ = timed(unfused_explicit, False)
-            explicit_out = out.cpu().numpy()
-
-    kernel_s = statistics.mean(kernel_ms) / 1e3
-    achieved = abytes / kernel_s / 1e9
+    info = xt.xtvxy_get_device_info()
+    ctx = {"device_peak_gbs": round(info.hbm_bytes_per_s / 1e9, 1), "ceiling_gbs": None}
+    ceiling = None
+    if not args.no_ceiling and not args.tune:
+        ceiling = stream_read_ceiling(xt, torch, dev)
+        ctx["ceiling_gbs"] = ceiling["gbs"]
+        torch.cuda.empty_cache()
+    print("[bench] %s" % args.workload, file=sys.stderr, flush=True)
+    rec = measure_workload(args.workload, args, args.steps, args.warmup, 0 if args.no_unfused else args.unfused_steps,
+                           args.cpu_budget, True, ctx)
+    if "tune" in rec:
+        return
+    torch.cuda.empty_cache()
     record = {
         "metric": METRIC,
-        "value": round(abytes / step_s / 1e9, 3),
+        "value": rec.pop("value"),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 5),
+        "steps": rec.pop("steps"),
+        "warmup": rec.pop("warmup"),
+        "ms_per_step": rec.pop("ms_per_step"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic (seeded generators, seed %d)" % args.seed,
-        "config": dict({"workload": args.workload, "algorithmic_bytes": abytes, "plan_forced": bool(forced),
-                        "plan": {k: v_ for k, v_ in plan.as_dict().items() if k != "predicted_seconds"}},
-                       **shape),
-        "hbm_peak_fraction": round(abytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
-        "roofline": {"bound": "hbm", "kernel": kernel_name(plan), "achieved": round(achieved, 3),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(args.workload, kernel_name(plan),
-                                             "csr_waves" if kernel_name(plan) == "csr_waves" else kind),
-                     "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
-                     "kernel_ms_min": round(min(kernel_ms), 5)},
     }
-    if unfused_s is not None and bf16:  # the comparison is the fp32 fused path on the widened X
-        record["f32_fused_ms_per_step"] = round(unfused_s * 1e3, 5)
-        record["speedup_vs_f32_fused"] = round(unfused_s / step_s, 3)
-    elif unfused_s is not None:
-        record["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
-        record["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
-    if explicit_s is not None:  # the same chain with X^T kept as a second CSR matrix
-        record["unfused_explicit_transpose_ms_per_step"] = round(explicit_s * 1e3, 5)
-        record["speedup_vs_unfused_explicit_transpose"] = round(explicit_s / step_s, 3)
-
-    # parity of the timed outputs against the oracle (max elementwise error relative to the bound)
-    if not args.fused_only:
-        import oracle
-        if kind == "dense":
-            ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
-            bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
-        else:
-            ref = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
-            bnd = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
-        den = np.where(bnd > 0, bnd, 1.0)
-        record["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
-        if unfused_s is not None:
-            key = "f32_fused_max_rel_err" if bf16 else "unfused_max_rel_err"
-            record[key] = float(np.max(np.abs(unfused_out.astype(np.float64) - ref) / den))
-        if explicit_s is not None:
-            record["unfused_explicit_transpose_max_rel_err"] = float(
-                np.max(np.abs(explicit_out.astype(np.float64) - ref) / den))
-        if not args.no_cpu_baseline:
-            record["cpu_baseline"] = cpu_baseline(p, args.cpu_budget)
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    record.update(rec)
+    if ceiling is not None:
+        record["stream_read_ceiling"] = ceiling
+    others = {}
+    for w in also:
+        print("[bench] %s" % w, file=sys.stderr, flush=True)
+        o = measure_workload(w, args, args.also_steps, args.also_warmup, 0 if args.no_unfused else args.unfused_steps,
+                             args.also_cpu_budget, False, ctx)
+        others[w] = o
+        torch.cuda.empty_cache()
+    if others:
+        record["other_configs"] = others
     print(json.dumps(record), flush=True)
 
 

@@ -350,4 +350,10 @@ WORKLOADS = {
         m, n, seed, s_row=1.5, max_row=2726, s_col=1.2, permute_columns=permute_columns,
         values="uniform", y="uniform", v="uniform", z="uniform", alpha=0.7, beta=0.3,
         name="csr_5000000x1000000_zipf"),
+    # the same matrix with a seeded random permutation of the columns: the hot columns are spread
+    # over the whole index range instead of sitting at the lowest indices
+    "csr_5000000x1000000_zipf_permuted": lambda seed=0, m=5_000_000, n=1_000_000: csr_zipf(
+        m, n, seed, s_row=1.5, max_row=2726, s_col=1.2, permute_columns=True,
+        values="uniform", y="uniform", v="uniform", z="uniform", alpha=0.7, beta=0.3,
+        name="csr_5000000x1000000_zipf_permuted"),
 }

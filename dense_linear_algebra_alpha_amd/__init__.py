@@ -32,7 +32,7 @@ __all__ = [
     "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
     "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
-    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
+    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
     "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
@@ -56,6 +56,14 @@ def xtvxy_status_string(status: int) -> str:
 
 def xtvxy_set_kernel_timing_events(before_main, after_main):
     return _abi.call("xtvxy_set_kernel_timing_events", before_main, after_main)
+
+
+def xtvxy_test_group_wait(polls: int, unanswered: int):
+    return _abi.call("xtvxy_test_group_wait", int(polls), int(unanswered))
+
+
+def xtvxy_read_probe(buffer, nbytes, grid, sink, stream):
+    return _abi.call("xtvxy_read_probe", buffer, nbytes, grid, sink, stream)
 
 
 def xtvxy_get_device_info(device: int = -1) -> xtvxy_device_info:
@@ -298,6 +306,17 @@ def _workspace(nbytes: int, device):
     return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
 
 
+def _keep_for_stream(stream, *tensors):
+    """Tensors allocated here on the current stream but used by kernels launched on `stream`: tell
+    the caching allocator, so that their memory is not handed out again before that stream has
+    passed the call (it would otherwise be reusable as soon as the helper returns)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def dense_plan(m, n, ldx=None, aligned=True, dev=None, bf16=False) -> xtvxy_launch_params:
     fn = xtvxy_dense_bf16_plan if bf16 else xtvxy_dense_f32_plan
     return fn(m, n, n if ldx is None else ldx, 1 if aligned else 0, dev)
@@ -330,14 +349,16 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
     _check_vec("z", z, n, device, required=beta != 0)
-    if out is None:
+    made_out = out is None
+    if made_out:
         out = torch.empty(n, dtype=torch.float32, device=device)
     _check_vec("out", out, n, device)
     if plan is None:
         need = (xtvxy_dense_bf16_workspace_size if bf16 else xtvxy_dense_f32_workspace_size)(m, n, ldx)
     else:
         need = int(plan.workspace_bytes)
-    if workspace is None:
+    made_ws = workspace is None
+    if made_ws:
         workspace = _workspace(need, device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     args = (m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(),
@@ -346,6 +367,7 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
         (xtvxy_dense_bf16 if bf16 else xtvxy_dense_f32)(*args)
     else:
         (xtvxy_dense_bf16_ex if bf16 else xtvxy_dense_f32_ex)(*args, plan)
+    _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
 
@@ -365,11 +387,13 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
     _check_vec("z", z, n, device, required=beta != 0)
-    if out is None:
+    made_out = out is None
+    if made_out:
         out = torch.empty(n, dtype=torch.float32, device=device)
     _check_vec("out", out, n, device)
     need = xtvxy_csr_f32_workspace_size(m, n, nnz) if plan is None else int(plan.workspace_bytes)
-    if workspace is None:
+    made_ws = workspace is None
+    if made_ws:
         workspace = _workspace(need, device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
@@ -379,6 +403,7 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
         xtvxy_csr_f32(*args)
     else:
         xtvxy_csr_f32_ex(*args, plan)
+    _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
 
@@ -402,7 +427,8 @@ def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
     _check_vec("t0", t0, m, device, required=beta != 0)
-    if out is None:
+    made_out = out is None
+    if made_out:
         out = torch.empty(m, dtype=torch.float32, device=device)
     _check_vec("out", out, m, device)
     args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
@@ -412,6 +438,7 @@ def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=
         xtvxy_csr_f32_rowdot(*args)
     else:
         xtvxy_csr_f32_rowdot_ex(*args, plan)
+    _keep_for_stream(stream, out if made_out else None)
     return out
 
 
@@ -422,11 +449,13 @@ def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, out=Non
     m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
     _check_vec("u", u, m, device)
     _check_vec("z", z, n, device, required=beta != 0)
-    if out is None:
+    made_out = out is None
+    if made_out:
         out = torch.empty(n, dtype=torch.float32, device=device)
     _check_vec("out", out, n, device)
     need = xtvxy_csr_f32_workspace_size(m, n, nnz) if plan is None else int(plan.workspace_bytes)
-    if workspace is None:
+    made_ws = workspace is None
+    if made_ws:
         workspace = _workspace(need, device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     args = (m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
@@ -436,6 +465,7 @@ def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, out=Non
         xtvxy_csr_f32_tmv(*args)
     else:
         xtvxy_csr_f32_tmv_ex(*args, plan)
+    _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
 
@@ -445,6 +475,8 @@ def csr_check(row_ptr, col_idx, n, stream=None) -> int:
     flag = torch.zeros(1, dtype=torch.int32, device=row_ptr.device)
     xtvxy_csr_check(row_ptr.numel() - 1, n, col_idx.numel(), row_ptr.data_ptr(),
                     col_idx.data_ptr() if col_idx.numel() else None, flag.data_ptr(), _stream_handle(stream))
+    if stream is not None:  # the check ran on `stream`; .item() below waits for the current stream only
+        stream.synchronize()
     return int(flag.item())
 
 
@@ -457,13 +489,16 @@ def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, worksp
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
     _check_vec("z", z, n, device, required=beta != 0)
-    if out is None:
+    made_out = out is None
+    if made_out:
         out = torch.empty(n, dtype=torch.float32, device=device)
-    if workspace is None:
+    made_ws = workspace is None
+    if made_ws:
         workspace = _workspace(xtvxy_dense_f32_unfused_reference_workspace_size(m, n), device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
     xtvxy_dense_f32_unfused_reference(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta),
                                       _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
+    _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
 
@@ -484,10 +519,12 @@ class CsrUnfusedPlan:
 
     def __call__(self, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, stream=None):
         torch = _torch()
-        if out is None:
+        made_out = out is None
+        if made_out:
             out = torch.empty(self.n, dtype=torch.float32, device=y.device)
         xtvxy_csr_f32_unfused_reference(self.handle, float(alpha), _ptr(v), y.data_ptr(), float(beta), _ptr(z),
                                         out.data_ptr(), _stream_handle(stream))
+        _keep_for_stream(stream, out if made_out else None)
         return out
 
     def close(self):

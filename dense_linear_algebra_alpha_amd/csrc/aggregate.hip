@@ -27,7 +27,8 @@ template <int kAggCols>
 __global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __restrict__ partial, int64_t rows,
                                                                 int64_t ldp, const float* __restrict__ acc,
                                                                 int64_t n, float alpha, float beta, const float* z,
-                                                                float* out, BinPartials bins) {
+                                                                float* out, BinPartials bins,
+                                                                const uint32_t* __restrict__ error) {
   constexpr int kAggRows = kAggThreads / kAggCols;
   __shared__ double sh[kAggRows][kAggCols];
   const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
@@ -53,7 +54,8 @@ __global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __r
     if (acc) t += (double)acc[j];
     double o = (double)alpha * t;
     if (beta != 0.0f) o += (double)beta * (double)z[j];
-    out[j] = (float)o;
+    // a group-row wait that gave up left some partial sums incomplete: the result is NaN
+    out[j] = (error != nullptr && *error != 0u) ? __builtin_nanf("") : (float)o;
   }
 }
 
@@ -95,18 +97,18 @@ unsigned grid_for(int64_t count, int block) {
 
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
                             float alpha, float beta, const float* z, float* out, hipStream_t s,
-                            const BinPartials* bins) {
+                            const BinPartials* bins, const uint32_t* error) {
   if (n <= 0) return hipSuccess;
   const BinPartials none{nullptr, nullptr, 0, 0};
   if (n <= kNarrowOutput) {
     hipLaunchKernelGGL(aggregate_kernel<16>, dim3((unsigned)((n + 15) / 16)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
   } else if (n <= kWideOutput) {
     hipLaunchKernelGGL(aggregate_kernel<64>, dim3((unsigned)((n + 63) / 64)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
   } else {
     hipLaunchKernelGGL(aggregate_kernel<256>, dim3((unsigned)((n + 255) / 256)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
   }
   return hipGetLastError();
 }

@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <utility>
 
 #include "internal.h"
 
@@ -56,8 +58,17 @@ bool mul_overflows(int64_t a, int64_t b) { return a != 0 && b > INT64_MAX / a; }
 
 xtvxy_status launch_status(hipError_t e) { return e == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH; }
 
-// Measurement hook: events recorded around the main fused kernel of each call.
-hipEvent_t g_before_main = nullptr, g_after_main = nullptr;
+// Measurement hook: events recorded around the main fused kernel of each call made by the thread
+// that set them (per thread, so that calls from other threads are never bracketed by them).
+thread_local hipEvent_t g_before_main = nullptr, g_after_main = nullptr;
+
+// Failure-path test hook of the group-row kernel (per thread): polls per wait, and whether the
+// waits look for a tag that no member publishes.
+thread_local uint32_t g_wait_polls = 0, g_wait_unanswered = 0;
+
+// (device, kernel) pairs whose dynamic-LDS limit has been raised to the device's LDS.
+std::mutex g_lds_mutex;
+std::set<std::pair<int, const void*>> g_lds_done;
 
 hipError_t mark(hipEvent_t e, hipStream_t s) { return e ? hipEventRecord(e, s) : hipSuccess; }
 
@@ -247,6 +258,8 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
   if (plan.kernel == XTVXY_DENSE_GROUP_ROWS) {
     a.xchg = base + w.xchg_off;
     a.error = reinterpret_cast<uint32_t*>(base + w.error_off);
+    a.wait_polls = g_wait_polls;
+    a.wait_tag_skew = g_wait_unanswered ? 0x80000000u : 0u;
     hipError_t e = launch_zero(base + w.xchg_off, w.total - w.xchg_off, stream);
     if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   }
@@ -255,7 +268,8 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
   hipError_t e = launch_dense(a, plan, stream);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, nullptr, n, alpha, beta, z, out, stream);
+  e = launch_aggregate(a.partial, (int64_t)w.partial_rows, n, nullptr, n, alpha, beta, z, out, stream, nullptr,
+                       plan.kernel == XTVXY_DENSE_GROUP_ROWS ? a.error : nullptr);
   return launch_status(e);
 }
 
@@ -461,6 +475,13 @@ xtvxy_status xtvxy_set_kernel_timing_events(hipEvent_t before_main, hipEvent_t a
   return XTVXY_SUCCESS;
 }
 
+xtvxy_status xtvxy_test_group_wait(int32_t polls, int32_t unanswered) {
+  if (polls < 0) return XTVXY_ERROR_INVALID_VALUE;
+  g_wait_polls = (uint32_t)polls;
+  g_wait_unanswered = unanswered != 0 ? 1u : 0u;
+  return XTVXY_SUCCESS;
+}
+
 xtvxy_status xtvxy_get_device_info(int device, xtvxy_device_info* info) {
   if (!info) return XTVXY_ERROR_NULL_POINTER;
   return device_info(device, info);
@@ -629,5 +650,22 @@ xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, cons
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
                             float beta, const float* z, const float* out, bool* quick) {
   return check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, quick);
+}
+}  // namespace xtvxy
+
+namespace xtvxy {
+hipError_t allow_dynamic_lds(const void* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_lds_mutex);
+  if (g_lds_done.count({dev, fn})) return hipSuccess;
+  int lds = 0;
+  e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+  if (e != hipSuccess) return e;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  g_lds_done.insert({dev, fn});
+  return hipSuccess;
 }
 }  // namespace xtvxy

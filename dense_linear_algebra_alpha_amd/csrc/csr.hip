@@ -614,7 +614,7 @@ hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t 
   size_t lds = ((size_t)a.lds_window + (YMODE == kYGlobal ? 0 : (size_t)a.y_window)) * sizeof(float);
   if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
   const void* fn = reinterpret_cast<const void*>(&csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_dynamic_lds(fn);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
                      s, a);

@@ -186,8 +186,7 @@ hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = sizeof(float) << a.bin_shift;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bin_accumulate_kernel),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  e = allow_dynamic_lds(reinterpret_cast<const void*>(&bin_accumulate_kernel));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(bin_accumulate_kernel, dim3((unsigned)a.max_units), dim3(kAccThreads), lds, s, a);
   return hipGetLastError();

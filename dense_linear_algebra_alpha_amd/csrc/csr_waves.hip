@@ -464,7 +464,7 @@ template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MOD
 hipError_t launch_w(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const size_t lds = csr_waves_dynamic_lds(a.lds_window, YMODE == kYGlobal ? 0 : a.y_window, a.bins, BLK);
   const void* fn = reinterpret_cast<const void*>(&csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = allow_dynamic_lds(fn);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
                      s, a);

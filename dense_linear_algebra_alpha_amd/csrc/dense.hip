@@ -41,6 +41,7 @@ namespace xtvxy {
 namespace {
 
 constexpr uint32_t kSpinLimit = 1u << 24;  // a barrier wait gives up (and flags an error) after this
+                                           // many polls, unless the call sets a smaller bound
 
 template <class E, int VEC, int NCH, int UNR>
 __global__ __launch_bounds__(kBlock) void dense_wave_rows(DenseArgs a) {
@@ -266,8 +267,10 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
         const int c = threadIdx.x / R, r = threadIdx.x % R;
         uint64_t w = __hip_atomic_load(sl + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
-        while ((uint32_t)(w >> 32) != tag) {
-          if (++spins > kSpinLimit) {
+        const uint32_t limit = a.wait_polls ? a.wait_polls : kSpinLimit;
+        const uint32_t want = tag + a.wait_tag_skew;  // skew 0 except under the failure-path test hook
+        while ((uint32_t)(w >> 32) != want) {
+          if (++spins > limit) {
             __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }

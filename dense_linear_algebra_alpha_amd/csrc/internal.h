@@ -57,6 +57,9 @@ struct DenseArgs {
   int32_t group;      // group-row path: workgroups per row
   void* xchg;         // group-row path: [groups][2][group][rows per step] 64-bit tagged slots (zeroed)
   uint32_t* error;    // group-row path: set when a wait for the other members gives up
+  uint32_t wait_polls;     // group-row path: polls before a wait gives up (0: the kernel's own bound)
+  uint32_t wait_tag_skew;  // group-row path: 0; nonzero only under the failure-path test hook (the
+                           // waits then look for a step tag nobody publishes and always give up)
 };
 
 // Arguments of the CSR fused kernels.
@@ -102,6 +105,10 @@ struct CsrBinArgs {
   float* partial2;         // [max_units][2^bin_shift] per-unit sums of the bin's columns
 };
 
+// Lets kernel `fn` take up to the device's whole LDS as dynamic LDS. The attribute is set once per
+// (device, kernel) for the process; later calls only look it up (api.cpp).
+hipError_t allow_dynamic_lds(const void* fn);
+
 // Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first
 // HIP error it meets.
 hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStream_t s);
@@ -125,9 +132,11 @@ struct BinPartials {
 //                   + sum over the units u of j's bin of partial2[u][j - bin start] [binned j])
 //          + (beta != 0 ? beta * z[j] : 0),
 // in fp64, the partial rows summed in ascending order, rounded once.
+// When `error` is given and the word it points to is nonzero when the kernel runs (a group-row
+// wait gave up), every out[j] is NaN instead.
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
                             float alpha, float beta, const float* z, float* out, hipStream_t s,
-                            const BinPartials* bins = nullptr);
+                            const BinPartials* bins = nullptr, const uint32_t* error = nullptr);
 // out[j] = (beta != 0) ? beta * z[j] : 0
 hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s);
 // p[i] = 0 for i < count (a kernel, so that the call stays graph-capturable)

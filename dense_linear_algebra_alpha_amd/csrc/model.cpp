@@ -43,8 +43,8 @@ constexpr double kLaunch = 3.0e-6;      // seconds per dependent kernel launch
 constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wavefronts)
 constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
 constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output and y windows
-constexpr int kCsrThreadsPerCuLarge = 1024;
-constexpr int64_t kWaveRowsMaxMean = 16;      // CSR: mean entries per row up to which the wavefront kernel is used  // CSR: threads per CU the windows leave room for when n is large
+constexpr int kCsrThreadsPerCuLarge = 1024;  // CSR: threads per CU the windows leave room for when n is large
+constexpr int64_t kWaveRowsMaxMean = 16;      // CSR: mean entries per row up to which the wavefront kernel is used
 constexpr int kMaxThreadsPerCu = 2048;       // 32 wavefronts
 
 int next_pow2(int64_t x) {

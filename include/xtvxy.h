@@ -119,7 +119,9 @@ typedef struct xtvxy_launch_params {
 } xtvxy_launch_params;
 
 /* Model-chosen plan for a dense problem; `dev` NULL = the current device.
- * X_aligned16 states whether X is 16-byte aligned (pointer % 16 == 0). */
+ * X_aligned16 states whether X is 16-byte aligned (pointer % 16 == 0): the plan
+ * depends on it (16-byte loads need an aligned X) and on the device's resources,
+ * which `dev` may describe so that plans can be made without a GPU. */
 xtvxy_status xtvxy_dense_f32_plan(int64_t m, int64_t n, int64_t ldx, int X_aligned16,
                                   const xtvxy_device_info *dev, xtvxy_launch_params *plan);
 
@@ -144,6 +146,9 @@ xtvxy_status xtvxy_dense_f32_workspace_size(int64_t m, int64_t n, int64_t ldx, s
 xtvxy_status xtvxy_dense_f32(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx,
                              const float *v, const float *y, float beta, const float *z, float *out,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+/* (Plans of the group-row kernel: if a member's bounded wait for the others gives up, which the
+ * cooperative launch's co-residency rules out in normal operation, every element of out is NaN;
+ * see xtvxy_test_group_wait.) */
 
 /* As xtvxy_dense_f32 with the launch parameters forced (NULL = model). The
  * workspace must hold force->workspace_bytes as returned by xtvxy_dense_f32_plan
@@ -240,12 +245,31 @@ xtvxy_status xtvxy_csr_f32_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha
 xtvxy_status xtvxy_csr_check(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
                              const int32_t *col_idx, int32_t *d_flag, hipStream_t stream);
 
-/* Timing hook for measurements (process-wide, not thread-safe). While both
- * events are non-NULL, every fused call records `before_main` on its stream
- * just before its main fused kernel and `after_main` just after it (before the
- * aggregation kernel), so that hipEventElapsedTime gives that kernel's time.
- * NULL, NULL switches the hook off. The events are the caller's. */
+/* Timing hook for measurements, per calling thread. While both events are
+ * non-NULL, every fused call made by the thread that set them records
+ * `before_main` on its stream just before its main fused kernel and
+ * `after_main` just after it (before the aggregation kernel), so that
+ * hipEventElapsedTime gives that kernel's time; calls from other threads are
+ * not bracketed. NULL, NULL switches the hook off for the thread. The events
+ * are the caller's. */
 xtvxy_status xtvxy_set_kernel_timing_events(hipEvent_t before_main, hipEvent_t after_main);
+
+/* Test hook of the dense group-row kernel's failure path, per calling thread. The members of a
+ * group (XTVXY_DENSE_GROUP_ROWS) wait for each other's partial dot products with a bounded wait;
+ * when a wait gives up (which the cooperative launch's co-residency normally rules out), the call
+ * completes and every element of `out` is NaN. With `polls` > 0 each wait gives up after that
+ * many polls; with `unanswered` nonzero the waits look for a step tag no member publishes, so
+ * every wait gives up and the result must be all NaN (0, 0 restores normal operation). For tests
+ * of that path only; XTVXY_ERROR_INVALID_VALUE for polls < 0. */
+xtvxy_status xtvxy_test_group_wait(int32_t polls, int32_t unanswered);
+
+/* Measurement helper, not part of the pattern: one kernel that reads `bytes` (a multiple of 16)
+ * from the 16-byte aligned device buffer with 16-byte non-temporal loads over `grid` workgroups
+ * of 256 threads, each taking one contiguous stretch, and writes nothing (the device float
+ * `sink` is written only if the data sum to a value a zeroed buffer never gives). Its time gives
+ * the GPU's streaming-read ceiling, the practical bound of the HBM-bound fused kernels.
+ * Asynchronous on `stream`. */
+xtvxy_status xtvxy_read_probe(const void *buffer, size_t bytes, int64_t grid, float *sink, hipStream_t stream);
 
 /* ------------------------------------------------------------------------ */
 /* Unfused comparator: the same result from operator-level library calls    */
@@ -266,7 +290,15 @@ xtvxy_status xtvxy_dense_f32_unfused_reference(int64_t m, int64_t n, float alpha
                                                hipStream_t stream);
 
 /* The CSR comparator keeps rocSPARSE descriptors and the result of the
- * structure analysis in a plan, made once per matrix (blocking, allocates). */
+ * structure analysis in a plan, made once per matrix (blocking, allocates).
+ * Unlike the dense comparator it does not take xtvxy_csr_f32's argument list
+ * with a caller workspace: rocSPARSE's SpMV needs a structure analysis of the
+ * matrix and an opaque buffer whose size and contents are rocSPARSE's, made
+ * once per matrix, and a fair comparison keeps that set-up out of the timed
+ * calls (as the fused path needs no set-up at all). So the plan owns those
+ * buffers (there is no separate workspace query), the per-call entry point
+ * takes the plan in place of the matrix arrays, and the other arguments
+ * (alpha, v, y, beta, z, out, stream) keep xtvxy_csr_f32's meaning and rules. */
 typedef struct xtvxy_csr_unfused_plan_s *xtvxy_csr_unfused_plan;
 
 xtvxy_status xtvxy_csr_f32_unfused_plan_create(int64_t m, int64_t n, int64_t nnz,

@@ -26,11 +26,13 @@ WIDTHS = [1, 2, 3, 4, 5, 31, 64, 100, 128, 255, 256, 257, 511, 512, 600, 1000, 1
           4096, 5000, 8191, 8192, 8193, 12000, 16385, 20000]
 
 
-@pytest.mark.parametrize("n", WIDTHS)
-@pytest.mark.parametrize("m", [1, 3, 70, 1000])
+# (m, n) pairs of the width sweep: every width with 1, 3 and 70 rows, and with 1000 rows while the
+# matrix stays within 8e6 elements (the wider ones are covered by the smaller m)
+SHAPES = [(m, n) for m in (1, 3, 70, 1000) for n in WIDTHS if m * n <= 8_000_000]
+
+
+@pytest.mark.parametrize("m,n", SHAPES)
 def test_shapes(m, n):
-    if m * n > 8_000_000:
-        pytest.skip("covered by smaller m")
     check(datagen.dense_problem(m, n, seed=m * 7919 + n))
 
 
@@ -192,3 +194,45 @@ def test_full_size_8192x65536_column_slices():
     plan = xt.xtvxy_dense_f32_plan(p.m, p.n, p.ldx, 1)
     assert plan.kernel == xt.XTVXY_DENSE_GROUP_ROWS
     check(p)
+
+
+def test_group_wait_failure_is_visible():
+    # The failure path of the group-row kernel's bounded wait, forced from the host: every wait
+    # looks for a step tag that no member publishes and gives up after 4 polls, so every kernel
+    # still ends normally; the call must then deliver NaN in every element, and the next call with
+    # the hook off must be correct again.
+    m, n = 96, 20000
+    p = datagen.dense_problem(m, n, seed=41)
+    ref, bnd = dense_oracle(p)
+    d = DenseOnDevice(p)
+    plan = xt.xtvxy_dense_f32_plan_complete(m, n, n, xt.xtvxy_launch_params(
+        kernel=xt.XTVXY_DENSE_GROUP_ROWS, block_threads=256, vec=4, chunks=8, group=3, grid=12))
+    note("group-row wait failure forced, plan %s" % plan.as_dict())
+    xt.xtvxy_test_group_wait(4, 1)
+    try:
+        failed = d.run(plan=plan)
+    finally:
+        xt.xtvxy_test_group_wait(0, 0)
+    assert np.isnan(failed).all()
+    note("group-row plan again, hook off")
+    assert_parity(d.run(plan=plan), ref, bnd, "after the forced failure")
+
+
+def test_helpers_on_a_non_current_stream():
+    # the tensor helpers allocate their workspace (and out) on the current stream and launch on
+    # the caller's: the allocations are recorded on that stream, so the caching allocator cannot
+    # hand them to other work while the kernels still use them
+    import torch
+    p = datagen.dense_problem(4000, 3000, seed=42)
+    ref, bnd = dense_oracle(p)
+    d = DenseOnDevice(p)
+    s = torch.cuda.Stream()
+    note("dense on a side stream")
+    with torch.cuda.stream(torch.cuda.current_stream()):
+        outs = [xt.dense(d.X, d.y, d.v, d.z, p.alpha, p.beta, m=p.m, n=p.n, stream=s) for _ in range(3)]
+        junk = [torch.full((1 << 22,), float("nan"), device=d.X.device) for _ in range(8)]  # reuse pressure
+    s.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    for o in outs:
+        assert_parity(o.cpu().numpy(), ref, bnd, "side stream")

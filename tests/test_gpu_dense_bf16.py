@@ -23,11 +23,12 @@ def check(p, plan=None, X_offset=0, what=""):
 WIDTHS = [1, 3, 8, 64, 100, 256, 264, 512, 1000, 1024, 2040, 2048, 2056, 3000, 8184, 8192, 8200, 20000]
 
 
-@pytest.mark.parametrize("n", WIDTHS)
-@pytest.mark.parametrize("m", [1, 70, 1000])
+# every width with 1 and 70 rows, and with 1000 rows while the matrix stays within 8e6 elements
+SHAPES = [(m, n) for m in (1, 70, 1000) for n in WIDTHS if m * n <= 8_000_000]
+
+
+@pytest.mark.parametrize("m,n", SHAPES)
 def test_shapes(m, n):
-    if m * n > 8_000_000:
-        pytest.skip("covered by smaller m")
     check(datagen.dense_problem(m, n, seed=m * 31 + n, x_dtype="bf16", z="uniform", beta=0.5))
 
 
