@@ -211,13 +211,22 @@ xtvxy_status dense_workspace_query(int64_t m, int64_t n, int64_t ldx, size_t* by
   if (m < 0 || n < 0 || ldx < (n > 1 ? n : 1)) return XTVXY_ERROR_INVALID_VALUE;
   *bytes = 0;
   if (m == 0 || n == 0) return XTVXY_SUCCESS;
+  // the larger of the two plans (X 16-byte aligned or not); a width that only an aligned X
+  // supports (4-byte loads cover fewer columns per group) takes the aligned plan's size
   size_t best = 0;
+  xtvxy_status first_error = XTVXY_SUCCESS;
+  int planned = 0;
   for (int aligned = 0; aligned < 2; ++aligned) {
     xtvxy_launch_params p;
     xtvxy_status st = dense_plan_query(m, n, ldx, aligned, nullptr, &p, elem_bytes);
-    if (st != XTVXY_SUCCESS) return st;
+    if (st != XTVXY_SUCCESS) {
+      if (first_error == XTVXY_SUCCESS) first_error = st;
+      continue;
+    }
+    ++planned;
     if ((size_t)p.workspace_bytes > best) best = (size_t)p.workspace_bytes;
   }
+  if (planned == 0) return first_error;
   *bytes = best;
   return XTVXY_SUCCESS;
 }
@@ -663,7 +672,12 @@ hipError_t allow_dynamic_lds(const void* fn) {
   int lds = 0;
   e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
   if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipFuncAttributes attr;
+  e = hipFuncGetAttributes(&attr, fn);
+  if (e != hipSuccess) return e;
+  const int dynamic = lds - (int)attr.sharedSizeBytes;  // the kernel's static LDS comes out of the same budget
+  if (dynamic <= 0) return hipErrorInvalidValue;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dynamic);
   if (e != hipSuccess) return e;
   g_lds_done.insert({dev, fn});
   return hipSuccess;

@@ -105,8 +105,8 @@ struct CsrBinArgs {
   float* partial2;         // [max_units][2^bin_shift] per-unit sums of the bin's columns
 };
 
-// Lets kernel `fn` take up to the device's whole LDS as dynamic LDS. The attribute is set once per
-// (device, kernel) for the process; later calls only look it up (api.cpp).
+// Lets kernel `fn` take as dynamic LDS all of the device's LDS that its static LDS leaves. The
+// attribute is set once per (device, kernel) for the process; later calls only look it up (api.cpp).
 hipError_t allow_dynamic_lds(const void* fn);
 
 // Kernel launchers (dense.hip, csr.hip, aggregate.hip). Each returns the first

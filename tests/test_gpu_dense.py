@@ -229,10 +229,19 @@ def test_helpers_on_a_non_current_stream():
     s = torch.cuda.Stream()
     note("dense on a side stream")
     with torch.cuda.stream(torch.cuda.current_stream()):
-        outs = [xt.dense(d.X, d.y, d.v, d.z, p.alpha, p.beta, m=p.m, n=p.n, stream=s) for _ in range(3)]
+        outs = [xt.dense(d.X, d.y, d.v, d.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, stream=s) for _ in range(3)]
         junk = [torch.full((1 << 22,), float("nan"), device=d.X.device) for _ in range(8)]  # reuse pressure
     s.synchronize()
     torch.cuda.synchronize()
     del junk
     for o in outs:
         assert_parity(o.cpu().numpy(), ref, bnd, "side stream")
+
+
+def test_workspace_query_for_widths_only_aligned_X_supports():
+    # beyond 262,144 columns only 16-byte loads (an aligned X) give a plan: the workspace query
+    # must return that plan's size instead of failing on the unaligned one
+    m, n = 16, 300_000
+    need = xt.xtvxy_dense_f32_workspace_size(m, n, n)
+    assert need == xt.xtvxy_dense_f32_plan(m, n, n, 1).workspace_bytes
+    check(datagen.dense_problem(m, n, seed=43), what="aligned-only width")
