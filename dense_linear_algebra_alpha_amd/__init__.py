@@ -32,7 +32,8 @@ __all__ = [
     "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
     "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
-    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
+    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe",
+    "xtvxy_dense_f32_noalloc", "xtvxy_dense_f32_noalloc_max_workspace", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
     "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
@@ -60,6 +61,16 @@ def xtvxy_set_kernel_timing_events(before_main, after_main):
 
 def xtvxy_test_group_wait(polls: int, unanswered: int):
     return _abi.call("xtvxy_test_group_wait", int(polls), int(unanswered))
+
+
+def xtvxy_dense_f32_noalloc_max_workspace() -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_dense_f32_noalloc_max_workspace", ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_dense_f32_noalloc(m, n, alpha, X, ldx, v, y, beta, z, out, stream):
+    return _abi.call("xtvxy_dense_f32_noalloc", m, n, alpha, X, ldx, v, y, beta, z, out, stream)
 
 
 def xtvxy_read_probe(buffer, nbytes, grid, sink, stream):

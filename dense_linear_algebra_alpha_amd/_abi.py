@@ -128,6 +128,8 @@ SIGNATURES = {
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
     "xtvxy_test_group_wait": [_i32, _i32],
     "xtvxy_read_probe": [_vp, _sz, _i64, _vp, _vp],
+    "xtvxy_dense_f32_noalloc_max_workspace": [_P(_sz)],
+    "xtvxy_dense_f32_noalloc": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_dense_f32_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
                              _P(xtvxy_tune_report)],
     "xtvxy_dense_bf16_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,

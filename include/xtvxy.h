@@ -164,6 +164,22 @@ xtvxy_status xtvxy_dense_f32_ex(int64_t m, int64_t n, float alpha, const float *
 xtvxy_status xtvxy_dense_f32_plan_complete(int64_t m, int64_t n, int64_t ldx,
                                            const xtvxy_device_info *dev, xtvxy_launch_params *plan);
 
+/* For callers that cannot allocate device memory or provide a workspace (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): xtvxy_dense_f32 with the same
+ * arguments minus the workspace, which is instead a fixed array of the library in device memory
+ * (xtvxy_dense_f32_noalloc_max_workspace bytes, 32 MiB, held by every device the library runs on
+ * until the process ends; its address is looked up on the first call on each device). Calls no
+ * allocating routine. Shapes whose workspace (xtvxy_dense_f32_workspace_size) exceeds the array
+ * return XTVXY_ERROR_WORKSPACE before anything is enqueued; other errors as xtvxy_dense_f32, and
+ * the same result bit for bit (same launch plan). All calls on one device share the array:
+ * calls that overlap in time on one device (concurrent streams or threads) race and give
+ * undefined results; calls ordered on one stream are safe (the array keeps the last call's
+ * contents, and each call clears what must start at zero). */
+xtvxy_status xtvxy_dense_f32_noalloc_max_workspace(size_t *bytes);
+xtvxy_status xtvxy_dense_f32_noalloc(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx,
+                                     const float *v, const float *y, float beta, const float *z, float *out,
+                                     hipStream_t stream);
+
 /* Reduced-precision storage of dense X: the same pattern with X held as bf16 (bfloat16 bit
  * patterns, uint16_t; an element is the upper 16 bits of an fp32 and widens to it exactly).
  * v, y, z and out stay fp32 and every operation is fp32 as in xtvxy_dense_f32, so the result is
