@@ -19,7 +19,7 @@ from __future__ import annotations
 import ctypes
 
 from . import _abi
-from ._abi import (XTVXY_CSR_TILES, XTVXY_CSR_WAVES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
+from ._abi import (XTVXY_CSR_ROWS, XTVXY_CSR_TILES, XTVXY_CSR_WAVES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
                    XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
                    XTVXY_UNFUSED_EXPLICIT_TRANSPOSE, XTVXY_UNFUSED_TRANSPOSE_OP,
                    XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,
@@ -42,6 +42,9 @@ __all__ = [
     "xtvxy_tune_cache_save", "xtvxy_tune_cache_load", "xtvxy_tune_report", "dense_tune", "csr_tune",
     "xtvxy_dense_bf16_workspace_size", "xtvxy_dense_bf16_plan", "xtvxy_dense_bf16_plan_complete",
     "xtvxy_dense_bf16", "xtvxy_dense_bf16_ex", "xtvxy_dense_bf16_tune",
+    "xtvxy_csr_f32_analyse", "xtvxy_csr_f32_analysis_destroy", "xtvxy_csr_f32_analysed_plan",
+    "xtvxy_csr_f32_analysed_plan_complete", "xtvxy_csr_f32_analysed_workspace_size", "xtvxy_csr_f32_analysed",
+    "xtvxy_csr_f32_analysed_ex", "CsrAnalysis",
 ]
 
 load = _abi.load
@@ -193,6 +196,44 @@ def xtvxy_csr_f32_tmv_ex(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z,
                          stream, force):
     return _abi.call("xtvxy_csr_f32_tmv_ex", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out,
                      workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_f32_analyse(m, n, nnz, row_ptr, col_idx, stream) -> int:
+    h = ctypes.c_void_p()
+    _abi.call("xtvxy_csr_f32_analyse", m, n, nnz, row_ptr, col_idx, stream, ctypes.byref(h))
+    return h.value or 0
+
+
+def xtvxy_csr_f32_analysis_destroy(analysis):
+    return _abi.call("xtvxy_csr_f32_analysis_destroy", analysis)
+
+
+def xtvxy_csr_f32_analysed_plan(analysis) -> xtvxy_launch_params:
+    p = xtvxy_launch_params()
+    _abi.call("xtvxy_csr_f32_analysed_plan", analysis, ctypes.byref(p))
+    return p
+
+
+def xtvxy_csr_f32_analysed_plan_complete(analysis, plan: xtvxy_launch_params) -> xtvxy_launch_params:
+    _abi.call("xtvxy_csr_f32_analysed_plan_complete", analysis, ctypes.byref(plan))
+    return plan
+
+
+def xtvxy_csr_f32_analysed_workspace_size(analysis) -> int:
+    b = ctypes.c_size_t()
+    _abi.call("xtvxy_csr_f32_analysed_workspace_size", analysis, ctypes.byref(b))
+    return b.value
+
+
+def xtvxy_csr_f32_analysed(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream):
+    return _abi.call("xtvxy_csr_f32_analysed", analysis, alpha, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_f32_analysed_ex(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream,
+                              force):
+    return _abi.call("xtvxy_csr_f32_analysed_ex", analysis, alpha, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
 
 
 def xtvxy_csr_check(m, n, nnz, row_ptr, col_idx, d_flag, stream):
@@ -511,6 +552,67 @@ def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, worksp
                                       _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
+
+
+class CsrAnalysis:
+    """A structure analysis of one CSR matrix (xtvxy_csr_f32_analyse) and calls that use it: the
+    columns relabelled by frequency, the rows grouped by length class and the model's plan. It keeps
+    references to row_ptr (read by every call) and col_idx; values change per call."""
+
+    def __init__(self, row_ptr, col_idx, n, stream=None):
+        torch = _torch()
+        device = row_ptr.device
+        for name, t in (("row_ptr", row_ptr), ("col_idx", col_idx)):
+            if t.dtype != torch.int32 or t.device != device or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous int32 tensor on %s" % (name, device))
+        m, nnz = row_ptr.numel() - 1, col_idx.numel()
+        self.m, self.n, self.nnz, self.device = m, int(n), nnz, device
+        self._keep = (row_ptr, col_idx)
+        self.handle = xtvxy_csr_f32_analyse(m, int(n), nnz, row_ptr.data_ptr(),
+                                            col_idx.data_ptr() if nnz else None, _stream_handle(stream))
+
+    def plan(self) -> xtvxy_launch_params:
+        return xtvxy_csr_f32_analysed_plan(self.handle)
+
+    def complete(self, plan: xtvxy_launch_params) -> xtvxy_launch_params:
+        return xtvxy_csr_f32_analysed_plan_complete(self.handle, plan)
+
+    def __call__(self, values, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None,
+                 stream=None):
+        torch = _torch()
+        if values.dtype != torch.float32 or values.numel() != self.nnz or not values.is_contiguous():
+            raise ValueError("values must be a contiguous float32 tensor of nnz elements")
+        _check_vec("y", y, self.n, self.device)
+        _check_vec("v", v, self.m, self.device, required=False)
+        _check_vec("z", z, self.n, self.device, required=beta != 0)
+        made_out = out is None
+        if made_out:
+            out = torch.empty(self.n, dtype=torch.float32, device=self.device)
+        _check_vec("out", out, self.n, self.device)
+        need = xtvxy_csr_f32_analysed_workspace_size(self.handle) if plan is None else int(plan.workspace_bytes)
+        made_ws = workspace is None
+        if made_ws:
+            workspace = _workspace(need, self.device)
+        ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
+        args = (self.handle, float(alpha), _ptr(values) if self.nnz else None, _ptr(v), y.data_ptr(), float(beta),
+                _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
+        if plan is None:
+            xtvxy_csr_f32_analysed(*args)
+        else:
+            xtvxy_csr_f32_analysed_ex(*args, plan)
+        _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
+        return out
+
+    def close(self):
+        if getattr(self, "handle", 0):
+            xtvxy_csr_f32_analysis_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class CsrUnfusedPlan:

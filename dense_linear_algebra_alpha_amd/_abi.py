@@ -26,6 +26,7 @@ XTVXY_DENSE_BLOCK_ROWS = 2
 XTVXY_DENSE_GROUP_ROWS = 3
 XTVXY_CSR_TILES = 11
 XTVXY_CSR_WAVES = 12
+XTVXY_CSR_ROWS = 13
 
 
 class xtvxy_device_info(ctypes.Structure):
@@ -127,6 +128,13 @@ SIGNATURES = {
     "xtvxy_csr_f32_unfused_reference": [_vp, _f32, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_set_kernel_timing_events": [_vp, _vp],
     "xtvxy_test_group_wait": [_i32, _i32],
+    "xtvxy_csr_f32_analyse": [_i64, _i64, _i64, _vp, _vp, _vp, _P(_vp)],
+    "xtvxy_csr_f32_analysis_destroy": [_vp],
+    "xtvxy_csr_f32_analysed_plan": [_vp, _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_analysed_plan_complete": [_vp, _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_analysed_workspace_size": [_vp, _P(_sz)],
+    "xtvxy_csr_f32_analysed": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_f32_analysed_ex": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp, _P(xtvxy_launch_params)],
     "xtvxy_read_probe": [_vp, _sz, _i64, _vp, _vp],
     "xtvxy_dense_f32_noalloc_max_workspace": [_P(_sz)],
     "xtvxy_dense_f32_noalloc": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp],

@@ -21,7 +21,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "model.cpp", "unfused.cpp", "logreg.cpp", "tune.cpp", "dense.hip", "csr.hip", "csr_waves.hip", "csr_bins.hip",
+SOURCES = ["api.cpp", "model.cpp", "unfused.cpp", "logreg.cpp", "tune.cpp", "csr_analysis.cpp", "dense.hip", "csr.hip",
+           "csr_waves.hip", "csr_rows.hip", "csr_bins.hip",
            "aggregate.hip", "logreg.hip", "probe.hip", "noalloc.hip"]
 HEADERS = ["internal.h", "device_util.h", "csr_common.h"]
 

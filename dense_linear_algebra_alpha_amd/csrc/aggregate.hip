@@ -13,7 +13,10 @@
 // in a fixed order, so the result is bitwise reproducible for a given plan.
 // The epilogue is also evaluated in fp64 and rounded once. beta == 0 never
 // reads z; out may alias z (each element is read before it is written by the
-// same thread).
+// same thread). After a CSR structure analysis the columns are relabelled by
+// frequency: the sums of relabelled column j then go to out[perm[j]], with
+// z[perm[j]] (perm a permutation, so each element is still read and written by
+// one thread).
 #include "internal.h"
 
 namespace xtvxy {
@@ -28,7 +31,8 @@ __global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __r
                                                                 int64_t ldp, const float* __restrict__ acc,
                                                                 int64_t n, float alpha, float beta, const float* z,
                                                                 float* out, BinPartials bins,
-                                                                const uint32_t* __restrict__ error) {
+                                                                const uint32_t* __restrict__ error,
+                                                                const int32_t* __restrict__ out_perm) {
   constexpr int kAggRows = kAggThreads / kAggCols;
   __shared__ double sh[kAggRows][kAggCols];
   const int tx = threadIdx.x % kAggCols, ty = threadIdx.x / kAggCols;
@@ -52,10 +56,12 @@ __global__ __launch_bounds__(kAggThreads) void aggregate_kernel(const float* __r
 #pragma unroll
     for (int k = 1; k < kAggRows; ++k) t += sh[k][tx];
     if (acc) t += (double)acc[j];
+    // relabelled columns: sum j belongs to column out_perm[j]
+    const int64_t oj = out_perm != nullptr ? (int64_t)out_perm[j] : j;
     double o = (double)alpha * t;
-    if (beta != 0.0f) o += (double)beta * (double)z[j];
+    if (beta != 0.0f) o += (double)beta * (double)z[oj];
     // a group-row wait that gave up left some partial sums incomplete: the result is NaN
-    out[j] = (error != nullptr && *error != 0u) ? __builtin_nanf("") : (float)o;
+    out[oj] = (error != nullptr && *error != 0u) ? __builtin_nanf("") : (float)o;
   }
 }
 
@@ -97,18 +103,18 @@ unsigned grid_for(int64_t count, int block) {
 
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
                             float alpha, float beta, const float* z, float* out, hipStream_t s,
-                            const BinPartials* bins, const uint32_t* error) {
+                            const BinPartials* bins, const uint32_t* error, const int32_t* out_perm) {
   if (n <= 0) return hipSuccess;
   const BinPartials none{nullptr, nullptr, 0, 0};
   if (n <= kNarrowOutput) {
     hipLaunchKernelGGL(aggregate_kernel<16>, dim3((unsigned)((n + 15) / 16)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error, out_perm);
   } else if (n <= kWideOutput) {
     hipLaunchKernelGGL(aggregate_kernel<64>, dim3((unsigned)((n + 63) / 64)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error, out_perm);
   } else {
     hipLaunchKernelGGL(aggregate_kernel<256>, dim3((unsigned)((n + 255) / 256)), dim3(kAggThreads), 0, s, partial,
-                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error);
+                       rows, ldp, acc, n, alpha, beta, z, out, bins ? *bins : none, error, out_perm);
   }
   return hipGetLastError();
 }

@@ -287,13 +287,16 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
 xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                     const xtvxy_launch_params* force) {
+                     const xtvxy_launch_params* force, const CsrExtras* extras = nullptr) {
   xtvxy_device_info d;
   xtvxy_status st = device_info(-1, &d);
   if (st != XTVXY_SUCCESS) return st;
   xtvxy_launch_params plan;
   st = csr_plan_for(m, n, nnz, d, force, &plan, mode == kCsrFused);
   if (st != XTVXY_SUCCESS) return st;
+  // the row-class kernel runs on an analysis's work list, and on the whole pattern only
+  if (plan.kernel == XTVXY_CSR_ROWS && (extras == nullptr || extras->rows == nullptr || mode != kCsrFused))
+    return XTVXY_ERROR_INVALID_VALUE;
   if (mode == kCsrTmv && plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
   if (mode == kCsrTmv && plan.y_window != 0) {  // no y to gather: the plan with no y window
     plan.y_window = 0;
@@ -319,6 +322,12 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   const bool binned = w.bins > 0;
   a.acc = (plan.lds_window < n && !binned) ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
   a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
+  if (extras) {
+    a.rows = extras->rows;
+    a.units = extras->units;
+    a.unit_prefix = extras->unit_prefix;
+    a.units_count = extras->units_count;
+  }
   CsrBinArgs bargs{};
   if (binned) {
     a.bins = w.bins;
@@ -354,7 +363,9 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   }
   const hipEvent_t before = g_before_main, after = g_after_main;
   if (before && after && mark(before, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  e = plan.kernel == XTVXY_CSR_WAVES ? launch_csr_waves(a, plan, stream, mode) : launch_csr(a, plan, stream, mode);
+  e = plan.kernel == XTVXY_CSR_ROWS    ? launch_csr_rows(a, plan, stream)
+      : plan.kernel == XTVXY_CSR_WAVES ? launch_csr_waves(a, plan, stream, mode)
+                                       : launch_csr(a, plan, stream, mode);
   if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   if (before && after && mark(after, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   BinPartials bp{bargs.partial2, bargs.unit_start, plan.lds_window, w.bin_shift};
@@ -363,7 +374,7 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
     if (e != hipSuccess) return XTVXY_ERROR_LAUNCH;
   }
   e = launch_aggregate(a.partial, (int64_t)w.partial_rows, plan.lds_window, a.acc, n, alpha, beta, z, out, stream,
-                       binned ? &bp : nullptr);
+                       binned ? &bp : nullptr, nullptr, extras ? extras->out_perm : nullptr);
   return launch_status(e);
 }
 
@@ -681,5 +692,22 @@ hipError_t allow_dynamic_lds(const void* fn) {
   if (e != hipSuccess) return e;
   g_lds_done.insert({dev, fn});
   return hipSuccess;
+}
+}  // namespace xtvxy
+
+namespace xtvxy {
+xtvxy_status csr_run_fused(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                           const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                           const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                           const xtvxy_launch_params* force, const CsrExtras* extras) {
+  return csr_run(kCsrFused, m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, ws, ws_bytes, stream,
+                 force, extras);
+}
+xtvxy_status current_device_info(xtvxy_device_info* d) { return device_info(-1, d); }
+hipError_t mark_before_main(hipStream_t s) {
+  return g_before_main && g_after_main ? hipEventRecord(g_before_main, s) : hipSuccess;
+}
+hipError_t mark_after_main(hipStream_t s) {
+  return g_before_main && g_after_main ? hipEventRecord(g_after_main, s) : hipSuccess;
 }
 }  // namespace xtvxy

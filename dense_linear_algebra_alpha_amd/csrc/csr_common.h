@@ -20,6 +20,15 @@ enum CsrColdMode { kColdNone = 0, kColdAtomic = 1, kColdBinned = 2 };
 // y[0, y_window) and global memory beyond.
 enum CsrYMode { kYGlobal = 0, kYLds = 1, kYSplit = 2 };
 
+// The wavefront's LDS writes made visible to its own later LDS reads: a wavefront's LDS
+// operations complete in order, so only the compiler has to be kept from moving accesses
+// across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Smallest r in [0, m] with rp[r] >= target (m when none), by one full wavefront: each round
 // probes 64 evenly spaced positions and keeps the span between the last probe below the target
 // and the first at or above it.

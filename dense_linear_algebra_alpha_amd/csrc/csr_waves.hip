@@ -41,15 +41,6 @@ namespace {
 typedef int32_t i4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
-// The wavefront's LDS writes made visible to its own later LDS reads: a wavefront's LDS
-// operations complete in order, so only the compiler has to be kept from moving accesses
-// across this point.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // The loads of one tile, held in registers while the previous tile is processed.
 template <int K>
 struct WaveTile {

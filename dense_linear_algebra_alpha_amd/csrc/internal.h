@@ -37,6 +37,17 @@ constexpr size_t kCsrBinStateBytes = 32;
 // dynamic LDS: output and y windows, then each wavefront's bin state (6 words per bin).
 constexpr size_t kCsrWaveBinStateBytes = 24;
 constexpr size_t csr_waves_static_lds(int blk) { return (size_t)(blk / 64) * (512 + 512) + 4 * (size_t)blk; }
+// Row-class CSR kernel (csr_rows.hip): no static LDS; the dynamic LDS holds the output and y
+// windows, then each wavefront's bin state (6 words per bin), laid out as csr_waves_dynamic_lds.
+constexpr int kRowsSlots = 16;        // entry slots per lane and batch (four 16-byte quads)
+constexpr int kRowsVeryLong = 7;      // class of the rows longer than a wavefront's 64 * 16 slots
+constexpr int kRowsUnitEntries = 4096;  // entries a work unit of short-row batches aims at
+// Class of a nonempty row of `len` entries: the smallest c with len + 3 <= 16 * 2^c (a group of
+// 2^c lanes covers the row's quads, whatever the row's first entry mod 4), kRowsVeryLong beyond 2^6.
+constexpr int csr_row_class(int64_t len) {
+  return len + 3 <= 16 ? 0 : len + 3 <= 32 ? 1 : len + 3 <= 64 ? 2 : len + 3 <= 128 ? 3
+       : len + 3 <= 256 ? 4 : len + 3 <= 512 ? 5 : len + 3 <= 1024 ? 6 : kRowsVeryLong;
+}
 constexpr size_t csr_waves_dynamic_lds(int64_t window, int64_t y_window, int32_t bins, int blk) {
   return (((size_t)(window + y_window) * 4 + 7) & ~(size_t)7) +
          (bins > 0 ? (size_t)bins * kCsrWaveBinStateBytes * (size_t)(blk / 64) : 0);
@@ -87,6 +98,12 @@ struct CsrArgs {
   int2* pool;              // [P][kBinChunkItems] items {column, product bits}
   int32_t* chunk_bin;      // [P] bin of each handed-out chunk
   int32_t* chunk_fill;     // [P] items in each handed-out chunk
+  // row-class kernel (csr_rows.hip): the analysis's nonempty rows grouped by class and its work
+  // units {first position in rows, row count, class, 0}, with unit_prefix[u] = entries before unit u
+  const int32_t* rows;
+  const int32_t* units;
+  const int32_t* unit_prefix;  // [units_count + 1]
+  int32_t units_count;
 };
 
 // Arguments of the bin passes (csr_bins.hip) that follow a binned fused launch.
@@ -119,6 +136,13 @@ enum CsrLaunchMode { kCsrFused = 0, kCsrRowdot = 1, kCsrTmv = 2 };
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
 // The same launches by the wavefront kernel (plan kernel XTVXY_CSR_WAVES).
 hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode = kCsrFused);
+// The row-class kernel (plan kernel XTVXY_CSR_ROWS; the fused pattern only).
+hipError_t launch_csr_rows(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s);
+// Structure analysis kernels (csr_rows.hip): counts[col] += 1 for every stored entry (counts
+// zeroed by the caller); out[p] = slot[col_idx[p]]; yp[s] = y[perm[s]].
+hipError_t launch_col_count(const int32_t* col_idx, int64_t nnz, uint32_t* counts, hipStream_t s);
+hipError_t launch_relabel(const int32_t* col_idx, int64_t nnz, const int32_t* slot, int32_t* out, hipStream_t s);
+hipError_t launch_permute(const float* y, const int32_t* perm, int64_t n, float* yp, hipStream_t s);
 // Bin passes: group the handed-out chunks by bin, then accumulate every unit of a bin in LDS.
 hipError_t launch_csr_bins(const CsrBinArgs& a, hipStream_t s);
 // Per-bin partial sums for the aggregation (null: no binning).
@@ -133,10 +157,13 @@ struct BinPartials {
 //          + (beta != 0 ? beta * z[j] : 0),
 // in fp64, the partial rows summed in ascending order, rounded once.
 // When `error` is given and the word it points to is nonzero when the kernel runs (a group-row
-// wait gave up), every out[j] is NaN instead.
+// wait gave up), every out[j] is NaN instead. With `out_perm` (columns relabelled by a CSR
+// analysis) the sums are those of relabelled column j, and the result goes to
+// out[out_perm[j]] with z[out_perm[j]].
 hipError_t launch_aggregate(const float* partial, int64_t rows, int64_t ldp, const float* acc, int64_t n,
                             float alpha, float beta, const float* z, float* out, hipStream_t s,
-                            const BinPartials* bins = nullptr, const uint32_t* error = nullptr);
+                            const BinPartials* bins = nullptr, const uint32_t* error = nullptr,
+                            const int32_t* out_perm = nullptr);
 // out[j] = (beta != 0) ? beta * z[j] : 0
 hipError_t launch_beta_only(int64_t n, float beta, const float* z, float* out, hipStream_t s);
 // p[i] = 0 for i < count (a kernel, so that the call stays graph-capturable)
@@ -162,6 +189,10 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
                        xtvxy_launch_params* p, bool fused = true);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p);
+// The row-class kernel's plan for an analysed matrix whose columns are relabelled most frequent
+// first: covered[k] = entries in the k most frequent columns (k = 0..n).
+xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
+                            const int64_t* covered, xtvxy_launch_params* p);
 
 // Argument checks shared by the fused entry points and the comparator (api.cpp). On
 // success *quick tells that only out = beta z (or nothing, when n == 0) remains to do.
@@ -170,6 +201,27 @@ xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const void* X, 
 xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
                             float beta, const float* z, const float* out, bool* quick);
+
+// What an analysed CSR call adds to a fused CSR launch: the row-class work list (for the
+// XTVXY_CSR_ROWS kernel) and the permutation of the relabelled output columns.
+struct CsrExtras {
+  const int32_t* rows;
+  const int32_t* units;
+  const int32_t* unit_prefix;
+  int32_t units_count;
+  const int32_t* out_perm;  // sums of relabelled column j go to out[out_perm[j]]
+};
+// The fused CSR path for checked arguments (api.cpp): the plan (`force`, completed here; the model's
+// when null), the main kernel, the bin passes and the aggregation, on `stream`.
+xtvxy_status csr_run_fused(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                           const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                           const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                           const xtvxy_launch_params* force, const CsrExtras* extras);
+// The device description of the current device (cached).
+xtvxy_status current_device_info(xtvxy_device_info* d);
+// Records the measurement hook's events around a main kernel (api.cpp).
+hipError_t mark_before_main(hipStream_t s);
+hipError_t mark_after_main(hipStream_t s);
 
 // Halves of the pattern through the rocSPARSE comparator's plan (unfused.cpp).
 xtvxy_status unfused_rowdot(xtvxy_csr_unfused_plan p, const float* y, float* t, hipStream_t stream);

@@ -104,7 +104,9 @@ CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch
   while ((1 << shift) < p.bin_columns) ++shift;
   w.bin_shift = shift;
   w.bins = (int32_t)ceil_div(n - p.lds_window, (int64_t)p.bin_columns);
-  const int64_t owners = p.kernel == XTVXY_CSR_WAVES ? p.grid * (int64_t)(p.block_threads / 64) : p.grid;
+  const int64_t owners = p.kernel == XTVXY_CSR_WAVES || p.kernel == XTVXY_CSR_ROWS
+                             ? p.grid * (int64_t)(p.block_threads / 64)
+                             : p.grid;
   w.pool_chunks = ceil_div(std::max<int64_t>(nnz, 1), kBinChunkItems) + owners * (int64_t)w.bins;
   w.max_units = ceil_div(w.pool_chunks, kBinUnitChunks) + w.bins;
   w.counter_off = off;
@@ -247,6 +249,8 @@ int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
   if (p.kernel == XTVXY_CSR_WAVES)
     return (int64_t)(csr_waves_dynamic_lds(p.lds_window, p.y_window, bins, p.block_threads) +
                      csr_waves_static_lds(p.block_threads));
+  if (p.kernel == XTVXY_CSR_ROWS)
+    return (int64_t)csr_waves_dynamic_lds(p.lds_window, p.y_window, bins, p.block_threads);
   int64_t lds = ((int64_t)p.lds_window + (int64_t)p.y_window) * (int64_t)sizeof(float);
   if (bins > 0) lds = ((lds + 7) & ~(int64_t)7) + (int64_t)bins * (int64_t)kCsrBinStateBytes;
   return lds + (int64_t)csr_static_lds(p.entries_per_thread, p.block_threads);
@@ -254,15 +258,17 @@ int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
 
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p) {
-  if ((p->kernel != XTVXY_CSR_TILES && p->kernel != XTVXY_CSR_WAVES) || p->grid <= 0 || p->grid > INT32_MAX)
+  if ((p->kernel != XTVXY_CSR_TILES && p->kernel != XTVXY_CSR_WAVES && p->kernel != XTVXY_CSR_ROWS) ||
+      p->grid <= 0 || p->grid > INT32_MAX)
     return XTVXY_ERROR_INVALID_VALUE;
-  // (threads, entries per thread): tiles 256 x 4, 256 x 8 or 512 x 8; wavefronts 256, 512 or 1024 x 8
+  // (threads, entries per thread): tiles 256 x 4, 256 x 8 or 512 x 8; wavefronts 256, 512 or 1024 x 8;
+  // row classes 256, 512 or 1024 x 16
+  const bool any_blk = p->block_threads == 256 || p->block_threads == 512 || p->block_threads == 1024;
   const bool shape_ok =
       p->kernel == XTVXY_CSR_TILES
           ? (p->block_threads == 256 && (p->entries_per_thread == 4 || p->entries_per_thread == 8)) ||
                 (p->block_threads == 512 && p->entries_per_thread == 8)
-          : (p->block_threads == 256 || p->block_threads == 512 || p->block_threads == 1024) &&
-                p->entries_per_thread == 8;
+          : any_blk && p->entries_per_thread == (p->kernel == XTVXY_CSR_ROWS ? kRowsSlots : 8);
   if (!shape_ok) return XTVXY_ERROR_INVALID_VALUE;
   if (p->lds_window < 0 || p->lds_window > n || p->y_window < 0 || p->y_window > n)
     return XTVXY_ERROR_INVALID_VALUE;
@@ -375,6 +381,66 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
     if (complete_csr(m, n, nnz, d, &q) == XTVXY_SUCCESS) *p = q;
   }
   return XTVXY_SUCCESS;
+}
+
+}  // namespace xtvxy
+
+namespace xtvxy {
+
+// Row-class kernel on an analysed matrix (columns relabelled most frequent first, so that the
+// windows [0, W) and [0, Wy) hold the hottest columns). Every wavefront works alone, so latency is
+// hidden by wavefronts, not barriers: one workgroup of 1024 threads per CU gets a CU's whole LDS
+// for the windows. When both windows hold all of n nothing is cold; otherwise the LDS left after
+// the wavefronts' bin state is split between the two windows to minimise the cost of what falls
+// outside them, counted from the analysis: an entry whose column is outside the y window is one
+// gather from global memory (an L2 request, and an HBM read of a line when it misses), one
+// outside the output window is a binned item (an 8-byte store, its read in the bin pass and an
+// LDS add there); both are priced alike (kRowsColdGather, kRowsColdItem, seconds per entry).
+constexpr double kRowsColdGather = 8.0e-12;
+constexpr double kRowsColdItem = 8.0e-12;
+
+xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d, const int64_t* covered,
+                            xtvxy_launch_params* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->kernel = XTVXY_CSR_ROWS;
+  p->vec = 1;
+  p->chunks = 1;
+  p->group = 1;
+  p->entries_per_thread = kRowsSlots;
+  p->block_threads = 1024;
+  p->grid = std::max<int64_t>(1, d.compute_units);
+  const int waves = p->block_threads / 64;
+  const int64_t lds = d.lds_bytes - 256;  // a little slack for the launch's own use
+  double cold_cost = 0.0;
+  if ((int64_t)n * 8 <= lds) {
+    p->lds_window = (int32_t)n;
+    p->y_window = (int32_t)n;
+  } else {
+    double best = 1e300;
+    for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
+      const int64_t bins_max = ceil_div(n, bc);
+      if (bins_max > kMaxBins) continue;
+      const int64_t state = bins_max * (int64_t)kCsrWaveBinStateBytes * waves;
+      const int64_t cols = std::max<int64_t>(0, (lds - state) / 4 - 2);
+      const int64_t step = std::max<int64_t>(256, cols / 256);
+      for (int64_t w = 0; w <= std::min<int64_t>(cols, n); w += step) {
+        const int64_t wy = std::min<int64_t>(n, cols - w);
+        const double cost = (double)(nnz - (covered ? covered[w] : (int64_t)((double)nnz * w / n))) * kRowsColdItem +
+                            (double)(nnz - (covered ? covered[wy] : (int64_t)((double)nnz * wy / n))) * kRowsColdGather;
+        if (cost < best * 0.9999) {
+          best = cost;
+          p->lds_window = (int32_t)w;
+          p->y_window = (int32_t)wy;
+          p->bin_columns = bc;
+        }
+      }
+    }
+    if (best > 1e299) return XTVXY_ERROR_UNSUPPORTED;
+    cold_cost = best;
+  }
+  const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
+  p->predicted_seconds = io_bytes / (kSustained * d.hbm_bytes_per_s) + cold_cost + 4 * kLaunch;
+  return complete_csr(m, n, nnz, d, p);
 }
 
 }  // namespace xtvxy

@@ -93,7 +93,13 @@ enum {
    * tiles of whole rows of its own (at most 64 rows and 512 entries), so the
    * workgroup never waits at a barrier per tile; block_threads 256, 512 or 1024,
    * entries_per_thread 8 */
-  XTVXY_CSR_WAVES = 12
+  XTVXY_CSR_WAVES = 12,
+  /* rows by length class (needs a structure analysis, xtvxy_csr_f32_analyse): a group of 2^c
+   * lanes takes each row of class c (rows of up to 16 * 2^c - 3 entries) with 16 entry slots per
+   * lane, a wavefront takes each row longer than 1021 entries in slices; every wavefront works
+   * alone, the scatter is the others' (LDS window, then atomics or bins); block_threads 256, 512
+   * or 1024, entries_per_thread 16 */
+  XTVXY_CSR_ROWS = 13
 };
 
 /* Launch parameters chosen by the analytical model (the *_plan queries) or
@@ -224,6 +230,49 @@ xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha,
 
 xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
                                          const xtvxy_device_info *dev, xtvxy_launch_params *plan);
+
+/* Structure analysis of a CSR matrix, made once and used by any number of calls whose values
+ * change ("On optimizing machine learning workloads via kernel fusion", abstract: the launch
+ * parameters come from the input's characteristics; here they are read from the structure):
+ *   - the columns are relabelled by how many entries they hold, most first (ties by column), so
+ *     that the output and y windows kept in LDS hold the hottest columns whatever their indices;
+ *     the analysis keeps the relabelled column indices (4 nnz bytes of device memory) and the
+ *     permutation (4 n bytes); each call gathers y into that order (n floats of its workspace)
+ *     and writes every output column back to its own index, so results are those of
+ *     xtvxy_csr_f32 on the caller's matrix (up to the order of fp32 additions);
+ *   - the nonempty rows are grouped by length class for the row-class kernel (XTVXY_CSR_ROWS; a
+ *     row list of 4 bytes per row and work units of about 4096 entries);
+ *   - the model's plan for the analysed matrix (the window sizes from the column counts).
+ * xtvxy_csr_f32_analyse is a set-up call: it allocates device memory, synchronises `stream` and
+ * reads back row_ptr and the column counts. It keeps row_ptr and values pointers of no call:
+ * row_ptr (device) must stay valid and unchanged while the analysis is used (each call reads it);
+ * col_idx is read only here. The same CSR conventions and errors as xtvxy_csr_f32 (a malformed
+ * structure is undefined behaviour). A matrix with no rows, columns or entries gives an analysis
+ * whose calls compute out = beta * z. Destroy it before freeing row_ptr; not thread-safe per
+ * analysis; used on the device current when it was made (XTVXY_ERROR_INVALID_VALUE otherwise). */
+typedef struct xtvxy_csr_analysis_s *xtvxy_csr_analysis;
+xtvxy_status xtvxy_csr_f32_analyse(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                   const int32_t *col_idx, hipStream_t stream, xtvxy_csr_analysis *analysis);
+xtvxy_status xtvxy_csr_f32_analysis_destroy(xtvxy_csr_analysis analysis);
+/* The model's plan for the analysed matrix (workspace_bytes included). */
+xtvxy_status xtvxy_csr_f32_analysed_plan(xtvxy_csr_analysis analysis, xtvxy_launch_params *plan);
+/* Checks a caller-edited plan for the analysed matrix and fills in its workspace_bytes. Any CSR
+ * kernel: XTVXY_CSR_ROWS (the model's), or XTVXY_CSR_TILES / XTVXY_CSR_WAVES on the relabelled
+ * columns. */
+xtvxy_status xtvxy_csr_f32_analysed_plan_complete(xtvxy_csr_analysis analysis, xtvxy_launch_params *plan);
+/* Workspace bytes of xtvxy_csr_f32_analysed (the model's plan). */
+xtvxy_status xtvxy_csr_f32_analysed_workspace_size(xtvxy_csr_analysis analysis, size_t *bytes);
+/* out = alpha * X^T (v .* (X y)) + beta * z for the analysed matrix with these values (nnz fp32 in
+ * the caller's storage order). Pointer rules, aliasing rules (out against values, v, y and row_ptr;
+ * out == z allowed) and errors as xtvxy_csr_f32; the workspace is the caller's. Asynchronous on
+ * `stream`. The _ex form takes a plan completed by xtvxy_csr_f32_analysed_plan_complete. */
+xtvxy_status xtvxy_csr_f32_analysed(xtvxy_csr_analysis analysis, float alpha, const float *values, const float *v,
+                                    const float *y, float beta, const float *z, float *out, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis analysis, float alpha, const float *values,
+                                       const float *v, const float *y, float beta, const float *z, float *out,
+                                       void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                       const xtvxy_launch_params *force);
 
 /* The two halves of the pattern on their own, for CSR X ("On optimizing machine learning
  * workloads via kernel fusion", abstract: the pattern chains X y and X^T (.); iterative solvers

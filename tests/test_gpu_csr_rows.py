@@ -1,0 +1,240 @@
+"""GPU parity of the analysed CSR path (xtvxy_csr_f32_analyse / xtvxy_csr_f32_analysed: columns
+relabelled by frequency, rows by length class, the row-class kernel) against the fp64 oracle,
+through the C ABI."""
+import numpy as np
+import pytest
+
+import datagen
+import dense_linear_algebra_alpha_amd as xt
+from gpu_util import assert_parity, csr_oracle, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+LDS = 163840
+
+
+class Analysed:
+    """A CsrProblem on the GPU with its analysis."""
+
+    def __init__(self, p, values_offset=0):
+        import torch
+        self.p = p
+        self.rp, self.ci = to_dev(p.row_ptr), to_dev(p.col_idx)
+        if values_offset:
+            buf = torch.empty(p.nnz + values_offset, dtype=torch.float32, device="cuda")
+            buf[values_offset:].copy_(torch.from_numpy(p.values))
+            self.vals = buf[values_offset:]
+        else:
+            self.vals = to_dev(p.values)
+        self.y, self.v, self.z = to_dev(p.y), to_dev(p.v), to_dev(p.z)
+        self.an = xt.CsrAnalysis(self.rp, self.ci, p.n)
+
+    def run(self, plan=None, values=None, out=None, alpha=None, beta=None, z="default"):
+        import torch
+        p = self.p
+        r = self.an(self.vals if values is None else values, self.y, self.v, self.z if isinstance(z, str) else z,
+                    p.alpha if alpha is None else alpha, p.beta if beta is None else beta, out=out, plan=plan)
+        torch.cuda.synchronize()
+        return r.cpu().numpy()
+
+
+def rows_plan(an, blk=1024, grid=None, window=None, y_window=None, bin_columns=None, kernel=None, ept=None):
+    """The analysis's model plan with some fields replaced, completed for the analysed matrix."""
+    lp = an.plan()
+    if kernel is not None:
+        lp.kernel = kernel
+        lp.entries_per_thread = 16 if kernel == xt.XTVXY_CSR_ROWS else 8
+    if ept is not None:
+        lp.entries_per_thread = ept
+    lp.block_threads = blk
+    if grid is not None:
+        lp.grid = grid
+    if window is not None:
+        lp.lds_window = window
+    if y_window is not None:
+        lp.y_window = y_window
+    if bin_columns is not None:
+        lp.bin_columns = bin_columns
+    return an.complete(lp)
+
+
+def check(p, what="", plans=(None,), values_offset=0):
+    ref, bnd = csr_oracle(p)
+    a = Analysed(p, values_offset)
+    for plan in plans:
+        if callable(plan):
+            plan = plan(a.an)
+        note("analysed %s m=%d n=%d nnz=%d plan=%s" % (what or p.name, p.m, p.n, p.nnz,
+                                                      None if plan is None else plan.as_dict()))
+        assert_parity(a.run(plan=plan), ref, bnd, "analysed %s plan %s" % (what, None if plan is None else plan.as_dict()))
+    return a
+
+
+def matrix_with_lengths(lens, n, seed, alpha=0.8, beta=-0.6, sorted_cols=True, dup=False):
+    """CSR with the given row lengths (distinct random columns per row unless dup)."""
+    g = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int64)
+    rp = np.zeros(lens.size + 1, np.int64)
+    rp[1:] = np.cumsum(lens)
+    parts = []
+    for L in lens:
+        c = g.integers(0, n, size=L) if dup else g.choice(n, size=L, replace=False)
+        parts.append(np.sort(c) if sorted_cols else c)
+    cols = np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+    m, nnz = lens.size, int(rp[-1])
+    return datagen.CsrProblem(m, n, rp.astype(np.int32), cols, datagen.uniform(nnz, seed, "vals"),
+                              datagen.uniform(n, seed, "y"), datagen.uniform(m, seed, "v"),
+                              datagen.uniform(n, seed, "z"), alpha, beta, "lengths")
+
+
+@pytest.mark.parametrize("m,n", [(1, 1), (5, 7), (100, 3), (3000, 1000), (2500, 20000), (4000, 70000),
+                                 (700, 300000)])
+@pytest.mark.parametrize("mean_len", [1.0, 6.0, 40.0])
+def test_irregular_matrices(m, n, mean_len):
+    check(datagen.csr_random(m, n, seed=m + n + int(mean_len), mean_len=mean_len, empty_frac=0.2, dup_frac=0.1),
+          what="random")
+
+
+def test_every_row_class_and_its_boundaries():
+    # lengths around every class limit (16 * 2^c - 3), the very long class and beyond one slice,
+    # with row starts of every residue mod 4, between empty rows
+    limits = [16 * (1 << c) - 3 for c in range(7)]
+    lens = []
+    for L in limits:
+        lens += [L - 1, L, L + 1, 0]
+    lens += [1, 2, 3, 4, 5, 1021, 1022, 1024, 1025, 2047, 2048, 2049, 3071, 4099, 0, 7, 1]
+    n = 6000
+    for shift in range(4):  # shift every row start by prefixing a row of `shift` entries
+        p = matrix_with_lengths([shift] + lens, n, seed=10 + shift)
+        check(p, what="class boundaries shift %d" % shift)
+
+
+@pytest.mark.parametrize("blk", [256, 512, 1024])
+def test_forced_plans(blk):
+    # windows from none to all of n, y from global memory, LDS or split, atomics or bins (of 1024
+    # columns: many bins), a few grids
+    g = np.random.default_rng(blk)
+    lens = np.minimum(g.zipf(1.5, size=6000), 2500)  # every class, a few very long rows
+    lens[::11] = 0
+    p = matrix_with_lengths(lens, 9000, seed=blk, sorted_cols=False, dup=True)
+    assert np.diff(p.row_ptr).max() > 1021
+    plans = []
+    for w, yw in ((0, 0), (0, 9000), (7, 300), (4096, 0), (4096, 4096), (9000, 9000), (9000, 0)):
+        if (w + yw) * 4 + 40000 > LDS:
+            continue
+        for bc in ((0, 1024) if w < 9000 else (0,)):
+            for grid in (1, 5, 64):
+                plans.append(lambda an, w=w, yw=yw, bc=bc, grid=grid: rows_plan(
+                    an, blk=blk, grid=grid, window=w, y_window=yw, bin_columns=bc))
+    check(p, what="forced blk %d" % blk, plans=plans)
+
+
+def test_tile_and_wavefront_kernels_on_the_relabelled_columns():
+    p = datagen.csr_random(5000, 40000, seed=3, mean_len=25.0, empty_frac=0.1, dup_frac=0.05)
+    plans = [lambda an: rows_plan(an, blk=512, kernel=xt.XTVXY_CSR_TILES, grid=256, window=8000, y_window=2000,
+                                  bin_columns=16384),
+             lambda an: rows_plan(an, blk=256, kernel=xt.XTVXY_CSR_TILES, grid=64, window=4000, y_window=0,
+                                  bin_columns=0),
+             lambda an: rows_plan(an, blk=512, kernel=xt.XTVXY_CSR_WAVES, grid=128, window=6000, y_window=3000,
+                                  bin_columns=8192)]
+    check(p, what="relabelled, other kernels", plans=plans)
+
+
+@pytest.mark.parametrize("values_offset", [1, 2, 3])
+def test_misaligned_values(values_offset):
+    p = matrix_with_lengths([5, 0, 13, 14, 29, 100, 1100, 3, 2, 1], 3000, seed=21)
+    check(p, what="values offset %d" % values_offset, values_offset=values_offset)
+
+
+def test_values_change_between_calls_and_workspace_reuse():
+    import torch
+    p = datagen.csr_random(3000, 50000, seed=9, mean_len=40.0, empty_frac=0.1, dup_frac=0.1)
+    a = Analysed(p)
+    ws = torch.full((a.an.plan().workspace_bytes,), 255, dtype=torch.uint8, device="cuda")  # dirty workspace
+    for k in range(3):
+        vals = datagen.uniform(p.nnz, 100 + k, "vals")
+        q = datagen.CsrProblem(p.m, p.n, p.row_ptr, p.col_idx, vals, p.y, p.v, p.z, p.alpha, p.beta, "values %d" % k)
+        ref, bnd = csr_oracle(q)
+        note("analysed, values set %d" % k)
+        got = a.an(to_dev(vals), a.y, a.v, a.z, p.alpha, p.beta, workspace=ws)
+        torch.cuda.synchronize()
+        assert_parity(got.cpu().numpy(), ref, bnd, "values set %d" % k)
+
+
+def test_exact_integers_bitwise():
+    # integer data: every partial sum is exact in fp32, so any summation order gives the oracle's value
+    g = np.random.default_rng(12)
+    m, n = 4000, 30000
+    lens = np.minimum(g.zipf(1.6, size=m), 3000)
+    lens[::7] = 0
+    p = matrix_with_lengths(lens, n, seed=12, sorted_cols=False)
+    vals = g.integers(-1, 2, size=p.nnz).astype(np.float32)
+    y, v, z = (g.integers(-1, 2, size=k).astype(np.float32) for k in (n, m, n))
+    q = datagen.CsrProblem(m, n, p.row_ptr, p.col_idx, vals, y, v, z, 1.5, 0.5, "integers")
+    ref, _ = csr_oracle(q)
+    assert np.all(np.abs(ref) < 2 ** 23)
+    a = Analysed(q)
+    for plan in (None, lambda an: rows_plan(an, blk=256, grid=7, window=1000, y_window=500, bin_columns=1024)):
+        note("analysed exact integers plan %s" % plan)
+        got = a.run(plan=plan(a.an) if plan else None)
+        assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_special_cases():
+    import torch
+    p = datagen.csr_random(500, 800, seed=5, mean_len=20.0)
+    ref, bnd = csr_oracle(p)
+    a = Analysed(p)
+    # alpha == 0: beta z, values and y unread
+    note("analysed alpha 0")
+    nan_vals = torch.full((p.nnz,), float("nan"), device="cuda")
+    got = a.run(values=nan_vals, alpha=0.0)
+    assert np.array_equal(got, (np.float32(p.beta) * p.z).astype(np.float32))
+    # beta == 0: z unread
+    note("analysed beta 0, z NaN")
+    ref0 = datagen.CsrProblem(p.m, p.n, p.row_ptr, p.col_idx, p.values, p.y, p.v, None, p.alpha, 0.0, "b0")
+    r0, b0 = csr_oracle(ref0)
+    assert_parity(a.run(beta=0.0, z=torch.full((p.n,), float("nan"), device="cuda")), r0, b0, "beta 0")
+    # out == z in place
+    note("analysed out == z")
+    zz = a.z.clone()
+    got = a.an(a.vals, a.y, a.v, zz, p.alpha, p.beta, out=zz)
+    torch.cuda.synchronize()
+    assert_parity(got.cpu().numpy(), ref, bnd, "out == z")
+    # an empty matrix: out = beta z
+    for m, n in ((0, 5), (4, 5)):
+        rp = torch.zeros(m + 1, dtype=torch.int32, device="cuda")
+        an = xt.CsrAnalysis(rp, torch.zeros(0, dtype=torch.int32, device="cuda"), n)
+        z = torch.arange(n, dtype=torch.float32, device="cuda")
+        out = an(torch.zeros(0, device="cuda"), torch.ones(n, device="cuda"), None, z, 1.0, 2.0)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), 2.0 * np.arange(n, dtype=np.float32))
+
+
+def test_nan_stays_in_its_row():
+    # rows of 3, 1, 2, 6 and 1 entries: entries 0-2, 3, 4-5, 6-11, 12. A NaN at entry 3 (row 1)
+    # shares its 16-byte quad with row 0, an Inf at entry 4 (row 2) shares one with row 3: each
+    # must reach only its own row's columns
+    p = matrix_with_lengths([3, 1, 2, 6, 1], 40, seed=8)
+    vals = p.values.copy()
+    vals[3] = np.nan
+    vals[4] = np.inf
+    q = datagen.CsrProblem(p.m, p.n, p.row_ptr, p.col_idx, vals, p.y, p.v, p.z, 1.0, 1.0, "nan")
+    ref, bnd = csr_oracle(q)
+    assert np.isnan(ref).any() and np.isfinite(ref).any()
+    a = Analysed(q)
+    note("analysed NaN and Inf rows")
+    assert_parity(a.run(), ref, bnd, "NaN and Inf rows")
+
+
+@pytest.mark.parametrize("permuted", [False, True])
+def test_zipf_scaled(permuted):
+    p = datagen.csr_zipf(200_000, 200_000, seed=1, permute_columns=permuted)
+    check(p, what="zipf scaled permuted=%s" % permuted)
+
+
+@pytest.mark.parametrize("name", ["csr_5000000x1000000_zipf", "csr_5000000x1000000_zipf_permuted",
+                                  "csr_10000000x1000_logistic_hvp"])
+def test_full_size_workloads(name):
+    p = datagen.WORKLOADS[name]()
+    check(p, what=name)
