@@ -94,7 +94,8 @@ class HipEvents:
 def kernel_sources_hash(kind: str) -> str:
     csrc = os.path.join(ROOT, "dense_linear_algebra_alpha_amd", "csrc")
     files = ["device_util.h", "internal.h"] + {"csr": ["csr_common.h", "csr.hip"],
-                                                "csr_waves": ["csr_common.h", "csr_waves.hip"]}.get(kind, ["dense.hip"])
+                                                "csr_waves": ["csr_common.h", "csr_waves.hip"],
+                                                "csr_rows": ["csr_common.h", "csr_rows.hip"]}.get(kind, ["dense.hip"])
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
@@ -108,7 +109,7 @@ def kernel_name(plan) -> str:
     import dense_linear_algebra_alpha_amd as xt
     names = {xt.XTVXY_DENSE_WAVE_ROWS: "dense_wave_rows", xt.XTVXY_DENSE_BLOCK_ROWS: "dense_block_rows",
              xt.XTVXY_DENSE_GROUP_ROWS: "dense_group_rows", xt.XTVXY_CSR_TILES: "csr_fused",
-             xt.XTVXY_CSR_WAVES: "csr_waves"}
+             xt.XTVXY_CSR_WAVES: "csr_waves", xt.XTVXY_CSR_ROWS: "csr_rows"}
     return names.get(plan.kernel, "kernel%d" % plan.kernel)
 
 
@@ -363,8 +364,10 @@ def report_tuning(args, p, kind, abytes, env):
     return record
 
 
-def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headline, ctx):
-    """Times one workload's fused call (and its comparators); returns the record's fields."""
+def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headline, ctx, csr_path="plain"):
+    """Times one workload's fused call (and its comparators); returns the record's fields. CSR
+    workloads take the plain entry point (csr_path "plain") or the analysed one ("analysed": the
+    structure analysis made once, outside the timed region)."""
     import numpy as np
     import torch
 
@@ -431,16 +434,36 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
         env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
     else:
         rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
-        plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
-        forced = override(plan, plan_text)
-        if forced:
-            plan = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, plan)
-        ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
+        analysed = csr_path == "analysed"
+        analysis = None
+        if analysed:
+            # the structure analysis (column counts, relabelled columns, row classes): set-up,
+            # outside every timed region, like the comparators' plans below
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            analysis = xt.CsrAnalysis(rp, ci, p.n)
+            torch.cuda.synchronize()
+            analysis_s = time.perf_counter() - t0
+            plan = analysis.plan()
+            forced = override(plan, plan_text)
+            if forced:
+                plan = analysis.complete(plan)
+            ws_bytes = plan.workspace_bytes
+        else:
+            plan = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
+            forced = override(plan, plan_text)
+            if forced:
+                plan = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, plan)
+            ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uplan = uplan_t = None
 
         def fused():
-            if forced:
+            if analysed:
+                xt.xtvxy_csr_f32_analysed_ex(analysis.handle, p.alpha, vals.data_ptr(), xt._ptr(v), y.data_ptr(),
+                                             p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh,
+                                             plan if forced else None)
+            elif forced:
                 xt.xtvxy_csr_f32_ex(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
                                     xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
                                     ws_bytes, sh, plan)
@@ -462,7 +485,10 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
             uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
         else:
             unfused_explicit = None
-        shape = {"m": p.m, "n": p.n, "nnz": p.nnz}
+        shape = {"m": p.m, "n": p.n, "nnz": p.nnz, "entry_point": "xtvxy_csr_f32_analysed" if analysed
+                 else "xtvxy_csr_f32"}
+        if analysed:
+            shape["analysis_seconds"] = round(analysis_s, 4)
         env = {"rp": rp, "ci": ci, "vals": vals, "y": y, "v": v, "z": z, "out": out, "sh": sh}
 
     abytes = algorithmic_bytes(p)
@@ -520,7 +546,7 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
         "kernel_ms": percentiles(kernel_ms),
         "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 3),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": load_traffic(name, kname, "csr_waves" if kname == "csr_waves" else kind),
+                     "traffic": load_traffic(name, kname, kname if kname in ("csr_waves", "csr_rows") else kind),
                      "kernel_ms_mean": round(statistics.mean(kernel_ms), 5),
                      "kernel_ms_min": round(min(kernel_ms), 5)},
         "peaks": {"published_gbs": HBM_PEAK_GBS, "device_properties_gbs": ctx["device_peak_gbs"],
@@ -587,6 +613,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle runs for cpu_baseline")
     ap.add_argument("--also-cpu-budget", type=float, default=2.0, help="seconds of oracle runs per further workload")
     ap.add_argument("--fused-only", action="store_true", help="time the fused path only (for profilers)")
+    ap.add_argument("--csr-path", choices=("analysed", "plain", "both"), default="both",
+                    help="CSR workloads: the analysed entry point, the plain one, or both (the analysed call is "
+                         "the record's, the plain one under plain_call)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling measurement")
     ap.add_argument("--plan", default=None,
                     help="JSON object of launch-parameter fields that replace the model's choice, e.g. "
@@ -649,9 +678,24 @@ def main():
         ceiling = stream_read_ceiling(xt, torch, dev)
         ctx["ceiling_gbs"] = ceiling["gbs"]
         torch.cuda.empty_cache()
+    def measure(w, steps, warmup, cpu_budget, headline):
+        """The workload's record; a CSR workload with --csr-path both: the analysed call's record with
+        the plain call's under plain_call (same inputs, same comparators)."""
+        is_csr = w in datagen.WORKLOADS and w.startswith("csr_")
+        unf = 0 if args.no_unfused else args.unfused_steps
+        if not is_csr:
+            return measure_workload(w, args, steps, warmup, unf, cpu_budget, headline, ctx)
+        if args.csr_path != "both":
+            return measure_workload(w, args, steps, warmup, unf, cpu_budget, headline, ctx, args.csr_path)
+        r = measure_workload(w, args, steps, warmup, unf, cpu_budget, headline, ctx, "analysed")
+        torch.cuda.empty_cache()
+        plain = measure_workload(w, args, steps, warmup, 0, 0.0, headline, ctx, "plain")
+        r["plain_call"] = {k: plain[k] for k in ("value", "ms_per_step", "call_ms", "kernel_ms", "roofline", "config",
+                                                 "max_rel_err") if k in plain}
+        return r
+
     print("[bench] %s" % args.workload, file=sys.stderr, flush=True)
-    rec = measure_workload(args.workload, args, args.steps, args.warmup, 0 if args.no_unfused else args.unfused_steps,
-                           args.cpu_budget, True, ctx)
+    rec = measure(args.workload, args.steps, args.warmup, args.cpu_budget, True)
     if "tune" in rec:
         return
     torch.cuda.empty_cache()
@@ -675,8 +719,7 @@ def main():
     others = {}
     for w in also:
         print("[bench] %s" % w, file=sys.stderr, flush=True)
-        o = measure_workload(w, args, args.also_steps, args.also_warmup, 0 if args.no_unfused else args.unfused_steps,
-                             args.also_cpu_budget, False, ctx)
+        o = measure(w, args.also_steps, args.also_warmup, args.also_cpu_budget, False)
         others[w] = o
         torch.cuda.empty_cache()
     if others:

@@ -324,9 +324,10 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
   if (extras) {
     a.rows = extras->rows;
-    a.units = extras->units;
-    a.unit_prefix = extras->unit_prefix;
-    a.units_count = extras->units_count;
+    a.bounds = extras->bounds;
+    a.batches = extras->batches;
+    a.batch_prefix = extras->batch_prefix;
+    a.batches_count = extras->batches_count;
   }
   CsrBinArgs bargs{};
   if (binned) {

@@ -8,8 +8,8 @@
 //   2. the columns ordered by count, most first, ties by index: perm[s] = the column of slot s;
 //      the relabelled indices col_slot[p] = slot of col_idx[p] (a gather kernel);
 //   3. the nonempty rows grouped by class (csr_row_class: very long rows first, then classes
-//      6 down to 0, each in row order) and cut into work units: one row per unit for very long
-//      rows, else whole batches of 64 / 2^c rows until a unit holds kRowsUnitEntries entries;
+//      6 down to 0, each in row order) with their entry bounds, and cut into batches: 64 / 2^c
+//      rows of class c < 7 (a row per group of 2^c lanes), one very long row;
 //   4. the model's plan from the coverage of the most frequent columns.
 // Per call: yp[s] = y[perm[s]] into the workspace, the fused kernel on (row_ptr, col_slot, values,
 // v, yp), the bin passes, and the aggregation writing out[perm[s]].
@@ -32,9 +32,10 @@ struct xtvxy_csr_analysis_s {
   int32_t* col_slot = nullptr;       // [nnz] relabelled column indices (owned)
   int32_t* perm = nullptr;           // [n] column of each slot (owned)
   int32_t* rows = nullptr;           // nonempty rows by class (owned)
-  int32_t* units = nullptr;          // [units_count][4] (owned)
-  int32_t* unit_prefix = nullptr;    // [units_count + 1] (owned)
-  int32_t units_count = 0;
+  int32_t* bounds = nullptr;         // [rows][2] their entry bounds (owned)
+  int32_t* batches = nullptr;        // [batches_count][2] (owned)
+  int32_t* batch_prefix = nullptr;   // [batches_count + 1] (owned)
+  int32_t batches_count = 0;
   std::vector<int64_t> covered;      // entries in the k most frequent columns, k = 0..n
   xtvxy_launch_params plan{};        // the model's, workspace_bytes including the gathered y
 };
@@ -43,7 +44,8 @@ namespace {
 
 void release(xtvxy_csr_analysis a) {
   if (!a) return;
-  for (void* p : {(void*)a->col_slot, (void*)a->perm, (void*)a->rows, (void*)a->units, (void*)a->unit_prefix})
+  for (void* p : {(void*)a->col_slot, (void*)a->perm, (void*)a->rows, (void*)a->bounds, (void*)a->batches,
+                  (void*)a->batch_prefix})
     if (p) (void)hipFree(p);
   delete a;
 }
@@ -110,39 +112,38 @@ xtvxy_status analyse(xtvxy_csr_analysis an, const int32_t* row_ptr, const int32_
   if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void**>(&an->col_slot), (size_t)nnz * sizeof(int32_t));
   if (e == hipSuccess) e = launch_relabel(col_idx, nnz, d_slot, an->col_slot, stream);
 
-  // 3. rows by class, work units
+  // 3. rows by class with their bounds, batches
   std::vector<std::vector<int32_t>> by_class(kRowsVeryLong + 1);
   for (int64_t i = 0; i < m; ++i) {
     const int64_t len = (int64_t)h_rp[(size_t)i + 1] - h_rp[(size_t)i];
     if (len > 0) by_class[(size_t)csr_row_class(len)].push_back((int32_t)i);
   }
-  std::vector<int32_t> rows, units, prefix(1, 0);
+  std::vector<int32_t> rows, bounds, batches, prefix(1, 0);
   rows.reserve((size_t)m);
-  auto len_of = [&](int32_t r) { return (int64_t)h_rp[(size_t)r + 1] - h_rp[(size_t)r]; };
+  bounds.reserve(2 * (size_t)m);
   for (int c = kRowsVeryLong; c >= 0; --c) {
     const std::vector<int32_t>& rc = by_class[(size_t)c];
-    const int32_t base = (int32_t)rows.size();
-    rows.insert(rows.end(), rc.begin(), rc.end());
     const size_t per = c == kRowsVeryLong ? 1 : (size_t)(64 >> c);
-    size_t i = 0;
-    while (i < rc.size()) {
-      // whole batches of `per` rows until the unit holds kRowsUnitEntries entries (very long
-      // rows: one per unit)
-      const size_t start = i;
+    for (size_t i = 0; i < rc.size(); i += per) {
+      const size_t end = std::min(rc.size(), i + per);
+      batches.push_back((int32_t)rows.size());
+      batches.push_back(c * 256 + (int32_t)(end - i));
       int64_t entries = 0;
-      do {
-        const size_t end = std::min(rc.size(), i + per);
-        for (size_t k = i; k < end; ++k) entries += len_of(rc[k]);
-        i = end;
-      } while (c != kRowsVeryLong && i < rc.size() && entries < kRowsUnitEntries);
-      units.insert(units.end(), {base + (int32_t)start, (int32_t)(i - start), c, 0});
+      for (size_t k = i; k < end; ++k) {
+        const int32_t r = rc[k];
+        rows.push_back(r);
+        bounds.push_back(h_rp[(size_t)r]);
+        bounds.push_back(h_rp[(size_t)r + 1]);
+        entries += (int64_t)h_rp[(size_t)r + 1] - h_rp[(size_t)r];
+      }
       prefix.push_back(prefix.back() + (int32_t)entries);
     }
   }
-  an->units_count = (int32_t)(units.size() / 4);
+  an->batches_count = (int32_t)(batches.size() / 2);
   if (e == hipSuccess) e = upload(&an->rows, rows, stream);
-  if (e == hipSuccess) e = upload(&an->units, units, stream);
-  if (e == hipSuccess) e = upload(&an->unit_prefix, prefix, stream);
+  if (e == hipSuccess) e = upload(&an->bounds, bounds, stream);
+  if (e == hipSuccess) e = upload(&an->batches, batches, stream);
+  if (e == hipSuccess) e = upload(&an->batch_prefix, prefix, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);  // the host vectors above outlive their copies
   if (d_slot) (void)hipFree(d_slot);
   return e == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH;
@@ -174,7 +175,9 @@ xtvxy_status xtvxy_csr_f32_analyse(int64_t m, int64_t n, int64_t nnz, const int3
     if (st == XTVXY_SUCCESS) {
       xtvxy_device_info d;
       st = current_device_info(&d);
-      if (st == XTVXY_SUCCESS) st = model_csr_rows(m, n, nnz, d, an->covered.data(), &an->plan);
+      // the model's plan for the relabelled matrix: its output and y windows [0, W) and [0, Wy) now
+      // hold the most frequent columns whatever the caller's column order
+      if (st == XTVXY_SUCCESS) st = model_csr(m, n, nnz, d, &an->plan);
       if (st == XTVXY_SUCCESS) st = complete_for(an, &an->plan);
     }
     if (st != XTVXY_SUCCESS) {
@@ -243,7 +246,7 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const
   const size_t yoff = yp_offset(an, plan);
   float* yp = reinterpret_cast<float*>(static_cast<char*>(workspace) + yoff);
   if (launch_permute(y, an->perm, n, yp, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  CsrExtras x{an->rows, an->units, an->unit_prefix, an->units_count, an->perm};
+  CsrExtras x{an->rows, an->bounds, an->batches, an->batch_prefix, an->batches_count, an->perm};
   return csr_run_fused(m, n, nnz, alpha, an->row_ptr, an->col_slot, values, v, yp, beta, z, out, workspace, yoff,
                        stream, &plan, &x);
 }

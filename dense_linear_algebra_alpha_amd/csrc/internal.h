@@ -37,20 +37,23 @@ constexpr size_t kCsrBinStateBytes = 32;
 // dynamic LDS: output and y windows, then each wavefront's bin state (6 words per bin).
 constexpr size_t kCsrWaveBinStateBytes = 24;
 constexpr size_t csr_waves_static_lds(int blk) { return (size_t)(blk / 64) * (512 + 512) + 4 * (size_t)blk; }
-// Row-class CSR kernel (csr_rows.hip): no static LDS; the dynamic LDS holds the output and y
-// windows, then each wavefront's bin state (6 words per bin), laid out as csr_waves_dynamic_lds.
-constexpr int kRowsSlots = 16;        // entry slots per lane and batch (four 16-byte quads)
-constexpr int kRowsVeryLong = 7;      // class of the rows longer than a wavefront's 64 * 16 slots
-constexpr int kRowsUnitEntries = 4096;  // entries a work unit of short-row batches aims at
-// Class of a nonempty row of `len` entries: the smallest c with len + 3 <= 16 * 2^c (a group of
-// 2^c lanes covers the row's quads, whatever the row's first entry mod 4), kRowsVeryLong beyond 2^6.
-constexpr int csr_row_class(int64_t len) {
-  return len + 3 <= 16 ? 0 : len + 3 <= 32 ? 1 : len + 3 <= 64 ? 2 : len + 3 <= 128 ? 3
-       : len + 3 <= 256 ? 4 : len + 3 <= 512 ? 5 : len + 3 <= 1024 ? 6 : kRowsVeryLong;
-}
 constexpr size_t csr_waves_dynamic_lds(int64_t window, int64_t y_window, int32_t bins, int blk) {
   return (((size_t)(window + y_window) * 4 + 7) & ~(size_t)7) +
          (bins > 0 ? (size_t)bins * kCsrWaveBinStateBytes * (size_t)(blk / 64) : 0);
+}
+// Row-class CSR kernel (csr_rows.hip): no static LDS; the dynamic LDS holds the output and y
+// windows, a sink word per thread, then each wavefront's bin state (6 words per bin).
+constexpr int kRowsSlots = 8;       // entry slots per lane and batch (two 16-byte quads)
+constexpr int kRowsVeryLong = 7;    // class of the rows longer than a wavefront's 64 * 8 slots
+constexpr size_t csr_rows_dynamic_lds(int64_t window, int64_t y_window, int32_t bins, int blk) {
+  return (size_t)(window + y_window + blk) * 4 +
+         (bins > 0 ? (size_t)bins * kCsrWaveBinStateBytes * (size_t)(blk / 64) : 0);
+}
+// Class of a nonempty row of `len` entries: the smallest c with len + 3 <= 8 * 2^c (a group of 2^c
+// lanes covers the row's quads, whatever the row's first entry mod 4), kRowsVeryLong beyond c = 6.
+constexpr int csr_row_class(int64_t len) {
+  return len + 3 <= 8 ? 0 : len + 3 <= 16 ? 1 : len + 3 <= 32 ? 2 : len + 3 <= 64 ? 3
+       : len + 3 <= 128 ? 4 : len + 3 <= 256 ? 5 : len + 3 <= 512 ? 6 : kRowsVeryLong;
 }
 
 inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
@@ -98,12 +101,14 @@ struct CsrArgs {
   int2* pool;              // [P][kBinChunkItems] items {column, product bits}
   int32_t* chunk_bin;      // [P] bin of each handed-out chunk
   int32_t* chunk_fill;     // [P] items in each handed-out chunk
-  // row-class kernel (csr_rows.hip): the analysis's nonempty rows grouped by class and its work
-  // units {first position in rows, row count, class, 0}, with unit_prefix[u] = entries before unit u
+  // row-class kernel (csr_rows.hip): the analysis's nonempty rows grouped by class (index, and
+  // entry bounds {s, e} per position) and its batches {first position, class * 256 + rows}, with
+  // batch_prefix[k] = entries before batch k
   const int32_t* rows;
-  const int32_t* units;
-  const int32_t* unit_prefix;  // [units_count + 1]
-  int32_t units_count;
+  const int32_t* bounds;        // [positions][2]
+  const int32_t* batches;       // [batches_count][2]
+  const int32_t* batch_prefix;  // [batches_count + 1]
+  int32_t batches_count;
 };
 
 // Arguments of the bin passes (csr_bins.hip) that follow a binned fused launch.
@@ -206,9 +211,10 @@ xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, cons
 // XTVXY_CSR_ROWS kernel) and the permutation of the relabelled output columns.
 struct CsrExtras {
   const int32_t* rows;
-  const int32_t* units;
-  const int32_t* unit_prefix;
-  int32_t units_count;
+  const int32_t* bounds;
+  const int32_t* batches;
+  const int32_t* batch_prefix;
+  int32_t batches_count;
   const int32_t* out_perm;  // sums of relabelled column j go to out[out_perm[j]]
 };
 // The fused CSR path for checked arguments (api.cpp): the plan (`force`, completed here; the model's

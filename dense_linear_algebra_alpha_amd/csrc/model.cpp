@@ -250,7 +250,7 @@ int64_t csr_fused_lds(int64_t n, const xtvxy_launch_params& p, int32_t bins) {
     return (int64_t)(csr_waves_dynamic_lds(p.lds_window, p.y_window, bins, p.block_threads) +
                      csr_waves_static_lds(p.block_threads));
   if (p.kernel == XTVXY_CSR_ROWS)
-    return (int64_t)csr_waves_dynamic_lds(p.lds_window, p.y_window, bins, p.block_threads);
+    return (int64_t)csr_rows_dynamic_lds(p.lds_window, p.y_window, bins, p.block_threads);
   int64_t lds = ((int64_t)p.lds_window + (int64_t)p.y_window) * (int64_t)sizeof(float);
   if (bins > 0) lds = ((lds + 7) & ~(int64_t)7) + (int64_t)bins * (int64_t)kCsrBinStateBytes;
   return lds + (int64_t)csr_static_lds(p.entries_per_thread, p.block_threads);
@@ -412,7 +412,7 @@ xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_devic
   const int waves = p->block_threads / 64;
   const int64_t lds = d.lds_bytes - 256;  // a little slack for the launch's own use
   double cold_cost = 0.0;
-  if ((int64_t)n * 8 <= lds) {
+  if ((int64_t)n * 8 + 4 * (int64_t)p->block_threads <= lds) {
     p->lds_window = (int32_t)n;
     p->y_window = (int32_t)n;
   } else {
@@ -420,7 +420,7 @@ xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_devic
     for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
       const int64_t bins_max = ceil_div(n, bc);
       if (bins_max > kMaxBins) continue;
-      const int64_t state = bins_max * (int64_t)kCsrWaveBinStateBytes * waves;
+      const int64_t state = bins_max * (int64_t)kCsrWaveBinStateBytes * waves + 4 * (int64_t)p->block_threads;
       const int64_t cols = std::max<int64_t>(0, (lds - state) / 4 - 2);
       const int64_t step = std::max<int64_t>(256, cols / 256);
       for (int64_t w = 0; w <= std::min<int64_t>(cols, n); w += step) {

@@ -39,16 +39,13 @@ class Analysed:
 
 
 def rows_plan(an, blk=1024, grid=None, window=None, y_window=None, bin_columns=None, kernel=None, ept=None):
-    """The analysis's model plan with some fields replaced, completed for the analysed matrix."""
+    """The analysis's model plan with some fields replaced (by default the row-class kernel with 8
+    slots per lane), completed for the analysed matrix."""
     lp = an.plan()
-    if kernel is not None:
-        lp.kernel = kernel
-        lp.entries_per_thread = 16 if kernel == xt.XTVXY_CSR_ROWS else 8
-    if ept is not None:
-        lp.entries_per_thread = ept
+    lp.kernel = xt.XTVXY_CSR_ROWS if kernel is None else kernel
+    lp.entries_per_thread = 8 if ept is None else ept
     lp.block_threads = blk
-    if grid is not None:
-        lp.grid = grid
+    lp.grid = 256 if grid is None else grid
     if window is not None:
         lp.lds_window = window
     if y_window is not None:
@@ -58,7 +55,17 @@ def rows_plan(an, blk=1024, grid=None, window=None, y_window=None, bin_columns=N
     return an.complete(lp)
 
 
-def check(p, what="", plans=(None,), values_offset=0):
+def row_class_plan(an):
+    """The row-class kernel with the model's windows (its LDS also holds a sink word per thread)."""
+    lp = an.plan()
+    w, yw = lp.lds_window, lp.y_window
+    while (w + yw + 1024) * 4 + 16 * 24 * 64 > LDS:  # room for the sink words and bin state
+        w, yw = w * 3 // 4, yw * 3 // 4
+    return rows_plan(an, blk=1024, grid=256, window=w, y_window=yw,
+                     bin_columns=lp.bin_columns if lp.bin_columns else 16384)
+
+
+def check(p, what="", plans=(None, row_class_plan), values_offset=0):
     ref, bnd = csr_oracle(p)
     a = Analysed(p, values_offset)
     for plan in plans:
