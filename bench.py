@@ -195,6 +195,49 @@ def stream_read_ceiling(xt, torch, dev, nbytes=2 << 30, reps=20):
             "bytes": nbytes, "what": "16-byte non-temporal loads over %d workgroups, best of %d launches" % (grid, reps)}
 
 
+def scatter_probe(args):
+    """Rates of the primitives a scatter to columns outside an LDS window could use, from the
+    library's probe kernel: updates per second (best and median of 10 timed launches after 3
+    warmup launches, HIP events) and the time the given number of updates takes."""
+    import torch
+
+    import dense_linear_algebra_alpha_amd as xt
+
+    xt.load()
+    dev = torch.device("cuda", 0)
+    n, items = args.probe_columns, args.probe_updates
+    grid = 8 * xt.xtvxy_get_device_info().compute_units
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream or None
+    ev = HipEvents()
+    kinds = [("fp32 atomics, one copy per XCD, workgroup scope", xt.XTVXY_PROBE_ATOMIC_PER_XCD, 8 * n * 4),
+             ("fp32 atomics, one copy, device scope", xt.XTVXY_PROBE_ATOMIC_DEVICE, n * 4),
+             ("8-byte item stores, scattered", xt.XTVXY_PROBE_ITEM_STORES, n * 8),
+             ("4-byte gathers, scattered", xt.XTVXY_PROBE_GATHERS, n * 4)]
+    rows = []
+    for skew in (0, 1):
+        for what, kind, nbytes in kinds:
+            buf = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+            for _ in range(3):
+                xt.xtvxy_scatter_probe(kind, buf.data_ptr(), nbytes, n, items, skew, grid, sink.data_ptr(), sh)
+            pairs = [(ev.create(), ev.create()) for _ in range(10)]
+            for a, b in pairs:
+                ev.record(a, sh)
+                xt.xtvxy_scatter_probe(kind, buf.data_ptr(), nbytes, n, items, skew, grid, sink.data_ptr(), sh)
+                ev.record(b, sh)
+            torch.cuda.synchronize()
+            ms = [ev.elapsed_ms(a, b) for a, b in pairs]
+            for a, b in pairs:
+                ev.destroy(a)
+                ev.destroy(b)
+            rows.append({"what": what, "skew": skew, "updates": items, "columns": n,
+                         "best_ms": round(min(ms), 4), "median_ms": round(statistics.median(ms), 4),
+                         "g_updates_per_s": round(items / (min(ms) / 1e3) / 1e9, 2)})
+            print(json.dumps(rows[-1]), flush=True)
+            del buf
+    print(json.dumps({"scatter_probe": rows, "grid": grid, "threads_per_workgroup": 256}))
+
+
 LOGREG_METRIC = "Newton-CG logistic regression: ms per Newton iteration (fixed schedule), fused vs unfused products"
 
 
@@ -631,6 +674,13 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--scatter-probe", action="store_true",
+                    help="only measure the rates of the scatter primitives (global fp32 atomics into one copy "
+                         "or one copy per XCD, scattered 8-byte item stores, random gathers) and exit")
+    ap.add_argument("--probe-columns", type=int, default=1_000_000, help="--scatter-probe: columns n")
+    ap.add_argument("--probe-updates", type=int, default=54_782_000,
+                    help="--scatter-probe: updates per launch (default: the Zipf matrix's products outside "
+                         "an 8986-column window)")
     args = ap.parse_args()
     if args.calibration_copy:
         import torch
@@ -641,6 +691,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration_copy_bytes": a.numel() * 4, "repeats": 3}))
         return
+    if args.scatter_probe:
+        return scatter_probe(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -20,7 +20,8 @@ import ctypes
 
 from . import _abi
 from ._abi import (XTVXY_CSR_ROWS, XTVXY_CSR_TILES, XTVXY_CSR_WAVES, XTVXY_DENSE_BLOCK_ROWS, XTVXY_DENSE_GROUP_ROWS,  # noqa: F401
-                   XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED,
+                   XTVXY_DENSE_WAVE_ROWS, XTVXY_LOGREG_CONVERGED, XTVXY_LOGREG_FUSED, XTVXY_PROBE_ATOMIC_DEVICE,
+                   XTVXY_PROBE_ATOMIC_PER_XCD, XTVXY_PROBE_GATHERS, XTVXY_PROBE_ITEM_STORES,
                    XTVXY_UNFUSED_EXPLICIT_TRANSPOSE, XTVXY_UNFUSED_TRANSPOSE_OP,
                    XTVXY_LOGREG_ITERATION_LIMIT, XTVXY_LOGREG_LINE_SEARCH_FAILED, XTVXY_LOGREG_UNFUSED, XtvxyError,
                    xtvxy_device_info, xtvxy_launch_params, xtvxy_logreg_options, xtvxy_logreg_report,
@@ -32,7 +33,7 @@ __all__ = [
     "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
     "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
-    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe",
+    "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe", "xtvxy_scatter_probe",
     "xtvxy_dense_f32_noalloc", "xtvxy_dense_f32_noalloc_max_workspace", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
     "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
@@ -78,6 +79,10 @@ def xtvxy_dense_f32_noalloc(m, n, alpha, X, ldx, v, y, beta, z, out, stream):
 
 def xtvxy_read_probe(buffer, nbytes, grid, sink, stream):
     return _abi.call("xtvxy_read_probe", buffer, nbytes, grid, sink, stream)
+
+
+def xtvxy_scatter_probe(kind, buffer, nbytes, n, items, skew, grid, sink, stream):
+    return _abi.call("xtvxy_scatter_probe", kind, buffer, nbytes, n, items, skew, grid, sink, stream)
 
 
 def xtvxy_get_device_info(device: int = -1) -> xtvxy_device_info:

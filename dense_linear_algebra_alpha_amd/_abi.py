@@ -28,6 +28,11 @@ XTVXY_CSR_TILES = 11
 XTVXY_CSR_WAVES = 12
 XTVXY_CSR_ROWS = 13
 
+XTVXY_PROBE_ATOMIC_PER_XCD = 0
+XTVXY_PROBE_ATOMIC_DEVICE = 1
+XTVXY_PROBE_ITEM_STORES = 2
+XTVXY_PROBE_GATHERS = 3
+
 
 class xtvxy_device_info(ctypes.Structure):
     _fields_ = [("compute_units", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
@@ -136,6 +141,7 @@ SIGNATURES = {
     "xtvxy_csr_f32_analysed": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_analysed_ex": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp, _P(xtvxy_launch_params)],
     "xtvxy_read_probe": [_vp, _sz, _i64, _vp, _vp],
+    "xtvxy_scatter_probe": [_i32, _vp, _sz, ctypes.c_uint32, ctypes.c_uint32, _i32, _i64, _vp, _vp],
     "xtvxy_dense_f32_noalloc_max_workspace": [_P(_sz)],
     "xtvxy_dense_f32_noalloc": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_dense_f32_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,

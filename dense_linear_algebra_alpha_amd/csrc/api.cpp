@@ -303,9 +303,9 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
     st = complete_csr(m, n, nnz, d, &plan);
     if (st != XTVXY_SUCCESS) return st;
   }
-  if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
+  const CsrWorkspace w = csr_workspace(m, n, nnz, plan, extras ? extras->binned_items : -1);
+  if (w.total > 0 && (!ws || ws_bytes < w.total)) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
-  const CsrWorkspace w = csr_workspace(m, n, nnz, plan);
   CsrArgs a{};
   a.m = m;
   a.n = n;

@@ -50,9 +50,18 @@ void release(xtvxy_csr_analysis a) {
   delete a;
 }
 
-// Bytes of the fused path's workspace for a completed plan, then the gathered y.
+// Entries whose relabelled column lies outside the plan's output window: those outside the
+// lds_window most frequent columns.
+int64_t binned_items(const xtvxy_csr_analysis a, const xtvxy_launch_params& p) {
+  if (a->covered.empty()) return -1;  // an empty matrix was not analysed
+  const int64_t w = std::min<int64_t>(std::max<int64_t>(p.lds_window, 0), a->n);
+  return a->nnz - a->covered[(size_t)w];
+}
+
+// Bytes of the fused path's workspace for a completed plan (its bin pool sized for the entries
+// the plan bins), then the gathered y.
 size_t yp_offset(const xtvxy_csr_analysis a, const xtvxy_launch_params& p) {
-  return align_up((size_t)csr_workspace(a->m, a->n, a->nnz, p).total);
+  return align_up((size_t)csr_workspace(a->m, a->n, a->nnz, p, binned_items(a, p)).total);
 }
 
 xtvxy_status complete_for(const xtvxy_csr_analysis a, xtvxy_launch_params* p) {
@@ -246,7 +255,8 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const
   const size_t yoff = yp_offset(an, plan);
   float* yp = reinterpret_cast<float*>(static_cast<char*>(workspace) + yoff);
   if (launch_permute(y, an->perm, n, yp, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
-  CsrExtras x{an->rows, an->bounds, an->batches, an->batch_prefix, an->batches_count, an->perm};
+  CsrExtras x{an->rows, an->bounds, an->batches, an->batch_prefix, an->batches_count, an->perm,
+              binned_items(an, plan)};
   return csr_run_fused(m, n, nnz, alpha, an->row_ptr, an->col_slot, values, v, yp, beta, z, out, workspace, yoff,
                        stream, &plan, &x);
 }

@@ -216,6 +216,7 @@ struct CsrExtras {
   const int32_t* batch_prefix;
   int32_t batches_count;
   const int32_t* out_perm;  // sums of relabelled column j go to out[out_perm[j]]
+  int64_t binned_items;     // entries outside the plan's output window (sizes the bin pool), or -1
 };
 // The fused CSR path for checked arguments (api.cpp): the plan (`force`, completed here; the model's
 // when null), the main kernel, the bin passes and the aggregation, on `stream`.
@@ -288,6 +289,8 @@ struct CsrWorkspace {
       unit_start_off, partial2_off;
   size_t total;
 };
-CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p);
+// `binned` is the number of entries whose column lies outside the output window when known (a
+// structure analysis counts them), negative when not: every entry is then assumed binned.
+CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p, int64_t binned = -1);
 
 }  // namespace xtvxy

@@ -83,7 +83,7 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
   return w;
 }
 
-CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p) {
+CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch_params& p, int64_t binned) {
   (void)m;
   CsrWorkspace w{};
   w.partial_off = 0;
@@ -99,7 +99,8 @@ CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch
     return w;
   }
   // binning: every (workgroup, bin) pair (the wavefront kernel: every (wavefront, bin) pair)
-  // leaves at most one chunk partly filled, so ceil(nnz / S) + owners * B chunks always suffice
+  // leaves at most one chunk partly filled, so ceil(items / S) + owners * B chunks always suffice,
+  // items being the binned entries (all nnz when their number is not known)
   int shift = 0;
   while ((1 << shift) < p.bin_columns) ++shift;
   w.bin_shift = shift;
@@ -107,7 +108,8 @@ CsrWorkspace csr_workspace(int64_t m, int64_t n, int64_t nnz, const xtvxy_launch
   const int64_t owners = p.kernel == XTVXY_CSR_WAVES || p.kernel == XTVXY_CSR_ROWS
                              ? p.grid * (int64_t)(p.block_threads / 64)
                              : p.grid;
-  w.pool_chunks = ceil_div(std::max<int64_t>(nnz, 1), kBinChunkItems) + owners * (int64_t)w.bins;
+  const int64_t items = binned >= 0 ? std::min(binned, nnz) : nnz;
+  w.pool_chunks = ceil_div(std::max<int64_t>(items, 1), kBinChunkItems) + owners * (int64_t)w.bins;
   w.max_units = ceil_div(w.pool_chunks, kBinUnitChunks) + w.bins;
   w.counter_off = off;
   off = align_up(off + sizeof(uint32_t));

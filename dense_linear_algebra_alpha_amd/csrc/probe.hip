@@ -1,7 +1,12 @@
-// Streaming-read ceiling for measurements: how fast this GPU reads a large buffer from HBM when
-// the reads are as simple as they get (16-byte non-temporal loads, every workgroup a contiguous
-// stretch, one add per load). Benchmarks report the fused kernels against it beside the
-// published HBM peak. Not part of the fused path.
+// Measurement probes, not part of the fused path:
+//   - the streaming-read ceiling: how fast this GPU reads a large buffer from HBM when the reads
+//     are as simple as they get (16-byte non-temporal loads, every workgroup a contiguous
+//     stretch, one add per load); benchmarks report the fused kernels against it beside the
+//     published HBM peak;
+//   - the rates of the primitives a scatter of products to columns outside an LDS window could
+//     be built on (fp32 atomics into one copy of the output or into one copy per XCD, scattered
+//     8-byte item stores, random 4-byte gathers), on synthetic hashed column streams, so the
+//     choice of binning for those columns rests on measured rates.
 #include "device_util.h"
 #include "internal.h"
 
@@ -32,8 +37,65 @@ __global__ __launch_bounds__(kProbeThreads) void read_probe_kernel(const f4* __r
   if (acc == 1.2345678e-30f) sink[0] = acc;  // keeps the loads; never true for the probe's zeroed buffer
 }
 
+// Column of update k: a hash of k, uniform over [0, n) (skew 0) or n u^3 for a uniform u (skew 1,
+// a quarter of the updates on the first 1.6% of the columns).
+__device__ __forceinline__ uint32_t probe_column(uint32_t k, uint32_t n, int skew) {
+  uint32_t h = k * 2654435761u + 12345u;
+  h ^= h >> 16;
+  h *= 0x7feb352du;
+  h ^= h >> 15;
+  h *= 0x846ca68bu;
+  h ^= h >> 16;
+  if (!skew) return h % n;
+  const float u = (float)(h >> 8) * (1.0f / 16777216.0f);
+  const uint32_t c = (uint32_t)(u * u * u * (float)n);
+  return c < n ? c : n - 1;
+}
+
+// The XCD (accelerator complex die) the wavefront runs on, 0..7 on MI355X.
+__device__ __forceinline__ uint32_t probe_xcd() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7u;  // hwreg(HW_REG_XCC_ID, 0, 4)
+}
+
+__global__ __launch_bounds__(kProbeThreads) void scatter_probe_kernel(int kind, float* f, int2* pool, uint32_t n,
+                                                                      uint32_t items, int skew, float* sink) {
+  float acc = 0.0f;
+  const float* gf = f;
+  float* mine = kind == XTVXY_PROBE_ATOMIC_PER_XCD ? f + (size_t)probe_xcd() * n : f;
+  for (uint32_t k = blockIdx.x * kProbeThreads + threadIdx.x; k < items; k += gridDim.x * kProbeThreads) {
+    const uint32_t c = probe_column(k, n, skew);
+    if (kind == XTVXY_PROBE_ATOMIC_PER_XCD)
+      __hip_atomic_fetch_add(mine + c, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    else if (kind == XTVXY_PROBE_ATOMIC_DEVICE)
+      __hip_atomic_fetch_add(mine + c, 1.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else if (kind == XTVXY_PROBE_ITEM_STORES)
+      pool[c] = make_int2((int)k, 1);
+    else
+      acc += gf[c];
+  }
+  if (acc == 1.2345678e-30f) sink[0] = acc;  // keeps the gathers
+}
+
 }  // namespace
 }  // namespace xtvxy
+
+extern "C" xtvxy_status xtvxy_scatter_probe(int kind, void* buffer, size_t bytes, uint32_t n, uint32_t items,
+                                            int skew, int64_t grid, float* sink, hipStream_t stream) {
+  using namespace xtvxy;
+  if (!buffer || !sink) return XTVXY_ERROR_NULL_POINTER;
+  if (kind < XTVXY_PROBE_ATOMIC_PER_XCD || kind > XTVXY_PROBE_GATHERS || n == 0 || (skew != 0 && skew != 1) ||
+      grid <= 0 || grid > INT32_MAX || reinterpret_cast<uintptr_t>(buffer) % 16 != 0)
+    return XTVXY_ERROR_INVALID_VALUE;
+  // the columns index n floats (8 copies of them per XCD), or n 8-byte items
+  const size_t need = kind == XTVXY_PROBE_ATOMIC_PER_XCD ? (size_t)8 * n * sizeof(float)
+                      : kind == XTVXY_PROBE_ITEM_STORES  ? (size_t)n * sizeof(int2)
+                                                         : (size_t)n * sizeof(float);
+  if (bytes < need) return XTVXY_ERROR_WORKSPACE;
+  if (items == 0) return XTVXY_SUCCESS;
+  hipLaunchKernelGGL(scatter_probe_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream, kind,
+                     static_cast<float*>(buffer), static_cast<int2*>(buffer), n, items, skew, sink);
+  return hipGetLastError() == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH;
+}
 
 extern "C" xtvxy_status xtvxy_read_probe(const void* buffer, size_t bytes, int64_t grid, float* sink,
                                          hipStream_t stream) {

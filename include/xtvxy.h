@@ -336,6 +336,31 @@ xtvxy_status xtvxy_test_group_wait(int32_t polls, int32_t unanswered);
  * Asynchronous on `stream`. */
 xtvxy_status xtvxy_read_probe(const void *buffer, size_t bytes, int64_t grid, float *sink, hipStream_t stream);
 
+/* What xtvxy_scatter_probe measures. */
+typedef enum {
+  XTVXY_PROBE_ATOMIC_PER_XCD = 0, /* fp32 atomic add of 1 into the copy of the XCD the wavefront runs on
+                                     (8 copies of n floats), workgroup scope */
+  XTVXY_PROBE_ATOMIC_DEVICE = 1,  /* fp32 atomic add of 1 into one copy of n floats, device scope */
+  XTVXY_PROBE_ITEM_STORES = 2,    /* an 8-byte store {k, 1} to item slot c of n slots */
+  XTVXY_PROBE_GATHERS = 3         /* a 4-byte load of float c of n */
+} xtvxy_probe_kind;
+
+/* Measurement helper, not part of the pattern: the rates of the primitives a scatter of products
+ * to columns outside an LDS window could use. "On optimizing machine learning workloads via
+ * kernel fusion" (abstract) aggregates partial results hierarchically; for the columns outside
+ * the window the library bins products instead of adding them with global atomics, and this
+ * probe measures that choice. One kernel of `grid` workgroups of 256 threads performs `items`
+ * updates of kind `kind`; update k targets column c = hash(k) mod n (skew 0), or n u^3 with u a
+ * uniform of the hash (skew 1: a quarter of the updates on the first 1.6% of the columns).
+ * `buffer` (16-byte aligned device memory of `bytes` bytes) must hold 8 n floats for
+ * XTVXY_PROBE_ATOMIC_PER_XCD, n 8-byte items for XTVXY_PROBE_ITEM_STORES and n floats otherwise
+ * (else XTVXY_ERROR_WORKSPACE); the atomics add to its contents, the stores overwrite it, the
+ * gathers only read it (the device float `sink` is written only if the gathered values sum to a
+ * value a zeroed buffer never gives). XTVXY_ERROR_INVALID_VALUE for an unknown kind, n == 0, a
+ * skew other than 0 or 1 or grid outside [1, 2^31). Asynchronous on `stream`. */
+xtvxy_status xtvxy_scatter_probe(int kind, void *buffer, size_t bytes, uint32_t n, uint32_t items, int skew,
+                                 int64_t grid, float *sink, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Unfused comparator: the same result from operator-level library calls    */
 /* (the pages' baseline of several library kernel launches)               */

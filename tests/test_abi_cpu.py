@@ -114,6 +114,30 @@ def test_query_argument_errors(lib):
         _abi.XTVXY_ERROR_NULL_POINTER
 
 
+def test_probe_argument_errors(lib):
+    assert lib.xtvxy_read_probe(None, 16, 1, FAKE, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert lib.xtvxy_read_probe(FAKE, 15, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_read_probe(FAKE + 4, 16, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert lib.xtvxy_read_probe(FAKE, 16, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    probe = lib.xtvxy_scatter_probe
+    assert probe(_abi.XTVXY_PROBE_GATHERS, None, 64, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 64, 16, 8, 0, 1, None, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    for kind in (-1, 4):
+        assert probe(kind, FAKE, 1 << 20, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 64, 0, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 64, 16, 8, 2, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 64, 16, 8, 0, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE + 4, 64, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    # the buffer must cover what the kind indexes: n floats, n 8-byte items, 8 copies of n floats
+    assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 63, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_WORKSPACE
+    assert probe(_abi.XTVXY_PROBE_ATOMIC_DEVICE, FAKE, 63, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_WORKSPACE
+    assert probe(_abi.XTVXY_PROBE_ITEM_STORES, FAKE, 127, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_WORKSPACE
+    assert probe(_abi.XTVXY_PROBE_ATOMIC_PER_XCD, FAKE, 511, 16, 8, 0, 1, FAKE, None) == \
+        _abi.XTVXY_ERROR_WORKSPACE
+    # no updates: nothing to launch
+    assert probe(_abi.XTVXY_PROBE_ATOMIC_PER_XCD, FAKE, 512, 16, 0, 1, 1, FAKE, None) == _abi.XTVXY_SUCCESS
+
+
 SHAPES = [(2048, 128), (1_000_000, 256), (65_536, 8192), (8192, 65_536), (1, 1), (7, 3), (100, 1000),
           (5, 1025), (3, 8193), (1000, 200_000)]
 

@@ -234,6 +234,35 @@ def test_nan_stays_in_its_row():
     assert_parity(a.run(), ref, bnd, "NaN and Inf rows")
 
 
+def binned_entries(p, window):
+    """Entries outside the `window` most frequent columns (ties by index): those an analysed call bins."""
+    counts = np.bincount(p.col_idx, minlength=p.n)
+    order = np.argsort(-counts, kind="stable")
+    return int(p.nnz - counts[order[:window]].sum())
+
+
+@pytest.mark.parametrize("kernel,blk,grid", [(xt.XTVXY_CSR_TILES, 256, 1), (xt.XTVXY_CSR_TILES, 512, 300),
+                                             (xt.XTVXY_CSR_WAVES, 256, 7), (xt.XTVXY_CSR_WAVES, 1024, 256)])
+def test_bin_pool_sized_for_the_binned_entries(kernel, blk, grid):
+    # nearly every entry outside a one-column window, over many workgroups and bins: the analysed
+    # call's pool holds exactly the binned entries' chunks plus one partial chunk per owner and bin
+    p = datagen.csr_random(20000, 60000, seed=21, mean_len=12.0, empty_frac=0.1, dup_frac=0.05)
+    ref, bnd = csr_oracle(p)
+    a = Analysed(p)
+    plan = rows_plan(a.an, blk=blk, grid=grid, window=1, y_window=0, bin_columns=1024, kernel=kernel)
+    binned = binned_entries(p, 1)
+    assert binned > 0.99 * p.nnz
+    bins = -(-(p.n - 1) // 1024)
+    owners = grid * (blk // 64 if kernel == xt.XTVXY_CSR_WAVES else 1)
+    chunk_items = 512
+    pool_bytes = (-(-binned // chunk_items) + owners * bins) * chunk_items * 8
+    plain = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, xt.xtvxy_launch_params.from_buffer_copy(plan))
+    # the analysed workspace also holds the relabelled y (n floats)
+    assert pool_bytes <= plan.workspace_bytes <= plain.workspace_bytes + -(-p.n * 4 // 256) * 256
+    note("analysed pool m=%d n=%d nnz=%d binned=%d plan=%s" % (p.m, p.n, p.nnz, binned, plan.as_dict()))
+    assert_parity(a.run(plan=plan), ref, bnd, "analysed pool plan %s" % plan.as_dict())
+
+
 @pytest.mark.parametrize("permuted", [False, True])
 def test_zipf_scaled(permuted):
     p = datagen.csr_zipf(200_000, 200_000, seed=1, permute_columns=permuted)
@@ -244,4 +273,9 @@ def test_zipf_scaled(permuted):
                                   "csr_10000000x1000_logistic_hvp"])
 def test_full_size_workloads(name):
     p = datagen.WORKLOADS[name]()
-    check(p, what=name)
+    a = check(p, what=name)
+    plan = a.an.plan()
+    if plan.lds_window < p.n:  # the bin pool holds the entries outside the window, not all nnz
+        assert plan.workspace_bytes >= 8 * binned_entries(p, plan.lds_window)
+        plain = xt.xtvxy_csr_f32_plan_complete(p.m, p.n, p.nnz, xt.xtvxy_launch_params.from_buffer_copy(plan))
+        assert plan.workspace_bytes < plain.workspace_bytes / 2
