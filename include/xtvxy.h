@@ -94,11 +94,11 @@ enum {
    * workgroup never waits at a barrier per tile; block_threads 256, 512 or 1024,
    * entries_per_thread 8 */
   XTVXY_CSR_WAVES = 12,
-  /* rows by length class (needs a structure analysis, xtvxy_csr_f32_analyse): a group of 2^c
-   * lanes takes each row of class c (rows of up to 16 * 2^c - 3 entries) with 16 entry slots per
-   * lane, a wavefront takes each row longer than 1021 entries in slices; every wavefront works
-   * alone, the scatter is the others' (LDS window, then atomics or bins); block_threads 256, 512
-   * or 1024, entries_per_thread 16 */
+  /* rows by length class (needs a structure analysis, xtvxy_csr_f32_analyse; forced plans only,
+   * the model never picks it): a group of 2^c lanes takes each row of class c (rows of up to
+   * 8 * 2^c - 3 entries) with 8 entry slots per lane, a wavefront takes each row longer than 509
+   * entries in slices of 512; every wavefront works alone, the scatter is the others' (LDS window,
+   * then atomics or bins); block_threads 256, 512 or 1024, entries_per_thread 8 */
   XTVXY_CSR_ROWS = 13
 };
 
@@ -113,14 +113,16 @@ typedef struct xtvxy_launch_params {
   int32_t group;           /* dense group path: workgroups per row (column slices); 1 otherwise */
   int64_t grid;            /* workgroups launched */
   int64_t rows_per_unit;   /* dense: rows per workgroup (wave/block paths) or per group */
-  int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile (4 or 8) */
+  int32_t entries_per_thread; /* csr: nonzeros each thread holds per tile (4 or 8; 8 for the wavefront and
+                                 row-class kernels) */
   int32_t lds_window;      /* csr: output columns [0, lds_window) accumulated in LDS (0..n) */
   int32_t y_window;        /* csr: y[0, y_window) is copied into each workgroup's LDS and gathered from
                               there, columns >= y_window from global memory (0..n) */
   int32_t bin_columns;     /* csr: 0 = cold columns by global atomics; else columns per bin (power of
                               two, 1024..32768; at most 512 bins, i.e. n - lds_window <= 512 bin_columns) */
   int64_t workspace_bytes; /* workspace the plan needs (filled in by the plan queries); with binning it
-                              grows with nnz: about 8 bytes per stored entry plus per-bin partial sums */
+                              grows with nnz: about 8 bytes per stored entry plus per-bin partial sums
+                              (analysed calls: 8 bytes per entry outside the output window) */
   double predicted_seconds;/* the model's estimate for this plan */
 } xtvxy_launch_params;
 
@@ -240,9 +242,11 @@ xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
  *     permutation (4 n bytes); each call gathers y into that order (n floats of its workspace)
  *     and writes every output column back to its own index, so results are those of
  *     xtvxy_csr_f32 on the caller's matrix (up to the order of fp32 additions);
- *   - the nonempty rows are grouped by length class for the row-class kernel (XTVXY_CSR_ROWS; a
- *     row list of 4 bytes per row and work units of about 4096 entries);
- *   - the model's plan for the analysed matrix (the window sizes from the column counts).
+ *   - the nonempty rows are grouped by length class for the row-class kernel (XTVXY_CSR_ROWS: the
+ *     rows with their entry bounds, 12 bytes per nonempty row, in batches of one class);
+ *   - the model's plan for the relabelled matrix (the tiled or wavefront kernel; its windows
+ *     [0, W) and [0, Wy) now hold the most frequent columns), and the number of entries outside
+ *     any output window, so the bin pool of each call holds exactly the binned entries.
  * xtvxy_csr_f32_analyse is a set-up call: it allocates device memory, synchronises `stream` and
  * reads back row_ptr and the column counts. It keeps row_ptr and values pointers of no call:
  * row_ptr (device) must stay valid and unchanged while the analysis is used (each call reads it);
@@ -257,8 +261,8 @@ xtvxy_status xtvxy_csr_f32_analysis_destroy(xtvxy_csr_analysis analysis);
 /* The model's plan for the analysed matrix (workspace_bytes included). */
 xtvxy_status xtvxy_csr_f32_analysed_plan(xtvxy_csr_analysis analysis, xtvxy_launch_params *plan);
 /* Checks a caller-edited plan for the analysed matrix and fills in its workspace_bytes. Any CSR
- * kernel: XTVXY_CSR_ROWS (the model's), or XTVXY_CSR_TILES / XTVXY_CSR_WAVES on the relabelled
- * columns. */
+ * kernel on the relabelled columns: XTVXY_CSR_TILES or XTVXY_CSR_WAVES (the model's choices), or
+ * XTVXY_CSR_ROWS (forced plans only). */
 xtvxy_status xtvxy_csr_f32_analysed_plan_complete(xtvxy_csr_analysis analysis, xtvxy_launch_params *plan);
 /* Workspace bytes of xtvxy_csr_f32_analysed (the model's plan). */
 xtvxy_status xtvxy_csr_f32_analysed_workspace_size(xtvxy_csr_analysis analysis, size_t *bytes);
