@@ -44,7 +44,7 @@ constexpr int kMaxWgPerCu = 8;          // 256-thread workgroups per CU (32 wave
 constexpr double kAtomicRate = 2.0e10;  // global fp32 atomics per second on distinct addresses (measured)
 constexpr int64_t kCsrLdsBudget = 64 * 1024;  // CSR: LDS bytes for the output and y windows
 constexpr int kCsrThreadsPerCuLarge = 1024;  // CSR: threads per CU the windows leave room for when n is large
-constexpr int64_t kWaveRowsMaxMean = 16;      // CSR: mean entries per row up to which the wavefront kernel is used
+constexpr int64_t kWaveRowsMaxMean = 128;     // CSR: mean entries per row up to which the wavefront kernel is used
 constexpr int kMaxThreadsPerCu = 2048;       // 32 wavefronts
 
 int next_pow2(int64_t x) {
@@ -369,11 +369,13 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   p->predicted_seconds = best;
   xtvxy_status st = complete_csr(m, n, nnz, d, p);
   if (st != XTVXY_SUCCESS || !fused) return st;
-  // Narrow matrices with short rows (both windows hold all of n, at most kWaveRowsMaxMean entries
-  // per row on average): the wavefront kernel on the same grid. Its tiles of 512 entries are
-  // one wavefront's, so it needs no workgroup barrier per tile (measured 14% faster on a
-  // 10^7 x 1000 matrix of 10 entries per row); rows longer than a tile take two sweeps, which
-  // is why long or heavy-tailed rows keep the workgroup tiles. The halves alone keep them too:
+  // Narrow matrices (both windows hold all of n) with at most kWaveRowsMaxMean entries per row on
+  // average: the wavefront kernel on the same grid. Its tiles of 512 entries are one wavefront's,
+  // so it needs no workgroup barrier per tile. Measured on narrow matrices of 500 to 8192 columns
+  // (uniform rows of 3 to 100 entries, and Zipf rows of mean 19 and 40 with rows of up to 600 and
+  // 2726 entries) it ran 7-26% faster than the workgroup tiles at their best grid; rows longer
+  // than a tile take two sweeps, so much longer mean rows keep the workgroup tiles. The halves
+  // alone keep them too:
   // without a scatter (rowdot) or without gathers (tmv) the tiles' barriers cost little, and the
   // wavefront kernel measured no faster (rowdot) or 6% slower (tmv) there.
   if (p->lds_window == n && p->y_window == n && p->block_threads == 256 && p->entries_per_thread == 8 &&

@@ -160,7 +160,7 @@ std::vector<xtvxy_launch_params> csr_candidates(int64_t m, int64_t n, int64_t nn
       for (int32_t bc : {0, 16384, 32768}) {
         if (wy.first >= n && bc != 0) continue;
         if (sh.kernel == XTVXY_CSR_WAVES && wy.first < n) continue;
-        for (int k : {1, 2, 4, 8}) {
+        for (int k : {1, 2, 3, 4, 6, 8}) {
           if ((int64_t)sh.threads * k > 2048) continue;  // threads per CU
           xtvxy_launch_params p{};
           p.kernel = sh.kernel;

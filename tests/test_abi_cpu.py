@@ -192,11 +192,13 @@ def test_plan_complete_rejects_plans_that_do_not_cover(lib):
 
 
 @pytest.mark.parametrize("m,n,nnz", [(10_000_000, 1000, 100_000_000), (5_000_000, 1_000_000, 200_000_000),
+                                     (1_000_000, 1000, 100_000_000), (100_000, 8192, 20_000_000),
                                      (10, 5, 7), (1, 1, 1)])
 def test_csr_model_plans(lib, m, n, nnz):
     p = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
-    # narrow matrices of short rows take the wavefront kernel, the rest workgroup tiles
-    waves = n * 8 <= 64 * 1024 and nnz <= 16 * m
+    # narrow matrices of at most 128 entries per row on average take the wavefront kernel, the
+    # rest workgroup tiles
+    waves = n * 8 <= 64 * 1024 and nnz <= 128 * m
     assert p.kernel == (xt.XTVXY_CSR_WAVES if waves else xt.XTVXY_CSR_TILES)
     assert p.grid >= 1 and p.entries_per_thread in (4, 8, 16)
     assert 0 < p.lds_window <= n and p.workspace_bytes >= p.grid * p.lds_window * 4
