@@ -15,6 +15,9 @@ the CSR Zipf matrix and its column-permuted form) carried on the same line under
   peaks            the published 8 TB/s, the device properties' theoretical peak and
                    the measured streaming-read ceiling, with the kernel's fraction of each
   speedup_vs_unfused  wall time of the rocBLAS/rocSPARSE chain / fused wall time
+  speedup_vs_unfused_explicit_transpose
+                   the same chain with X^T kept as a second matrix (made once, outside the
+                   timed region), so that both products take the library's fast path
   cpu_baseline     the CPU oracle on the host cores (same algorithmic-bytes formula)
 Algorithmic bytes: every operand once — dense 4mn (X) + 4m (v, if given) + 4n (y)
 + 4n (z, if beta != 0) + 4n (out); CSR 8 nnz + 4(m + 1) + 4m (v) + 4n (y) + 4n (z)
@@ -473,6 +476,17 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
                                                      y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
                                                      uws.data_ptr(), uws_bytes, sh)
         unfused_explicit = None
+        if with_unfused and not bf16:
+            # the stronger comparator: X^T copied once (set-up, outside every timed region) so
+            # that both products are transposed sgemvs
+            Xt = torch.empty((p.n, p.m), dtype=torch.float32, device=dev)
+            xt.xtvxy_dense_f32_transpose(p.m, p.n, X.data_ptr(), p.ldx, Xt.data_ptr(), p.m, sh)
+            torch.cuda.synchronize()
+
+            def unfused_explicit():
+                xt.xtvxy_dense_f32_unfused_reference_explicit(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, Xt.data_ptr(),
+                                                              p.m, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                                                              out.data_ptr(), uws.data_ptr(), uws_bytes, sh)
         shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": "bf16" if bf16 else "f32"}
         env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
     else:
@@ -607,7 +621,7 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
         rec["unfused_ms_per_step"] = round(unfused_s * 1e3, 5)
         rec["unfused_calls_timed"] = unfused_calls
         rec["speedup_vs_unfused"] = round(unfused_s / step_s, 3)
-    if explicit_s is not None:  # the same chain with X^T kept as a second CSR matrix
+    if explicit_s is not None:  # the same chain with X^T kept as a second matrix (CSR, or dense row-major)
         rec["unfused_explicit_transpose_ms_per_step"] = round(explicit_s * 1e3, 5)
         rec["speedup_vs_unfused_explicit_transpose"] = round(explicit_s / step_s, 3)
 

@@ -32,10 +32,11 @@ __all__ = [
     "xtvxy_csr_f32_plan_complete", "xtvxy_dense_f32_workspace_size", "xtvxy_dense_f32", "xtvxy_dense_f32_ex",
     "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
     "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
+    "xtvxy_dense_f32_transpose", "xtvxy_dense_f32_unfused_reference_explicit",
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
     "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe", "xtvxy_scatter_probe",
     "xtvxy_dense_f32_noalloc", "xtvxy_dense_f32_noalloc_max_workspace", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
-    "dense", "csr", "dense_unfused", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
+    "dense", "csr", "dense_unfused", "dense_transpose", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
     "xtvxy_logreg_options", "xtvxy_logreg_report", "xtvxy_csr_f32_unfused_plan_create_ex",
@@ -249,6 +250,16 @@ def xtvxy_dense_f32_unfused_reference(m, n, alpha, X, ldx, v, y, beta, z, out, w
                                       stream):
     return _abi.call("xtvxy_dense_f32_unfused_reference", m, n, alpha, X, ldx, v, y, beta, z, out, workspace,
                      workspace_bytes, stream)
+
+
+def xtvxy_dense_f32_transpose(m, n, X, ldx, Xt, ldxt, stream):
+    return _abi.call("xtvxy_dense_f32_transpose", m, n, X, ldx, Xt, ldxt, stream)
+
+
+def xtvxy_dense_f32_unfused_reference_explicit(m, n, alpha, X, ldx, Xt, ldxt, v, y, beta, z, out, workspace,
+                                               workspace_bytes, stream):
+    return _abi.call("xtvxy_dense_f32_unfused_reference_explicit", m, n, alpha, X, ldx, Xt, ldxt, v, y, beta, z, out,
+                     workspace, workspace_bytes, stream)
 
 
 def xtvxy_csr_f32_unfused_plan_create(m, n, nnz, row_ptr, col_idx, values, stream) -> int:
@@ -537,8 +548,20 @@ def csr_check(row_ptr, col_idx, n, stream=None) -> int:
     return int(flag.item())
 
 
-def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, workspace=None, stream=None):
-    """The comparator: rocBLAS sgemv, elementwise scale, rocBLAS sgemv."""
+def dense_transpose(X, stream=None):
+    """X^T as a new row-major n x m fp32 tensor (rocBLAS sgeam): the comparator's copy of X^T."""
+    torch = _torch()
+    m, n = X.shape
+    ldx = max(X.stride(0) if m > 1 else n, n, 1)
+    Xt = torch.empty((n, m), dtype=torch.float32, device=X.device)
+    xtvxy_dense_f32_transpose(m, n, X.data_ptr(), ldx, Xt.data_ptr(), max(m, 1), _stream_handle(stream))
+    _keep_for_stream(stream, Xt)
+    return Xt
+
+
+def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, Xt=None, workspace=None, stream=None):
+    """The comparator: rocBLAS sgemv, elementwise scale, rocBLAS sgemv; with Xt (X^T, n x m, from
+    dense_transpose) the last step is a transposed sgemv on it."""
     torch = _torch()
     m, n = X.shape
     ldx = max(X.stride(0) if m > 1 else n, n, 1)
@@ -553,8 +576,16 @@ def dense_unfused(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, worksp
     if made_ws:
         workspace = _workspace(xtvxy_dense_f32_unfused_reference_workspace_size(m, n), device)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(), workspace.numel())
-    xtvxy_dense_f32_unfused_reference(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta),
-                                      _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
+    if Xt is None:
+        xtvxy_dense_f32_unfused_reference(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta),
+                                          _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
+    else:
+        if tuple(Xt.shape) != (n, m) or Xt.dtype != torch.float32 or Xt.device != device:
+            raise ValueError("Xt must be an n x m fp32 tensor on %s" % device)
+        ldxt = max(Xt.stride(0) if n > 1 else m, m, 1)
+        xtvxy_dense_f32_unfused_reference_explicit(m, n, float(alpha), X.data_ptr(), ldx, Xt.data_ptr(), ldxt, _ptr(v),
+                                                   y.data_ptr(), float(beta), _ptr(z), out.data_ptr(), ws_ptr,
+                                                   ws_bytes, _stream_handle(stream))
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 

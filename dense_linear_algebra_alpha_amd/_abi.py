@@ -127,6 +127,9 @@ SIGNATURES = {
     "xtvxy_csr_check": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "xtvxy_dense_f32_unfused_reference_workspace_size": [_i64, _i64, _P(_sz)],
     "xtvxy_dense_f32_unfused_reference": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_dense_f32_transpose": [_i64, _i64, _vp, _i64, _vp, _i64, _vp],
+    "xtvxy_dense_f32_unfused_reference_explicit": [_i64, _i64, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _f32, _vp, _vp,
+                                                   _vp, _sz, _vp],
     "xtvxy_csr_f32_unfused_plan_create": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _P(_vp)],
     "xtvxy_csr_f32_unfused_plan_destroy": [_vp],
     "xtvxy_csr_f32_unfused_plan_create_ex": [_i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp, _P(_vp)],

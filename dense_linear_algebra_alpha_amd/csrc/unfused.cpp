@@ -8,7 +8,10 @@
 //   t   = v .* t                   (elementwise kernel; skipped when v is absent)
 //   out = z                        (device copy, when beta != 0 and out != z)
 //   out = alpha X^T t + beta out   (sgemv / spmv on the transpose, reads X again)
-// so X crosses HBM twice and t makes a round trip, against once for the fused path. rocSPARSE's
+// so X crosses HBM twice and t makes a round trip, against once for the fused path. rocBLAS's
+// sgemv without transpose on the column-major view of a row-major X (the last step) is slow when
+// X has few columns and many rows; xtvxy_dense_f32_unfused_reference_explicit takes a caller-made
+// copy of X^T (xtvxy_dense_f32_transpose) so that both steps are transposed sgemvs. rocSPARSE's
 // transposed SpMV serialises on output columns that many rows share; the plan option
 // XTVXY_UNFUSED_EXPLICIT_TRANSPOSE keeps a CSR copy of X^T (made once with csr2csc) so that the
 // last step is a forward SpMV: the stronger operator-level baseline.
@@ -200,6 +203,73 @@ xtvxy_status xtvxy_dense_f32_unfused_reference(int64_t m, int64_t n, float alpha
     return XTVXY_ERROR_LAUNCH;
   if (rocblas_sgemv(h, rocblas_operation_none, (rocblas_int)n, (rocblas_int)m, &alpha, X, (rocblas_int)ldx, t, 1,
                     &beta, out, 1) != rocblas_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_dense_f32_transpose(int64_t m, int64_t n, const float* X, int64_t ldx, float* Xt, int64_t ldxt,
+                                       hipStream_t stream) {
+  if (m < 0 || n < 0) return XTVXY_ERROR_INVALID_VALUE;
+  if (m == 0 || n == 0) return XTVXY_SUCCESS;
+  if (ldx < n || ldxt < m) return XTVXY_ERROR_INVALID_VALUE;
+  if (m > INT32_MAX || n > INT32_MAX || ldx > INT32_MAX || ldxt > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (!X || !Xt) return XTVXY_ERROR_NULL_POINTER;
+  const size_t xb = ((size_t)(m - 1) * ldx + n) * sizeof(float), tb = ((size_t)(n - 1) * ldxt + m) * sizeof(float);
+  if (reinterpret_cast<uintptr_t>(X) < reinterpret_cast<uintptr_t>(Xt) + tb &&
+      reinterpret_cast<uintptr_t>(Xt) < reinterpret_cast<uintptr_t>(X) + xb)
+    return XTVXY_ERROR_ALIASING;
+  rocblas_handle h;
+  xtvxy_status st = blas_handle(&h);
+  if (st != XTVXY_SUCCESS) return st;
+  if (rocblas_set_stream(h, stream) != rocblas_status_success ||
+      rocblas_set_pointer_mode(h, rocblas_pointer_mode_host) != rocblas_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  // Column-major: X is the n x m matrix A (lda = ldx), Xt the m x n matrix C (ldc = ldxt), C = A^T
+  // (beta = 0: the second operand, C itself, is not read).
+  const float one = 1.0f, zero = 0.0f;
+  if (rocblas_sgeam(h, rocblas_operation_transpose, rocblas_operation_none, (rocblas_int)m, (rocblas_int)n, &one, X,
+                    (rocblas_int)ldx, &zero, Xt, (rocblas_int)ldxt, Xt, (rocblas_int)ldxt) != rocblas_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_dense_f32_unfused_reference_explicit(int64_t m, int64_t n, float alpha, const float* X, int64_t ldx,
+                                                        const float* Xt, int64_t ldxt, const float* v, const float* y,
+                                                        float beta, const float* z, float* out, void* workspace,
+                                                        size_t workspace_bytes, hipStream_t stream) {
+  bool quick = false;
+  xtvxy_status st = check_dense_args(m, n, alpha, X, ldx, v, y, beta, z, out, &quick);
+  if (st != XTVXY_SUCCESS) return st;
+  if (quick) return n == 0 ? XTVXY_SUCCESS
+                           : (launch_beta_only(n, beta, z, out, stream) == hipSuccess ? XTVXY_SUCCESS
+                                                                                      : XTVXY_ERROR_LAUNCH);
+  if (ldxt < m) return XTVXY_ERROR_INVALID_VALUE;
+  if (m > INT32_MAX || n > INT32_MAX || ldx > INT32_MAX || ldxt > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
+  if (!Xt) return XTVXY_ERROR_NULL_POINTER;
+  const size_t tb = ((size_t)(n - 1) * ldxt + m) * sizeof(float);
+  if (reinterpret_cast<uintptr_t>(out) < reinterpret_cast<uintptr_t>(Xt) + tb &&
+      reinterpret_cast<uintptr_t>(Xt) < reinterpret_cast<uintptr_t>(out) + (size_t)n * sizeof(float))
+    return XTVXY_ERROR_ALIASING;
+  if (!workspace || workspace_bytes < (size_t)m * sizeof(float)) return XTVXY_ERROR_WORKSPACE;
+  rocblas_handle h;
+  st = blas_handle(&h);
+  if (st != XTVXY_SUCCESS) return st;
+  if (rocblas_set_stream(h, stream) != rocblas_status_success ||
+      rocblas_set_pointer_mode(h, rocblas_pointer_mode_host) != rocblas_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  float* t = static_cast<float*>(workspace);
+  const float one = 1.0f, zero = 0.0f;
+  // X y = A^T y with A the column-major n x m view of X; X^T t = B^T t with B the column-major
+  // m x n view of Xt. Both are transposed products, each reading its matrix along its rows.
+  if (rocblas_sgemv(h, rocblas_operation_transpose, (rocblas_int)n, (rocblas_int)m, &one, X, (rocblas_int)ldx, y, 1,
+                    &zero, t, 1) != rocblas_status_success)
+    return XTVXY_ERROR_LIBRARY;
+  if (v && launch_scale(m, v, t, stream) != hipSuccess) return XTVXY_ERROR_LAUNCH;
+  if (beta != 0.0f && out != z &&
+      hipMemcpyAsync(out, z, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return XTVXY_ERROR_LAUNCH;
+  if (rocblas_sgemv(h, rocblas_operation_transpose, (rocblas_int)m, (rocblas_int)n, &alpha, Xt, (rocblas_int)ldxt, t,
+                    1, &beta, out, 1) != rocblas_status_success)
     return XTVXY_ERROR_LIBRARY;
   return XTVXY_SUCCESS;
 }

@@ -383,6 +383,28 @@ xtvxy_status xtvxy_dense_f32_unfused_reference(int64_t m, int64_t n, float alpha
                                                void *workspace, size_t workspace_bytes,
                                                hipStream_t stream);
 
+/* The stronger dense comparator. rocBLAS's sgemv without transpose on the column-major view of a
+ * row-major X (the comparator's last step, X^T t) is slow when X has few columns and many rows
+ * (about 55 GB/s at 10^6 x 256). Given a copy of X^T, both steps are transposed sgemvs, each
+ * reading its matrix along its rows, as the CSR comparator's explicit-transpose plan does for
+ * SpMV.
+ *   xtvxy_dense_f32_transpose: Xt (n x m, row-major, leading dimension ldxt >= m) = X^T, by
+ *     rocBLAS sgeam; a set-up call for the comparator, kept out of timed regions. X and Xt must
+ *     not overlap (XTVXY_ERROR_ALIASING). XTVXY_ERROR_INVALID_VALUE for negative sizes,
+ *     ldx < n or ldxt < m; XTVXY_ERROR_UNSUPPORTED beyond 2^31 - 1; nothing to do when m or n
+ *     is 0. Asynchronous on `stream`.
+ *   xtvxy_dense_f32_unfused_reference_explicit: the comparator above with X^T t computed from Xt
+ *     (n x m, ldxt >= m, made from the same X; the caller keeps the two consistent). Otherwise
+ *     the same arguments, rules and workspace as xtvxy_dense_f32_unfused_reference; Xt is read
+ *     only when X is, and out must not overlap it. */
+xtvxy_status xtvxy_dense_f32_transpose(int64_t m, int64_t n, const float *X, int64_t ldx, float *Xt, int64_t ldxt,
+                                       hipStream_t stream);
+xtvxy_status xtvxy_dense_f32_unfused_reference_explicit(int64_t m, int64_t n, float alpha, const float *X,
+                                                        int64_t ldx, const float *Xt, int64_t ldxt, const float *v,
+                                                        const float *y, float beta, const float *z, float *out,
+                                                        void *workspace, size_t workspace_bytes,
+                                                        hipStream_t stream);
+
 /* The CSR comparator keeps rocSPARSE descriptors and the result of the
  * structure analysis in a plan, made once per matrix (blocking, allocates).
  * Unlike the dense comparator it does not take xtvxy_csr_f32's argument list

@@ -76,6 +76,29 @@ def test_dense_argument_errors(lib, fn):
     assert dense_status(n=0, ldx=1, fn=fn) == _abi.XTVXY_SUCCESS
 
 
+def test_dense_explicit_comparator_argument_errors(lib):
+    def explicit(m=8, n=8, X=FAKE, ldx=8, Xt=FAKE + (1 << 20), ldxt=8, y=FAKE + 4096, out=FAKE + 8192, ws=None, wsb=0):
+        return lib.xtvxy_dense_f32_unfused_reference_explicit(m, n, 1.0, X, ldx, Xt, ldxt, None, y, 0.0, None, out, ws,
+                                                              wsb, None)
+    assert explicit(m=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert explicit(ldx=7) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert explicit(ldxt=7) == _abi.XTVXY_ERROR_INVALID_VALUE      # ldxt < m
+    assert explicit(Xt=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert explicit(X=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert explicit(out=FAKE + (1 << 20) + 64) == _abi.XTVXY_ERROR_ALIASING  # out inside Xt
+    assert explicit(out=FAKE + 16) == _abi.XTVXY_ERROR_ALIASING             # out inside X
+    assert explicit() == _abi.XTVXY_ERROR_WORKSPACE                          # no workspace for t
+    assert explicit(n=0, ldx=1) == _abi.XTVXY_SUCCESS
+    tr = lib.xtvxy_dense_f32_transpose
+    assert tr(-1, 8, FAKE, 8, FAKE + (1 << 20), 8, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert tr(8, 8, FAKE, 7, FAKE + (1 << 20), 8, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert tr(8, 8, FAKE, 8, FAKE + (1 << 20), 7, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert tr(8, 8, None, 8, FAKE + (1 << 20), 8, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert tr(8, 8, FAKE, 8, FAKE + 128, 8, None) == _abi.XTVXY_ERROR_ALIASING
+    assert tr(0, 8, None, 8, None, 1, None) == _abi.XTVXY_SUCCESS
+    assert tr(1 << 32, 8, FAKE, 8, FAKE + (1 << 20), 1 << 32, None) == _abi.XTVXY_ERROR_UNSUPPORTED
+
+
 def csr_status(m=8, n=8, nnz=16, alpha=1.0, rp=FAKE, ci=FAKE + 1024, vals=FAKE + 2048, v=None, y=FAKE + 4096,
                beta=0.0, z=None, out=FAKE + 8192):
     return _abi.load().xtvxy_csr_f32(m, n, nnz, alpha, rp, ci, vals, v, y, beta, z, out, None, 0, None)

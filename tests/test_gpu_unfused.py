@@ -31,6 +31,30 @@ def test_dense_comparator_in_place_and_quick_returns():
     assert np.array_equal(d.run(unfused=True, alpha=0.0, beta=0.5), (np.float32(0.5) * p.z).astype(np.float32))
 
 
+@pytest.mark.parametrize("m,n,v,beta,pad", [(2048, 128, "uniform", 0.5, 0), (20000, 256, None, 0.0, 3),
+                                            (300, 8192, "uniform", 1.0, 0), (64, 20000, "uniform01", -1.0, 5),
+                                            (1, 1, "uniform", 0.5, 0), (7, 3, None, 0.25, 1)])
+def test_dense_explicit_transpose_comparator(m, n, v, beta, pad):
+    # X^T made once (rocBLAS sgeam, exact), then both products as transposed sgemvs; Xt may be padded
+    import torch
+    p = datagen.dense_problem(m, n, seed=m + 2 * n, v=v, z="uniform", beta=beta)
+    d = DenseOnDevice(p)
+    note("dense unfused explicit transpose m=%d n=%d ldxt=%d" % (m, n, m + pad))
+    X = d.X.view(p.m, p.ldx)[:, : p.n]
+    buf = torch.full((n, m + pad), float("nan"), dtype=torch.float32, device="cuda")
+    Xt = buf[:, :m]
+    ldx = max(X.stride(0) if m > 1 else n, n, 1)
+    xt.xtvxy_dense_f32_transpose(m, n, X.data_ptr(), ldx, Xt.data_ptr(), m + pad, None)
+    torch.cuda.synchronize()
+    assert torch.equal(Xt.cpu(), X.cpu().t())
+    assert bool(torch.isnan(buf[:, m:]).all())  # the padding is not written
+    out = torch.full((n,), float("nan"), device="cuda")  # beta == 0 must not read out
+    xt.dense_unfused(X, d.y, d.v, d.z, p.alpha, beta, out=out, Xt=Xt)
+    torch.cuda.synchronize()
+    ref, bnd = dense_oracle(p)
+    assert_parity(out.cpu().numpy(), ref, bnd, "dense unfused explicit")
+
+
 @pytest.mark.parametrize("explicit", [False, True])
 @pytest.mark.parametrize("m,n,mean_len", [(3000, 1000, 10.0), (2000, 50000, 30.0), (10, 5, 2.0)])
 @pytest.mark.parametrize("beta", [0.0, 0.75])
