@@ -194,10 +194,6 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
                        xtvxy_launch_params* p, bool fused = true);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p);
-// The row-class kernel's plan for an analysed matrix whose columns are relabelled most frequent
-// first: covered[k] = entries in the k most frequent columns (k = 0..n).
-xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
-                            const int64_t* covered, xtvxy_launch_params* p);
 
 // Argument checks shared by the fused entry points and the comparator (api.cpp). On
 // success *quick tells that only out = beta z (or nothing, when n == 0) remains to do.

@@ -388,63 +388,3 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
 }
 
 }  // namespace xtvxy
-
-namespace xtvxy {
-
-// Row-class kernel on an analysed matrix (columns relabelled most frequent first, so that the
-// windows [0, W) and [0, Wy) hold the hottest columns). Every wavefront works alone, so latency is
-// hidden by wavefronts, not barriers: one workgroup of 1024 threads per CU gets a CU's whole LDS
-// for the windows. When both windows hold all of n nothing is cold; otherwise the LDS left after
-// the wavefronts' bin state is split between the two windows to minimise the cost of what falls
-// outside them, counted from the analysis: an entry whose column is outside the y window is one
-// gather from global memory (an L2 request, and an HBM read of a line when it misses), one
-// outside the output window is a binned item (an 8-byte store, its read in the bin pass and an
-// LDS add there); both are priced alike (kRowsColdGather, kRowsColdItem, seconds per entry).
-constexpr double kRowsColdGather = 8.0e-12;
-constexpr double kRowsColdItem = 8.0e-12;
-
-xtvxy_status model_csr_rows(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d, const int64_t* covered,
-                            xtvxy_launch_params* p) {
-  std::memset(p, 0, sizeof(*p));
-  p->kernel = XTVXY_CSR_ROWS;
-  p->vec = 1;
-  p->chunks = 1;
-  p->group = 1;
-  p->entries_per_thread = kRowsSlots;
-  p->block_threads = 1024;
-  p->grid = std::max<int64_t>(1, d.compute_units);
-  const int waves = p->block_threads / 64;
-  const int64_t lds = d.lds_bytes - 256;  // a little slack for the launch's own use
-  double cold_cost = 0.0;
-  if ((int64_t)n * 8 + 4 * (int64_t)p->block_threads <= lds) {
-    p->lds_window = (int32_t)n;
-    p->y_window = (int32_t)n;
-  } else {
-    double best = 1e300;
-    for (int32_t bc = 16384; bc <= 32768; bc *= 2) {
-      const int64_t bins_max = ceil_div(n, bc);
-      if (bins_max > kMaxBins) continue;
-      const int64_t state = bins_max * (int64_t)kCsrWaveBinStateBytes * waves + 4 * (int64_t)p->block_threads;
-      const int64_t cols = std::max<int64_t>(0, (lds - state) / 4 - 2);
-      const int64_t step = std::max<int64_t>(256, cols / 256);
-      for (int64_t w = 0; w <= std::min<int64_t>(cols, n); w += step) {
-        const int64_t wy = std::min<int64_t>(n, cols - w);
-        const double cost = (double)(nnz - (covered ? covered[w] : (int64_t)((double)nnz * w / n))) * kRowsColdItem +
-                            (double)(nnz - (covered ? covered[wy] : (int64_t)((double)nnz * wy / n))) * kRowsColdGather;
-        if (cost < best * 0.9999) {
-          best = cost;
-          p->lds_window = (int32_t)w;
-          p->y_window = (int32_t)wy;
-          p->bin_columns = bc;
-        }
-      }
-    }
-    if (best > 1e299) return XTVXY_ERROR_UNSUPPORTED;
-    cold_cost = best;
-  }
-  const double io_bytes = 8.0 * nnz + 4.0 * (m + 1) + 4.0 * m + 12.0 * n;
-  p->predicted_seconds = io_bytes / (kSustained * d.hbm_bytes_per_s) + cold_cost + 4 * kLaunch;
-  return complete_csr(m, n, nnz, d, p);
-}
-
-}  // namespace xtvxy
