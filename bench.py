@@ -312,18 +312,20 @@ def bench_logreg(args):
     v = torch.from_numpy(X.v).to(dev)
     d = torch.from_numpy(X.y).to(dev)
     q = torch.empty_like(d)
-    hws_bytes = xt.xtvxy_csr_f32_workspace_size(X.m, X.n, X.nnz)
+    # the plan the solver's products take: the model's, refined by the longest row
+    hplan = xt.xtvxy_csr_f32_plan_rows(X.m, X.n, X.nnz, int(np.diff(X.row_ptr).max(initial=0)))
+    hws_bytes = hplan.workspace_bytes
     hws = torch.empty(max(hws_bytes, 1), dtype=torch.uint8, device=dev)
     sh = torch.cuda.current_stream().cuda_stream or None
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
     for _ in range(args.warmup):
-        xt.xtvxy_csr_f32(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
-                         d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh)
+        xt.xtvxy_csr_f32_ex(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+                            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
     for i in range(args.steps):
         xt.xtvxy_set_kernel_timing_events(pairs[i][0], pairs[i][1])
-        xt.xtvxy_csr_f32(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
-                         d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh)
+        xt.xtvxy_csr_f32_ex(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+                            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
     torch.cuda.synchronize()
     xt.xtvxy_set_kernel_timing_events(None, None)
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
@@ -356,7 +358,7 @@ def bench_logreg(args):
         "speedup_vs_unfused": round(results["unfused"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
         "speedup_vs_unfused_explicit_transpose": round(
             results["unfused_explicit_transpose"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
-        "roofline": {"bound": "hbm", "kernel": kernel_name(xt.xtvxy_csr_f32_plan(X.m, X.n, X.nnz)),
+        "roofline": {"bound": "hbm", "kernel": kernel_name(hplan), "grid": hplan.grid,
                      "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                      "what": "the Hessian-vector product alone (one fused call, v = p(1 - p), y = z = d, "

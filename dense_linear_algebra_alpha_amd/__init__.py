@@ -29,7 +29,7 @@ from ._abi import (XTVXY_CSR_ROWS, XTVXY_CSR_TILES, XTVXY_CSR_WAVES, XTVXY_DENSE
 
 __all__ = [
     "xtvxy_get_device_info", "xtvxy_dense_f32_plan", "xtvxy_dense_f32_plan_complete", "xtvxy_csr_f32_plan",
-    "xtvxy_csr_f32_plan_complete", "xtvxy_dense_f32_workspace_size", "xtvxy_dense_f32", "xtvxy_dense_f32_ex",
+    "xtvxy_csr_f32_plan_complete", "xtvxy_csr_f32_plan_rows", "xtvxy_dense_f32_workspace_size", "xtvxy_dense_f32", "xtvxy_dense_f32_ex",
     "xtvxy_csr_f32_workspace_size", "xtvxy_csr_f32", "xtvxy_csr_f32_ex", "xtvxy_csr_check",
     "xtvxy_dense_f32_unfused_reference_workspace_size", "xtvxy_dense_f32_unfused_reference",
     "xtvxy_dense_f32_transpose", "xtvxy_dense_f32_unfused_reference_explicit",
@@ -135,6 +135,12 @@ def xtvxy_dense_bf16_ex(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, work
 def xtvxy_csr_f32_plan(m, n, nnz, dev=None) -> xtvxy_launch_params:
     p = xtvxy_launch_params()
     _abi.call("xtvxy_csr_f32_plan", m, n, nnz, ctypes.byref(dev) if dev else None, ctypes.byref(p))
+    return p
+
+
+def xtvxy_csr_f32_plan_rows(m, n, nnz, longest_row, dev=None) -> xtvxy_launch_params:
+    p = xtvxy_launch_params()
+    _abi.call("xtvxy_csr_f32_plan_rows", m, n, nnz, longest_row, ctypes.byref(dev) if dev else None, ctypes.byref(p))
     return p
 
 

@@ -103,6 +103,7 @@ SIGNATURES = {
     "xtvxy_dense_f32_plan": [_i64, _i64, _i64, _i32, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
     "xtvxy_dense_f32_plan_complete": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_plan": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
+    "xtvxy_csr_f32_plan_rows": [_i64, _i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_plan_complete": [_i64, _i64, _i64, _P(xtvxy_device_info), _P(xtvxy_launch_params)],
     "xtvxy_dense_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_dense_f32": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],

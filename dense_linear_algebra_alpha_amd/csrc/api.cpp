@@ -546,6 +546,22 @@ xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_d
   return model_csr(m, n, nnz, d, plan);
 }
 
+xtvxy_status xtvxy_csr_f32_plan_rows(int64_t m, int64_t n, int64_t nnz, int64_t longest_row,
+                                     const xtvxy_device_info* dev, xtvxy_launch_params* plan) {
+  if (!plan) return XTVXY_ERROR_NULL_POINTER;
+  if (longest_row < 0 || longest_row > nnz) return XTVXY_ERROR_INVALID_VALUE;
+  xtvxy_status st = xtvxy_csr_f32_plan(m, n, nnz, dev, plan);
+  if (st != XTVXY_SUCCESS) return st;
+  xtvxy_device_info d;
+  if (dev) {
+    d = *dev;
+  } else if ((st = device_info(-1, &d)) != XTVXY_SUCCESS) {
+    return st;
+  }
+  (void)refine_waves_grid(m, n, nnz, longest_row, d, plan);
+  return XTVXY_SUCCESS;
+}
+
 xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info* dev,
                                          xtvxy_launch_params* plan) {
   if (!plan) return XTVXY_ERROR_NULL_POINTER;

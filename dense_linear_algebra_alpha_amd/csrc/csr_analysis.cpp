@@ -36,7 +36,7 @@ struct xtvxy_csr_analysis_s {
   int32_t* batches = nullptr;        // [batches_count][2] (owned)
   int32_t* batch_prefix = nullptr;   // [batches_count + 1] (owned)
   int32_t batches_count = 0;
-  int64_t very_long_rows = 0;        // rows longer than csr_row_class's classes (> 509 entries)
+  int64_t longest_row = 0;           // entries of the longest row
   std::vector<int64_t> covered;      // entries in the k most frequent columns, k = 0..n
   xtvxy_launch_params plan{};        // the model's, workspace_bytes including the gathered y
 };
@@ -150,7 +150,8 @@ xtvxy_status analyse(xtvxy_csr_analysis an, const int32_t* row_ptr, const int32_
     }
   }
   an->batches_count = (int32_t)(batches.size() / 2);
-  an->very_long_rows = (int64_t)by_class[kRowsVeryLong].size();
+  for (int64_t i = 0; i < m; ++i)
+    an->longest_row = std::max<int64_t>(an->longest_row, (int64_t)h_rp[(size_t)i + 1] - h_rp[(size_t)i]);
   if (e == hipSuccess) e = upload(&an->rows, rows, stream);
   if (e == hipSuccess) e = upload(&an->bounds, bounds, stream);
   if (e == hipSuccess) e = upload(&an->batches, batches, stream);
@@ -189,15 +190,8 @@ xtvxy_status xtvxy_csr_f32_analyse(int64_t m, int64_t n, int64_t nnz, const int3
       // the model's plan for the relabelled matrix: its output and y windows [0, W) and [0, Wy) now
       // hold the most frequent columns whatever the caller's column order
       if (st == XTVXY_SUCCESS) st = model_csr(m, n, nnz, d, &an->plan);
-      // The row lengths refine the wavefront kernel's grid: when every row fits a 512-slot tile
-      // and rows hold 8 or more entries on average, its tiles are full and three 256-thread
-      // workgroups per CU ran fastest (uniform rows of 10-100 entries: 7-8% faster than four);
-      // shorter rows (tiles capped at 64 rows) or rows longer than a tile (two sweeps) ran
-      // faster with four or more, the model's choice.
-      xtvxy_launch_params& pl = an->plan;
-      if (st == XTVXY_SUCCESS && pl.kernel == XTVXY_CSR_WAVES && pl.block_threads == 256 &&
-          an->very_long_rows == 0 && nnz >= 8 * m && pl.grid > 3 * (int64_t)d.compute_units)
-        pl.grid = 3 * (int64_t)d.compute_units;
+      // the longest row refines the wavefront kernel's grid
+      if (st == XTVXY_SUCCESS) (void)refine_waves_grid(m, n, nnz, an->longest_row, d, &an->plan);
       if (st == XTVXY_SUCCESS) st = complete_for(an, &an->plan);
     }
     if (st != XTVXY_SUCCESS) {

@@ -194,6 +194,11 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
                        xtvxy_launch_params* p, bool fused = true);
 xtvxy_status complete_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info& d,
                           xtvxy_launch_params* p);
+// The wavefront kernel's grid for a matrix whose longest row is known (a structure analysis, the
+// solver's row scan): three 256-thread workgroups per CU when every row fits a tile and rows hold
+// 8 or more entries on average, completed; false (plan unchanged) otherwise.
+bool refine_waves_grid(int64_t m, int64_t n, int64_t nnz, int64_t longest_row, const xtvxy_device_info& d,
+                       xtvxy_launch_params* p);
 
 // Argument checks shared by the fused entry points and the comparator (api.cpp). On
 // success *quick tells that only out = beta z (or nothing, when n == 0) remains to do.
@@ -242,7 +247,7 @@ struct LrScalars {  // device-side scalars of the solver, in its workspace
   int32_t neg;             // CG met a direction of non-positive curvature (later iterations do nothing)
   int32_t done;            // CG's residual vanished exactly (later iterations do nothing)
   int32_t iters;           // CG iterations performed (the one that met neg included)
-  int32_t pad;
+  uint32_t max_row;        // entries of the longest row (set once per solve by launch_lr_max_row)
 };
 constexpr int kLrMaxParts = 2048;     // partial sums per reduction row (workgroups of a streaming kernel)
 constexpr int kLrRows = 4;            // reduction rows
@@ -254,6 +259,8 @@ inline int lr_grid(int64_t count) {
   const int64_t g = (count + 1023) / 1024;
   return (int)(g < kLrMaxParts ? g : kLrMaxParts);
 }
+// *longest = the largest row_ptr[i + 1] - row_ptr[i] (zeroed here, then an atomic maximum per wavefront).
+hipError_t launch_lr_max_row(int64_t m, const int32_t* row_ptr, uint32_t* longest, hipStream_t s);
 hipError_t launch_lr_link(int64_t m, float* t, const float* xs, float step, const float* c, float* u, float* v,
                           double* part, hipStream_t s);
 hipError_t launch_lr_trial(int64_t m, const float* t, const float* xs, double a, const float* c, double* part,

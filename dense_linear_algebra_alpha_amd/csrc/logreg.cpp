@@ -85,8 +85,12 @@ struct Engine {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  const xtvxy_launch_params* hvp_plan;  // the fused H d's plan when the row lengths refine it, else null
 
   xtvxy_status hvp(const float* v, float lam, const float* d, float* q) const {
+    if (kind == XTVXY_LOGREG_FUSED && hvp_plan)
+      return xtvxy_csr_f32_ex(m, n, nnz, 1.0f, row_ptr, col_idx, values, v, d, lam, d, q, ws, ws_bytes, stream,
+                              hvp_plan);
     if (kind == XTVXY_LOGREG_FUSED)
       return xtvxy_csr_f32(m, n, nnz, 1.0f, row_ptr, col_idx, values, v, d, lam, d, q, ws, ws_bytes, stream);
     return xtvxy_csr_f32_unfused_reference(plan, 1.0f, v, d, lam, d, q, stream);
@@ -160,8 +164,6 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
   float* q = reinterpret_cast<float*>(base + L.q_off);
   double* part = reinterpret_cast<double*>(base + L.part_off);
   LrScalars* S = reinterpret_cast<LrScalars*>(base + L.scalars_off);
-  const Engine E{opt->engine, m, n, nnz, row_ptr, col_idx, values, unfused, base + L.product_off, L.product_bytes,
-                 stream};
   const float lam = opt->lambda;
   LrScalars h{};
   auto launched = [](hipError_t e) { return e == hipSuccess ? XTVXY_SUCCESS : XTVXY_ERROR_LAUNCH; };
@@ -171,6 +173,24 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
       return XTVXY_ERROR_LAUNCH;
     return XTVXY_SUCCESS;
   };
+  // The Hessian-vector products are most of a step. Their plan is the model's, except that the
+  // longest row (one scan of row_ptr and one read-back per solve) can refine the wavefront
+  // kernel's grid, as a structure analysis does (refine_waves_grid).
+  xtvxy_launch_params hvp_plan{};
+  bool refined = false;
+  if (opt->engine == XTVXY_LOGREG_FUSED && m > 0 && nnz > 0 && n > 0) {
+    xtvxy_device_info dinfo;
+    if ((st = current_device_info(&dinfo)) != XTVXY_SUCCESS) return st;
+    if ((st = xtvxy_csr_f32_plan(m, n, nnz, &dinfo, &hvp_plan)) != XTVXY_SUCCESS) return st;
+    if (hvp_plan.kernel == XTVXY_CSR_WAVES) {
+      if ((st = launched(launch_lr_max_row(m, row_ptr, &S->max_row, stream))) != XTVXY_SUCCESS) return st;
+      if ((st = read_scalars()) != XTVXY_SUCCESS) return st;
+      refined = refine_waves_grid(m, n, nnz, (int64_t)h.max_row, dinfo, &hvp_plan) &&
+                (size_t)hvp_plan.workspace_bytes <= L.product_bytes;
+    }
+  }
+  const Engine E{opt->engine, m, n, nnz, row_ptr, col_idx, values, unfused, base + L.product_off, L.product_bytes,
+                 stream, refined ? &hvp_plan : nullptr};
   const double nan = std::numeric_limits<double>::quiet_NaN();
   auto record = [&](int64_t k, int col, double value) {
     if (k < history_rows) history[k * kHistoryCols + col] = value;

@@ -86,6 +86,17 @@ struct DotArgs {
 };
 
 // Partial sums of up to three dot products of n-vectors, into rows row0 .. row0 + k - 1.
+// The longest row: each wavefront's maximum of row_ptr[i + 1] - row_ptr[i], folded into *longest
+// by one vector atomic maximum (the caller zeroes it).
+__global__ __launch_bounds__(kThreads) void lr_max_row_kernel(int64_t m, const int32_t* __restrict__ rp,
+                                                               uint32_t* longest) {
+  uint32_t mx = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < m; i += (int64_t)gridDim.x * kThreads)
+    mx = max(mx, (uint32_t)(rp[i + 1] - rp[i]));
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(longest, mx);
+}
+
 __global__ __launch_bounds__(kThreads) void lr_dots_kernel(int64_t n, DotArgs a, int row0, double* __restrict__ part) {
   __shared__ double red[kThreads / 64];
   double s[3] = {0.0, 0.0, 0.0};
@@ -296,6 +307,13 @@ hipError_t launch_lr_trial(int64_t m, const float* t, const float* xs, double a,
                            hipStream_t s) {
   if (m == 0) return hipSuccess;
   hipLaunchKernelGGL(lr_trial_kernel, grid_for(m), dim3(kThreads), 0, s, m, t, xs, a, c, part);
+  return hipGetLastError();
+}
+
+hipError_t launch_lr_max_row(int64_t m, const int32_t* row_ptr, uint32_t* longest, hipStream_t s) {
+  hipError_t e = launch_zero(longest, sizeof(uint32_t), s);
+  if (e != hipSuccess || m <= 0) return e;
+  hipLaunchKernelGGL(lr_max_row_kernel, grid_for(m), dim3(kThreads), 0, s, m, row_ptr, longest);
   return hipGetLastError();
 }
 

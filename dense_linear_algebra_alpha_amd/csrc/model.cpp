@@ -387,4 +387,21 @@ xtvxy_status model_csr(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_inf
   return XTVXY_SUCCESS;
 }
 
+bool refine_waves_grid(int64_t m, int64_t n, int64_t nnz, int64_t longest_row, const xtvxy_device_info& d,
+                       xtvxy_launch_params* p) {
+  // When every row fits a 512-slot tile (a row of len entries spans len + 3 slots from its quad)
+  // and rows hold 8 or more entries on average, the wavefront kernel's tiles are full, and three
+  // 256-thread workgroups per CU ran fastest (uniform rows of 10-100 entries: 7-8% faster than
+  // four). Shorter rows (tiles capped at 64 rows) or rows longer than a tile (two sweeps) ran
+  // faster with four or more, the model's choice.
+  if (p->kernel != XTVXY_CSR_WAVES || p->block_threads != 256 || longest_row + 3 > 512 || nnz < 8 * m ||
+      p->grid <= 3 * (int64_t)d.compute_units)
+    return false;
+  xtvxy_launch_params q = *p;
+  q.grid = 3 * (int64_t)d.compute_units;
+  if (complete_csr(m, n, nnz, d, &q) != XTVXY_SUCCESS) return false;
+  *p = q;
+  return true;
+}
+
 }  // namespace xtvxy

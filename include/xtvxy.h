@@ -137,6 +137,18 @@ xtvxy_status xtvxy_dense_f32_plan(int64_t m, int64_t n, int64_t ldx, int X_align
 xtvxy_status xtvxy_csr_f32_plan(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_info *dev,
                                 xtvxy_launch_params *plan);
 
+/* The same plan for a caller who knows the matrix's longest row (entries): the launch parameters
+ * follow the input's characteristics ("On optimizing machine learning workloads via kernel
+ * fusion", abstract), and the row lengths are one the shape does not give. When the model takes
+ * the wavefront kernel (XTVXY_CSR_WAVES, 256 threads), every row fits its 512-slot tiles
+ * (longest_row + 3 <= 512) and rows hold 8 or more entries on average, the plan runs three
+ * workgroups per CU instead of the model's four (full tiles need fewer wavefronts to hide their
+ * latency); otherwise it is xtvxy_csr_f32_plan's. Completed (workspace_bytes filled in); pass it
+ * to xtvxy_csr_f32_ex. XTVXY_ERROR_INVALID_VALUE when longest_row is negative or above nnz. The
+ * structure analysis and the Newton-CG solver apply the same rule. */
+xtvxy_status xtvxy_csr_f32_plan_rows(int64_t m, int64_t n, int64_t nnz, int64_t longest_row,
+                                     const xtvxy_device_info *dev, xtvxy_launch_params *plan);
+
 /* ------------------------------------------------------------------------ */
 /* Fused entry points                                                       */
 /* ------------------------------------------------------------------------ */

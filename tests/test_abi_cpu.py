@@ -270,6 +270,26 @@ def test_csr_wave_plans(lib):
                                        MI355X)
 
 
+def test_csr_plan_rows(lib):
+    """Three workgroups per CU for the wavefront kernel when every row fits its 512-slot tiles and
+    rows hold 8 or more entries on average; the model's plan otherwise."""
+    base = xt.xtvxy_csr_f32_plan(10_000_000, 1000, 100_000_000, MI355X)
+    assert base.kernel == xt.XTVXY_CSR_WAVES and base.grid == 4 * 256
+    p = xt.xtvxy_csr_f32_plan_rows(10_000_000, 1000, 100_000_000, 40, MI355X)
+    assert p.kernel == xt.XTVXY_CSR_WAVES and p.grid == 3 * 256 and p.workspace_bytes == 768 * 1000 * 4
+    assert xt.xtvxy_csr_f32_plan_rows(10_000_000, 1000, 100_000_000, 509, MI355X).grid == 768
+    for m, n, nnz, longest in ((10_000_000, 1000, 100_000_000, 510),  # a row longer than a tile
+                               (10_000_000, 1000, 50_000_000, 40),    # 5 entries per row
+                               (5_000_000, 1_000_000, 200_000_000, 2726)):  # wide: workgroup tiles
+        q = xt.xtvxy_csr_f32_plan_rows(m, n, nnz, longest, MI355X)
+        r = xt.xtvxy_csr_f32_plan(m, n, nnz, MI355X)
+        assert (q.kernel, q.grid, q.lds_window, q.y_window, q.bin_columns) == (r.kernel, r.grid, r.lds_window,
+                                                                               r.y_window, r.bin_columns)
+    for longest in (-1, 100_000_001):
+        with pytest.raises(xt.XtvxyError):
+            xt.xtvxy_csr_f32_plan_rows(10_000_000, 1000, 100_000_000, longest, MI355X)
+
+
 def test_csr_model_bins_the_wide_zipf_matrix_and_not_the_narrow_one(lib):
     assert xt.xtvxy_csr_f32_plan(5_000_000, 1_000_000, 200_000_000, MI355X).bin_columns == 16384
     assert xt.xtvxy_csr_f32_plan(10_000_000, 1000, 100_000_000, MI355X).bin_columns == 0
