@@ -29,8 +29,8 @@ using namespace xtvxy;
 
 namespace {
 
-constexpr int kWarmup = 2;
-constexpr int kFinalists = 4;  // re-timed together with the model's plan
+constexpr int kWarmup = 5;
+constexpr int kFinalists = 6;  // re-timed together with the model's plan
 
 struct Key {
   std::string device;

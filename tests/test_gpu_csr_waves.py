@@ -160,3 +160,31 @@ def test_zipf_scaled():
 def test_full_size_zipf_5000000x1000000():
     p = datagen.WORKLOADS["csr_5000000x1000000_zipf"]()
     check(p, wave_plan(p.m, p.n, p.nnz, 1024, 256, 28000, 0, 16384), what="waves zipf full")
+
+
+@pytest.mark.parametrize("m,n,mean_len,longest", [(200_000, 1000, 10.0, None), (100_000, 4000, 40.0, None),
+                                                  (150_000, 2000, 12.0, 600)])
+def test_plan_from_the_longest_row(m, n, mean_len, longest):
+    # xtvxy_csr_f32_plan_rows: three workgroups per CU when every row fits a tile and rows hold 8 or
+    # more entries on average (the first two matrices), the model's plan when a row is longer than
+    # a tile (the third, with one row made 600 entries long)
+    p = datagen.csr_random(m, n, seed=m + n + 7, mean_len=mean_len, empty_frac=0.05, dup_frac=0.05)
+    if longest:
+        rl = np.diff(p.row_ptr).astype(np.int64)
+        rl[m // 2] = longest
+        rp = np.zeros(m + 1, dtype=np.int64)
+        np.cumsum(rl, out=rp[1:])
+        g = np.random.default_rng(3)
+        cols = g.integers(0, n, size=int(rp[-1])).astype(np.int32)
+        vals = g.uniform(-1, 1, size=int(rp[-1])).astype(np.float32)
+        p = datagen.CsrProblem(m, n, rp.astype(np.int32), cols, vals, p.y, p.v, p.z, p.alpha, p.beta, "long row")
+    lr = int(np.diff(p.row_ptr).max())
+    plan = xt.xtvxy_csr_f32_plan_rows(p.m, p.n, p.nnz, lr)
+    model = xt.xtvxy_csr_f32_plan(p.m, p.n, p.nnz)
+    cus = xt.xtvxy_get_device_info().compute_units
+    assert plan.kernel == xt.XTVXY_CSR_WAVES
+    if lr + 3 <= 512 and p.nnz >= 8 * p.m and model.grid > 3 * cus:
+        assert plan.grid == 3 * cus
+    else:
+        assert plan.grid == model.grid
+    check(p, plan, "plan from the longest row (%d)" % lr)
