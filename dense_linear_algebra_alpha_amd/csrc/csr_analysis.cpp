@@ -10,7 +10,9 @@
 //   3. the nonempty rows grouped by class (csr_row_class: very long rows first, then classes
 //      6 down to 0, each in row order) with their entry bounds, and cut into batches: 64 / 2^c
 //      rows of class c < 7 (a row per group of 2^c lanes), one very long row;
-//   4. the model's plan from the coverage of the most frequent columns.
+//   4. the model's plan for the relabelled matrix, the wavefront kernel's grid refined by the
+//      longest row (refine_waves_grid); the prefix sums of the sorted column counts give the
+//      entries outside any output window, so each call's bin pool holds exactly those.
 // Per call: yp[s] = y[perm[s]] into the workspace, the fused kernel on (row_ptr, col_slot, values,
 // v, yp), the bin passes, and the aggregation writing out[perm[s]].
 #include <hip/hip_runtime.h>
