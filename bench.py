@@ -158,7 +158,20 @@ def cpu_baseline(p, budget_s: float, threads=None, min_runs=3):
     med = statistics.median(runs)
     oracle.set_threads(len(os.sched_getaffinity(0)))
     return {"value": round(algorithmic_bytes(p) / med / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "sample": "the full workload, %d runs (median %.3f s each)" % (len(runs), med)}
+            "kind": "oracle", "sample": "the full workload, %d runs (median %.3f s each)" % (len(runs), med),
+            "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def percentiles(ms):
