@@ -389,7 +389,7 @@ def bench_logreg(args):
         record["cpu_baseline"] = {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
                                   "sample": "one Newton step of the same schedule on the full workload (fp64 "
                                             "scipy.sparse products, single-threaded), setup included; threads "
-                                            "available %d" % threads}
+                                            "available %d" % threads, "cpu_model": cpu_model()}
     print(json.dumps(record), flush=True)
 
 
