@@ -36,7 +36,7 @@ __all__ = [
     "xtvxy_csr_f32_unfused_plan_create", "xtvxy_csr_f32_unfused_plan_destroy", "xtvxy_csr_f32_unfused_reference",
     "xtvxy_status_string", "xtvxy_set_kernel_timing_events", "xtvxy_test_group_wait", "xtvxy_read_probe", "xtvxy_scatter_probe",
     "xtvxy_dense_f32_noalloc", "xtvxy_dense_f32_noalloc_max_workspace", "XtvxyError", "xtvxy_device_info", "xtvxy_launch_params",
-    "dense", "csr", "dense_unfused", "dense_transpose", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
+    "dense", "csr", "csr_tensor", "dense_unfused", "dense_transpose", "CsrUnfusedPlan", "csr_check", "dense_plan", "csr_plan", "load",
     "xtvxy_csr_f32_rowdot", "xtvxy_csr_f32_rowdot_ex", "xtvxy_csr_f32_tmv", "xtvxy_csr_f32_tmv_ex", "csr_rowdot",
     "csr_tmv", "xtvxy_logreg_newton_cg_f32_workspace_size", "xtvxy_logreg_newton_cg_f32", "logreg_newton_cg",
     "xtvxy_logreg_options", "xtvxy_logreg_report", "xtvxy_csr_f32_unfused_plan_create_ex",
@@ -479,6 +479,19 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
         xtvxy_csr_f32_ex(*args, plan)
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
+
+
+def csr_tensor(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None, stream=None):
+    """csr() for X given as a torch sparse CSR tensor (torch.sparse_csr_tensor) with int32 indices
+    and float32 values on the GPU; its crow_indices, col_indices and values are passed as they are."""
+    torch = _torch()
+    if X.layout != torch.sparse_csr or X.dim() != 2:
+        raise ValueError("X must be a 2-D torch.sparse_csr tensor")
+    rp, ci, vals = X.crow_indices(), X.col_indices(), X.values()
+    if rp.dtype != torch.int32 or ci.dtype != torch.int32:
+        raise ValueError("X's indices must be int32 (torch.sparse_csr_tensor(..., dtype=torch.float32) with int32 "
+                         "crow_indices and col_indices)")
+    return csr(rp, ci, vals, X.shape[1], y, v, z, alpha, beta, out, plan=plan, workspace=workspace, stream=stream)
 
 
 def _check_csr_arrays(row_ptr, col_idx, values):

@@ -279,3 +279,24 @@ def test_binned_workspace_reuse_and_shrinking_input():
     torch.cuda.synchronize()
     ref_q, bnd_q = csr_oracle(q)
     assert_parity(out.cpu().numpy(), ref_q, bnd_q, "binned smaller")
+
+
+def test_torch_sparse_csr_tensor_input():
+    # the convenience wrapper over torch.sparse_csr_tensor passes the tensor's own arrays
+    import torch
+    p = datagen.csr_random(3000, 700, seed=77, mean_len=9.0, empty_frac=0.1, dup_frac=0.05)
+    ref, bnd = csr_oracle(p)
+    X = torch.sparse_csr_tensor(torch.from_numpy(p.row_ptr).cuda(), torch.from_numpy(p.col_idx).cuda(),
+                                torch.from_numpy(p.values).cuda(), size=(p.m, p.n))
+    d = CsrOnDevice(p)
+    note("csr from torch.sparse_csr_tensor m=%d n=%d nnz=%d" % (p.m, p.n, p.nnz))
+    got = xt.csr_tensor(X, d.y, d.v, d.z, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    assert_parity(got.cpu().numpy(), ref, bnd, "sparse_csr_tensor")
+    with pytest.raises(ValueError):
+        xt.csr_tensor(X.to_dense(), d.y)
+    X64 = torch.sparse_csr_tensor(torch.from_numpy(p.row_ptr.astype(np.int64)).cuda(),
+                                  torch.from_numpy(p.col_idx.astype(np.int64)).cuda(),
+                                  torch.from_numpy(p.values).cuda(), size=(p.m, p.n))
+    with pytest.raises(ValueError):
+        xt.csr_tensor(X64, d.y)
