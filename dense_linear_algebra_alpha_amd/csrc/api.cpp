@@ -151,8 +151,10 @@ xtvxy_status csr_plan_for(int64_t m, int64_t n, int64_t nnz, const xtvxy_device_
   return model_csr(m, n, nnz, d, plan, fused);
 }
 
-// The co-resident limit of the cooperative group-row kernel is only known on the device:
-// shrink the grid to it (whole groups) and recompute the coarsening.
+// The group-row kernel's grid stays within what the device runs at once (whole groups), so
+// that every member finds a slot while the others wait for it (its launches are also ordered
+// per device). That limit is only known on the device: shrink the model's grid to it and
+// recompute the coarsening; a forced grid beyond it is refused.
 xtvxy_status fit_group_grid(int64_t m, int64_t n, int64_t ldx, const xtvxy_device_info& d,
                             xtvxy_launch_params* plan, bool forced, int elem_bytes = 4) {
   if (plan->kernel != XTVXY_DENSE_GROUP_ROWS) return XTVXY_SUCCESS;

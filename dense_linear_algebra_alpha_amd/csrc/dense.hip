@@ -17,12 +17,14 @@
 //              and permlane-swap lane exchanges (no LDS round trips).
 //   block rows (n <= 8192): the 256 threads of a workgroup share a row; the dot
 //              is reduced across the four wavefronts through LDS.
-//   group rows (wider):     `group` co-resident workgroups split a row into
-//              column slices. Each member publishes its slice dots in 64-bit
-//              slots that carry the value and the step number together, so a
-//              reader needs no fence: it waits until a slot shows the step it
-//              expects. Cooperative launch guarantees that the members are
-//              resident together; a bounded wait flags an error instead of hanging.
+//   group rows (wider):     `group` workgroups split a row into column
+//              slices. Each member publishes its slice dots in 64-bit slots
+//              that carry the value and the step number together, so a reader
+//              needs no fence: it waits until a slot shows the step it expects.
+//              The grid never exceeds what the device holds at once and the
+//              library runs group-row launches of a device one after another,
+//              so every member gets a slot; a bounded wait flags an error
+//              instead of hanging, and a member whose wait gave up waits no more.
 //
 // X is fp32, or bf16 (reduced-precision storage: each element widened to fp32 as it is
 // loaded, all arithmetic fp32). A chunk is VEC consecutive elements read by one load: 4 fp32 or
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 
   int parity = 0;
   uint32_t step = 0;
+  bool gave_up = false;
   for (int64_t base = r0; base < r1; base += R) {
     if constexpr (!kPrefetch) {
 #pragma unroll
@@ -267,10 +270,11 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
         const int c = threadIdx.x / R, r = threadIdx.x % R;
         uint64_t w = __hip_atomic_load(sl + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
-        const uint32_t limit = a.wait_polls ? a.wait_polls : kSpinLimit;
+        const uint32_t limit = gave_up ? 0u : a.wait_polls ? a.wait_polls : kSpinLimit;
         const uint32_t want = tag + a.wait_tag_skew;  // skew 0 except under the failure-path test hook
         while ((uint32_t)(w >> 32) != want) {
           if (++spins > limit) {
+            gave_up = true;  // the result is flagged as failed: later steps do not wait again
             __hip_atomic_store(a.error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
           }
@@ -417,6 +421,43 @@ int resident_per_cu(const void* k, int* cus) {
   return per_cu;
 }
 
+// Group-row launches of one device run one after another, whatever their streams: each waits
+// for the previous one to finish, so two grids that each fit the device never hold the slots
+// the other's members need. A stream under graph capture keeps the graph's own order.
+std::mutex g_group_mutex;
+struct GroupLast {
+  hipEvent_t done = nullptr;     // recorded after the device's latest group-row launch
+  hipStream_t stream = nullptr;  // the stream it was recorded on
+};
+std::map<int, GroupLast> g_group_last;
+
+hipError_t launch_group_ordered(const void* k, unsigned grid, void** params, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(s, &capture);
+  if (e != hipSuccess) return e;
+  if (capture != hipStreamCaptureStatusNone) return hipLaunchKernel(k, dim3(grid), dim3(kBlock), params, 0, s);
+  std::lock_guard<std::mutex> lock(g_group_mutex);
+  GroupLast& last = g_group_last[dev];
+  if (!last.done) {
+    e = hipEventCreateWithFlags(&last.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      last.done = nullptr;
+      return e;
+    }
+  } else if (last.stream != s) {  // on the same stream, stream order already serialises them
+    e = hipStreamWaitEvent(s, last.done, 0);
+    if (e != hipSuccess) return e;
+  }
+  e = hipLaunchKernel(k, dim3(grid), dim3(kBlock), params, 0, s);
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(last.done, s);
+  last.stream = e == hipSuccess ? s : nullptr;
+  return e;
+}
+
 }  // namespace
 
 int dense_resident_per_cu(const xtvxy_launch_params& p, int elem_bytes) {
@@ -454,7 +495,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;
       void* params[] = {&args};
-      return hipLaunchCooperativeKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
+      return launch_group_ordered(k, (unsigned)p.grid, params, s);
     }
   }
   return hipErrorInvalidValue;

@@ -80,7 +80,7 @@ xtvxy_status xtvxy_get_device_info(int device, xtvxy_device_info *info);
 enum {
   XTVXY_DENSE_WAVE_ROWS = 1,  /* rows of <= 1024 columns: lane groups within a wavefront own a row */
   XTVXY_DENSE_BLOCK_ROWS = 2, /* rows of <= 8192 columns: one workgroup owns a row */
-  XTVXY_DENSE_GROUP_ROWS = 3  /* wider rows: `group` co-resident workgroups split a row by columns */
+  XTVXY_DENSE_GROUP_ROWS = 3  /* wider rows: `group` workgroups split a row by columns */
 };
 /* CSR kernel: tiles of whole rows; output columns [0, lds_window) accumulate in
  * LDS. The other ("cold") columns either go to a global fp32 accumulator with
@@ -166,9 +166,11 @@ xtvxy_status xtvxy_dense_f32_workspace_size(int64_t m, int64_t n, int64_t ldx, s
 xtvxy_status xtvxy_dense_f32(int64_t m, int64_t n, float alpha, const float *X, int64_t ldx,
                              const float *v, const float *y, float beta, const float *z, float *out,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
-/* (Plans of the group-row kernel: if a member's bounded wait for the others gives up, which the
- * cooperative launch's co-residency rules out in normal operation, every element of out is NaN;
- * see xtvxy_test_group_wait.) */
+/* (Plans of the group-row kernel: its grid never exceeds what the device holds at once, and its
+ * launches on one device run one after another whatever their streams (each waits for the
+ * previous one; not under graph capture), so every member of a group gets a slot. If a member's
+ * bounded wait for the others still gives up, every element of out is NaN; see
+ * xtvxy_test_group_wait.) */
 
 /* As xtvxy_dense_f32 with the launch parameters forced (NULL = model). The
  * workspace must hold force->workspace_bytes as returned by xtvxy_dense_f32_plan
@@ -337,7 +339,7 @@ xtvxy_status xtvxy_set_kernel_timing_events(hipEvent_t before_main, hipEvent_t a
 
 /* Test hook of the dense group-row kernel's failure path, per calling thread. The members of a
  * group (XTVXY_DENSE_GROUP_ROWS) wait for each other's partial dot products with a bounded wait;
- * when a wait gives up (which the cooperative launch's co-residency normally rules out), the call
+ * when a wait gives up (which does not happen in normal operation), the call
  * completes and every element of `out` is NaN. With `polls` > 0 each wait gives up after that
  * many polls; with `unanswered` nonzero the waits look for a step tag no member publishes, so
  * every wait gives up and the result must be all NaN (0, 0 restores normal operation). For tests

@@ -218,6 +218,29 @@ def test_group_wait_failure_is_visible():
     assert_parity(d.run(plan=plan), ref, bnd, "after the forced failure")
 
 
+def test_group_rows_on_two_streams_at_once():
+    # Two group-row calls on two streams with nothing ordering them, each grid as large as the
+    # device holds: the library runs group-row launches of a device one after another, so every
+    # member of each call finds a slot and both results are correct.
+    import torch
+    m, n = 1024, 40000
+    probs = [datagen.dense_problem(m, n, seed=s) for s in (44, 45)]
+    refs = [dense_oracle(p) for p in probs]
+    ds = [DenseOnDevice(p) for p in probs]
+    plan = xt.xtvxy_dense_f32_plan(m, n, n, 1)
+    assert plan.kernel == xt.XTVXY_DENSE_GROUP_ROWS
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    note("group rows on two streams, plan %s" % plan.as_dict())
+    outs = []
+    for _ in range(3):
+        for p, d, s in zip(probs, ds, streams):
+            outs.append(xt.dense(d.X, d.y, d.v, d.z, p.alpha, p.beta, m=m, n=n, ldx=n, stream=s))
+    torch.cuda.synchronize()
+    for k, o in enumerate(outs):
+        ref, bnd = refs[k % 2]
+        assert_parity(o.cpu().numpy(), ref, bnd, "stream %d, call %d" % (k % 2, k // 2))
+
+
 def test_helpers_on_a_non_current_stream():
     # the tensor helpers allocate their workspace (and out) on the current stream and launch on
     # the caller's: the allocations are recorded on that stream, so the caching allocator cannot
