@@ -252,7 +252,7 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
   if (plan.workspace_bytes > 0 && (!ws || ws_bytes < (size_t)plan.workspace_bytes)) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
 
-  const DenseWorkspace w = dense_workspace(n, plan);
+  const DenseWorkspace w = dense_workspace(n, plan, elem_bytes);
   char* base = static_cast<char*>(ws);
   DenseArgs a{};
   a.m = m;

@@ -18,7 +18,8 @@
 //   block rows (n <= 8192): the 256 threads of a workgroup share a row; the dot
 //              is reduced across the four wavefronts through LDS.
 //   group rows (wider):     `group` workgroups split a row into column
-//              slices. Each member publishes its slice dots in 64-bit slots
+//              slices (fp32: each thread's column sums in LDS, 4 rows of 8
+//              chunks per exchange). Each member publishes its slice dots in 64-bit slots
 //              that carry the value and the step number together, so a reader
 //              needs no fence: it waits until a slot shows the step it expects.
 //              The grid never exceeds what the device holds at once and the
@@ -160,10 +161,14 @@ __device__ __forceinline__ uint64_t pack_slot(float v, uint32_t tag) {
 
 template <class E, int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
-  constexpr int R = GROUP ? group_rows_per_step(NCH) : kBlockRowsInFlight;
-  constexpr int kMaxGroup = kBlock / R;
+  constexpr int R = GROUP ? group_rows_per_step(NCH, VEC, (int)sizeof(E)) : kBlockRowsInFlight;
+  constexpr int kMaxGroup = kGroupMaxMembers;
+  // fp32 group rows keep each thread's column sums in LDS, in words no other thread touches (so
+  // no barrier guards them); the registers they free hold more rows per exchange of dots.
+  constexpr bool kSumsInLds = GROUP && sizeof(E) == 4;
   __shared__ float red[2][R][kWaves];
   __shared__ float gx[GROUP ? R : 1][GROUP ? kMaxGroup : 1];
+  __shared__ __align__(16) float acc_s[kSumsInLds ? NCH * kBlock * VEC : 1];  // [chunk][thread][VEC]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t n = a.n;
   const int gsz = GROUP ? a.group : 1;
@@ -173,7 +178,8 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   const int64_t r0 = unit * a.rows_per_unit;
   const int64_t r1 = min(a.m, r0 + a.rows_per_unit);
 
-  float yv[NCH][VEC], acc[NCH][VEC];
+  float yv[NCH][VEC], acc[kSumsInLds ? 1 : NCH][VEC];
+  auto acc_word = [&](int c, int k) -> float& { return acc_s[(c * kBlock + (int)threadIdx.x) * VEC + k]; };
   bool cok[NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
@@ -182,7 +188,11 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
       yv[c][k] = (col0 + k < n) ? a.y[col0 + k] : 0.0f;
-      acc[c][k] = 0.0f;
+      if constexpr (kSumsInLds) {
+        acc_word(c, k) = 0.0f;
+      } else {
+        acc[c][k] = 0.0f;
+      }
     }
   }
   uint64_t* slots = GROUP ? reinterpret_cast<uint64_t*>(a.xchg) + unit * 2 * gsz * R : nullptr;
@@ -266,8 +276,8 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
         __hip_atomic_store(sl + member * R + threadIdx.x, pack_slot(mine, tag), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (threadIdx.x < gsz * R) {
-        const int c = threadIdx.x / R, r = threadIdx.x % R;
+      for (int j = threadIdx.x; j < gsz * R; j += kBlock) {  // every member's dot of every row
+        const int c = j / R, r = j % R;
         uint64_t w = __hip_atomic_load(sl + c * R + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         uint32_t spins = 0;
         const uint32_t limit = gave_up ? 0u : a.wait_polls ? a.wait_polls : kSpinLimit;
@@ -292,16 +302,31 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
       }
       ++step;
     }
+    float uu[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t row = base + r;
       const bool rok = row < r1;
       const float vv = a.v ? (rok ? a.v[row] : 0.0f) : 1.0f;
-      const float uu = rok ? vv * t[r] : 0.0f;
+      uu[r] = rok ? vv * t[r] : 0.0f;
+    }
+    if constexpr (kSumsInLds) {  // one read and one write of each sum per step, rows in order
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
-        for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu, xv[r][c].get(k), acc[c][k]);
+        for (int k = 0; k < VEC; ++k) {
+          float s_ck = acc_word(c, k);
+#pragma unroll
+          for (int r = 0; r < R; ++r) s_ck = fmaf(uu[r], xv[r][c].get(k), s_ck);
+          acc_word(c, k) = s_ck;
+        }
+    } else {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c)
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) acc[c][k] = fmaf(uu[r], xv[r][c].get(k), acc[c][k]);
     }
     if constexpr (kPrefetch) {
 #pragma unroll
@@ -318,7 +343,11 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
       const int64_t col = c0 + ((int64_t)c * kBlock + threadIdx.x) * VEC + k;
-      if (col < n) dst[col] = acc[c][k];
+      if constexpr (kSumsInLds) {
+        if (col < n) dst[col] = acc_word(c, k);
+      } else {
+        if (col < n) dst[col] = acc[c][k];
+      }
     }
 }
 
@@ -490,7 +519,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
       return hipLaunchKernel(k, dim3((unsigned)p.grid), dim3(kBlock), params, 0, s);
     }
     case XTVXY_DENSE_GROUP_ROWS: {
-      if (p.group < 1 || p.group > kBlock / group_rows_per_step(p.chunks)) return hipErrorInvalidValue;
+      if (p.group < 1 || p.group > kGroupMaxMembers) return hipErrorInvalidValue;
       const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, true);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;

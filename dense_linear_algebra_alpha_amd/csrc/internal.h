@@ -15,10 +15,19 @@ namespace xtvxy {
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row workgroup loads per step
-// Rows a group-row workgroup loads per step: 16 / chunks, so that a step always holds 16 chunks
-// per thread (the registers of 2 rows of 8 chunks) and fewer chunks per thread (wider groups)
-// buy more rows per exchange of partial dots between the members.
-constexpr int group_rows_per_step(int chunks) { return chunks >= 1 && chunks <= 16 ? 16 / chunks : 1; }
+// Rows a group-row workgroup loads per step, i.e. per exchange of partial dots between the
+// members. fp32 keeps each thread's column sums in LDS, so a step's rows may take 128 registers
+// (4 rows of 8 chunks of 4 floats, at most 16 rows); bf16 keeps its sums in registers and a step
+// holds 16 packed chunks per thread (4 rows of 4 chunks). Fewer chunks per thread (wider groups)
+// buy more rows per exchange.
+// Members of a group-row group at most: 128 x 8192 = 1,048,576 columns with 16-byte loads.
+constexpr int kGroupMaxMembers = 128;
+constexpr int group_rows_per_step(int chunks, int vec, int elem_bytes) {
+  if (chunks < 1 || chunks > 16) return 1;
+  if (elem_bytes == 2) return 16 / chunks;
+  const int words = chunks * (vec > 0 ? vec : 1);  // fp32: one register per element
+  return words >= 128 ? 1 : (128 / words > 16 ? 16 : 128 / words);
+}
 // CSR kernel: LDS besides the output and y windows, for workgroups of `blk` threads holding
 // `ept` entries each: row_ptr, v and dots of two tiles, a sink word per thread and small
 // scalars (29 blk + 64 bytes), plus two tiles of 16-bit row-start marks (4 blk ept bytes)
@@ -280,7 +289,7 @@ struct DenseWorkspace {
   size_t xchg_off, error_off;  // group-row path only
   size_t total;
 };
-DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p);
+DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p, int elem_bytes);
 
 struct CsrWorkspace {
   size_t partial_off, partial_rows;  // [grid][lds_window]

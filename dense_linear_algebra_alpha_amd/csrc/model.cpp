@@ -65,7 +65,7 @@ int wave_unroll(int chunks) { return 8 / chunks; }
 
 }  // namespace
 
-DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
+DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p, int elem_bytes) {
   DenseWorkspace w{};
   if (p.kernel == XTVXY_DENSE_GROUP_ROWS) {
     const int64_t groups = p.grid / std::max<int32_t>(p.group, 1);
@@ -73,7 +73,8 @@ DenseWorkspace dense_workspace(int64_t n, const xtvxy_launch_params& p) {
     w.partial_off = 0;
     w.xchg_off = align_up(w.partial_off + (size_t)groups * n * sizeof(float));
     w.error_off =
-        align_up(w.xchg_off + (size_t)groups * 2 * p.group * group_rows_per_step(p.chunks) * sizeof(uint64_t));
+        align_up(w.xchg_off + (size_t)groups * 2 * p.group * group_rows_per_step(p.chunks, p.vec, elem_bytes) *
+                                  sizeof(uint64_t));
     w.total = align_up(w.error_off + sizeof(uint32_t));
   } else {
     w.partial_rows = (size_t)p.grid;
@@ -159,7 +160,7 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
         p->group = 1;
         if (slice < n) return XTVXY_ERROR_INVALID_VALUE;
       } else {
-        if (p->group < 1 || p->group > kBlock / group_rows_per_step(p->chunks) || (int64_t)p->group * slice < n ||
+        if (p->group < 1 || p->group > kGroupMaxMembers || (int64_t)p->group * slice < n ||
             p->grid % p->group != 0)
           return XTVXY_ERROR_INVALID_VALUE;
       }
@@ -172,7 +173,7 @@ xtvxy_status complete_dense(int64_t m, int64_t n, int64_t ldx, const xtvxy_devic
   const int64_t units = p->grid / p->group;
   if (p->rows_per_unit <= 0) p->rows_per_unit = std::max<int64_t>(1, ceil_div(m, units));
   if (p->rows_per_unit * units < m) return XTVXY_ERROR_INVALID_VALUE;
-  p->workspace_bytes = (int64_t)dense_workspace(n, *p).total;
+  p->workspace_bytes = (int64_t)dense_workspace(n, *p, elem_bytes).total;
   (void)d;
   return XTVXY_SUCCESS;
 }
@@ -210,7 +211,7 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
     const int64_t slice = ceil_div(n, p->group);
     p->chunks = (slice <= per) ? 1 : (slice <= 2 * per) ? 2 : (slice <= 4 * per) ? 4 : 8;
     p->lanes_per_row = kBlock;
-    rows_per_step = group_rows_per_step(p->chunks);
+    rows_per_step = group_rows_per_step(p->chunks, p->vec, elem_bytes);
     inflight_per_wg = (double)rows_per_step * slice * elem_bytes;
   }
 
@@ -235,7 +236,11 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
     const double bw = bandwidth(d, std::max(resident_per_cu, 1.0 / d.compute_units) * inflight_per_wg, latency);
     const double partial_bytes = 2.0 * (double)(grid / p->group) * n * sizeof(float);
     const double t = io_bytes / bw + partial_bytes / (kSustained * d.hbm_bytes_per_s) + 2 * kLaunch;
-    if (t < best * 0.999) {
+    // The group-row kernel takes as many workgroups per CU as reside (at most two), whatever the
+    // cost says: its members wait for each other's dots with nothing in flight, which the cost
+    // does not see, and a second workgroup streams meanwhile (8192 x 65536: one per CU 40% slower).
+    const bool group_more = p->kernel == XTVXY_DENSE_GROUP_ROWS;
+    if (t < best * 0.999 || group_more) {
       best = t;
       best_grid = grid;
     }

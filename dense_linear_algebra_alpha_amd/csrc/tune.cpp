@@ -111,7 +111,7 @@ std::vector<xtvxy_launch_params> dense_candidates(int64_t m, int64_t n, int64_t 
     for (int chunks : {1, 2, 4, 8}) {
       const int64_t g0 = ceil_div(n, (int64_t)kBlock * vec * chunks);
       for (int64_t g : {g0, 2 * g0}) {
-        if (g < 2 || g > kBlock / group_rows_per_step(chunks)) continue;
+        if (g < 2 || g > kGroupMaxMembers) continue;
         for (int k : {1, 2}) {
           xtvxy_launch_params p{};
           p.kernel = XTVXY_DENSE_GROUP_ROWS;
