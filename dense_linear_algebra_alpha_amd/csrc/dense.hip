@@ -161,11 +161,12 @@ __device__ __forceinline__ uint64_t pack_slot(float v, uint32_t tag) {
 
 template <class E, int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
-  constexpr int R = GROUP ? group_rows_per_step(NCH, VEC, (int)sizeof(E)) : kBlockRowsInFlight;
+  constexpr int R = GROUP ? group_rows_per_step(NCH, VEC, (int)sizeof(E)) : block_rows_per_step(NCH, VEC, (int)sizeof(E));
   constexpr int kMaxGroup = kGroupMaxMembers;
-  // fp32 group rows keep each thread's column sums in LDS, in words no other thread touches (so
-  // no barrier guards them); the registers they free hold more rows per exchange of dots.
-  constexpr bool kSumsInLds = GROUP && sizeof(E) == 4;
+  // fp32 group rows (and fp32 block rows of 8 chunks of 4) keep each thread's column sums in LDS,
+  // in words no other thread touches (so no barrier guards them); the registers they free hold
+  // more rows per exchange of dots (per barrier, for block rows).
+  constexpr bool kSumsInLds = (GROUP && sizeof(E) == 4) || (!GROUP && block_sums_in_lds(NCH, VEC, (int)sizeof(E)));
   __shared__ float red[2][R][kWaves];
   __shared__ float gx[GROUP ? R : 1][GROUP ? kMaxGroup : 1];
   __shared__ __align__(16) float acc_s[kSumsInLds ? NCH * kBlock * VEC : 1];  // [chunk][thread][VEC]

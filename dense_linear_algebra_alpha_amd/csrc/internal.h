@@ -14,7 +14,7 @@ namespace xtvxy {
 
 constexpr int kBlock = 256;          // threads per workgroup of every fused kernel
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
-constexpr int kBlockRowsInFlight = 2;  // rows a block-row workgroup loads per step
+constexpr int kBlockRowsInFlight = 2;  // rows a block-row workgroup loads per step (but see below)
 // Rows a group-row workgroup loads per step, i.e. per exchange of partial dots between the
 // members. fp32 keeps each thread's column sums in LDS, so a step's rows may take 128 registers
 // (4 rows of 8 chunks of 4 floats, at most 16 rows); bf16 keeps its sums in registers and a step
@@ -27,6 +27,16 @@ constexpr int group_rows_per_step(int chunks, int vec, int elem_bytes) {
   if (elem_bytes == 2) return 16 / chunks;
   const int words = chunks * (vec > 0 ? vec : 1);  // fp32: one register per element
   return words >= 128 ? 1 : (128 / words > 16 ? 16 : 128 / words);
+}
+// fp32 block rows of 8 chunks of 4 (too many registers for the next step's rows to be requested
+// early) keep their column sums in LDS like the group rows and take as many rows per step
+// (4 instead of 2); every other block-row layout takes kBlockRowsInFlight rows and its prefetch.
+constexpr bool block_sums_in_lds(int chunks, int vec, int elem_bytes) {
+  return elem_bytes == 4 && vec == 4 && chunks == 8;
+}
+constexpr int block_rows_per_step(int chunks, int vec, int elem_bytes) {
+  return block_sums_in_lds(chunks, vec, elem_bytes) ? group_rows_per_step(chunks, vec, elem_bytes)
+                                                     : kBlockRowsInFlight;
 }
 // CSR kernel: LDS besides the output and y windows, for workgroups of `blk` threads holding
 // `ept` entries each: row_ptr, v and dots of two tiles, a sink word per thread and small

@@ -202,8 +202,8 @@ xtvxy_status model_dense(int64_t m, int64_t n, int64_t ldx, bool aligned16, cons
     p->chunks = (n <= per) ? 1 : (n <= 2 * per) ? 2 : (n <= 4 * per) ? 4 : 8;
     p->group = 1;
     p->lanes_per_row = kBlock;
-    rows_per_step = kBlockRowsInFlight;
-    inflight_per_wg = (double)kBlockRowsInFlight * n * elem_bytes;
+    rows_per_step = block_rows_per_step(p->chunks, vec, elem_bytes);
+    inflight_per_wg = (double)rows_per_step * n * elem_bytes;
   } else {
     p->kernel = XTVXY_DENSE_GROUP_ROWS;
     const int64_t per = (int64_t)kBlock * vec;
