@@ -49,7 +49,8 @@ HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E peak
 
 def algorithmic_bytes(p) -> int:
     if hasattr(p, "col_idx"):
-        b = 8 * p.nnz + 4 * (p.m + 1) + 4 * p.n + 4 * p.n
+        vb = 2 if getattr(p, "values_dtype", "f32") == "bf16" else 4  # bf16 values: 2 bytes each
+        b = (vb + 4) * p.nnz + 4 * (p.m + 1) + 4 * p.n + 4 * p.n
         b += 4 * p.m if p.v is not None else 0
     else:
         xb = 2 if getattr(p, "x_dtype", "f32") == "bf16" else 4  # bf16 storage of X: 2 bytes per element
@@ -147,11 +148,12 @@ def cpu_baseline(p, budget_s: float, threads=None, min_runs=3):
     import oracle
     threads = oracle.set_threads(threads or len(os.sched_getaffinity(0)))
     runs = []
+    vals = p.values_f32() if hasattr(p, "col_idx") else None  # bf16 values widened (exactly) once
     t_end = time.perf_counter() + budget_s
     while len(runs) < min_runs or (time.perf_counter() < t_end and len(runs) < 200):
         t0 = time.perf_counter()
         if hasattr(p, "col_idx"):
-            oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+            oracle.csr(p.row_ptr, p.col_idx, vals, p.n, p.y, p.v, p.z, p.alpha, p.beta)
         else:
             oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
         runs.append(time.perf_counter() - t0)
@@ -406,6 +408,8 @@ def report_tuning(args, p, kind, abytes, env):
                                       xt._ptr(z), out.data_ptr(), args.tune_repeats, sh)
     else:
         rp, ci, vals = env["rp"], env["ci"], env["vals"]
+        if env.get("bf16"):
+            raise SystemExit("the CSR tuner takes fp32 values")
         rep = xt.xtvxy_csr_f32_tune(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
                                     xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
                                     args.tune_repeats, sh)
@@ -451,7 +455,8 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
     out = torch.empty(p.n, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream or None
-    bf16 = getattr(p, "x_dtype", "f32") == "bf16"
+    # bf16 storage: of X (dense) or of the values (CSR)
+    bf16 = getattr(p, "x_dtype", "f32") == "bf16" or getattr(p, "values_dtype", "f32") == "bf16"
     plan_text = args.plan if headline else None
     with_unfused = unfused_calls > 0 and not args.fused_only
     if kind == "dense":
@@ -529,39 +534,47 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
             ws_bytes = plan.workspace_bytes if forced else xt.xtvxy_csr_f32_workspace_size(p.m, p.n, p.nnz)
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uplan = uplan_t = None
+        # bf16 values: the comparison is the fp32 fused path (same entry point) on the widened values
+        vals32 = t(p.values_f32()) if bf16 and with_unfused else vals
+
+        def fused_call(vt, bf):
+            if analysed:
+                (xt.xtvxy_csr_bf16_analysed_ex if bf else xt.xtvxy_csr_f32_analysed_ex)(
+                    analysis.handle, p.alpha, vt.data_ptr(), xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
+                    out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan if forced else None)
+            elif forced:
+                (xt.xtvxy_csr_bf16_ex if bf else xt.xtvxy_csr_f32_ex)(
+                    p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vt.data_ptr(), xt._ptr(v), y.data_ptr(),
+                    p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh, plan)
+            else:
+                (xt.xtvxy_csr_bf16 if bf else xt.xtvxy_csr_f32)(
+                    p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vt.data_ptr(), xt._ptr(v), y.data_ptr(),
+                    p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh)
 
         def fused():
-            if analysed:
-                xt.xtvxy_csr_f32_analysed_ex(analysis.handle, p.alpha, vals.data_ptr(), xt._ptr(v), y.data_ptr(),
-                                             p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(), ws_bytes, sh,
-                                             plan if forced else None)
-            elif forced:
-                xt.xtvxy_csr_f32_ex(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
-                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
-                                    ws_bytes, sh, plan)
-            else:
-                xt.xtvxy_csr_f32(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
-                                 xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), ws.data_ptr(),
-                                 ws_bytes, sh)
+            fused_call(vals, bf16)
 
         def unfused():
+            if bf16:
+                fused_call(vals32, False)
+                return
             xt.xtvxy_csr_f32_unfused_reference(uplan.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
                                                out.data_ptr(), sh)
 
         def unfused_explicit():
             xt.xtvxy_csr_f32_unfused_reference(uplan_t.handle, p.alpha, xt._ptr(v), y.data_ptr(), p.beta,
                                                xt._ptr(z), out.data_ptr(), sh)
-        if with_unfused and not args.tune:
+        if with_unfused and not args.tune and not bf16:
             # structure analysis and the transposed copy: outside every timed region
             uplan = xt.CsrUnfusedPlan(rp, ci, vals, p.n)
             uplan_t = xt.CsrUnfusedPlan(rp, ci, vals, p.n, explicit_transpose=True)
         else:
             unfused_explicit = None
-        shape = {"m": p.m, "n": p.n, "nnz": p.nnz, "entry_point": "xtvxy_csr_f32_analysed" if analysed
-                 else "xtvxy_csr_f32"}
+        entry = ("xtvxy_csr_bf16" if bf16 else "xtvxy_csr_f32") + ("_analysed" if analysed else "")
+        shape = {"m": p.m, "n": p.n, "nnz": p.nnz, "entry_point": entry, "values_storage": "bf16" if bf16 else "f32"}
         if analysed:
             shape["analysis_seconds"] = round(analysis_s, 4)
-        env = {"rp": rp, "ci": ci, "vals": vals, "y": y, "v": v, "z": z, "out": out, "sh": sh}
+        env = {"rp": rp, "ci": ci, "vals": vals, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
 
     abytes = algorithmic_bytes(p)
     if args.tune:
@@ -629,7 +642,7 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
                   "call_frac_of_ceiling": (round(abytes / step_s / 1e9 / ctx["ceiling_gbs"], 4)
                                            if ctx["ceiling_gbs"] else None)},
     }
-    if unfused_s is not None and bf16:  # the comparison is the fp32 fused path on the widened X
+    if unfused_s is not None and bf16:  # the comparison is the fp32 fused path on the widened X or values
         rec["f32_fused_ms_per_step"] = round(unfused_s * 1e3, 5)
         rec["speedup_vs_f32_fused"] = round(unfused_s / step_s, 3)
     elif unfused_s is not None:
@@ -647,8 +660,9 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
             ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
             bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
         else:
-            ref = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
-            bnd = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
+            vals64 = p.values_f32()  # bf16 values widened exactly
+            ref = oracle.csr(p.row_ptr, p.col_idx, vals64, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+            bnd = oracle.csr(p.row_ptr, p.col_idx, vals64, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
         den = np.where(bnd > 0, bnd, 1.0)
         rec["max_rel_err"] = float(np.max(np.abs(fused_out.astype(np.float64) - ref) / den))
         if unfused_s is not None:

@@ -147,7 +147,8 @@ class DenseProblem:
 
 @dataclass
 class CsrProblem:
-    """CSR X (zero-based int32 row_ptr[m+1], col_idx[nnz], fp32 values[nnz]) and vectors."""
+    """CSR X (zero-based int32 row_ptr[m+1], col_idx[nnz], values[nnz]) and vectors. values are
+    fp32, or with values_dtype "bf16" uint16 bf16 bit patterns."""
     m: int
     n: int
     row_ptr: np.ndarray
@@ -160,10 +161,21 @@ class CsrProblem:
     beta: float
     name: str = ""
     info: dict = field(default_factory=dict)
+    values_dtype: str = "f32"     # "f32" or "bf16"
 
     @property
     def nnz(self) -> int:
         return int(self.col_idx.shape[0])
+
+    def values_f32(self) -> np.ndarray:
+        """The values as the fp32 numbers they denote (bf16 widened exactly)."""
+        return bf16_to_f32(self.values) if self.values_dtype == "bf16" else self.values
+
+
+def csr_values_bf16(p: CsrProblem, name: str = "") -> CsrProblem:
+    """The same problem with its values rounded to bf16 (to_bf16) and stored as uint16 bit patterns."""
+    return CsrProblem(p.m, p.n, p.row_ptr, p.col_idx, to_bf16(p.values), p.y, p.v, p.z, p.alpha, p.beta,
+                      name or p.name + "_bf16", dict(p.info), "bf16")
 
 
 def dense_problem(m, n, seed=0, *, x="uniform", y="uniform", v="uniform", z="uniform", alpha=1.5,
@@ -356,4 +368,13 @@ WORKLOADS = {
         m, n, seed, s_row=1.5, max_row=2726, s_col=1.2, permute_columns=True,
         values="uniform", y="uniform", v="uniform", z="uniform", alpha=0.7, beta=0.3,
         name="csr_5000000x1000000_zipf_permuted"),
+    # the two CSR workloads with their values stored as bf16 (rounded to nearest even from the fp32
+    # draw); the structure stays int32
+    "csr_10000000x1000_logistic_hvp_bf16": lambda seed=0, m=10_000_000, n=1000: csr_values_bf16(csr_bernoulli(
+        m, n, 0.01, seed, values="normal", y="normal", v="logistic", z=None, alpha=1.0, beta=0.0,
+        name="csr_10000000x1000_logistic_hvp"), "csr_10000000x1000_logistic_hvp_bf16"),
+    "csr_5000000x1000000_zipf_bf16": lambda seed=0, m=5_000_000, n=1_000_000: csr_values_bf16(csr_zipf(
+        m, n, seed, s_row=1.5, max_row=2726, s_col=1.2, permute_columns=False,
+        values="uniform", y="uniform", v="uniform", z="uniform", alpha=0.7, beta=0.3,
+        name="csr_5000000x1000000_zipf"), "csr_5000000x1000000_zipf_bf16"),
 }

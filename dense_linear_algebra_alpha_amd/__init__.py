@@ -46,7 +46,8 @@ __all__ = [
     "xtvxy_dense_bf16", "xtvxy_dense_bf16_ex", "xtvxy_dense_bf16_tune",
     "xtvxy_csr_f32_analyse", "xtvxy_csr_f32_analysis_destroy", "xtvxy_csr_f32_analysed_plan",
     "xtvxy_csr_f32_analysed_plan_complete", "xtvxy_csr_f32_analysed_workspace_size", "xtvxy_csr_f32_analysed",
-    "xtvxy_csr_f32_analysed_ex", "CsrAnalysis",
+    "xtvxy_csr_f32_analysed_ex", "CsrAnalysis", "xtvxy_csr_bf16", "xtvxy_csr_bf16_ex", "xtvxy_csr_bf16_analysed",
+    "xtvxy_csr_bf16_analysed_ex",
 ]
 
 load = _abi.load
@@ -189,6 +190,18 @@ def xtvxy_csr_f32_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, 
                      workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
 
 
+def xtvxy_csr_bf16(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                   stream):
+    return _abi.call("xtvxy_csr_bf16", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_bf16_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                      stream, force):
+    return _abi.call("xtvxy_csr_bf16_ex", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out,
+                     workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
 def xtvxy_csr_f32_rowdot(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream):
     return _abi.call("xtvxy_csr_f32_rowdot", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream)
 
@@ -245,6 +258,17 @@ def xtvxy_csr_f32_analysed(analysis, alpha, values, v, y, beta, z, out, workspac
 def xtvxy_csr_f32_analysed_ex(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream,
                               force):
     return _abi.call("xtvxy_csr_f32_analysed_ex", analysis, alpha, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_bf16_analysed(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream):
+    return _abi.call("xtvxy_csr_bf16_analysed", analysis, alpha, values, v, y, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_bf16_analysed_ex(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream,
+                               force):
+    return _abi.call("xtvxy_csr_bf16_analysed_ex", analysis, alpha, values, v, y, beta, z, out, workspace,
                      workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
 
 
@@ -447,13 +471,15 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
 
 def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None,
         workspace=None, stream=None):
-    """The same pattern for CSR X given as int32 row_ptr / col_idx and float32 values tensors."""
+    """The same pattern for CSR X given as int32 row_ptr / col_idx and float32 values tensors; bf16
+    values (torch.bfloat16, or uint16 bit patterns) take the xtvxy_csr_bf16 entry points."""
     torch = _torch()
     m = row_ptr.numel() - 1
     nnz = col_idx.numel()
     device = row_ptr.device
+    bf16 = values.dtype in (torch.bfloat16, torch.uint16)
     for name, t, dt in (("row_ptr", row_ptr, torch.int32), ("col_idx", col_idx, torch.int32),
-                        ("values", values, torch.float32)):
+                        ("values", values, values.dtype if bf16 else torch.float32)):
         if t.dtype != dt or t.device != device or not t.is_contiguous():
             raise ValueError("%s must be a contiguous %s tensor on %s" % (name, dt, device))
     if values.numel() != nnz:
@@ -474,9 +500,9 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
             _ptr(values) if nnz else None, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(), ws_ptr,
             ws_bytes, _stream_handle(stream))
     if plan is None:
-        xtvxy_csr_f32(*args)
+        (xtvxy_csr_bf16 if bf16 else xtvxy_csr_f32)(*args)
     else:
-        xtvxy_csr_f32_ex(*args, plan)
+        (xtvxy_csr_bf16_ex if bf16 else xtvxy_csr_f32_ex)(*args, plan)
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
@@ -635,8 +661,9 @@ class CsrAnalysis:
     def __call__(self, values, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None,
                  stream=None):
         torch = _torch()
-        if values.dtype != torch.float32 or values.numel() != self.nnz or not values.is_contiguous():
-            raise ValueError("values must be a contiguous float32 tensor of nnz elements")
+        bf16 = values.dtype in (torch.bfloat16, torch.uint16)
+        if (values.dtype != torch.float32 and not bf16) or values.numel() != self.nnz or not values.is_contiguous():
+            raise ValueError("values must be a contiguous float32 (or bf16) tensor of nnz elements")
         _check_vec("y", y, self.n, self.device)
         _check_vec("v", v, self.m, self.device, required=False)
         _check_vec("z", z, self.n, self.device, required=beta != 0)
@@ -652,9 +679,9 @@ class CsrAnalysis:
         args = (self.handle, float(alpha), _ptr(values) if self.nnz else None, _ptr(v), y.data_ptr(), float(beta),
                 _ptr(z), out.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream))
         if plan is None:
-            xtvxy_csr_f32_analysed(*args)
+            (xtvxy_csr_bf16_analysed if bf16 else xtvxy_csr_f32_analysed)(*args)
         else:
-            xtvxy_csr_f32_analysed_ex(*args, plan)
+            (xtvxy_csr_bf16_analysed_ex if bf16 else xtvxy_csr_f32_analysed_ex)(*args, plan)
         _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
         return out
 

@@ -117,7 +117,10 @@ SIGNATURES = {
                             _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_csr_f32": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_bf16": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                         _P(xtvxy_launch_params)],
+    "xtvxy_csr_bf16_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
                          _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_rowdot": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp],
     "xtvxy_csr_f32_rowdot_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
@@ -144,6 +147,8 @@ SIGNATURES = {
     "xtvxy_csr_f32_analysed_workspace_size": [_vp, _P(_sz)],
     "xtvxy_csr_f32_analysed": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_analysed_ex": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp, _P(xtvxy_launch_params)],
+    "xtvxy_csr_bf16_analysed": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_bf16_analysed_ex": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp, _P(xtvxy_launch_params)],
     "xtvxy_read_probe": [_vp, _sz, _i64, _vp, _vp],
     "xtvxy_scatter_probe": [_i32, _vp, _sz, ctypes.c_uint32, ctypes.c_uint32, _i32, _i64, _vp, _vp],
     "xtvxy_dense_f32_noalloc_max_workspace": [_P(_sz)],

@@ -101,8 +101,8 @@ xtvxy_status check_dense(int64_t m, int64_t n, float alpha, const void* X, int64
 }
 
 xtvxy_status check_csr(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                       const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
-                       const float* z, const float* out, bool* quick) {
+                       const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
+                       const float* z, const float* out, bool* quick, int value_bytes = 4) {
   *quick = false;
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
   if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
@@ -117,7 +117,7 @@ xtvxy_status check_csr(int64_t m, int64_t n, int64_t nnz, float alpha, const int
   const size_t nb = (size_t)n * sizeof(float);
   if (reads_x) {
     if (overlap(out, nb, row_ptr, (size_t)(m + 1) * 4) || overlap(out, nb, col_idx, (size_t)nnz * 4) ||
-        overlap(out, nb, values, (size_t)nnz * 4) || overlap(out, nb, y, nb) ||
+        overlap(out, nb, values, (size_t)nnz * (size_t)value_bytes) || overlap(out, nb, y, nb) ||
         (v && overlap(out, nb, v, (size_t)m * sizeof(float))))
       return XTVXY_ERROR_ALIASING;
   }
@@ -285,11 +285,13 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
 }
 
 // The fused kernel (mode kCsrFused, with v and y) or its second half alone (kCsrTmv, with u
-// passed as v and no y), then the bin passes and the aggregation, for checked arguments.
+// passed as v and no y), then the bin passes and the aggregation, for checked arguments. Values
+// are fp32 (value_bytes 4) or, for the fused pattern on the tile and wavefront kernels, bf16 (2).
 xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                     const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                     const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                     const xtvxy_launch_params* force, const CsrExtras* extras = nullptr) {
+                     const xtvxy_launch_params* force, const CsrExtras* extras = nullptr, int value_bytes = 4) {
+  if (value_bytes != 4 && (value_bytes != 2 || mode != kCsrFused)) return XTVXY_ERROR_INVALID_VALUE;
   xtvxy_device_info d;
   xtvxy_status st = device_info(-1, &d);
   if (st != XTVXY_SUCCESS) return st;
@@ -297,7 +299,8 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   st = csr_plan_for(m, n, nnz, d, force, &plan, mode == kCsrFused);
   if (st != XTVXY_SUCCESS) return st;
   // the row-class kernel runs on an analysis's work list, and on the whole pattern only
-  if (plan.kernel == XTVXY_CSR_ROWS && (extras == nullptr || extras->rows == nullptr || mode != kCsrFused))
+  if (plan.kernel == XTVXY_CSR_ROWS &&
+      (extras == nullptr || extras->rows == nullptr || mode != kCsrFused || value_bytes != 4))
     return XTVXY_ERROR_INVALID_VALUE;
   if (mode == kCsrTmv && plan.entries_per_thread != 8) return XTVXY_ERROR_INVALID_VALUE;
   if (mode == kCsrTmv && plan.y_window != 0) {  // no y to gather: the plan with no y window
@@ -315,6 +318,7 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.values = values;
+  a.value_bytes = value_bytes;
   a.v = v;
   a.y = y;
   char* base = static_cast<char*>(ws);
@@ -323,7 +327,9 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
   a.y_window = plan.y_window;
   const bool binned = w.bins > 0;
   a.acc = (plan.lds_window < n && !binned) ? reinterpret_cast<float*>(base + w.acc_off) : nullptr;
-  a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
+  // vector loads of 4 entries: 16 bytes of column indices and 4 * value_bytes of values
+  a.aligned = reinterpret_cast<uintptr_t>(values) % (uintptr_t)(4 * value_bytes) == 0 &&
+              reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
   if (extras) {
     a.rows = extras->rows;
     a.bounds = extras->bounds;
@@ -382,15 +388,15 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
 }
 
 xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                      const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                      const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
                       const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                      const xtvxy_launch_params* force) {
+                      const xtvxy_launch_params* force, int value_bytes = 4) {
   bool quick = false;
-  xtvxy_status st = check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick);
+  xtvxy_status st = check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick, value_bytes);
   if (st != XTVXY_SUCCESS) return st;
   if (quick) return n == 0 ? XTVXY_SUCCESS : launch_status(launch_beta_only(n, beta, z, out, stream));
   return csr_run(kCsrFused, m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, ws, ws_bytes, stream,
-                 force);
+                 force, nullptr, value_bytes);
 }
 
 // out = alpha X^T u + beta z (the second half of the pattern alone).
@@ -455,6 +461,7 @@ xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const i
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.values = values;
+  a.value_bytes = 4;
   a.v = v;
   a.y = y;
   a.lds_window = 0;
@@ -639,6 +646,22 @@ xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha, co
                   stream, force);
 }
 
+xtvxy_status xtvxy_csr_bf16(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                            const int32_t* col_idx, const uint16_t* values, const float* v, const float* y,
+                            float beta, const float* z, float* out, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                  stream, nullptr, 2);
+}
+
+xtvxy_status xtvxy_csr_bf16_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                               const int32_t* col_idx, const uint16_t* values, const float* v, const float* y,
+                               float beta, const float* z, float* out, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, const xtvxy_launch_params* force) {
+  return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
+                  stream, force, 2);
+}
+
 xtvxy_status xtvxy_csr_f32_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                                   const int32_t* col_idx, const float* values, const float* v, const float* y,
                                   float beta, const float* t0, float* t, hipStream_t stream) {
@@ -716,11 +739,11 @@ hipError_t allow_dynamic_lds(const void* fn) {
 
 namespace xtvxy {
 xtvxy_status csr_run_fused(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                           const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                           const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
                            const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                           const xtvxy_launch_params* force, const CsrExtras* extras) {
+                           const xtvxy_launch_params* force, const CsrExtras* extras, int value_bytes) {
   return csr_run(kCsrFused, m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, ws, ws_bytes, stream,
-                 force, extras);
+                 force, extras, value_bytes);
 }
 xtvxy_status current_device_info(xtvxy_device_info* d) { return device_info(-1, d); }
 hipError_t mark_before_main(hipStream_t s) {

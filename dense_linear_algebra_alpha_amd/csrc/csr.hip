@@ -71,7 +71,7 @@ struct TileRegs {
   float yv[K];  // y[col] of the entries (gathered one step ahead when y is read from global memory)
 };
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
+template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512, "workgroups of 256 or 512 threads");
   static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
@@ -258,14 +258,13 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
 #pragma unroll
       for (int k = 0; k < K; k += 4) {
         if constexpr (ALIGNED) {
-          const f4 vv = *reinterpret_cast<const f4*>(a.values + e0 + k);
+          csr_value_quad<VT>(a.values, e0 + k, val + k);
           const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + e0 + k);
-          val[k] = vv.x; val[k + 1] = vv.y; val[k + 2] = vv.z; val[k + 3] = vv.w;
           col[k] = cc.x; col[k + 1] = cc.y; col[k + 2] = cc.z; col[k + 3] = cc.w;
         } else {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            val[k + q] = a.values[e0 + k + q];
+            val[k + q] = csr_value<VT>(a.values, e0 + k + q);
             col[k + q] = a.col_idx[e0 + k + q];
           }
         }
@@ -275,7 +274,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
       for (int k = 0; k < K; ++k) {
         const bool in = e0 + k < nnz;
         const uint32_t p = in ? e0 + k : nnz - 1;
-        const float x = a.values[p];
+        const float x = csr_value<VT>(a.values, p);
         const int32_t c = a.col_idx[p];
         val[k] = in ? x : 0.0f;
         col[k] = in ? c : 0;
@@ -295,15 +294,14 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     for (int k = 0; k < K; k += 4) {
       if constexpr (ALIGNED) {
         const uint32_t q = min(e0 + k, last_quad);
-        const f4 vv = *reinterpret_cast<const f4*>(a.values + q);
+        csr_value_quad<VT>(a.values, q, val + k);
         const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + q);
-        val[k] = vv.x; val[k + 1] = vv.y; val[k + 2] = vv.z; val[k + 3] = vv.w;
         col[k] = cc.x; col[k + 1] = cc.y; col[k + 2] = cc.z; col[k + 3] = cc.w;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t p = min(e0 + k + q, nnz - 1u);
-          val[k + q] = a.values[p];
+          val[k + q] = csr_value<VT>(a.values, p);
           col[k + q] = a.col_idx[p];
         }
       }
@@ -320,7 +318,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
         for (int k = 0; k < K; ++k) {
           const uint32_t p = e0 + k;
           if (p >= nnz_full && p < nnz) {
-            g.val[k] = a.values[p];
+            g.val[k] = csr_value<VT>(a.values, p);
             g.col[k] = a.col_idx[p];
           }
         }
@@ -609,52 +607,52 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   }
 }
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
+template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 hipError_t launch_k(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   size_t lds = ((size_t)a.lds_window + (YMODE == kYGlobal ? 0 : (size_t)a.y_window)) * sizeof(float);
   if (COLD == kColdBinned) lds = ((lds + 7) & ~(size_t)7) + (size_t)a.bins * kCsrBinStateBytes;
-  const void* fn = reinterpret_cast<const void*>(&csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
+  const void* fn = reinterpret_cast<const void*>(&csr_fused<VT, BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
   hipError_t e = allow_dynamic_lds(fn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_fused<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
+  hipLaunchKernelGGL((csr_fused<VT, BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
                      s, a);
   return hipGetLastError();
 }
 
-template <int BLK, int K, int COLD, int YMODE, int MODE>
+template <class VT, int BLK, int K, int COLD, int YMODE, int MODE>
 hipError_t launch_kv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const bool al = a.aligned && a.nnz >= 4;  // 16-byte loads need one whole quad of entries
+  const bool al = a.aligned && a.nnz >= 4;  // vector loads need one whole quad of entries
   if constexpr (MODE == kModeTmv) {  // u is always given
-    return al ? launch_k<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
-              : launch_k<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+    return al ? launch_k<VT, BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+              : launch_k<VT, BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
   } else {
     if (a.v != nullptr)
-      return al ? launch_k<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
-                : launch_k<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
-    return al ? launch_k<BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
-              : launch_k<BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
+      return al ? launch_k<VT, BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+                : launch_k<VT, BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+    return al ? launch_k<VT, BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
+              : launch_k<VT, BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
   }
 }
 
-template <int BLK, int K, int COLD, int MODE>
+template <class VT, int BLK, int K, int COLD, int MODE>
 hipError_t launch_kk(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if constexpr (MODE == kModeTmv) {
-    return launch_kv<BLK, K, COLD, kYGlobal, MODE>(a, p, s);  // no y
+    return launch_kv<VT, BLK, K, COLD, kYGlobal, MODE>(a, p, s);  // no y
   } else {
-    if (a.y_window >= a.n) return launch_kv<BLK, K, COLD, kYLds, MODE>(a, p, s);
-    if (a.y_window > 0) return launch_kv<BLK, K, COLD, kYSplit, MODE>(a, p, s);
-    return launch_kv<BLK, K, COLD, kYGlobal, MODE>(a, p, s);
+    if (a.y_window >= a.n) return launch_kv<VT, BLK, K, COLD, kYLds, MODE>(a, p, s);
+    if (a.y_window > 0) return launch_kv<VT, BLK, K, COLD, kYSplit, MODE>(a, p, s);
+    return launch_kv<VT, BLK, K, COLD, kYGlobal, MODE>(a, p, s);
   }
 }
 
-template <int BLK, int K, int MODE>
+template <int BLK, int K, int MODE, class VT = float>
 hipError_t launch_cold(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if constexpr (MODE == kModeRowdot) {
-    return launch_kk<BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
+    return launch_kk<VT, BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
   } else {
-    if (a.bins > 0) return launch_kk<BLK, K, kColdBinned, MODE>(a, p, s);
-    if (a.lds_window < a.n) return launch_kk<BLK, K, kColdAtomic, MODE>(a, p, s);
-    return launch_kk<BLK, K, kColdNone, MODE>(a, p, s);
+    if (a.bins > 0) return launch_kk<VT, BLK, K, kColdBinned, MODE>(a, p, s);
+    if (a.lds_window < a.n) return launch_kk<VT, BLK, K, kColdAtomic, MODE>(a, p, s);
+    return launch_kk<VT, BLK, K, kColdNone, MODE>(a, p, s);
   }
 }
 
@@ -669,6 +667,14 @@ hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
+  if (a.value_bytes == 2) {  // bf16 values: the whole pattern only
+    if (mode != kCsrFused || (!binned && a.lds_window < a.n && a.acc == nullptr)) return hipErrorInvalidValue;
+    if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4, kModeFused, bf16_t>(a, p, s);
+    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeFused, bf16_t>(a, p, s);
+    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeFused, bf16_t>(a, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.value_bytes != 4) return hipErrorInvalidValue;
   if (mode == kCsrRowdot) {
     // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
     if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))

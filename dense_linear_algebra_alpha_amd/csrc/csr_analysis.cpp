@@ -231,9 +231,14 @@ xtvxy_status xtvxy_csr_f32_analysed_workspace_size(xtvxy_csr_analysis analysis, 
   return XTVXY_SUCCESS;
 }
 
-xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const float* values, const float* v,
-                                       const float* y, float beta, const float* z, float* out, void* workspace,
-                                       size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+}  // extern "C"
+
+namespace {
+
+// An analysed call with fp32 (value_bytes 4) or bf16 (2) values.
+xtvxy_status analysed_impl(xtvxy_csr_analysis an, float alpha, const void* values, int value_bytes, const float* v,
+                           const float* y, float beta, const float* z, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
   if (!an) return XTVXY_ERROR_NULL_POINTER;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return XTVXY_ERROR_LAUNCH;
@@ -246,7 +251,8 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const
   if (reads_x && !values) return XTVXY_ERROR_NULL_POINTER;
   const size_t nb = (size_t)n * sizeof(float);
   if (reads_x) {
-    if (overlap(out, nb, an->row_ptr, (size_t)(m + 1) * 4) || overlap(out, nb, values, (size_t)nnz * 4) ||
+    if (overlap(out, nb, an->row_ptr, (size_t)(m + 1) * 4) ||
+        overlap(out, nb, values, (size_t)nnz * (size_t)value_bytes) ||
         overlap(out, nb, y, nb) || (v && overlap(out, nb, v, (size_t)m * sizeof(float))))
       return XTVXY_ERROR_ALIASING;
   }
@@ -257,6 +263,7 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const
     xtvxy_status st = complete_for(an, &plan);
     if (st != XTVXY_SUCCESS) return st;
   }
+  if (value_bytes != 4 && plan.kernel == XTVXY_CSR_ROWS) return XTVXY_ERROR_INVALID_VALUE;  // fp32 values only
   if (!workspace || workspace_bytes < (size_t)plan.workspace_bytes) return XTVXY_ERROR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0) return XTVXY_ERROR_WORKSPACE;
   const size_t yoff = yp_offset(an, plan);
@@ -265,14 +272,36 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const
   CsrExtras x{an->rows, an->bounds, an->batches, an->batch_prefix, an->batches_count, an->perm,
               binned_items(an, plan)};
   return csr_run_fused(m, n, nnz, alpha, an->row_ptr, an->col_slot, values, v, yp, beta, z, out, workspace, yoff,
-                       stream, &plan, &x);
+                       stream, &plan, &x, value_bytes);
+}
+
+}  // namespace
+
+extern "C" {
+
+xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis an, float alpha, const float* values, const float* v,
+                                       const float* y, float beta, const float* z, float* out, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+  return analysed_impl(an, alpha, values, 4, v, y, beta, z, out, workspace, workspace_bytes, stream, force);
 }
 
 xtvxy_status xtvxy_csr_f32_analysed(xtvxy_csr_analysis analysis, float alpha, const float* values, const float* v,
                                     const float* y, float beta, const float* z, float* out, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
-  return xtvxy_csr_f32_analysed_ex(analysis, alpha, values, v, y, beta, z, out, workspace, workspace_bytes, stream,
-                                   nullptr);
+  return analysed_impl(analysis, alpha, values, 4, v, y, beta, z, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+xtvxy_status xtvxy_csr_bf16_analysed_ex(xtvxy_csr_analysis an, float alpha, const uint16_t* values, const float* v,
+                                        const float* y, float beta, const float* z, float* out, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream,
+                                        const xtvxy_launch_params* force) {
+  return analysed_impl(an, alpha, values, 2, v, y, beta, z, out, workspace, workspace_bytes, stream, force);
+}
+
+xtvxy_status xtvxy_csr_bf16_analysed(xtvxy_csr_analysis analysis, float alpha, const uint16_t* values,
+                                     const float* v, const float* y, float beta, const float* z, float* out,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return analysed_impl(analysis, alpha, values, 2, v, y, beta, z, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"

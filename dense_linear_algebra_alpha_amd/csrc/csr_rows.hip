@@ -59,7 +59,7 @@ __global__ __launch_bounds__(BLK) void csr_rows(CsrArgs a) {
   const int32_t window = (int32_t)a.lds_window;
   const int32_t y_window = YMODE == kYGlobal ? 0 : (int32_t)a.y_window;
   const uint32_t nnz_full = nnz & ~3u;  // entries in whole quads
-  const float* __restrict__ values = a.values;
+  const float* __restrict__ values = static_cast<const float*>(a.values);  // fp32 only (checked at launch)
   const int32_t* __restrict__ cols = a.col_idx;
   const int bins = BINNED ? a.bins : 0;
   // after the windows: a sink word per thread (masked-off LDS adds), then this wavefront's bins
@@ -451,7 +451,7 @@ hipError_t launch_csr_rows(const CsrArgs& a, const xtvxy_launch_params& p, hipSt
     return hipErrorInvalidValue;
   if (a.nnz <= 0 || a.nnz > INT32_MAX || a.m <= 0 || a.m > INT32_MAX - 1024 || a.lds_window < 0 ||
       a.lds_window > a.n || a.y_window < 0 || a.y_window > a.n || a.rows == nullptr || a.bounds == nullptr ||
-      a.batches == nullptr || a.batch_prefix == nullptr || a.batches_count < 0)
+      a.batches == nullptr || a.batch_prefix == nullptr || a.batches_count < 0 || a.value_bytes != 4)
     return hipErrorInvalidValue;
   const bool binned = a.bins > 0;
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||

@@ -57,7 +57,7 @@ struct WaveTile {
 // of X^T u, u given in place of v, no y and no dots).
 enum WaveMode { kWaveFused = 0, kWaveRowdot = 1, kWaveTmv = 2 };
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
+template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512 || BLK == 1024, "workgroups of 256, 512 or 1024 threads");
   static_assert(K == 8, "eight entries per lane: two 16-byte vectors, one 8-byte word of marks");
@@ -134,15 +134,14 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
     for (int k = 0; k < K; k += 4) {
       if constexpr (ALIGNED) {
         const uint32_t q = min(e0 + k, last_quad);
-        const f4 vv = *reinterpret_cast<const f4*>(a.values + q);
+        csr_value_quad<VT>(a.values, q, val + k);
         const i4 cc = *reinterpret_cast<const i4*>(a.col_idx + q);
-        val[k] = vv.x; val[k + 1] = vv.y; val[k + 2] = vv.z; val[k + 3] = vv.w;
         col[k] = cc.x; col[k + 1] = cc.y; col[k + 2] = cc.z; col[k + 3] = cc.w;
       } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t p = min(e0 + k + q, nnz - 1u);
-          val[k + q] = a.values[p];
+          val[k + q] = csr_value<VT>(a.values, p);
           col[k + q] = a.col_idx[p];
         }
       }
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
         for (int k = 0; k < K; ++k) {
           const uint32_t p = e0 + k;
           if (p >= nnz_full && p < nnz) {
-            val[k] = a.values[p];
+            val[k] = csr_value<VT>(a.values, p);
             col[k] = a.col_idx[p];
           }
         }
@@ -451,56 +450,56 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   }
 }
 
-template <int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
+template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 hipError_t launch_w(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   const size_t lds = csr_waves_dynamic_lds(a.lds_window, YMODE == kYGlobal ? 0 : a.y_window, a.bins, BLK);
-  const void* fn = reinterpret_cast<const void*>(&csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
+  const void* fn = reinterpret_cast<const void*>(&csr_waves<VT, BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>);
   hipError_t e = allow_dynamic_lds(fn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((csr_waves<BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
+  hipLaunchKernelGGL((csr_waves<VT, BLK, K, YMODE, HAS_V, ALIGNED, COLD, MODE>), dim3((unsigned)p.grid), dim3(BLK), lds,
                      s, a);
   return hipGetLastError();
 }
 
-template <int BLK, int K, int YMODE, int COLD, int MODE>
+template <class VT, int BLK, int K, int YMODE, int COLD, int MODE>
 hipError_t launch_wv(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  const bool al = a.aligned && a.nnz >= 4;  // 16-byte loads need one whole quad of entries
+  const bool al = a.aligned && a.nnz >= 4;  // vector loads need one whole quad of entries
   if (MODE == kWaveTmv || a.v != nullptr)   // u is always given to the second half
-    return al ? launch_w<BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
-              : launch_w<BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
+    return al ? launch_w<VT, BLK, K, YMODE, true, true, COLD, MODE>(a, p, s)
+              : launch_w<VT, BLK, K, YMODE, true, false, COLD, MODE>(a, p, s);
   if constexpr (MODE != kWaveTmv)
-    return al ? launch_w<BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
-              : launch_w<BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
+    return al ? launch_w<VT, BLK, K, YMODE, false, true, COLD, MODE>(a, p, s)
+              : launch_w<VT, BLK, K, YMODE, false, false, COLD, MODE>(a, p, s);
   return hipErrorInvalidValue;
 }
 
-template <int BLK, int K, int COLD, int MODE>
+template <class VT, int BLK, int K, int COLD, int MODE>
 hipError_t launch_wy(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if constexpr (MODE == kWaveTmv) {
-    return launch_wv<BLK, K, kYGlobal, COLD, MODE>(a, p, s);  // no y
+    return launch_wv<VT, BLK, K, kYGlobal, COLD, MODE>(a, p, s);  // no y
   } else {
-    if (a.y_window >= a.n) return launch_wv<BLK, K, kYLds, COLD, MODE>(a, p, s);
-    if (a.y_window > 0) return launch_wv<BLK, K, kYSplit, COLD, MODE>(a, p, s);
-    return launch_wv<BLK, K, kYGlobal, COLD, MODE>(a, p, s);
+    if (a.y_window >= a.n) return launch_wv<VT, BLK, K, kYLds, COLD, MODE>(a, p, s);
+    if (a.y_window > 0) return launch_wv<VT, BLK, K, kYSplit, COLD, MODE>(a, p, s);
+    return launch_wv<VT, BLK, K, kYGlobal, COLD, MODE>(a, p, s);
   }
 }
 
-template <int BLK, int K, int MODE>
+template <class VT, int BLK, int K, int MODE>
 hipError_t launch_wc(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
   if constexpr (MODE == kWaveRowdot) {
-    return launch_wy<BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
+    return launch_wy<VT, BLK, K, kColdNone, MODE>(a, p, s);  // no scatter
   } else {
-    if (a.bins > 0) return launch_wy<BLK, K, kColdBinned, MODE>(a, p, s);
-    if (a.lds_window < a.n) return launch_wy<BLK, K, kColdAtomic, MODE>(a, p, s);
-    return launch_wy<BLK, K, kColdNone, MODE>(a, p, s);
+    if (a.bins > 0) return launch_wy<VT, BLK, K, kColdBinned, MODE>(a, p, s);
+    if (a.lds_window < a.n) return launch_wy<VT, BLK, K, kColdAtomic, MODE>(a, p, s);
+    return launch_wy<VT, BLK, K, kColdNone, MODE>(a, p, s);
   }
 }
 
-template <int MODE>
+template <int MODE, class VT = float>
 hipError_t launch_wb(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s) {
-  if (p.block_threads == 256) return launch_wc<256, 8, MODE>(a, p, s);
-  if (p.block_threads == 512) return launch_wc<512, 8, MODE>(a, p, s);
-  if (p.block_threads == 1024) return launch_wc<1024, 8, MODE>(a, p, s);
+  if (p.block_threads == 256) return launch_wc<VT, 256, 8, MODE>(a, p, s);
+  if (p.block_threads == 512) return launch_wc<VT, 512, 8, MODE>(a, p, s);
+  if (p.block_threads == 1024) return launch_wc<VT, 1024, 8, MODE>(a, p, s);
   return hipErrorInvalidValue;
 }
 
@@ -516,6 +515,11 @@ hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipS
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
+  if (a.value_bytes == 2) {  // bf16 values: the whole pattern only
+    if (mode != kCsrFused || (!binned && a.lds_window < a.n && a.acc == nullptr)) return hipErrorInvalidValue;
+    return launch_wb<kWaveFused, bf16_t>(a, p, s);
+  }
+  if (a.value_bytes != 4) return hipErrorInvalidValue;
   if (mode == kCsrRowdot) {
     // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
     if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))

@@ -234,4 +234,34 @@ __device__ __forceinline__ void load_x(const E* __restrict__ xr, int64_t col, bo
   }
 }
 
+// Stored values of a CSR matrix: fp32, or bf16 (VT = bf16_t: the upper 16 bits of an fp32 bit
+// pattern, widened exactly as it is loaded). Every load returns fp32.
+template <class VT>
+__device__ __forceinline__ float csr_value(const void* values, uint32_t p) {
+  if constexpr (sizeof(VT) == 4) {
+    return static_cast<const float*>(values)[p];
+  } else {
+    return __uint_as_float((uint32_t)static_cast<const bf16_t*>(values)[p] << 16);
+  }
+}
+// Values q .. q+3 (q a multiple of 4) by one load: 16 bytes of fp32 (16-byte aligned values) or
+// 8 bytes of bf16 (8-byte aligned values); the caller guarantees the alignment.
+typedef unsigned int vu2 __attribute__((ext_vector_type(2)));
+template <class VT>
+__device__ __forceinline__ void csr_value_quad(const void* values, uint32_t q, float* o) {
+  if constexpr (sizeof(VT) == 4) {
+    const f4 vv = *reinterpret_cast<const f4*>(static_cast<const float*>(values) + q);
+    o[0] = vv.x;
+    o[1] = vv.y;
+    o[2] = vv.z;
+    o[3] = vv.w;
+  } else {
+    const vu2 w = *reinterpret_cast<const vu2*>(static_cast<const bf16_t*>(values) + q);
+    o[0] = bf16_lo(w.x);
+    o[1] = bf16_hi(w.x);
+    o[2] = bf16_lo(w.y);
+    o[3] = bf16_hi(w.y);
+  }
+}
+
 }  // namespace xtvxy

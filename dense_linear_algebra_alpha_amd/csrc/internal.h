@@ -100,14 +100,16 @@ struct CsrArgs {
   int64_t m, n, nnz;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  const float* values;
+  const void* values;     // fp32, or bf16 bit patterns when value_bytes == 2
+  int32_t value_bytes;    // 4 or 2
   const float* v;
   const float* y;
   float* partial;     // [grid][lds_window] per-workgroup partial sums of output columns [0, lds_window)
   float* acc;         // [n] global accumulator of columns >= lds_window (zeroed before launch), or null
   int64_t lds_window;
   int64_t y_window;   // y[0, y_window) is gathered from an LDS copy, the rest from global memory
-  bool aligned;       // values and col_idx are 16-byte aligned: entries load as vectors
+  bool aligned;       // col_idx 16-byte and values 16-byte (fp32) or 8-byte (bf16) aligned:
+                      // entries load as vectors
   // the first half of the pattern alone (launch mode kCsrRowdot): t_out = alpha v .* (X y) + beta t0
   float alpha, beta;
   const float* t0;    // read only when beta != 0 (may equal t_out)
@@ -240,10 +242,11 @@ struct CsrExtras {
 };
 // The fused CSR path for checked arguments (api.cpp): the plan (`force`, completed here; the model's
 // when null), the main kernel, the bin passes and the aggregation, on `stream`.
+// Values are fp32 (value_bytes 4) or bf16 bit patterns (2).
 xtvxy_status csr_run_fused(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                           const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
+                           const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
                            const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
-                           const xtvxy_launch_params* force, const CsrExtras* extras);
+                           const xtvxy_launch_params* force, const CsrExtras* extras, int value_bytes = 4);
 // The device description of the current device (cached).
 xtvxy_status current_device_info(xtvxy_device_info* d);
 // Records the measurement hook's events around a main kernel (api.cpp).

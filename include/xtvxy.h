@@ -247,6 +247,25 @@ xtvxy_status xtvxy_csr_f32_ex(int64_t m, int64_t n, int64_t nnz, float alpha,
 xtvxy_status xtvxy_csr_f32_plan_complete(int64_t m, int64_t n, int64_t nnz,
                                          const xtvxy_device_info *dev, xtvxy_launch_params *plan);
 
+/* The CSR pattern with the values stored as bf16: reduced-precision storage of X (its values; the
+ * structure stays int32), all arithmetic fp32 ("On optimizing machine learning workloads via
+ * kernel fusion", abstract: the fused path reads X once, so its bytes set the time; a bf16 value
+ * halves the 8 bytes of a stored entry's value and column to 6). values[nnz] are bf16 bit
+ * patterns (the upper 16 bits of an fp32, widened exactly as they are loaded), so the result is
+ * that of xtvxy_csr_f32 on the widened values, up to the order of fp32 additions. Everything else
+ * as xtvxy_csr_f32: the same plans, the same workspace (xtvxy_csr_f32_workspace_size), the same
+ * conventions, pointer, aliasing (out against 2 nnz bytes of values) and error rules; vector loads
+ * when col_idx is 16-byte and values 8-byte aligned. The tile and wavefront kernels take bf16
+ * values; a forced XTVXY_CSR_ROWS plan gives XTVXY_ERROR_INVALID_VALUE. */
+xtvxy_status xtvxy_csr_bf16(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                            const int32_t *col_idx, const uint16_t *values, const float *v, const float *y,
+                            float beta, const float *z, float *out, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+xtvxy_status xtvxy_csr_bf16_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                               const int32_t *col_idx, const uint16_t *values, const float *v, const float *y,
+                               float beta, const float *z, float *out, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream, const xtvxy_launch_params *force);
+
 /* Structure analysis of a CSR matrix, made once and used by any number of calls whose values
  * change ("On optimizing machine learning workloads via kernel fusion", abstract: the launch
  * parameters come from the input's characteristics; here they are read from the structure):
@@ -291,6 +310,16 @@ xtvxy_status xtvxy_csr_f32_analysed_ex(xtvxy_csr_analysis analysis, float alpha,
                                        const float *v, const float *y, float beta, const float *z, float *out,
                                        void *workspace, size_t workspace_bytes, hipStream_t stream,
                                        const xtvxy_launch_params *force);
+/* The analysed call with bf16 values (nnz bf16 bit patterns in the caller's storage order), as
+ * xtvxy_csr_bf16 is to xtvxy_csr_f32: same analysis, plans and workspace as the fp32 call; a forced
+ * XTVXY_CSR_ROWS plan gives XTVXY_ERROR_INVALID_VALUE. */
+xtvxy_status xtvxy_csr_bf16_analysed(xtvxy_csr_analysis analysis, float alpha, const uint16_t *values,
+                                     const float *v, const float *y, float beta, const float *z, float *out,
+                                     void *workspace, size_t workspace_bytes, hipStream_t stream);
+xtvxy_status xtvxy_csr_bf16_analysed_ex(xtvxy_csr_analysis analysis, float alpha, const uint16_t *values,
+                                        const float *v, const float *y, float beta, const float *z, float *out,
+                                        void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                        const xtvxy_launch_params *force);
 
 /* The two halves of the pattern on their own, for CSR X ("On optimizing machine learning
  * workloads via kernel fusion", abstract: the pattern chains X y and X^T (.); iterative solvers

@@ -44,8 +44,9 @@ def dense_oracle(p):
 
 
 def csr_oracle(p):
-    ref = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta)
-    bnd = oracle.csr(p.row_ptr, p.col_idx, p.values, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
+    vals = p.values_f32()  # bf16 values widened exactly: the oracle computes on the numbers they denote
+    ref = oracle.csr(p.row_ptr, p.col_idx, vals, p.n, p.y, p.v, p.z, p.alpha, p.beta)
+    bnd = oracle.csr(p.row_ptr, p.col_idx, vals, p.n, p.y, p.v, p.z, p.alpha, p.beta, bound=True)
     return ref, bnd
 
 

@@ -100,25 +100,34 @@ def test_dense_explicit_comparator_argument_errors(lib):
 
 
 def csr_status(m=8, n=8, nnz=16, alpha=1.0, rp=FAKE, ci=FAKE + 1024, vals=FAKE + 2048, v=None, y=FAKE + 4096,
-               beta=0.0, z=None, out=FAKE + 8192):
-    return _abi.load().xtvxy_csr_f32(m, n, nnz, alpha, rp, ci, vals, v, y, beta, z, out, None, 0, None)
+               beta=0.0, z=None, out=FAKE + 8192, fn="xtvxy_csr_f32"):
+    return getattr(_abi.load(), fn)(m, n, nnz, alpha, rp, ci, vals, v, y, beta, z, out, None, 0, None)
 
 
-def test_csr_argument_errors(lib):
-    assert csr_status(m=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
-    assert csr_status(nnz=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
-    assert csr_status(nnz=1 << 31) == _abi.XTVXY_ERROR_UNSUPPORTED
-    assert csr_status(m=1 << 31) == _abi.XTVXY_ERROR_UNSUPPORTED
-    assert csr_status(rp=None) == _abi.XTVXY_ERROR_NULL_POINTER
-    assert csr_status(ci=None) == _abi.XTVXY_ERROR_NULL_POINTER
-    assert csr_status(vals=None) == _abi.XTVXY_ERROR_NULL_POINTER
-    assert csr_status(y=None) == _abi.XTVXY_ERROR_NULL_POINTER
-    assert csr_status(beta=2.0) == _abi.XTVXY_ERROR_NULL_POINTER
-    assert csr_status(out=FAKE + 1024 + 60) == _abi.XTVXY_ERROR_ALIASING        # overlaps col_idx
-    assert csr_status(out=FAKE + 4) == _abi.XTVXY_ERROR_ALIASING                # overlaps row_ptr
-    assert csr_status(n=0) == _abi.XTVXY_SUCCESS
+@pytest.mark.parametrize("fn", ["xtvxy_csr_f32", "xtvxy_csr_bf16"])
+def test_csr_argument_errors(lib, fn):
+    assert csr_status(m=-1, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert csr_status(nnz=-1, fn=fn) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert csr_status(nnz=1 << 31, fn=fn) == _abi.XTVXY_ERROR_UNSUPPORTED
+    assert csr_status(m=1 << 31, fn=fn) == _abi.XTVXY_ERROR_UNSUPPORTED
+    assert csr_status(rp=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(ci=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(vals=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(y=None, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(beta=2.0, fn=fn) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert csr_status(out=FAKE + 1024 + 60, fn=fn) == _abi.XTVXY_ERROR_ALIASING        # overlaps col_idx
+    assert csr_status(out=FAKE + 4, fn=fn) == _abi.XTVXY_ERROR_ALIASING                # overlaps row_ptr
+    assert csr_status(out=FAKE + 2048 + 28, fn=fn) == _abi.XTVXY_ERROR_ALIASING        # overlaps values
+    assert csr_status(n=0, fn=fn) == _abi.XTVXY_SUCCESS
     st = lib.xtvxy_csr_check(4, 4, 4, None, FAKE, FAKE, None)
     assert st == _abi.XTVXY_ERROR_NULL_POINTER
+
+
+def test_csr_bf16_values_span_two_bytes_each(lib):
+    # 16 values end 64 bytes after their start as fp32 but 32 bytes after it as bf16: an out that
+    # starts 40 bytes in overlaps the fp32 values only (the bf16 call then fails later, with no GPU)
+    assert csr_status(out=FAKE + 2048 + 40) == _abi.XTVXY_ERROR_ALIASING
+    assert csr_status(out=FAKE + 2048 + 40, fn="xtvxy_csr_bf16") != _abi.XTVXY_ERROR_ALIASING
 
 
 def test_query_argument_errors(lib):
