@@ -13,8 +13,9 @@
 // longest run of whole rows whose entries fit:
 //   1. thread t holds the K consecutive entries starting at base + K t (base =
 //      the tile's first entry rounded down to a multiple of 4), loaded as
-//      16-byte vectors of values and of column indices, and gathers y[column]
-//      (from an LDS copy of y when it is small);
+//      vectors of 4 values (16 bytes of fp32, or 8 of bf16 widened exactly to
+//      fp32: reduced-precision storage of the values) and of 4 column indices,
+//      and gathers y[column] (from an LDS copy of y when it is small);
 //   2. the row of each entry comes from row-start marks: every nonempty row of
 //      the tile writes its index at the LDS slot of its first entry, each
 //      thread reads the marks of its K slots, and a running maximum over the
@@ -74,7 +75,7 @@ struct TileRegs {
 template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512, "workgroups of 256 or 512 threads");
-  static_assert(K == 4 || K == 8, "entries are loaded as 16-byte vectors; marks as 8 or 16 bytes");
+  static_assert(K == 4 || K == 8, "entries are loaded as vectors of 4; marks as 8 or 16 bytes");
   constexpr int T = BLK * K;  // entry slots of a tile; a tile also holds at most BLK rows
   constexpr bool BINNED = COLD == kColdBinned;
   // per-tile state, double-buffered by tile parity
@@ -282,7 +283,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
     }
   };
   // The same entries loaded a step ahead, with no branch at all (see the top of the file): with
-  // 16-byte loads a quad at or past the last whole quad of the arrays is read at the last whole
+  // vector loads a quad at or past the last whole quad of the arrays is read at the last whole
   // quad instead (the launch guarantees nnz >= 4), element loads are clamped to nnz - 1. Slots
   // past the tile then hold entries of other positions; every use masks them, and their column
   // indices are valid. The up to three entries after the whole quads are patched in by
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
       }
     }
   };
-  // Entries nnz_full .. nnz - 1 of a tile loaded by load_entries_ahead with 16-byte loads. The
+  // Entries nnz_full .. nnz - 1 of a tile loaded by load_entries_ahead with vector loads. The
   // branch is the same for the whole workgroup and taken by the last tile or two only.
   auto fix_tail = [&](uint32_t first_entry, TileRegs<K>& g) {
     if constexpr (ALIGNED && kGatherAhead) {

@@ -15,7 +15,8 @@
 //     [g q, (g + 1) q), q = ceil(nnz / G), found by a 64-way search of row_ptr;
 //   - it takes them in tiles of whole rows, at most 64 rows and 64 K entry slots:
 //     lane l holds the K consecutive entries from base + K l (base = the tile's
-//     first entry rounded down to 4), loaded as 16-byte vectors;
+//     first entry rounded down to 4), loaded as vectors of 4 (values fp32, or
+//     bf16 widened exactly as they are loaded);
 //   - the row of each entry comes from row-start marks in the wavefront's own LDS
 //     bytes (a running maximum within the lane, then across the wavefront); per-row
 //     dots are summed in registers and finished by a segmented sum across the
@@ -60,7 +61,7 @@ enum WaveMode { kWaveFused = 0, kWaveRowdot = 1, kWaveTmv = 2 };
 template <class VT, int BLK, int K, int YMODE, bool HAS_V, bool ALIGNED, int COLD, int MODE>
 __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   static_assert(BLK == 256 || BLK == 512 || BLK == 1024, "workgroups of 256, 512 or 1024 threads");
-  static_assert(K == 8, "eight entries per lane: two 16-byte vectors, one 8-byte word of marks");
+  static_assert(K == 8, "eight entries per lane: two vectors of 4, one 8-byte word of marks");
   constexpr int NW = BLK / 64;  // wavefronts of the workgroup
   constexpr int TW = 64 * K;    // entry slots of a wavefront's tile
   constexpr bool BINNED = COLD == kColdBinned;
