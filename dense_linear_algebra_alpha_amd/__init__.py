@@ -509,7 +509,8 @@ def csr(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out
 
 def csr_tensor(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None, stream=None):
     """csr() for X given as a torch sparse CSR tensor (torch.sparse_csr_tensor) with int32 indices
-    and float32 values on the GPU; its crow_indices, col_indices and values are passed as they are."""
+    and float32 (or bfloat16) values on the GPU; its crow_indices, col_indices and values are passed
+    as they are."""
     torch = _torch()
     if X.layout != torch.sparse_csr or X.dim() != 2:
         raise ValueError("X must be a 2-D torch.sparse_csr tensor")

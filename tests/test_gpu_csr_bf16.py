@@ -7,7 +7,7 @@ import pytest
 
 import datagen
 import dense_linear_algebra_alpha_amd as xt
-from gpu_util import CsrOnDevice, assert_parity, csr_oracle, note, to_dev
+from gpu_util import CsrOnDevice, assert_parity, csr_oracle, note
 from test_gpu_csr import forced_plans
 from test_gpu_csr_waves import wave_plans
 
@@ -129,10 +129,9 @@ def test_special_scalars_and_nan():
     q = bf16(datagen.csr_random(300, 200, seed=6, mean_len=4.0, empty_frac=0.0))
     q.values = q.values.copy()
     q.values[0] = 0x7FC0  # bf16 NaN
-    r0 = int(np.searchsorted(q.row_ptr, 0, side="right") - 1)
     got = CsrOnDevice(q).run()
     ref, _ = csr_oracle(q)
-    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).any(), r0
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.isnan(got).any()
 
 
 def test_analysed_calls():
@@ -174,6 +173,19 @@ def test_matches_fp32_on_the_widened_values():
     b = CsrOnDevice(q).run()
     assert_parity(a, ref, bnd, "bf16")
     assert_parity(b, ref, bnd, "fp32 widened")
+
+
+def test_torch_sparse_csr_tensor_with_bf16_values():
+    import torch
+    p = bf16(datagen.csr_random(3000, 700, seed=78, mean_len=9.0, empty_frac=0.1, dup_frac=0.05))
+    ref, bnd = csr_oracle(p)
+    d = CsrOnDevice(p)
+    X = torch.sparse_csr_tensor(d.rp, d.ci, d.vals, size=(p.m, p.n))
+    assert X.values().dtype == torch.bfloat16
+    note("bf16 csr from torch.sparse_csr_tensor m=%d n=%d nnz=%d" % (p.m, p.n, p.nnz))
+    got = xt.csr_tensor(X, d.y, d.v, d.z, p.alpha, p.beta)
+    torch.cuda.synchronize()
+    assert_parity(got.cpu().numpy(), ref, bnd, "bf16 sparse_csr_tensor")
 
 
 @pytest.mark.parametrize("name", ["csr_10000000x1000_logistic_hvp_bf16", "csr_5000000x1000000_zipf_bf16"])
