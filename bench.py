@@ -53,7 +53,7 @@ def algorithmic_bytes(p) -> int:
         b = (vb + 4) * p.nnz + 4 * (p.m + 1) + 4 * p.n + 4 * p.n
         b += 4 * p.m if p.v is not None else 0
     else:
-        xb = 2 if getattr(p, "x_dtype", "f32") == "bf16" else 4  # bf16 storage of X: 2 bytes per element
+        xb = 2 if getattr(p, "x_dtype", "f32") in ("bf16", "f16") else 4  # 16-bit X: 2 bytes per element
         b = xb * p.m * p.n + 4 * p.n + 4 * p.n
         b += 4 * p.m if p.v is not None else 0
     b += 4 * p.n if p.beta != 0 else 0
@@ -145,17 +145,20 @@ def override(plan, text):
 
 def cpu_baseline(p, budget_s: float, threads=None, min_runs=3):
     """The oracle, as it is, on the host cores: repeated runs of the full workload for ~budget_s."""
+    import numpy as np
+
     import oracle
     threads = oracle.set_threads(threads or len(os.sched_getaffinity(0)))
     runs = []
     vals = p.values_f32() if hasattr(p, "col_idx") else None  # bf16 values widened (exactly) once
+    X = None if hasattr(p, "col_idx") else (p.X.astype(np.float32) if p.x_dtype == "f16" else p.X)  # fp16: widened
     t_end = time.perf_counter() + budget_s
     while len(runs) < min_runs or (time.perf_counter() < t_end and len(runs) < 200):
         t0 = time.perf_counter()
         if hasattr(p, "col_idx"):
             oracle.csr(p.row_ptr, p.col_idx, vals, p.n, p.y, p.v, p.z, p.alpha, p.beta)
         else:
-            oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+            oracle.dense(X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
         runs.append(time.perf_counter() - t0)
     med = statistics.median(runs)
     oracle.set_threads(len(os.sched_getaffinity(0)))
@@ -455,15 +458,20 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
     out = torch.empty(p.n, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream or None
-    # bf16 storage: of X (dense) or of the values (CSR)
-    bf16 = getattr(p, "x_dtype", "f32") == "bf16" or getattr(p, "values_dtype", "f32") == "bf16"
+    # 16-bit storage: of X (dense, bf16 or fp16) or of the values (CSR, bf16); the comparison is then
+    # the fp32 fused path on the widened numbers
+    f16 = getattr(p, "x_dtype", "f32") == "f16"
+    bf16 = getattr(p, "x_dtype", "f32") == "bf16" or f16 or getattr(p, "values_dtype", "f32") == "bf16"
+    if f16 and args.tune:
+        raise SystemExit("the tuner takes fp32 or bf16 X")
     plan_text = args.plan if headline else None
     with_unfused = unfused_calls > 0 and not args.fused_only
     if kind == "dense":
         X = t(p.X)
         plan_fn, complete_fn, ws_fn, call, call_ex = (
             (xt.xtvxy_dense_bf16_plan, xt.xtvxy_dense_bf16_plan_complete, xt.xtvxy_dense_bf16_workspace_size,
-             xt.xtvxy_dense_bf16, xt.xtvxy_dense_bf16_ex) if bf16 else
+             xt.xtvxy_dense_f16 if f16 else xt.xtvxy_dense_bf16, xt.xtvxy_dense_f16_ex if f16 else xt.xtvxy_dense_bf16_ex)
+            if bf16 else
             (xt.xtvxy_dense_f32_plan, xt.xtvxy_dense_f32_plan_complete, xt.xtvxy_dense_f32_workspace_size,
              xt.xtvxy_dense_f32, xt.xtvxy_dense_f32_ex))
         plan = plan_fn(p.m, p.n, p.ldx, 1 if X.data_ptr() % 16 == 0 else 0)
@@ -474,8 +482,8 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
         ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
         uws_bytes = xt.xtvxy_dense_f32_unfused_reference_workspace_size(p.m, p.n)
         uws = torch.empty(max(uws_bytes, 1), dtype=torch.uint8, device=dev) if with_unfused else None
-        # bf16 X: the comparison is the fp32 fused path on the same matrix widened to fp32
-        X32 = t(datagen.bf16_to_f32(p.X)) if bf16 and with_unfused else X
+        # 16-bit X: the comparison is the fp32 fused path on the same matrix widened to fp32
+        X32 = t(p.X_f32()) if bf16 and with_unfused else X
         ws32_bytes = xt.xtvxy_dense_f32_workspace_size(p.m, p.n, p.ldx)
         ws32 = torch.empty(max(ws32_bytes, 1), dtype=torch.uint8, device=dev) if bf16 and with_unfused else None
 
@@ -507,7 +515,7 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
                 xt.xtvxy_dense_f32_unfused_reference_explicit(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, Xt.data_ptr(),
                                                               p.m, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
                                                               out.data_ptr(), uws.data_ptr(), uws_bytes, sh)
-        shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": "bf16" if bf16 else "f32"}
+        shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": p.x_dtype}
         env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
     else:
         rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
@@ -657,8 +665,9 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
     if not args.fused_only:
         import oracle
         if kind == "dense":
-            ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
-            bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
+            X = p.X.astype(np.float32) if p.x_dtype == "f16" else p.X  # fp16 X widened exactly by numpy
+            ref = oracle.dense(X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+            bnd = oracle.dense(X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
         else:
             vals64 = p.values_f32()  # bf16 values widened exactly
             ref = oracle.csr(p.row_ptr, p.col_idx, vals64, p.n, p.y, p.v, p.z, p.alpha, p.beta)

@@ -132,17 +132,25 @@ class DenseProblem:
     m: int
     n: int
     ldx: int
-    X: np.ndarray                 # flat, length m*ldx (padding columns hold NaN): fp32, or uint16 bf16 bits
+    X: np.ndarray                 # flat, length m*ldx (padding columns hold NaN): fp32, uint16 bf16 bits or fp16
     y: np.ndarray
     v: Optional[np.ndarray]
     z: Optional[np.ndarray]
     alpha: float
     beta: float
     name: str = ""
-    x_dtype: str = "f32"          # "f32" or "bf16"
+    x_dtype: str = "f32"          # "f32", "bf16" or "f16"
 
     def X2d(self) -> np.ndarray:
         return self.X.reshape(self.m, self.ldx)[:, : self.n]
+
+    def X_f32(self) -> np.ndarray:
+        """X as the fp32 numbers it denotes: bf16 and fp16 widened exactly (fp16 by numpy)."""
+        if self.x_dtype == "bf16":
+            return bf16_to_f32(self.X)
+        if self.x_dtype == "f16":
+            return self.X.astype(np.float32)
+        return self.X
 
 
 @dataclass
@@ -181,12 +189,13 @@ def csr_values_bf16(p: CsrProblem, name: str = "") -> CsrProblem:
 def dense_problem(m, n, seed=0, *, x="uniform", y="uniform", v="uniform", z="uniform", alpha=1.5,
                   beta=0.5, ldx=None, name="", x_dtype="f32") -> DenseProblem:
     """Dense problem whose entries follow the named distributions (None = argument absent). With
-    x_dtype "bf16" the same X is rounded to bf16 (to_bf16) and stored as uint16 bit patterns."""
+    x_dtype "bf16" the same X is rounded to bf16 (to_bf16) and stored as uint16 bit patterns; with
+    "f16" it is rounded to IEEE fp16 (to nearest, ties to even; numpy) and stored as float16."""
     ldx = n if ldx is None else int(ldx)
     if ldx < n:
         raise ValueError("ldx < n")
-    if x_dtype not in ("f32", "bf16"):
-        raise ValueError("x_dtype must be f32 or bf16")
+    if x_dtype not in ("f32", "bf16", "f16"):
+        raise ValueError("x_dtype must be f32, bf16 or f16")
     body = _vector(x, m * n, seed, "X")
     if ldx == n:
         X = body if body is not None else np.zeros(m * n, np.float32)
@@ -195,6 +204,8 @@ def dense_problem(m, n, seed=0, *, x="uniform", y="uniform", v="uniform", z="uni
         X.reshape(m, ldx)[:, :n] = body.reshape(m, n)
     if x_dtype == "bf16":
         X = to_bf16(X)
+    elif x_dtype == "f16":
+        X = X.astype(np.float16)
     return DenseProblem(m, n, ldx, X, _vector(y, n, seed, "y"), _vector(v, m, seed, "v"),
                         _vector(z, n, seed, "z"), float(alpha), float(beta), name, x_dtype)
 
@@ -351,6 +362,16 @@ WORKLOADS = {
     "dense_8192x65536_bf16": lambda seed=0, m=8192, n=65536: dense_problem(
         m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
         name="dense_8192x65536_bf16", x_dtype="bf16"),
+    # and with X stored as IEEE fp16 (rounded to nearest even from the fp32 draw)
+    "dense_1000000x256_normal_equations_f16": lambda seed=0, m=1_000_000, n=256: dense_problem(
+        m, n, seed, x="normal", y="normal", v=None, z=None, alpha=1.0, beta=0.0,
+        name="dense_1000000x256_normal_equations_f16", x_dtype="f16"),
+    "dense_65536x8192_f16": lambda seed=0, m=65536, n=8192: dense_problem(
+        m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
+        name="dense_65536x8192_f16", x_dtype="f16"),
+    "dense_8192x65536_f16": lambda seed=0, m=8192, n=65536: dense_problem(
+        m, n, seed, x="uniform", y="uniform", v="uniform01", z="uniform", alpha=1.0, beta=1.0,
+        name="dense_8192x65536_f16", x_dtype="f16"),
     # logistic-regression Hessian-vector product: 1% Bernoulli sparsity, values and y ~ N(0, 1),
     # v = p(1 - p) with p = sigmoid(X w), w ~ N(0, 0.1^2), beta 0
     "csr_10000000x1000_logistic_hvp": lambda seed=0, m=10_000_000, n=1000: csr_bernoulli(

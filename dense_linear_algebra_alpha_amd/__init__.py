@@ -47,7 +47,7 @@ __all__ = [
     "xtvxy_csr_f32_analyse", "xtvxy_csr_f32_analysis_destroy", "xtvxy_csr_f32_analysed_plan",
     "xtvxy_csr_f32_analysed_plan_complete", "xtvxy_csr_f32_analysed_workspace_size", "xtvxy_csr_f32_analysed",
     "xtvxy_csr_f32_analysed_ex", "CsrAnalysis", "xtvxy_csr_bf16", "xtvxy_csr_bf16_ex", "xtvxy_csr_bf16_analysed",
-    "xtvxy_csr_bf16_analysed_ex",
+    "xtvxy_csr_bf16_analysed_ex", "xtvxy_dense_f16", "xtvxy_dense_f16_ex",
 ]
 
 load = _abi.load
@@ -130,6 +130,16 @@ def xtvxy_dense_bf16(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspa
 
 def xtvxy_dense_bf16_ex(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force):
     return _abi.call("xtvxy_dense_bf16_ex", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_dense_f16(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream):
+    return _abi.call("xtvxy_dense_f16", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
+                     stream)
+
+
+def xtvxy_dense_f16_ex(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force):
+    return _abi.call("xtvxy_dense_f16_ex", m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes,
                      stream, ctypes.byref(force) if force is not None else None)
 
 
@@ -429,8 +439,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
     """out = alpha X^T (v .* (X y)) + beta z for dense row-major X on the GPU.
 
     X is a 2-D CUDA tensor with unit column stride (row stride = ldx), or a flat buffer with m,
-    n and ldx given; float32, or bf16 storage (torch.bfloat16, or uint16 bit patterns), which
-    takes the xtvxy_dense_bf16 entry points. ``plan`` forces launch parameters."""
+    n and ldx given; float32, bf16 storage (torch.bfloat16, or uint16 bit patterns), which takes
+    the xtvxy_dense_bf16 entry points, or fp16 storage (torch.float16: xtvxy_dense_f16).
+    ``plan`` forces launch parameters."""
     torch = _torch()
     if X.dim() == 2 and m is None:
         m, n = X.shape
@@ -441,8 +452,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
     if m is None or n is None or ldx is None:
         raise ValueError("flat X needs m, n and ldx")
     bf16 = X.dtype in (torch.bfloat16, torch.uint16)
-    if X.dtype != torch.float32 and not bf16:
-        raise ValueError("X must be float32, bfloat16 or uint16 (bf16 bits)")
+    f16 = X.dtype == torch.float16
+    if X.dtype != torch.float32 and not bf16 and not f16:
+        raise ValueError("X must be float32, bfloat16, uint16 (bf16 bits) or float16")
     device = X.device
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
@@ -452,7 +464,7 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
         out = torch.empty(n, dtype=torch.float32, device=device)
     _check_vec("out", out, n, device)
     if plan is None:
-        need = (xtvxy_dense_bf16_workspace_size if bf16 else xtvxy_dense_f32_workspace_size)(m, n, ldx)
+        need = (xtvxy_dense_bf16_workspace_size if bf16 or f16 else xtvxy_dense_f32_workspace_size)(m, n, ldx)
     else:
         need = int(plan.workspace_bytes)
     made_ws = workspace is None
@@ -462,9 +474,9 @@ def dense(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, m=None, n=None
     args = (m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z), out.data_ptr(),
             ws_ptr, ws_bytes, _stream_handle(stream))
     if plan is None:
-        (xtvxy_dense_bf16 if bf16 else xtvxy_dense_f32)(*args)
+        (xtvxy_dense_f16 if f16 else xtvxy_dense_bf16 if bf16 else xtvxy_dense_f32)(*args)
     else:
-        (xtvxy_dense_bf16_ex if bf16 else xtvxy_dense_f32_ex)(*args, plan)
+        (xtvxy_dense_f16_ex if f16 else xtvxy_dense_bf16_ex if bf16 else xtvxy_dense_f32_ex)(*args, plan)
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
@@ -787,6 +799,8 @@ def dense_tune(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=1
     ldx = max(X.stride(0) if m > 1 else n, n, 1)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=X.device)
+    if X.dtype == torch.float16:
+        raise ValueError("the tuner takes float32 or bf16 X (fp16 X takes the bf16 plans)")
     fn = xtvxy_dense_bf16_tune if X.dtype in (torch.bfloat16, torch.uint16) else xtvxy_dense_f32_tune
     return fn(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z),
                                 out.data_ptr(), repeats, _stream_handle(stream)).as_dict()

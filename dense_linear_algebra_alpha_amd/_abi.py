@@ -115,6 +115,9 @@ SIGNATURES = {
     "xtvxy_dense_bf16": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_dense_bf16_ex": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
                             _P(xtvxy_launch_params)],
+    "xtvxy_dense_f16": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_dense_f16_ex": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                            _P(xtvxy_launch_params)],
     "xtvxy_csr_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_csr_f32": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_bf16": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],

@@ -235,7 +235,8 @@ xtvxy_status dense_workspace_query(int64_t m, int64_t n, int64_t ldx, size_t* by
 
 xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
                         const float* y, float beta, const float* z, float* out, void* ws, size_t ws_bytes,
-                        hipStream_t stream, const xtvxy_launch_params* force, int elem_bytes = 4) {
+                        hipStream_t stream, const xtvxy_launch_params* force, int elem_bytes = 4,
+                        bool f16 = false) {
   bool quick = false;
   xtvxy_status st = check_dense(m, n, alpha, X, ldx, v, y, beta, z, out, &quick, elem_bytes);
   if (st != XTVXY_SUCCESS) return st;
@@ -260,6 +261,7 @@ xtvxy_status dense_impl(int64_t m, int64_t n, float alpha, const void* X, int64_
   a.ldx = ldx;
   a.X = X;
   a.elem_bytes = elem_bytes;
+  a.f16 = f16 ? 1 : 0;
   a.v = v;
   a.y = y;
   a.partial = reinterpret_cast<float*>(base + w.partial_off);
@@ -628,6 +630,18 @@ xtvxy_status xtvxy_dense_bf16_ex(int64_t m, int64_t n, float alpha, const uint16
                                  const float* y, float beta, const float* z, float* out, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
   return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force, 2);
+}
+
+xtvxy_status xtvxy_dense_f16(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx, const float* v,
+                             const float* y, float beta, const float* z, float* out, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, nullptr, 2, true);
+}
+
+xtvxy_status xtvxy_dense_f16_ex(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx, const float* v,
+                                const float* y, float beta, const float* z, float* out, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+  return dense_impl(m, n, alpha, X, ldx, v, y, beta, z, out, workspace, workspace_bytes, stream, force, 2, true);
 }
 
 xtvxy_status xtvxy_csr_f32(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,

@@ -365,7 +365,7 @@ hipError_t launch_wave(const DenseArgs& a, const xtvxy_launch_params& p, hipStre
 }
 
 // The wave-row kernel for an element size, chunk width and chunk count (nullptr: none).
-const void* wave_kernel_for(int elem_bytes, int vec, int chunks) {
+const void* wave_kernel_for(int elem_bytes, int vec, int chunks, bool f16 = false) {
 #define XTVXY_WAVE(E, V)                                                                       \
   switch (chunks) {                                                                          \
     case 1: return reinterpret_cast<const void*>(&dense_wave_rows<E, V, 1, 8>);              \
@@ -375,8 +375,10 @@ const void* wave_kernel_for(int elem_bytes, int vec, int chunks) {
   return nullptr;
   if (elem_bytes == 4 && vec == 4) { XTVXY_WAVE(float, 4) }
   if (elem_bytes == 4 && vec == 1) { XTVXY_WAVE(float, 1) }
-  if (elem_bytes == 2 && vec == 8) { XTVXY_WAVE(bf16_t, 8) }
-  if (elem_bytes == 2 && vec == 1) { XTVXY_WAVE(bf16_t, 1) }
+  if (elem_bytes == 2 && vec == 8 && !f16) { XTVXY_WAVE(bf16_t, 8) }
+  if (elem_bytes == 2 && vec == 1 && !f16) { XTVXY_WAVE(bf16_t, 1) }
+  if (elem_bytes == 2 && vec == 8 && f16) { XTVXY_WAVE(f16_t, 8) }
+  if (elem_bytes == 2 && vec == 1 && f16) { XTVXY_WAVE(f16_t, 1) }
 #undef XTVXY_WAVE
   return nullptr;
 }
@@ -387,9 +389,29 @@ const void* block_kernel(bool group) {
                : reinterpret_cast<const void*>(&dense_block_rows<E, VEC, NCH, false>);
 }
 
-// The block/group-row kernel for an element size, chunk width and chunk count (nullptr: none).
-// bf16 chunks of 8 stop at 4 chunks per thread, the same registers as 8 fp32 chunks of 4.
-const void* block_kernel_for(int elem_bytes, int vec, int chunks, bool group) {
+template <class E16>
+const void* block_kernel_16(int vec, int chunks, bool group) {
+  if (vec == 8) {
+    switch (chunks) {
+      case 1: return block_kernel<E16, 8, 1>(group);
+      case 2: return block_kernel<E16, 8, 2>(group);
+      case 4: return block_kernel<E16, 8, 4>(group);
+    }
+  } else if (vec == 1) {
+    switch (chunks) {
+      case 1: return block_kernel<E16, 1, 1>(group);
+      case 2: return block_kernel<E16, 1, 2>(group);
+      case 4: return block_kernel<E16, 1, 4>(group);
+      case 8: return block_kernel<E16, 1, 8>(group);
+    }
+  }
+  return nullptr;
+}
+
+// The block/group-row kernel for an element size (and, for 16-bit elements, bf16 or fp16), chunk
+// width and chunk count (nullptr: none). 16-bit chunks of 8 stop at 4 chunks per thread, the same
+// registers as 8 fp32 chunks of 4.
+const void* block_kernel_for(int elem_bytes, int vec, int chunks, bool group, bool f16 = false) {
   if (elem_bytes == 4 && vec == 4) {
     switch (chunks) {
       case 1: return block_kernel<float, 4, 1>(group);
@@ -404,19 +426,8 @@ const void* block_kernel_for(int elem_bytes, int vec, int chunks, bool group) {
       case 4: return block_kernel<float, 1, 4>(group);
       case 8: return block_kernel<float, 1, 8>(group);
     }
-  } else if (elem_bytes == 2 && vec == 8) {
-    switch (chunks) {
-      case 1: return block_kernel<bf16_t, 8, 1>(group);
-      case 2: return block_kernel<bf16_t, 8, 2>(group);
-      case 4: return block_kernel<bf16_t, 8, 4>(group);
-    }
-  } else if (elem_bytes == 2 && vec == 1) {
-    switch (chunks) {
-      case 1: return block_kernel<bf16_t, 1, 1>(group);
-      case 2: return block_kernel<bf16_t, 1, 2>(group);
-      case 4: return block_kernel<bf16_t, 1, 4>(group);
-      case 8: return block_kernel<bf16_t, 1, 8>(group);
-    }
+  } else if (elem_bytes == 2) {
+    return f16 ? block_kernel_16<f16_t>(vec, chunks, group) : block_kernel_16<bf16_t>(vec, chunks, group);
   }
   return nullptr;
 }
@@ -490,6 +501,8 @@ hipError_t launch_group_ordered(const void* k, unsigned grid, void** params, hip
 
 }  // namespace
 
+// (16-bit elements: the bf16 kernels stand for the fp16 ones, which differ only in the conversion
+// at each use; their register counts differ by one at most, which leaves the residency unchanged.)
 int dense_resident_per_cu(const xtvxy_launch_params& p, int elem_bytes) {
   const void* k = p.kernel == XTVXY_DENSE_WAVE_ROWS ? wave_kernel_for(elem_bytes, p.vec, p.chunks)
                                                     : block_kernel_for(elem_bytes, p.vec, p.chunks,
@@ -509,11 +522,11 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
     case XTVXY_DENSE_WAVE_ROWS:
       if (a.elem_bytes == 4 && p.vec == 4) return launch_wave<float, 4>(a, p, s);
       if (a.elem_bytes == 4 && p.vec == 1) return launch_wave<float, 1>(a, p, s);
-      if (a.elem_bytes == 2 && p.vec == 8) return launch_wave<bf16_t, 8>(a, p, s);
-      if (a.elem_bytes == 2 && p.vec == 1) return launch_wave<bf16_t, 1>(a, p, s);
+      if (a.elem_bytes == 2 && p.vec == 8) return a.f16 ? launch_wave<f16_t, 8>(a, p, s) : launch_wave<bf16_t, 8>(a, p, s);
+      if (a.elem_bytes == 2 && p.vec == 1) return a.f16 ? launch_wave<f16_t, 1>(a, p, s) : launch_wave<bf16_t, 1>(a, p, s);
       return hipErrorInvalidValue;
     case XTVXY_DENSE_BLOCK_ROWS: {
-      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, false);
+      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, false, a.f16 != 0);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;
       void* params[] = {&args};
@@ -521,7 +534,7 @@ hipError_t launch_dense(const DenseArgs& a, const xtvxy_launch_params& p, hipStr
     }
     case XTVXY_DENSE_GROUP_ROWS: {
       if (p.group < 1 || p.group > kGroupMaxMembers) return hipErrorInvalidValue;
-      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, true);
+      const void* k = block_kernel_for(a.elem_bytes, p.vec, p.chunks, true, a.f16 != 0);
       if (!k) return hipErrorInvalidValue;
       DenseArgs args = a;
       void* params[] = {&args};

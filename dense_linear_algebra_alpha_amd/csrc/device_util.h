@@ -210,9 +210,29 @@ struct XChunk<bf16_t, 1> {
   __device__ __forceinline__ float get(int) const { return bf16_lo(w); }
 };
 
-// Chunk of row `xr` from column `col` when `ok`, else zeros. fp32 rows take load_chunk; bf16 rows
-// take one 16-byte load of 8 elements (VEC == 8: the caller guarantees 16-byte alignment and
-// n % 8 == 0) or one 2-byte load (VEC == 1). Clamped address, unconditional non-temporal load,
+// fp16 storage of X: IEEE binary16, kept packed like bf16 and widened exactly (every fp16 value,
+// subnormals, infinities and NaN included, is an fp32 value) by a conversion at each use.
+typedef _Float16 f16_t;
+__device__ __forceinline__ float f16_lo(unsigned int w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(unsigned int w) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16));
+}
+template <>
+struct XChunk<f16_t, 8> {
+  unsigned int w[4];
+  __device__ __forceinline__ float get(int k) const { return (k & 1) ? f16_hi(w[k >> 1]) : f16_lo(w[k >> 1]); }
+};
+template <>
+struct XChunk<f16_t, 1> {
+  unsigned int w;
+  __device__ __forceinline__ float get(int) const { return f16_lo(w); }
+};
+
+// Chunk of row `xr` from column `col` when `ok`, else zeros. fp32 rows take load_chunk; bf16 and
+// fp16 rows take one 16-byte load of 8 elements (VEC == 8: the caller guarantees 16-byte
+// alignment and n % 8 == 0) or one 2-byte load (VEC == 1). Clamped address, unconditional non-temporal load,
 // as in load_chunk.
 template <class E, int VEC>
 __device__ __forceinline__ void load_x(const E* __restrict__ xr, int64_t col, bool ok, XChunk<E, VEC>& o) {
@@ -227,7 +247,7 @@ __device__ __forceinline__ void load_x(const E* __restrict__ xr, int64_t col, bo
       o.w[2] = ok ? t.z : 0u;
       o.w[3] = ok ? t.w : 0u;
     } else {
-      static_assert(VEC == 1, "bf16 rows load 8 or 1 elements");
+      static_assert(VEC == 1, "16-bit rows load 8 or 1 elements");
       const unsigned int h = __builtin_nontemporal_load(reinterpret_cast<const unsigned short*>(xr + c));
       o.w = ok ? h : 0u;
     }

@@ -80,8 +80,9 @@ inline size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a
 // Arguments of the dense fused kernels.
 struct DenseArgs {
   int64_t m, n, ldx;
-  const void* X;      // fp32 or bf16 elements (elem_bytes 4 or 2)
+  const void* X;      // fp32 or 16-bit elements (elem_bytes 4 or 2)
   int32_t elem_bytes;
+  int32_t f16;        // 16-bit elements are fp16 (1) or bf16 (0)
   const float* v;     // nullptr: v = 1
   const float* y;
   float* partial;     // [rows of partials][n] fp32

@@ -222,6 +222,17 @@ xtvxy_status xtvxy_dense_bf16(int64_t m, int64_t n, float alpha, const uint16_t 
 xtvxy_status xtvxy_dense_bf16_ex(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx, const float *v,
                                  const float *y, float beta, const float *z, float *out, void *workspace,
                                  size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params *force);
+/* The same with X held as IEEE fp16 (binary16 bit patterns, uint16_t; every fp16 value widens to
+ * fp32 exactly, subnormals, infinities and NaN included): all arithmetic fp32, the result that of
+ * xtvxy_dense_f32 on the widened matrix up to rounding order. Plans, workspace sizes and every rule
+ * are those of the bf16 entry points (the same 2 bytes per element): use
+ * xtvxy_dense_bf16_plan, _plan_complete and _workspace_size. */
+xtvxy_status xtvxy_dense_f16(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx, const float *v,
+                             const float *y, float beta, const float *z, float *out, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+xtvxy_status xtvxy_dense_f16_ex(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx, const float *v,
+                                const float *y, float beta, const float *z, float *out, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream, const xtvxy_launch_params *force);
 
 /* Workspace bytes xtvxy_csr_f32 needs for this shape on the current device. */
 xtvxy_status xtvxy_csr_f32_workspace_size(int64_t m, int64_t n, int64_t nnz, size_t *bytes);

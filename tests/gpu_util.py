@@ -38,8 +38,10 @@ def to_dev(a):
 
 
 def dense_oracle(p):
-    ref = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
-    bnd = oracle.dense(p.X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
+    # fp16 X goes to the oracle widened by numpy (exact); bf16 and fp32 X as stored
+    X = p.X.astype(np.float32) if getattr(p, "x_dtype", "f32") == "f16" else p.X
+    ref = oracle.dense(X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx)
+    bnd = oracle.dense(X, p.y, p.v, p.z, p.alpha, p.beta, m=p.m, n=p.n, ldx=p.ldx, bound=True)
     return ref, bnd
 
 

@@ -119,3 +119,25 @@ def test_bf16_rounding():
     p = datagen.dense_problem(20, 8, seed=3, x_dtype="bf16", ldx=9)
     q = datagen.dense_problem(20, 8, seed=3, ldx=9)
     assert p.X.dtype == np.uint16 and np.array_equal(p.X, datagen.to_bf16(q.X))
+
+
+def test_f16_storage_rounds_to_nearest_even_and_widens_exactly():
+    # the generator rounds the fp32 draw to IEEE fp16 once; the bit patterns below are fixed by the
+    # binary16 format: signed zeros, the smallest and largest subnormals, the smallest normal, 1,
+    # -2, the largest finite value and the infinities
+    bits = np.array([0x0000, 0x8000, 0x0001, 0x03FF, 0x0400, 0x3C00, 0xC000, 0x7BFF, 0x7C00, 0xFC00], np.uint16)
+    want = np.array([0.0, -0.0, 2.0 ** -24, 1023 * 2.0 ** -24, 2.0 ** -14, 1.0, -2.0, 65504.0, np.inf, -np.inf],
+                    np.float32)
+    p = datagen.DenseProblem(1, 10, 10, bits.view(np.float16), np.zeros(10, np.float32), None, None, 1.0, 0.0,
+                             "f16 patterns", "f16")
+    got = p.X_f32()
+    assert got.dtype == np.float32 and np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+    # ties to even: 1 + 2^-11 lies halfway between 1 and 1 + 2^-10, 1 + 3 * 2^-11 between 1 + 2^-10 and 1 + 2^-9
+    x = np.array([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1 + 2.0 ** -12], np.float32)
+    assert np.array_equal(x.astype(np.float16).astype(np.float32),
+                          np.array([1.0, 1 + 2.0 ** -9, 1.0], np.float32))
+    q = datagen.dense_problem(20, 8, seed=3, x_dtype="f16", ldx=9)
+    r = datagen.dense_problem(20, 8, seed=3, x_dtype="f32", ldx=9)
+    assert q.X.dtype == np.float16
+    assert np.array_equal(q.X2d().astype(np.float32), r.X2d().astype(np.float16).astype(np.float32))
