@@ -262,12 +262,12 @@ def scatter_probe(args):
 LOGREG_METRIC = "Newton-CG logistic regression: ms per Newton iteration (fixed schedule), fused vs unfused products"
 
 
-def logreg_iteration_bytes(m, n, nnz, J, trials) -> int:
+def logreg_iteration_bytes(m, n, nnz, J, trials, value_bytes=4) -> int:
     """Algorithmic bytes of one Newton step with J CG iterations and `trials` line-search trials:
     the link pass (read t, X s, labels; write t, u, v), the gradient X^T u + lambda w, J
     Hessian-vector products, X s, and the trials (read t, X s, labels). The n-vector algebra
-    is left out (n << m)."""
-    rows = 4 * (m + 1) + 8 * nnz
+    is left out (n << m). A stored entry is a 4-byte column index and a value of value_bytes."""
+    rows = 4 * (m + 1) + (4 + value_bytes) * nnz
     link = 24 * m
     grad = rows + 4 * m + 12 * n
     hvp = rows + 4 * m + 12 * n
@@ -279,7 +279,9 @@ def bench_logreg(args):
     """The Newton-CG solver on its workload: a fixed schedule (K Newton steps of J CG iterations,
     grad_tol 0) timed for both engines, a run to |g| <= 1e-4 |g_0| for both, the Hessian-vector
     kernel's roofline at the solver's final curvature weights, and the oracle's time for one step
-    of the same schedule on the host cores."""
+    of the same schedule on the host cores. With bf16 values the fused engine runs on them and the
+    comparisons (the fused engine on the values widened to fp32, and the unfused engines, which
+    take fp32 only) on the widened values."""
     import numpy as np
     import torch
 
@@ -291,10 +293,15 @@ def bench_logreg(args):
     torch.cuda.set_device(dev)
     P = datagen.LOGISTIC_WORKLOADS[args.workload](seed=args.seed)
     X = P.X
-    rp, ci, vals = (torch.from_numpy(a).to(dev) for a in (X.row_ptr, X.col_idx, X.values))
+    bf16 = X.values_dtype == "bf16"
+    vb = 2 if bf16 else 4
+    rp, ci = (torch.from_numpy(a).to(dev) for a in (X.row_ptr, X.col_idx))
+    vals = (torch.from_numpy(X.values.view(np.int16)).view(torch.bfloat16) if bf16
+            else torch.from_numpy(X.values)).to(dev)
+    vals32 = torch.from_numpy(X.values_f32()).to(dev) if bf16 else vals
     lab = torch.from_numpy(P.labels).to(dev)
-    plans = {"unfused": xt.CsrUnfusedPlan(rp, ci, vals, X.n),
-             "unfused_explicit_transpose": xt.CsrUnfusedPlan(rp, ci, vals, X.n, explicit_transpose=True)}
+    plans = {"unfused": xt.CsrUnfusedPlan(rp, ci, vals32, X.n),
+             "unfused_explicit_transpose": xt.CsrUnfusedPlan(rp, ci, vals32, X.n, explicit_transpose=True)}
     ws = torch.empty(xt.xtvxy_logreg_newton_cg_f32_workspace_size(X.m, X.n, X.nnz), dtype=torch.uint8, device=dev)
     K, J = args.newton_steps, args.cg_steps
 
@@ -302,15 +309,17 @@ def bench_logreg(args):
         w = torch.zeros(X.n, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        w, rep, hist = xt.logreg_newton_cg(rp, ci, vals, X.n, lab, P.lam, w,
-                                           engine="fused" if engine == "fused" else "unfused",
+        fused = engine.startswith("fused")
+        w, rep, hist = xt.logreg_newton_cg(rp, ci, vals if engine == "fused" else vals32, X.n, lab, P.lam, w,
+                                           engine="fused" if fused else "unfused",
                                            unfused_plan=plans.get(engine), workspace=ws, **kw)
         torch.cuda.synchronize()
         return time.perf_counter() - t0, w, rep, hist
 
     fixed = dict(grad_tol=0.0, max_newton=K, max_cg=J, fixed_cg=True)
     results = {}
-    for engine in ("fused", "unfused", "unfused_explicit_transpose"):
+    engines = ("fused",) + (("fused_f32_values",) if bf16 else ()) + ("unfused", "unfused_explicit_transpose")
+    for engine in engines:
         for _ in range(args.warmup_solves):
             solve(engine, **fixed)
         runs = [solve(engine, **fixed) for _ in range(args.solves)]
@@ -324,7 +333,7 @@ def bench_logreg(args):
                                        "loss": conv[2]["loss"]}}
     fz = results["fused"]
     trials = fz["line_search_trials"] / K
-    ibytes = logreg_iteration_bytes(X.m, X.n, X.nnz, J, trials)
+    ibytes = logreg_iteration_bytes(X.m, X.n, X.nnz, J, trials, vb)
     # the Hessian-vector kernel alone, with the generator's curvature weights p(1 - p) of the planted
     # model and the generator's y as the direction
     v = torch.from_numpy(X.v).to(dev)
@@ -337,20 +346,21 @@ def bench_logreg(args):
     sh = torch.cuda.current_stream().cuda_stream or None
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    hvp = xt.xtvxy_csr_bf16_ex if bf16 else xt.xtvxy_csr_f32_ex
     for _ in range(args.warmup):
-        xt.xtvxy_csr_f32_ex(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
-                            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
+        hvp(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
     for i in range(args.steps):
         xt.xtvxy_set_kernel_timing_events(pairs[i][0], pairs[i][1])
-        xt.xtvxy_csr_f32_ex(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
-                            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
+        hvp(X.m, X.n, X.nnz, 1.0, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(), v.data_ptr(),
+            d.data_ptr(), P.lam, d.data_ptr(), q.data_ptr(), hws.data_ptr(), hws_bytes, sh, hplan)
     torch.cuda.synchronize()
     xt.xtvxy_set_kernel_timing_events(None, None)
     kernel_ms = [ev.elapsed_ms(a, b) for a, b in pairs]
     for a, b in pairs:
         ev.destroy(a)
         ev.destroy(b)
-    hvp_bytes = 8 * X.nnz + 4 * (X.m + 1) + 4 * X.m + 12 * X.n
+    hvp_bytes = (4 + vb) * X.nnz + 4 * (X.m + 1) + 4 * X.m + 12 * X.n
     achieved = hvp_bytes / (statistics.mean(kernel_ms) / 1e3) / 1e9
     iter_s = fz["ms_per_newton_iteration"] / 1e3
     record = {
@@ -367,10 +377,14 @@ def bench_logreg(args):
         "dtype": "f32",
         "data": "synthetic (seeded generators, seed %d): labels of a planted model" % args.seed,
         "config": {"workload": args.workload, "m": X.m, "n": X.n, "nnz": X.nnz, "lambda": P.lam,
+                   "values_storage": "bf16" if bf16 else "f32",
                    "schedule": "%d Newton steps x %d CG iterations, grad_tol 0" % (K, J),
                    "iteration_algorithmic_bytes": int(ibytes)},
         "iteration_effective_gbs": round(ibytes / iter_s / 1e9, 3),
         "fused": fz,
+        **({"fused_f32_values": results["fused_f32_values"],
+            "speedup_vs_fused_f32_values": round(results["fused_f32_values"]["ms_per_newton_iteration"] /
+                                                 fz["ms_per_newton_iteration"], 3)} if bf16 else {}),
         "unfused": results["unfused"],
         "unfused_explicit_transpose": results["unfused_explicit_transpose"],
         "speedup_vs_unfused": round(results["unfused"]["ms_per_newton_iteration"] / fz["ms_per_newton_iteration"], 3),
@@ -388,8 +402,8 @@ def bench_logreg(args):
         import oracle.logreg as lr
         threads = oracle.set_threads(len(os.sched_getaffinity(0)))
         t0 = time.perf_counter()
-        lr.newton_cg(X.row_ptr, X.col_idx, X.values, X.n, P.labels, P.lam, max_newton=1, max_cg=J, fixed_cg=True,
-                     grad_tol=0.0)
+        lr.newton_cg(X.row_ptr, X.col_idx, X.values_f32(), X.n, P.labels, P.lam, max_newton=1, max_cg=J,
+                     fixed_cg=True, grad_tol=0.0)
         cpu_s = time.perf_counter() - t0
         record["cpu_baseline"] = {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
                                   "sample": "one Newton step of the same schedule on the full workload (fp64 "

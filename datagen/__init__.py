@@ -328,9 +328,19 @@ def csr_from_dense(X2d: np.ndarray):
 
 # Newton-CG for L2-regularised logistic regression on the 10,000,000 x 1000 Hessian-vector workload's
 # generator: 1% Bernoulli sparsity, N(0, 1) values, labels of the planted w ~ N(0, 0.1^2), lambda 1.
+def logistic_values_bf16(P: LogisticProblem, name: str = "") -> LogisticProblem:
+    """The same problem (same labels) with X's values rounded to bf16 (csr_values_bf16)."""
+    name = name or P.name + "_bf16"
+    return LogisticProblem(csr_values_bf16(P.X, name), P.labels, P.lam, name)
+
+
 LOGISTIC_WORKLOADS = {
     "logreg_csr_10000000x1000": lambda seed=0, m=10_000_000, n=1000, lam=1.0: logistic_problem(
         m, n, 0.01, seed, lam=lam, w_std=0.1, name="logreg_csr_10000000x1000"),
+    # the same problem, its values stored as bf16 (the labels are those of the fp32 values)
+    "logreg_csr_10000000x1000_bf16": lambda seed=0, m=10_000_000, n=1000, lam=1.0: logistic_values_bf16(
+        logistic_problem(m, n, 0.01, seed, lam=lam, w_std=0.1, name="logreg_csr_10000000x1000"),
+        "logreg_csr_10000000x1000_bf16"),
 }
 
 # The measured workloads, named by what they are. Each entry builds the full-size

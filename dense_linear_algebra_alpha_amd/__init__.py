@@ -47,7 +47,8 @@ __all__ = [
     "xtvxy_csr_f32_analyse", "xtvxy_csr_f32_analysis_destroy", "xtvxy_csr_f32_analysed_plan",
     "xtvxy_csr_f32_analysed_plan_complete", "xtvxy_csr_f32_analysed_workspace_size", "xtvxy_csr_f32_analysed",
     "xtvxy_csr_f32_analysed_ex", "CsrAnalysis", "xtvxy_csr_bf16", "xtvxy_csr_bf16_ex", "xtvxy_csr_bf16_analysed",
-    "xtvxy_csr_bf16_analysed_ex", "xtvxy_dense_f16", "xtvxy_dense_f16_ex",
+    "xtvxy_csr_bf16_analysed_ex", "xtvxy_dense_f16", "xtvxy_dense_f16_ex", "xtvxy_csr_bf16_rowdot",
+    "xtvxy_csr_bf16_rowdot_ex", "xtvxy_csr_bf16_tmv", "xtvxy_csr_bf16_tmv_ex", "xtvxy_logreg_newton_cg_bf16",
 ]
 
 load = _abi.load
@@ -233,6 +234,27 @@ def xtvxy_csr_f32_tmv_ex(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z,
                      workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
 
 
+def xtvxy_csr_bf16_rowdot(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream):
+    return _abi.call("xtvxy_csr_bf16_rowdot", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream)
+
+
+def xtvxy_csr_bf16_rowdot_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, force):
+    return _abi.call("xtvxy_csr_bf16_rowdot_ex", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t,
+                     stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_csr_bf16_tmv(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes,
+                       stream):
+    return _abi.call("xtvxy_csr_bf16_tmv", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace,
+                     workspace_bytes, stream)
+
+
+def xtvxy_csr_bf16_tmv_ex(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes,
+                          stream, force):
+    return _abi.call("xtvxy_csr_bf16_tmv_ex", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out,
+                     workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
 def xtvxy_csr_f32_analyse(m, n, nnz, row_ptr, col_idx, stream) -> int:
     h = ctypes.c_void_p()
     _abi.call("xtvxy_csr_f32_analyse", m, n, nnz, row_ptr, col_idx, stream, ctypes.byref(h))
@@ -375,6 +397,13 @@ def xtvxy_logreg_newton_cg_f32(m, n, nnz, row_ptr, col_idx, values, labels, w, o
                                workspace_bytes, stream, report, history, history_rows):
     return _abi.call("xtvxy_logreg_newton_cg_f32", m, n, nnz, row_ptr, col_idx, values, labels, w,
                      ctypes.byref(opt), unfused, workspace, workspace_bytes, stream,
+                     ctypes.byref(report) if report is not None else None, history, history_rows)
+
+
+def xtvxy_logreg_newton_cg_bf16(m, n, nnz, row_ptr, col_idx, values, labels, w, opt, workspace, workspace_bytes,
+                                stream, report, history, history_rows):
+    return _abi.call("xtvxy_logreg_newton_cg_bf16", m, n, nnz, row_ptr, col_idx, values, labels, w,
+                     ctypes.byref(opt), workspace, workspace_bytes, stream,
                      ctypes.byref(report) if report is not None else None, history, history_rows)
 
 
@@ -533,11 +562,17 @@ def csr_tensor(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None
     return csr(rp, ci, vals, X.shape[1], y, v, z, alpha, beta, out, plan=plan, workspace=workspace, stream=stream)
 
 
-def _check_csr_arrays(row_ptr, col_idx, values):
+def _is_bf16(values) -> bool:
+    torch = _torch()
+    return values.dtype in (torch.bfloat16, torch.uint16)
+
+
+def _check_csr_arrays(row_ptr, col_idx, values, bf16_ok=False):
     torch = _torch()
     device = row_ptr.device
+    vdt = values.dtype if bf16_ok and _is_bf16(values) else torch.float32
     for name, t, dt in (("row_ptr", row_ptr, torch.int32), ("col_idx", col_idx, torch.int32),
-                        ("values", values, torch.float32)):
+                        ("values", values, vdt)):
         if t.dtype != dt or t.device != device or not t.is_contiguous():
             raise ValueError("%s must be a contiguous %s tensor on %s" % (name, dt, device))
     if values.numel() != col_idx.numel():
@@ -547,9 +582,11 @@ def _check_csr_arrays(row_ptr, col_idx, values):
 
 def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=0.0, out=None, *, plan=None,
                stream=None):
-    """t = alpha v .* (X y) + beta t0 (the first half of the pattern) for CSR X; returns t."""
+    """t = alpha v .* (X y) + beta t0 (the first half of the pattern) for CSR X; returns t. bf16
+    values (torch.bfloat16, or uint16 bit patterns) take xtvxy_csr_bf16_rowdot."""
     torch = _torch()
-    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values, bf16_ok=True)
+    bf16 = _is_bf16(values)
     _check_vec("y", y, n, device)
     _check_vec("v", v, m, device, required=False)
     _check_vec("t0", t0, m, device, required=beta != 0)
@@ -561,18 +598,20 @@ def csr_rowdot(row_ptr, col_idx, values, n, y, v=None, t0=None, alpha=1.0, beta=
             _ptr(values) if nnz else None, _ptr(v), y.data_ptr(), float(beta), _ptr(t0), out.data_ptr(),
             _stream_handle(stream))
     if plan is None:
-        xtvxy_csr_f32_rowdot(*args)
+        (xtvxy_csr_bf16_rowdot if bf16 else xtvxy_csr_f32_rowdot)(*args)
     else:
-        xtvxy_csr_f32_rowdot_ex(*args, plan)
+        (xtvxy_csr_bf16_rowdot_ex if bf16 else xtvxy_csr_f32_rowdot_ex)(*args, plan)
     _keep_for_stream(stream, out if made_out else None)
     return out
 
 
 def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, out=None, *, plan=None, workspace=None,
             stream=None):
-    """out = alpha X^T u + beta z (the second half of the pattern) for CSR X; returns out."""
+    """out = alpha X^T u + beta z (the second half of the pattern) for CSR X; returns out. bf16
+    values (torch.bfloat16, or uint16 bit patterns) take xtvxy_csr_bf16_tmv."""
     torch = _torch()
-    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values, bf16_ok=True)
+    bf16 = _is_bf16(values)
     _check_vec("u", u, m, device)
     _check_vec("z", z, n, device, required=beta != 0)
     made_out = out is None
@@ -588,9 +627,9 @@ def csr_tmv(row_ptr, col_idx, values, n, u, z=None, alpha=1.0, beta=0.0, out=Non
             _ptr(values) if nnz else None, u.data_ptr(), float(beta), _ptr(z), out.data_ptr(), ws_ptr, ws_bytes,
             _stream_handle(stream))
     if plan is None:
-        xtvxy_csr_f32_tmv(*args)
+        (xtvxy_csr_bf16_tmv if bf16 else xtvxy_csr_f32_tmv)(*args)
     else:
-        xtvxy_csr_f32_tmv_ex(*args, plan)
+        (xtvxy_csr_bf16_tmv_ex if bf16 else xtvxy_csr_f32_tmv_ex)(*args, plan)
     _keep_for_stream(stream, out if made_out else None, workspace if made_ws else None)
     return out
 
@@ -758,15 +797,19 @@ def logreg_newton_cg(row_ptr, col_idx, values, n, labels, lam, w=None, *, max_ne
     ``w`` (float32 CUDA tensor of n elements) is the start point and is overwritten with the
     result; None starts from zeros. ``engine`` is "fused" (this library's products) or "unfused"
     (rocSPARSE through ``unfused_plan``, a CsrUnfusedPlan of the same tensors; made here when
-    None). Returns (w, report dict, history list of per-iterate dicts)."""
+    None). bf16 values (torch.bfloat16, or uint16 bit patterns) take xtvxy_logreg_newton_cg_bf16,
+    which runs the fused engine only. Returns (w, report dict, history list of per-iterate dicts)."""
     torch = _torch()
-    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values, bf16_ok=True)
+    bf16 = _is_bf16(values)
     _check_vec("labels", labels, m, device)
     if w is None:
         w = torch.zeros(n, dtype=torch.float32, device=device)
     _check_vec("w", w, n, device)
     if engine not in ("fused", "unfused"):
         raise ValueError("engine must be 'fused' or 'unfused'")
+    if bf16 and engine != "fused":
+        raise ValueError("bf16 values run the fused engine only")
     plan_handle = None
     if engine == "unfused":
         if unfused_plan is None:
@@ -781,10 +824,13 @@ def logreg_newton_cg(row_ptr, col_idx, values, n, labels, lam, w=None, *, max_ne
     rows = int(max_newton) + 1
     hist = (ctypes.c_double * (rows * len(_HISTORY_KEYS)))()
     rep = xtvxy_logreg_report()
-    xtvxy_logreg_newton_cg_f32(m, n, nnz, row_ptr.data_ptr(), _ptr(col_idx) if nnz else None,
-                               _ptr(values) if nnz else None, _ptr(labels) if m else None, _ptr(w) if n else None,
-                               opt, plan_handle, workspace.data_ptr(), workspace.numel(), _stream_handle(stream),
-                               rep, hist, rows)
+    mats = (m, n, nnz, row_ptr.data_ptr(), _ptr(col_idx) if nnz else None, _ptr(values) if nnz else None,
+            _ptr(labels) if m else None, _ptr(w) if n else None, opt)
+    tail = (workspace.data_ptr(), workspace.numel(), _stream_handle(stream), rep, hist, rows)
+    if bf16:
+        xtvxy_logreg_newton_cg_bf16(*mats, *tail)
+    else:
+        xtvxy_logreg_newton_cg_f32(*mats, plan_handle, *tail)
     history = []
     for k in range(min(rows, rep.newton_iterations + 1)):
         row = {key: hist[k * len(_HISTORY_KEYS) + i] for i, key in enumerate(_HISTORY_KEYS)}

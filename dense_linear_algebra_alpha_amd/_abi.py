@@ -131,6 +131,12 @@ SIGNATURES = {
     "xtvxy_csr_f32_tmv": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_f32_tmv_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
                              _P(xtvxy_launch_params)],
+    "xtvxy_csr_bf16_rowdot": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp],
+    "xtvxy_csr_bf16_rowdot_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp,
+                                 _P(xtvxy_launch_params)],
+    "xtvxy_csr_bf16_tmv": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
+    "xtvxy_csr_bf16_tmv_ex": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp,
+                              _P(xtvxy_launch_params)],
     "xtvxy_csr_check": [_i64, _i64, _i64, _vp, _vp, _vp, _vp],
     "xtvxy_dense_f32_unfused_reference_workspace_size": [_i64, _i64, _P(_sz)],
     "xtvxy_dense_f32_unfused_reference": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
@@ -169,6 +175,8 @@ SIGNATURES = {
     "xtvxy_logreg_newton_cg_f32_workspace_size": [_i64, _i64, _i64, _P(_sz)],
     "xtvxy_logreg_newton_cg_f32": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _P(xtvxy_logreg_options), _vp, _vp,
                                    _sz, _vp, _P(xtvxy_logreg_report), _P(ctypes.c_double), _i64],
+    "xtvxy_logreg_newton_cg_bf16": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _P(xtvxy_logreg_options), _vp, _sz,
+                                    _vp, _P(xtvxy_logreg_report), _P(ctypes.c_double), _i64],
 }
 
 _lib = None

@@ -293,7 +293,7 @@ xtvxy_status csr_run(int mode, int64_t m, int64_t n, int64_t nnz, float alpha, c
                      const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
                      const float* z, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
                      const xtvxy_launch_params* force, const CsrExtras* extras = nullptr, int value_bytes = 4) {
-  if (value_bytes != 4 && (value_bytes != 2 || mode != kCsrFused)) return XTVXY_ERROR_INVALID_VALUE;
+  if (value_bytes != 4 && value_bytes != 2) return XTVXY_ERROR_INVALID_VALUE;
   xtvxy_device_info d;
   xtvxy_status st = device_info(-1, &d);
   if (st != XTVXY_SUCCESS) return st;
@@ -403,8 +403,9 @@ xtvxy_status csr_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
 
 // out = alpha X^T u + beta z (the second half of the pattern alone).
 xtvxy_status tmv_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                      const int32_t* col_idx, const float* values, const float* u, float beta, const float* z,
-                      float* out, void* ws, size_t ws_bytes, hipStream_t stream, const xtvxy_launch_params* force) {
+                      const int32_t* col_idx, const void* values, const float* u, float beta, const float* z,
+                      float* out, void* ws, size_t ws_bytes, hipStream_t stream, const xtvxy_launch_params* force,
+                      int value_bytes = 4) {
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
   if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   if (n == 0) return XTVXY_SUCCESS;
@@ -415,19 +416,20 @@ xtvxy_status tmv_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int3
   if (reads_x) {
     if (!row_ptr || !col_idx || !values || !u) return XTVXY_ERROR_NULL_POINTER;
     if (overlap(out, nb, row_ptr, (size_t)(m + 1) * 4) || overlap(out, nb, col_idx, (size_t)nnz * 4) ||
-        overlap(out, nb, values, (size_t)nnz * 4) || overlap(out, nb, u, (size_t)m * sizeof(float)))
+        overlap(out, nb, values, (size_t)nnz * (size_t)value_bytes) || overlap(out, nb, u, (size_t)m * sizeof(float)))
       return XTVXY_ERROR_ALIASING;
   }
   if (beta != 0.0f && z != out && overlap(out, nb, z, nb)) return XTVXY_ERROR_ALIASING;
   if (!reads_x) return launch_status(launch_beta_only(n, beta, z, out, stream));
   return csr_run(kCsrTmv, m, n, nnz, alpha, row_ptr, col_idx, values, u, nullptr, beta, z, out, ws, ws_bytes,
-                 stream, force);
+                 stream, force, nullptr, value_bytes);
 }
 
 // t = alpha v .* (X y) + beta t0 (the first half of the pattern alone); needs no workspace.
 xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                         const int32_t* col_idx, const float* values, const float* v, const float* y, float beta,
-                         const float* t0, float* t, hipStream_t stream, const xtvxy_launch_params* force) {
+                         const int32_t* col_idx, const void* values, const float* v, const float* y, float beta,
+                         const float* t0, float* t, hipStream_t stream, const xtvxy_launch_params* force,
+                         int value_bytes = 4) {
   if (m < 0 || n < 0 || nnz < 0) return XTVXY_ERROR_INVALID_VALUE;
   if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   if (m == 0) return XTVXY_SUCCESS;
@@ -438,7 +440,7 @@ xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const i
   if (reads_x) {
     if (!row_ptr || !col_idx || !values || !y) return XTVXY_ERROR_NULL_POINTER;
     if (overlap(t, mb, row_ptr, (size_t)(m + 1) * 4) || overlap(t, mb, col_idx, (size_t)nnz * 4) ||
-        overlap(t, mb, values, (size_t)nnz * 4) || overlap(t, mb, y, (size_t)n * sizeof(float)) ||
+        overlap(t, mb, values, (size_t)nnz * (size_t)value_bytes) || overlap(t, mb, y, (size_t)n * sizeof(float)) ||
         (v && overlap(t, mb, v, mb)))
       return XTVXY_ERROR_ALIASING;
   }
@@ -463,12 +465,13 @@ xtvxy_status rowdot_impl(int64_t m, int64_t n, int64_t nnz, float alpha, const i
   a.row_ptr = row_ptr;
   a.col_idx = col_idx;
   a.values = values;
-  a.value_bytes = 4;
+  a.value_bytes = value_bytes;
   a.v = v;
   a.y = y;
   a.lds_window = 0;
   a.y_window = plan.y_window;
-  a.aligned = reinterpret_cast<uintptr_t>(values) % 16 == 0 && reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
+  a.aligned = reinterpret_cast<uintptr_t>(values) % (uintptr_t)(4 * value_bytes) == 0 &&
+              reinterpret_cast<uintptr_t>(col_idx) % 16 == 0;
   a.alpha = alpha;
   a.beta = beta;
   a.t0 = t0;
@@ -674,6 +677,35 @@ xtvxy_status xtvxy_csr_bf16_ex(int64_t m, int64_t n, int64_t nnz, float alpha, c
                                hipStream_t stream, const xtvxy_launch_params* force) {
   return csr_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, workspace, workspace_bytes,
                   stream, force, 2);
+}
+
+xtvxy_status xtvxy_csr_bf16_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                   const int32_t* col_idx, const uint16_t* values, const float* v, const float* y,
+                                   float beta, const float* t0, float* t, hipStream_t stream) {
+  return rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, nullptr, 2);
+}
+
+xtvxy_status xtvxy_csr_bf16_rowdot_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                      const int32_t* col_idx, const uint16_t* values, const float* v, const float* y,
+                                      float beta, const float* t0, float* t, hipStream_t stream,
+                                      const xtvxy_launch_params* force) {
+  return rowdot_impl(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, t0, t, stream, force, 2);
+}
+
+xtvxy_status xtvxy_csr_bf16_tmv(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                const int32_t* col_idx, const uint16_t* values, const float* u, float beta,
+                                const float* z, float* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes, stream,
+                  nullptr, 2);
+}
+
+xtvxy_status xtvxy_csr_bf16_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                   const int32_t* col_idx, const uint16_t* values, const float* u, float beta,
+                                   const float* z, float* out, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream, const xtvxy_launch_params* force) {
+  return tmv_impl(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out, workspace, workspace_bytes, stream,
+                  force, 2);
 }
 
 xtvxy_status xtvxy_csr_f32_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,

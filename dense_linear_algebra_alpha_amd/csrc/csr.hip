@@ -657,6 +657,34 @@ hipError_t launch_cold(const CsrArgs& a, const xtvxy_launch_params& p, hipStream
   }
 }
 
+// The launch for a mode (the whole pattern or one half) and stored value type, for checked
+// arguments and binning buffers.
+template <class VT>
+hipError_t launch_modes(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode) {
+  const bool binned = a.bins > 0;
+  if (mode == kCsrRowdot) {
+    // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
+    if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))
+      return hipErrorInvalidValue;
+    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeRowdot, VT>(a, p, s);
+    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeRowdot, VT>(a, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
+  if (mode == kCsrTmv) {
+    if (a.v == nullptr) return hipErrorInvalidValue;  // u
+    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeTmv, VT>(a, p, s);
+    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeTmv, VT>(a, p, s);
+    return hipErrorInvalidValue;
+  }
+  if (mode != kCsrFused) return hipErrorInvalidValue;
+  // (threads, entries per thread): 256 x 4, 256 x 8 and 512 x 8
+  if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4, kModeFused, VT>(a, p, s);
+  if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeFused, VT>(a, p, s);
+  if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeFused, VT>(a, p, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_t s, int mode) {
@@ -668,35 +696,9 @@ hipError_t launch_csr(const CsrArgs& a, const xtvxy_launch_params& p, hipStream_
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
-  if (a.value_bytes == 2) {  // bf16 values: the whole pattern only
-    if (mode != kCsrFused || (!binned && a.lds_window < a.n && a.acc == nullptr)) return hipErrorInvalidValue;
-    if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4, kModeFused, bf16_t>(a, p, s);
-    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeFused, bf16_t>(a, p, s);
-    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeFused, bf16_t>(a, p, s);
-    return hipErrorInvalidValue;
-  }
+  if (a.value_bytes == 2) return launch_modes<bf16_t>(a, p, s, mode);  // bf16 values
   if (a.value_bytes != 4) return hipErrorInvalidValue;
-  if (mode == kCsrRowdot) {
-    // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
-    if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))
-      return hipErrorInvalidValue;
-    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeRowdot>(a, p, s);
-    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeRowdot>(a, p, s);
-    return hipErrorInvalidValue;
-  }
-  if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
-  if (mode == kCsrTmv) {
-    if (a.v == nullptr) return hipErrorInvalidValue;  // u
-    if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeTmv>(a, p, s);
-    if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeTmv>(a, p, s);
-    return hipErrorInvalidValue;
-  }
-  if (mode != kCsrFused) return hipErrorInvalidValue;
-  // (threads, entries per thread): 256 x 4, 256 x 8 and 512 x 8
-  if (p.block_threads == 256 && p.entries_per_thread == 4) return launch_cold<256, 4, kModeFused>(a, p, s);
-  if (p.block_threads == 256 && p.entries_per_thread == 8) return launch_cold<256, 8, kModeFused>(a, p, s);
-  if (p.block_threads == 512 && p.entries_per_thread == 8) return launch_cold<512, 8, kModeFused>(a, p, s);
-  return hipErrorInvalidValue;
+  return launch_modes<float>(a, p, s, mode);
 }
 
 }  // namespace xtvxy

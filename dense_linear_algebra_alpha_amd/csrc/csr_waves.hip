@@ -516,24 +516,21 @@ hipError_t launch_csr_waves(const CsrArgs& a, const xtvxy_launch_params& p, hipS
   if (binned && (a.pool == nullptr || a.pool_next == nullptr || a.chunk_bin == nullptr || a.chunk_fill == nullptr ||
                  a.bins > kMaxBins || a.acc != nullptr))
     return hipErrorInvalidValue;
-  if (a.value_bytes == 2) {  // bf16 values: the whole pattern only
-    if (mode != kCsrFused || (!binned && a.lds_window < a.n && a.acc == nullptr)) return hipErrorInvalidValue;
-    return launch_wb<kWaveFused, bf16_t>(a, p, s);
-  }
-  if (a.value_bytes != 4) return hipErrorInvalidValue;
+  if (a.value_bytes != 4 && a.value_bytes != 2) return hipErrorInvalidValue;
+  const bool b16 = a.value_bytes == 2;  // bf16 values
   if (mode == kCsrRowdot) {
     // the first half alone: no output window and no scatter; t_out (and t0 when beta != 0)
     if (a.lds_window != 0 || binned || a.t_out == nullptr || (a.beta != 0.0f && a.t0 == nullptr))
       return hipErrorInvalidValue;
-    return launch_wb<kWaveRowdot>(a, p, s);
+    return b16 ? launch_wb<kWaveRowdot, bf16_t>(a, p, s) : launch_wb<kWaveRowdot>(a, p, s);
   }
   if (!binned && a.lds_window < a.n && a.acc == nullptr) return hipErrorInvalidValue;
   if (mode == kCsrTmv) {
     if (a.v == nullptr) return hipErrorInvalidValue;  // u
-    return launch_wb<kWaveTmv>(a, p, s);
+    return b16 ? launch_wb<kWaveTmv, bf16_t>(a, p, s) : launch_wb<kWaveTmv>(a, p, s);
   }
   if (mode != kCsrFused) return hipErrorInvalidValue;
-  return launch_wb<kWaveFused>(a, p, s);
+  return b16 ? launch_wb<kWaveFused, bf16_t>(a, p, s) : launch_wb<kWaveFused>(a, p, s);
 }
 
 }  // namespace xtvxy

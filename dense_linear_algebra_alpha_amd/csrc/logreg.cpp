@@ -80,29 +80,38 @@ struct Engine {
   int64_t m, n, nnz;
   const int32_t* row_ptr;
   const int32_t* col_idx;
-  const float* values;
+  const void* values;       // fp32, or bf16 bit patterns (value_bytes 2; the fused engine only)
+  int value_bytes;
   xtvxy_csr_unfused_plan plan;
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
   const xtvxy_launch_params* hvp_plan;  // the fused H d's plan when the row lengths refine it, else null
 
+  const float* f32() const { return static_cast<const float*>(values); }
+  const uint16_t* b16() const { return static_cast<const uint16_t*>(values); }
+
   xtvxy_status hvp(const float* v, float lam, const float* d, float* q) const {
-    if (kind == XTVXY_LOGREG_FUSED && hvp_plan)
-      return xtvxy_csr_f32_ex(m, n, nnz, 1.0f, row_ptr, col_idx, values, v, d, lam, d, q, ws, ws_bytes, stream,
-                              hvp_plan);
+    if (kind == XTVXY_LOGREG_FUSED && value_bytes == 2)
+      return xtvxy_csr_bf16_ex(m, n, nnz, 1.0f, row_ptr, col_idx, b16(), v, d, lam, d, q, ws, ws_bytes, stream,
+                               hvp_plan);
     if (kind == XTVXY_LOGREG_FUSED)
-      return xtvxy_csr_f32(m, n, nnz, 1.0f, row_ptr, col_idx, values, v, d, lam, d, q, ws, ws_bytes, stream);
+      return xtvxy_csr_f32_ex(m, n, nnz, 1.0f, row_ptr, col_idx, f32(), v, d, lam, d, q, ws, ws_bytes, stream,
+                              hvp_plan);
     return xtvxy_csr_f32_unfused_reference(plan, 1.0f, v, d, lam, d, q, stream);
   }
   xtvxy_status gradient(const float* u, float lam, const float* w, float* g) const {
+    if (kind == XTVXY_LOGREG_FUSED && value_bytes == 2)
+      return xtvxy_csr_bf16_tmv(m, n, nnz, 1.0f, row_ptr, col_idx, b16(), u, lam, w, g, ws, ws_bytes, stream);
     if (kind == XTVXY_LOGREG_FUSED)
-      return xtvxy_csr_f32_tmv(m, n, nnz, 1.0f, row_ptr, col_idx, values, u, lam, w, g, ws, ws_bytes, stream);
+      return xtvxy_csr_f32_tmv(m, n, nnz, 1.0f, row_ptr, col_idx, f32(), u, lam, w, g, ws, ws_bytes, stream);
     return unfused_tmv(plan, 1.0f, u, lam, w, g, stream);
   }
   xtvxy_status margins(const float* y, float* t) const {
+    if (kind == XTVXY_LOGREG_FUSED && value_bytes == 2)
+      return xtvxy_csr_bf16_rowdot(m, n, nnz, 1.0f, row_ptr, col_idx, b16(), nullptr, y, 0.0f, nullptr, t, stream);
     if (kind == XTVXY_LOGREG_FUSED)
-      return xtvxy_csr_f32_rowdot(m, n, nnz, 1.0f, row_ptr, col_idx, values, nullptr, y, 0.0f, nullptr, t, stream);
+      return xtvxy_csr_f32_rowdot(m, n, nnz, 1.0f, row_ptr, col_idx, f32(), nullptr, y, 0.0f, nullptr, t, stream);
     return unfused_rowdot(plan, y, t, stream);
   }
 };
@@ -122,16 +131,18 @@ xtvxy_status xtvxy_logreg_newton_cg_f32_workspace_size(int64_t m, int64_t n, int
   return XTVXY_SUCCESS;
 }
 
-xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
-                                        const int32_t* col_idx, const float* values, const float* labels, float* w,
-                                        const xtvxy_logreg_options* opt, xtvxy_csr_unfused_plan unfused,
-                                        void* workspace, size_t workspace_bytes, hipStream_t stream,
-                                        xtvxy_logreg_report* report, double* history, int64_t history_rows) {
+// The solver with fp32 (value_bytes 4) or bf16 (2; the fused engine only) values.
+static xtvxy_status newton_cg(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr, const int32_t* col_idx,
+                              const void* values, int value_bytes, const float* labels, float* w,
+                              const xtvxy_logreg_options* opt, xtvxy_csr_unfused_plan unfused, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream, xtvxy_logreg_report* report,
+                              double* history, int64_t history_rows) {
   // ---- argument checks, before anything touches the device
   if (m < 0 || n < 0 || nnz < 0 || history_rows < 0) return XTVXY_ERROR_INVALID_VALUE;
   if (nnz > INT32_MAX || m > INT32_MAX - 1024 || n > INT32_MAX) return XTVXY_ERROR_UNSUPPORTED;
   xtvxy_status st = check_options(opt);
   if (st != XTVXY_SUCCESS) return st;
+  if (value_bytes == 2 && opt->engine != XTVXY_LOGREG_FUSED) return XTVXY_ERROR_INVALID_VALUE;
   if (!row_ptr || (nnz > 0 && (!col_idx || !values)) || (m > 0 && !labels) || (n > 0 && !w))
     return XTVXY_ERROR_NULL_POINTER;
   if (history_rows > 0 && !history) return XTVXY_ERROR_NULL_POINTER;
@@ -189,8 +200,8 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
                 (size_t)hvp_plan.workspace_bytes <= L.product_bytes;
     }
   }
-  const Engine E{opt->engine, m, n, nnz, row_ptr, col_idx, values, unfused, base + L.product_off, L.product_bytes,
-                 stream, refined ? &hvp_plan : nullptr};
+  const Engine E{opt->engine, m, n, nnz, row_ptr, col_idx, values, value_bytes, unfused, base + L.product_off,
+                 L.product_bytes, stream, refined ? &hvp_plan : nullptr};
   const double nan = std::numeric_limits<double>::quiet_NaN();
   auto record = [&](int64_t k, int col, double value) {
     if (k < history_rows) history[k * kHistoryCols + col] = value;
@@ -298,6 +309,24 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
   rep.seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t_start).count();
   if (report) *report = rep;
   return XTVXY_SUCCESS;
+}
+
+xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
+                                        const int32_t* col_idx, const float* values, const float* labels, float* w,
+                                        const xtvxy_logreg_options* opt, xtvxy_csr_unfused_plan unfused,
+                                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                        xtvxy_logreg_report* report, double* history, int64_t history_rows) {
+  return newton_cg(m, n, nnz, row_ptr, col_idx, values, 4, labels, w, opt, unfused, workspace, workspace_bytes,
+                   stream, report, history, history_rows);
+}
+
+xtvxy_status xtvxy_logreg_newton_cg_bf16(int64_t m, int64_t n, int64_t nnz, const int32_t* row_ptr,
+                                         const int32_t* col_idx, const uint16_t* values, const float* labels,
+                                         float* w, const xtvxy_logreg_options* opt, void* workspace,
+                                         size_t workspace_bytes, hipStream_t stream, xtvxy_logreg_report* report,
+                                         double* history, int64_t history_rows) {
+  return newton_cg(m, n, nnz, row_ptr, col_idx, values, 2, labels, w, opt, nullptr, workspace, workspace_bytes,
+                   stream, report, history, history_rows);
 }
 
 }  // extern "C"

@@ -360,6 +360,24 @@ xtvxy_status xtvxy_csr_f32_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha
                                   const int32_t *col_idx, const float *values, const float *u, float beta,
                                   const float *z, float *out, void *workspace, size_t workspace_bytes,
                                   hipStream_t stream, const xtvxy_launch_params *force);
+/* The two halves with the values stored as bf16 (as xtvxy_csr_bf16 is to xtvxy_csr_f32): the same
+ * rules, plans and workspace as the fp32 halves; values[nnz] are bf16 bit patterns widened exactly
+ * as they are loaded. */
+xtvxy_status xtvxy_csr_bf16_rowdot(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                   const int32_t *col_idx, const uint16_t *values, const float *v, const float *y,
+                                   float beta, const float *t0, float *t, hipStream_t stream);
+xtvxy_status xtvxy_csr_bf16_rowdot_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                      const int32_t *col_idx, const uint16_t *values, const float *v, const float *y,
+                                      float beta, const float *t0, float *t, hipStream_t stream,
+                                      const xtvxy_launch_params *force);
+xtvxy_status xtvxy_csr_bf16_tmv(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                const int32_t *col_idx, const uint16_t *values, const float *u, float beta,
+                                const float *z, float *out, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+xtvxy_status xtvxy_csr_bf16_tmv_ex(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                   const int32_t *col_idx, const uint16_t *values, const float *u, float beta,
+                                   const float *z, float *out, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream, const xtvxy_launch_params *force);
 
 /* Device-side structure check of a CSR matrix. Writes to *d_flag (a device
  * int32) 0 when row_ptr[0] == 0, row_ptr is non-decreasing, row_ptr[m] == nnz
@@ -627,6 +645,19 @@ xtvxy_status xtvxy_logreg_newton_cg_f32(int64_t m, int64_t n, int64_t nnz, const
                                         float *w, const xtvxy_logreg_options *opt, xtvxy_csr_unfused_plan unfused,
                                         void *workspace, size_t workspace_bytes, hipStream_t stream,
                                         xtvxy_logreg_report *report, double *history, int64_t history_rows);
+
+/* The same solver with X's values stored as bf16 bit patterns (nnz uint16_t, device), each
+ * widened exactly to fp32 where it is read, as in xtvxy_csr_bf16; labels, w and every vector
+ * and reduction are as above. Only the fused engine takes bf16 values: opt->engine must be
+ * XTVXY_LOGREG_FUSED (else XTVXY_ERROR_INVALID_VALUE), and the workspace is the one of
+ * xtvxy_logreg_newton_cg_f32_workspace_size. The products are xtvxy_csr_bf16, _bf16_tmv and
+ * _bf16_rowdot; the iterates equal those of the fp32 solver run on the widened values, up to
+ * the rounding of the products' sums. */
+xtvxy_status xtvxy_logreg_newton_cg_bf16(int64_t m, int64_t n, int64_t nnz, const int32_t *row_ptr,
+                                         const int32_t *col_idx, const uint16_t *values, const float *labels,
+                                         float *w, const xtvxy_logreg_options *opt, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream, xtvxy_logreg_report *report,
+                                         double *history, int64_t history_rows);
 
 #ifdef __cplusplus
 }

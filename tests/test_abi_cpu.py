@@ -379,6 +379,57 @@ def test_logreg_argument_errors(lib):
     assert lib.xtvxy_logreg_newton_cg_f32_workspace_size(4, 4, 4, None) == E.XTVXY_ERROR_NULL_POINTER
 
 
+def logreg_bf16_status(m=8, n=4, nnz=16, vals=FAKE + 2048, ws=FAKE + 65536, **kw):
+    o = xt.xtvxy_logreg_options(1.0, 5, 10, 30, 1e-6, 0.5, 0, xt.XTVXY_LOGREG_FUSED)
+    for k, v in kw.items():
+        setattr(o, k, v)
+    return _abi.load().xtvxy_logreg_newton_cg_bf16(m, n, nnz, FAKE, FAKE + 1024, vals, FAKE + 4096, FAKE + 8192,
+                                                   ctypes.byref(o), ws, 1 << 20, None, None, None, 0)
+
+
+def test_logreg_bf16_argument_errors(lib):
+    E = _abi
+    assert logreg_bf16_status(engine=xt.XTVXY_LOGREG_UNFUSED) == E.XTVXY_ERROR_INVALID_VALUE  # fused engine only
+    assert logreg_bf16_status(m=-1) == E.XTVXY_ERROR_INVALID_VALUE
+    assert logreg_bf16_status(max_cg=0) == E.XTVXY_ERROR_INVALID_VALUE
+    assert logreg_bf16_status(vals=None) == E.XTVXY_ERROR_NULL_POINTER
+    assert logreg_bf16_status(ws=None) == E.XTVXY_ERROR_WORKSPACE
+
+
+@pytest.mark.parametrize("fn", ["xtvxy_csr_f32_rowdot", "xtvxy_csr_bf16_rowdot"])
+def test_rowdot_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    # m n nnz alpha row_ptr col_idx values v y beta t0 t stream
+    ok = [8, 8, 16, 1.0, FAKE, FAKE + 1024, FAKE + 2048, None, FAKE + 4096, 0.0, None, FAKE + 8192, None]
+    def st(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert st(a0=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert st(a2=1 << 31) == _abi.XTVXY_ERROR_UNSUPPORTED
+    assert st(a6=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert st(a9=1.0) == _abi.XTVXY_ERROR_NULL_POINTER          # beta != 0 without t0
+    assert st(a11=FAKE + 2048 + 16) == _abi.XTVXY_ERROR_ALIASING  # t overlaps the values
+
+
+@pytest.mark.parametrize("fn", ["xtvxy_csr_f32_tmv", "xtvxy_csr_bf16_tmv"])
+def test_tmv_argument_errors(lib, fn):
+    f = getattr(lib, fn)
+    # m n nnz alpha row_ptr col_idx values u beta z out workspace bytes stream
+    ok = [8, 8, 16, 1.0, FAKE, FAKE + 1024, FAKE + 2048, FAKE + 4096, 0.0, None, FAKE + 8192, None, 0, None]
+    def st(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert st(a1=-1) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert st(a6=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert st(a7=None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert st(a8=1.0) == _abi.XTVXY_ERROR_NULL_POINTER           # beta != 0 without z
+    assert st(a10=FAKE + 2048 + 16) == _abi.XTVXY_ERROR_ALIASING  # out overlaps the values
+
+
 def test_tune_argument_errors(lib):
     rep = xt.xtvxy_tune_report()
     assert lib.xtvxy_dense_f32_tune(8, 8, 1.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 10, None,

@@ -85,6 +85,17 @@ def test_dense_padding_is_nan():
     assert np.all(np.isnan(X[:, 3:])) and np.all(np.isfinite(X[:, :3]))
 
 
+def test_logistic_bf16_workload_rounds_the_values_only():
+    P = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000"](m=20_000)
+    B = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000_bf16"](m=20_000)
+    assert B.X.values_dtype == "bf16" and B.X.values.dtype == np.uint16
+    assert np.array_equal(B.labels, P.labels) and B.lam == P.lam
+    assert np.array_equal(B.X.row_ptr, P.X.row_ptr) and np.array_equal(B.X.col_idx, P.X.col_idx)
+    assert np.array_equal(B.X.values, datagen.to_bf16(P.X.values))
+    # rounding to nearest bf16: within half a unit of the last of 8 significant bits
+    assert np.all(np.abs(B.X.values_f32() - P.X.values) <= np.abs(P.X.values) * 2.0 ** -8)
+
+
 def test_logistic_labels():
     P = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000"](m=200_000)
     Q = datagen.LOGISTIC_WORKLOADS["logreg_csr_10000000x1000"](m=200_000)
