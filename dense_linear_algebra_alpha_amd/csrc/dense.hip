@@ -163,10 +163,10 @@ template <class E, int VEC, int NCH, bool GROUP>
 __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
   constexpr int R = GROUP ? group_rows_per_step(NCH, VEC, (int)sizeof(E)) : block_rows_per_step(NCH, VEC, (int)sizeof(E));
   constexpr int kMaxGroup = kGroupMaxMembers;
-  // fp32 group rows (and fp32 block rows of 8 chunks of 4) keep each thread's column sums in LDS,
-  // in words no other thread touches (so no barrier guards them); the registers they free hold
-  // more rows per exchange of dots (per barrier, for block rows).
-  constexpr bool kSumsInLds = (GROUP && sizeof(E) == 4) || (!GROUP && block_sums_in_lds(NCH, VEC, (int)sizeof(E)));
+  // Group rows (and fp32 block rows of 8 chunks of 4) keep each thread's column sums in LDS, in
+  // words no other thread touches (so no barrier guards them); the registers they free hold more
+  // rows per exchange of dots (per barrier, for block rows).
+  constexpr bool kSumsInLds = GROUP || block_sums_in_lds(NCH, VEC, (int)sizeof(E));
   __shared__ float red[2][R][kWaves];
   __shared__ float gx[GROUP ? R : 1][GROUP ? kMaxGroup : 1];
   __shared__ __align__(16) float acc_s[kSumsInLds ? NCH * kBlock * VEC : 1];  // [chunk][thread][VEC]
@@ -310,6 +310,15 @@ __global__ __launch_bounds__(kBlock) void dense_block_rows(DenseArgs a) {
       const bool rok = row < r1;
       const float vv = a.v ? (rok ? a.v[row] : 0.0f) : 1.0f;
       uu[r] = rok ? vv * t[r] : 0.0f;
+    }
+    if constexpr (GROUP && sizeof(E) == 2) {
+      // 16-bit group rows are widened again for the accumulation rather than kept widened since
+      // the dots: the packed words take half the registers, which hold twice the rows per
+      // exchange of dots, and the widening is one operation per element
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) xv[r][c].opaque();
     }
     if constexpr (kSumsInLds) {  // one read and one write of each sum per step, rows in order
 #pragma unroll

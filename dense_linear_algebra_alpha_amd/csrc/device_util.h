@@ -203,11 +203,17 @@ template <>
 struct XChunk<bf16_t, 8> {
   unsigned int w[4];
   __device__ __forceinline__ float get(int k) const { return (k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]); }
+  // the words become opaque to the compiler: values widened from them before are not reused
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w[i]));
+  }
 };
 template <>
 struct XChunk<bf16_t, 1> {
   unsigned int w;
   __device__ __forceinline__ float get(int) const { return bf16_lo(w); }
+  __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(w)); }
 };
 
 // fp16 storage of X: IEEE binary16, kept packed like bf16 and widened exactly (every fp16 value,
@@ -223,11 +229,17 @@ template <>
 struct XChunk<f16_t, 8> {
   unsigned int w[4];
   __device__ __forceinline__ float get(int k) const { return (k & 1) ? f16_hi(w[k >> 1]) : f16_lo(w[k >> 1]); }
+  // the words become opaque to the compiler: values widened from them before are not reused
+  __device__ __forceinline__ void opaque() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(w[i]));
+  }
 };
 template <>
 struct XChunk<f16_t, 1> {
   unsigned int w;
   __device__ __forceinline__ float get(int) const { return f16_lo(w); }
+  __device__ __forceinline__ void opaque() { asm volatile("" : "+v"(w)); }
 };
 
 // Chunk of row `xr` from column `col` when `ok`, else zeros. fp32 rows take load_chunk; bf16 and

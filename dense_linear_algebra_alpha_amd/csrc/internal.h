@@ -16,15 +16,16 @@ constexpr int kBlock = 256;          // threads per workgroup of every fused ker
 constexpr int kWaves = kBlock / 64;  // wavefronts per workgroup
 constexpr int kBlockRowsInFlight = 2;  // rows a block-row workgroup loads per step (but see below)
 // Rows a group-row workgroup loads per step, i.e. per exchange of partial dots between the
-// members. fp32 keeps each thread's column sums in LDS, so a step's rows may take 128 registers
-// (4 rows of 8 chunks of 4 floats, at most 16 rows); bf16 keeps its sums in registers and a step
-// holds 16 packed chunks per thread (4 rows of 4 chunks). Fewer chunks per thread (wider groups)
-// buy more rows per exchange.
+// members. Each thread's column sums live in LDS, so a step's rows may take 128 registers: fp32
+// 4 rows of 8 chunks of 4 floats (at most 16 rows); 16-bit elements stay packed (two to a
+// register, widened at each use), so 8 rows of 4 chunks of 8, or 16 rows of 1 or 2 chunks, and
+// 2 rows of 8 chunks (their y takes 64 registers). Fewer chunks per thread (wider groups) buy
+// more rows per exchange.
 // Members of a group-row group at most: 128 x 8192 = 1,048,576 columns with 16-byte loads.
 constexpr int kGroupMaxMembers = 128;
 constexpr int group_rows_per_step(int chunks, int vec, int elem_bytes) {
   if (chunks < 1 || chunks > 16) return 1;
-  if (elem_bytes == 2) return 16 / chunks;
+  if (elem_bytes == 2) return chunks <= 2 ? 16 : chunks == 4 ? 8 : 16 / chunks;
   const int words = chunks * (vec > 0 ? vec : 1);  // fp32: one register per element
   return words >= 128 ? 1 : (128 / words > 16 ? 16 : 128 / words);
 }
