@@ -215,9 +215,9 @@ __global__ __launch_bounds__(BLK) void csr_fused(CsrArgs a) {
 
   if (wave == 0) {
     const int64_t q = (a.nnz + gridDim.x - 1) / gridDim.x;
-    const int64_t rb = wave_lower_bound(a.row_ptr, a.m, (int64_t)blockIdx.x * q);
-    const int64_t re =
-        (blockIdx.x + 1 == gridDim.x) ? a.m : wave_lower_bound(a.row_ptr, a.m, (int64_t)(blockIdx.x + 1) * q);
+    int64_t rb, re;
+    wave_lower_bound_pair(a.row_ptr, a.m, (int64_t)blockIdx.x * q, (int64_t)(blockIdx.x + 1) * q, rb, re);
+    if (blockIdx.x + 1 == gridDim.x) re = a.m;
     if (lane == 0) {
       range_s[0] = (int32_t)rb;
       range_s[1] = (int32_t)re;

@@ -54,4 +54,48 @@ __device__ inline int64_t wave_lower_bound(const int32_t* __restrict__ rp, int64
   return min(lo + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi);
 }
 
+// wave_lower_bound for two targets at once: both searches take their rounds together, so each
+// round's two probes are requested before either is waited for (one latency per round, not two).
+__device__ inline void wave_lower_bound_pair(const int32_t* __restrict__ rp, int64_t m, int64_t ta, int64_t tb,
+                                             int64_t& ra, int64_t& rb) {
+  const int lane = threadIdx.x & 63;
+  int64_t lo[2] = {0, 0}, hi[2] = {m, m};
+  const int64_t target[2] = {ta, tb};
+  while (hi[0] - lo[0] > 64 || hi[1] - lo[1] > 64) {
+    int64_t probe[2];
+    int32_t v[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int64_t step = hi[s] - lo[s] > 64 ? (hi[s] - lo[s] + 63) / 64 : 0;  // 0: this one is done
+      probe[s] = min(lo[s] + (int64_t)(lane + 1) * step, hi[s]);
+      v[s] = rp[probe[s]];  // probe <= hi <= m: inside row_ptr
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (hi[s] - lo[s] <= 64) continue;  // wavefront-uniform
+      const uint64_t mask = __ballot(probe[s] >= hi[s] || (int64_t)v[s] >= target[s]);
+      const int k = __ffsll((unsigned long long)mask) - 1;  // lane 63 always qualifies
+      const int64_t nhi = __shfl(probe[s], k, 64);
+      const int64_t nlo = (k == 0) ? lo[s] : __shfl(probe[s], k - 1, 64) + 1;
+      lo[s] = nlo;
+      hi[s] = nhi;
+    }
+  }
+  int64_t res[2];
+  int64_t probe[2];
+  int32_t v[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    probe[s] = min(lo[s] + (int64_t)lane, hi[s]);
+    v[s] = rp[probe[s]];
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const uint64_t mask = __ballot(probe[s] >= hi[s] || (int64_t)v[s] >= target[s]);
+    res[s] = target[s] <= 0 ? 0 : mask == 0 ? hi[s] : min(lo[s] + (int64_t)(__ffsll((unsigned long long)mask) - 1), hi[s]);
+  }
+  ra = res[0];
+  rb = res[1];
+}
+
 }  // namespace xtvxy

@@ -70,8 +70,7 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   static_assert(kScatter || COLD == kColdNone, "the first half alone has no window and no bins");
   constexpr uint32_t S = kBinChunkItems;
   __shared__ __align__(16) uint8_t mark_s[NW][TW];  // 1 + tile row whose first entry sits at slot q, else 0
-  __shared__ float u_s[NW][64];                     // u_row = v_row * dot of the tile's rows
-  __shared__ float v_s[NW][64];                     // v of the tile's rows
+  __shared__ float u_s[NW][64];                     // the dots of the tile's rows, then u_row = v_row * dot
   __shared__ float sink_s[BLK];                     // a private LDS word per thread for masked-off adds
   extern __shared__ __align__(16) float dyn[];
   float* out_s = dyn;                 // [lds_window], shared by the wavefronts
@@ -252,8 +251,10 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
   const int64_t G = (int64_t)gridDim.x * NW;
   const int64_t gw = (int64_t)blockIdx.x * NW + wave;
   const int64_t q = (a.nnz + G - 1) / G;
-  const int32_t rb = (int32_t)wave_lower_bound(a.row_ptr, a.m, gw * q);
-  const int32_t re = (gw + 1 == G) ? (int32_t)a.m : (int32_t)wave_lower_bound(a.row_ptr, a.m, (gw + 1) * q);
+  int64_t rb64, re64;
+  wave_lower_bound_pair(a.row_ptr, a.m, gw * q, (gw + 1) * q, rb64, re64);
+  const int32_t rb = (int32_t)rb64;
+  const int32_t re = (gw + 1 == G) ? (int32_t)a.m : (int32_t)re64;
 
   auto issue = [&](int32_t r, int32_t re_, uint32_t first_entry, WaveTile<K>& g) {
     g.rp = a.row_ptr[min(r + lane, re_)];
@@ -350,10 +351,8 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
         }
       }
     } else {
-      // row-start marks of the tile's nonempty rows, and v of its rows
+      // row-start marks of the tile's nonempty rows
       if (lane < R && g.rp1 > g.rp) mark_s[wave][(uint32_t)g.rp - base] = (uint8_t)(lane + 1);
-      v_s[wave][lane] = g.v;
-      if constexpr (MODE == kWaveRowdot) u_s[wave][lane] = 0.0f;  // empty rows get t = beta t0
       wave_lds_sync();
       int mk[K];
       {
@@ -382,7 +381,8 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       // inside the lane is stored; the first and last runs are finished by a segmented sum
       // across the wavefront. Every row ends inside the tile, so each gets one write. Slots
       // outside the tile belong to its first row (before it) or its last nonempty row (after
-      // it) and add a zero product there, so the row logic needs no mask.
+      // it) and add a zero product there, so the row logic needs no mask. Lane j then scales
+      // the dot of the tile's row j by that row's v, which it holds.
       if constexpr (MODE == kWaveTmv) {
         u_s[wave][lane] = g.v;  // the given u of the tile's rows
       } else {
@@ -394,7 +394,7 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
 #pragma unroll
       for (int k = 1; k < K; ++k) {
         const bool fresh = rk[k] != rk[k - 1];
-        if (fresh && rk[k - 1] != r0) u_s[wave][rk[k - 1]] = v_s[wave][rk[k - 1]] * run;
+        if (fresh && rk[k - 1] != r0) u_s[wave][rk[k - 1]] = run;
         head = (fresh && rk[k - 1] == r0) ? run : head;
         run = fresh ? pk[k] : run + pk[k];
       }
@@ -402,13 +402,20 @@ __global__ __launch_bounds__(BLK) void csr_waves(CsrArgs a) {
       const float prev_tails = dpp_float<dpp::kWaveShr1>(0.0f, tails);
       const int prev_key = dpp_int<dpp::kWaveShr1>(-1, r1);
       const int next_r0 = dpp_int<dpp::kWaveShl1>(-1, r0);
-      if (r0 != r1) u_s[wave][r0] = v_s[wave][r0] * (head + (prev_key == r0 ? prev_tails : 0.0f));
-      if (next_r0 != r1) u_s[wave][r1] = v_s[wave][r1] * tails;
+      if (r0 != r1) u_s[wave][r0] = head + (prev_key == r0 ? prev_tails : 0.0f);
+      if (next_r0 != r1) u_s[wave][r1] = tails;
       }
       wave_lds_sync();
       if constexpr (MODE == kWaveRowdot) {
-        if (lane < R) a.t_out[r + lane] = a.alpha * u_s[wave][lane] + (a.beta != 0.0f ? a.beta * a.t0[r + lane] : 0.0f);
+        if (lane < R) {
+          const float u = g.rp1 > g.rp ? g.v * u_s[wave][lane] : 0.0f;  // an empty row's dot is 0, whatever v
+          a.t_out[r + lane] = a.alpha * u + (a.beta != 0.0f ? a.beta * a.t0[r + lane] : 0.0f);
+        }
       } else {
+        if constexpr (MODE == kWaveFused && HAS_V) {
+          if (lane < R) u_s[wave][lane] *= g.v;
+          wave_lds_sync();
+        }
         float c[K];
 #pragma unroll
         for (int k = 0; k < K; ++k) c[k] = u_s[wave][rk[k]] * g.val[k];

@@ -53,10 +53,10 @@ constexpr int kBinSortGroups = 256;  // workgroups of the counting sort of chunk
 // positions) when binning
 constexpr size_t kCsrBinStateBytes = 32;
 // Wavefront CSR kernel (csr_waves.hip): static LDS per workgroup of `blk` threads (row-start
-// marks of 512 entry slots, u and v of 64 rows per wavefront, a sink word per thread), and the
+// marks of 512 entry slots, u of 64 rows per wavefront, a sink word per thread), and the
 // dynamic LDS: output and y windows, then each wavefront's bin state (6 words per bin).
 constexpr size_t kCsrWaveBinStateBytes = 24;
-constexpr size_t csr_waves_static_lds(int blk) { return (size_t)(blk / 64) * (512 + 512) + 4 * (size_t)blk; }
+constexpr size_t csr_waves_static_lds(int blk) { return (size_t)(blk / 64) * (512 + 256) + 4 * (size_t)blk; }
 constexpr size_t csr_waves_dynamic_lds(int64_t window, int64_t y_window, int32_t bins, int blk) {
   return (((size_t)(window + y_window) * 4 + 7) & ~(size_t)7) +
          (bins > 0 ? (size_t)bins * kCsrWaveBinStateBytes * (size_t)(blk / 64) : 0);
