@@ -259,6 +259,52 @@ def scatter_probe(args):
     print(json.dumps({"scatter_probe": rows, "grid": grid, "threads_per_workgroup": 256}))
 
 
+def tile_stream_probe(args):
+    """The wavefront CSR kernel's access pattern alone (xtvxy_tile_stream_probe) on as many
+    entries of the logistic workload's size as the launch shape divides: each wavefront its own
+    stretch (the kernel's layout) and the workgroup's wavefronts interleaved, at the kernel's
+    launch shape (256 threads, 3 workgroups per CU) and around it; GB/s counts 8 bytes per entry
+    (best and median of 20 launches after 5 warmup launches, HIP events)."""
+    import torch
+
+    import dense_linear_algebra_alpha_amd as xt
+
+    xt.load()
+    dev = torch.device("cuda", 0)
+    cus = xt.xtvxy_get_device_info().compute_units
+    nnz = args.probe_entries
+    sink = torch.zeros(1, dtype=torch.float32, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream or None
+    ev = HipEvents()
+    rows = []
+    for per_cu in (2, 3, 4):
+        grid = per_cu * cus
+        entries = nnz // (grid * 2048) * (grid * 2048)
+        a = torch.zeros(entries, dtype=torch.int32, device=dev)
+        b = torch.zeros(entries, dtype=torch.float32, device=dev)
+        for interleave in (0, 1):
+            for _ in range(5):
+                xt.xtvxy_tile_stream_probe(a.data_ptr(), b.data_ptr(), entries, grid, interleave, sink.data_ptr(), sh)
+            pairs = [(ev.create(), ev.create()) for _ in range(20)]
+            for p0, p1 in pairs:
+                ev.record(p0, sh)
+                xt.xtvxy_tile_stream_probe(a.data_ptr(), b.data_ptr(), entries, grid, interleave, sink.data_ptr(), sh)
+                ev.record(p1, sh)
+            torch.cuda.synchronize()
+            ms = [ev.elapsed_ms(p0, p1) for p0, p1 in pairs]
+            for p0, p1 in pairs:
+                ev.destroy(p0)
+                ev.destroy(p1)
+            rows.append({"layout": "workgroup's wavefronts interleaved" if interleave else "wavefront's own stretch",
+                         "grid": grid, "workgroups_per_cu": per_cu, "entries": entries,
+                         "best_us": round(min(ms) * 1e3, 1), "median_us": round(statistics.median(ms) * 1e3, 1),
+                         "gbs": round(8 * entries / (min(ms) / 1e3) / 1e9, 1),
+                         "median_gbs": round(8 * entries / (statistics.median(ms) / 1e3) / 1e9, 1)})
+            print(json.dumps(rows[-1]), flush=True)
+        del a, b
+    print(json.dumps({"tile_stream_probe": rows, "threads_per_workgroup": 256}))
+
+
 LOGREG_METRIC = "Newton-CG logistic regression: ms per Newton iteration (fixed schedule), fused vs unfused products"
 
 
@@ -740,6 +786,11 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference reading "
                          "for the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--tile-stream-probe", action="store_true",
+                    help="the wavefront CSR kernel's access pattern alone (two arrays, 8 entries per lane), "
+                         "each wavefront's own stretch against the workgroup's wavefronts interleaved")
+    ap.add_argument("--probe-entries", type=int, default=100_006_237,
+                    help="entries for --tile-stream-probe (default: the logistic workload's nnz)")
     ap.add_argument("--scatter-probe", action="store_true",
                     help="only measure the rates of the scatter primitives (global fp32 atomics into one copy "
                          "or one copy per XCD, scattered 8-byte item stores, random gathers) and exit")
@@ -759,6 +810,8 @@ def main():
         return
     if args.scatter_probe:
         return scatter_probe(args)
+    if args.tile_stream_probe:
+        return tile_stream_probe(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

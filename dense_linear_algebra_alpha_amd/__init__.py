@@ -49,6 +49,7 @@ __all__ = [
     "xtvxy_csr_f32_analysed_ex", "CsrAnalysis", "xtvxy_csr_bf16", "xtvxy_csr_bf16_ex", "xtvxy_csr_bf16_analysed",
     "xtvxy_csr_bf16_analysed_ex", "xtvxy_dense_f16", "xtvxy_dense_f16_ex", "xtvxy_csr_bf16_rowdot",
     "xtvxy_csr_bf16_rowdot_ex", "xtvxy_csr_bf16_tmv", "xtvxy_csr_bf16_tmv_ex", "xtvxy_logreg_newton_cg_bf16",
+    "xtvxy_tile_stream_probe",
 ]
 
 load = _abi.load
@@ -253,6 +254,10 @@ def xtvxy_csr_bf16_tmv_ex(m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z
                           stream, force):
     return _abi.call("xtvxy_csr_bf16_tmv_ex", m, n, nnz, alpha, row_ptr, col_idx, values, u, beta, z, out,
                      workspace, workspace_bytes, stream, ctypes.byref(force) if force is not None else None)
+
+
+def xtvxy_tile_stream_probe(indices, values, entries, grid, interleave, sink, stream):
+    return _abi.call("xtvxy_tile_stream_probe", indices, values, entries, grid, interleave, sink, stream)
 
 
 def xtvxy_csr_f32_analyse(m, n, nnz, row_ptr, col_idx, stream) -> int:

@@ -159,6 +159,7 @@ SIGNATURES = {
     "xtvxy_csr_bf16_analysed": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp],
     "xtvxy_csr_bf16_analysed_ex": [_vp, _f32, _vp, _vp, _vp, _f32, _vp, _vp, _vp, _sz, _vp, _P(xtvxy_launch_params)],
     "xtvxy_read_probe": [_vp, _sz, _i64, _vp, _vp],
+    "xtvxy_tile_stream_probe": [_vp, _vp, _i64, _i64, _i32, _vp, _vp],
     "xtvxy_scatter_probe": [_i32, _vp, _sz, ctypes.c_uint32, ctypes.c_uint32, _i32, _i64, _vp, _vp],
     "xtvxy_dense_f32_noalloc_max_workspace": [_P(_sz)],
     "xtvxy_dense_f32_noalloc": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _vp],

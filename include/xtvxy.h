@@ -412,6 +412,18 @@ xtvxy_status xtvxy_test_group_wait(int32_t polls, int32_t unanswered);
  * Asynchronous on `stream`. */
 xtvxy_status xtvxy_read_probe(const void *buffer, size_t bytes, int64_t grid, float *sink, hipStream_t stream);
 
+/* Measurement helper, not part of the pattern: the access pattern of the wavefront CSR kernel
+ * alone. Reads `entries` 4-byte elements from each of the two 16-byte aligned device arrays
+ * (column indices and values in the kernel) over `grid` workgroups of 4 wavefronts, in tiles of
+ * 512 entries per wavefront (8 per lane, two 16-byte loads per array), the next tile requested
+ * before the current one is used; with `interleave` 0 each wavefront reads one contiguous
+ * stretch (the kernel's layout), with 1 the 4 wavefronts of a workgroup take alternate tiles of
+ * the workgroup's stretch. `entries` must be a positive multiple of grid * 2048
+ * (XTVXY_ERROR_INVALID_VALUE otherwise). Writes nothing but `sink` (only for data a zeroed pair of
+ * arrays never holds). Asynchronous on `stream`. */
+xtvxy_status xtvxy_tile_stream_probe(const void *indices, const void *values, int64_t entries, int64_t grid,
+                                     int32_t interleave, float *sink, hipStream_t stream);
+
 /* What xtvxy_scatter_probe measures. */
 typedef enum {
   XTVXY_PROBE_ATOMIC_PER_XCD = 0, /* fp32 atomic add of 1 into the copy of the XCD the wavefront runs on

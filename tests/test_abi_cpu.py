@@ -151,6 +151,13 @@ def test_probe_argument_errors(lib):
     assert lib.xtvxy_read_probe(FAKE, 15, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
     assert lib.xtvxy_read_probe(FAKE + 4, 16, 1, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
     assert lib.xtvxy_read_probe(FAKE, 16, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    tp = lib.xtvxy_tile_stream_probe
+    assert tp(None, FAKE, 2048, 1, 0, FAKE, None) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert tp(FAKE, FAKE, 2047, 1, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE   # not whole tiles
+    assert tp(FAKE, FAKE, 4096, 3, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE   # not a multiple of grid
+    assert tp(FAKE + 4, FAKE, 2048, 1, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert tp(FAKE, FAKE, 2048, 1, 2, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
+    assert tp(FAKE, FAKE, 0, 1, 0, FAKE, None) == _abi.XTVXY_ERROR_INVALID_VALUE
     probe = lib.xtvxy_scatter_probe
     assert probe(_abi.XTVXY_PROBE_GATHERS, None, 64, 16, 8, 0, 1, FAKE, None) == _abi.XTVXY_ERROR_NULL_POINTER
     assert probe(_abi.XTVXY_PROBE_GATHERS, FAKE, 64, 16, 8, 0, 1, None, None) == _abi.XTVXY_ERROR_NULL_POINTER
@@ -249,8 +256,8 @@ def test_csr_model_plans(lib, m, n, nnz):
 
 
 def test_csr_wave_plans(lib):
-    """The wavefront kernel: 256, 512 or 1024 threads of 8 entries; its LDS (windows, 1 KiB of
-    marks, u and v per wavefront, a word per thread, 24 bytes per bin and wavefront) must fit;
+    """The wavefront kernel: 256, 512 or 1024 threads of 8 entries; its LDS (windows, 512 bytes of
+    marks and 256 of u per wavefront, a word per thread, 24 bytes per bin and wavefront) must fit;
     its bin pool leaves room for one partly filled chunk per (wavefront, bin)."""
     def lp(blk, window, y_window, bc, grid=64, ept=8):
         return xt.xtvxy_launch_params(kernel=xt.XTVXY_CSR_WAVES, block_threads=blk, entries_per_thread=ept, grid=grid,
@@ -261,8 +268,8 @@ def test_csr_wave_plans(lib):
     for blk, ept in ((128, 8), (256, 4), (2048, 8)):
         with pytest.raises(xt.XtvxyError):
             xt.xtvxy_csr_f32_plan_complete(1000, 900, 9000, lp(blk, 900, 900, 0, ept=ept), MI355X)
-    # the largest window that fits beside the 1024-thread workgroup's static LDS (20 KiB)
-    static = 16 * 1024 + 4 * 1024
+    # the largest window that fits beside the 1024-thread workgroup's static LDS (16 KiB)
+    static = 16 * (512 + 256) + 4 * 1024
     w = (MI355X.lds_bytes - static) // 4
     xt.xtvxy_csr_f32_plan_complete(1000, 10**6, 10**6, lp(1024, w, 0, 0), MI355X)
     with pytest.raises(xt.XtvxyError):
