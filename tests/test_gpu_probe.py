@@ -1,5 +1,6 @@
 """The measurement probes on the GPU: every update of the scatter probe lands (exact integer counts
-in fp32), per XCD copy or in one copy, and the gathers and the streaming read write nothing."""
+in fp32), per XCD copy or in one copy, and the gathers, the streaming read and the tile-stream read
+write nothing."""
 import pytest
 
 import dense_linear_algebra_alpha_amd as xt
@@ -48,3 +49,19 @@ def test_scatter_probe_stores_and_gathers():
     assert bool(((items_view[written, 0] >= 0) & (items_view[written, 0] < items)).all())
     assert bool((items_view[~written] == -1).all())
     assert float(sink[0]) == 0.0
+
+
+@pytest.mark.parametrize("interleave", [0, 1])
+def test_tile_stream_probe_reads_and_writes_nothing(interleave):
+    import torch
+    grid = 64
+    entries = grid * 2048 * 3  # three tiles per wavefront
+    note("tile stream probe grid=%d entries=%d interleave=%d" % (grid, entries, interleave))
+    a = torch.zeros(entries, dtype=torch.int32, device="cuda")
+    b = torch.zeros(entries, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    xt.xtvxy_tile_stream_probe(a.data_ptr(), b.data_ptr(), entries, grid, interleave, sink.data_ptr(), None)
+    torch.cuda.synchronize()
+    assert float(sink[0]) == 0.0
+    with pytest.raises(xt.XtvxyError):  # not a whole number of tiles per wavefront
+        xt.xtvxy_tile_stream_probe(a.data_ptr(), b.data_ptr(), entries - 4, grid, interleave, sink.data_ptr(), None)
