@@ -466,16 +466,15 @@ def report_tuning(args, p, kind, abytes, env):
     t0 = time.perf_counter()
     if kind == "dense":
         X = env["X"]
-        tune_fn = xt.xtvxy_dense_bf16_tune if env["bf16"] else xt.xtvxy_dense_f32_tune
+        tune_fn = (xt.xtvxy_dense_f16_tune if env.get("f16") else
+                   xt.xtvxy_dense_bf16_tune if env["bf16"] else xt.xtvxy_dense_f32_tune)
         rep = tune_fn(p.m, p.n, p.alpha, X.data_ptr(), p.ldx, xt._ptr(v), y.data_ptr(), p.beta,
                                       xt._ptr(z), out.data_ptr(), args.tune_repeats, sh)
     else:
         rp, ci, vals = env["rp"], env["ci"], env["vals"]
-        if env.get("bf16"):
-            raise SystemExit("the CSR tuner takes fp32 values")
-        rep = xt.xtvxy_csr_f32_tune(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
-                                    xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(),
-                                    args.tune_repeats, sh)
+        tune_fn = xt.xtvxy_csr_bf16_tune if env.get("bf16") else xt.xtvxy_csr_f32_tune
+        rep = tune_fn(p.m, p.n, p.nnz, p.alpha, rp.data_ptr(), ci.data_ptr(), vals.data_ptr(),
+                      xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z), out.data_ptr(), args.tune_repeats, sh)
     wall = time.perf_counter() - t0
     r = rep.as_dict()
     keep = lambda d: {k: v_ for k, v_ in d.items() if k != "predicted_seconds"}
@@ -522,8 +521,6 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
     # the fp32 fused path on the widened numbers
     f16 = getattr(p, "x_dtype", "f32") == "f16"
     bf16 = getattr(p, "x_dtype", "f32") == "bf16" or f16 or getattr(p, "values_dtype", "f32") == "bf16"
-    if f16 and args.tune:
-        raise SystemExit("the tuner takes fp32 or bf16 X")
     plan_text = args.plan if headline else None
     with_unfused = unfused_calls > 0 and not args.fused_only
     if kind == "dense":
@@ -576,7 +573,7 @@ def measure_workload(name, args, steps, warmup, unfused_calls, cpu_budget, headl
                                                               p.m, xt._ptr(v), y.data_ptr(), p.beta, xt._ptr(z),
                                                               out.data_ptr(), uws.data_ptr(), uws_bytes, sh)
         shape = {"m": p.m, "n": p.n, "ldx": p.ldx, "x_storage": p.x_dtype}
-        env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16}
+        env = {"X": X, "y": y, "v": v, "z": z, "out": out, "sh": sh, "bf16": bf16, "f16": f16}
     else:
         rp, ci, vals = t(p.row_ptr), t(p.col_idx), t(p.values)
         analysed = csr_path == "analysed"

@@ -49,7 +49,7 @@ __all__ = [
     "xtvxy_csr_f32_analysed_ex", "CsrAnalysis", "xtvxy_csr_bf16", "xtvxy_csr_bf16_ex", "xtvxy_csr_bf16_analysed",
     "xtvxy_csr_bf16_analysed_ex", "xtvxy_dense_f16", "xtvxy_dense_f16_ex", "xtvxy_csr_bf16_rowdot",
     "xtvxy_csr_bf16_rowdot_ex", "xtvxy_csr_bf16_tmv", "xtvxy_csr_bf16_tmv_ex", "xtvxy_logreg_newton_cg_bf16",
-    "xtvxy_tile_stream_probe",
+    "xtvxy_tile_stream_probe", "xtvxy_dense_f16_tune", "xtvxy_csr_bf16_tune",
 ]
 
 load = _abi.load
@@ -369,6 +369,21 @@ def xtvxy_csr_f32_tune(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z
     rep = xtvxy_tune_report()
     _abi.call("xtvxy_csr_f32_tune", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, int(repeats),
               stream, ctypes.byref(rep))
+    return rep
+
+
+def xtvxy_csr_bf16_tune(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, repeats,
+                        stream) -> xtvxy_tune_report:
+    rep = xtvxy_tune_report()
+    _abi.call("xtvxy_csr_bf16_tune", m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, int(repeats),
+              stream, ctypes.byref(rep))
+    return rep
+
+
+def xtvxy_dense_f16_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream) -> xtvxy_tune_report:
+    rep = xtvxy_tune_report()
+    _abi.call("xtvxy_dense_f16_tune", m, n, alpha, X, ldx, v, y, beta, z, out, int(repeats), stream,
+              ctypes.byref(rep))
     return rep
 
 
@@ -850,20 +865,20 @@ def dense_tune(X, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=1
     ldx = max(X.stride(0) if m > 1 else n, n, 1)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=X.device)
-    if X.dtype == torch.float16:
-        raise ValueError("the tuner takes float32 or bf16 X (fp16 X takes the bf16 plans)")
-    fn = xtvxy_dense_bf16_tune if X.dtype in (torch.bfloat16, torch.uint16) else xtvxy_dense_f32_tune
+    fn = (xtvxy_dense_f16_tune if X.dtype == torch.float16 else
+          xtvxy_dense_bf16_tune if X.dtype in (torch.bfloat16, torch.uint16) else xtvxy_dense_f32_tune)
     return fn(m, n, float(alpha), X.data_ptr(), ldx, _ptr(v), y.data_ptr(), float(beta), _ptr(z),
                                 out.data_ptr(), repeats, _stream_handle(stream)).as_dict()
 
 
 def csr_tune(row_ptr, col_idx, values, n, y, v=None, z=None, alpha=1.0, beta=0.0, out=None, *, repeats=10,
              stream=None) -> dict:
-    """Tune the CSR fused call on these tensors; returns the report."""
+    """Tune the CSR fused call on these tensors (bf16 values take xtvxy_csr_bf16_tune); returns the
+    report."""
     torch = _torch()
-    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values)
+    m, nnz, device = _check_csr_arrays(row_ptr, col_idx, values, bf16_ok=True)
     if out is None:
         out = torch.empty(n, dtype=torch.float32, device=device)
-    return xtvxy_csr_f32_tune(m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx), _ptr(values), _ptr(v),
+    return (xtvxy_csr_bf16_tune if _is_bf16(values) else xtvxy_csr_f32_tune)(m, n, nnz, float(alpha), row_ptr.data_ptr(), _ptr(col_idx), _ptr(values), _ptr(v),
                               y.data_ptr(), float(beta), _ptr(z), out.data_ptr(), repeats,
                               _stream_handle(stream)).as_dict()

@@ -169,6 +169,10 @@ SIGNATURES = {
                               _P(xtvxy_tune_report)],
     "xtvxy_csr_f32_tune": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
                            _P(xtvxy_tune_report)],
+    "xtvxy_dense_f16_tune": [_i64, _i64, _f32, _vp, _i64, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                             _P(xtvxy_tune_report)],
+    "xtvxy_csr_bf16_tune": [_i64, _i64, _i64, _f32, _vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _vp,
+                            _P(xtvxy_tune_report)],
     "xtvxy_tune_cache_lookup": [_i32, _i64, _i64, _i64, _i32, _P(xtvxy_tune_report), _P(ctypes.c_int32)],
     "xtvxy_tune_cache_clear": [],
     "xtvxy_tune_cache_save": [ctypes.c_char_p],

@@ -756,8 +756,8 @@ xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const void* X, 
 }
 xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
-                            float beta, const float* z, const float* out, bool* quick) {
-  return check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, quick);
+                            float beta, const float* z, const float* out, bool* quick, int value_bytes) {
+  return check_csr(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, quick, value_bytes);
 }
 }  // namespace xtvxy
 

@@ -229,7 +229,7 @@ xtvxy_status check_dense_args(int64_t m, int64_t n, float alpha, const void* X, 
                               const float* y, float beta, const float* z, const float* out, bool* quick, int elem_bytes = 4);
 xtvxy_status check_csr_args(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
                             const int32_t* col_idx, const float* values, const float* v, const float* y,
-                            float beta, const float* z, const float* out, bool* quick);
+                            float beta, const float* z, const float* out, bool* quick, int value_bytes = 4);
 
 // What an analysed CSR call adds to a fused CSR launch: the row-class work list (for the
 // XTVXY_CSR_ROWS kernel) and the permutation of the relabelled output columns.

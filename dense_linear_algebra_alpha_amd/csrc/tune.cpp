@@ -34,7 +34,7 @@ constexpr int kFinalists = 6;  // re-timed together with the model's plan
 
 struct Key {
   std::string device;
-  int32_t kind;  // 0 dense fp32, 1 csr, 2 dense bf16
+  int32_t kind;  // 0 dense fp32, 1 csr fp32 values, 2 dense bf16, 3 dense fp16, 4 csr bf16 values
   int64_t m, n, k;  // k: ldx (dense) or nnz (csr)
   int32_t aligned;
   bool operator<(const Key& o) const {
@@ -325,7 +325,7 @@ extern "C" {
 
 static xtvxy_status dense_tune(int64_t m, int64_t n, float alpha, const void* X, int64_t ldx, const float* v,
                                const float* y, float beta, const float* z, float* out, int32_t repeats,
-                               hipStream_t stream, xtvxy_tune_report* report, int elem_bytes) {
+                               hipStream_t stream, xtvxy_tune_report* report, int elem_bytes, bool f16 = false) {
   if (!report) return XTVXY_ERROR_NULL_POINTER;
   if (repeats < 1 || repeats > 10000) return XTVXY_ERROR_INVALID_VALUE;
   bool quick = false;
@@ -335,7 +335,7 @@ static xtvxy_status dense_tune(int64_t m, int64_t n, float alpha, const void* X,
   const int aligned = (reinterpret_cast<uintptr_t>(X) % 16 == 0) ? 1 : 0;
   Key key;
   if ((st = device_key(&key.device)) != XTVXY_SUCCESS) return st;
-  key.kind = elem_bytes == 2 ? 2 : 0;
+  key.kind = f16 ? 3 : elem_bytes == 2 ? 2 : 0;
   key.m = m;
   key.n = n;
   key.k = ldx;
@@ -353,6 +353,9 @@ static xtvxy_status dense_tune(int64_t m, int64_t n, float alpha, const void* X,
   DeviceBuffer ws;
   if (ws_bytes > 0 && hipMalloc(&ws.p, ws_bytes) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   auto run = [&](const xtvxy_launch_params& p) {
+    if (f16)
+      return xtvxy_dense_f16_ex(m, n, alpha, static_cast<const uint16_t*>(X), ldx, v, y, beta, z, out, ws.p,
+                                ws_bytes, stream, &p);
     if (elem_bytes == 2)
       return xtvxy_dense_bf16_ex(m, n, alpha, static_cast<const uint16_t*>(X), ldx, v, y, beta, z, out, ws.p,
                                  ws_bytes, stream, &p);
@@ -378,19 +381,28 @@ xtvxy_status xtvxy_dense_bf16_tune(int64_t m, int64_t n, float alpha, const uint
   return dense_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream, report, 2);
 }
 
-xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
-                                const int32_t* col_idx, const float* values, const float* v, const float* y,
-                                float beta, const float* z, float* out, int32_t repeats, hipStream_t stream,
-                                xtvxy_tune_report* report) {
+xtvxy_status xtvxy_dense_f16_tune(int64_t m, int64_t n, float alpha, const uint16_t* X, int64_t ldx,
+                                  const float* v, const float* y, float beta, const float* z, float* out,
+                                  int32_t repeats, hipStream_t stream, xtvxy_tune_report* report) {
+  return dense_tune(m, n, alpha, X, ldx, v, y, beta, z, out, repeats, stream, report, 2, true);
+}
+
+// CSR with fp32 (value_bytes 4) or bf16 (2) values; bf16 values take the tile and wavefront
+// candidates only (the row-class kernel reads fp32 values).
+static xtvxy_status csr_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                             const int32_t* col_idx, const void* values, int value_bytes, const float* v,
+                             const float* y, float beta, const float* z, float* out, int32_t repeats,
+                             hipStream_t stream, xtvxy_tune_report* report) {
   if (!report) return XTVXY_ERROR_NULL_POINTER;
   if (repeats < 1 || repeats > 10000) return XTVXY_ERROR_INVALID_VALUE;
   bool quick = false;
-  xtvxy_status st = check_csr_args(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, &quick);
+  xtvxy_status st = check_csr_args(m, n, nnz, alpha, row_ptr, col_idx, static_cast<const float*>(values), v, y,
+                                   beta, z, out, &quick, value_bytes);
   if (st != XTVXY_SUCCESS) return st;
   if (quick) return XTVXY_ERROR_INVALID_VALUE;
   Key key;
   if ((st = device_key(&key.device)) != XTVXY_SUCCESS) return st;
-  key.kind = 1;
+  key.kind = value_bytes == 2 ? 4 : 1;
   key.m = m;
   key.n = n;
   key.k = nnz;
@@ -401,13 +413,20 @@ xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, 
   xtvxy_launch_params model;
   if ((st = xtvxy_csr_f32_plan(m, n, nnz, nullptr, &model)) != XTVXY_SUCCESS) return st;
   std::vector<xtvxy_launch_params> cands = csr_candidates(m, n, nnz, d, model);
+  if (value_bytes == 2)
+    cands.erase(std::remove_if(cands.begin(), cands.end(),
+                               [](const xtvxy_launch_params& c) { return c.kernel == XTVXY_CSR_ROWS; }),
+                cands.end());
   size_t ws_bytes = (size_t)model.workspace_bytes;
   for (const auto& c : cands) ws_bytes = std::max(ws_bytes, (size_t)c.workspace_bytes);
   DeviceBuffer ws;
   if (ws_bytes > 0 && hipMalloc(&ws.p, ws_bytes) != hipSuccess) return XTVXY_ERROR_LAUNCH;
   auto run = [&](const xtvxy_launch_params& p) {
-    return xtvxy_csr_f32_ex(m, n, nnz, alpha, row_ptr, col_idx, values, v, y, beta, z, out, ws.p, ws_bytes,
-                            stream, &p);
+    if (value_bytes == 2)
+      return xtvxy_csr_bf16_ex(m, n, nnz, alpha, row_ptr, col_idx, static_cast<const uint16_t*>(values), v, y, beta,
+                               z, out, ws.p, ws_bytes, stream, &p);
+    return xtvxy_csr_f32_ex(m, n, nnz, alpha, row_ptr, col_idx, static_cast<const float*>(values), v, y, beta, z,
+                            out, ws.p, ws_bytes, stream, &p);
   };
   xtvxy_tune_report rep{};
   if ((st = tune(cands, model, run, repeats, stream, &rep)) != XTVXY_SUCCESS) return st;
@@ -416,10 +435,24 @@ xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, 
   return XTVXY_SUCCESS;
 }
 
+xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                const int32_t* col_idx, const float* values, const float* v, const float* y,
+                                float beta, const float* z, float* out, int32_t repeats, hipStream_t stream,
+                                xtvxy_tune_report* report) {
+  return csr_tune(m, n, nnz, alpha, row_ptr, col_idx, values, 4, v, y, beta, z, out, repeats, stream, report);
+}
+
+xtvxy_status xtvxy_csr_bf16_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t* row_ptr,
+                                 const int32_t* col_idx, const uint16_t* values, const float* v, const float* y,
+                                 float beta, const float* z, float* out, int32_t repeats, hipStream_t stream,
+                                 xtvxy_tune_report* report) {
+  return csr_tune(m, n, nnz, alpha, row_ptr, col_idx, values, 2, v, y, beta, z, out, repeats, stream, report);
+}
+
 xtvxy_status xtvxy_tune_cache_lookup(int32_t kind, int64_t m, int64_t n, int64_t k, int32_t aligned,
                                      xtvxy_tune_report* report, int32_t* found) {
   if (!report || !found) return XTVXY_ERROR_NULL_POINTER;
-  if (kind != 0 && kind != 1 && kind != 2) return XTVXY_ERROR_INVALID_VALUE;
+  if (kind < 0 || kind > 4) return XTVXY_ERROR_INVALID_VALUE;
   Key key;
   const xtvxy_status st = device_key(&key.device);
   if (st != XTVXY_SUCCESS) return st;
@@ -485,7 +518,7 @@ xtvxy_status xtvxy_tune_cache_load(const char* path) {
     }
     double best_s = 0, model_s = 0;
     if (!bad && std::sscanf(p, " %lf %lf %d", &best_s, &model_s, &cands) != 3) bad = true;
-    if (bad || kind < 0 || kind > 2 || m < 0 || n < 0 || k < 0 || !(best_s > 0) || !(model_s > 0)) {
+    if (bad || kind < 0 || kind > 4 || m < 0 || n < 0 || k < 0 || !(best_s > 0) || !(model_s > 0)) {
       bad = true;
       break;
     }

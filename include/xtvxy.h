@@ -567,9 +567,18 @@ xtvxy_status xtvxy_csr_f32_tune(int64_t m, int64_t n, int64_t nnz, float alpha, 
                                 const int32_t *col_idx, const float *values, const float *v, const float *y,
                                 float beta, const float *z, float *out, int32_t repeats, hipStream_t stream,
                                 xtvxy_tune_report *report);
-/* Cache access: kind 0 = dense fp32 X and 2 = dense bf16 X (k = ldx, aligned = X % 16 == 0), 1 = CSR
- * (k = nnz, aligned = values and col_idx 16-byte aligned); *found = 0 when the shape was not tuned
- * on the current device.
+/* The same for fp16 X (the candidates of bf16 X, timed with the fp16 kernels) and for bf16 CSR
+ * values (the tile and wavefront candidates; the row-class kernel takes fp32 values only). */
+xtvxy_status xtvxy_dense_f16_tune(int64_t m, int64_t n, float alpha, const uint16_t *X, int64_t ldx,
+                                  const float *v, const float *y, float beta, const float *z, float *out,
+                                  int32_t repeats, hipStream_t stream, xtvxy_tune_report *report);
+xtvxy_status xtvxy_csr_bf16_tune(int64_t m, int64_t n, int64_t nnz, float alpha, const int32_t *row_ptr,
+                                 const int32_t *col_idx, const uint16_t *values, const float *v, const float *y,
+                                 float beta, const float *z, float *out, int32_t repeats, hipStream_t stream,
+                                 xtvxy_tune_report *report);
+/* Cache access: kind 0 = dense fp32 X, 2 = dense bf16 X and 3 = dense fp16 X (k = ldx, aligned =
+ * X % 16 == 0), 1 = CSR with fp32 values and 4 = CSR with bf16 values (k = nnz, aligned = values
+ * and col_idx 16-byte aligned); *found = 0 when the shape was not tuned on the current device.
  * save/load use a text file (one line per entry); load merges, and takes nothing from a file with
  * a malformed line (XTVXY_ERROR_INVALID_VALUE). Plans read from a file are checked again by the
  * _ex entry points that use them. */

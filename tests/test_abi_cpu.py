@@ -452,9 +452,22 @@ def test_tune_argument_errors(lib):
                                   None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_NULL_POINTER
     assert lib.xtvxy_csr_f32_tune(8, 8, 0, 1.0, FAKE, None, None, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5,
                                   None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # nnz = 0
+    # the fp16 dense and bf16 CSR tuners check as the others do (bf16 values span 2 bytes each)
+    assert lib.xtvxy_dense_f16_tune(8, 8, 1.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 0, None,
+                                    ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # repeats
+    assert lib.xtvxy_dense_f16_tune(8, 8, 0.0, FAKE, 8, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5, None,
+                                    ctypes.byref(rep)) == _abi.XTVXY_ERROR_INVALID_VALUE  # nothing to tune
+    assert lib.xtvxy_csr_bf16_tune(8, 8, 16, 1.0, None, FAKE, FAKE, None, FAKE + 4096, 0.0, None, FAKE + 8192, 5,
+                                   None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_NULL_POINTER
+    assert lib.xtvxy_csr_bf16_tune(8, 8, 16, 1.0, FAKE, FAKE + 1024, FAKE + 2048, None, FAKE + 4096, 0.0, None,
+                                   FAKE + 2048 + 28, 5, None, ctypes.byref(rep)) == _abi.XTVXY_ERROR_ALIASING
     found = ctypes.c_int32()
-    assert lib.xtvxy_tune_cache_lookup(3, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) == \
-        _abi.XTVXY_ERROR_INVALID_VALUE
+    for kind in (-1, 5):
+        assert lib.xtvxy_tune_cache_lookup(kind, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) == \
+            _abi.XTVXY_ERROR_INVALID_VALUE
+    for kind in range(5):  # nothing tuned yet: found = 0
+        assert lib.xtvxy_tune_cache_lookup(kind, 1, 1, 1, 0, ctypes.byref(rep), ctypes.byref(found)) in \
+            (_abi.XTVXY_SUCCESS, _abi.XTVXY_ERROR_LAUNCH)  # no device here: the key cannot be made
 
 
 def test_tune_cache_file_round_trip(lib, tmp_path):

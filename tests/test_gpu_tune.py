@@ -58,3 +58,36 @@ def test_csr_tune_picks_a_correct_plan(m, n, mean_len):
     if n > 8192:  # a wide matrix offers windows, atomics and bins to choose from
         assert rep["candidates"] >= 20
     xt.xtvxy_tune_cache_clear()
+
+
+@pytest.mark.parametrize("x_dtype,kind", [("bf16", 2), ("f16", 3)])
+def test_dense_tune_on_16_bit_x(x_dtype, kind):
+    p = datagen.dense_problem(3000, 3000, seed=77, x_dtype=x_dtype, z="uniform", beta=0.5)
+    d = DenseOnDevice(p)
+    xt.xtvxy_tune_cache_clear()
+    note("dense tune %s" % x_dtype)
+    rep = xt.dense_tune(d.X.view(p.m, p.n), d.y, d.v, d.z, p.alpha, p.beta, repeats=3)
+    check_report(rep)
+    ref, bnd = dense_oracle(p)
+    assert_parity(d.run(plan=xt.xtvxy_launch_params(**rep["best"])), ref, bnd, "dense %s tuned plan" % x_dtype)
+    aligned = 1 if d.X.data_ptr() % 16 == 0 else 0
+    found_rep, found = xt.xtvxy_tune_cache_lookup(kind, p.m, p.n, p.n, aligned)
+    assert found and found_rep.best.as_dict() == rep["best"]
+    assert not xt.xtvxy_tune_cache_lookup(0 if kind != 0 else 2, p.m, p.n, p.n, aligned)[1]  # kinds kept apart
+    xt.xtvxy_tune_cache_clear()
+
+
+def test_csr_tune_on_bf16_values():
+    p = datagen.csr_values_bf16(datagen.csr_random(20000, 200000, seed=5, mean_len=20.0, beta=0.5))
+    d = CsrOnDevice(p)
+    xt.xtvxy_tune_cache_clear()
+    note("csr tune bf16 values")
+    rep = xt.csr_tune(d.rp, d.ci, d.vals, p.n, d.y, d.v, d.z, p.alpha, p.beta, repeats=3)
+    check_report(rep)
+    assert rep["best"]["kernel"] != xt.XTVXY_CSR_ROWS
+    ref, bnd = csr_oracle(p)
+    assert_parity(d.run(plan=xt.xtvxy_launch_params(**rep["best"])), ref, bnd, "csr bf16 tuned plan")
+    aligned = 1 if d.vals.data_ptr() % 16 == 0 and d.ci.data_ptr() % 16 == 0 else 0
+    assert xt.xtvxy_tune_cache_lookup(4, p.m, p.n, p.nnz, aligned)[1]
+    assert not xt.xtvxy_tune_cache_lookup(1, p.m, p.n, p.nnz, aligned)[1]
+    xt.xtvxy_tune_cache_clear()
